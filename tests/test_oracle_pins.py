@@ -1,0 +1,508 @@
+"""Pins of the CPU oracle to facts outside itself (runs on CPU, no GPU).
+
+Each pin is written as a function that raises AssertionError when the oracle
+disagrees with: the worked example printed by [p3] 'How FlashInfer's Paged KV
+Cache Attention Outperforms SDPA Fallback in Streaming Inference'
+(§Inspecting Cache Statistics), closed forms of the append-only special
+stream, the definition of the visible set, PyTorch's
+scaled_dot_product_attention (an independent library routine), brute force
+on tiny inputs, and softmax invariants.  The last tests plant plausible
+mistakes in the oracle and check that some pin catches each one.
+"""
+import collections
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import kvc_synth as syn
+from oracle import kvc_oracle as ko
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def tiny_cfg(**kw):
+    wl = syn.WORKLOADS["tiny"]
+    d = dict(num_heads=wl.num_heads, head_dim=wl.head_dim, tokens_per_frame=wl.tokens_per_frame,
+             num_special_tokens=wl.num_special_tokens, page_size=wl.page_size,
+             scale_frames=wl.scale_frames, sliding_window=wl.sliding_window,
+             max_patch_pages=wl.max_patch_pages, max_special_pages=wl.max_special_pages)
+    d.update(kw)
+    return ko.OracleConfig(**d)
+
+
+def rand_bits(rng, shape, scale=1.0):
+    return syn.f32_to_bf16_bits(rng.standard_normal(shape).astype(np.float32) * np.float32(scale))
+
+
+def frame_source(cfg, seed, scale_q=1.0):
+    cache = {}
+
+    def kv(s, f, b):
+        key = (s, f, b)
+        if key not in cache:
+            args = (cfg.tokens_per_frame, cfg.num_heads, cfg.head_dim, cfg.num_special_tokens, cfg.row_offset)
+            cache[key] = (syn.frame_tensor(seed, s, f, b, "k", *args),
+                          syn.frame_tensor(seed, s, f, b, "v", *args))
+        return cache[key]
+
+    def q(s, f, b):
+        return syn.frame_tensor(seed, s, f, b, "q", cfg.tokens_per_frame, cfg.num_heads, cfg.head_dim,
+                                cfg.num_special_tokens, cfg.row_offset, scale=scale_q)
+    return kv, q
+
+
+# --------------------------------------------------------------------------
+# pins (each raises AssertionError on disagreement)
+# --------------------------------------------------------------------------
+
+def pin_worked_example(oracle=ko):
+    with open(os.path.join(GOLDEN, "cache_stats_example.json")) as fh:
+        g = json.load(fh)
+    c = g["config"]
+    cfg = oracle.OracleConfig(num_heads=1, head_dim=8, tokens_per_frame=c["tokens_per_frame"],
+                              num_special_tokens=c["num_special_tokens"], page_size=c["page_size"],
+                              scale_frames=c["scale_frames"], sliding_window=c["sliding_window"],
+                              max_patch_pages=c["max_patch_pages"],
+                              max_special_pages=-(-c["max_total_frames"] * c["num_special_tokens"] // c["page_size"]))
+    a = oracle.AllocatorReplay(cfg)
+    for _ in range(g["frames"]):
+        a.append_frame(0)
+        a.evict_frames(0)
+    assert a.get_cache_stats(0) == g["expected"], (a.get_cache_stats(0), g["expected"])
+
+
+def pin_special_closed_forms(oracle=ko):
+    for n_s, pg, frames in [(6, 256, [1, 42, 200, 10000]), (6, 16, list(range(1, 13))),
+                            (6, 1024, [500]), (6, 256, [50, 400, 1500, 4000]), (5, 7, list(range(1, 30)))]:
+        F_max = max(frames)
+        P = min(pg, 16)
+        cfg = oracle.OracleConfig(num_heads=1, head_dim=8, tokens_per_frame=P + n_s,
+                                  num_special_tokens=n_s, page_size=pg,
+                                  scale_frames=1, sliding_window=2, max_patch_pages=4,
+                                  max_special_pages=-(-F_max * n_s // pg))
+        pg_eff = pg
+        a = oracle.AllocatorReplay(cfg)
+        for F in range(1, F_max + 1):
+            a.append_frame(0)
+            a.evict_frames(0)
+            if F in frames:
+                st = a.get_cache_stats(0)
+                assert st["special_tokens"] == n_s * F
+                plan = a.plan([0])
+                assert plan["n_special_pages"][0] == -(-n_s * F // pg_eff)
+                assert plan["last_page_len"][0] == ((n_s * F - 1) % pg_eff) + 1
+    # values quoted for the benchmark workloads
+    expect = {200: (5, 176), 10000: (235, 96), 50: (2, 44), 400: (10, 96), 1500: (36, 40), 4000: (94, 192)}
+    for F, (pages, last) in expect.items():
+        assert -(-6 * F // 256) == pages and ((6 * F - 1) % 256) + 1 == last
+
+
+def pin_visible_set(oracle=ko, S=8, W=64, frames=300):
+    cfg = oracle.OracleConfig(num_heads=1, head_dim=8, tokens_per_frame=262, num_special_tokens=6,
+                              page_size=256, scale_frames=S, sliding_window=W, max_patch_pages=S + W + 1,
+                              max_special_pages=-(-frames * 6 // 256))
+    a = oracle.AllocatorReplay(cfg)
+    for t in range(frames):
+        a.append_frame(0)
+        a.evict_frames(0)
+        plan = a.plan([0])
+        n_patch = int(plan["n_patch_pages"][0])
+        assert n_patch == min(t + 1, S + W)
+        vis = [f for f in range(t + 1) if f < S or f > t - W]          # independent definition
+        pages_by_frame = [a.streams[0].frames[f].patch_page for f in vis]
+        assert list(plan["kv_indices"][:n_patch]) == pages_by_frame
+        # order scale -> window -> specials
+        assert list(plan["kv_indices"][n_patch:]) == a.streams[0].all_special_pages
+    assert n_patch == 72 or (S, W) != (8, 64)
+
+
+def pin_sdpa(oracle=ko, seed=0):
+    """oracle attention == PyTorch scaled_dot_product_attention (fp64, CPU)."""
+    rng = np.random.default_rng(seed)
+    for T, L, H, D, sc in [(22, 152, 2, 32, 1.0), (7, 300, 3, 64, 3.0), (5, 1, 1, 16, 1.0), (262, 700, 2, 64, 1.0)]:
+        q, k, v = rand_bits(rng, (T, H, D), sc), rand_bits(rng, (L, H, D)), rand_bits(rng, (L, H, D))
+        ours = oracle.attention_fp64(q, k, v)
+        tq = torch.from_numpy(syn.bf16_bits_to_f32(q).astype(np.float64)).permute(1, 0, 2)[None]
+        tk = torch.from_numpy(syn.bf16_bits_to_f32(k).astype(np.float64)).permute(1, 0, 2)[None]
+        tv = torch.from_numpy(syn.bf16_bits_to_f32(v).astype(np.float64)).permute(1, 0, 2)[None]
+        ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv)[0].permute(1, 0, 2).numpy()
+        np.testing.assert_allclose(ours, ref, rtol=1e-12, atol=1e-12)
+
+
+def pin_bruteforce(oracle=ko, seed=1):
+    """Scalar loops straight from the definition of softmax attention."""
+    rng = np.random.default_rng(seed)
+    T, L, H, D = 3, 5, 2, 4
+    q, k, v = rand_bits(rng, (T, H, D), 2.0), rand_bits(rng, (L, H, D)), rand_bits(rng, (L, H, D))
+    Q, K, V = (syn.bf16_bits_to_f32(x).astype(float).tolist() for x in (q, k, v))
+    out = oracle.attention_fp64(q, k, v)
+    for i in range(T):
+        for h in range(H):
+            logits = [sum(Q[i][h][d] * K[j][h][d] for d in range(D)) / math.sqrt(D) for j in range(L)]
+            w = [math.exp(x) for x in logits]
+            z = sum(w)
+            for d in range(D):
+                o = sum(w[j] * V[j][h][d] for j in range(L)) / z
+                assert abs(o - out[i, h, d]) < 1e-12
+
+
+def pin_softmax_invariants(oracle=ko, seed=2):
+    rng = np.random.default_rng(seed)
+    T, L, H, D = 9, 40, 2, 32
+    q, k = rand_bits(rng, (T, H, D)), rand_bits(rng, (L, H, D))
+    c = syn.f32_to_bf16_bits(np.full((L, H, D), 0.7109375, np.float32))    # exactly representable
+    o = oracle.attention_fp64(q, k, c)
+    np.testing.assert_allclose(o, 0.7109375, rtol=0, atol=1e-14)
+    # planted key k* = alpha * q_0 dominates query row 0
+    v = rand_bits(rng, (L, H, D))
+    qf = syn.bf16_bits_to_f32(q)
+    k2 = k.copy()
+    k2[17] = syn.f32_to_bf16_bits(qf[0] * 8.0)
+    o = oracle.attention_fp64(q, k2, v)
+    np.testing.assert_allclose(o[0], syn.bf16_bits_to_f32(v[17]), atol=1e-6)
+    # joint permutation of keys and values
+    perm = rng.permutation(L)
+    o1 = oracle.attention_fp64(q, k, v)
+    o2 = oracle.attention_fp64(q, k[perm], v[perm])
+    np.testing.assert_allclose(o1, o2, rtol=1e-12, atol=1e-13)
+    # a query of zeros averages the values uniformly
+    qz = np.zeros_like(q)
+    np.testing.assert_allclose(oracle.attention_fp64(qz, k, v),
+                               np.broadcast_to(syn.bf16_bits_to_f32(v).astype(np.float64).mean(0), (T, H, D)),
+                               atol=1e-14)
+
+
+def pin_paged_equals_dense(oracle=ko, cfg=None, frames=12, seed=0, orders=(None, None), check_every=1):
+    """Paged attention over the simulated pool == dense attention over the
+    history gathered from the definition of the visible set (bitwise)."""
+    cfg = cfg or tiny_cfg()
+    kv, q = frame_source(cfg, seed)
+    o = oracle.OracleStream(cfg, blocks=(0,), free_patch_order=orders[0], free_special_order=orders[1])
+    outs = []
+    for t in range(frames):
+        plan = o.step([0], kv)
+        if t % check_every and t != frames - 1:
+            continue
+        qb = q(0, t, 0)
+        paged = o.attend(plan, 0, qb)
+        kd, vd = oracle.gather_dense(cfg, t, lambda f: kv(0, f, 0))
+        dense = oracle.attention_fp64(qb, kd, vd)
+        assert np.array_equal(paged, dense), f"step {t}"
+        outs.append(paged)
+    return outs
+
+
+# --------------------------------------------------------------------------
+# tests
+# --------------------------------------------------------------------------
+
+def test_worked_example_cache_stats():
+    pin_worked_example()
+
+
+def test_special_stream_closed_forms():
+    pin_special_closed_forms()
+
+
+def test_visible_set_and_order():
+    pin_visible_set()
+    pin_visible_set(S=1, W=4, frames=40)
+
+
+def test_attention_matches_torch_sdpa():
+    pin_sdpa()
+
+
+def test_attention_bruteforce():
+    pin_bruteforce()
+
+
+def test_softmax_invariants():
+    pin_softmax_invariants()
+
+
+def test_paged_equals_dense_tiny():
+    pin_paged_equals_dense()
+
+
+def test_paged_equals_dense_base_shape():
+    # base page geometry (256 patches + 6 specials, S=8, W=64) at reduced H, D
+    cfg = ko.OracleConfig(num_heads=1, head_dim=16, tokens_per_frame=262, num_special_tokens=6, page_size=256,
+                          scale_frames=8, sliding_window=64, max_patch_pages=88, max_special_pages=4)
+    pin_paged_equals_dense(cfg=cfg, frames=150, check_every=37)
+
+
+def test_padded_patch_pages_equal_dense():
+    # page_size > P: 13 patches in 16-slot pages (pad slots never attended)
+    cfg = ko.OracleConfig(num_heads=2, head_dim=16, tokens_per_frame=19, num_special_tokens=6, page_size=16,
+                          scale_frames=2, sliding_window=3, max_patch_pages=6, max_special_pages=10)
+    pin_paged_equals_dense(cfg=cfg, frames=20)
+
+
+def test_specials_first_row_layout():
+    cfg = tiny_cfg(special_row_offset=0)
+    pin_paged_equals_dense(cfg=cfg, frames=12)
+
+
+def test_page_permutation_invariance():
+    cfg = tiny_cfg()
+    base = pin_paged_equals_dense(cfg=cfg, frames=12)
+    po = syn.free_list_order(7, cfg.max_patch_pages, 0, 0)
+    so = syn.free_list_order(7, cfg.max_special_pages, cfg.max_patch_pages, 1)
+    assert list(po) != list(range(cfg.max_patch_pages))
+    perm = pin_paged_equals_dense(cfg=cfg, frames=12, orders=(po, so))
+    for a, b in zip(base, perm):
+        assert np.array_equal(a, b)
+
+
+def test_single_frame_reduces_to_sdpa():
+    cfg = tiny_cfg()
+    kv, q = frame_source(cfg, 3)
+    o = ko.OracleStream(cfg)
+    plan = o.step([0], kv)
+    qb = q(0, 0, 0)
+    out = o.attend(plan, 0, qb)
+    k, v = kv(0, 0, 0)
+    sel = np.concatenate([syn.patch_rows(22, 6, 16), syn.special_rows(22, 6, 16)])
+    tq, tk, tv = (torch.from_numpy(syn.bf16_bits_to_f32(x).astype(np.float64)).permute(1, 0, 2)[None]
+                  for x in (qb, k[sel], v[sel]))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv)[0].permute(1, 0, 2).numpy()
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_tiny_boundary_cases():
+    cfg = tiny_cfg()
+    a = ko.AllocatorReplay(cfg)
+    seen_full_tail = seen_straddle = seen_reuse = False
+    last_freed = []
+    for t in range(12):
+        fs = a.append_frame(0)
+        if last_freed:
+            # one spare page beyond S+W: the page freed last step is the one reused now
+            assert fs.patch_page == last_freed[0]
+            seen_reuse = True
+        pages = {p for p, _ in fs.special}
+        if len(pages) == 2:
+            seen_straddle = True
+            if t == 2:      # tokens 12..17: slots 12..15 of one page, 0..1 of the next
+                assert [s for _, s in fs.special] == [12, 13, 14, 15, 0, 1]
+        last_freed = a.evict_frames(0)
+        plan = a.plan([0])
+        if plan["last_page_len"][0] == cfg.page_size:
+            seen_full_tail = True
+            assert t == 7
+    assert seen_full_tail and seen_straddle and seen_reuse
+
+
+def test_conservation_and_uniqueness_multi_stream():
+    wl = syn.WORKLOADS["frag"]
+    cfg = ko.OracleConfig(num_heads=1, head_dim=8, tokens_per_frame=wl.tokens_per_frame,
+                          num_special_tokens=6, page_size=256, scale_frames=wl.scale_frames,
+                          sliding_window=wl.sliding_window, max_patch_pages=wl.max_patch_pages,
+                          max_special_pages=wl.max_special_pages, num_streams=4)
+    a = ko.AllocatorReplay(cfg, syn.free_list_order(wl.seed, wl.max_patch_pages, 0, 0),
+                           syn.free_list_order(wl.seed, wl.max_special_pages, wl.max_patch_pages, 1))
+    total = max(wl.frames)
+    for step in range(total):
+        active = [s for s in range(4) if step >= syn.stream_join_step(wl, s)]
+        for s in active:
+            a.append_frame(s)
+        for s in active:
+            a.evict_frames(s)
+        if step % 97 == 0 or step == total - 1:
+            plan = a.plan(active)
+            idx = plan["kv_indices"]
+            assert len(set(idx.tolist())) == len(idx)
+            held = sum(len(a.streams[s].scale_patch_pages) + len(a.streams[s].live_window_patch_pages)
+                       for s in range(4))
+            assert held + len(a.free_patch_pages) == cfg.max_patch_pages
+            held_sp = sum(len(a.streams[s].all_special_pages) for s in range(4))
+            assert held_sp + len(a.free_special_pages) == cfg.max_special_pages
+    assert [a.streams[s].frame_count for s in range(4)] == list(wl.frames)
+    # free special pool is exactly used up by the sizing rule
+    assert len(a.free_special_pages) == 0
+
+
+def test_streams_are_independent():
+    # two streams sharing one pool and free lists attend exactly as alone
+    cfg = tiny_cfg(num_streams=2, max_patch_pages=12, max_special_pages=10)
+    kv, q = frame_source(cfg, 5)
+    both = ko.OracleStream(cfg)
+    solo_cfg = tiny_cfg()
+    for t in range(12):
+        plan = both.step([0, 1], kv)
+        qb = np.concatenate([q(0, t, 0), q(1, t, 0)])
+        out = both.attend(plan, 0, qb)
+        for s in range(2):
+            kd, vd = ko.gather_dense(solo_cfg, t, lambda f: kv(s, f, 0))
+            ref = ko.attention_fp64(q(s, t, 0), kd, vd)
+            assert np.array_equal(out[s * 22:(s + 1) * 22], ref)
+
+
+def test_pool_exhaustion_leaves_state_unchanged():
+    cfg = tiny_cfg(max_special_pages=3)      # 48 special slots: 8 frames of 6
+    a = ko.AllocatorReplay(cfg)
+    for _ in range(8):
+        a.append_frame(0)
+        a.evict_frames(0)
+    before = (a.get_cache_stats(0), list(a.free_patch_pages), list(a.free_special_pages))
+    with pytest.raises(ko.PoolExhausted):
+        a.append_frame(0)
+    assert (a.get_cache_stats(0), list(a.free_patch_pages), list(a.free_special_pages)) == before
+
+
+def test_constant_footprint_long_stream():
+    wl = syn.WORKLOADS["long"]
+    cfg = ko.OracleConfig(num_heads=wl.num_heads, head_dim=wl.head_dim, tokens_per_frame=wl.tokens_per_frame,
+                          num_special_tokens=6, page_size=256, scale_frames=8, sliding_window=64,
+                          max_patch_pages=wl.max_patch_pages, max_special_pages=wl.max_special_pages)
+    before = ko.pool_bytes(cfg, wl.num_blocks)
+    a = ko.AllocatorReplay(cfg)
+    for t in range(10000):
+        a.append_frame(0)
+        a.evict_frames(0)
+        assert len(a.streams[0].live_window_patch_pages) <= 64
+        assert len(a.free_patch_pages) >= 88 - 72 - 1
+    plan = a.plan([0])
+    assert plan["n_patch_pages"][0] == 72 and plan["n_special_pages"][0] == 235
+    assert plan["last_page_len"][0] == 96
+    assert ko.pool_bytes(cfg, wl.num_blocks) == before == 24 * (88 + 235) * 2 * 256 * 16 * 64 * 2
+
+
+def test_reset_replays_identically():
+    cfg = tiny_cfg()
+    a = ko.AllocatorReplay(cfg)
+    first = []
+    for _ in range(9):
+        a.append_frame(0)
+        a.evict_frames(0)
+        first.append({k: v.tolist() for k, v in a.plan([0]).items()})
+    a.reset()
+    for i in range(9):
+        a.append_frame(0)
+        a.evict_frames(0)
+        assert {k: v.tolist() for k, v in a.plan([0]).items()} == first[i]
+
+
+# --------------------------------------------------------------------------
+# planted mistakes: each must be caught by at least one pin
+# --------------------------------------------------------------------------
+
+class _Mutant:
+    """A copy of the oracle module's namespace with one function replaced."""
+
+    def __init__(self, **overrides):
+        self.__dict__.update({k: getattr(ko, k) for k in dir(ko) if not k.startswith("__")})
+        self.__dict__.update(overrides)
+
+
+def _no_scale(q_bits, k_bits, v_bits):
+    q = syn.bf16_bits_to_f32(q_bits).astype(np.float64)
+    k = syn.bf16_bits_to_f32(k_bits).astype(np.float64)
+    v = syn.bf16_bits_to_f32(v_bits).astype(np.float64)
+    out = np.empty(q.shape)
+    for h in range(q.shape[1]):
+        s = q[:, h, :] @ k[:, h, :].T
+        p = np.exp(s - s.max(1, keepdims=True))
+        out[:, h, :] = (p / p.sum(1, keepdims=True)) @ v[:, h, :]
+    return out
+
+
+def _values_are_keys(q_bits, k_bits, v_bits):
+    return ko.attention_fp64(q_bits, k_bits, k_bits)
+
+
+def _sum_over_queries(q_bits, k_bits, v_bits):
+    q = syn.bf16_bits_to_f32(q_bits).astype(np.float64)
+    k = syn.bf16_bits_to_f32(k_bits).astype(np.float64)
+    v = syn.bf16_bits_to_f32(v_bits).astype(np.float64)
+    out = np.empty(q.shape)
+    for h in range(q.shape[1]):
+        s = (q[:, h, :] @ k[:, h, :].T) / math.sqrt(q.shape[2])
+        p = np.exp(s - s.max(0, keepdims=True))
+        p = p / p.sum(0, keepdims=True)          # normalised over the wrong axis
+        out[:, h, :] = p @ v[:, h, :]
+    return out
+
+
+class _OffByOneWindow(ko.AllocatorReplay):
+    def evict_frames(self, stream):
+        st = self.streams[stream]
+        while len(st.live_window_patch_pages) > self.cfg.sliding_window - 1:
+            self.free_patch_pages.append(st.live_window_patch_pages.popleft())
+
+
+class _SpecialsFirst(ko.AllocatorReplay):
+    def build_visible_page_table(self, stream):
+        st = self.streams[stream]
+        return list(st.all_special_pages) + list(st.scale_patch_pages) + list(st.live_window_patch_pages)
+
+
+class _LastPageZeroWhenFull(ko.AllocatorReplay):
+    def compute_last_page_len(self, stream):
+        return super().compute_last_page_len(stream) % self.cfg.page_size
+
+
+class _ScaleEvicted(ko.AllocatorReplay):
+    def append_frame(self, stream):
+        fs = super().append_frame(stream)
+        st = self.streams[stream]
+        if len(st.scale_patch_pages) == self.cfg.scale_frames and st.frame_count == self.cfg.scale_frames:
+            # wrongly treat scale frames as ordinary window frames
+            st.live_window_patch_pages.extendleft(reversed(st.scale_patch_pages))
+            st.scale_patch_pages.clear()
+        return fs
+
+
+class _LifoSpecialReuse(ko.AllocatorReplay):
+    def append_frame(self, stream):
+        fs = super().append_frame(stream)
+        self.streams[stream].special_tokens += 0 if fs.patch_page % 2 else 1   # drifts the special count
+        return fs
+
+
+def _pins_fail(mutant, pins):
+    for pin in pins:
+        try:
+            pin(mutant)
+        except AssertionError:
+            return True
+    return False
+
+
+ALL_PINS = [pin_worked_example, pin_special_closed_forms, pin_visible_set, pin_sdpa, pin_bruteforce,
+            pin_softmax_invariants, pin_paged_equals_dense]
+
+
+@pytest.mark.parametrize("mutant", [
+    _Mutant(attention_fp64=_no_scale),
+    _Mutant(attention_fp64=_values_are_keys),
+    _Mutant(attention_fp64=_sum_over_queries),
+    _Mutant(AllocatorReplay=_OffByOneWindow),
+    _Mutant(AllocatorReplay=_SpecialsFirst),
+    _Mutant(AllocatorReplay=_LastPageZeroWhenFull),
+    _Mutant(AllocatorReplay=_ScaleEvicted),
+    _Mutant(AllocatorReplay=_LifoSpecialReuse),
+], ids=["no_scale", "values_are_keys", "wrong_softmax_axis", "window_off_by_one", "specials_first",
+        "last_page_zero", "scale_evicted", "special_count_drift"])
+def test_planted_mistake_is_caught(mutant):
+    # OracleStream inside the mutant must use the mutant's allocator
+    class _Stream(ko.OracleStream):
+        def __init__(self, cfg, blocks=(0,), free_patch_order=None, free_special_order=None):
+            self.cfg = cfg
+            self.alloc = mutant.AllocatorReplay(cfg, free_patch_order, free_special_order)
+            self.pools = {b: ko.SimulatedPool(cfg) for b in blocks}
+
+        def attend(self, plan, block, q_bits):
+            T = self.cfg.tokens_per_frame
+            outs = []
+            for i in range(len(plan["last_page_len"])):
+                k, v = mutant.gather_paged(self.cfg, self.pools[block], plan, i)
+                outs.append(mutant.attention_fp64(q_bits[i * T:(i + 1) * T], k, v))
+            return np.concatenate(outs)
+    mutant.OracleStream = _Stream
+    assert _pins_fail(mutant, ALL_PINS)
