@@ -1,0 +1,302 @@
+#!/usr/bin/env python3
+"""Throughput of the two-stream paged KV-cache attention hot path on one GPU.
+
+A step is one frame step of the whole path: for every stream, the new frame
+is appended to every block's pool, the window is evicted, one plan is built
+and uploaded, and paged attention runs for every block.  The default
+workload is the 256-patch, 64-frame-window stream (24 blocks, H=16, D=64,
+256 patch + 6 special tokens per frame, page_size 256, 8 scale frames, 200
+frames); the timed steps are the last --steps frames of the 200-frame stream,
+preceded by --warmup full steps and an untimed append-only fast-forward.
+
+Inputs are synthetic: a device-resident bank of distinct seeded N(0,1) bf16
+frames per block, indexed by frame; the kernels have no data-dependent
+control flow.  Everything timed is resident in HBM when timing starts.
+
+Prints one JSON line: frame-steps/s, the attention kernel's roofline
+(algorithmic bytes or FLOP per launch over its HIP-event-measured duration),
+and the CPU oracle timed on the host as a reported baseline.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "frame-steps/sec (all blocks) + attn TFLOP/s & HBM GB/s vs MI355X peak"
+PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2516.6
+BANK = 8
+
+
+def progress(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    p = os.path.join(ROOT, "paged_kv_cache_kvc_amd", "csrc", "kvc_kernels.hip")
+    with open(p, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def read_traffic(workload):
+    """HBM bytes per attention launch measured by rocprofv3 counters (committed
+    under profiles/), or None when missing or taken on other kernel source."""
+    p = os.path.join(ROOT, "profiles", f"attn_{workload}_traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as fh:
+        t = json.load(fh)
+    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, seconds):
+    """The CPU oracle as it stands, timed on this host: dense float64
+    attention (gather of the visible tokens + softmax(QK^T/sqrt(D))V) for the
+    blocks of steady-state steps at the end of the stream."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    import kvc_synth as syn
+    from oracle import kvc_oracle as ko
+
+    T, H, D = wl.tokens_per_frame, wl.num_heads, wl.head_dim
+    F = max(wl.frames)
+    t = F - 1
+    ocfg = ko.OracleConfig(num_heads=H, head_dim=D, tokens_per_frame=T, num_special_tokens=wl.num_special_tokens,
+                           page_size=wl.page_size, scale_frames=wl.scale_frames, sliding_window=wl.sliding_window,
+                           max_patch_pages=wl.max_patch_pages, max_special_pages=wl.max_special_pages)
+    vis = set(ko.visible_frames(t, wl.scale_frames, wl.sliding_window))
+    cache = {}
+
+    def frame_kv(f):
+        if f not in cache:
+            args = (T, H, D, wl.num_special_tokens, wl.row_offset)
+            real = f in vis
+            cache[f] = (syn.frame_tensor(wl.seed, 0, f, 0, "k", *args, patch_real=real),
+                        syn.frame_tensor(wl.seed, 0, f, 0, "v", *args, patch_real=real))
+        return cache[f]
+
+    q = syn.frame_tensor(wl.seed, 0, t, 0, "q", T, H, D, wl.num_special_tokens, wl.row_offset)
+    for f in range(F):
+        frame_kv(f)
+    blocks = 0
+    t0 = time.perf_counter()
+    while True:
+        k, v = ko.gather_dense(ocfg, t, frame_kv)
+        ko.attention_fp64(q, k, v)
+        blocks += 1
+        el = time.perf_counter() - t0
+        if el >= seconds and blocks >= 1:
+            break
+    L = k.shape[0]
+    threads = 1
+    for info in threadpool_info():
+        if info.get("user_api") == "blas":
+            threads = max(threads, int(info.get("num_threads", 1)))
+    steps = blocks / wl.num_blocks
+    return {
+        "value": steps / el,
+        "unit": "frame-steps/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"{blocks} block(s) of dense float64 oracle attention (gather + softmax) at frame {F}, "
+                   f"T={T}, L={L}, H={H}, D={D}; {el:.1f} s on {threads} BLAS thread(s) of "
+                   f"{len(os.sched_getaffinity(0))} available; one block's seeded history reused per block; "
+                   f"frame-steps/s = blocks/{wl.num_blocks}/s"),
+        "gflops": 4.0 * T * L * H * D * blocks / el / 1e9,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="base", choices=["base", "r518", "long", "frag"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--target-wgs", type=int, default=None)
+    ap.add_argument("--max-splits", type=int, default=None)
+    ap.add_argument("--no-profile", action="store_true", help="time without per-launch HIP events")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only: this path has no multi-GPU mode (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE {world}); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import kvc_synth as syn
+    import paged_kv_cache_kvc_amd as kvc
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = syn.WORKLOADS[args.workload]
+    F = max(wl.frames)
+    K, W = args.steps, args.warmup
+    if K < 1 or W < 0 or K + W > F:
+        print(f"need 1 <= steps and steps + warmup <= {F}", file=sys.stderr)
+        sys.exit(2)
+    nb, T, H, D = wl.num_blocks, wl.tokens_per_frame, wl.num_heads, wl.head_dim
+    ns = wl.num_streams
+
+    cfg = kvc.make_config(nb, H, D, T, wl.num_special_tokens, page_size=wl.page_size, scale_frames=wl.scale_frames,
+                          sliding_window=wl.sliding_window, num_streams=ns, max_patch_pages=wl.max_patch_pages,
+                          max_special_pages=wl.max_special_pages, special_row_offset=wl.row_offset)
+    po = so = None
+    if wl.shuffle_free_lists:
+        po = syn.free_list_order(wl.seed, wl.max_patch_pages, 0, 0)
+        so = syn.free_list_order(wl.seed, wl.max_special_pages, wl.max_patch_pages, 1)
+    cache = kvc.PagedKVCache(cfg, device=dev, free_patch_order=po, free_special_order=so)
+    if args.target_wgs:
+        cache.set_option(kvc.KVC_OPT_TARGET_WORKGROUPS, args.target_wgs)
+    if args.max_splits:
+        cache.set_option(kvc.KVC_OPT_MAX_SPLITS, args.max_splits)
+
+    # device-resident input bank: [stream][bank][block] frames
+    progress(f"workload {wl.name}: generating input bank")
+    g = torch.Generator(device=dev)
+    g.manual_seed(wl.seed)
+
+    def bank(scale=1.0):
+        x = torch.randn((ns, BANK, nb, T, H, D), generator=g, device=dev, dtype=torch.float32)
+        return x.mul_(scale).to(torch.bfloat16)
+    qb, kb, vb = bank(), bank(), bank()
+    ob = torch.empty((ns * T, H, D), dtype=torch.bfloat16, device=dev)
+    qcat = torch.empty((BANK, nb, ns * T, H, D), dtype=torch.bfloat16, device=dev)
+    for s in range(ns):
+        qcat[:, :, s * T:(s + 1) * T] = qb[s]
+
+    hs = torch.cuda.current_stream(dev).cuda_stream
+    frame_of = [0] * ns
+    gstep = [0]
+
+    def active():
+        return [s for s in range(ns) if gstep[0] >= syn.stream_join_step(wl, s)]
+
+    def kv_ptrs(s, b):
+        f = frame_of[s] % BANK
+        return kb[s, f, b].data_ptr(), vb[s, f, b].data_ptr()
+
+    def step(run):
+        act = active()
+        for s in act:
+            kp, vp = kv_ptrs(s, 0)
+            cache.raw_append(0, kp, vp, s, hs)
+        for s in act:
+            cache.evict_frames(s)
+        if run:
+            if len(act) != ns:
+                raise RuntimeError("timed steps must advance every stream")
+            cache.raw_plan(hs)
+            qf = qcat[frame_of[0] % BANK]
+            cache.raw_run(0, qf[0].data_ptr(), ob.data_ptr(), hs)
+        for b in range(1, nb):
+            for s in act:
+                kp, vp = kv_ptrs(s, b)
+                cache.raw_append(b, kp, vp, s, hs)
+            if run:
+                cache.raw_run(b, qf[b].data_ptr(), ob.data_ptr(), hs)
+        for s in act:
+            frame_of[s] += 1
+        gstep[0] += 1
+
+    total_steps = F
+    ff = total_steps - K - W
+    progress(f"fast-forward {ff} append-only steps")
+    for i in range(ff):
+        step(False)
+        if i % 1000 == 999:
+            torch.cuda.synchronize()
+            progress(f"  {i + 1} steps")
+    for _ in range(W):
+        step(True)
+    torch.cuda.synchronize()
+
+    # algorithmic work per timed step: visible valid tokens from the cache stats
+    def step_work():
+        fl = by = 0.0
+        for s in range(ns):
+            st = cache.get_cache_stats(s)
+            L = (st["scale_pages"] + st["live_pages"]) * wl.patch_tokens + st["special_tokens"]
+            fl += 4.0 * T * L * H * D
+            by += 4.0 * L * H * D + 4.0 * T * H * D   # K and V (bf16) read once, Q read, O written
+        return fl, by
+
+    if not args.no_profile:
+        cache.set_option(kvc.KVC_OPT_PROFILE, 1)
+        for k in (kvc.KVC_KERNEL_ATTENTION, kvc.KVC_KERNEL_MERGE, kvc.KVC_KERNEL_APPEND):
+            cache.profile_read(k, reset=True)
+    progress(f"timing {K} steps")
+    flops = bytes_ = 0.0
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(K):
+        step(True)
+        fl, by = step_work()
+        flops += fl * nb
+        bytes_ += by * nb
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = e0.elapsed_time(e1)
+    elapsed = max(wall, gpu_ms / 1e3)
+    value = K / elapsed
+
+    out = {
+        "metric": METRIC, "value": value, "unit": "frame-steps/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": 1e3 * elapsed / K, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": (f"{wl.name}: {nb} blocks, H={H}, D={D}, {wl.patch_tokens} patch + "
+                                f"{wl.num_special_tokens} special tokens/frame, page_size {wl.page_size}, "
+                                f"scale {wl.scale_frames}, window {wl.sliding_window}, streams {ns} at "
+                                f"{list(wl.frames)} frames; timed steps = last {K} frames"),
+                   "num_blocks": nb, "tokens_per_frame": T, "num_heads": H, "head_dim": D,
+                   "page_size": wl.page_size, "frames": list(wl.frames), "streams": ns},
+    }
+    if not args.no_profile:
+        a_ms, a_n = cache.profile_read(kvc.KVC_KERNEL_ATTENTION)
+        m_ms, m_n = cache.profile_read(kvc.KVC_KERNEL_MERGE)
+        p_ms, p_n = cache.profile_read(kvc.KVC_KERNEL_APPEND)
+        gbs = bytes_ / (a_ms / 1e3) / 1e9
+        tfl = flops / (a_ms / 1e3) / 1e12
+        bound = "hbm" if flops / bytes_ < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9) else "mfma"
+        traffic = read_traffic(wl.name)
+        if bound == "hbm":
+            roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS}
+        else:
+            roof = {"bound": "mfma", "achieved": tfl, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": tfl / PEAK_BF16_TFLOPS}
+        roof["traffic"] = traffic
+        out["roofline"] = roof
+        out["attention"] = {
+            "kernel": "attn_kernel", "launches": a_n, "avg_us": 1e3 * a_ms / max(a_n, 1),
+            "tflops": tfl, "gbs": gbs, "frac_hbm": gbs / PEAK_HBM_GBS, "frac_mfma": tfl / PEAK_BF16_TFLOPS,
+            "alg_bytes_per_launch": bytes_ / max(a_n, 1), "alg_flop_per_launch": flops / max(a_n, 1),
+            "merge_avg_us": 1e3 * m_ms / max(m_n, 1), "merge_launches": m_n,
+            "append_avg_us": 1e3 * p_ms / max(p_n, 1), "append_launches": p_n,
+        }
+    progress(json.dumps({k: out[k] for k in ("value", "ms_per_step")}))
+    if not args.no_cpu_baseline:
+        progress("timing the CPU oracle")
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

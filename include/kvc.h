@@ -1,0 +1,252 @@
+/*
+ * kvc.h - two-stream paged KV-cache prefill attention for streaming 3-D
+ * reconstruction, native to AMD Instinct MI355X (gfx950).
+ *
+ * Sources are five web pages on the lingbot-map paged KV cache, cited by tag
+ * and section:
+ *   [p1] "How FlashInfer KV Cache Attention Accelerates Streaming 3D
+ *        Reconstruction Over SDPA"
+ *   [p2] "How LingBot-Map Uses FlashInfer KV Cache for Streaming 3D
+ *        Reconstruction"
+ *   [p3] "How FlashInfer's Paged KV Cache Attention Outperforms SDPA Fallback
+ *        in Streaming Inference"
+ *   [p4] "FlashInfer Backend in LingBot-Map: Accelerating Streaming Inference
+ *        with Paged KV Cache"
+ *   [p5] "How Paged KV Cache Attention Achieves Stable Inference in
+ *        Ling-Bot-Map"
+ *
+ * What the library computes.  Each transformer block owns a page pool
+ * [max_num_pages, 2, page_size, H, D] of bf16 in NHD order, dimension 1 being
+ * 0 = K and 1 = V ([p1] §Paged KV Cache Memory Layout; [p5] §Core
+ * Implementation Mechanics).  Patch page IDs are [0, max_patch_pages), special
+ * page IDs [max_patch_pages, max_num_pages) ([p2] §Patch Stream and Special
+ * Stream).  Each frame's patch tokens fill one recyclable patch page; its
+ * special tokens pack continuously into an append-only special stream
+ * ([p3] §Two-Stream Design).  The frame's queries then attend, without a mask,
+ * over the visible page table scale -> live window -> specials, the last page
+ * holding last_page_len valid tokens ([p2] §Page Table Planning and Reuse):
+ *     o = softmax(q K^T / sqrt(D)) V   over every valid visible token.
+ * One plan is built per frame step and reused by every block ([p3] §Plan-Run
+ * Execution Workflow).
+ *
+ * Conventions.
+ *   - Every call returns kvc_status: KVC_OK (0) or a negative error code.  On
+ *     error kvc_last_error() describes it and host state is unchanged, except
+ *     for KVC_ERR_HIP where a device call failed after host state changed.
+ *   - Device pointers are HIP device addresses; "host" pointers are ordinary
+ *     process memory.  The caller owns every buffer it passes; the library
+ *     never allocates or frees device memory, so the device footprint is fixed
+ *     when the caller allocates the pools and workspace ([p5] FAQ on the
+ *     sliding window: memory does not grow with stream length).
+ *   - Device work is enqueued on the caller's HIP stream (kvc_stream_t is a
+ *     hipStream_t; NULL is the null stream).  Use one stream per context.
+ *   - A context is not thread-safe.
+ *
+ * Per frame step, the calls must come in this order ([p1] §FlashInferAttention
+ * Forward Pass: append, evict, then attention with the shared plan):
+ *   1. kvc_append_frame(s, block 0, ...) for every stream s that advances
+ *      (allocates its pages);
+ *   2. kvc_evict(s) for those streams;
+ *   3. kvc_plan() once (plans the streams of step 1, ascending stream index);
+ *   4. kvc_run(block 0, ...);
+ *   5. for every block b >= 1: kvc_append_frame(s, b, ...) for every planned
+ *      stream, then kvc_run(b, ...).
+ * Out-of-order calls return KVC_ERR_STATE.  The first kvc_append_frame(s, 0)
+ * after a plan, or a second one for the same stream before any plan, starts
+ * the next step (a step need not be planned: streaming ahead without
+ * attention is append + evict only).
+ */
+#ifndef KVC_H
+#define KVC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVC_ABI_VERSION 1
+
+typedef struct kvc_ctx kvc_ctx;
+typedef void* kvc_stream_t;   /* hipStream_t */
+typedef int32_t kvc_status;
+
+enum {
+  KVC_OK = 0,
+  KVC_ERR_ARG = -1,             /* bad argument (null, out of range, wrong size) */
+  KVC_ERR_STATE = -2,           /* call out of the per-step order */
+  KVC_ERR_POOL_EXHAUSTED = -3,  /* no free patch page, or the special pool is full ([p2] §Patch Stream and Special Stream) */
+  KVC_ERR_CAPACITY = -4,        /* configuration cannot hold the steady state */
+  KVC_ERR_HIP = -5,             /* a HIP runtime call failed */
+  KVC_ERR_UNSUPPORTED = -6      /* shape outside what the kernels are built for */
+};
+
+/* Sizing and shape of one cache ([p2] §Initializing the Cache Manager;
+ * [p5] §Initializing the Cache Manager).  All fields are required. */
+typedef struct kvc_config {
+  int32_t num_blocks;          /* transformer blocks, one pool each, >= 1 */
+  int32_t num_heads;           /* H: query and KV heads, >= 1 */
+  int32_t head_dim;            /* D: 32, 64 or 128 */
+  int32_t tokens_per_frame;    /* T = patch tokens P + special tokens n_s, >= 1 */
+  int32_t num_special_tokens;  /* n_s, 0 <= n_s < T, n_s <= 64 */
+  int32_t special_row_offset;  /* row of a frame's first special token in its [T] rows;
+                                  patch rows are the others in order (P means specials last) */
+  int32_t page_size;           /* tokens per page, >= P; P gives unpadded patch pages and larger
+                                  values zero-padded ones ([p1] §Efficient Attention Masking and Padding) */
+  int32_t scale_frames;        /* S: first S frames kept permanently ([p2] §Scale Frames vs Sliding Window) */
+  int32_t sliding_window;      /* W >= 1: most recent non-scale frames kept */
+  int32_t num_streams;         /* independent frame streams sharing the pools, >= 1 */
+  int32_t max_patch_pages;     /* >= num_streams * (S + W + 1) */
+  int32_t max_special_pages;   /* special pages shared by all streams, >= 0 */
+} kvc_config;
+
+/* [p3] §Inspecting Cache Statistics, plus the special-page counters. */
+typedef struct kvc_stats {
+  int64_t frame_count;         /* frames appended to this stream since create/reset */
+  int64_t special_tokens;      /* special tokens held by this stream */
+  int32_t scale_pages;         /* scale patch pages of this stream */
+  int32_t live_pages;          /* live-window patch pages of this stream */
+  int32_t free_pages;          /* free patch pages (shared by all streams) */
+  int32_t special_pages;       /* special pages of this stream */
+  int32_t free_special_pages;  /* free special pages (shared) */
+  int32_t reserved;
+} kvc_stats;
+
+/* Tunables for kvc_set_option / kvc_get_option. */
+enum {
+  KVC_OPT_TARGET_WORKGROUPS = 1, /* attention work-groups the planner aims for per run (default 2 per CU) */
+  KVC_OPT_MAX_SPLITS = 2,        /* cap on KV splits per stream; 1 disables split-KV (default 64, the maximum) */
+  KVC_OPT_PROFILE = 3            /* 1: time every attention/merge/append launch with HIP events */
+};
+
+/* Kernels for kvc_profile_read. */
+enum { KVC_KERNEL_ATTENTION = 0, KVC_KERNEL_MERGE = 1, KVC_KERNEL_APPEND = 2 };
+
+int32_t kvc_abi_version(void);
+const char* kvc_status_string(kvc_status status);
+
+/* Bytes of ONE block's pool: max_num_pages * 2 * page_size * H * D * 2, where
+ * max_num_pages = max_patch_pages + max_special_pages ([p2] §Physical Memory
+ * Layout).  Returns 0 for an invalid configuration. */
+size_t kvc_pool_bytes(const kvc_config* cfg);
+
+/* Bytes of device workspace the caller allocates for kvc_create: two plan
+ * buffers and the split-KV partial outputs (float32), sized for the maximum
+ * split count.  Returns 0 for an invalid configuration. */
+size_t kvc_workspace_bytes(const kvc_config* cfg);
+
+/* Bytes of pinned (page-locked) host staging for the per-step plan upload,
+ * double-buffered.  The caller allocates it with hipHostMalloc or an
+ * equivalent pinned allocator.  Returns 0 for an invalid configuration. */
+size_t kvc_staging_bytes(const kvc_config* cfg);
+
+/* Create a context on the current HIP device.
+ *   cfg:        configuration, copied.
+ *   pools:      host array of num_blocks device pointers, each to
+ *               kvc_pool_bytes(cfg) bytes, 16-byte aligned; zero-filled here
+ *               (synchronously) so pad slots are defined.
+ *   workspace:  device pointer to kvc_workspace_bytes(cfg) bytes, 256-byte
+ *               aligned.
+ *   staging:    pinned host pointer to kvc_staging_bytes(cfg) bytes.
+ *   free_patch_order / free_special_order: optional host arrays giving the
+ *               initial order of the free lists (permutations of
+ *               [0, max_patch_pages) and [max_patch_pages, max_num_pages));
+ *               NULL means ascending.  Pages are taken from the front and
+ *               freed to the back ([p1] §Two-Stream Design for Token Types:
+ *               deques).
+ *   out:        receives the context.
+ * Errors: KVC_ERR_ARG, KVC_ERR_CAPACITY (max_patch_pages too small),
+ * KVC_ERR_UNSUPPORTED (head_dim, or a shape the kernels do not cover),
+ * KVC_ERR_HIP. */
+kvc_status kvc_create(const kvc_config* cfg, void* const* pools, void* workspace, void* staging,
+                      const int32_t* free_patch_order, const int32_t* free_special_order,
+                      kvc_ctx** out);
+
+/* Create a context that keeps only the page bookkeeping and planning (no
+ * device buffers, no HIP calls).  kvc_append_frame takes k = v = NULL and
+ * only allocates; kvc_plan builds the host plan only; kvc_run returns
+ * KVC_ERR_STATE.  Used to replay or inspect plans without a GPU. */
+kvc_status kvc_create_metadata_only(const kvc_config* cfg, const int32_t* free_patch_order,
+                                    const int32_t* free_special_order, kvc_ctx** out);
+
+kvc_status kvc_destroy(kvc_ctx* ctx);
+
+/* [p5] §Resetting for New Sequences: clear page lists and counters and keep
+ * the buffers (pool contents are left as they are; only valid visible slots
+ * are ever read). */
+kvc_status kvc_reset(kvc_ctx* ctx);
+
+/* Write one frame's K and V for one block ([p5] §Frame Appending Without
+ * Dispatch Overhead; [p3] §Two-Stream Design).
+ *   k, v: device [T, H, D] bf16, NHD, contiguous, 16-byte aligned.
+ * At block 0 this also allocates the frame: one patch page from the free list
+ * (a scale page while the stream has fewer than S, else a live-window page)
+ * and the next n_s slots of the stream's special stream, taking a new special
+ * page whenever the tail page is full.  Blocks >= 1 reuse that page and those
+ * slots.  One kernel launch writes the patch rows to slots [0, P) of the page
+ * and each special row to its slot; pad slots are never written.
+ * Errors: KVC_ERR_ARG, KVC_ERR_STATE (block >= 1 before block 0 of the step,
+ * or a block >= 1 appended twice in one step), KVC_ERR_POOL_EXHAUSTED (block
+ * 0 only; nothing changes), KVC_ERR_HIP. */
+kvc_status kvc_append_frame(kvc_ctx* ctx, int32_t stream, int32_t block, const void* k, const void* v,
+                            kvc_stream_t hip_stream);
+
+/* [p5] §Sliding-Window Eviction Strategy: move the oldest live-window pages
+ * beyond the window back to the free list (host metadata only; scale pages
+ * are kept).  Idempotent within a step. */
+kvc_status kvc_evict(kvc_ctx* ctx, int32_t stream);
+
+/* Build the step's plan ([p3] §Plan-Run Execution Workflow): for each stream
+ * that appended block 0 this step, in ascending order, the visible page table
+ * (scale -> live window -> specials, [p2] §Page Table Planning and Reuse),
+ * the last page length ([p5] §Kernel Dispatch and Sequence Lengths), the
+ * query row ranges and the split-KV work list; then one asynchronous copy of
+ * the plan from pinned staging to the workspace on hip_stream.
+ * Errors: KVC_ERR_STATE (no stream appended, or already planned this step),
+ * KVC_ERR_HIP. */
+kvc_status kvc_plan(kvc_ctx* ctx, kvc_stream_t hip_stream);
+
+/* Paged attention for one block with the step's plan ([p2] §Attention Kernel
+ * Execution):
+ *   q: device [R, H, D] bf16, R = T * (number of planned streams), rows in
+ *      plan order (stream i's frame at rows [i*T, (i+1)*T)).
+ *   o: device [R, H, D] bf16, written; must not overlap q.
+ * Each stream's queries attend only to its own visible tokens.  Launches the
+ * attention kernel and, when a stream's KV is split, the merge kernel.
+ * Errors: KVC_ERR_ARG, KVC_ERR_STATE (not planned, or a planned stream has
+ * not appended this block), KVC_ERR_HIP. */
+kvc_status kvc_run(kvc_ctx* ctx, int32_t block, const void* q, void* o, kvc_stream_t hip_stream);
+
+/* Copy the current plan to host arrays (for bit-exact checks).
+ *   planned_streams[capacity_streams], kv_indptr[capacity_streams + 1],
+ *   last_page_len[capacity_streams], n_patch_pages[capacity_streams],
+ *   qo_indptr[capacity_streams + 1], n_splits[capacity_streams]:
+ *   per planned stream; kv_indices[capacity_indices]: concatenated tables.
+ *   Any array pointer may be NULL.  num_planned / num_indices receive the
+ *   sizes.  Errors: KVC_ERR_STATE (no plan), KVC_ERR_ARG (capacity short). */
+kvc_status kvc_get_plan(const kvc_ctx* ctx, int32_t* planned_streams, int32_t* kv_indptr,
+                        int32_t* kv_indices, int32_t* last_page_len, int32_t* n_patch_pages,
+                        int32_t* qo_indptr, int32_t* n_splits, int32_t capacity_streams,
+                        int32_t capacity_indices, int32_t* num_planned, int32_t* num_indices);
+
+/* [p3] §Inspecting Cache Statistics for one stream. */
+kvc_status kvc_get_stats(const kvc_ctx* ctx, int32_t stream, kvc_stats* out);
+
+kvc_status kvc_set_option(kvc_ctx* ctx, int32_t option, int64_t value);
+kvc_status kvc_get_option(const kvc_ctx* ctx, int32_t option, int64_t* value);
+
+/* Launch timing collected while KVC_OPT_PROFILE is 1: total milliseconds and
+ * number of launches of one kernel (KVC_KERNEL_*), measured with HIP events
+ * recorded around each launch on its stream.  Synchronizes with the recorded
+ * events.  reset != 0 clears the counters afterwards. */
+kvc_status kvc_profile_read(kvc_ctx* ctx, int32_t kernel, double* total_ms, int64_t* launches, int32_t reset);
+
+/* Description of the last error on this context (empty when none). */
+const char* kvc_last_error(const kvc_ctx* ctx);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVC_H */

@@ -1,0 +1,65 @@
+"""Build libkvc.so in-tree for gfx950 (MI355X).
+
+    python -m paged_kv_cache_kvc_amd.build
+
+HIP kernels are compiled by hipcc; the host allocator, planner and C-ABI are
+plain C++17 compiled by g++ against the HIP runtime headers; hipcc links the
+shared library.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+BUILD = os.path.join(HERE, "_build")
+LIB = os.path.join(HERE, "libkvc.so")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+ARCH = "gfx950"
+
+HIP_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
+    # packed fp32 VALU forms stay disabled: plain fp32 code is used instead
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-command-line-argument",
+]
+CXX_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-Wall", "-Wextra", "-Wno-unused-parameter",
+             "-D__HIP_PLATFORM_AMD__", f"-I{ROCM}/include"]
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"build step failed ({r.returncode}): {' '.join(cmd)}\n{out}")
+    if verbose and out.strip():
+        print(out)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link libkvc.so; always rebuilds."""
+    hipcc = os.path.join(ROCM, "bin", "hipcc")
+    cxx = shutil.which("g++") or "g++"
+    os.makedirs(BUILD, exist_ok=True)
+    objs = []
+    o = os.path.join(BUILD, "kvc_kernels.o")
+    _run([hipcc, *HIP_FLAGS, "-c", os.path.join(CSRC, "kvc_kernels.hip"), "-o", o], verbose)
+    objs.append(o)
+    for src in ("kvc_host.cpp", "kvc_api.cpp"):
+        o = os.path.join(BUILD, src.replace(".cpp", ".o"))
+        _run([cxx, *CXX_FLAGS, "-c", os.path.join(CSRC, src), "-o", o], verbose)
+        objs.append(o)
+    tmp = LIB + ".tmp"
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp,
+          f"-L{ROCM}/lib", "-lamdhip64", f"-Wl,-rpath,{ROCM}/lib"], verbose)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,512 @@
+// C-ABI of the two-stream paged KV cache (declared in include/kvc.h).
+//
+// Owns host metadata only: the page allocator, the per-step state machine and
+// the plan.  Every device buffer (pools, workspace) and the pinned staging
+// belong to the caller; the library never allocates device memory.
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/kvc.h"
+#include "kvc_host.hpp"
+#include "kvc_kernels.h"
+
+namespace {
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+kvc::Config to_cfg(const kvc_config& c) {
+  kvc::Config k;
+  k.num_blocks = c.num_blocks;
+  k.num_heads = c.num_heads;
+  k.head_dim = c.head_dim;
+  k.tokens_per_frame = c.tokens_per_frame;
+  k.num_special_tokens = c.num_special_tokens;
+  k.special_row_offset = c.special_row_offset;
+  k.page_size = c.page_size;
+  k.scale_frames = c.scale_frames;
+  k.sliding_window = c.sliding_window;
+  k.num_streams = c.num_streams;
+  k.max_patch_pages = c.max_patch_pages;
+  k.max_special_pages = c.max_special_pages;
+  return k;
+}
+
+// Workspace layout: [plan 0][plan 1][partial lse][partial o], 256-byte aligned.
+struct Layout {
+  size_t plan_bytes, plan0, plan1, lse, part_o, total;
+};
+
+Layout layout_of(const kvc::Config& c) {
+  Layout l;
+  l.plan_bytes = align_up(kvc::plan_image_ints(c) * sizeof(int32_t), 256);
+  l.plan0 = 0;
+  l.plan1 = l.plan_bytes;
+  l.lse = 2 * l.plan_bytes;
+  const size_t rows = (size_t)c.rows_capacity();
+  l.part_o = l.lse + align_up((size_t)KVC_MAX_SPLITS * rows * c.num_heads * sizeof(float), 256);
+  l.total = l.part_o + align_up((size_t)KVC_MAX_SPLITS * rows * c.num_heads * c.head_dim * sizeof(float), 256);
+  return l;
+}
+
+struct EventPair {
+  hipEvent_t start, stop;
+};
+
+}  // namespace
+
+struct kvc_ctx {
+  kvc::Config cfg;
+  bool metadata_only = false;
+  kvc::Allocator alloc;
+  std::vector<void*> pools;
+  char* workspace = nullptr;
+  char* staging = nullptr;
+  Layout lay;
+
+  // per-step state
+  bool planned = false;
+  bool have_plan = false;
+  std::vector<uint8_t> advanced;      // [stream]: appended block 0 this step
+  std::vector<uint8_t> block_done;    // [stream * num_blocks + block]
+  std::vector<kvc::FrameSlots> slots; // [stream]: this step's frame slots
+  kvc::HostPlan plan;
+  int plan_buf = 0;
+  hipEvent_t staging_done[2] = {nullptr, nullptr};
+  bool staging_recorded[2] = {false, false};
+
+  kvc::PlanPolicy policy;
+  int cu_count = 256;
+
+  bool profile = false;
+  std::vector<EventPair> pending[3];
+  std::vector<hipEvent_t> spare;
+  double prof_ms[3] = {0, 0, 0};
+  int64_t prof_n[3] = {0, 0, 0};
+
+  std::string err;
+};
+
+static kvc_status fail(kvc_ctx* c, kvc_status code, const std::string& msg) {
+  if (c) c->err = msg;
+  return code;
+}
+
+static kvc_status hip_fail(kvc_ctx* c, int e, const char* what) {
+  return fail(c, KVC_ERR_HIP, std::string(what) + ": " + hipGetErrorString((hipError_t)e));
+}
+
+static hipEvent_t take_event(kvc_ctx* c) {
+  if (!c->spare.empty()) {
+    hipEvent_t e = c->spare.back();
+    c->spare.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Records an event pair around `launch` when profiling is on.
+template <class F>
+static int timed(kvc_ctx* c, int kernel, void* stream, F launch) {
+  if (!c->profile) return launch();
+  EventPair ev{take_event(c), take_event(c)};
+  if (!ev.start || !ev.stop) return (int)hipErrorOutOfMemory;
+  (void)hipEventRecord(ev.start, (hipStream_t)stream);
+  const int rc = launch();
+  (void)hipEventRecord(ev.stop, (hipStream_t)stream);
+  c->pending[kernel].push_back(ev);
+  return rc;
+}
+
+extern "C" {
+
+int32_t kvc_abi_version(void) { return KVC_ABI_VERSION; }
+
+const char* kvc_status_string(kvc_status s) {
+  switch (s) {
+    case KVC_OK: return "ok";
+    case KVC_ERR_ARG: return "invalid argument";
+    case KVC_ERR_STATE: return "call out of order";
+    case KVC_ERR_POOL_EXHAUSTED: return "page pool exhausted";
+    case KVC_ERR_CAPACITY: return "capacity too small";
+    case KVC_ERR_HIP: return "HIP runtime error";
+    case KVC_ERR_UNSUPPORTED: return "unsupported shape";
+    default: return "unknown status";
+  }
+}
+
+size_t kvc_pool_bytes(const kvc_config* cfg) {
+  if (!cfg) return 0;
+  const kvc::Config c = to_cfg(*cfg);
+  if (kvc::validate(c, nullptr) != kvc::OK) return 0;
+  return (size_t)c.max_num_pages() * 2 * c.page_size * c.num_heads * c.head_dim * 2;
+}
+
+size_t kvc_workspace_bytes(const kvc_config* cfg) {
+  if (!cfg) return 0;
+  const kvc::Config c = to_cfg(*cfg);
+  if (kvc::validate(c, nullptr) != kvc::OK) return 0;
+  return layout_of(c).total;
+}
+
+size_t kvc_staging_bytes(const kvc_config* cfg) {
+  if (!cfg) return 0;
+  const kvc::Config c = to_cfg(*cfg);
+  if (kvc::validate(c, nullptr) != kvc::OK) return 0;
+  return 2 * layout_of(c).plan_bytes;
+}
+
+static kvc_status create_common(const kvc_config* cfg, const int32_t* fpo, const int32_t* fso, kvc_ctx** out,
+                                kvc_ctx** made) {
+  if (!cfg || !out) return KVC_ERR_ARG;
+  *out = nullptr;
+  kvc::Config c = to_cfg(*cfg);
+  std::string why;
+  const int v = kvc::validate(c, &why);
+  if (v != kvc::OK) return (kvc_status)v;
+  kvc_ctx* x = new (std::nothrow) kvc_ctx();
+  if (!x) return KVC_ERR_ARG;
+  x->cfg = c;
+  std::vector<int32_t> fp, fs;
+  if (fpo) fp.assign(fpo, fpo + c.max_patch_pages);
+  if (fso) fs.assign(fso, fso + c.max_special_pages);
+  if (fso && c.max_special_pages == 0) fs.clear();
+  const int rc = x->alloc.init(c, fp, fs, &why);
+  if (rc != kvc::OK) {
+    delete x;
+    return (kvc_status)rc;
+  }
+  x->advanced.assign(c.num_streams, 0);
+  x->block_done.assign((size_t)c.num_streams * c.num_blocks, 0);
+  x->slots.assign(c.num_streams, kvc::FrameSlots());
+  x->lay = layout_of(c);
+  *made = x;
+  return KVC_OK;
+}
+
+kvc_status kvc_create_metadata_only(const kvc_config* cfg, const int32_t* fpo, const int32_t* fso, kvc_ctx** out) {
+  kvc_ctx* x = nullptr;
+  const kvc_status rc = create_common(cfg, fpo, fso, out, &x);
+  if (rc != KVC_OK) return rc;
+  x->metadata_only = true;
+  x->policy.target_workgroups = 2 * x->cu_count;
+  *out = x;
+  return KVC_OK;
+}
+
+kvc_status kvc_create(const kvc_config* cfg, void* const* pools, void* workspace, void* staging,
+                      const int32_t* fpo, const int32_t* fso, kvc_ctx** out) {
+  if (!pools || !workspace || !staging) return KVC_ERR_ARG;
+  if (((uintptr_t)workspace & 255) != 0) return KVC_ERR_ARG;
+  kvc_ctx* x = nullptr;
+  const kvc_status rc = create_common(cfg, fpo, fso, out, &x);
+  if (rc != KVC_OK) return rc;
+  const size_t pb = kvc_pool_bytes(cfg);
+  for (int b = 0; b < x->cfg.num_blocks; ++b) {
+    if (!pools[b] || ((uintptr_t)pools[b] & 15) != 0) {
+      delete x;
+      return KVC_ERR_ARG;
+    }
+    x->pools.push_back(pools[b]);
+  }
+  x->workspace = static_cast<char*>(workspace);
+  x->staging = static_cast<char*>(staging);
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&x->cu_count, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+    delete x;
+    return KVC_ERR_HIP;
+  }
+  x->policy.target_workgroups = 2 * x->cu_count;
+  for (int b = 0; b < x->cfg.num_blocks; ++b) {
+    if (hipMemset(x->pools[b], 0, pb) != hipSuccess) {
+      delete x;
+      return KVC_ERR_HIP;
+    }
+  }
+  for (int i = 0; i < 2; ++i) {
+    if (hipEventCreateWithFlags(&x->staging_done[i], hipEventDisableTiming) != hipSuccess) {
+      delete x;
+      return KVC_ERR_HIP;
+    }
+  }
+  *out = x;
+  return KVC_OK;
+}
+
+kvc_status kvc_destroy(kvc_ctx* c) {
+  if (!c) return KVC_ERR_ARG;
+  if (!c->metadata_only) {
+    for (int i = 0; i < 2; ++i)
+      if (c->staging_done[i]) {
+        (void)hipEventSynchronize(c->staging_done[i]);
+        (void)hipEventDestroy(c->staging_done[i]);
+      }
+    for (int k = 0; k < 3; ++k)
+      for (auto& e : c->pending[k]) {
+        (void)hipEventSynchronize(e.stop);
+        (void)hipEventDestroy(e.start);
+        (void)hipEventDestroy(e.stop);
+      }
+    for (auto e : c->spare) (void)hipEventDestroy(e);
+  }
+  delete c;
+  return KVC_OK;
+}
+
+kvc_status kvc_reset(kvc_ctx* c) {
+  if (!c) return KVC_ERR_ARG;
+  c->alloc.reset();
+  c->planned = false;
+  c->have_plan = false;
+  std::fill(c->advanced.begin(), c->advanced.end(), 0);
+  std::fill(c->block_done.begin(), c->block_done.end(), 0);
+  c->err.clear();
+  return KVC_OK;
+}
+
+kvc_status kvc_append_frame(kvc_ctx* c, int32_t stream, int32_t block, const void* k, const void* v,
+                            kvc_stream_t hs) {
+  if (!c) return KVC_ERR_ARG;
+  const kvc::Config& cf = c->cfg;
+  if (stream < 0 || stream >= cf.num_streams) return fail(c, KVC_ERR_ARG, "stream out of range");
+  if (block < 0 || block >= cf.num_blocks) return fail(c, KVC_ERR_ARG, "block out of range");
+  if (c->metadata_only) {
+    if (k || v) return fail(c, KVC_ERR_ARG, "metadata-only context takes k = v = NULL");
+  } else if (!k || !v || ((uintptr_t)k & 15) || ((uintptr_t)v & 15)) {
+    return fail(c, KVC_ERR_ARG, "k and v must be 16-byte aligned device pointers");
+  }
+  const size_t bd = (size_t)stream * cf.num_blocks + block;
+  if (block == 0) {
+    // A plan, or a second block-0 append of the same stream, ends the step
+    // (an unplanned step simply runs no attention, as when fast-forwarding).
+    const bool new_step = c->planned || c->advanced[stream];
+    kvc::FrameSlots fs;
+    std::string why;
+    const int rc = c->alloc.append(stream, &fs, &why);
+    if (rc != kvc::OK) return fail(c, (kvc_status)rc, why);
+    if (new_step) {
+      c->planned = false;
+      std::fill(c->advanced.begin(), c->advanced.end(), 0);
+      std::fill(c->block_done.begin(), c->block_done.end(), 0);
+    }
+    c->advanced[stream] = 1;
+    c->slots[stream] = fs;
+  } else {
+    if (!c->advanced[stream]) return fail(c, KVC_ERR_STATE, "append of block >= 1 before block 0 in this step");
+    if (c->block_done[bd]) return fail(c, KVC_ERR_STATE, "block already appended for this stream in this step");
+  }
+  c->block_done[bd] = 1;
+  if (c->metadata_only) return KVC_OK;
+
+  const kvc::FrameSlots& fs = c->slots[stream];
+  kvc::AppendParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.pool = c->pools[block];
+  p.k = k;
+  p.v = v;
+  p.T = cf.tokens_per_frame;
+  p.row_elems = cf.num_heads * cf.head_dim;
+  p.special_row_offset = cf.special_row_offset;
+  p.n_special = cf.num_special_tokens;
+  p.page_size = cf.page_size;
+  p.patch_page = fs.patch_page;
+  p.sp_slot0 = fs.sp_slot0;
+  p.n_sp_pages = fs.n_sp_pages;
+  for (int i = 0; i < KVC_MAX_APPEND_SPECIAL_PAGES; ++i) p.sp_pages[i] = fs.sp_pages[i];
+  const int e = timed(c, KVC_KERNEL_APPEND, hs, [&] { return kvc::launch_append(p, hs); });
+  if (e) return hip_fail(c, e, "append launch");
+  return KVC_OK;
+}
+
+kvc_status kvc_evict(kvc_ctx* c, int32_t stream) {
+  if (!c) return KVC_ERR_ARG;
+  if (stream < 0 || stream >= c->cfg.num_streams) return fail(c, KVC_ERR_ARG, "stream out of range");
+  c->alloc.evict(stream);
+  return KVC_OK;
+}
+
+kvc_status kvc_plan(kvc_ctx* c, kvc_stream_t hs) {
+  if (!c) return KVC_ERR_ARG;
+  if (c->planned) return fail(c, KVC_ERR_STATE, "already planned this step");
+  std::vector<int32_t> streams;
+  for (int s = 0; s < c->cfg.num_streams; ++s)
+    if (c->advanced[s]) streams.push_back(s);
+  if (streams.empty()) return fail(c, KVC_ERR_STATE, "no stream appended block 0 this step");
+  kvc::build_plan(c->alloc, streams, c->policy, &c->plan);
+  c->planned = true;
+  c->have_plan = true;
+  if (c->metadata_only) return KVC_OK;
+
+  const int b = c->plan_buf ^ 1;
+  if (c->staging_recorded[b]) {
+    const hipError_t e = hipEventSynchronize(c->staging_done[b]);
+    if (e != hipSuccess) return hip_fail(c, e, "plan staging wait");
+  }
+  const size_t bytes = c->plan.image.size() * sizeof(int32_t);
+  char* host = c->staging + b * c->lay.plan_bytes;
+  std::memcpy(host, c->plan.image.data(), bytes);
+  char* dev = c->workspace + (b ? c->lay.plan1 : c->lay.plan0);
+  hipError_t e = hipMemcpyAsync(dev, host, bytes, hipMemcpyHostToDevice, (hipStream_t)hs);
+  if (e != hipSuccess) return hip_fail(c, e, "plan upload");
+  e = hipEventRecord(c->staging_done[b], (hipStream_t)hs);
+  if (e != hipSuccess) return hip_fail(c, e, "plan upload event");
+  c->staging_recorded[b] = true;
+  c->plan_buf = b;
+  return KVC_OK;
+}
+
+kvc_status kvc_run(kvc_ctx* c, int32_t block, const void* q, void* o, kvc_stream_t hs) {
+  if (!c) return KVC_ERR_ARG;
+  if (c->metadata_only) return fail(c, KVC_ERR_STATE, "metadata-only context cannot run");
+  const kvc::Config& cf = c->cfg;
+  if (block < 0 || block >= cf.num_blocks) return fail(c, KVC_ERR_ARG, "block out of range");
+  if (!q || !o || ((uintptr_t)q & 15) || ((uintptr_t)o & 15)) return fail(c, KVC_ERR_ARG, "q and o must be 16-byte aligned");
+  if (q == o) return fail(c, KVC_ERR_ARG, "o must not alias q");
+  if (!c->planned) return fail(c, KVC_ERR_STATE, "run before plan in this step");
+  for (int32_t s : c->plan.planned)
+    if (!c->block_done[(size_t)s * cf.num_blocks + block])
+      return fail(c, KVC_ERR_STATE, "a planned stream has not appended this block");
+
+  const int32_t* dplan = reinterpret_cast<const int32_t*>(c->workspace + (c->plan_buf ? c->lay.plan1 : c->lay.plan0));
+  float* lse = reinterpret_cast<float*>(c->workspace + c->lay.lse);
+  float* po = reinterpret_cast<float*>(c->workspace + c->lay.part_o);
+
+  kvc::AttnParams a;
+  std::memset(&a, 0, sizeof(a));
+  a.plan = dplan;
+  a.pool = c->pools[block];
+  a.q = q;
+  a.o = o;
+  a.part_o = po;
+  a.part_lse = lse;
+  a.num_heads = cf.num_heads;
+  a.head_dim = cf.head_dim;
+  a.page_size = cf.page_size;
+  a.patch_tokens = cf.patch_tokens();
+  a.rows_cap = cf.rows_capacity();
+  a.div_patch = kvc::make_fastdiv((uint32_t)std::max(1, cf.patch_tokens()));
+  a.div_page = kvc::make_fastdiv((uint32_t)cf.page_size);
+  a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)cf.head_dim));
+  a.num_items = c->plan.num_items;
+  a.items_per_xcd = (c->plan.num_items + 7) / 8;
+  const int32_t grid = 8 * a.items_per_xcd;
+  int e = timed(c, KVC_KERNEL_ATTENTION, hs, [&] { return kvc::launch_attention(a, grid, hs); });
+  if (e) return hip_fail(c, e, "attention launch");
+  if (c->plan.any_split) {
+    kvc::MergeParams m;
+    m.plan = dplan;
+    m.part_o = po;
+    m.part_lse = lse;
+    m.o = o;
+    m.num_heads = cf.num_heads;
+    m.head_dim = cf.head_dim;
+    m.rows_cap = cf.rows_capacity();
+    m.num_rows = c->plan.num_rows;
+    e = timed(c, KVC_KERNEL_MERGE, hs, [&] { return kvc::launch_merge(m, hs); });
+    if (e) return hip_fail(c, e, "merge launch");
+  }
+  return KVC_OK;
+}
+
+kvc_status kvc_get_plan(const kvc_ctx* c, int32_t* planned, int32_t* kv_indptr, int32_t* kv_indices,
+                        int32_t* last_page_len, int32_t* n_patch_pages, int32_t* qo_indptr, int32_t* n_splits,
+                        int32_t cap_streams, int32_t cap_indices, int32_t* num_planned, int32_t* num_indices) {
+  if (!c) return KVC_ERR_ARG;
+  kvc_ctx* m = const_cast<kvc_ctx*>(c);
+  if (!c->have_plan) return fail(m, KVC_ERR_STATE, "no plan");
+  const kvc::HostPlan& p = c->plan;
+  const int32_t n = (int32_t)p.planned.size();
+  const int32_t ni = (int32_t)p.kv_indices.size();
+  if (num_planned) *num_planned = n;
+  if (num_indices) *num_indices = ni;
+  if ((planned || kv_indptr || last_page_len || n_patch_pages || qo_indptr || n_splits) && cap_streams < n)
+    return fail(m, KVC_ERR_ARG, "capacity_streams too small");
+  if (kv_indices && cap_indices < ni) return fail(m, KVC_ERR_ARG, "capacity_indices too small");
+  if (planned) std::copy(p.planned.begin(), p.planned.end(), planned);
+  if (kv_indptr) std::copy(p.kv_indptr.begin(), p.kv_indptr.end(), kv_indptr);
+  if (kv_indices) std::copy(p.kv_indices.begin(), p.kv_indices.end(), kv_indices);
+  if (last_page_len) std::copy(p.last_page_len.begin(), p.last_page_len.end(), last_page_len);
+  if (n_patch_pages) std::copy(p.n_patch_pages.begin(), p.n_patch_pages.end(), n_patch_pages);
+  if (qo_indptr) std::copy(p.qo_indptr.begin(), p.qo_indptr.end(), qo_indptr);
+  if (n_splits) std::copy(p.n_split.begin(), p.n_split.end(), n_splits);
+  return KVC_OK;
+}
+
+kvc_status kvc_get_stats(const kvc_ctx* c, int32_t stream, kvc_stats* out) {
+  if (!c || !out) return KVC_ERR_ARG;
+  if (stream < 0 || stream >= c->cfg.num_streams) return KVC_ERR_ARG;
+  const kvc::StreamState& st = c->alloc.stream(stream);
+  std::memset(out, 0, sizeof(*out));
+  out->frame_count = st.frame_count;
+  out->special_tokens = st.special_tokens;
+  out->scale_pages = (int32_t)st.scale_pages.size();
+  out->live_pages = (int32_t)st.live_pages.size();
+  out->free_pages = c->alloc.free_patch_count();
+  out->special_pages = (int32_t)st.special_pages.size();
+  out->free_special_pages = c->alloc.free_special_count();
+  return KVC_OK;
+}
+
+kvc_status kvc_set_option(kvc_ctx* c, int32_t option, int64_t value) {
+  if (!c) return KVC_ERR_ARG;
+  switch (option) {
+    case KVC_OPT_TARGET_WORKGROUPS:
+      if (value < 1 || value > (1 << 20)) return fail(c, KVC_ERR_ARG, "target workgroups out of range");
+      c->policy.target_workgroups = (int32_t)value;
+      return KVC_OK;
+    case KVC_OPT_MAX_SPLITS:
+      if (value < 1 || value > KVC_MAX_SPLITS) return fail(c, KVC_ERR_ARG, "max splits must be in [1, 64]");
+      c->policy.max_splits = (int32_t)value;
+      return KVC_OK;
+    case KVC_OPT_PROFILE:
+      if (c->metadata_only && value) return fail(c, KVC_ERR_STATE, "metadata-only context has no kernels");
+      c->profile = value != 0;
+      return KVC_OK;
+    default:
+      return fail(c, KVC_ERR_ARG, "unknown option");
+  }
+}
+
+kvc_status kvc_get_option(const kvc_ctx* c, int32_t option, int64_t* value) {
+  if (!c || !value) return KVC_ERR_ARG;
+  switch (option) {
+    case KVC_OPT_TARGET_WORKGROUPS: *value = c->policy.target_workgroups; return KVC_OK;
+    case KVC_OPT_MAX_SPLITS: *value = c->policy.max_splits; return KVC_OK;
+    case KVC_OPT_PROFILE: *value = c->profile ? 1 : 0; return KVC_OK;
+    default: return KVC_ERR_ARG;
+  }
+}
+
+kvc_status kvc_profile_read(kvc_ctx* c, int32_t kernel, double* total_ms, int64_t* launches, int32_t reset) {
+  if (!c || kernel < 0 || kernel > 2) return KVC_ERR_ARG;
+  for (auto& ev : c->pending[kernel]) {
+    hipError_t e = hipEventSynchronize(ev.stop);
+    if (e != hipSuccess) return hip_fail(c, e, "profile event");
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, ev.start, ev.stop);
+    if (e != hipSuccess) return hip_fail(c, e, "profile elapsed");
+    c->prof_ms[kernel] += ms;
+    c->prof_n[kernel] += 1;
+    c->spare.push_back(ev.start);
+    c->spare.push_back(ev.stop);
+  }
+  c->pending[kernel].clear();
+  if (total_ms) *total_ms = c->prof_ms[kernel];
+  if (launches) *launches = c->prof_n[kernel];
+  if (reset) {
+    c->prof_ms[kernel] = 0;
+    c->prof_n[kernel] = 0;
+  }
+  return KVC_OK;
+}
+
+const char* kvc_last_error(const kvc_ctx* c) { return c ? c->err.c_str() : "null context"; }
+
+}  // extern "C"

@@ -1,0 +1,233 @@
+// Host page allocator and per-step planner (see kvc_host.hpp).
+#include "kvc_host.hpp"
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+
+namespace kvc {
+
+static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int validate(const Config& c, std::string* why) {
+  auto fail = [&](int code, const char* msg) {
+    if (why) *why = msg;
+    return code;
+  };
+  if (c.num_blocks < 1 || c.num_heads < 1 || c.num_streams < 1) return fail(ERR_ARG, "num_blocks, num_heads and num_streams must be >= 1");
+  if (c.head_dim != 32 && c.head_dim != 64 && c.head_dim != 128) return fail(ERR_UNSUPPORTED, "head_dim must be 32, 64 or 128");
+  if (c.tokens_per_frame < 1) return fail(ERR_ARG, "tokens_per_frame must be >= 1");
+  if (c.num_special_tokens < 0 || c.num_special_tokens >= c.tokens_per_frame)
+    return fail(ERR_ARG, "num_special_tokens must be in [0, tokens_per_frame)");
+  if (c.num_special_tokens > KVC_MAX_SPECIAL_PER_FRAME) return fail(ERR_UNSUPPORTED, "num_special_tokens above 64");
+  if (c.special_row_offset < 0 || c.special_row_offset + c.num_special_tokens > c.tokens_per_frame)
+    return fail(ERR_ARG, "special rows [special_row_offset, +n_s) must lie inside the frame");
+  if (c.page_size < c.patch_tokens() || c.page_size < 1) return fail(ERR_ARG, "page_size must be >= patch tokens");
+  if (c.num_special_tokens > 0 &&
+      ceil_div(c.page_size - 1 + c.num_special_tokens, c.page_size) > KVC_MAX_APPEND_SPECIAL_PAGES)
+    return fail(ERR_UNSUPPORTED, "one frame's specials would span more than 8 special pages");
+  if (c.scale_frames < 0 || c.sliding_window < 1) return fail(ERR_ARG, "scale_frames >= 0 and sliding_window >= 1 required");
+  if (c.max_special_pages < 0 || c.max_patch_pages < 0) return fail(ERR_ARG, "page counts must be >= 0");
+  if ((int64_t)c.max_patch_pages < (int64_t)c.num_streams * (c.scale_frames + c.sliding_window + 1))
+    return fail(ERR_CAPACITY, "max_patch_pages must be >= num_streams * (scale_frames + sliding_window + 1)");
+  const int64_t pages = (int64_t)c.max_patch_pages + c.max_special_pages;
+  if (pages * c.page_size >= (int64_t)1 << 31) return fail(ERR_UNSUPPORTED, "pool slots per block must be < 2^31");
+  if ((int64_t)c.num_heads * c.head_dim > 65536) return fail(ERR_UNSUPPORTED, "num_heads * head_dim above 65536");
+  if ((int64_t)c.num_streams * c.tokens_per_frame >= (int64_t)1 << 24) return fail(ERR_UNSUPPORTED, "too many query rows");
+  return OK;
+}
+
+int Allocator::init(const Config& cfg, const std::vector<int32_t>& fp, const std::vector<int32_t>& fs,
+                    std::string* why) {
+  cfg_ = cfg;
+  init_patch_.clear();
+  init_special_.clear();
+  if (fp.empty()) {
+    for (int32_t i = 0; i < cfg.max_patch_pages; ++i) init_patch_.push_back(i);
+  } else {
+    if ((int32_t)fp.size() != cfg.max_patch_pages) {
+      if (why) *why = "free_patch_order must list max_patch_pages IDs";
+      return ERR_ARG;
+    }
+    std::vector<char> seen(cfg.max_patch_pages, 0);
+    for (int32_t p : fp) {
+      if (p < 0 || p >= cfg.max_patch_pages || seen[p]) {
+        if (why) *why = "free_patch_order is not a permutation of [0, max_patch_pages)";
+        return ERR_ARG;
+      }
+      seen[p] = 1;
+    }
+    init_patch_ = fp;
+  }
+  if (fs.empty()) {
+    for (int32_t i = 0; i < cfg.max_special_pages; ++i) init_special_.push_back(cfg.max_patch_pages + i);
+  } else {
+    if ((int32_t)fs.size() != cfg.max_special_pages) {
+      if (why) *why = "free_special_order must list max_special_pages IDs";
+      return ERR_ARG;
+    }
+    std::vector<char> seen(cfg.max_special_pages, 0);
+    for (int32_t p : fs) {
+      const int32_t i = p - cfg.max_patch_pages;
+      if (i < 0 || i >= cfg.max_special_pages || seen[i]) {
+        if (why) *why = "free_special_order is not a permutation of [max_patch_pages, max_num_pages)";
+        return ERR_ARG;
+      }
+      seen[i] = 1;
+    }
+    init_special_ = fs;
+  }
+  reset();
+  return OK;
+}
+
+void Allocator::reset() {
+  free_patch_.assign(init_patch_.begin(), init_patch_.end());
+  free_special_.assign(init_special_.begin(), init_special_.end());
+  streams_.assign(cfg_.num_streams, StreamState());
+}
+
+int Allocator::append(int s, FrameSlots* out, std::string* why) {
+  StreamState& st = streams_[s];
+  const int64_t pg = cfg_.page_size;
+  const int n_s = cfg_.num_special_tokens;
+  if (free_patch_.empty()) {
+    if (why) *why = "no free patch page (evict, or raise max_patch_pages)";
+    return ERR_POOL;
+  }
+  // special pages this frame opens: one per token landing at slot 0 of a page
+  int64_t need = 0;
+  for (int j = 0; j < n_s; ++j)
+    if ((st.special_tokens + j) % pg == 0) ++need;
+  if (need > (int64_t)free_special_.size()) {
+    if (why) *why = "special page pool exhausted";
+    return ERR_POOL;
+  }
+  FrameSlots fs;
+  fs.patch_page = free_patch_.front();
+  free_patch_.pop_front();
+  if ((int32_t)st.scale_pages.size() < cfg_.scale_frames)
+    st.scale_pages.push_back(fs.patch_page);
+  else
+    st.live_pages.push_back(fs.patch_page);
+  if (n_s > 0) {
+    fs.sp_slot0 = (int32_t)(st.special_tokens % pg);
+    if (fs.sp_slot0 != 0) fs.sp_pages[fs.n_sp_pages++] = st.special_pages.back();
+    for (int j = 0; j < n_s; ++j) {
+      if (st.special_tokens % pg == 0) {
+        st.special_pages.push_back(free_special_.front());
+        free_special_.pop_front();
+        fs.sp_pages[fs.n_sp_pages++] = st.special_pages.back();
+      }
+      st.special_tokens += 1;
+    }
+  }
+  st.frame_count += 1;
+  if (out) *out = fs;
+  return OK;
+}
+
+int Allocator::evict(int s) {
+  StreamState& st = streams_[s];
+  int n = 0;
+  while ((int32_t)st.live_pages.size() > cfg_.sliding_window) {
+    free_patch_.push_back(st.live_pages.front());
+    st.live_pages.pop_front();
+    ++n;
+  }
+  return n;
+}
+
+int32_t Allocator::last_page_len(int s) const {
+  const StreamState& st = streams_[s];
+  if (!st.special_pages.empty())
+    return (int32_t)(st.special_tokens - (int64_t)cfg_.page_size * ((int64_t)st.special_pages.size() - 1));
+  return cfg_.patch_tokens();
+}
+
+size_t plan_image_ints(const Config& c) {
+  return KVC_PLAN_HEADER_INTS + (size_t)KVC_STREAM_REC_INTS * c.num_streams + (size_t)c.max_num_pages();
+}
+
+void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const PlanPolicy& pol, HostPlan* out) {
+  const Config& c = a.config();
+  HostPlan& p = *out;
+  const int n = (int)streams.size();
+  p.planned = streams;
+  p.kv_indptr.assign(1, 0);
+  p.kv_indices.clear();
+  p.last_page_len.clear();
+  p.n_patch_pages.clear();
+  p.qo_indptr.assign(1, 0);
+  p.n_split.clear();
+
+  const int32_t P = c.patch_tokens();
+  std::vector<int64_t> kv_len(n);
+  for (int i = 0; i < n; ++i) {
+    const StreamState& st = a.stream(streams[i]);
+    // [p2] "How LingBot-Map Uses FlashInfer KV Cache for Streaming 3D
+    // Reconstruction" §Page Table Planning and Reuse: scale -> window -> specials
+    p.kv_indices.insert(p.kv_indices.end(), st.scale_pages.begin(), st.scale_pages.end());
+    p.kv_indices.insert(p.kv_indices.end(), st.live_pages.begin(), st.live_pages.end());
+    p.kv_indices.insert(p.kv_indices.end(), st.special_pages.begin(), st.special_pages.end());
+    p.kv_indptr.push_back((int32_t)p.kv_indices.size());
+    const int32_t n_patch = (int32_t)(st.scale_pages.size() + st.live_pages.size());
+    p.n_patch_pages.push_back(n_patch);
+    p.last_page_len.push_back(a.last_page_len(streams[i]));
+    p.qo_indptr.push_back(p.qo_indptr.back() + c.tokens_per_frame);
+    kv_len[i] = (int64_t)n_patch * P + st.special_tokens;
+  }
+
+  // Work decomposition: each work item is (stream, head, KV split, query
+  // group).  Query groups hold at most KVC_ATTN_WAVES * tiles_per_wave tiles;
+  // KV splits share the target work-group count in proportion to each
+  // stream's visible length, in whole KVC_KV_TILE units.
+  const int32_t nqt = (int32_t)ceil_div(c.tokens_per_frame, KVC_Q_TILE);
+  const int32_t per_group = KVC_ATTN_WAVES * kvc_tiles_per_wave(c.head_dim);
+  const int32_t n_group = (int32_t)ceil_div(nqt, per_group);
+  int64_t total_len = 0;
+  for (int i = 0; i < n; ++i) total_len += kv_len[i];
+  const int32_t max_splits = std::max(1, std::min<int32_t>(pol.max_splits, KVC_MAX_SPLITS));
+
+  p.image.assign(KVC_PLAN_HEADER_INTS + (size_t)KVC_STREAM_REC_INTS * n + p.kv_indices.size(), 0);
+  int32_t item = 0;
+  p.any_split = false;
+  for (int i = 0; i < n; ++i) {
+    const int64_t units = std::max<int64_t>(1, ceil_div(kv_len[i], KVC_KV_TILE));
+    double want = total_len > 0 ? (double)pol.target_workgroups * (double)kv_len[i] / (double)total_len /
+                                      ((double)c.num_heads * n_group)
+                                : 1.0;
+    int64_t ns = (int64_t)std::llround(want);
+    ns = std::max<int64_t>(1, std::min<int64_t>(ns, std::min<int64_t>(max_splits, units)));
+    p.n_split.push_back((int32_t)ns);
+    if (ns > 1) p.any_split = true;
+
+    kvc_dev_stream rec;
+    std::memset(&rec, 0, sizeof(rec));
+    rec.q_row0 = p.qo_indptr[i];
+    rec.n_q = c.tokens_per_frame;
+    rec.page0 = p.kv_indptr[i];
+    rec.n_patch = p.n_patch_pages[i];
+    rec.n_pages = p.kv_indptr[i + 1] - p.kv_indptr[i];
+    rec.last_len = p.last_page_len[i];
+    rec.kv_len = (int32_t)kv_len[i];
+    rec.patch_tok = rec.n_patch * P;
+    rec.n_units = (int32_t)units;
+    rec.n_split = (int32_t)ns;
+    rec.n_group = n_group;
+    rec.item0 = item;
+    rec.n_items = c.num_heads * (int32_t)ns * n_group;
+    item += rec.n_items;
+    std::memcpy(&p.image[KVC_PLAN_HEADER_INTS + (size_t)KVC_STREAM_REC_INTS * i], &rec, sizeof(rec));
+  }
+  p.num_items = item;
+  p.num_rows = p.qo_indptr.back();
+  p.image[KVC_HDR_NUM_STREAMS] = n;
+  p.image[KVC_HDR_NUM_ITEMS] = item;
+  p.image[KVC_HDR_NUM_ROWS] = p.num_rows;
+  p.image[KVC_HDR_ANY_SPLIT] = p.any_split ? 1 : 0;
+  std::copy(p.kv_indices.begin(), p.kv_indices.end(),
+            p.image.begin() + KVC_PLAN_HEADER_INTS + (size_t)KVC_STREAM_REC_INTS * n);
+}
+
+}  // namespace kvc

@@ -1,0 +1,113 @@
+// Host page allocator and per-step planner of the two-stream paged KV cache.
+// Plain C++17: no HIP headers, so it builds and is tested with the host
+// compiler alone.
+//
+// Page bookkeeping follows [p1] "How FlashInfer KV Cache Attention Accelerates
+// Streaming 3D Reconstruction Over SDPA" §Two-Stream Design for Token Types
+// (deques of free / scale / live-window patch pages; append-only special
+// pages) and [p3] "How FlashInfer's Paged KV Cache Attention Outperforms SDPA
+// Fallback in Streaming Inference" §Two-Stream Design (one patch page per
+// frame; specials pack continuously across pages).
+#ifndef KVC_HOST_HPP
+#define KVC_HOST_HPP
+
+#include <cstdint>
+#include <deque>
+#include <string>
+#include <vector>
+
+#include "kvc_plan_layout.h"
+
+namespace kvc {
+
+struct Config {
+  int32_t num_blocks = 0, num_heads = 0, head_dim = 0, tokens_per_frame = 0;
+  int32_t num_special_tokens = 0, special_row_offset = 0, page_size = 0;
+  int32_t scale_frames = 0, sliding_window = 0, num_streams = 0;
+  int32_t max_patch_pages = 0, max_special_pages = 0;
+
+  int32_t patch_tokens() const { return tokens_per_frame - num_special_tokens; }
+  int32_t max_num_pages() const { return max_patch_pages + max_special_pages; }
+  int32_t rows_capacity() const { return num_streams * tokens_per_frame; }
+};
+
+// Result codes mirror kvc_status.
+enum Code { OK = 0, ERR_ARG = -1, ERR_STATE = -2, ERR_POOL = -3, ERR_CAPACITY = -4, ERR_UNSUPPORTED = -6 };
+
+// Validates a configuration; returns OK or an error code with a message.
+int validate(const Config& c, std::string* why);
+
+// Where one frame's tokens go.  Special token j of the frame is at page
+// sp_pages[(sp_slot0 + j) / page_size], slot (sp_slot0 + j) % page_size.
+struct FrameSlots {
+  int32_t patch_page = -1;
+  int32_t sp_slot0 = 0;
+  int32_t n_sp_pages = 0;
+  int32_t sp_pages[KVC_MAX_APPEND_SPECIAL_PAGES] = {0};
+};
+
+struct StreamState {
+  std::vector<int32_t> scale_pages;    // permanent, in frame order
+  std::deque<int32_t> live_pages;      // sliding window, oldest first
+  std::vector<int32_t> special_pages;  // append-only
+  int64_t special_tokens = 0;
+  int64_t frame_count = 0;
+};
+
+class Allocator {
+ public:
+  // free_patch_order / free_special_order may be empty (ascending IDs).
+  int init(const Config& cfg, const std::vector<int32_t>& free_patch_order,
+           const std::vector<int32_t>& free_special_order, std::string* why);
+  void reset();
+  // Allocate one frame of `stream`; state is unchanged on error.
+  int append(int stream, FrameSlots* out, std::string* why);
+  // Free live-window pages beyond the window; returns the number freed.
+  int evict(int stream);
+
+  const Config& config() const { return cfg_; }
+  const StreamState& stream(int s) const { return streams_[s]; }
+  int32_t free_patch_count() const { return (int32_t)free_patch_.size(); }
+  int32_t free_special_count() const { return (int32_t)free_special_.size(); }
+  // Valid tokens on the last page of the stream's visible table ([p5] "How
+  // Paged KV Cache Attention Achieves Stable Inference in Ling-Bot-Map"
+  // §Kernel Dispatch and Sequence Lengths).
+  int32_t last_page_len(int stream) const;
+
+ private:
+  Config cfg_;
+  std::vector<int32_t> init_patch_, init_special_;
+  std::deque<int32_t> free_patch_, free_special_;
+  std::vector<StreamState> streams_;
+};
+
+// Split / group policy of the attention launch.
+struct PlanPolicy {
+  int32_t target_workgroups = 512;
+  int32_t max_splits = KVC_MAX_SPLITS;
+};
+
+// Host image of one step's plan.
+struct HostPlan {
+  std::vector<int32_t> planned;        // stream ids, ascending
+  std::vector<int32_t> kv_indptr;      // size n+1
+  std::vector<int32_t> kv_indices;
+  std::vector<int32_t> last_page_len;
+  std::vector<int32_t> n_patch_pages;
+  std::vector<int32_t> qo_indptr;      // size n+1
+  std::vector<int32_t> n_split;
+  std::vector<int32_t> image;          // device layout (kvc_plan_layout.h)
+  int32_t num_items = 0;
+  int32_t num_rows = 0;
+  bool any_split = false;
+};
+
+// Plan the given streams (ascending) from the allocator's current lists.
+void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const PlanPolicy& pol, HostPlan* out);
+
+// int32 entries of the device plan image for a configuration (upper bound).
+size_t plan_image_ints(const Config& c);
+
+}  // namespace kvc
+
+#endif

@@ -1,0 +1,57 @@
+// Launch interface of the HIP kernels (plain types; no HIP headers needed).
+#ifndef KVC_KERNELS_H
+#define KVC_KERNELS_H
+
+#include <stdint.h>
+
+#include "kvc_plan_layout.h"
+
+namespace kvc {
+
+// Exact unsigned division n / d for 0 <= n < 2^31 by a multiply-high:
+// q = (umulhi(n, mul) + n) >> shr, with shr = ceil(log2 d) and
+// mul = ceil(2^(32+shr) / d) - 2^32.
+struct FastDiv {
+  uint32_t div, mul, shr;
+};
+FastDiv make_fastdiv(uint32_t d);
+
+struct AppendParams {
+  void* pool;               // this block's pool
+  const void* k;            // [T, H, D] bf16
+  const void* v;
+  int32_t T, row_elems;     // row_elems = H * D
+  int32_t special_row_offset, n_special, page_size;
+  int32_t patch_page, sp_slot0, n_sp_pages;
+  int32_t sp_pages[KVC_MAX_APPEND_SPECIAL_PAGES];
+};
+
+struct AttnParams {
+  const int32_t* plan;      // device plan image
+  const void* pool;
+  const void* q;            // [R, H, D] bf16
+  void* o;                  // [R, H, D] bf16
+  float* part_o;            // [KVC_MAX_SPLITS][rows_cap][H][D]
+  float* part_lse;          // [KVC_MAX_SPLITS][rows_cap][H]
+  int32_t num_heads, head_dim, page_size, patch_tokens, rows_cap;
+  FastDiv div_patch, div_page;
+  float scale_log2;         // log2(e) / sqrt(D)
+  int32_t num_items, items_per_xcd;
+};
+
+struct MergeParams {
+  const int32_t* plan;
+  const float* part_o;
+  const float* part_lse;
+  void* o;
+  int32_t num_heads, head_dim, rows_cap, num_rows;
+};
+
+// Return 0 on success or the hipError_t value.
+int launch_append(const AppendParams& p, void* hip_stream);
+int launch_attention(const AttnParams& p, int32_t grid, void* hip_stream);
+int launch_merge(const MergeParams& p, void* hip_stream);
+
+}  // namespace kvc
+
+#endif

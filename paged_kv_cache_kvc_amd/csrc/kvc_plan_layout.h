@@ -1,0 +1,63 @@
+// Device-side plan layout: what kvc_plan uploads once per frame step and every
+// kvc_run of that step reads ([p3] "How FlashInfer's Paged KV Cache Attention
+// Outperforms SDPA Fallback in Streaming Inference", §Plan-Run Execution
+// Workflow: plan once at block 0, reuse in every block).
+//
+// Plain C layout, included by the host planner and by the HIP kernels.
+//
+// Buffer of int32:
+//   [0, KVC_PLAN_HEADER_INTS)                      header
+//   [.., + KVC_STREAM_REC_INTS * num_streams)      one record per planned stream
+//   [.., + total visible pages)                    kv_indices: concatenated page
+//                                                  tables, scale -> live -> special
+#ifndef KVC_PLAN_LAYOUT_H
+#define KVC_PLAN_LAYOUT_H
+
+#include <stdint.h>
+
+#define KVC_PLAN_HEADER_INTS 8
+#define KVC_STREAM_REC_INTS 16
+
+// KV tokens per attention pipeline stage; split boundaries are multiples of it.
+#define KVC_KV_TILE 64
+// Query rows per MFMA tile, and waves per attention work-group.
+#define KVC_Q_TILE 16
+#define KVC_ATTN_WAVES 4
+// Upper bound of KV splits per stream (sizes the partial-output workspace).
+#define KVC_MAX_SPLITS 64
+// Largest n_s, and the most special pages one frame's specials can touch.
+#define KVC_MAX_SPECIAL_PER_FRAME 64
+#define KVC_MAX_APPEND_SPECIAL_PAGES 8
+
+// Header fields.
+#define KVC_HDR_NUM_STREAMS 0
+#define KVC_HDR_NUM_ITEMS 1
+#define KVC_HDR_NUM_ROWS 2
+#define KVC_HDR_ANY_SPLIT 3
+
+typedef struct kvc_dev_stream {
+  int32_t q_row0;     // first query/output row of this stream
+  int32_t n_q;        // query rows (T)
+  int32_t page0;      // offset of this stream's table in kv_indices
+  int32_t n_patch;    // patch pages in the table (scale + live)
+  int32_t n_pages;    // pages in the table
+  int32_t last_len;   // valid tokens on the last page
+  int32_t kv_len;     // valid visible tokens L
+  int32_t patch_tok;  // n_patch * P: first token of the special region
+  int32_t n_units;    // ceil(L / KVC_KV_TILE)
+  int32_t n_split;    // KV splits
+  int32_t n_group;    // query groups
+  int32_t item0;      // first attention work item of this stream
+  int32_t n_items;    // H * n_split * n_group
+  int32_t split_base; // index of this stream's first split slot (always 0: partials are per row)
+  int32_t reserved0;
+  int32_t reserved1;
+} kvc_dev_stream;
+
+// Max query tiles (of KVC_Q_TILE rows) one wave holds, per head_dim; a query
+// group spans at most KVC_ATTN_WAVES * this many tiles.
+static inline int kvc_tiles_per_wave(int head_dim) {
+  return head_dim <= 64 ? 5 : 3;
+}
+
+#endif

@@ -1,0 +1,165 @@
+"""Drives the HIP library and the CPU oracle through the same synthetic frame
+stream (test helper; used by the GPU parity tests, the smoke check and the
+bench's parity spot check)."""
+from __future__ import annotations
+
+import time
+from typing import Callable, Dict, List, Optional, Sequence
+
+import numpy as np
+
+import kvc_synth as syn
+from oracle import kvc_oracle as ko
+
+
+def cfg_args(wl: syn.Workload, num_blocks: int):
+    return dict(num_blocks=num_blocks, num_heads=wl.num_heads, head_dim=wl.head_dim,
+                tokens_per_frame=wl.tokens_per_frame, num_special_tokens=wl.num_special_tokens,
+                page_size=wl.page_size, scale_frames=wl.scale_frames, sliding_window=wl.sliding_window,
+                num_streams=wl.num_streams, max_patch_pages=wl.max_patch_pages,
+                max_special_pages=wl.max_special_pages, special_row_offset=wl.row_offset)
+
+
+def oracle_cfg(wl: syn.Workload) -> ko.OracleConfig:
+    return ko.OracleConfig(num_heads=wl.num_heads, head_dim=wl.head_dim, tokens_per_frame=wl.tokens_per_frame,
+                           num_special_tokens=wl.num_special_tokens, page_size=wl.page_size,
+                           scale_frames=wl.scale_frames, sliding_window=wl.sliding_window,
+                           max_patch_pages=wl.max_patch_pages, max_special_pages=wl.max_special_pages,
+                           num_streams=wl.num_streams, special_row_offset=wl.special_row_offset)
+
+
+def free_orders(wl: syn.Workload, seed: Optional[int] = None):
+    if seed is None:
+        if not wl.shuffle_free_lists:
+            return None, None
+        seed = wl.seed
+    return (syn.free_list_order(seed, wl.max_patch_pages, 0, 0),
+            syn.free_list_order(seed, wl.max_special_pages, wl.max_patch_pages, 1))
+
+
+def final_visible(wl: syn.Workload, stream: int, extra_steps: Sequence[int] = ()) -> set:
+    """Frames of a stream whose patch rows are visible at its last step or at
+    any of the given (stream-local) steps."""
+    F = wl.frames[stream]
+    out = set()
+    for t in [F - 1, *extra_steps]:
+        out.update(ko.visible_frames(t, wl.scale_frames, wl.sliding_window))
+    return out
+
+
+def bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    return syn.bf16_bits_to_f32(bits)
+
+
+def check_close(out_bits: np.ndarray, ref: np.ndarray, atol=1e-2, rtol=1e-2) -> Dict[str, float]:
+    """The acceptance test: |o - o_ref| <= atol + rtol * |o_ref| elementwise;
+    returns error statistics."""
+    o = bits_to_f32(out_bits).astype(np.float64)
+    err = np.abs(o - ref)
+    bound = atol + rtol * np.abs(ref)
+    bad = err > bound
+    stats = {"max_abs": float(err.max()), "max_over_std": float(err.max() / max(ref.std(), 1e-30)),
+             "frac_over_half_tol": float((err > 0.5 * bound).mean()), "n_bad": int(bad.sum())}
+    assert not bad.any(), f"{bad.sum()} elements out of tolerance; {stats}"
+    return stats
+
+
+class Harness:
+    """The GPU cache and the oracle side by side.
+
+    blocks: how many block pools to exercise (block b draws its inputs with
+    block index b).  real_patch(stream, frame) says whether a frame's patch
+    rows are drawn (else zero; only for frames never visible at a checked
+    step)."""
+
+    def __init__(self, wl: syn.Workload, num_blocks: int = 1, q_scale: float = 1.0,
+                 real_patch: Optional[Callable[[int, int], bool]] = None, orders=None,
+                 options: Optional[Dict[int, int]] = None, device="cuda", oracle_blocks: Sequence[int] = (0,)):
+        import torch
+        import paged_kv_cache_kvc_amd as kvc
+        self.torch = torch
+        self.kvc = kvc
+        self.wl = wl
+        self.nb = num_blocks
+        self.q_scale = q_scale
+        self.real_patch = real_patch or (lambda s, f: True)
+        po, so = orders if orders is not None else free_orders(wl)
+        self.gpu = kvc.PagedKVCache(kvc.make_config(**cfg_args(wl, num_blocks)), device=device,
+                                    free_patch_order=po, free_special_order=so)
+        for k, v in (options or {}).items():
+            self.gpu.set_option(k, v)
+        self.ocfg = oracle_cfg(wl)
+        self.ora = ko.OracleStream(self.ocfg, blocks=tuple(oracle_blocks), free_patch_order=po,
+                                   free_special_order=so)
+        self.global_step = 0
+        self.frame_of = [0] * wl.num_streams
+        T, H, D = wl.tokens_per_frame, wl.num_heads, wl.head_dim
+        self.kbuf = torch.empty((T, H, D), dtype=torch.bfloat16, device=device)
+        self.vbuf = torch.empty_like(self.kbuf)
+        self.device = device
+
+    def _frame(self, s, f, b, which):
+        wl = self.wl
+        return syn.frame_tensor(wl.seed, s, f, b, which, wl.tokens_per_frame, wl.num_heads, wl.head_dim,
+                                wl.num_special_tokens, wl.row_offset,
+                                scale=self.q_scale if which == "q" else 1.0,
+                                patch_real=self.real_patch(s, f) or which == "q")
+
+    def to_dev(self, bits: np.ndarray, out=None):
+        t = self.torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(self.torch.bfloat16)
+        if out is None:
+            return t.to(self.device)
+        out.copy_(t)
+        return out
+
+    def active(self) -> List[int]:
+        return [s for s in range(self.wl.num_streams) if self.global_step >= syn.stream_join_step(self.wl, s)]
+
+    def step(self, run: bool = True, check: bool = False, blocks_to_run: Optional[Sequence[int]] = None):
+        """One frame step for every active stream.  Returns a dict with the
+        GPU outputs (bits per block) and, when check, the oracle outputs and
+        plans."""
+        act = self.active()
+        frames = {s: self.frame_of[s] for s in act}
+        kv_cache = {}
+
+        def frame_kv(s, f, b):
+            key = (s, b)
+            if key not in kv_cache:
+                kv_cache[key] = (self._frame(s, f, b, "k"), self._frame(s, f, b, "v"))
+            return kv_cache[key]
+
+        res = {"active": act, "frames": frames}
+        run_blocks = list(range(self.nb)) if blocks_to_run is None else list(blocks_to_run)
+        outs = {}
+        for b in range(self.nb):
+            for s in act:
+                k, v = frame_kv(s, frames[s], b)
+                self.to_dev(k, self.kbuf)
+                self.to_dev(v, self.vbuf)
+                self.gpu.append_frame(b, self.kbuf, self.vbuf, stream_id=s)
+            if b == 0:
+                for s in act:
+                    self.gpu.evict_frames(s)
+                if run:
+                    self.gpu.plan()
+            if run and b in run_blocks:
+                q = np.concatenate([self._frame(s, frames[s], b, "q") for s in act])
+                qd = self.to_dev(q)
+                out = self.gpu.compute_attention(b, qd)
+                outs[b] = (q, out)
+        # oracle replay (allocator always; pools only for its blocks)
+        ora_plan = self.ora.step(act, frame_kv)
+        res["ora_plan"] = ora_plan
+        if run:
+            res["gpu_plan"] = self.gpu.get_plan()
+        res["out_bits"] = {b: out.view(self.torch.int16).cpu().numpy().view(np.uint16) for b, (q, out) in outs.items()}
+        if check:
+            res["ref"] = {b: self.ora.attend(ora_plan, b, q) for b, (q, out) in outs.items() if b in self.ora.pools}
+        for s in act:
+            self.frame_of[s] += 1
+        self.global_step += 1
+        return res
+
+    def pool_bits(self, block: int) -> np.ndarray:
+        return self.gpu.pools[block].view(self.torch.int16).cpu().numpy().view(np.uint16)
