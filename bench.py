@@ -197,10 +197,10 @@ def main():
             cache.raw_append(0, kp, vp, s, hs)
         for s in act:
             cache.evict_frames(s)
+        cache.raw_plan(hs)          # a plan closes every step, timed or not
         if run:
             if len(act) != ns:
                 raise RuntimeError("timed steps must advance every stream")
-            cache.raw_plan(hs)
             qf = qcat[frame_of[0] % BANK]
             cache.raw_run(0, qf[0].data_ptr(), ob.data_ptr(), hs)
         for b in range(1, nb):

@@ -51,10 +51,10 @@
  *   4. kvc_run(block 0, ...);
  *   5. for every block b >= 1: kvc_append_frame(s, b, ...) for every planned
  *      stream, then kvc_run(b, ...).
- * Out-of-order calls return KVC_ERR_STATE.  The first kvc_append_frame(s, 0)
- * after a plan, or a second one for the same stream before any plan, starts
- * the next step (a step need not be planned: streaming ahead without
- * attention is append + evict only).
+ * Out-of-order calls return KVC_ERR_STATE.  kvc_plan ends a step: the first
+ * kvc_append_frame(s, 0) after it starts the next one.  A step that runs no
+ * attention (streaming ahead) is still closed by kvc_plan, which then only
+ * costs the host build and one small copy.
  */
 #ifndef KVC_H
 #define KVC_H
@@ -187,8 +187,8 @@ kvc_status kvc_reset(kvc_ctx* ctx);
  * slots.  One kernel launch writes the patch rows to slots [0, P) of the page
  * and each special row to its slot; pad slots are never written.
  * Errors: KVC_ERR_ARG, KVC_ERR_STATE (block >= 1 before block 0 of the step,
- * or a block >= 1 appended twice in one step), KVC_ERR_POOL_EXHAUSTED (block
- * 0 only; nothing changes), KVC_ERR_HIP. */
+ * or a block appended twice in one step), KVC_ERR_POOL_EXHAUSTED (block 0
+ * only; nothing changes), KVC_ERR_HIP. */
 kvc_status kvc_append_frame(kvc_ctx* ctx, int32_t stream, int32_t block, const void* k, const void* v,
                             kvc_stream_t hip_stream);
 

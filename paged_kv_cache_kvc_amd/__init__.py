@@ -157,6 +157,8 @@ class PagedKVCache:
         import torch
         self.torch = torch
         self.device = torch.device(device)
+        if self.device.type == "cuda" and self.device.index is None:
+            self.device = torch.device("cuda", torch.cuda.current_device())
         pool_bytes = self.lib.kvc_pool_bytes(ctypes.byref(config))
         ws_bytes = self.lib.kvc_workspace_bytes(ctypes.byref(config))
         st_bytes = self.lib.kvc_staging_bytes(ctypes.byref(config))

@@ -284,9 +284,10 @@ kvc_status kvc_append_frame(kvc_ctx* c, int32_t stream, int32_t block, const voi
   }
   const size_t bd = (size_t)stream * cf.num_blocks + block;
   if (block == 0) {
-    // A plan, or a second block-0 append of the same stream, ends the step
-    // (an unplanned step simply runs no attention, as when fast-forwarding).
-    const bool new_step = c->planned || c->advanced[stream];
+    // kvc_plan ends a step; the first block-0 append after it starts the next.
+    const bool new_step = c->planned;
+    if (!new_step && c->advanced[stream])
+      return fail(c, KVC_ERR_STATE, "stream already appended block 0 this step (kvc_plan ends a step)");
     kvc::FrameSlots fs;
     std::string why;
     const int rc = c->alloc.append(stream, &fs, &why);

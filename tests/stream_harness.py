@@ -141,8 +141,7 @@ class Harness:
             if b == 0:
                 for s in act:
                     self.gpu.evict_frames(s)
-                if run:
-                    self.gpu.plan()
+                self.gpu.plan()           # a plan closes every step, run or not
             if run and b in run_blocks:
                 q = np.concatenate([self._frame(s, frames[s], b, "q") for s in act])
                 qd = self.to_dev(q)
@@ -151,8 +150,7 @@ class Harness:
         # oracle replay (allocator always; pools only for its blocks)
         ora_plan = self.ora.step(act, frame_kv)
         res["ora_plan"] = ora_plan
-        if run:
-            res["gpu_plan"] = self.gpu.get_plan()
+        res["gpu_plan"] = self.gpu.get_plan()
         res["out_bits"] = {b: out.view(self.torch.int16).cpu().numpy().view(np.uint16) for b, (q, out) in outs.items()}
         if check:
             res["ref"] = {b: self.ora.attend(ora_plan, b, q) for b, (q, out) in outs.items() if b in self.ora.pools}

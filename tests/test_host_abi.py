@@ -96,6 +96,7 @@ def test_worked_example_through_abi():
     for _ in range(42):
         cache.append_frame(0)
         cache.evict_frames()
+        cache.plan()
     st = cache.get_cache_stats()
     assert {k: st[k] for k in ("frame_count", "scale_pages", "live_pages", "free_pages", "special_tokens")} == \
         {"frame_count": 42, "scale_pages": 8, "live_pages": 34, "free_pages": 46, "special_tokens": 252}
@@ -118,10 +119,11 @@ def test_call_order_is_enforced():
         c.append_frame(1)                          # block 1 before block 0
     assert e.value.status == kvc.KVC_ERR_STATE
     c.append_frame(0)
-    c.append_frame(0)                              # unplanned step: the second block-0 append starts the next
-    assert c.get_cache_stats()["frame_count"] == 2
     with pytest.raises(kvc.KvcError) as e:
-        c.append_frame(2)
+        c.append_frame(0)                          # block 0 twice in one step
+    assert e.value.status == kvc.KVC_ERR_STATE
+    c.append_frame(2)
+    with pytest.raises(kvc.KvcError) as e:
         c.append_frame(2)                          # block appended twice in one step
     assert e.value.status == kvc.KVC_ERR_STATE
     c.evict_frames()
@@ -138,7 +140,7 @@ def test_call_order_is_enforced():
     assert lib.kvc_run(c._ctx, 0, 16, 32, None) == kvc.KVC_ERR_STATE
     # next step starts with block 0
     c.append_frame(0)
-    assert c.get_cache_stats()["frame_count"] == 3
+    assert c.get_cache_stats()["frame_count"] == 2
 
 
 def test_bad_arguments_and_capacity():
@@ -176,6 +178,7 @@ def test_special_pool_exhaustion_at_predicted_frame_leaves_state():
     for _ in range(8):
         c.append_frame(0)
         c.evict_frames()
+        c.plan()
     before = c.get_cache_stats()
     with pytest.raises(kvc.KvcError) as e:
         c.append_frame(0)
