@@ -126,6 +126,8 @@ def main():
     ap.add_argument("--target-wgs", type=int, default=None)
     ap.add_argument("--max-splits", type=int, default=None)
     ap.add_argument("--no-profile", action="store_true", help="time without per-launch HIP events")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB five times (HBM counter calibration)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -143,6 +145,15 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "launches": 5}), flush=True)
+        return
     wl = syn.WORKLOADS[args.workload]
     F = max(wl.frames)
     K, W = args.steps, args.warmup

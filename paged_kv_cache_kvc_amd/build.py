@@ -25,6 +25,8 @@ HIP_FLAGS = [
     # packed fp32 VALU forms stay disabled: plain fp32 code is used instead
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
+    # MFMA accumulators in VGPRs: avoids AGPR<->VGPR copies around every MFMA
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 CXX_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-Wall", "-Wextra", "-Wno-unused-parameter",
              "-D__HIP_PLATFORM_AMD__", f"-I{ROCM}/include"]

@@ -34,6 +34,15 @@ int validate(const Config& c, std::string* why) {
   if (pages * c.page_size >= (int64_t)1 << 31) return fail(ERR_UNSUPPORTED, "pool slots per block must be < 2^31");
   if ((int64_t)c.num_heads * c.head_dim > 65536) return fail(ERR_UNSUPPORTED, "num_heads * head_dim above 65536");
   if ((int64_t)c.num_streams * c.tokens_per_frame >= (int64_t)1 << 24) return fail(ERR_UNSUPPORTED, "too many query rows");
+  {
+    // longest possible visible stream must fit KVC_MAX_SPLITS splits of at
+    // most KVC_MAX_SPLIT_PAGES pages each
+    const int64_t min_valid = std::max<int32_t>(1, std::min(c.patch_tokens(), c.page_size));
+    const int64_t per_split = (int64_t)(KVC_MAX_SPLIT_PAGES - 2) * min_valid / KVC_KV_TILE;
+    const int64_t max_tokens = (int64_t)c.max_patch_pages * c.patch_tokens() + (int64_t)c.max_special_pages * c.page_size;
+    if (per_split < 1 || ceil_div(ceil_div(max_tokens, KVC_KV_TILE), per_split) > KVC_MAX_SPLITS)
+      return fail(ERR_UNSUPPORTED, "pages too small for the stream length (split page limit)");
+  }
   return OK;
 }
 
@@ -199,6 +208,11 @@ void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const P
                                 : 1.0;
     int64_t ns = (int64_t)std::llround(want);
     ns = std::max<int64_t>(1, std::min<int64_t>(ns, std::min<int64_t>(max_splits, units)));
+    // a split's page IDs are staged in LDS: it may span at most
+    // KVC_MAX_SPLIT_PAGES pages (each holds >= min(P, page_size) tokens)
+    const int64_t min_valid = std::max<int32_t>(1, std::min(P, c.page_size));
+    const int64_t per_split = (int64_t)(KVC_MAX_SPLIT_PAGES - 2) * min_valid / KVC_KV_TILE;
+    ns = std::max<int64_t>(ns, ceil_div(units, std::max<int64_t>(1, per_split)));
     p.n_split.push_back((int32_t)ns);
     if (ns > 1) p.any_split = true;
 

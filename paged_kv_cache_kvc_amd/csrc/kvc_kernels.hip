@@ -98,29 +98,90 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
 template <int D>
 struct Shape {
   static constexpr int CPR = D / 8;                      // 16-byte chunks per K/V row
+  static constexpr int ROW_BYTES = D * 2;
   static constexpr int KSTEPS = D / 32;                  // k-steps of S^T = K Q^T
   static constexpr int DBLK = D / 16;                    // 16-row blocks of O^T
-  static constexpr int K_BYTES = KT * D * 2;             // K stage, row-major [kv][d]
-  static constexpr int V_BYTES = D * KT * 2;             // V stage, transposed [d][kv]
-  static constexpr int STAGE_BYTES = K_BYTES + V_BYTES;
-  // Loads: threads [0,128) bring K rows, [128,256) bring V as 4-token x
-  // 8-dim blocks that they transpose in registers.
-  static constexpr int K_PER_THREAD = KT * CPR / 128;
-  static constexpr int K_ROWS_PER_PASS = 128 / CPR;
-  static constexpr int V_BLOCKS = (KT / 4) * CPR;
-  static constexpr int V_PER_THREAD = (V_BLOCKS + 127) / 128;
-  static constexpr int STG = (K_PER_THREAD > 4 * V_PER_THREAD) ? K_PER_THREAD : 4 * V_PER_THREAD;
+  static constexpr int HALF_BYTES = KT * ROW_BYTES;      // K (or V) part of a stage, [kv][d]
+  static constexpr int STAGE_BYTES = 2 * HALF_BYTES;
+  static constexpr int NSTAGE = 4;                       // LDS ring of stages
+  static constexpr int DIST = 2;                         // stages loaded ahead (<= NSTAGE - 2)
+  static constexpr int LOADS = STAGE_BYTES / 1024;       // 1 KiB direct-to-LDS loads per stage
+  static constexpr int LOADS_PER_WAVE = LOADS / KVC_ATTN_WAVES;
 };
 
-// LDS chunk swizzles (XOR on the 16-byte chunk index inside a row) that keep
-// the MFMA operand reads and the transposing V writes spread over banks.
-__device__ __forceinline__ int swz_k(int row) { return (row & 3) | ((row >> 1) & 4); }
-__device__ __forceinline__ int swz_v(int d) { return (d ^ (d >> 3)) & 7; }
+// 16-byte chunk swizzle inside a K/V row of LDS: keeps the MFMA operand reads
+// of 16 rows spread over the banks.
+__device__ __forceinline__ int swz(int row) { return ((row >> 1) & 1) | (((row >> 3) & 3) << 1); }
 
-template <int D>
-__device__ __forceinline__ const uint16_t* kv_row(const AttnParams& p, const kvc_dev_stream& st,
-                                                  const int32_t* kvidx, int tok, int kv, int h) {
-  int pi, slot;
+// The ring of stages is filled by direct global->LDS loads that the kernel
+// issues, waits for and publishes itself: the compiler would otherwise treat
+// every LDS read as depending on every load in flight and drain the ring at
+// each barrier.  Completion is tracked with vmcnt (vector memory operations
+// retire in issue order), then a barrier makes a stage visible to all waves.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// 16 bytes from `src` (per lane) to LDS byte address lds_base + 16 * lane.
+__device__ __forceinline__ void load_lds16(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_base) : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* generic) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)generic;
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ i16x4 ds_read_tr16(const uint8_t* lds_generic) {
+  const lds_i16x4* p = (const lds_i16x4*)(__attribute__((address_space(3))) const uint8_t*)lds_generic;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+}
+
+// Exchange with the lane 32 (or 16) apart: after the swap, each lane holds
+// its own value and its partner's in (a, b).  Issued directly because the
+// compiler builtin's second result is not usable.
+__device__ __forceinline__ void swap32(uint32_t& a, uint32_t& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void swap16(uint32_t& a, uint32_t& b) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+
+// max / sum over lanes l, l^16, l^32, l^48: the four lane groups that hold
+// one query column of an MFMA accumulator
+__device__ __forceinline__ float lane_swap_max(float x) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  swap32(a, b);
+  x = fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+  a = __builtin_bit_cast(uint32_t, x);
+  b = a;
+  swap16(a, b);
+  return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+}
+
+__device__ __forceinline__ float lane_swap_sum(float x) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  swap32(a, b);
+  x = __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+  a = __builtin_bit_cast(uint32_t, x);
+  b = a;
+  swap16(a, b);
+  return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+}
+
+// Page index and slot of visible token `tok` of a stream: patch pages hold P
+// tokens, special pages page_size ([p1] "How FlashInfer KV Cache Attention
+// Accelerates Streaming 3D Reconstruction Over SDPA" §Efficient Attention
+// Masking and Padding: lengths, not masks, delimit the valid tokens).
+__device__ __forceinline__ void token_page(const AttnParams& p, const kvc_dev_stream& st, int tok, int& pi,
+                                           int& slot) {
   if (tok < st.patch_tok) {
     pi = (int)fdiv((uint32_t)tok, p.div_patch);
     slot = tok - pi * p.patch_tokens;
@@ -130,15 +191,17 @@ __device__ __forceinline__ const uint16_t* kv_row(const AttnParams& p, const kvc
     pi = st.n_patch + pj;
     slot = t2 - pj * p.page_size;
   }
-  const int page = kvidx[pi];
-  return static_cast<const uint16_t*>(p.pool) +
-         ((((size_t)page * 2 + kv) * p.page_size + slot) * p.num_heads + h) * D;
 }
+
+// Rescale threshold of the running maximum, in log2 units of the scaled
+// scores: probabilities up to 2^8 are kept without renormalising.
+constexpr float RESCALE_LOG2 = 8.0f;
 
 template <int D, int QTW>
 __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
   using S = Shape<D>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * S::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[S::NSTAGE * S::STAGE_BYTES];
+  __shared__ int32_t s_pages[KVC_MAX_SPLIT_PAGES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -176,6 +239,12 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
   const float sl = p.scale_log2;
   const int H = p.num_heads;
 
+  // page IDs of this split's tokens, staged in LDS
+  int pi_first, pi_last, tmp;
+  token_page(p, st, tok0, pi_first, tmp);
+  token_page(p, st, tok1 - 1, pi_last, tmp);
+  for (int i = tid; i <= pi_last - pi_first; i += 256) s_pages[i] = kvidx[pi_first + i];
+
   // ---- this wave's query tiles: t_lo + wave + 4k ----
   int ntw = 0;
 #pragma unroll
@@ -183,105 +252,60 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
     if (t_lo + wave + KVC_ATTN_WAVES * k < t_hi) ntw = k + 1;
 
   bf16x8 qop[QTW][S::KSTEPS];
-  float m_run[QTW], l_run[QTW];
+  float mb_run[QTW], l_run[QTW];
   f32x4 oacc[QTW][S::DBLK];
 #pragma unroll
   for (int k = 0; k < QTW; ++k) {
     const int row = KVC_Q_TILE * (t_lo + wave + KVC_ATTN_WAVES * k) + r16;
     const bool ok = k < ntw && row < st.n_q;
-    const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + ((size_t)(st.q_row0 + row) * H + h) * D;
+    const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + ((size_t)(st.q_row0 + (ok ? row : 0)) * H + h) * D;
 #pragma unroll
     for (int ks = 0; ks < S::KSTEPS; ++ks) {
-      if (ok) {
-        qop[k][ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks + 8 * g4);
-      } else {
+      qop[k][ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks + 8 * g4);
+      if (!ok) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) qop[k][ks][j] = (__bf16)0.0f;
       }
     }
-    m_run[k] = -INFINITY;
+    mb_run[k] = -INFINITY;
     l_run[k] = 0.0f;
 #pragma unroll
     for (int db = 0; db < S::DBLK; ++db) oacc[k][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  __syncthreads();   // s_pages ready
 
-  // ---- global -> registers -> LDS staging ----
-  u32x4 stg[S::STG];
-  auto load_stage = [&](int sidx) {
+  // ---- direct global -> LDS loads of one stage (K rows, then V rows) ----
+  // Load instruction i of a stage fills 1 KiB of LDS, lane l writing bytes
+  // [16 l, 16 l + 16); the lane fetches the logical chunk that the swizzle
+  // places there.  Rows past the split end re-read its last token (finite
+  // data; their scores are masked to -inf).
+  const uint16_t* pool = static_cast<const uint16_t*>(p.pool);
+  auto issue = [&](int sidx) {
     const int base = tok0 + sidx * KT;
-    const int valid = min(KT, tok1 - base);
-    if (tid < 128) {
-      const int cc = tid % S::CPR;
-      const int rg = tid / S::CPR;
+    uint8_t* stage = ring + (sidx % S::NSTAGE) * S::STAGE_BYTES;
 #pragma unroll
-      for (int i = 0; i < S::K_PER_THREAD; ++i) {
-        const int row = rg + S::K_ROWS_PER_PASS * i;
-        if (row < valid)
-          stg[i] = *reinterpret_cast<const u32x4*>(kv_row<D>(p, st, kvidx, base + row, 0, h) + cc * 8);
-        else
-          stg[i] = u32x4{0u, 0u, 0u, 0u};
-      }
-    } else {
-      const int u = tid - 128;
-#pragma unroll
-      for (int j = 0; j < S::V_PER_THREAD; ++j) {
-        const int b = u + 128 * j;
-        const int cc = b % S::CPR;
-        const int kg = b / S::CPR;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = 4 * kg + i;
-          if (b < S::V_BLOCKS && row < valid)
-            stg[4 * j + i] = *reinterpret_cast<const u32x4*>(kv_row<D>(p, st, kvidx, base + row, 1, h) + cc * 8);
-          else
-            stg[4 * j + i] = u32x4{0u, 0u, 0u, 0u};
-        }
-      }
-    }
-  };
-  auto store_stage = [&](int buf) {
-    uint8_t* kb = smem + buf * S::STAGE_BYTES;
-    uint8_t* vb = kb + S::K_BYTES;
-    if (tid < 128) {
-      const int cc = tid % S::CPR;
-      const int rg = tid / S::CPR;
-#pragma unroll
-      for (int i = 0; i < S::K_PER_THREAD; ++i) {
-        const int row = rg + S::K_ROWS_PER_PASS * i;
-        *reinterpret_cast<u32x4*>(kb + row * (D * 2) + ((cc ^ (swz_k(row) & (S::CPR - 1))) << 4)) = stg[i];
-      }
-    } else {
-      const int u = tid - 128;
-#pragma unroll
-      for (int j = 0; j < S::V_PER_THREAD; ++j) {
-        const int b = u + 128 * j;
-        if (b >= S::V_BLOCKS) continue;
-        const int cc = b % S::CPR;
-        const int kg = b / S::CPR;
-        const u32x4 r0 = stg[4 * j + 0], r1 = stg[4 * j + 1], r2 = stg[4 * j + 2], r3 = stg[4 * j + 3];
-#pragma unroll
-        for (int dd = 0; dd < 8; ++dd) {
-          const int w = dd >> 1;
-          uint32_t lo, hi;
-          if (dd & 1) {
-            lo = (r0[w] >> 16) | (r1[w] & 0xffff0000u);
-            hi = (r2[w] >> 16) | (r3[w] & 0xffff0000u);
-          } else {
-            lo = (r0[w] & 0xffffu) | (r1[w] << 16);
-            hi = (r2[w] & 0xffffu) | (r3[w] << 16);
-          }
-          const int d = 8 * cc + dd;
-          const int off = d * (KT * 2) + (((kg >> 1) ^ swz_v(d)) << 4) + ((kg & 1) << 3);
-          *reinterpret_cast<u32x2*>(vb + off) = u32x2{lo, hi};
-        }
-      }
+    for (int j = 0; j < S::LOADS_PER_WAVE; ++j) {
+      const int inst = wave * S::LOADS_PER_WAVE + j;
+      const int kv = inst >= S::LOADS / 2 ? 1 : 0;
+      const int blk = inst - kv * (S::LOADS / 2);
+      const int off = blk * 1024 + lane * 16;
+      const int row = off / S::ROW_BYTES;
+      const int pch = (off % S::ROW_BYTES) >> 4;
+      const int lch = pch ^ (swz(row) & (S::CPR - 1));
+      const int tok = min(base + row, tok1 - 1);
+      int pi, slot;
+      token_page(p, st, tok, pi, slot);
+      const int page = s_pages[pi - pi_first];
+      const uint16_t* src = pool + ((((size_t)page * 2 + kv) * p.page_size + slot) * H + h) * D + lch * 8;
+      load_lds16(src, __builtin_amdgcn_readfirstlane(lds_addr(stage + kv * S::HALF_BYTES + blk * 1024)));
     }
   };
 
-  auto compute_stage = [&](int buf, int valid) {
-    const uint8_t* kb = smem + buf * S::STAGE_BYTES;
-    const uint8_t* vb = kb + S::K_BYTES;
-    // K operand rows: block kb_i (= 2*pair + half) row r16 holds kv
+  // ---- one stage of 64 tokens for every query tile of this wave ----
+  auto compute = [&](int sidx, int valid) {
+    const uint8_t* kb = ring + (sidx % S::NSTAGE) * S::STAGE_BYTES;
+    const uint8_t* vb = kb + S::HALF_BYTES;
+    // K operand rows: block kbi (= 2*pair + half) row r16 holds kv
     // 32*pair + 8*(r16/4) + 4*half + r16%4, so that after the MFMA lane group
     // g4 holds kv 32*pair + 8*g4 + [0, 8) of each query column.
     bf16x8 kop[4][S::KSTEPS];
@@ -291,18 +315,28 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
 #pragma unroll
       for (int ks = 0; ks < S::KSTEPS; ++ks) {
         const int chunk = 4 * ks + g4;
-        kop[kbi][ks] = *reinterpret_cast<const bf16x8*>(
-            kb + kvrow * (D * 2) + ((chunk ^ (swz_k(kvrow) & (S::CPR - 1))) << 4));
+        kop[kbi][ks] = *reinterpret_cast<const bf16x8*>(kb + kvrow * S::ROW_BYTES +
+                                                        ((chunk ^ (swz(kvrow) & (S::CPR - 1))) << 4));
       }
     }
+    // V^T operands by transposing reads of row-major V: lane (g4, r16) gets
+    // V[32*pair + 8*g4 + j][16*db + r16], j = 0..7.
     bf16x8 vop[S::DBLK][2];
 #pragma unroll
     for (int db = 0; db < S::DBLK; ++db) {
-      const int d = 16 * db + r16;
 #pragma unroll
       for (int pp = 0; pp < 2; ++pp) {
-        const int chunk = 4 * pp + g4;
-        vop[db][pp] = *reinterpret_cast<const bf16x8*>(vb + d * (KT * 2) + ((chunk ^ swz_v(d)) << 4));
+        i16x4 half[2];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          const int row = 32 * pp + 8 * g4 + 4 * r + (r16 >> 2);
+          const int chunk = 2 * db + ((r16 & 3) >> 1);
+          half[r] = ds_read_tr16(vb + row * S::ROW_BYTES + ((chunk ^ (swz(row) & (S::CPR - 1))) << 4) +
+                                 ((r16 & 1) << 3));
+        }
+        const i16x4 a = half[0], b = half[1];
+        vop[db][pp] = __builtin_bit_cast(bf16x8, (short __attribute__((ext_vector_type(8)))){
+                                                     a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]});
       }
     }
 #pragma unroll
@@ -323,60 +357,68 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
             for (int i = 0; i < 4; ++i)
               if (32 * (kbi >> 1) + 8 * g4 + 4 * (kbi & 1) + i >= valid) sacc[kbi][i] = -INFINITY;
         }
-        float mx = sacc[0][0];
+        float mx = fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3]));
 #pragma unroll
-        for (int kbi = 0; kbi < 4; ++kbi)
+        for (int kbi = 1; kbi < 4; ++kbi)
+          mx = fmaxf(mx, fmaxf(fmaxf(sacc[kbi][0], sacc[kbi][1]), fmaxf(sacc[kbi][2], sacc[kbi][3])));
+        mx = lane_swap_max(mx) * sl;
+        // Renormalise only when some column's maximum grew past the
+        // threshold; softmax does not depend on the offset.
+        if (__builtin_amdgcn_ballot_w64(mx > mb_run[k] + RESCALE_LOG2)) {
+          const float nm = fmaxf(mb_run[k], mx);
+          const float alpha = __builtin_amdgcn_exp2f(mb_run[k] - nm);
+          mb_run[k] = nm;
+          l_run[k] *= alpha;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[kbi][i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run[k], mx);
-        const float alpha = __builtin_amdgcn_exp2f((m_run[k] - m_new) * sl);
-        m_run[k] = m_new;
-        const float mb = m_new * sl;
-        float lsum = 0.f;
+          for (int db = 0; db < S::DBLK; ++db) oacc[k][db] *= alpha;
+        }
+        const float mb = mb_run[k];
         bf16x8 pb[2];
 #pragma unroll
         for (int kbi = 0; kbi < 4; ++kbi)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kbi][i], sl, -mb));
-            lsum += pv;
-            pb[kbi >> 1][4 * (kbi & 1) + i] = (__bf16)pv;
-          }
-        l_run[k] = l_run[k] * alpha + lsum;
+          for (int i = 0; i < 4; ++i)
+            pb[kbi >> 1][4 * (kbi & 1) + i] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kbi][i], sl, -mb));
+        // row sums of the bf16 probabilities the P.V product uses
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+        float ls = l_run[k];
 #pragma unroll
-        for (int db = 0; db < S::DBLK; ++db) {
-          oacc[k][db] *= alpha;
+        for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            ls = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[pp][2 * j], pb[pp][2 * j + 1]}, ones, ls, false);
+        l_run[k] = ls;
+#pragma unroll
+        for (int db = 0; db < S::DBLK; ++db)
 #pragma unroll
           for (int pp = 0; pp < 2; ++pp)
             oacc[k][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[db][pp], pb[pp], oacc[k][db], 0, 0, 0);
-        }
       }
     }
   };
 
-  if (nstage > 0) {
-    load_stage(0);
-    store_stage(0);
-  }
-  __syncthreads();
+#pragma unroll
+  for (int d = 0; d < S::DIST; ++d)
+    if (d < nstage) issue(d);
   for (int sidx = 0; sidx < nstage; ++sidx) {
-    const int buf = sidx & 1;
-    const bool more = sidx + 1 < nstage;
-    if (more) load_stage(sidx + 1);
-    compute_stage(buf, min(KT, tok1 - (tok0 + sidx * KT)));
-    if (more) store_stage(buf ^ 1);
-    __syncthreads();
+    if (sidx + S::DIST < nstage) issue(sidx + S::DIST);
+    const int ahead = min(S::DIST, nstage - 1 - sidx);
+    if (ahead >= 2)
+      wait_vmcnt<2 * S::LOADS_PER_WAVE>();
+    else if (ahead == 1)
+      wait_vmcnt<S::LOADS_PER_WAVE>();
+    else
+      wait_vmcnt<0>();
+    block_barrier();
+    compute(sidx, min(KT, tok1 - (tok0 + sidx * KT)));
   }
 
   // ---- epilogue ----
 #pragma unroll
   for (int k = 0; k < QTW; ++k) {
     if (k < ntw) {
-      float l = l_run[k];
-      l += __shfl_xor(l, 16);
-      l += __shfl_xor(l, 32);
+      const float l = lane_swap_sum(l_run[k]);
       const float inv = 1.0f / l;
       const int row = KVC_Q_TILE * (t_lo + wave + KVC_ATTN_WAVES * k) + r16;
       if (row < st.n_q) {
@@ -399,7 +441,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
 #pragma unroll
           for (int db = 0; db < S::DBLK; ++db)
             *reinterpret_cast<f32x4*>(po + 16 * db + 4 * g4) = oacc[k][db] * inv;
-          if (g4 == 0) p.part_lse[prow] = m_run[k] * sl + __log2f(l);
+          if (g4 == 0) p.part_lse[prow] = mb_run[k] + __log2f(l);
         }
       }
     }

@@ -25,6 +25,8 @@
 #define KVC_ATTN_WAVES 4
 // Upper bound of KV splits per stream (sizes the partial-output workspace).
 #define KVC_MAX_SPLITS 64
+// Most pages one KV split may span (their IDs are staged in LDS).
+#define KVC_MAX_SPLIT_PAGES 512
 // Largest n_s, and the most special pages one frame's specials can touch.
 #define KVC_MAX_SPECIAL_PER_FRAME 64
 #define KVC_MAX_APPEND_SPECIAL_PAGES 8
