@@ -27,6 +27,8 @@ HIP_FLAGS = [
     "-Wno-unused-command-line-argument",
     # MFMA accumulators in VGPRs: avoids AGPR<->VGPR copies around every MFMA
     "-mllvm", "-amdgpu-mfma-vgpr-form",
+    # scores are never NaN (masked slots are -inf): max needs no NaN quieting
+    "-fno-honor-nans",
 ]
 CXX_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-Wall", "-Wextra", "-Wno-unused-parameter",
              "-D__HIP_PLATFORM_AMD__", f"-I{ROCM}/include"]

@@ -35,13 +35,12 @@ int validate(const Config& c, std::string* why) {
   if ((int64_t)c.num_heads * c.head_dim > 65536) return fail(ERR_UNSUPPORTED, "num_heads * head_dim above 65536");
   if ((int64_t)c.num_streams * c.tokens_per_frame >= (int64_t)1 << 24) return fail(ERR_UNSUPPORTED, "too many query rows");
   {
-    // longest possible visible stream must fit KVC_MAX_SPLITS splits of at
-    // most KVC_MAX_SPLIT_PAGES pages each
-    const int64_t min_valid = std::max<int32_t>(1, std::min(c.patch_tokens(), c.page_size));
-    const int64_t per_split = (int64_t)(KVC_MAX_SPLIT_PAGES - 2) * min_valid / KVC_KV_TILE;
-    const int64_t max_tokens = (int64_t)c.max_patch_pages * c.patch_tokens() + (int64_t)c.max_special_pages * c.page_size;
-    if (per_split < 1 || ceil_div(ceil_div(max_tokens, KVC_KV_TILE), per_split) > KVC_MAX_SPLITS)
-      return fail(ERR_UNSUPPORTED, "pages too small for the stream length (split page limit)");
+    // the longest possible visible stream must fit KVC_MAX_SPLITS splits of
+    // at most KVC_MAX_SPLIT_STAGES units each
+    const int64_t units = (int64_t)c.max_patch_pages * ceil_div(std::max(1, c.patch_tokens()), KVC_KV_TILE) +
+                          (int64_t)c.max_special_pages * ceil_div(c.page_size, KVC_KV_TILE);
+    if (ceil_div(units, KVC_MAX_SPLIT_STAGES) > KVC_MAX_SPLITS)
+      return fail(ERR_UNSUPPORTED, "too many pages for the split limits");
   }
   return OK;
 }
@@ -192,7 +191,7 @@ void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const P
   // KV splits share the target work-group count in proportion to each
   // stream's visible length, in whole KVC_KV_TILE units.
   const int32_t nqt = (int32_t)ceil_div(c.tokens_per_frame, KVC_Q_TILE);
-  const int32_t per_group = KVC_ATTN_WAVES * kvc_tiles_per_wave(c.head_dim);
+  const int32_t per_group = kvc_group_tiles(c.head_dim);
   const int32_t n_group = (int32_t)ceil_div(nqt, per_group);
   int64_t total_len = 0;
   for (int i = 0; i < n; ++i) total_len += kv_len[i];
@@ -201,18 +200,21 @@ void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const P
   p.image.assign(KVC_PLAN_HEADER_INTS + (size_t)KVC_STREAM_REC_INTS * n + p.kv_indices.size(), 0);
   int32_t item = 0;
   p.any_split = false;
+  const int32_t upp = (int32_t)ceil_div(std::max(1, P), KVC_KV_TILE);
+  const int32_t ups = (int32_t)ceil_div(c.page_size, KVC_KV_TILE);
   for (int i = 0; i < n; ++i) {
-    const int64_t units = std::max<int64_t>(1, ceil_div(kv_len[i], KVC_KV_TILE));
+    const int32_t n_patch = p.n_patch_pages[i];
+    const int32_t n_special = p.kv_indptr[i + 1] - p.kv_indptr[i] - n_patch;
+    const int64_t units = std::max<int64_t>(
+        1, (int64_t)n_patch * upp +
+               (n_special > 0 ? (int64_t)(n_special - 1) * ups + ceil_div(p.last_page_len[i], KVC_KV_TILE) : 0));
     double want = total_len > 0 ? (double)pol.target_workgroups * (double)kv_len[i] / (double)total_len /
                                       ((double)c.num_heads * n_group)
                                 : 1.0;
     int64_t ns = (int64_t)std::llround(want);
     ns = std::max<int64_t>(1, std::min<int64_t>(ns, std::min<int64_t>(max_splits, units)));
-    // a split's page IDs are staged in LDS: it may span at most
-    // KVC_MAX_SPLIT_PAGES pages (each holds >= min(P, page_size) tokens)
-    const int64_t min_valid = std::max<int32_t>(1, std::min(P, c.page_size));
-    const int64_t per_split = (int64_t)(KVC_MAX_SPLIT_PAGES - 2) * min_valid / KVC_KV_TILE;
-    ns = std::max<int64_t>(ns, ceil_div(units, std::max<int64_t>(1, per_split)));
+    // a split's stage table lives in LDS: at most KVC_MAX_SPLIT_STAGES units
+    ns = std::max<int64_t>(ns, ceil_div(units, KVC_MAX_SPLIT_STAGES));
     p.n_split.push_back((int32_t)ns);
     if (ns > 1) p.any_split = true;
 
@@ -227,6 +229,8 @@ void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const P
     rec.kv_len = (int32_t)kv_len[i];
     rec.patch_tok = rec.n_patch * P;
     rec.n_units = (int32_t)units;
+    rec.upp = upp;
+    rec.ups = ups;
     rec.n_split = (int32_t)ns;
     rec.n_group = n_group;
     rec.item0 = item;

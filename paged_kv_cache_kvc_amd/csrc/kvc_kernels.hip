@@ -18,14 +18,15 @@
 // Over SDPA" §Paged KV Cache Memory Layout); q, o [rows, H, D] bf16.
 //
 // Attention work item = (stream, head, KV split, query group).  A work-group
-// of 4 waves streams its split's KV tokens through LDS in stages of 64
-// tokens, double-buffered: K row-major, V transposed (V^T[d][kv]) so that the
-// P.V contraction over kv reads 8 consecutive kv per lane.  The scores are
-// computed transposed, S^T = K Q^T (16x16x32 bf16 MFMA, kv on rows, queries on
-// columns), so each lane's accumulators belong to one query column: the
-// softmax column max needs only two cross-lane steps, and the probabilities
-// feed the P.V MFMA (O^T = V^T P^T) straight from registers.  Each wave owns a
-// set of 16-query tiles.
+// of 4 waves streams its split's KV through a ring of LDS stages (64 slots of
+// one page each) with direct global-to-LDS loads.  K and V stay row-major in
+// LDS; V is read as the transposed MFMA operand with ds_read_b64_tr_b16.  The
+// scores are computed transposed, S^T = K Q^T (16x16x32 bf16 MFMA, kv on rows,
+// queries on columns), so each lane's accumulators belong to one query column:
+// the softmax column max needs only two cross-lane steps, and the
+// probabilities feed the P.V MFMA (O^T = V^T P^T) straight from registers.
+// Rule kept throughout: an MFMA result is never read by a vector instruction
+// right after its MFMA is issued; every consumer is one pipelined tile later.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -126,10 +127,20 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-// 16 bytes from `src` (per lane) to LDS byte address lds_base + 16 * lane.
-__device__ __forceinline__ void load_lds16(const void* src, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_base) : "memory", "m0");
+// 16 bytes from base + offset (per lane) to LDS byte address
+// lds_base + 16 * lane.  base is wave-uniform (scalar registers).
+__device__ __forceinline__ void load_lds16(const void* base, uint32_t offset, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(offset), "s"(base),
+               "s"(lds_base)
+               : "memory", "m0");
 }
+
+// Maximum of scores (never NaN: masked slots are -inf).  Written with the
+// compiler's own max so that its hazard tracking sees the MFMA results these
+// read (an opaque instruction reading an MFMA accumulator too early would see
+// a partially written register).
+__device__ __forceinline__ float max3(float a, float b, float c) { return __builtin_fmaxf(__builtin_fmaxf(a, b), c); }
+__device__ __forceinline__ float max2(float a, float b) { return __builtin_fmaxf(a, b); }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* generic) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)generic;
@@ -159,11 +170,11 @@ __device__ __forceinline__ void swap16(uint32_t& a, uint32_t& b) {
 __device__ __forceinline__ float lane_swap_max(float x) {
   uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
   swap32(a, b);
-  x = fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+  x = max2(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
   a = __builtin_bit_cast(uint32_t, x);
   b = a;
   swap16(a, b);
-  return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+  return max2(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
 }
 
 __device__ __forceinline__ float lane_swap_sum(float x) {
@@ -176,36 +187,153 @@ __device__ __forceinline__ float lane_swap_sum(float x) {
   return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
 }
 
-// Page index and slot of visible token `tok` of a stream: patch pages hold P
-// tokens, special pages page_size ([p1] "How FlashInfer KV Cache Attention
-// Accelerates Streaming 3D Reconstruction Over SDPA" §Efficient Attention
-// Masking and Padding: lengths, not masks, delimit the valid tokens).
-__device__ __forceinline__ void token_page(const AttnParams& p, const kvc_dev_stream& st, int tok, int& pi,
-                                           int& slot) {
-  if (tok < st.patch_tok) {
-    pi = (int)fdiv((uint32_t)tok, p.div_patch);
-    slot = tok - pi * p.patch_tokens;
-  } else {
-    const int t2 = tok - st.patch_tok;
-    const int pj = (int)fdiv((uint32_t)t2, p.div_page);
-    pi = st.n_patch + pj;
-    slot = t2 - pj * p.page_size;
-  }
-}
-
 // Rescale threshold of the running maximum, in log2 units of the scaled
 // scores: probabilities up to 2^8 are kept without renormalising.
 constexpr float RESCALE_LOG2 = 8.0f;
 
+// Work of one query tile over one 64-slot stage, in three parts so that
+// the next tile's QK^T MFMAs can be issued before this tile's softmax (the
+// matrix core then runs while the vector unit computes exponentials).
+template <int D>
+struct TileOps {
+  using S = Shape<D>;
+
+  // S^T[64 kv x 16 q] = K Q^T for the four 16-kv blocks of the stage
+  static __device__ __forceinline__ void qk(const bf16x8 (&kop)[4][S::KSTEPS], const bf16x8 (&q)[S::KSTEPS],
+                                            f32x4 (&sacc)[4]) {
+#pragma unroll
+    for (int kbi = 0; kbi < 4; ++kbi) {
+      sacc[kbi] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < S::KSTEPS; ++ks)
+        sacc[kbi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kbi][ks], q[ks], sacc[kbi], 0, 0, 0);
+    }
+  }
+
+  // Online softmax of one tile's stage scores (fp32): mask slots past
+  // `valid`, column max over the 64 kv, renormalise only when a column's
+  // maximum grew by more than 2^RESCALE_LOG2, then p = 2^(s*sl - m) rounded
+  // to bf16 into the P^T operand, and the row sums of those bf16 values.
+  static __device__ __forceinline__ void softmax(f32x4 (&sacc)[4], int valid, int g4, float sl, float& mb, float& l,
+                                                 f32x4 (&o)[S::DBLK], bf16x8 (&pb)[2]) {
+    if (valid < KT) {
+#pragma unroll
+      for (int kbi = 0; kbi < 4; ++kbi)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (32 * (kbi >> 1) + 8 * g4 + 4 * (kbi & 1) + i >= valid) sacc[kbi][i] = -INFINITY;
+    }
+    float mx = max3(sacc[0][0], sacc[0][1], sacc[0][2]);
+    mx = max3(mx, sacc[0][3], sacc[1][0]);
+    mx = max3(mx, sacc[1][1], sacc[1][2]);
+    mx = max3(mx, sacc[1][3], sacc[2][0]);
+    mx = max3(mx, sacc[2][1], sacc[2][2]);
+    mx = max3(mx, sacc[2][3], sacc[3][0]);
+    mx = max3(mx, sacc[3][1], sacc[3][2]);
+    mx = max2(mx, sacc[3][3]);
+    mx = lane_swap_max(mx) * sl;
+    if (__builtin_amdgcn_ballot_w64(mx > mb + RESCALE_LOG2)) {
+      const float nm = fmaxf(mb, mx);
+      const float alpha = __builtin_amdgcn_exp2f(mb - nm);
+      mb = nm;
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < S::DBLK; ++db) o[db] *= alpha;
+    }
+#pragma unroll
+    for (int kbi = 0; kbi < 4; ++kbi)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        pb[kbi >> 1][4 * (kbi & 1) + i] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kbi][i], sl, -mb));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        l = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[pp][2 * j], pb[pp][2 * j + 1]}, ones, l, false);
+  }
+
+  // O^T[D x 16 q] += V^T P^T
+  static __device__ __forceinline__ void pv(const bf16x8 (&vop)[S::DBLK][2], const bf16x8 (&pb)[2],
+                                            f32x4 (&o)[S::DBLK]) {
+#pragma unroll
+    for (int db = 0; db < S::DBLK; ++db)
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp)
+        o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[db][pp], pb[pp], o[db], 0, 0, 0);
+  }
+
+  // The shared tile on one 16-kv block BLK of the stage (BLK = 2*pair +
+  // half), in two parts like the own tiles: QK^T first (issued one tile
+  // ahead of its use), then softmax over its 4 scores per lane and P.V with
+  // the other half of the pair's P^T operand zero.  A block whose slots are
+  // all past the end of the stage is skipped.
+  template <int BLK>
+  static __device__ __forceinline__ bool block_live(int valid) {
+    return 32 * (BLK >> 1) + 4 * (BLK & 1) < valid;
+  }
+  template <int BLK>
+  static __device__ __forceinline__ f32x4 shared_qk(const bf16x8 (&kop)[4][S::KSTEPS], const bf16x8 (&q)[S::KSTEPS]) {
+    f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < S::KSTEPS; ++ks)
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[BLK][ks], q[ks], sc, 0, 0, 0);
+    return sc;
+  }
+  template <int BLK>
+  static __device__ __forceinline__ void shared_rest(f32x4 sc, const bf16x8 (&vop)[S::DBLK][2], int valid, int g4,
+                                                     float sl, float& mb, float& l, f32x4 (&o)[S::DBLK]) {
+    constexpr int PP = BLK >> 1, TT = BLK & 1;
+    if (valid < KT) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (32 * PP + 8 * g4 + 4 * TT + i >= valid) sc[i] = -INFINITY;
+    }
+    float mx = max2(max3(sc[0], sc[1], sc[2]), sc[3]);
+    mx = lane_swap_max(mx) * sl;
+    if (__builtin_amdgcn_ballot_w64(mx > mb + RESCALE_LOG2)) {
+      const float nm = fmaxf(mb, mx);
+      const float alpha = __builtin_amdgcn_exp2f(mb - nm);
+      mb = nm;
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < S::DBLK; ++db) o[db] *= alpha;
+    }
+    bf16x8 pb;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) pb[j] = (__bf16)0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pb[4 * TT + i] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], sl, -mb));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    l = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[4 * TT], pb[4 * TT + 1]}, ones, l, false);
+    l = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[4 * TT + 2], pb[4 * TT + 3]}, ones, l, false);
+#pragma unroll
+    for (int db = 0; db < S::DBLK; ++db)
+      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[db][PP], pb, o[db], 0, 0, 0);
+  }
+};
+
+// Attention over one KV split for one head and one query group.  The group's
+// query tiles are spread over the 4 waves: each wave owns up to QTW tiles
+// (t_lo + wave + 4k); when the group has 4m+1 tiles, the last one is shared:
+// every wave processes one 16-kv block of it in every stage, and the four
+// partial softmax states are merged through LDS at the end.  Every SIMD thus
+// carries the same MFMA work per stage.
 template <int D, int QTW>
 __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
   using S = Shape<D>;
+  using T = TileOps<D>;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[S::NSTAGE * S::STAGE_BYTES];
-  __shared__ int32_t s_pages[KVC_MAX_SPLIT_PAGES];
+  // per stage of this split: byte offset of its first K row in the pool
+  // (lo, hi) and its valid slot count
+  __shared__ int4 s_stage[KVC_MAX_SPLIT_STAGES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);   // same value, known uniform
   const int r16 = lane & 15;
   const int g4 = lane >> 4;
 
@@ -231,77 +359,118 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
   const int nqt = (st.n_q + KVC_Q_TILE - 1) / KVC_Q_TILE;
   const int t_lo = grp * nqt / st.n_group;
   const int t_hi = (grp + 1) * nqt / st.n_group;
+  const int ntile = t_hi - t_lo;
+  const bool has_shared = ntile >= 5 && (ntile & 3) == 1;
+  const int n_own = ntile - (has_shared ? 1 : 0);
   const int u0 = split * st.n_units / st.n_split;
   const int u1 = (split + 1) * st.n_units / st.n_split;
-  const int tok0 = u0 * KT;
-  const int tok1 = min(st.kv_len, u1 * KT);
   const int nstage = u1 - u0;
   const float sl = p.scale_log2;
   const int H = p.num_heads;
+  const uint32_t slot_bytes = (uint32_t)H * D * 2;
 
-  // page IDs of this split's tokens, staged in LDS
-  int pi_first, pi_last, tmp;
-  token_page(p, st, tok0, pi_first, tmp);
-  token_page(p, st, tok1 - 1, pi_last, tmp);
-  for (int i = tid; i <= pi_last - pi_first; i += 256) s_pages[i] = kvidx[pi_first + i];
+  // Stage table of this split.  Unit u is the 64-slot chunk cu of visible
+  // page pi: patch pages hold P valid slots, special pages page_size, the
+  // last page last_len ([p1] "How FlashInfer KV Cache Attention Accelerates
+  // Streaming 3D Reconstruction Over SDPA" §Efficient Attention Masking and
+  // Padding: lengths, not masks, delimit the valid tokens).
+  for (int i = tid; i < nstage; i += 256) {
+    const int u = u0 + i;
+    const int patch_units = st.n_patch * st.upp;
+    int pi, cu;
+    if (u < patch_units) {
+      pi = u / st.upp;
+      cu = u - pi * st.upp;
+    } else {
+      const int pj = (u - patch_units) / st.ups;
+      pi = st.n_patch + pj;
+      cu = u - patch_units - pj * st.ups;
+    }
+    const int len = pi == st.n_pages - 1 ? st.last_len : (pi < st.n_patch ? p.patch_tokens : p.page_size);
+    const uint64_t off = (((uint64_t)kvidx[pi] * 2) * p.page_size + (uint64_t)KT * cu) * slot_bytes +
+                         (uint64_t)h * D * 2;
+    s_stage[i] = int4{(int)(uint32_t)off, (int)(uint32_t)(off >> 32), min(KT, len - KT * cu), 0};
+  }
 
-  // ---- this wave's query tiles: t_lo + wave + 4k ----
+  // ---- query operands (Q^T as the MFMA B operand) ----
+  auto load_q = [&](int tile, bool ok, bf16x8 (&q)[S::KSTEPS]) {
+    const int row = KVC_Q_TILE * tile + r16;
+    ok = ok && row < st.n_q;
+    const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + ((size_t)(st.q_row0 + (ok ? row : 0)) * H + h) * D;
+#pragma unroll
+    for (int ks = 0; ks < S::KSTEPS; ++ks) {
+      q[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks + 8 * g4);
+      if (!ok) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) q[ks][j] = (__bf16)0.0f;
+      }
+    }
+  };
   int ntw = 0;
 #pragma unroll
   for (int k = 0; k < QTW; ++k)
-    if (t_lo + wave + KVC_ATTN_WAVES * k < t_hi) ntw = k + 1;
+    if (wave + KVC_ATTN_WAVES * k < n_own) ntw = k + 1;
 
   bf16x8 qop[QTW][S::KSTEPS];
   float mb_run[QTW], l_run[QTW];
   f32x4 oacc[QTW][S::DBLK];
 #pragma unroll
   for (int k = 0; k < QTW; ++k) {
-    const int row = KVC_Q_TILE * (t_lo + wave + KVC_ATTN_WAVES * k) + r16;
-    const bool ok = k < ntw && row < st.n_q;
-    const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + ((size_t)(st.q_row0 + (ok ? row : 0)) * H + h) * D;
-#pragma unroll
-    for (int ks = 0; ks < S::KSTEPS; ++ks) {
-      qop[k][ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks + 8 * g4);
-      if (!ok) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) qop[k][ks][j] = (__bf16)0.0f;
-      }
-    }
+    load_q(t_lo + wave + KVC_ATTN_WAVES * k, k < ntw, qop[k]);
     mb_run[k] = -INFINITY;
     l_run[k] = 0.0f;
 #pragma unroll
     for (int db = 0; db < S::DBLK; ++db) oacc[k][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  __syncthreads();   // s_pages ready
+  bf16x8 qsh[S::KSTEPS];
+  float mb_sh = -INFINITY, l_sh = 0.0f;
+  f32x4 osh[S::DBLK];
+  load_q(t_hi - 1, has_shared, qsh);
+#pragma unroll
+  for (int db = 0; db < S::DBLK; ++db) osh[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  __syncthreads();   // stage table ready
 
   // ---- direct global -> LDS loads of one stage (K rows, then V rows) ----
   // Load instruction i of a stage fills 1 KiB of LDS, lane l writing bytes
   // [16 l, 16 l + 16); the lane fetches the logical chunk that the swizzle
-  // places there.  Rows past the split end re-read its last token (finite
-  // data; their scores are masked to -inf).
-  const uint16_t* pool = static_cast<const uint16_t*>(p.pool);
+  // places there, from the stage's uniform base address plus a per-lane
+  // offset.  In a partial stage, rows past the valid count re-read the last
+  // valid row (finite data; their scores are masked to -inf).
+  const uint8_t* pool = static_cast<const uint8_t*>(p.pool);
+  const uint64_t v_half = (uint64_t)p.page_size * slot_bytes;
+  int lrow[S::LOADS_PER_WAVE];
+  uint32_t lofs[S::LOADS_PER_WAVE];
+#pragma unroll
+  for (int j = 0; j < S::LOADS_PER_WAVE; ++j) {
+    const int inst = wave * S::LOADS_PER_WAVE + j;
+    const int blk = inst % (S::LOADS / 2);
+    const int off = blk * 1024 + lane * 16;
+    const int row = off / S::ROW_BYTES;
+    const int pch = (off % S::ROW_BYTES) >> 4;
+    lrow[j] = row;
+    lofs[j] = (uint32_t)((pch ^ (swz(row) & (S::CPR - 1))) << 4);
+  }
   auto issue = [&](int sidx) {
-    const int base = tok0 + sidx * KT;
+    const int4 e = s_stage[sidx];
+    const uint64_t koff = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(e.x) |
+                          ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(e.y) << 32);
+    const int valid = __builtin_amdgcn_readfirstlane(e.z);
     uint8_t* stage = ring + (sidx % S::NSTAGE) * S::STAGE_BYTES;
 #pragma unroll
     for (int j = 0; j < S::LOADS_PER_WAVE; ++j) {
       const int inst = wave * S::LOADS_PER_WAVE + j;
       const int kv = inst >= S::LOADS / 2 ? 1 : 0;
       const int blk = inst - kv * (S::LOADS / 2);
-      const int off = blk * 1024 + lane * 16;
-      const int row = off / S::ROW_BYTES;
-      const int pch = (off % S::ROW_BYTES) >> 4;
-      const int lch = pch ^ (swz(row) & (S::CPR - 1));
-      const int tok = min(base + row, tok1 - 1);
-      int pi, slot;
-      token_page(p, st, tok, pi, slot);
-      const int page = s_pages[pi - pi_first];
-      const uint16_t* src = pool + ((((size_t)page * 2 + kv) * p.page_size + slot) * H + h) * D + lch * 8;
-      load_lds16(src, __builtin_amdgcn_readfirstlane(lds_addr(stage + kv * S::HALF_BYTES + blk * 1024)));
+      const uint32_t vofs = (uint32_t)min(lrow[j], valid - 1) * slot_bytes + lofs[j];
+      const uint64_t b = (uint64_t)(uintptr_t)(pool + koff + (kv ? v_half : 0));
+      const uint64_t ub = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b) |
+                          ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32);
+      load_lds16((const void*)(uintptr_t)ub, vofs,
+                 __builtin_amdgcn_readfirstlane(lds_addr(stage + kv * S::HALF_BYTES + blk * 1024)));
     }
   };
 
-  // ---- one stage of 64 tokens for every query tile of this wave ----
+  // ---- one stage of 64 slots for this wave's tiles ----
   auto compute = [&](int sidx, int valid) {
     const uint8_t* kb = ring + (sidx % S::NSTAGE) * S::STAGE_BYTES;
     const uint8_t* vb = kb + S::HALF_BYTES;
@@ -339,61 +508,46 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
                                                      a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]});
       }
     }
+    // This wave's block of the shared tile (wave-uniform index).
+    const bool sh_live = has_shared && (wv == 0   ? T::template block_live<0>(valid)
+                                        : wv == 1 ? T::template block_live<1>(valid)
+                                        : wv == 2 ? T::template block_live<2>(valid)
+                                                  : T::template block_live<3>(valid));
+    auto sh_qk = [&]() -> f32x4 {
+      switch (wv) {
+        case 0: return T::template shared_qk<0>(kop, qsh);
+        case 1: return T::template shared_qk<1>(kop, qsh);
+        case 2: return T::template shared_qk<2>(kop, qsh);
+        default: return T::template shared_qk<3>(kop, qsh);
+      }
+    };
+    // Own tiles, software-pipelined: the QK^T of the next tile (or of the
+    // shared block, after the last own tile) is issued before the softmax of
+    // the current one, so no MFMA result is read right after it is issued.
+    f32x4 sacc[2][4];
+    f32x4 ssh = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (ntw > 0)
+      T::qk(kop, qop[0], sacc[0]);
+    else if (sh_live)
+      ssh = sh_qk();
 #pragma unroll
     for (int k = 0; k < QTW; ++k) {
       if (k < ntw) {
-        f32x4 sacc[4];
-#pragma unroll
-        for (int kbi = 0; kbi < 4; ++kbi) {
-          sacc[kbi] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ks = 0; ks < S::KSTEPS; ++ks)
-            sacc[kbi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kbi][ks], qop[k][ks], sacc[kbi], 0, 0, 0);
-        }
-        if (valid < KT) {
-#pragma unroll
-          for (int kbi = 0; kbi < 4; ++kbi)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (32 * (kbi >> 1) + 8 * g4 + 4 * (kbi & 1) + i >= valid) sacc[kbi][i] = -INFINITY;
-        }
-        float mx = fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3]));
-#pragma unroll
-        for (int kbi = 1; kbi < 4; ++kbi)
-          mx = fmaxf(mx, fmaxf(fmaxf(sacc[kbi][0], sacc[kbi][1]), fmaxf(sacc[kbi][2], sacc[kbi][3])));
-        mx = lane_swap_max(mx) * sl;
-        // Renormalise only when some column's maximum grew past the
-        // threshold; softmax does not depend on the offset.
-        if (__builtin_amdgcn_ballot_w64(mx > mb_run[k] + RESCALE_LOG2)) {
-          const float nm = fmaxf(mb_run[k], mx);
-          const float alpha = __builtin_amdgcn_exp2f(mb_run[k] - nm);
-          mb_run[k] = nm;
-          l_run[k] *= alpha;
-#pragma unroll
-          for (int db = 0; db < S::DBLK; ++db) oacc[k][db] *= alpha;
-        }
-        const float mb = mb_run[k];
+        if (k + 1 < ntw)
+          T::qk(kop, qop[k + 1], sacc[(k + 1) & 1]);
+        else if (sh_live)
+          ssh = sh_qk();
         bf16x8 pb[2];
-#pragma unroll
-        for (int kbi = 0; kbi < 4; ++kbi)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            pb[kbi >> 1][4 * (kbi & 1) + i] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kbi][i], sl, -mb));
-        // row sums of the bf16 probabilities the P.V product uses
-        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-        float ls = l_run[k];
-#pragma unroll
-        for (int pp = 0; pp < 2; ++pp)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            ls = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[pp][2 * j], pb[pp][2 * j + 1]}, ones, ls, false);
-        l_run[k] = ls;
-#pragma unroll
-        for (int db = 0; db < S::DBLK; ++db)
-#pragma unroll
-          for (int pp = 0; pp < 2; ++pp)
-            oacc[k][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[db][pp], pb[pp], oacc[k][db], 0, 0, 0);
+        T::softmax(sacc[k & 1], valid, g4, sl, mb_run[k], l_run[k], oacc[k], pb);
+        T::pv(vop, pb, oacc[k]);
+      }
+    }
+    if (sh_live) {
+      switch (wv) {
+        case 0: T::template shared_rest<0>(ssh, vop, valid, g4, sl, mb_sh, l_sh, osh); break;
+        case 1: T::template shared_rest<1>(ssh, vop, valid, g4, sl, mb_sh, l_sh, osh); break;
+        case 2: T::template shared_rest<2>(ssh, vop, valid, g4, sl, mb_sh, l_sh, osh); break;
+        default: T::template shared_rest<3>(ssh, vop, valid, g4, sl, mb_sh, l_sh, osh); break;
       }
     }
   };
@@ -411,39 +565,77 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
     else
       wait_vmcnt<0>();
     block_barrier();
-    compute(sidx, min(KT, tok1 - (tok0 + sidx * KT)));
+    compute(sidx, __builtin_amdgcn_readfirstlane(s_stage[sidx].z));
   }
 
+  // The epilogue reads the accumulators the last stage's MFMAs wrote; give
+  // those MFMAs their result latency regardless of how the loop exit is laid
+  // out (the compiler's wait states were not always inserted across branches).
+  asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+
   // ---- epilogue ----
+  auto store = [&](int tile, float mb, float l, const f32x4 (&o)[S::DBLK]) {
+    const float inv = 1.0f / l;
+    const int row = KVC_Q_TILE * tile + r16;
+    if (row >= st.n_q) return;
+    const int grow = st.q_row0 + row;
+    if (st.n_split == 1) {
+      uint16_t* orow = static_cast<uint16_t*>(p.o) + ((size_t)grow * H + h) * D;
 #pragma unroll
-  for (int k = 0; k < QTW; ++k) {
-    if (k < ntw) {
-      const float l = lane_swap_sum(l_run[k]);
-      const float inv = 1.0f / l;
-      const int row = KVC_Q_TILE * (t_lo + wave + KVC_ATTN_WAVES * k) + r16;
-      if (row < st.n_q) {
-        const int grow = st.q_row0 + row;
-        if (st.n_split == 1) {
-          uint16_t* orow = static_cast<uint16_t*>(p.o) + ((size_t)grow * H + h) * D;
-#pragma unroll
-          for (int db = 0; db < S::DBLK; ++db) {
-            const f32x4 v = oacc[k][db] * inv;
-            bf16x4 b;
-            b[0] = (__bf16)v[0];
-            b[1] = (__bf16)v[1];
-            b[2] = (__bf16)v[2];
-            b[3] = (__bf16)v[3];
-            *reinterpret_cast<bf16x4*>(orow + 16 * db + 4 * g4) = b;
-          }
-        } else {
-          const size_t prow = ((size_t)split * p.rows_cap + grow) * H + h;
-          float* po = p.part_o + prow * D;
-#pragma unroll
-          for (int db = 0; db < S::DBLK; ++db)
-            *reinterpret_cast<f32x4*>(po + 16 * db + 4 * g4) = oacc[k][db] * inv;
-          if (g4 == 0) p.part_lse[prow] = mb_run[k] + __log2f(l);
-        }
+      for (int db = 0; db < S::DBLK; ++db) {
+        const f32x4 v = o[db] * inv;
+        bf16x4 b;
+        b[0] = (__bf16)v[0];
+        b[1] = (__bf16)v[1];
+        b[2] = (__bf16)v[2];
+        b[3] = (__bf16)v[3];
+        *reinterpret_cast<bf16x4*>(orow + 16 * db + 4 * g4) = b;
       }
+    } else {
+      const size_t prow = ((size_t)split * p.rows_cap + grow) * H + h;
+      float* po = p.part_o + prow * D;
+#pragma unroll
+      for (int db = 0; db < S::DBLK; ++db) *reinterpret_cast<f32x4*>(po + 16 * db + 4 * g4) = o[db] * inv;
+      if (g4 == 0) p.part_lse[prow] = mb + __log2f(l);
+    }
+  };
+#pragma unroll
+  for (int k = 0; k < QTW; ++k)
+    if (k < ntw) store(t_lo + wave + KVC_ATTN_WAVES * k, mb_run[k], lane_swap_sum(l_run[k]), oacc[k]);
+
+  if (has_shared) {
+    // merge the four waves' partial states of the shared tile (one split
+    // merge: weights 2^(m_w - max m))
+    constexpr int NV = S::DBLK * 4 + 2;
+    float* xs = reinterpret_cast<float*>(ring);
+    const float lt = lane_swap_sum(l_sh);
+    __syncthreads();   // every wave is done with the ring
+#pragma unroll
+    for (int db = 0; db < S::DBLK; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xs[(wave * 64 + lane) * NV + 4 * db + i] = osh[db][i];
+    xs[(wave * 64 + lane) * NV + S::DBLK * 4] = mb_sh;
+    xs[(wave * 64 + lane) * NV + S::DBLK * 4 + 1] = lt;
+    __syncthreads();
+    if (wave == 0) {
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < KVC_ATTN_WAVES; ++w) M = fmaxf(M, xs[(w * 64 + lane) * NV + S::DBLK * 4]);
+      float lsum = 0.f;
+      f32x4 o[S::DBLK];
+#pragma unroll
+      for (int db = 0; db < S::DBLK; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < KVC_ATTN_WAVES; ++w) {
+        const float* x = xs + (w * 64 + lane) * NV;
+        const float wt = __builtin_amdgcn_exp2f(x[S::DBLK * 4] - M);
+        lsum += wt * x[S::DBLK * 4 + 1];
+#pragma unroll
+        for (int db = 0; db < S::DBLK; ++db)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[db][i] += wt * x[4 * db + i];
+      }
+      store(t_hi - 1, M, lsum, o);
     }
   }
 }
@@ -497,13 +689,13 @@ int launch_attention(const AttnParams& p, int32_t grid, void* s) {
   const hipStream_t hs = (hipStream_t)s;
   switch (p.head_dim) {
     case 32:
-      hipLaunchKernelGGL((attn_kernel<32, 5>), dim3(grid), dim3(256), 0, hs, p);
+      hipLaunchKernelGGL((attn_kernel<32, 4>), dim3(grid), dim3(256), 0, hs, p);
       break;
     case 64:
-      hipLaunchKernelGGL((attn_kernel<64, 5>), dim3(grid), dim3(256), 0, hs, p);
+      hipLaunchKernelGGL((attn_kernel<64, 4>), dim3(grid), dim3(256), 0, hs, p);
       break;
     case 128:
-      hipLaunchKernelGGL((attn_kernel<128, 3>), dim3(grid), dim3(256), 0, hs, p);
+      hipLaunchKernelGGL((attn_kernel<128, 4>), dim3(grid), dim3(256), 0, hs, p);
       break;
     default:
       return (int)hipErrorInvalidValue;

@@ -18,15 +18,17 @@
 #define KVC_PLAN_HEADER_INTS 8
 #define KVC_STREAM_REC_INTS 16
 
-// KV tokens per attention pipeline stage; split boundaries are multiples of it.
+// Slots per attention pipeline stage.  A stage never straddles a page: the
+// work unit is (page, 64-slot chunk of that page's valid slots), so a stage
+// is one contiguous run of slots.  Splits are ranges of units.
 #define KVC_KV_TILE 64
 // Query rows per MFMA tile, and waves per attention work-group.
 #define KVC_Q_TILE 16
 #define KVC_ATTN_WAVES 4
 // Upper bound of KV splits per stream (sizes the partial-output workspace).
 #define KVC_MAX_SPLITS 64
-// Most pages one KV split may span (their IDs are staged in LDS).
-#define KVC_MAX_SPLIT_PAGES 512
+// Most stages (units) one KV split may hold (its stage table lives in LDS).
+#define KVC_MAX_SPLIT_STAGES 512
 // Largest n_s, and the most special pages one frame's specials can touch.
 #define KVC_MAX_SPECIAL_PER_FRAME 64
 #define KVC_MAX_APPEND_SPECIAL_PAGES 8
@@ -46,20 +48,24 @@ typedef struct kvc_dev_stream {
   int32_t last_len;   // valid tokens on the last page
   int32_t kv_len;     // valid visible tokens L
   int32_t patch_tok;  // n_patch * P: first token of the special region
-  int32_t n_units;    // ceil(L / KVC_KV_TILE)
+  int32_t n_units;    // work units: n_patch * upp + full special pages * ups + units of the last page
   int32_t n_split;    // KV splits
   int32_t n_group;    // query groups
   int32_t item0;      // first attention work item of this stream
   int32_t n_items;    // H * n_split * n_group
-  int32_t split_base; // index of this stream's first split slot (always 0: partials are per row)
+  int32_t upp;        // units per patch page, ceil(P / KVC_KV_TILE)
+  int32_t ups;        // units per full special page, ceil(page_size / KVC_KV_TILE)
   int32_t reserved0;
-  int32_t reserved1;
 } kvc_dev_stream;
 
-// Max query tiles (of KVC_Q_TILE rows) one wave holds, per head_dim; a query
-// group spans at most KVC_ATTN_WAVES * this many tiles.
+// Query tiles (of KVC_Q_TILE rows) one wave owns, per head_dim.  A query
+// group spans at most KVC_ATTN_WAVES * this many tiles plus one tile shared
+// by all waves.
 static inline int kvc_tiles_per_wave(int head_dim) {
-  return head_dim <= 64 ? 5 : 3;
+  return head_dim <= 64 ? 4 : 4;
+}
+static inline int kvc_group_tiles(int head_dim) {
+  return KVC_ATTN_WAVES * kvc_tiles_per_wave(head_dim) + 1;
 }
 
 #endif
