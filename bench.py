@@ -22,6 +22,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -31,7 +32,7 @@ if ROOT not in sys.path:
 
 METRIC = "frame-steps/sec (all blocks) + attn TFLOP/s & HBM GB/s vs MI355X peak"
 PEAK_HBM_GBS = 8000.0
-PEAK_BF16_TFLOPS = 2516.6
+PEAK_BF16_TFLOPS = 2500.0
 BANK = 8
 
 
@@ -39,23 +40,35 @@ def progress(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+KERNEL_SOURCES = ("kvc_kernels.hip", "kvc_kernels.h", "kvc_plan_layout.h")
+
+
 def kernel_source_hash():
-    p = os.path.join(ROOT, "paged_kv_cache_kvc_amd", "csrc", "kvc_kernels.hip")
-    with open(p, "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()[:16]
+    """First 16 hex digits of the SHA-256 of the device code's sources."""
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "paged_kv_cache_kvc_amd", "csrc", name), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic(workload):
-    """HBM bytes per attention launch measured by rocprofv3 counters (committed
-    under profiles/), or None when missing or taken on other kernel source."""
-    p = os.path.join(ROOT, "profiles", f"attn_{workload}_traffic.json")
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE, calibrated against a plain copy), or
+    None when it is missing or was taken on other kernel source."""
+    p = os.path.join(ROOT, "profiles", f"attn_kernel_{workload}_hbm_traffic.md")
     if not os.path.exists(p):
         return None
+    fields = {}
     with open(p) as fh:
-        t = json.load(fh)
-    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+        for line in fh:
+            m = re.match(r"^(hbm_bytes_per_launch|kernel_source_sha256_16):\s*(\S+)\s*$", line)
+            if m:
+                fields[m.group(1)] = m.group(2)
+    if fields.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
-    return t.get("hbm_bytes_per_launch")
+    v = fields.get("hbm_bytes_per_launch")
+    return float(v) if v is not None else None
 
 
 def cpu_baseline(wl, seconds):
@@ -102,6 +115,15 @@ def cpu_baseline(wl, seconds):
         if info.get("user_api") == "blas":
             threads = max(threads, int(info.get("num_threads", 1)))
     steps = blocks / wl.num_blocks
+    cpu_model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {
         "value": steps / el,
         "unit": "frame-steps/s",
@@ -109,7 +131,7 @@ def cpu_baseline(wl, seconds):
         "kind": "oracle",
         "sample": (f"{blocks} block(s) of dense float64 oracle attention (gather + softmax) at frame {F}, "
                    f"T={T}, L={L}, H={H}, D={D}; {el:.1f} s on {threads} BLAS thread(s) of "
-                   f"{len(os.sched_getaffinity(0))} available; one block's seeded history reused per block; "
+                   f"{len(os.sched_getaffinity(0))} available ({cpu_model}); one block's seeded history reused per block; "
                    f"frame-steps/s = blocks/{wl.num_blocks}/s"),
         "gflops": 4.0 * T * L * H * D * blocks / el / 1e9,
     }

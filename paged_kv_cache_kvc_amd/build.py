@@ -30,8 +30,9 @@ HIP_FLAGS = [
     # scores are never NaN (masked slots are -inf): max needs no NaN quieting
     "-fno-honor-nans",
 ]
+INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 CXX_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-Wall", "-Wextra", "-Wno-unused-parameter",
-             "-D__HIP_PLATFORM_AMD__", f"-I{ROCM}/include"]
+             "-D__HIP_PLATFORM_AMD__", f"-I{ROCM}/include", f"-I{INCLUDE}"]
 
 
 def _run(cmd, verbose):

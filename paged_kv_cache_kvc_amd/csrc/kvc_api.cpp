@@ -11,7 +11,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/kvc.h"
+#include "kvc.h"
 #include "kvc_host.hpp"
 #include "kvc_kernels.h"
 

@@ -322,7 +322,7 @@ struct TileOps {
 // partial softmax states are merged through LDS at the end.  Every SIMD thus
 // carries the same MFMA work per stage.
 template <int D, int QTW>
-__global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
+__global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams p) {
   using S = Shape<D>;
   using T = TileOps<D>;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[S::NSTAGE * S::STAGE_BYTES];
@@ -643,12 +643,16 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
 // ---------------------------------------------------------------------------
 // merge of KV splits
 // ---------------------------------------------------------------------------
+// One wave per (row, head): lanes are split into groups of D/4 lanes (four
+// floats each); group g accumulates splits g, g + groups, ... weighted by
+// 2^(lse_c - max lse), and the groups are summed by lane exchanges.  The
+// order of every sum is fixed, so the result does not depend on timing.
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
-  constexpr int LPR = D / 4;              // lanes per (row, head), 4 floats each
-  constexpr int PER_BLOCK = 256 / LPR;
-  const int gid = blockIdx.x * PER_BLOCK + (int)threadIdx.x / LPR;
-  const int lr = (int)threadIdx.x % LPR;
+  constexpr int LPR = D / 4;   // lanes per output row
+  constexpr int SG = 64 / LPR; // split groups per wave
+  const int lane = threadIdx.x & 63;
+  const int gid = blockIdx.x * 4 + ((int)threadIdx.x >> 6);
   const int H = p.num_heads;
   const int row = gid / H;
   const int h = gid - row * H;
@@ -659,23 +663,36 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   while (si + 1 < nstreams && row >= recs[si + 1].q_row0) ++si;
   const int nsp = recs[si].n_split;
   if (nsp <= 1) return;
-  float M = -INFINITY;
-  for (int c = 0; c < nsp; ++c) M = fmaxf(M, p.part_lse[((size_t)c * p.rows_cap + row) * H + h]);
+  const size_t stride = (size_t)p.rows_cap * H;
+  const size_t base = (size_t)row * H + h;
+  float m = -INFINITY;
+  for (int c = lane; c < nsp; c += 64) m = fmaxf(m, p.part_lse[c * stride + base]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  const int sg = lane / LPR, lr = lane % LPR;
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
-  for (int c = 0; c < nsp; ++c) {
-    const size_t prow = ((size_t)c * p.rows_cap + row) * H + h;
-    const float w = __builtin_amdgcn_exp2f(p.part_lse[prow] - M);
+#pragma unroll 4
+  for (int c = sg; c < nsp; c += SG) {
+    const size_t prow = c * stride + base;
+    const float w = __builtin_amdgcn_exp2f(p.part_lse[prow] - m);
     acc += w * *reinterpret_cast<const f32x4*>(p.part_o + prow * D + 4 * lr);
     wsum += w;
   }
+#pragma unroll
+  for (int off = LPR; off < 64; off <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] += __shfl_xor(acc[i], off);
+    wsum += __shfl_xor(wsum, off);
+  }
+  if (sg != 0) return;
   const f32x4 v = acc * (1.0f / wsum);
   bf16x4 b;
   b[0] = (__bf16)v[0];
   b[1] = (__bf16)v[1];
   b[2] = (__bf16)v[2];
   b[3] = (__bf16)v[3];
-  *reinterpret_cast<bf16x4*>(static_cast<uint16_t*>(p.o) + ((size_t)row * H + h) * D + 4 * lr) = b;
+  *reinterpret_cast<bf16x4*>(static_cast<uint16_t*>(p.o) + base * D + 4 * lr) = b;
 }
 
 }  // namespace
@@ -689,10 +706,10 @@ int launch_attention(const AttnParams& p, int32_t grid, void* s) {
   const hipStream_t hs = (hipStream_t)s;
   switch (p.head_dim) {
     case 32:
-      hipLaunchKernelGGL((attn_kernel<32, 4>), dim3(grid), dim3(256), 0, hs, p);
+      hipLaunchKernelGGL((attn_kernel<32, KVC_QTW_SMALL_D>), dim3(grid), dim3(256), 0, hs, p);
       break;
     case 64:
-      hipLaunchKernelGGL((attn_kernel<64, 4>), dim3(grid), dim3(256), 0, hs, p);
+      hipLaunchKernelGGL((attn_kernel<64, KVC_QTW_SMALL_D>), dim3(grid), dim3(256), 0, hs, p);
       break;
     case 128:
       hipLaunchKernelGGL((attn_kernel<128, 4>), dim3(grid), dim3(256), 0, hs, p);
@@ -705,8 +722,7 @@ int launch_attention(const AttnParams& p, int32_t grid, void* s) {
 
 int launch_merge(const MergeParams& p, void* s) {
   const hipStream_t hs = (hipStream_t)s;
-  const int per_block = 256 / (p.head_dim / 4);
-  const int grid = (p.num_rows * p.num_heads + per_block - 1) / per_block;
+  const int grid = (p.num_rows * p.num_heads + 3) / 4;   // one wave per (row, head)
   switch (p.head_dim) {
     case 32:
       hipLaunchKernelGGL(merge_kernel<32>, dim3(grid), dim3(256), 0, hs, p);
