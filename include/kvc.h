@@ -132,7 +132,8 @@ const char* kvc_status_string(kvc_status status);
 size_t kvc_pool_bytes(const kvc_config* cfg);
 
 /* Bytes of device workspace the caller allocates for kvc_create: two plan
- * buffers and the split-KV partial outputs (float32), sized for the maximum
+ * buffers and the split-KV partial outputs (normalised bf16 outputs and float32
+ * log-sum-exps), sized for the maximum
  * split count.  Returns 0 for an invalid configuration. */
 size_t kvc_workspace_bytes(const kvc_config* cfg);
 

@@ -49,7 +49,7 @@ Layout layout_of(const kvc::Config& c) {
   l.lse = 2 * l.plan_bytes;
   const size_t rows = (size_t)c.rows_capacity();
   l.part_o = l.lse + align_up((size_t)KVC_MAX_SPLITS * rows * c.num_heads * sizeof(float), 256);
-  l.total = l.part_o + align_up((size_t)KVC_MAX_SPLITS * rows * c.num_heads * c.head_dim * sizeof(float), 256);
+  l.total = l.part_o + align_up((size_t)KVC_MAX_SPLITS * rows * c.num_heads * c.head_dim * sizeof(uint16_t), 256);
   return l;
 }
 
@@ -377,7 +377,7 @@ kvc_status kvc_run(kvc_ctx* c, int32_t block, const void* q, void* o, kvc_stream
 
   const int32_t* dplan = reinterpret_cast<const int32_t*>(c->workspace + (c->plan_buf ? c->lay.plan1 : c->lay.plan0));
   float* lse = reinterpret_cast<float*>(c->workspace + c->lay.lse);
-  float* po = reinterpret_cast<float*>(c->workspace + c->lay.part_o);
+  void* po = c->workspace + c->lay.part_o;
 
   kvc::AttnParams a;
   std::memset(&a, 0, sizeof(a));

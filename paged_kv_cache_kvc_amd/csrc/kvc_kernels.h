@@ -31,7 +31,7 @@ struct AttnParams {
   const void* pool;
   const void* q;            // [R, H, D] bf16
   void* o;                  // [R, H, D] bf16
-  float* part_o;            // [KVC_MAX_SPLITS][rows_cap][H][D]
+  void* part_o;             // [KVC_MAX_SPLITS][rows_cap][H][D] bf16, normalised
   float* part_lse;          // [KVC_MAX_SPLITS][rows_cap][H]
   int32_t num_heads, head_dim, page_size, patch_tokens, rows_cap;
   FastDiv div_patch, div_page;
@@ -41,7 +41,7 @@ struct AttnParams {
 
 struct MergeParams {
   const int32_t* plan;
-  const float* part_o;
+  const void* part_o;       // bf16
   const float* part_lse;
   void* o;
   int32_t num_heads, head_dim, rows_cap, num_rows;

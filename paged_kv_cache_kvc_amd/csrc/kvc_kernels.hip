@@ -110,9 +110,23 @@ struct Shape {
   static constexpr int LOADS_PER_WAVE = LOADS / KVC_ATTN_WAVES;
 };
 
-// 16-byte chunk swizzle inside a K/V row of LDS: keeps the MFMA operand reads
-// of 16 rows spread over the banks.
-__device__ __forceinline__ int swz(int row) { return ((row >> 1) & 1) | (((row >> 3) & 3) << 1); }
+// 16-byte chunk swizzle inside a K/V row of LDS (XORed into the chunk index).
+// Two read patterns must hit distinct banks (64 banks of 4 bytes):
+//  * K operand, ds_read_b128, 16 lanes per pass: one chunk of rows
+//    {8a + j : a, j in 0..3} (+ a multiple of 4): row bits 0, 1, 3, 4 vary;
+//  * V^T operand, ds_read_b64_tr_b16, 32 lanes per pass: the two chunks
+//    2 db + {0, 1} of rows {8 g + j : g in 0..1, j in 0..3}: row bits 0, 1, 3
+//    vary.
+// Rows of a 256-byte bank window that share their bank range (bit 0 for D=128,
+// none below) are separated by the chunk bits the swizzle assigns, so each
+// pattern maps its lanes one-to-one onto the banks.
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  const int b0 = row & 1, b1 = (row >> 1) & 1, b3 = (row >> 3) & 1, b4 = (row >> 4) & 1;
+  if constexpr (D == 32) return b4 | (b3 << 1);
+  else if constexpr (D == 64) return b4 | (b1 << 1) | (b3 << 2);
+  else return b4 | (b0 << 1) | (b1 << 2) | (b3 << 3);
+}
 
 // The ring of stages is filled by direct global->LDS loads that the kernel
 // issues, waits for and publishes itself: the compiler would otherwise treat
@@ -187,144 +201,151 @@ __device__ __forceinline__ float lane_swap_sum(float x) {
   return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
 }
 
-// Rescale threshold of the running maximum, in log2 units of the scaled
-// scores: probabilities up to 2^8 are kept without renormalising.
-constexpr float RESCALE_LOG2 = 8.0f;
+// Lazy renormalisation.  Each query tile keeps a reference value ref in log2
+// units (the running maximum as last renormalised); a stage's probabilities
+// are p = 2^(s * scale - ref), with scale = log2(e)/sqrt(D) applied in fp32 to
+// the exact MFMA scores.  The stage is first exponentiated against the
+// current ref; only when a lane's sum of those probabilities exceeds 2^8 (a
+// score more than a few units above ref, or an overflow to infinity) is it
+// redone against the exact column maximum.  A tile's first stage with a valid
+// slot always takes the exact path.
+constexpr float LAZY_SUM_LIMIT = 256.0f;
 
-// Work of one query tile over one 64-slot stage, in three parts so that
-// the next tile's QK^T MFMAs can be issued before this tile's softmax (the
-// matrix core then runs while the vector unit computes exponentials).
 template <int D>
-struct TileOps {
+struct Ops {
   using S = Shape<D>;
+  static constexpr int KS = S::KSTEPS;
+  static constexpr int DB = S::DBLK;
 
-  // S^T[64 kv x 16 q] = K Q^T for the four 16-kv blocks of the stage
-  static __device__ __forceinline__ void qk(const bf16x8 (&kop)[4][S::KSTEPS], const bf16x8 (&q)[S::KSTEPS],
-                                            f32x4 (&sacc)[4]) {
+  // S^T = K Q^T for the four 16-kv blocks of a stage
+  static __device__ __forceinline__ void qk(const bf16x8 (&kop)[4][KS], const bf16x8 (&q)[KS], f32x4 (&s)[4]) {
 #pragma unroll
     for (int kbi = 0; kbi < 4; ++kbi) {
-      sacc[kbi] = f32x4{0.f, 0.f, 0.f, 0.f};
+      s[kbi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kbi][0], q[0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
-      for (int ks = 0; ks < S::KSTEPS; ++ks)
-        sacc[kbi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kbi][ks], q[ks], sacc[kbi], 0, 0, 0);
+      for (int ks = 1; ks < KS; ++ks)
+        s[kbi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kbi][ks], q[ks], s[kbi], 0, 0, 0);
     }
   }
-
-  // Online softmax of one tile's stage scores (fp32): mask slots past
-  // `valid`, column max over the 64 kv, renormalise only when a column's
-  // maximum grew by more than 2^RESCALE_LOG2, then p = 2^(s*sl - m) rounded
-  // to bf16 into the P^T operand, and the row sums of those bf16 values.
-  static __device__ __forceinline__ void softmax(f32x4 (&sacc)[4], int valid, int g4, float sl, float& mb, float& l,
-                                                 f32x4 (&o)[S::DBLK], bf16x8 (&pb)[2]) {
-    if (valid < KT) {
+  // the same for one 16-kv block
+  static __device__ __forceinline__ void qk1(const bf16x8 (&k)[KS], const bf16x8 (&q)[KS], f32x4 (&s)[1]) {
+    s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k[0], q[0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
-      for (int kbi = 0; kbi < 4; ++kbi)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (32 * (kbi >> 1) + 8 * g4 + 4 * (kbi & 1) + i >= valid) sacc[kbi][i] = -INFINITY;
-    }
-    float mx = max3(sacc[0][0], sacc[0][1], sacc[0][2]);
-    mx = max3(mx, sacc[0][3], sacc[1][0]);
-    mx = max3(mx, sacc[1][1], sacc[1][2]);
-    mx = max3(mx, sacc[1][3], sacc[2][0]);
-    mx = max3(mx, sacc[2][1], sacc[2][2]);
-    mx = max3(mx, sacc[2][3], sacc[3][0]);
-    mx = max3(mx, sacc[3][1], sacc[3][2]);
-    mx = max2(mx, sacc[3][3]);
-    mx = lane_swap_max(mx) * sl;
-    if (__builtin_amdgcn_ballot_w64(mx > mb + RESCALE_LOG2)) {
-      const float nm = fmaxf(mb, mx);
-      const float alpha = __builtin_amdgcn_exp2f(mb - nm);
-      mb = nm;
-      l *= alpha;
-#pragma unroll
-      for (int db = 0; db < S::DBLK; ++db) o[db] *= alpha;
-    }
-#pragma unroll
-    for (int kbi = 0; kbi < 4; ++kbi)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        pb[kbi >> 1][4 * (kbi & 1) + i] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kbi][i], sl, -mb));
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-    for (int pp = 0; pp < 2; ++pp)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        l = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[pp][2 * j], pb[pp][2 * j + 1]}, ones, l, false);
+    for (int ks = 1; ks < KS; ++ks) s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k[ks], q[ks], s[0], 0, 0, 0);
   }
-
-  // O^T[D x 16 q] += V^T P^T
-  static __device__ __forceinline__ void pv(const bf16x8 (&vop)[S::DBLK][2], const bf16x8 (&pb)[2],
-                                            f32x4 (&o)[S::DBLK]) {
+  // O^T[D x 16 q] += V^T P^T over the stage's two 32-kv pairs
+  static __device__ __forceinline__ void pv(const bf16x8 (&vop)[DB][2], const u32x4 (&pb)[2], f32x4 (&o)[DB]) {
 #pragma unroll
-    for (int db = 0; db < S::DBLK; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int pp = 0; pp < 2; ++pp)
-        o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[db][pp], pb[pp], o[db], 0, 0, 0);
+        o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[db][pp], __builtin_bit_cast(bf16x8, pb[pp]), o[db], 0,
+                                                        0, 0);
   }
-
-  // The shared tile on one 16-kv block BLK of the stage (BLK = 2*pair +
-  // half), in two parts like the own tiles: QK^T first (issued one tile
-  // ahead of its use), then softmax over its 4 scores per lane and P.V with
-  // the other half of the pair's P^T operand zero.  A block whose slots are
-  // all past the end of the stage is skipped.
-  template <int BLK>
-  static __device__ __forceinline__ bool block_live(int valid) {
-    return 32 * (BLK >> 1) + 4 * (BLK & 1) < valid;
-  }
-  template <int BLK>
-  static __device__ __forceinline__ f32x4 shared_qk(const bf16x8 (&kop)[4][S::KSTEPS], const bf16x8 (&q)[S::KSTEPS]) {
-    f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+  // ... over one pair
+  template <int PP>
+  static __device__ __forceinline__ void pv1(const bf16x8 (&vop)[DB][2], const u32x4& pb, f32x4 (&o)[DB]) {
 #pragma unroll
-    for (int ks = 0; ks < S::KSTEPS; ++ks)
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[BLK][ks], q[ks], sc, 0, 0, 0);
-    return sc;
-  }
-  template <int BLK>
-  static __device__ __forceinline__ void shared_rest(f32x4 sc, const bf16x8 (&vop)[S::DBLK][2], int valid, int g4,
-                                                     float sl, float& mb, float& l, f32x4 (&o)[S::DBLK]) {
-    constexpr int PP = BLK >> 1, TT = BLK & 1;
-    if (valid < KT) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (32 * PP + 8 * g4 + 4 * TT + i >= valid) sc[i] = -INFINITY;
-    }
-    float mx = max2(max3(sc[0], sc[1], sc[2]), sc[3]);
-    mx = lane_swap_max(mx) * sl;
-    if (__builtin_amdgcn_ballot_w64(mx > mb + RESCALE_LOG2)) {
-      const float nm = fmaxf(mb, mx);
-      const float alpha = __builtin_amdgcn_exp2f(mb - nm);
-      mb = nm;
-      l *= alpha;
-#pragma unroll
-      for (int db = 0; db < S::DBLK; ++db) o[db] *= alpha;
-    }
-    bf16x8 pb;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) pb[j] = (__bf16)0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) pb[4 * TT + i] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], sl, -mb));
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-    l = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[4 * TT], pb[4 * TT + 1]}, ones, l, false);
-    l = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[4 * TT + 2], pb[4 * TT + 3]}, ones, l, false);
-#pragma unroll
-    for (int db = 0; db < S::DBLK; ++db)
-      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[db][PP], pb, o[db], 0, 0, 0);
+    for (int db = 0; db < DB; ++db)
+      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[db][PP], __builtin_bit_cast(bf16x8, pb), o[db], 0, 0, 0);
   }
 };
 
-// Attention over one KV split for one head and one query group.  The group's
-// query tiles are spread over the 4 waves: each wave owns up to QTW tiles
-// (t_lo + wave + 4k); when the group has 4m+1 tiles, the last one is shared:
-// every wave processes one 16-kv block of it in every stage, and the four
-// partial softmax states are merged through LDS at the end.  Every SIMD thus
-// carries the same MFMA work per stage.
-template <int D, int QTW>
+// p = 2^(s * scale - ref) rounded to bf16 and packed in pairs (the P^T
+// operand), and the lane's sum of the rounded values (the same numbers the
+// P.V product uses).
+template <int N>
+__device__ __forceinline__ float probs(const f32x4 (&s)[N], float sl, float nref, uint32_t (&pk)[2 * N]) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  float a = 0.f, b = 0.f;
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const bf16x2 v = {(__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[i][2 * h], sl, nref)),
+                        (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[i][2 * h + 1], sl, nref))};
+      pk[2 * i + h] = __builtin_bit_cast(uint32_t, v);
+      if (h == 0)
+        a = __builtin_amdgcn_fdot2_f32_bf16(v, ones, a, false);
+      else
+        b = __builtin_amdgcn_fdot2_f32_bf16(v, ones, b, false);
+    }
+  return a + b;
+}
+
+// Slots of block kbi held by lane group g4 are 32 (kbi/2) + 8 g4 + 4 (kbi%2)
+// + i; those at or past `valid` get score -inf (probability 0).  lim is
+// valid - 8 g4, made opaque so that the compares stay inside the (rarely
+// taken) branch of a partial stage.
+template <int N>
+__device__ __forceinline__ void mask_scores(f32x4 (&s)[N], const int (&kbi)[N], int valid, int g4) {
+  int lim = valid - 8 * g4;
+  asm volatile("" : "+v"(lim));
+#pragma unroll
+  for (int j = 0; j < N; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (32 * (kbi[j] >> 1) + 4 * (kbi[j] & 1) + i >= lim) s[j][i] = -INFINITY;
+}
+
+// Exact path: column maximum of s * scale - ref over the stage (the four lane groups
+// of a column hold its 64 slots), move ref up to it (while the tile has seen
+// no valid slot yet, `fresh`: set it), scale the running sum and output by
+// 2^-(shift), and recompute the probabilities.  Every column of a block has
+// the same masked slots, so the maximum is -inf in all lanes or in none; a
+// fresh tile whose slots were all masked stays fresh.  Taken rarely; a few
+// wait states at both ends keep it clear of the MFMAs around it.
+template <int N, int DB>
+__device__ __forceinline__ float renorm(const f32x4 (&s)[N], float sl, bool& fresh, float& ref, float& nref,
+                                        float& l, f32x4 (&o)[DB], uint32_t (&pk)[2 * N]) {
+  asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+  float m = s[0][0];
+#pragma unroll
+  for (int j = 0; j < N; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m = max2(m, s[j][i]);
+  m = __builtin_fmaf(lane_swap_max(m), sl, nref);
+  const bool first = fresh;
+  fresh = fresh && __builtin_amdgcn_ballot_w64(m == -INFINITY) != 0;
+  const float shift = first ? (m == -INFINITY ? 0.0f : m) : fmaxf(m, 0.0f);
+  if (!first) {
+    const float alpha = __builtin_amdgcn_exp2f(-shift);
+    l *= alpha;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] *= alpha;
+  }
+  ref += shift;
+  nref = -ref;
+  const float lt = probs<N>(s, sl, nref, pk);
+  asm volatile("s_nop 3" ::: "memory");
+  return lt;
+}
+
+// Attention over one KV split for one head and one query group of up to
+// 4 * 2 + 1 tiles of 16 queries.  Wave w owns tiles t_lo + w and t_lo + w + 4;
+// the ninth tile (if the group has one) is shared: in every stage each wave
+// takes one 16-kv block of it, and the four partial softmax states are merged
+// at the end.  Every wave thus does the same work per stage (2.25 tiles), and
+// the per-stage code is straight-line.
+//
+// Per stage s the wave runs three steps, one per tile (own 0, own 1, shared),
+// each pairing one tile's probabilities (vector unit) with the MFMAs of its
+// neighbours:
+//   step 0: QK(s, own 1)            | probs(s, own 0)   [+ P.V(s-1, shared)]
+//   step 1: QK(s, shared), PV(s, own 0) | probs(s, own 1)
+//   step 2: QK(s+1, own 0), PV(s, own 1) | probs(s, shared)
+// K operands of stage s+1 are read from LDS after step 0 (stage s+1 is
+// published there), V operands of stage s after step 0, the shared block's K
+// of stage s+1 after step 1.  An MFMA result is read by the vector unit one
+// step after its MFMA at the earliest.
+template <int D>
 __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams p) {
   using S = Shape<D>;
-  using T = TileOps<D>;
+  using O = Ops<D>;
+  constexpr int KS = S::KSTEPS;
+  constexpr int DB = S::DBLK;
+  constexpr int LPW = S::LOADS_PER_WAVE;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[S::NSTAGE * S::STAGE_BYTES];
   // per stage of this split: byte offset of its first K row in the pool
   // (lo, hi) and its valid slot count
@@ -360,12 +381,11 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
   const int t_lo = grp * nqt / st.n_group;
   const int t_hi = (grp + 1) * nqt / st.n_group;
   const int ntile = t_hi - t_lo;
-  const bool has_shared = ntile >= 5 && (ntile & 3) == 1;
-  const int n_own = ntile - (has_shared ? 1 : 0);
+  const bool has_shared = ntile == 4 * 2 + 1;
+  const int n_own = has_shared ? 8 : ntile;
   const int u0 = split * st.n_units / st.n_split;
   const int u1 = (split + 1) * st.n_units / st.n_split;
   const int nstage = u1 - u0;
-  const float sl = p.scale_log2;
   const int H = p.num_heads;
   const uint32_t slot_bytes = (uint32_t)H * D * 2;
 
@@ -392,13 +412,14 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
     s_stage[i] = int4{(int)(uint32_t)off, (int)(uint32_t)(off >> 32), min(KT, len - KT * cu), 0};
   }
 
-  // ---- query operands (Q^T as the MFMA B operand) ----
-  auto load_q = [&](int tile, bool ok, bf16x8 (&q)[S::KSTEPS]) {
+  // ---- query operands: Q^T as the MFMA B operand
+  const float sl = p.scale_log2;
+  auto load_q = [&](int tile, bool ok, bf16x8 (&q)[KS]) {
     const int row = KVC_Q_TILE * tile + r16;
     ok = ok && row < st.n_q;
     const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + ((size_t)(st.q_row0 + (ok ? row : 0)) * H + h) * D;
 #pragma unroll
-    for (int ks = 0; ks < S::KSTEPS; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
       q[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks + 8 * g4);
       if (!ok) {
 #pragma unroll
@@ -406,28 +427,21 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
       }
     }
   };
-  int ntw = 0;
-#pragma unroll
-  for (int k = 0; k < QTW; ++k)
-    if (wave + KVC_ATTN_WAVES * k < n_own) ntw = k + 1;
+  bf16x8 q0[KS], q1[KS], q2[KS];
+  load_q(t_lo + wave, wave < n_own, q0);
+  load_q(t_lo + wave + 4, wave + 4 < n_own, q1);
+  load_q(t_hi - 1, has_shared, q2);
 
-  bf16x8 qop[QTW][S::KSTEPS];
-  float mb_run[QTW], l_run[QTW];
-  f32x4 oacc[QTW][S::DBLK];
+  // softmax state of tiles own 0, own 1, shared
+  // ref of each tile and its negation; fresh: no valid slot seen yet (ref
+  // not set)
+  float ref0 = 0.f, ref1 = 0.f, ref2 = 0.f;
+  float nref0 = 0.f, nref1 = 0.f, nref2 = 0.f;
+  bool fresh0 = true, fresh1 = true, fresh2 = true;
+  float l0 = 0.f, l1 = 0.f, l2 = 0.f;
+  f32x4 o0[DB], o1[DB], o2[DB];
 #pragma unroll
-  for (int k = 0; k < QTW; ++k) {
-    load_q(t_lo + wave + KVC_ATTN_WAVES * k, k < ntw, qop[k]);
-    mb_run[k] = -INFINITY;
-    l_run[k] = 0.0f;
-#pragma unroll
-    for (int db = 0; db < S::DBLK; ++db) oacc[k][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  bf16x8 qsh[S::KSTEPS];
-  float mb_sh = -INFINITY, l_sh = 0.0f;
-  f32x4 osh[S::DBLK];
-  load_q(t_hi - 1, has_shared, qsh);
-#pragma unroll
-  for (int db = 0; db < S::DBLK; ++db) osh[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int db = 0; db < DB; ++db) o0[db] = o1[db] = o2[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   __syncthreads();   // stage table ready
 
   // ---- direct global -> LDS loads of one stage (K rows, then V rows) ----
@@ -438,143 +452,187 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
   // valid row (finite data; their scores are masked to -inf).
   const uint8_t* pool = static_cast<const uint8_t*>(p.pool);
   const uint64_t v_half = (uint64_t)p.page_size * slot_bytes;
-  int lrow[S::LOADS_PER_WAVE];
-  uint32_t lofs[S::LOADS_PER_WAVE];
+  // row of the stage that lane fetches for load j, and its offset from the
+  // stage base when every row is valid
+  auto lrow = [&](int j) { return ((wave * LPW + j) % (S::LOADS / 2) * 1024 + lane * 16) / S::ROW_BYTES; };
+  uint32_t vfull[LPW];
 #pragma unroll
-  for (int j = 0; j < S::LOADS_PER_WAVE; ++j) {
-    const int inst = wave * S::LOADS_PER_WAVE + j;
-    const int blk = inst % (S::LOADS / 2);
-    const int off = blk * 1024 + lane * 16;
+  for (int j = 0; j < LPW; ++j) {
+    const int off = (wave * LPW + j) % (S::LOADS / 2) * 1024 + lane * 16;
     const int row = off / S::ROW_BYTES;
     const int pch = (off % S::ROW_BYTES) >> 4;
-    lrow[j] = row;
-    lofs[j] = (uint32_t)((pch ^ (swz(row) & (S::CPR - 1))) << 4);
+    vfull[j] = (uint32_t)row * slot_bytes + (uint32_t)((pch ^ swz<D>(row)) << 4);
   }
+  // LDS byte address of the ring (uniform)
+  const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(lds_addr(ring));
   auto issue = [&](int sidx) {
     const int4 e = s_stage[sidx];
     const uint64_t koff = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(e.x) |
                           ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(e.y) << 32);
     const int valid = __builtin_amdgcn_readfirstlane(e.z);
-    uint8_t* stage = ring + (sidx % S::NSTAGE) * S::STAGE_BYTES;
+    const uint32_t slot = ring_lds + (uint32_t)(sidx % S::NSTAGE) * S::STAGE_BYTES;
 #pragma unroll
-    for (int j = 0; j < S::LOADS_PER_WAVE; ++j) {
-      const int inst = wave * S::LOADS_PER_WAVE + j;
+    for (int j = 0; j < LPW; ++j) {
+      const int inst = wv * LPW + j;
       const int kv = inst >= S::LOADS / 2 ? 1 : 0;
       const int blk = inst - kv * (S::LOADS / 2);
-      const uint32_t vofs = (uint32_t)min(lrow[j], valid - 1) * slot_bytes + lofs[j];
+      uint32_t vofs = vfull[j];
+      if (valid < KT) {
+        const int row = lrow(j);
+        vofs -= (uint32_t)(row - min(row, valid - 1)) * slot_bytes;
+      }
+      // the asm operand must be a scalar register pair
       const uint64_t b = (uint64_t)(uintptr_t)(pool + koff + (kv ? v_half : 0));
       const uint64_t ub = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b) |
                           ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32);
-      load_lds16((const void*)(uintptr_t)ub, vofs,
-                 __builtin_amdgcn_readfirstlane(lds_addr(stage + kv * S::HALF_BYTES + blk * 1024)));
+      load_lds16((const void*)(uintptr_t)ub, vofs, slot + (uint32_t)(kv * S::HALF_BYTES + blk * 1024));
     }
   };
 
-  // ---- one stage of 64 slots for this wave's tiles ----
-  auto compute = [&](int sidx, int valid) {
+  // ---- operand reads from a published stage ----
+  // K operand rows: block kbi (= 2*pair + half) row r16 holds kv
+  // 32*pair + 8*(r16/4) + 4*half + r16%4, so that after the MFMA lane group
+  // g4 holds kv 32*pair + 8*g4 + 4*half + [0, 4) of each query column.
+  // The row of a K operand read is 32*(kbi/2) + 4*(kbi%2) + kr (kr per
+  // lane, bits 0, 1, 3, 4), that of a V read 32*pp + 4*r + vr (vr per lane,
+  // bits 0, 1, 3, 4): the added bits 2 and 5 leave the swizzle unchanged, so
+  // every read is a per-lane offset (one per k-step, or per 16-wide d block)
+  // plus a compile-time constant.
+  const int kr = 8 * (r16 >> 2) + (r16 & 3);
+  const int vr = 8 * g4 + (r16 >> 2);
+  uint32_t kofs[KS], vofs_l[DB];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) kofs[ks] = (uint32_t)(kr * S::ROW_BYTES + (((4 * ks + g4) ^ swz<D>(kr)) << 4));
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+    vofs_l[db] = (uint32_t)(S::HALF_BYTES + vr * S::ROW_BYTES + (((2 * db + ((r16 & 3) >> 1)) ^ swz<D>(vr)) << 4) +
+                            ((r16 & 1) << 3));
+  auto read_k = [&](int sidx, bf16x8 (&kop)[4][KS]) {
     const uint8_t* kb = ring + (sidx % S::NSTAGE) * S::STAGE_BYTES;
-    const uint8_t* vb = kb + S::HALF_BYTES;
-    // K operand rows: block kbi (= 2*pair + half) row r16 holds kv
-    // 32*pair + 8*(r16/4) + 4*half + r16%4, so that after the MFMA lane group
-    // g4 holds kv 32*pair + 8*g4 + [0, 8) of each query column.
-    bf16x8 kop[4][S::KSTEPS];
 #pragma unroll
-    for (int kbi = 0; kbi < 4; ++kbi) {
-      const int kvrow = 32 * (kbi >> 1) + 8 * (r16 >> 2) + 4 * (kbi & 1) + (r16 & 3);
+    for (int kbi = 0; kbi < 4; ++kbi)
 #pragma unroll
-      for (int ks = 0; ks < S::KSTEPS; ++ks) {
-        const int chunk = 4 * ks + g4;
-        kop[kbi][ks] = *reinterpret_cast<const bf16x8*>(kb + kvrow * S::ROW_BYTES +
-                                                        ((chunk ^ (swz(kvrow) & (S::CPR - 1))) << 4));
-      }
-    }
-    // V^T operands by transposing reads of row-major V: lane (g4, r16) gets
-    // V[32*pair + 8*g4 + j][16*db + r16], j = 0..7.
-    bf16x8 vop[S::DBLK][2];
+      for (int ks = 0; ks < KS; ++ks)
+        kop[kbi][ks] =
+            *reinterpret_cast<const bf16x8*>(kb + kofs[ks] + (32 * (kbi >> 1) + 4 * (kbi & 1)) * S::ROW_BYTES);
+  };
+  // the shared tile's block of this wave: kbi = wave
+  const int shconst = (32 * (wv >> 1) + 4 * (wv & 1)) * S::ROW_BYTES;
+  auto read_ksh = [&](int sidx, bf16x8 (&k)[KS]) {
+    const uint8_t* kb = ring + (sidx % S::NSTAGE) * S::STAGE_BYTES + shconst;
 #pragma unroll
-    for (int db = 0; db < S::DBLK; ++db) {
+    for (int ks = 0; ks < KS; ++ks) k[ks] = *reinterpret_cast<const bf16x8*>(kb + kofs[ks]);
+  };
+  // V^T operands by transposing reads of row-major V: lane (g4, r16) gets
+  // V[32*pair + 8*g4 + j][16*db + r16], j = 0..7.
+  auto read_v = [&](int sidx, bf16x8 (&vop)[DB][2]) {
+    const uint8_t* vb = ring + (sidx % S::NSTAGE) * S::STAGE_BYTES;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int pp = 0; pp < 2; ++pp) {
         i16x4 half[2];
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
-          const int row = 32 * pp + 8 * g4 + 4 * r + (r16 >> 2);
-          const int chunk = 2 * db + ((r16 & 3) >> 1);
-          half[r] = ds_read_tr16(vb + row * S::ROW_BYTES + ((chunk ^ (swz(row) & (S::CPR - 1))) << 4) +
-                                 ((r16 & 1) << 3));
-        }
+        for (int r = 0; r < 2; ++r) half[r] = ds_read_tr16(vb + vofs_l[db] + (32 * pp + 4 * r) * S::ROW_BYTES);
         const i16x4 a = half[0], b = half[1];
-        vop[db][pp] = __builtin_bit_cast(bf16x8, (short __attribute__((ext_vector_type(8)))){
-                                                     a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]});
+        vop[db][pp] = __builtin_bit_cast(bf16x8, (short __attribute__((ext_vector_type(8)))){a[0], a[1], a[2], a[3],
+                                                                                             b[0], b[1], b[2], b[3]});
       }
-    }
-    // This wave's block of the shared tile (wave-uniform index).
-    const bool sh_live = has_shared && (wv == 0   ? T::template block_live<0>(valid)
-                                        : wv == 1 ? T::template block_live<1>(valid)
-                                        : wv == 2 ? T::template block_live<2>(valid)
-                                                  : T::template block_live<3>(valid));
-    auto sh_qk = [&]() -> f32x4 {
-      switch (wv) {
-        case 0: return T::template shared_qk<0>(kop, qsh);
-        case 1: return T::template shared_qk<1>(kop, qsh);
-        case 2: return T::template shared_qk<2>(kop, qsh);
-        default: return T::template shared_qk<3>(kop, qsh);
-      }
-    };
-    // Own tiles, software-pipelined: the QK^T of the next tile (or of the
-    // shared block, after the last own tile) is issued before the softmax of
-    // the current one, so no MFMA result is read right after it is issued.
-    f32x4 sacc[2][4];
-    f32x4 ssh = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (ntw > 0)
-      T::qk(kop, qop[0], sacc[0]);
-    else if (sh_live)
-      ssh = sh_qk();
-#pragma unroll
-    for (int k = 0; k < QTW; ++k) {
-      if (k < ntw) {
-        if (k + 1 < ntw)
-          T::qk(kop, qop[k + 1], sacc[(k + 1) & 1]);
-        else if (sh_live)
-          ssh = sh_qk();
-        bf16x8 pb[2];
-        T::softmax(sacc[k & 1], valid, g4, sl, mb_run[k], l_run[k], oacc[k], pb);
-        T::pv(vop, pb, oacc[k]);
-      }
-    }
-    if (sh_live) {
-      switch (wv) {
-        case 0: T::template shared_rest<0>(ssh, vop, valid, g4, sl, mb_sh, l_sh, osh); break;
-        case 1: T::template shared_rest<1>(ssh, vop, valid, g4, sl, mb_sh, l_sh, osh); break;
-        case 2: T::template shared_rest<2>(ssh, vop, valid, g4, sl, mb_sh, l_sh, osh); break;
-        default: T::template shared_rest<3>(ssh, vop, valid, g4, sl, mb_sh, l_sh, osh); break;
-      }
-    }
   };
 
-#pragma unroll
-  for (int d = 0; d < S::DIST; ++d)
-    if (d < nstage) issue(d);
-  for (int sidx = 0; sidx < nstage; ++sidx) {
-    if (sidx + S::DIST < nstage) issue(sidx + S::DIST);
-    const int ahead = min(S::DIST, nstage - 1 - sidx);
-    if (ahead >= 2)
-      wait_vmcnt<2 * S::LOADS_PER_WAVE>();
-    else if (ahead == 1)
-      wait_vmcnt<S::LOADS_PER_WAVE>();
-    else
-      wait_vmcnt<0>();
-    block_barrier();
-    compute(sidx, __builtin_amdgcn_readfirstlane(s_stage[sidx].z));
-  }
+  const int kb_own[4] = {0, 1, 2, 3};
+  const int kb_sh[1] = {wv};
+  const int shPP = wv >> 1, shTT = wv & 1;
 
-  // The epilogue reads the accumulators the last stage's MFMAs wrote; give
-  // those MFMAs their result latency regardless of how the loop exit is laid
-  // out (the compiler's wait states were not always inserted across branches).
-  asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+  bf16x8 kop[4][KS], ksh[KS], vop[DB][2];
+  f32x4 sc0[4], sc1[4], sc2[1];
+  uint32_t pk0[8], pk1[8], pk2[2];
+  u32x4 pbsh = u32x4{0u, 0u, 0u, 0u};
+
+  // ---- prologue: fill the ring, publish stage 0, issue its first QK ----
+#pragma unroll
+  for (int d = 0; d < 3; ++d)
+    if (d < nstage) issue(d);
+  if (nstage >= 3)
+    wait_vmcnt<2 * LPW>();
+  else if (nstage == 2)
+    wait_vmcnt<LPW>();
+  else
+    wait_vmcnt<0>();
+  block_barrier();
+  read_k(0, kop);
+  read_ksh(0, ksh);
+  O::qk(kop, q0, sc0);
+
+  for (int s = 0; s < nstage; ++s) {
+    const int valid = __builtin_amdgcn_readfirstlane(s_stage[s].z);
+    const bool partial = valid < KT;
+    const bool more = s + 1 < nstage;
+
+    // ---- step 0: own tile 0 ----
+    if (partial) mask_scores<4>(sc0, kb_own, valid, g4);
+    if (s > 0) {
+      if (shPP)
+        O::template pv1<1>(vop, pbsh, o2);
+      else
+        O::template pv1<0>(vop, pbsh, o2);
+    }
+    O::qk(kop, q1, sc1);
+    float lt = probs<4>(sc0, sl, nref0, pk0);
+    asm volatile("" ::"v"(lt));   // keep the common path ahead of the branch, next to the MFMAs
+    if (fresh0 || __builtin_amdgcn_ballot_w64(lt > LAZY_SUM_LIMIT)) lt = renorm<4, DB>(sc0, sl, fresh0, ref0, nref0, l0, o0, pk0);
+    l0 += lt;
+    // publish stage s+1, refill the ring slot of stage s-1
+    if (more) {
+      if (s + 2 < nstage)
+        wait_vmcnt<LPW>();
+      else
+        wait_vmcnt<0>();
+      block_barrier();
+      if (s + 3 < nstage) issue(s + 3);
+      read_k(s + 1, kop);
+    }
+    read_v(s, vop);
+
+    // ---- step 1: own tile 1 ----
+    if (partial) mask_scores<4>(sc1, kb_own, valid, g4);
+    O::qk1(ksh, q2, sc2);
+    {
+      u32x4 pb[2] = {u32x4{pk0[0], pk0[1], pk0[2], pk0[3]}, u32x4{pk0[4], pk0[5], pk0[6], pk0[7]}};
+      O::pv(vop, pb, o0);
+    }
+    lt = probs<4>(sc1, sl, nref1, pk1);
+    asm volatile("" ::"v"(lt));
+    if (fresh1 || __builtin_amdgcn_ballot_w64(lt > LAZY_SUM_LIMIT)) lt = renorm<4, DB>(sc1, sl, fresh1, ref1, nref1, l1, o1, pk1);
+    l1 += lt;
+    if (more) read_ksh(s + 1, ksh);
+
+    // ---- step 2: shared tile ----
+    if (partial) mask_scores<1>(sc2, kb_sh, valid, g4);
+    if (more) O::qk(kop, q0, sc0);
+    {
+      u32x4 pb[2] = {u32x4{pk1[0], pk1[1], pk1[2], pk1[3]}, u32x4{pk1[4], pk1[5], pk1[6], pk1[7]}};
+      O::pv(vop, pb, o1);
+    }
+    lt = probs<1>(sc2, sl, nref2, pk2);
+    asm volatile("" ::"v"(lt));
+    if (fresh2 || __builtin_amdgcn_ballot_w64(lt > LAZY_SUM_LIMIT)) lt = renorm<1, DB>(sc2, sl, fresh2, ref2, nref2, l2, o2, pk2);
+    l2 += lt;
+    // P^T of the shared block: its 4 slots sit at positions 4*half..4*half+3
+    // of the pair's operand; the other half is zero
+    pbsh = shTT ? u32x4{0u, 0u, pk2[0], pk2[1]} : u32x4{pk2[0], pk2[1], 0u, 0u};
+  }
+  if (shPP)
+    O::template pv1<1>(vop, pbsh, o2);
+  else
+    O::template pv1<0>(vop, pbsh, o2);
+
+  // The epilogue reads the accumulators the last MFMAs wrote; give those
+  // MFMAs their result latency regardless of how the loop exit is laid out.
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 
   // ---- epilogue ----
-  auto store = [&](int tile, float mb, float l, const f32x4 (&o)[S::DBLK]) {
+  auto store = [&](int tile, float ref, float l, const f32x4 (&o)[DB]) {
     const float inv = 1.0f / l;
     const int row = KVC_Q_TILE * tile + r16;
     if (row >= st.n_q) return;
@@ -582,7 +640,7 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
     if (st.n_split == 1) {
       uint16_t* orow = static_cast<uint16_t*>(p.o) + ((size_t)grow * H + h) * D;
 #pragma unroll
-      for (int db = 0; db < S::DBLK; ++db) {
+      for (int db = 0; db < DB; ++db) {
         const f32x4 v = o[db] * inv;
         bf16x4 b;
         b[0] = (__bf16)v[0];
@@ -592,46 +650,56 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
         *reinterpret_cast<bf16x4*>(orow + 16 * db + 4 * g4) = b;
       }
     } else {
+      // normalised partial output, rounded to bf16 (a convex combination of
+      // V rows, so within V's range), and its log-sum-exp in float32
       const size_t prow = ((size_t)split * p.rows_cap + grow) * H + h;
-      float* po = p.part_o + prow * D;
+      uint16_t* po = static_cast<uint16_t*>(p.part_o) + prow * D;
 #pragma unroll
-      for (int db = 0; db < S::DBLK; ++db) *reinterpret_cast<f32x4*>(po + 16 * db + 4 * g4) = o[db] * inv;
-      if (g4 == 0) p.part_lse[prow] = mb + __log2f(l);
+      for (int db = 0; db < DB; ++db) {
+        const f32x4 v = o[db] * inv;
+        bf16x4 b;
+        b[0] = (__bf16)v[0];
+        b[1] = (__bf16)v[1];
+        b[2] = (__bf16)v[2];
+        b[3] = (__bf16)v[3];
+        *reinterpret_cast<bf16x4*>(po + 16 * db + 4 * g4) = b;
+      }
+      if (g4 == 0) p.part_lse[prow] = ref + __log2f(l);
     }
   };
-#pragma unroll
-  for (int k = 0; k < QTW; ++k)
-    if (k < ntw) store(t_lo + wave + KVC_ATTN_WAVES * k, mb_run[k], lane_swap_sum(l_run[k]), oacc[k]);
+  if (wave < n_own) store(t_lo + wave, ref0, lane_swap_sum(l0), o0);
+  if (wave + 4 < n_own) store(t_lo + wave + 4, ref1, lane_swap_sum(l1), o1);
 
   if (has_shared) {
     // merge the four waves' partial states of the shared tile (one split
-    // merge: weights 2^(m_w - max m))
-    constexpr int NV = S::DBLK * 4 + 2;
+    // merge: weights 2^(ref_w - max ref))
+    constexpr int NV = DB * 4 + 2;
     float* xs = reinterpret_cast<float*>(ring);
-    const float lt = lane_swap_sum(l_sh);
+    const float lt2 = lane_swap_sum(l2);
     __syncthreads();   // every wave is done with the ring
 #pragma unroll
-    for (int db = 0; db < S::DBLK; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) xs[(wave * 64 + lane) * NV + 4 * db + i] = osh[db][i];
-    xs[(wave * 64 + lane) * NV + S::DBLK * 4] = mb_sh;
-    xs[(wave * 64 + lane) * NV + S::DBLK * 4 + 1] = lt;
+      for (int i = 0; i < 4; ++i) xs[(wave * 64 + lane) * NV + 4 * db + i] = o2[db][i];
+    // a wave whose block of the shared tile held no valid slot has l = 0
+    xs[(wave * 64 + lane) * NV + DB * 4] = lt2 > 0.0f ? ref2 : -INFINITY;
+    xs[(wave * 64 + lane) * NV + DB * 4 + 1] = lt2;
     __syncthreads();
     if (wave == 0) {
       float M = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < KVC_ATTN_WAVES; ++w) M = fmaxf(M, xs[(w * 64 + lane) * NV + S::DBLK * 4]);
+      for (int w = 0; w < KVC_ATTN_WAVES; ++w) M = fmaxf(M, xs[(w * 64 + lane) * NV + DB * 4]);
       float lsum = 0.f;
-      f32x4 o[S::DBLK];
+      f32x4 o[DB];
 #pragma unroll
-      for (int db = 0; db < S::DBLK; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int db = 0; db < DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int w = 0; w < KVC_ATTN_WAVES; ++w) {
         const float* x = xs + (w * 64 + lane) * NV;
-        const float wt = __builtin_amdgcn_exp2f(x[S::DBLK * 4] - M);
-        lsum += wt * x[S::DBLK * 4 + 1];
+        const float wt = __builtin_amdgcn_exp2f(x[DB * 4] - M);
+        lsum += wt * x[DB * 4 + 1];
 #pragma unroll
-        for (int db = 0; db < S::DBLK; ++db)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
           for (int i = 0; i < 4; ++i) o[db][i] += wt * x[4 * db + i];
       }
@@ -676,7 +744,8 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   for (int c = sg; c < nsp; c += SG) {
     const size_t prow = c * stride + base;
     const float w = __builtin_amdgcn_exp2f(p.part_lse[prow] - m);
-    acc += w * *reinterpret_cast<const f32x4*>(p.part_o + prow * D + 4 * lr);
+    const bf16x4 x = *reinterpret_cast<const bf16x4*>(static_cast<const uint16_t*>(p.part_o) + prow * D + 4 * lr);
+    acc += w * f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
     wsum += w;
   }
 #pragma unroll
@@ -706,13 +775,13 @@ int launch_attention(const AttnParams& p, int32_t grid, void* s) {
   const hipStream_t hs = (hipStream_t)s;
   switch (p.head_dim) {
     case 32:
-      hipLaunchKernelGGL((attn_kernel<32, KVC_QTW_SMALL_D>), dim3(grid), dim3(256), 0, hs, p);
+      hipLaunchKernelGGL((attn_kernel<32>), dim3(grid), dim3(256), 0, hs, p);
       break;
     case 64:
-      hipLaunchKernelGGL((attn_kernel<64, KVC_QTW_SMALL_D>), dim3(grid), dim3(256), 0, hs, p);
+      hipLaunchKernelGGL((attn_kernel<64>), dim3(grid), dim3(256), 0, hs, p);
       break;
     case 128:
-      hipLaunchKernelGGL((attn_kernel<128, 4>), dim3(grid), dim3(256), 0, hs, p);
+      hipLaunchKernelGGL((attn_kernel<128>), dim3(grid), dim3(256), 0, hs, p);
       break;
     default:
       return (int)hipErrorInvalidValue;

@@ -58,16 +58,11 @@ typedef struct kvc_dev_stream {
   int32_t reserved0;
 } kvc_dev_stream;
 
-// Query tiles (of KVC_Q_TILE rows) one wave owns, per head_dim: two for
-// D <= 64 so that two work-groups fit on a CU (their waves interleave the
-// matrix and vector work), four for D = 128 (one work-group per CU).
-#ifndef KVC_QTW_SMALL_D
-#define KVC_QTW_SMALL_D 2
-#endif
-// A query group spans at most KVC_ATTN_WAVES * this many tiles plus one tile shared
-// by all waves.
+// Query tiles (of KVC_Q_TILE rows) one wave owns.  A query group spans at
+// most KVC_ATTN_WAVES * this many tiles plus one tile shared by all waves.
 static inline int kvc_tiles_per_wave(int head_dim) {
-  return head_dim <= 64 ? KVC_QTW_SMALL_D : 4;
+  (void)head_dim;
+  return 2;
 }
 static inline int kvc_group_tiles(int head_dim) {
   return KVC_ATTN_WAVES * kvc_tiles_per_wave(head_dim) + 1;
