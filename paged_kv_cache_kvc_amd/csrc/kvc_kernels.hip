@@ -332,13 +332,15 @@ __device__ __forceinline__ float renorm(const f32x4 (&s)[N], float sl, bool& fre
 // Per stage s the wave runs three steps, one per tile (own 0, own 1, shared),
 // each pairing one tile's probabilities (vector unit) with the MFMAs of its
 // neighbours:
-//   step 0: QK(s, own 1)            | probs(s, own 0)   [+ P.V(s-1, shared)]
-//   step 1: QK(s, shared), PV(s, own 0) | probs(s, own 1)
-//   step 2: QK(s+1, own 0), PV(s, own 1) | probs(s, shared)
+//   step 0: QK(s, own 1), PV(s-1, own 1), PV(s-1, shared) | probs(s, own 0)
+//   step 1: QK(s, shared), PV(s, own 0)                   | probs(s, own 1)
+//   step 2: QK(s+1, own 0)                                 | probs(s, shared)
 // K operands of stage s+1 are read from LDS after step 0 (stage s+1 is
 // published there), V operands of stage s after step 0, the shared block's K
 // of stage s+1 after step 1.  An MFMA result is read by the vector unit one
-// step after its MFMA at the earliest.
+// step after its MFMA at the earliest.  After the last stage the same code
+// reads a ring slot that holds no stage and computes a QK^T that is never
+// used; every LDS address stays inside the ring.
 template <int D>
 __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams p) {
   using S = Shape<D>;
@@ -567,7 +569,6 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
   for (int s = 0; s < nstage; ++s) {
     const int valid = __builtin_amdgcn_readfirstlane(s_stage[s].z);
     const bool partial = valid < KT;
-    const bool more = s + 1 < nstage;
 
     // ---- step 0: own tile 0 ----
     if (partial) mask_scores<4>(sc0, kb_own, valid, g4);
@@ -576,6 +577,8 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
         O::template pv1<1>(vop, pbsh, o2);
       else
         O::template pv1<0>(vop, pbsh, o2);
+      u32x4 pb[2] = {u32x4{pk1[0], pk1[1], pk1[2], pk1[3]}, u32x4{pk1[4], pk1[5], pk1[6], pk1[7]}};
+      O::pv(vop, pb, o1);
     }
     O::qk(kop, q1, sc1);
     float lt = probs<4>(sc0, sl, nref0, pk0);
@@ -583,15 +586,13 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
     if (fresh0 || __builtin_amdgcn_ballot_w64(lt > LAZY_SUM_LIMIT)) lt = renorm<4, DB>(sc0, sl, fresh0, ref0, nref0, l0, o0, pk0);
     l0 += lt;
     // publish stage s+1, refill the ring slot of stage s-1
-    if (more) {
-      if (s + 2 < nstage)
-        wait_vmcnt<LPW>();
-      else
-        wait_vmcnt<0>();
-      block_barrier();
-      if (s + 3 < nstage) issue(s + 3);
-      read_k(s + 1, kop);
-    }
+    if (s + 2 < nstage)
+      wait_vmcnt<LPW>();
+    else
+      wait_vmcnt<0>();
+    block_barrier();
+    if (s + 3 < nstage) issue(s + 3);
+    read_k(s + 1, kop);
     read_v(s, vop);
 
     // ---- step 1: own tile 1 ----
@@ -605,15 +606,11 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
     asm volatile("" ::"v"(lt));
     if (fresh1 || __builtin_amdgcn_ballot_w64(lt > LAZY_SUM_LIMIT)) lt = renorm<4, DB>(sc1, sl, fresh1, ref1, nref1, l1, o1, pk1);
     l1 += lt;
-    if (more) read_ksh(s + 1, ksh);
+    read_ksh(s + 1, ksh);
 
     // ---- step 2: shared tile ----
     if (partial) mask_scores<1>(sc2, kb_sh, valid, g4);
-    if (more) O::qk(kop, q0, sc0);
-    {
-      u32x4 pb[2] = {u32x4{pk1[0], pk1[1], pk1[2], pk1[3]}, u32x4{pk1[4], pk1[5], pk1[6], pk1[7]}};
-      O::pv(vop, pb, o1);
-    }
+    O::qk(kop, q0, sc0);
     lt = probs<1>(sc2, sl, nref2, pk2);
     asm volatile("" ::"v"(lt));
     if (fresh2 || __builtin_amdgcn_ballot_w64(lt > LAZY_SUM_LIMIT)) lt = renorm<1, DB>(sc2, sl, fresh2, ref2, nref2, l2, o2, pk2);
@@ -626,6 +623,10 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
     O::template pv1<1>(vop, pbsh, o2);
   else
     O::template pv1<0>(vop, pbsh, o2);
+  {
+    u32x4 pb[2] = {u32x4{pk1[0], pk1[1], pk1[2], pk1[3]}, u32x4{pk1[4], pk1[5], pk1[6], pk1[7]}};
+    O::pv(vop, pb, o1);
+  }
 
   // The epilogue reads the accumulators the last MFMAs wrote; give those
   // MFMAs their result latency regardless of how the loop exit is laid out.
