@@ -47,7 +47,8 @@ Layout layout_of(const kvc::Config& c) {
   l.plan0 = 0;
   l.plan1 = l.plan_bytes;
   l.lse = 2 * l.plan_bytes;
-  const size_t rows = (size_t)c.rows_capacity();
+  // partial outputs are stored per query tile of KVC_Q_TILE rows
+  const size_t rows = (size_t)c.tiles_capacity() * KVC_Q_TILE;
   l.part_o = l.lse + align_up((size_t)KVC_MAX_SPLITS * rows * c.num_heads * sizeof(float), 256);
   l.total = l.part_o + align_up((size_t)KVC_MAX_SPLITS * rows * c.num_heads * c.head_dim * sizeof(uint16_t), 256);
   return l;
@@ -391,7 +392,7 @@ kvc_status kvc_run(kvc_ctx* c, int32_t block, const void* q, void* o, kvc_stream
   a.head_dim = cf.head_dim;
   a.page_size = cf.page_size;
   a.patch_tokens = cf.patch_tokens();
-  a.rows_cap = cf.rows_capacity();
+  a.tiles_cap = cf.tiles_capacity();
   a.div_patch = kvc::make_fastdiv((uint32_t)std::max(1, cf.patch_tokens()));
   a.div_page = kvc::make_fastdiv((uint32_t)cf.page_size);
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)cf.head_dim));
@@ -408,8 +409,8 @@ kvc_status kvc_run(kvc_ctx* c, int32_t block, const void* q, void* o, kvc_stream
     m.o = o;
     m.num_heads = cf.num_heads;
     m.head_dim = cf.head_dim;
-    m.rows_cap = cf.rows_capacity();
-    m.num_rows = c->plan.num_rows;
+    m.tiles_cap = cf.tiles_capacity();
+    m.num_tiles = c->plan.num_tiles;
     e = timed(c, KVC_KERNEL_MERGE, hs, [&] { return kvc::launch_merge(m, hs); });
     if (e) return hip_fail(c, e, "merge launch");
   }

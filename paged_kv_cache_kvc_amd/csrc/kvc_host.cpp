@@ -233,6 +233,7 @@ void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const P
     rec.ups = ups;
     rec.n_split = (int32_t)ns;
     rec.n_group = n_group;
+    rec.q_tile0 = i * nqt;
     rec.item0 = item;
     rec.n_items = c.num_heads * (int32_t)ns * n_group;
     item += rec.n_items;
@@ -240,10 +241,12 @@ void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const P
   }
   p.num_items = item;
   p.num_rows = p.qo_indptr.back();
+  p.num_tiles = n * nqt;
   p.image[KVC_HDR_NUM_STREAMS] = n;
   p.image[KVC_HDR_NUM_ITEMS] = item;
   p.image[KVC_HDR_NUM_ROWS] = p.num_rows;
   p.image[KVC_HDR_ANY_SPLIT] = p.any_split ? 1 : 0;
+  p.image[KVC_HDR_NUM_TILES] = p.num_tiles;
   std::copy(p.kv_indices.begin(), p.kv_indices.end(),
             p.image.begin() + KVC_PLAN_HEADER_INTS + (size_t)KVC_STREAM_REC_INTS * n);
 }

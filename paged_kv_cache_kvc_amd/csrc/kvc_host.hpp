@@ -29,6 +29,8 @@ struct Config {
   int32_t patch_tokens() const { return tokens_per_frame - num_special_tokens; }
   int32_t max_num_pages() const { return max_patch_pages + max_special_pages; }
   int32_t rows_capacity() const { return num_streams * tokens_per_frame; }
+  // query tiles of KVC_Q_TILE rows over all streams (split partial outputs)
+  int32_t tiles_capacity() const { return num_streams * ((tokens_per_frame + KVC_Q_TILE - 1) / KVC_Q_TILE); }
 };
 
 // Result codes mirror kvc_status.
@@ -99,6 +101,7 @@ struct HostPlan {
   std::vector<int32_t> image;          // device layout (kvc_plan_layout.h)
   int32_t num_items = 0;
   int32_t num_rows = 0;
+  int32_t num_tiles = 0;
   bool any_split = false;
 };
 

@@ -31,9 +31,13 @@ struct AttnParams {
   const void* pool;
   const void* q;            // [R, H, D] bf16
   void* o;                  // [R, H, D] bf16
-  void* part_o;             // [KVC_MAX_SPLITS][rows_cap][H][D] bf16, normalised
-  float* part_lse;          // [KVC_MAX_SPLITS][rows_cap][H]
-  int32_t num_heads, head_dim, page_size, patch_tokens, rows_cap;
+  // Split partial outputs, per query tile of 16 rows, in the lane order of the
+  // MFMA accumulators so that each store instruction writes 512 contiguous
+  // bytes: part_o[split][head][tile][d block of 16][lane][4] bf16 (normalised;
+  // lane = 16 * (d%16)/4 + row%16), part_lse[split][head][tile][16] float.
+  void* part_o;
+  float* part_lse;
+  int32_t num_heads, head_dim, page_size, patch_tokens, tiles_cap;
   FastDiv div_patch, div_page;
   float scale_log2;         // log2(e) / sqrt(D)
   int32_t num_items, items_per_xcd;
@@ -44,7 +48,7 @@ struct MergeParams {
   const void* part_o;       // bf16
   const float* part_lse;
   void* o;
-  int32_t num_heads, head_dim, rows_cap, num_rows;
+  int32_t num_heads, head_dim, tiles_cap, num_tiles;
 };
 
 // Return 0 on success or the hipError_t value.

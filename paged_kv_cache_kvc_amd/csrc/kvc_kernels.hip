@@ -636,9 +636,28 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
   auto store = [&](int tile, float ref, float l, const f32x4 (&o)[DB]) {
     const float inv = 1.0f / l;
     const int row = KVC_Q_TILE * tile + r16;
+    if (st.n_split > 1) {
+      // normalised partial output, rounded to bf16 (a convex combination of
+      // V rows, so within V's range), and its log-sum-exp in float32; rows
+      // past the stream's queries are stored too (finite; never merged)
+      const size_t pt = ((size_t)split * H + h) * p.tiles_cap + st.q_tile0 + tile;
+      uint16_t* po = static_cast<uint16_t*>(p.part_o) + pt * DB * 256 + lane * 4;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const f32x4 v = o[db] * inv;
+        bf16x4 b;
+        b[0] = (__bf16)v[0];
+        b[1] = (__bf16)v[1];
+        b[2] = (__bf16)v[2];
+        b[3] = (__bf16)v[3];
+        *reinterpret_cast<bf16x4*>(po + db * 256) = b;
+      }
+      if (g4 == 0) p.part_lse[pt * KVC_Q_TILE + r16] = ref + __log2f(l);
+      return;
+    }
     if (row >= st.n_q) return;
     const int grow = st.q_row0 + row;
-    if (st.n_split == 1) {
+    {
       uint16_t* orow = static_cast<uint16_t*>(p.o) + ((size_t)grow * H + h) * D;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
@@ -650,22 +669,6 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
         b[3] = (__bf16)v[3];
         *reinterpret_cast<bf16x4*>(orow + 16 * db + 4 * g4) = b;
       }
-    } else {
-      // normalised partial output, rounded to bf16 (a convex combination of
-      // V rows, so within V's range), and its log-sum-exp in float32
-      const size_t prow = ((size_t)split * p.rows_cap + grow) * H + h;
-      uint16_t* po = static_cast<uint16_t*>(p.part_o) + prow * D;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const f32x4 v = o[db] * inv;
-        bf16x4 b;
-        b[0] = (__bf16)v[0];
-        b[1] = (__bf16)v[1];
-        b[2] = (__bf16)v[2];
-        b[3] = (__bf16)v[3];
-        *reinterpret_cast<bf16x4*>(po + 16 * db + 4 * g4) = b;
-      }
-      if (g4 == 0) p.part_lse[prow] = ref + __log2f(l);
     }
   };
   if (wave < n_own) store(t_lo + wave, ref0, lane_swap_sum(l0), o0);
@@ -712,57 +715,74 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
 // ---------------------------------------------------------------------------
 // merge of KV splits
 // ---------------------------------------------------------------------------
-// One wave per (row, head): lanes are split into groups of D/4 lanes (four
-// floats each); group g accumulates splits g, g + groups, ... weighted by
-// 2^(lse_c - max lse), and the groups are summed by lane exchanges.  The
-// order of every sum is fixed, so the result does not depend on timing.
+// One work-group of 16 waves per (query tile, head).  Wave w takes d block
+// w % DB and split group w / DB (splits g, g + SG, ...); each lane the 4
+// values it holds in every split's partial (the accumulator lane order).  A
+// group folds its splits with weights 2^(lse_c - its max); the groups are then
+// combined through LDS, in group order, so every sum has a fixed order.
 template <int D>
-__global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
-  constexpr int LPR = D / 4;   // lanes per output row
-  constexpr int SG = 64 / LPR; // split groups per wave
+__global__ __launch_bounds__(1024) void merge_kernel(MergeParams p) {
+  constexpr int DB = D / 16;
+  constexpr int SG = 16 / DB;     // split groups
+  __shared__ float xs[SG][DB][6][64];
   const int lane = threadIdx.x & 63;
-  const int gid = blockIdx.x * 4 + ((int)threadIdx.x >> 6);
+  const int wave = threadIdx.x >> 6;
+  const int db = wave % DB, sg = wave / DB;
   const int H = p.num_heads;
-  const int row = gid / H;
-  const int h = gid - row * H;
-  if (row >= p.num_rows) return;
+  const int gt = blockIdx.x / H;          // global query tile
+  const int h = blockIdx.x - gt * H;
+  if (gt >= p.num_tiles) return;          // uniform over the work-group
   const int nstreams = p.plan[KVC_HDR_NUM_STREAMS];
   const kvc_dev_stream* recs = reinterpret_cast<const kvc_dev_stream*>(p.plan + KVC_PLAN_HEADER_INTS);
   int si = 0;
-  while (si + 1 < nstreams && row >= recs[si + 1].q_row0) ++si;
-  const int nsp = recs[si].n_split;
-  if (nsp <= 1) return;
-  const size_t stride = (size_t)p.rows_cap * H;
-  const size_t base = (size_t)row * H + h;
+  while (si + 1 < nstreams && gt >= recs[si + 1].q_tile0) ++si;
+  const kvc_dev_stream st = recs[si];
+  const int nsp = st.n_split;
+  if (nsp <= 1) return;                   // uniform over the work-group
+  const int r16 = lane & 15, g4 = lane >> 4;
+  const size_t tstride = (size_t)H * p.tiles_cap;   // between splits, in tiles
+  const size_t t0 = (size_t)h * p.tiles_cap + gt;
   float m = -INFINITY;
-  for (int c = lane; c < nsp; c += 64) m = fmaxf(m, p.part_lse[c * stride + base]);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  const int sg = lane / LPR, lr = lane % LPR;
+  for (int c = sg; c < nsp; c += SG) m = fmaxf(m, p.part_lse[(c * tstride + t0) * KVC_Q_TILE + r16]);
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
-#pragma unroll 4
   for (int c = sg; c < nsp; c += SG) {
-    const size_t prow = c * stride + base;
-    const float w = __builtin_amdgcn_exp2f(p.part_lse[prow] - m);
-    const bf16x4 x = *reinterpret_cast<const bf16x4*>(static_cast<const uint16_t*>(p.part_o) + prow * D + 4 * lr);
+    const size_t pt = c * tstride + t0;
+    const float w = __builtin_amdgcn_exp2f(p.part_lse[pt * KVC_Q_TILE + r16] - m);
+    const bf16x4 x =
+        *reinterpret_cast<const bf16x4*>(static_cast<const uint16_t*>(p.part_o) + (pt * DB + db) * 256 + lane * 4);
     acc += w * f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
     wsum += w;
   }
+  xs[sg][db][0][lane] = m;
+  xs[sg][db][1][lane] = wsum;
 #pragma unroll
-  for (int off = LPR; off < 64; off <<= 1) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] += __shfl_xor(acc[i], off);
-    wsum += __shfl_xor(wsum, off);
-  }
+  for (int i = 0; i < 4; ++i) xs[sg][db][2 + i][lane] = acc[i];
+  __syncthreads();
   if (sg != 0) return;
-  const f32x4 v = acc * (1.0f / wsum);
-  bf16x4 b;
-  b[0] = (__bf16)v[0];
-  b[1] = (__bf16)v[1];
-  b[2] = (__bf16)v[2];
-  b[3] = (__bf16)v[3];
-  *reinterpret_cast<bf16x4*>(static_cast<uint16_t*>(p.o) + base * D + 4 * lr) = b;
+  float M = -INFINITY;
+#pragma unroll
+  for (int g = 0; g < SG; ++g) M = fmaxf(M, xs[g][db][0][lane]);
+  f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
+  float tw = 0.f;
+#pragma unroll
+  for (int g = 0; g < SG; ++g) {
+    const float wg = xs[g][db][1][lane] > 0.f ? __builtin_amdgcn_exp2f(xs[g][db][0][lane] - M) : 0.f;
+    tw += wg * xs[g][db][1][lane];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t[i] += wg * xs[g][db][2 + i][lane];
+  }
+  const int row = KVC_Q_TILE * (gt - st.q_tile0) + r16;
+  if (row < st.n_q) {
+    const f32x4 v = t * (1.0f / tw);
+    bf16x4 b;
+    b[0] = (__bf16)v[0];
+    b[1] = (__bf16)v[1];
+    b[2] = (__bf16)v[2];
+    b[3] = (__bf16)v[3];
+    *reinterpret_cast<bf16x4*>(static_cast<uint16_t*>(p.o) + ((size_t)(st.q_row0 + row) * H + h) * D + 16 * db +
+                               4 * g4) = b;
+  }
 }
 
 }  // namespace
@@ -792,16 +812,16 @@ int launch_attention(const AttnParams& p, int32_t grid, void* s) {
 
 int launch_merge(const MergeParams& p, void* s) {
   const hipStream_t hs = (hipStream_t)s;
-  const int grid = (p.num_rows * p.num_heads + 3) / 4;   // one wave per (row, head)
+  const int grid = p.num_tiles * p.num_heads;   // one work-group per (query tile, head)
   switch (p.head_dim) {
     case 32:
-      hipLaunchKernelGGL(merge_kernel<32>, dim3(grid), dim3(256), 0, hs, p);
+      hipLaunchKernelGGL(merge_kernel<32>, dim3(grid), dim3(1024), 0, hs, p);
       break;
     case 64:
-      hipLaunchKernelGGL(merge_kernel<64>, dim3(grid), dim3(256), 0, hs, p);
+      hipLaunchKernelGGL(merge_kernel<64>, dim3(grid), dim3(1024), 0, hs, p);
       break;
     case 128:
-      hipLaunchKernelGGL(merge_kernel<128>, dim3(grid), dim3(256), 0, hs, p);
+      hipLaunchKernelGGL(merge_kernel<128>, dim3(grid), dim3(1024), 0, hs, p);
       break;
     default:
       return (int)hipErrorInvalidValue;

@@ -38,6 +38,7 @@
 #define KVC_HDR_NUM_ITEMS 1
 #define KVC_HDR_NUM_ROWS 2
 #define KVC_HDR_ANY_SPLIT 3
+#define KVC_HDR_NUM_TILES 4
 
 typedef struct kvc_dev_stream {
   int32_t q_row0;     // first query/output row of this stream
@@ -55,7 +56,7 @@ typedef struct kvc_dev_stream {
   int32_t n_items;    // H * n_split * n_group
   int32_t upp;        // units per patch page, ceil(P / KVC_KV_TILE)
   int32_t ups;        // units per full special page, ceil(page_size / KVC_KV_TILE)
-  int32_t reserved0;
+  int32_t q_tile0;    // first query tile of this stream in the split partial outputs
 } kvc_dev_stream;
 
 // Query tiles (of KVC_Q_TILE rows) one wave owns.  A query group spans at
