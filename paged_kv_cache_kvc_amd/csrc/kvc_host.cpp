@@ -34,14 +34,6 @@ int validate(const Config& c, std::string* why) {
   if (pages * c.page_size >= (int64_t)1 << 31) return fail(ERR_UNSUPPORTED, "pool slots per block must be < 2^31");
   if ((int64_t)c.num_heads * c.head_dim > 65536) return fail(ERR_UNSUPPORTED, "num_heads * head_dim above 65536");
   if ((int64_t)c.num_streams * c.tokens_per_frame >= (int64_t)1 << 24) return fail(ERR_UNSUPPORTED, "too many query rows");
-  {
-    // the longest possible visible stream must fit KVC_MAX_SPLITS splits of
-    // at most KVC_MAX_SPLIT_STAGES units each
-    const int64_t units = (int64_t)c.max_patch_pages * ceil_div(std::max(1, c.patch_tokens()), KVC_KV_TILE) +
-                          (int64_t)c.max_special_pages * ceil_div(c.page_size, KVC_KV_TILE);
-    if (ceil_div(units, KVC_MAX_SPLIT_STAGES) > KVC_MAX_SPLITS)
-      return fail(ERR_UNSUPPORTED, "too many pages for the split limits");
-  }
   return OK;
 }
 
@@ -153,8 +145,18 @@ int32_t Allocator::last_page_len(int s) const {
   return cfg_.patch_tokens();
 }
 
+// Upper bound of the work units over all planned streams: each stream sees at
+// most scale + window patch pages; the special pages are shared out.
+static size_t max_units(const Config& c) {
+  const size_t upp = (size_t)ceil_div(std::max(1, c.patch_tokens()), KVC_KV_TILE);
+  const size_t ups = (size_t)ceil_div(c.page_size, KVC_KV_TILE);
+  return (size_t)c.num_streams * (c.scale_frames + c.sliding_window) * upp + (size_t)c.max_special_pages * ups +
+         (size_t)c.num_streams;
+}
+
 size_t plan_image_ints(const Config& c) {
-  return KVC_PLAN_HEADER_INTS + (size_t)KVC_STREAM_REC_INTS * c.num_streams + (size_t)c.max_num_pages();
+  return KVC_PLAN_HEADER_INTS + (size_t)KVC_STREAM_REC_INTS * c.num_streams + (size_t)c.max_num_pages() + 4 +
+         (size_t)KVC_UNIT_INTS * max_units(c);
 }
 
 void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const PlanPolicy& pol, HostPlan* out) {
@@ -213,8 +215,6 @@ void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const P
                                 : 1.0;
     int64_t ns = (int64_t)std::llround(want);
     ns = std::max<int64_t>(1, std::min<int64_t>(ns, std::min<int64_t>(max_splits, units)));
-    // a split's stage table lives in LDS: at most KVC_MAX_SPLIT_STAGES units
-    ns = std::max<int64_t>(ns, ceil_div(units, KVC_MAX_SPLIT_STAGES));
     p.n_split.push_back((int32_t)ns);
     if (ns > 1) p.any_split = true;
 
@@ -227,7 +227,7 @@ void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const P
     rec.n_pages = p.kv_indptr[i + 1] - p.kv_indptr[i];
     rec.last_len = p.last_page_len[i];
     rec.kv_len = (int32_t)kv_len[i];
-    rec.patch_tok = rec.n_patch * P;
+    rec.unit0 = 0;   // set below, once the page tables are in place
     rec.n_units = (int32_t)units;
     rec.upp = upp;
     rec.ups = ups;
@@ -249,6 +249,43 @@ void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const P
   p.image[KVC_HDR_NUM_TILES] = p.num_tiles;
   std::copy(p.kv_indices.begin(), p.kv_indices.end(),
             p.image.begin() + KVC_PLAN_HEADER_INTS + (size_t)KVC_STREAM_REC_INTS * n);
+
+  // Unit tables: unit u of a stream is the 64-slot chunk cu of visible page
+  // pi.  Patch pages hold P valid slots, special pages page_size, the last
+  // page last_page_len ([p1] "How FlashInfer KV Cache Attention Accelerates
+  // Streaming 3D Reconstruction Over SDPA" §Efficient Attention Masking and
+  // Padding: lengths, not masks, delimit the valid tokens).
+  const uint64_t slot_bytes = (uint64_t)c.num_heads * c.head_dim * 2;
+  size_t at = (p.image.size() + 3) & ~(size_t)3;
+  for (int i = 0; i < n; ++i) {
+    kvc_dev_stream* rec = reinterpret_cast<kvc_dev_stream*>(&p.image[KVC_PLAN_HEADER_INTS + (size_t)KVC_STREAM_REC_INTS * i]);
+    kvc_dev_stream r;
+    std::memcpy(&r, rec, sizeof(r));
+    r.unit0 = (int32_t)at;
+    std::memcpy(rec, &r, sizeof(r));
+    p.image.resize(at + (size_t)KVC_UNIT_INTS * r.n_units, 0);
+    const int32_t* idx = &p.kv_indices[p.kv_indptr[i]];
+    const int32_t patch_units = r.n_patch * r.upp;
+    for (int32_t u = 0; u < r.n_units; ++u) {
+      int32_t pi, cu;
+      if (u < patch_units) {
+        pi = u / r.upp;
+        cu = u - pi * r.upp;
+      } else {
+        const int32_t pj = (u - patch_units) / r.ups;
+        pi = r.n_patch + pj;
+        cu = u - patch_units - pj * r.ups;
+      }
+      const int32_t len = pi == r.n_pages - 1 ? r.last_len : (pi < r.n_patch ? P : c.page_size);
+      const uint64_t off = ((uint64_t)idx[pi] * 2 * c.page_size + (uint64_t)KVC_KV_TILE * cu) * slot_bytes;
+      int32_t* e = &p.image[at + (size_t)KVC_UNIT_INTS * u];
+      e[0] = (int32_t)(uint32_t)off;
+      e[1] = (int32_t)(uint32_t)(off >> 32);
+      e[2] = std::min<int32_t>(KVC_KV_TILE, len - KVC_KV_TILE * cu);
+      e[3] = 0;
+    }
+    at += (size_t)KVC_UNIT_INTS * r.n_units;
+  }
 }
 
 }  // namespace kvc

@@ -141,6 +141,19 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
+// One work-unit entry of the plan (16 bytes at a wave-uniform address) read
+// into scalar registers.  The load completes asynchronously: unit_wait must
+// run before the value is used (it names the registers, so every use follows
+// it).  Scalar loads share the lgkm counter with LDS reads; an extra scalar
+// load in flight only makes the compiler's own LDS waits stricter.
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 unit_load(const int32_t* entry) {
+  i32x4 e;
+  asm volatile("s_load_dwordx4 %0, %1, 0x0" : "=s"(e) : "s"(entry) : "memory");
+  return e;
+}
+__device__ __forceinline__ void unit_wait(i32x4& e) { asm volatile("s_waitcnt lgkmcnt(0)" : "+s"(e)::"memory"); }
+
 // 16 bytes from base + offset (per lane) to LDS byte address
 // lds_base + 16 * lane.  base is wave-uniform (scalar registers).
 __device__ __forceinline__ void load_lds16(const void* base, uint32_t offset, uint32_t lds_base) {
@@ -349,9 +362,6 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
   constexpr int DB = S::DBLK;
   constexpr int LPW = S::LOADS_PER_WAVE;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[S::NSTAGE * S::STAGE_BYTES];
-  // per stage of this split: byte offset of its first K row in the pool
-  // (lo, hi) and its valid slot count
-  __shared__ int4 s_stage[KVC_MAX_SPLIT_STAGES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -371,7 +381,6 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
   int si = 0;
   while (si + 1 < nstreams && item >= recs[si + 1].item0) ++si;
   const kvc_dev_stream st = recs[si];
-  const int32_t* kvidx = p.plan + KVC_PLAN_HEADER_INTS + KVC_STREAM_REC_INTS * nstreams + st.page0;
 
   int local = item - st.item0;
   const int grp = local % st.n_group;
@@ -391,28 +400,10 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
   const int H = p.num_heads;
   const uint32_t slot_bytes = (uint32_t)H * D * 2;
 
-  // Stage table of this split.  Unit u is the 64-slot chunk cu of visible
-  // page pi: patch pages hold P valid slots, special pages page_size, the
-  // last page last_len ([p1] "How FlashInfer KV Cache Attention Accelerates
-  // Streaming 3D Reconstruction Over SDPA" §Efficient Attention Masking and
-  // Padding: lengths, not masks, delimit the valid tokens).
-  for (int i = tid; i < nstage; i += 256) {
-    const int u = u0 + i;
-    const int patch_units = st.n_patch * st.upp;
-    int pi, cu;
-    if (u < patch_units) {
-      pi = u / st.upp;
-      cu = u - pi * st.upp;
-    } else {
-      const int pj = (u - patch_units) / st.ups;
-      pi = st.n_patch + pj;
-      cu = u - patch_units - pj * st.ups;
-    }
-    const int len = pi == st.n_pages - 1 ? st.last_len : (pi < st.n_patch ? p.patch_tokens : p.page_size);
-    const uint64_t off = (((uint64_t)kvidx[pi] * 2) * p.page_size + (uint64_t)KT * cu) * slot_bytes +
-                         (uint64_t)h * D * 2;
-    s_stage[i] = int4{(int)(uint32_t)off, (int)(uint32_t)(off >> 32), min(KT, len - KT * cu), 0};
-  }
+  // This split's work units: entry i describes stage i (the host planner
+  // resolved pages, chunks and valid lengths).
+  const int32_t* units = p.plan + st.unit0 + KVC_UNIT_INTS * u0;
+  const uint64_t head_off = (uint64_t)h * D * 2;
 
   // ---- query operands: Q^T as the MFMA B operand
   const float sl = p.scale_log2;
@@ -444,7 +435,6 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
   f32x4 o0[DB], o1[DB], o2[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) o0[db] = o1[db] = o2[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  __syncthreads();   // stage table ready
 
   // ---- direct global -> LDS loads of one stage (K rows, then V rows) ----
   // Load instruction i of a stage fills 1 KiB of LDS, lane l writing bytes
@@ -467,11 +457,9 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
   }
   // LDS byte address of the ring (uniform)
   const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(lds_addr(ring));
-  auto issue = [&](int sidx) {
-    const int4 e = s_stage[sidx];
-    const uint64_t koff = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(e.x) |
-                          ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(e.y) << 32);
-    const int valid = __builtin_amdgcn_readfirstlane(e.z);
+  auto issue = [&](int sidx, const i32x4& e) {
+    const uint64_t koff = ((uint64_t)(uint32_t)e.x | ((uint64_t)(uint32_t)e.y << 32)) + head_off;
+    const int valid = e.z;
     const uint32_t slot = ring_lds + (uint32_t)(sidx % S::NSTAGE) * S::STAGE_BYTES;
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
@@ -483,11 +471,7 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
         const int row = lrow(j);
         vofs -= (uint32_t)(row - min(row, valid - 1)) * slot_bytes;
       }
-      // the asm operand must be a scalar register pair
-      const uint64_t b = (uint64_t)(uintptr_t)(pool + koff + (kv ? v_half : 0));
-      const uint64_t ub = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b) |
-                          ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32);
-      load_lds16((const void*)(uintptr_t)ub, vofs, slot + (uint32_t)(kv * S::HALF_BYTES + blk * 1024));
+      load_lds16(pool + koff + (kv ? v_half : 0), vofs, slot + (uint32_t)(kv * S::HALF_BYTES + blk * 1024));
     }
   };
 
@@ -552,9 +536,17 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
   u32x4 pbsh = u32x4{0u, 0u, 0u, 0u};
 
   // ---- prologue: fill the ring, publish stage 0, issue its first QK ----
-#pragma unroll
-  for (int d = 0; d < 3; ++d)
-    if (d < nstage) issue(d);
+  // Unit entries are read three stages ahead; vq holds the valid counts of
+  // stages s, s+1, s+2.
+  i32x4 e0 = unit_load(units), e1 = unit_load(units + KVC_UNIT_INTS * min(1, nstage - 1)),
+        e2 = unit_load(units + KVC_UNIT_INTS * min(2, nstage - 1));
+  unit_wait(e0);
+  unit_wait(e1);
+  unit_wait(e2);
+  issue(0, e0);
+  if (nstage > 1) issue(1, e1);
+  if (nstage > 2) issue(2, e2);
+  int vq0 = e0.z, vq1 = e1.z, vq2 = e2.z;
   if (nstage >= 3)
     wait_vmcnt<2 * LPW>();
   else if (nstage == 2)
@@ -567,8 +559,9 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
   O::qk(kop, q0, sc0);
 
   for (int s = 0; s < nstage; ++s) {
-    const int valid = __builtin_amdgcn_readfirstlane(s_stage[s].z);
+    const int valid = vq0;
     const bool partial = valid < KT;
+    i32x4 en = unit_load(units + KVC_UNIT_INTS * min(s + 3, nstage - 1));
 
     // ---- step 0: own tile 0 ----
     if (partial) mask_scores<4>(sc0, kb_own, valid, g4);
@@ -591,7 +584,11 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
     else
       wait_vmcnt<0>();
     block_barrier();
-    if (s + 3 < nstage) issue(s + 3);
+    unit_wait(en);
+    if (s + 3 < nstage) issue(s + 3, en);
+    vq0 = vq1;
+    vq1 = vq2;
+    vq2 = en.z;
     read_k(s + 1, kop);
     read_v(s, vop);
 

@@ -10,6 +10,9 @@
 //   [.., + KVC_STREAM_REC_INTS * num_streams)      one record per planned stream
 //   [.., + total visible pages)                    kv_indices: concatenated page
 //                                                  tables, scale -> live -> special
+//   [aligned to 4 ints, + 4 * total units)         unit tables: per stream, per
+//                                                  64-slot work unit in table order,
+//                                                  {K byte offset lo, hi, valid slots, 0}
 #ifndef KVC_PLAN_LAYOUT_H
 #define KVC_PLAN_LAYOUT_H
 
@@ -27,8 +30,9 @@
 #define KVC_ATTN_WAVES 4
 // Upper bound of KV splits per stream (sizes the partial-output workspace).
 #define KVC_MAX_SPLITS 64
-// Most stages (units) one KV split may hold (its stage table lives in LDS).
-#define KVC_MAX_SPLIT_STAGES 512
+// Ints per work-unit entry: byte offset of the unit's first K row of head 0
+// in the block's pool (64 bits), its valid slot count, padding.
+#define KVC_UNIT_INTS 4
 // Largest n_s, and the most special pages one frame's specials can touch.
 #define KVC_MAX_SPECIAL_PER_FRAME 64
 #define KVC_MAX_APPEND_SPECIAL_PAGES 8
@@ -48,7 +52,7 @@ typedef struct kvc_dev_stream {
   int32_t n_pages;    // pages in the table
   int32_t last_len;   // valid tokens on the last page
   int32_t kv_len;     // valid visible tokens L
-  int32_t patch_tok;  // n_patch * P: first token of the special region
+  int32_t unit0;      // offset in ints of this stream's unit table from the plan start
   int32_t n_units;    // work units: n_patch * upp + full special pages * ups + units of the last page
   int32_t n_split;    // KV splits
   int32_t n_group;    // query groups
