@@ -287,19 +287,19 @@ __device__ __forceinline__ float probs(const f32x4 (&s)[N], float sl, float nref
   return a + b;
 }
 
-// Slots of block kbi held by lane group g4 are 32 (kbi/2) + 8 g4 + 4 (kbi%2)
-// + i; those at or past `valid` get score -inf (probability 0).  lim is
-// valid - 8 g4, made opaque so that the compares stay inside the (rarely
-// taken) branch of a partial stage.
+// Slots of score block j held by lane group g4 are boff[j] + 8 g4 + i (boff
+// is the block's first slot); those at or past `valid` get score -inf
+// (probability 0).  lim is valid - 8 g4, made opaque so that the compares
+// stay inside the (rarely taken) branch of a partial stage.
 template <int N>
-__device__ __forceinline__ void mask_scores(f32x4 (&s)[N], const int (&kbi)[N], int valid, int g4) {
+__device__ __forceinline__ void mask_scores(f32x4 (&s)[N], const int (&boff)[N], int valid, int g4) {
   int lim = valid - 8 * g4;
   asm volatile("" : "+v"(lim));
 #pragma unroll
   for (int j = 0; j < N; ++j)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (32 * (kbi[j] >> 1) + 4 * (kbi[j] & 1) + i >= lim) s[j][i] = -INFINITY;
+      if (boff[j] + i >= lim) s[j][i] = -INFINITY;
 }
 
 // Exact path: column maximum of s * scale - ref over the stage (the four lane groups
@@ -369,6 +369,7 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
   const int wv = __builtin_amdgcn_readfirstlane(wave);   // same value, known uniform
   const int r16 = lane & 15;
   const int g4 = lane >> 4;
+  const int shPP = wv >> 1, shTT = wv & 1;   // pair and half of this wave's shared block
 
   // Work-groups are dispatched round-robin over the 8 XCDs; give each XCD a
   // contiguous range of work items so one head's splits share an L2.
@@ -479,38 +480,48 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
   // K operand rows: block kbi (= 2*pair + half) row r16 holds kv
   // 32*pair + 8*(r16/4) + 4*half + r16%4, so that after the MFMA lane group
   // g4 holds kv 32*pair + 8*g4 + 4*half + [0, 4) of each query column.
-  // The row of a K operand read is 32*(kbi/2) + 4*(kbi%2) + kr (kr per
-  // lane, bits 0, 1, 3, 4), that of a V read 32*pp + 4*r + vr (vr per lane,
-  // bits 0, 1, 3, 4): the added bits 2 and 5 leave the swizzle unchanged, so
-  // every read is a per-lane offset (one per k-step, or per 16-wide d block)
-  // plus a compile-time constant.
+  // The shared tile's block of wave w is the 16 slots 32*(w/2) + 4*(w%2) +
+  // {8 g + i}.  A wave whose block lies in the second 32-slot pair swaps the
+  // two pairs in all its operands: operand pair p holds slots of pair
+  // p ^ shPP, in the K rows (hence in the scores and the P^T operand) and in
+  // V^T alike, so every product is unchanged and the shared block's V^T is
+  // always operand pair 0.
+  //
+  // The row of a K operand read is 32*pair + 4*(kbi%2) + kr (kr per lane,
+  // bits 0, 1, 3, 4), that of a V read 32*pair + 4*r + vr (vr per lane, bits
+  // 0, 1, 3, 4): the added bits 2 and 5 leave the swizzle unchanged, so every
+  // read is a per-lane offset plus a compile-time constant.
   const int kr = 8 * (r16 >> 2) + (r16 & 3);
   const int vr = 8 * g4 + (r16 >> 2);
-  uint32_t kofs[KS], vofs_l[DB];
+  uint32_t kofs[2][KS], kshofs[KS], vofs_l[2][DB];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) kofs[ks] = (uint32_t)(kr * S::ROW_BYTES + (((4 * ks + g4) ^ swz<D>(kr)) << 4));
+  for (int pp = 0; pp < 2; ++pp) {
+    const int pair_rows = 32 * (pp ^ shPP) * S::ROW_BYTES;
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
-    vofs_l[db] = (uint32_t)(S::HALF_BYTES + vr * S::ROW_BYTES + (((2 * db + ((r16 & 3) >> 1)) ^ swz<D>(vr)) << 4) +
-                            ((r16 & 1) << 3));
+    for (int ks = 0; ks < KS; ++ks)
+      kofs[pp][ks] = (uint32_t)(pair_rows + kr * S::ROW_BYTES + (((4 * ks + g4) ^ swz<D>(kr)) << 4));
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      vofs_l[pp][db] = (uint32_t)(pair_rows + S::HALF_BYTES + vr * S::ROW_BYTES +
+                                  (((2 * db + ((r16 & 3) >> 1)) ^ swz<D>(vr)) << 4) + ((r16 & 1) << 3));
+  }
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) kshofs[ks] = kofs[0][ks] + 4 * shTT * S::ROW_BYTES;
   auto read_k = [&](int sidx, bf16x8 (&kop)[4][KS]) {
     const uint8_t* kb = ring + (sidx % S::NSTAGE) * S::STAGE_BYTES;
 #pragma unroll
     for (int kbi = 0; kbi < 4; ++kbi)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        kop[kbi][ks] =
-            *reinterpret_cast<const bf16x8*>(kb + kofs[ks] + (32 * (kbi >> 1) + 4 * (kbi & 1)) * S::ROW_BYTES);
+        kop[kbi][ks] = *reinterpret_cast<const bf16x8*>(kb + kofs[kbi >> 1][ks] + 4 * (kbi & 1) * S::ROW_BYTES);
   };
-  // the shared tile's block of this wave: kbi = wave
-  const int shconst = (32 * (wv >> 1) + 4 * (wv & 1)) * S::ROW_BYTES;
   auto read_ksh = [&](int sidx, bf16x8 (&k)[KS]) {
-    const uint8_t* kb = ring + (sidx % S::NSTAGE) * S::STAGE_BYTES + shconst;
+    const uint8_t* kb = ring + (sidx % S::NSTAGE) * S::STAGE_BYTES;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) k[ks] = *reinterpret_cast<const bf16x8*>(kb + kofs[ks]);
+    for (int ks = 0; ks < KS; ++ks) k[ks] = *reinterpret_cast<const bf16x8*>(kb + kshofs[ks]);
   };
   // V^T operands by transposing reads of row-major V: lane (g4, r16) gets
-  // V[32*pair + 8*g4 + j][16*db + r16], j = 0..7.
+  // V[32*(pair ^ shPP) + 8*g4 + j][16*db + r16], j = 0..7.
   auto read_v = [&](int sidx, bf16x8 (&vop)[DB][2]) {
     const uint8_t* vb = ring + (sidx % S::NSTAGE) * S::STAGE_BYTES;
 #pragma unroll
@@ -519,16 +530,16 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
       for (int pp = 0; pp < 2; ++pp) {
         i16x4 half[2];
 #pragma unroll
-        for (int r = 0; r < 2; ++r) half[r] = ds_read_tr16(vb + vofs_l[db] + (32 * pp + 4 * r) * S::ROW_BYTES);
+        for (int r = 0; r < 2; ++r) half[r] = ds_read_tr16(vb + vofs_l[pp][db] + 4 * r * S::ROW_BYTES);
         const i16x4 a = half[0], b = half[1];
         vop[db][pp] = __builtin_bit_cast(bf16x8, (short __attribute__((ext_vector_type(8)))){a[0], a[1], a[2], a[3],
                                                                                              b[0], b[1], b[2], b[3]});
       }
   };
 
-  const int kb_own[4] = {0, 1, 2, 3};
-  const int kb_sh[1] = {wv};
-  const int shPP = wv >> 1, shTT = wv & 1;
+  // first slot of each score block (after the pair swap) for masking
+  const int kb_own[4] = {32 * shPP, 32 * shPP + 4, 32 * (1 - shPP), 32 * (1 - shPP) + 4};
+  const int kb_sh[1] = {32 * shPP + 4 * shTT};
 
   bf16x8 kop[4][KS], ksh[KS], vop[DB][2];
   f32x4 sc0[4], sc1[4], sc2[1];
@@ -566,10 +577,7 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
     // ---- step 0: own tile 0 ----
     if (partial) mask_scores<4>(sc0, kb_own, valid, g4);
     if (s > 0) {
-      if (shPP)
-        O::template pv1<1>(vop, pbsh, o2);
-      else
-        O::template pv1<0>(vop, pbsh, o2);
+      O::template pv1<0>(vop, pbsh, o2);
       u32x4 pb[2] = {u32x4{pk1[0], pk1[1], pk1[2], pk1[3]}, u32x4{pk1[4], pk1[5], pk1[6], pk1[7]}};
       O::pv(vop, pb, o1);
     }
@@ -616,10 +624,7 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
     // of the pair's operand; the other half is zero
     pbsh = shTT ? u32x4{0u, 0u, pk2[0], pk2[1]} : u32x4{pk2[0], pk2[1], 0u, 0u};
   }
-  if (shPP)
-    O::template pv1<1>(vop, pbsh, o2);
-  else
-    O::template pv1<0>(vop, pbsh, o2);
+  O::template pv1<0>(vop, pbsh, o2);
   {
     u32x4 pb[2] = {u32x4{pk1[0], pk1[1], pk1[2], pk1[3]}, u32x4{pk1[4], pk1[5], pk1[6], pk1[7]}};
     O::pv(vop, pb, o1);
