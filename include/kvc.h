@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 1
+#define KVC_ABI_VERSION 2
 
 typedef struct kvc_ctx kvc_ctx;
 typedef void* kvc_stream_t;   /* hipStream_t */
@@ -99,6 +99,8 @@ typedef struct kvc_config {
   int32_t num_streams;         /* independent frame streams sharing the pools, >= 1 */
   int32_t max_patch_pages;     /* >= num_streams * (S + W + 1) */
   int32_t max_special_pages;   /* special pages shared by all streams, >= 0 */
+  int32_t max_frames_per_step; /* most frames one stream appends in one step, 1..64: above 1 for the
+                                  multi-frame scale phase ([p2] §Frame Processing Loop) */
 } kvc_config;
 
 /* [p3] §Inspecting Cache Statistics, plus the special-page counters. */
@@ -193,6 +195,22 @@ kvc_status kvc_reset(kvc_ctx* ctx);
 kvc_status kvc_append_frame(kvc_ctx* ctx, int32_t stream, int32_t block, const void* k, const void* v,
                             kvc_stream_t hip_stream);
 
+/* Several frames of one stream in one step: the scale phase, where the first
+ * frames are processed together and every frame's K/V is appended ([p2]
+ * §Frame Processing Loop, num_frames > 1).
+ *   k, v: device [num_frames, T, H, D] bf16, contiguous, 16-byte aligned.
+ *   num_frames: 1..max_frames_per_step; every block of the step passes the
+ *   same count.
+ * At block 0 the frames are allocated in order, exactly as num_frames calls
+ * of kvc_append_frame would (all or none: on KVC_ERR_POOL_EXHAUSTED nothing
+ * changes).  The step's queries are then the num_frames * T rows of those
+ * frames, and they attend to every visible token, the step's own frames
+ * included.  kvc_append_frame is this call with num_frames = 1.
+ * Errors: as kvc_append_frame, and KVC_ERR_ARG for a count outside
+ * 1..max_frames_per_step or different from block 0's. */
+kvc_status kvc_append_frames(kvc_ctx* ctx, int32_t stream, int32_t block, const void* k, const void* v,
+                             int32_t num_frames, kvc_stream_t hip_stream);
+
 /* [p5] §Sliding-Window Eviction Strategy: move the oldest live-window pages
  * beyond the window back to the free list (host metadata only; scale pages
  * are kept).  Idempotent within a step. */
@@ -210,8 +228,9 @@ kvc_status kvc_plan(kvc_ctx* ctx, kvc_stream_t hip_stream);
 
 /* Paged attention for one block with the step's plan ([p2] §Attention Kernel
  * Execution):
- *   q: device [R, H, D] bf16, R = T * (number of planned streams), rows in
- *      plan order (stream i's frame at rows [i*T, (i+1)*T)).
+ *   q: device [R, H, D] bf16, R = T * (frames appended this step, summed over
+ *      the planned streams), rows in plan order (stream i's frames at rows
+ *      [qo_indptr[i], qo_indptr[i+1]), frame by frame).
  *   o: device [R, H, D] bf16, written; must not overlap q.
  * Each stream's queries attend only to its own visible tokens.  Launches the
  * attention kernel and, when a stream's KV is split, the merge kernel.

@@ -210,16 +210,21 @@ class AllocatorReplay:
             return st.special_tokens - self.cfg.page_size * (len(st.all_special_pages) - 1)
         return self.cfg.patch_tokens
 
-    def plan(self, streams: Sequence[int]) -> Dict[str, np.ndarray]:
+    def plan(self, streams: Sequence[int], frames: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
         """The per-step plan for the given streams, concatenated in the given
-        order ([p3] §Plan-Run Execution Workflow)."""
+        order ([p3] §Plan-Run Execution Workflow).  frames[i] is the number of
+        frames stream i appended this step (default 1): the scale phase takes
+        several initialization frames in one pass ([p2] §Frame Processing
+        Loop), so the step's queries are all of those frames' rows."""
+        if frames is None:
+            frames = [1] * len(streams)
         indptr = [0]
         indices: List[int] = []
         last = []
         n_patch = []
         n_special = []
         qo = [0]
-        for s in streams:
+        for s, nf in zip(streams, frames):
             tbl = self.build_visible_page_table(s)
             indices += tbl
             indptr.append(len(indices))
@@ -227,7 +232,7 @@ class AllocatorReplay:
             st = self.streams[s]
             n_patch.append(len(st.scale_patch_pages) + len(st.live_window_patch_pages))
             n_special.append(len(st.all_special_pages))
-            qo.append(qo[-1] + self.cfg.tokens_per_frame)
+            qo.append(qo[-1] + nf * self.cfg.tokens_per_frame)
         return {
             "kv_indptr": np.array(indptr, dtype=np.int32),
             "kv_indices": np.array(indices, dtype=np.int32),
@@ -383,25 +388,31 @@ class OracleStream:
 
     def step(self, streams: Sequence[int],
              frame_kv: Callable[[int, int, int], Tuple[np.ndarray, np.ndarray]],
-             evict: bool = True) -> Dict[str, np.ndarray]:
-        """Advance the given streams by one frame.  frame_kv(stream, frame,
-        block) returns that frame's K and V bits.  Returns the step's plan."""
-        for s in streams:
-            f = self.alloc.streams[s].frame_count
-            slots = self.alloc.append_frame(s)
-            for b, pool in self.pools.items():
-                k, v = frame_kv(s, f, b)
-                pool.write_frame(slots, k, v)
+             evict: bool = True, frames: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
+        """Advance the given streams by frames[i] frames each (default one;
+        several in a scale-phase step, [p2] §Frame Processing Loop).
+        frame_kv(stream, frame, block) returns that frame's K and V bits.
+        Returns the step's plan."""
+        if frames is None:
+            frames = [1] * len(streams)
+        for s, nf in zip(streams, frames):
+            for _ in range(nf):
+                f = self.alloc.streams[s].frame_count
+                slots = self.alloc.append_frame(s)
+                for b, pool in self.pools.items():
+                    k, v = frame_kv(s, f, b)
+                    pool.write_frame(slots, k, v)
         if evict:
             for s in streams:
                 self.alloc.evict_frames(s)
-        return self.alloc.plan(streams)
+        return self.alloc.plan(streams, frames)
 
     def attend(self, plan: Dict[str, np.ndarray], block: int, q_bits: np.ndarray) -> np.ndarray:
-        """Paged attention of the step: q_bits [sum T, H, D] rows in plan order."""
-        T = self.cfg.tokens_per_frame
+        """Paged attention of the step: q_bits rows in plan order, stream i's
+        at [qo_indptr[i], qo_indptr[i+1])."""
+        qo = plan["qo_indptr"]
         outs = []
         for i in range(len(plan["last_page_len"])):
             k, v = gather_paged(self.cfg, self.pools[block], plan, i)
-            outs.append(attention_fp64(q_bits[i * T:(i + 1) * T], k, v))
+            outs.append(attention_fp64(q_bits[qo[i]:qo[i + 1]], k, v))
         return np.concatenate(outs, axis=0)

@@ -40,6 +40,7 @@ KVC_KERNEL_MERGE = 1
 KVC_KERNEL_APPEND = 2
 
 MAX_SPLITS = 64
+ABI_VERSION = 2   # KVC_ABI_VERSION of include/kvc.h
 
 
 class KvcError(RuntimeError):
@@ -52,7 +53,7 @@ class KvcConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "num_blocks", "num_heads", "head_dim", "tokens_per_frame", "num_special_tokens",
         "special_row_offset", "page_size", "scale_frames", "sliding_window", "num_streams",
-        "max_patch_pages", "max_special_pages")]
+        "max_patch_pages", "max_special_pages", "max_frames_per_step")]
 
 
 class KvcStats(ctypes.Structure):
@@ -77,6 +78,7 @@ SIGNATURES = {
     "kvc_destroy": (_I32, [_P]),
     "kvc_reset": (_I32, [_P]),
     "kvc_append_frame": (_I32, [_P, _I32, _I32, _P, _P, _P]),
+    "kvc_append_frames": (_I32, [_P, _I32, _I32, _P, _P, _I32, _P]),
     "kvc_evict": (_I32, [_P, _I32]),
     "kvc_plan": (_I32, [_P, _P]),
     "kvc_run": (_I32, [_P, _I32, _P, _P, _P]),
@@ -104,7 +106,7 @@ def load_library(path: str = LIB_PATH):
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
-    if lib.kvc_abi_version() != 1:
+    if lib.kvc_abi_version() != ABI_VERSION:
         raise ImportError("libkvc.so ABI version mismatch")
     if path == LIB_PATH:
         _lib = lib
@@ -117,7 +119,8 @@ def _ceil_div(a, b):
 
 def make_config(num_blocks, num_heads, head_dim, tokens_per_frame, num_special_tokens=6, page_size=None,
                 scale_frames=8, sliding_window=64, num_streams=1, max_patch_pages=None,
-                max_special_pages=None, max_total_frames=None, special_row_offset=None) -> KvcConfig:
+                max_special_pages=None, max_total_frames=None, special_row_offset=None,
+                max_frames_per_step=1) -> KvcConfig:
     """Build a kvc_config.  Defaults follow [p2] §Initializing the Cache
     Manager: page_size = patch tokens, patch pages = S + W + 16 headroom per
     stream, special pages sized for max_total_frames."""
@@ -132,7 +135,8 @@ def make_config(num_blocks, num_heads, head_dim, tokens_per_frame, num_special_t
     if special_row_offset is None:
         special_row_offset = P
     return KvcConfig(num_blocks, num_heads, head_dim, tokens_per_frame, num_special_tokens, special_row_offset,
-                     page_size, scale_frames, sliding_window, num_streams, max_patch_pages, max_special_pages)
+                     page_size, scale_frames, sliding_window, num_streams, max_patch_pages, max_special_pages,
+                     max_frames_per_step)
 
 
 class PagedKVCache:
@@ -218,6 +222,30 @@ class PagedKVCache:
         if block_idx == 0:
             self._planned = False
 
+    def append_frames(self, block_idx: int, k=None, v=None, num_frames: Optional[int] = None, stream_id: int = 0,
+                      stream=None):
+        """Write several frames' K and V ([F, T, H, D] or [F*T, H, D] bf16) of
+        one block in one step (the scale phase); at block 0 this also
+        allocates the F frames, all or none."""
+        if self.metadata_only:
+            if num_frames is None:
+                raise KvcError(KVC_ERR_ARG, "num_frames is required without tensors")
+            rc = self.lib.kvc_append_frames(self._ctx, stream_id, block_idx, None, None, num_frames, None)
+        else:
+            T = self.cfg.tokens_per_frame
+            F = k.shape[0] if k.dim() == 4 else k.shape[0] // T
+            if num_frames is not None and num_frames != F:
+                raise KvcError(KVC_ERR_ARG, f"num_frames {num_frames} does not match k ({F} frames)")
+            k2 = k.reshape(F * T, *k.shape[-2:])
+            v2 = v.reshape(F * T, *v.shape[-2:])
+            self._check_tensor(k2, F * T, "k")
+            self._check_tensor(v2, F * T, "v")
+            rc = self.lib.kvc_append_frames(self._ctx, stream_id, block_idx, k2.data_ptr(), v2.data_ptr(), F,
+                                            self._stream(stream))
+        self._check(rc, "append_frames")
+        if block_idx == 0:
+            self._planned = False
+
     def evict_frames(self, stream_id: int = 0, block_idx: Optional[int] = None):
         """Return live-window pages beyond the window to the free list (host
         metadata only, once per step; block_idx is accepted and ignored)."""
@@ -297,6 +325,12 @@ class PagedKVCache:
         if rc:
             self._check(rc, "plan")
         self._planned = True
+
+    def raw_append_frames(self, block_idx: int, k_ptr: int, v_ptr: int, num_frames: int, stream_id: int,
+                          hip_stream: int):
+        rc = self.lib.kvc_append_frames(self._ctx, stream_id, block_idx, k_ptr, v_ptr, num_frames, hip_stream)
+        if rc != KVC_OK:
+            self._check(rc, "append_frames")
 
     def raw_run(self, block_idx: int, q_ptr: int, o_ptr: int, hip_stream: int):
         rc = self.lib.kvc_run(self._ctx, block_idx, q_ptr, o_ptr, hip_stream)

@@ -33,6 +33,7 @@ kvc::Config to_cfg(const kvc_config& c) {
   k.num_streams = c.num_streams;
   k.max_patch_pages = c.max_patch_pages;
   k.max_special_pages = c.max_special_pages;
+  k.max_frames_per_step = c.max_frames_per_step;
   return k;
 }
 
@@ -74,7 +75,8 @@ struct kvc_ctx {
   bool have_plan = false;
   std::vector<uint8_t> advanced;      // [stream]: appended block 0 this step
   std::vector<uint8_t> block_done;    // [stream * num_blocks + block]
-  std::vector<kvc::FrameSlots> slots; // [stream]: this step's frame slots
+  std::vector<int32_t> nframes;       // [stream]: frames appended this step
+  std::vector<kvc::FrameSlots> slots; // [stream * max_frames_per_step + f]: this step's frame slots
   kvc::HostPlan plan;
   int plan_buf = 0;
   hipEvent_t staging_done[2] = {nullptr, nullptr};
@@ -185,7 +187,8 @@ static kvc_status create_common(const kvc_config* cfg, const int32_t* fpo, const
   }
   x->advanced.assign(c.num_streams, 0);
   x->block_done.assign((size_t)c.num_streams * c.num_blocks, 0);
-  x->slots.assign(c.num_streams, kvc::FrameSlots());
+  x->slots.assign((size_t)c.num_streams * c.max_frames_per_step, kvc::FrameSlots());
+  x->nframes.assign(c.num_streams, 0);
   x->lay = layout_of(c);
   *made = x;
   return KVC_OK;
@@ -272,59 +275,82 @@ kvc_status kvc_reset(kvc_ctx* c) {
   return KVC_OK;
 }
 
-kvc_status kvc_append_frame(kvc_ctx* c, int32_t stream, int32_t block, const void* k, const void* v,
-                            kvc_stream_t hs) {
+kvc_status kvc_append_frames(kvc_ctx* c, int32_t stream, int32_t block, const void* k, const void* v,
+                             int32_t num_frames, kvc_stream_t hs) {
   if (!c) return KVC_ERR_ARG;
   const kvc::Config& cf = c->cfg;
   if (stream < 0 || stream >= cf.num_streams) return fail(c, KVC_ERR_ARG, "stream out of range");
   if (block < 0 || block >= cf.num_blocks) return fail(c, KVC_ERR_ARG, "block out of range");
+  if (num_frames < 1 || num_frames > cf.max_frames_per_step)
+    return fail(c, KVC_ERR_ARG, "num_frames must be in [1, max_frames_per_step]");
   if (c->metadata_only) {
     if (k || v) return fail(c, KVC_ERR_ARG, "metadata-only context takes k = v = NULL");
   } else if (!k || !v || ((uintptr_t)k & 15) || ((uintptr_t)v & 15)) {
     return fail(c, KVC_ERR_ARG, "k and v must be 16-byte aligned device pointers");
   }
   const size_t bd = (size_t)stream * cf.num_blocks + block;
+  kvc::FrameSlots* fs = &c->slots[(size_t)stream * cf.max_frames_per_step];
   if (block == 0) {
     // kvc_plan ends a step; the first block-0 append after it starts the next.
     const bool new_step = c->planned;
     if (!new_step && c->advanced[stream])
       return fail(c, KVC_ERR_STATE, "stream already appended block 0 this step (kvc_plan ends a step)");
-    kvc::FrameSlots fs;
     std::string why;
-    const int rc = c->alloc.append(stream, &fs, &why);
-    if (rc != kvc::OK) return fail(c, (kvc_status)rc, why);
+    if (num_frames == 1) {
+      const int rc = c->alloc.append(stream, &fs[0], &why);
+      if (rc != kvc::OK) return fail(c, (kvc_status)rc, why);
+    } else {
+      // all frames or none
+      const kvc::Allocator before = c->alloc;
+      for (int32_t f = 0; f < num_frames; ++f) {
+        const int rc = c->alloc.append(stream, &fs[f], &why);
+        if (rc != kvc::OK) {
+          c->alloc = before;
+          return fail(c, (kvc_status)rc, why);
+        }
+      }
+    }
     if (new_step) {
       c->planned = false;
       std::fill(c->advanced.begin(), c->advanced.end(), 0);
       std::fill(c->block_done.begin(), c->block_done.end(), 0);
     }
     c->advanced[stream] = 1;
-    c->slots[stream] = fs;
+    c->nframes[stream] = num_frames;
   } else {
     if (!c->advanced[stream]) return fail(c, KVC_ERR_STATE, "append of block >= 1 before block 0 in this step");
     if (c->block_done[bd]) return fail(c, KVC_ERR_STATE, "block already appended for this stream in this step");
+    if (num_frames != c->nframes[stream])
+      return fail(c, KVC_ERR_ARG, "num_frames differs from this step's block-0 append");
   }
   c->block_done[bd] = 1;
   if (c->metadata_only) return KVC_OK;
 
-  const kvc::FrameSlots& fs = c->slots[stream];
-  kvc::AppendParams p;
-  std::memset(&p, 0, sizeof(p));
-  p.pool = c->pools[block];
-  p.k = k;
-  p.v = v;
-  p.T = cf.tokens_per_frame;
-  p.row_elems = cf.num_heads * cf.head_dim;
-  p.special_row_offset = cf.special_row_offset;
-  p.n_special = cf.num_special_tokens;
-  p.page_size = cf.page_size;
-  p.patch_page = fs.patch_page;
-  p.sp_slot0 = fs.sp_slot0;
-  p.n_sp_pages = fs.n_sp_pages;
-  for (int i = 0; i < KVC_MAX_APPEND_SPECIAL_PAGES; ++i) p.sp_pages[i] = fs.sp_pages[i];
-  const int e = timed(c, KVC_KERNEL_APPEND, hs, [&] { return kvc::launch_append(p, hs); });
-  if (e) return hip_fail(c, e, "append launch");
+  const size_t frame_bytes = (size_t)cf.tokens_per_frame * cf.num_heads * cf.head_dim * 2;
+  for (int32_t f = 0; f < num_frames; ++f) {
+    kvc::AppendParams p;
+    std::memset(&p, 0, sizeof(p));
+    p.pool = c->pools[block];
+    p.k = static_cast<const char*>(k) + f * frame_bytes;
+    p.v = static_cast<const char*>(v) + f * frame_bytes;
+    p.T = cf.tokens_per_frame;
+    p.row_elems = cf.num_heads * cf.head_dim;
+    p.special_row_offset = cf.special_row_offset;
+    p.n_special = cf.num_special_tokens;
+    p.page_size = cf.page_size;
+    p.patch_page = fs[f].patch_page;
+    p.sp_slot0 = fs[f].sp_slot0;
+    p.n_sp_pages = fs[f].n_sp_pages;
+    for (int i = 0; i < KVC_MAX_APPEND_SPECIAL_PAGES; ++i) p.sp_pages[i] = fs[f].sp_pages[i];
+    const int e = timed(c, KVC_KERNEL_APPEND, hs, [&] { return kvc::launch_append(p, hs); });
+    if (e) return hip_fail(c, e, "append launch");
+  }
   return KVC_OK;
+}
+
+kvc_status kvc_append_frame(kvc_ctx* c, int32_t stream, int32_t block, const void* k, const void* v,
+                            kvc_stream_t hs) {
+  return kvc_append_frames(c, stream, block, k, v, 1, hs);
 }
 
 kvc_status kvc_evict(kvc_ctx* c, int32_t stream) {
@@ -337,11 +363,14 @@ kvc_status kvc_evict(kvc_ctx* c, int32_t stream) {
 kvc_status kvc_plan(kvc_ctx* c, kvc_stream_t hs) {
   if (!c) return KVC_ERR_ARG;
   if (c->planned) return fail(c, KVC_ERR_STATE, "already planned this step");
-  std::vector<int32_t> streams;
+  std::vector<int32_t> streams, frames;
   for (int s = 0; s < c->cfg.num_streams; ++s)
-    if (c->advanced[s]) streams.push_back(s);
+    if (c->advanced[s]) {
+      streams.push_back(s);
+      frames.push_back(c->nframes[s]);
+    }
   if (streams.empty()) return fail(c, KVC_ERR_STATE, "no stream appended block 0 this step");
-  kvc::build_plan(c->alloc, streams, c->policy, &c->plan);
+  kvc::build_plan(c->alloc, streams, frames, c->policy, &c->plan);
   c->planned = true;
   c->have_plan = true;
   if (c->metadata_only) return KVC_OK;

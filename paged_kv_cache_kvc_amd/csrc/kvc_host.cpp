@@ -33,7 +33,10 @@ int validate(const Config& c, std::string* why) {
   const int64_t pages = (int64_t)c.max_patch_pages + c.max_special_pages;
   if (pages * c.page_size >= (int64_t)1 << 31) return fail(ERR_UNSUPPORTED, "pool slots per block must be < 2^31");
   if ((int64_t)c.num_heads * c.head_dim > 65536) return fail(ERR_UNSUPPORTED, "num_heads * head_dim above 65536");
-  if ((int64_t)c.num_streams * c.tokens_per_frame >= (int64_t)1 << 24) return fail(ERR_UNSUPPORTED, "too many query rows");
+  if (c.max_frames_per_step < 1 || c.max_frames_per_step > 64)
+    return fail(ERR_ARG, "max_frames_per_step must be in [1, 64]");
+  if ((int64_t)c.num_streams * c.max_frames_per_step * c.tokens_per_frame >= (int64_t)1 << 24)
+    return fail(ERR_UNSUPPORTED, "too many query rows");
   return OK;
 }
 
@@ -159,7 +162,8 @@ size_t plan_image_ints(const Config& c) {
          (size_t)KVC_UNIT_INTS * max_units(c);
 }
 
-void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const PlanPolicy& pol, HostPlan* out) {
+void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const std::vector<int32_t>& frames,
+                const PlanPolicy& pol, HostPlan* out) {
   const Config& c = a.config();
   HostPlan& p = *out;
   const int n = (int)streams.size();
@@ -184,7 +188,7 @@ void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const P
     const int32_t n_patch = (int32_t)(st.scale_pages.size() + st.live_pages.size());
     p.n_patch_pages.push_back(n_patch);
     p.last_page_len.push_back(a.last_page_len(streams[i]));
-    p.qo_indptr.push_back(p.qo_indptr.back() + c.tokens_per_frame);
+    p.qo_indptr.push_back(p.qo_indptr.back() + frames[i] * c.tokens_per_frame);
     kv_len[i] = (int64_t)n_patch * P + st.special_tokens;
   }
 
@@ -192,15 +196,14 @@ void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const P
   // group).  Query groups hold at most KVC_ATTN_WAVES * tiles_per_wave tiles;
   // KV splits share the target work-group count in proportion to each
   // stream's visible length, in whole KVC_KV_TILE units.
-  const int32_t nqt = (int32_t)ceil_div(c.tokens_per_frame, KVC_Q_TILE);
   const int32_t per_group = kvc_group_tiles(c.head_dim);
-  const int32_t n_group = (int32_t)ceil_div(nqt, per_group);
-  int64_t total_len = 0;
-  for (int i = 0; i < n; ++i) total_len += kv_len[i];
+  // work is proportional to queries x visible tokens
+  double total_work = 0;
+  for (int i = 0; i < n; ++i) total_work += (double)frames[i] * (double)kv_len[i];
   const int32_t max_splits = std::max(1, std::min<int32_t>(pol.max_splits, KVC_MAX_SPLITS));
 
   p.image.assign(KVC_PLAN_HEADER_INTS + (size_t)KVC_STREAM_REC_INTS * n + p.kv_indices.size(), 0);
-  int32_t item = 0;
+  int32_t item = 0, tiles = 0;
   p.any_split = false;
   const int32_t upp = (int32_t)ceil_div(std::max(1, P), KVC_KV_TILE);
   const int32_t ups = (int32_t)ceil_div(c.page_size, KVC_KV_TILE);
@@ -210,9 +213,12 @@ void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const P
     const int64_t units = std::max<int64_t>(
         1, (int64_t)n_patch * upp +
                (n_special > 0 ? (int64_t)(n_special - 1) * ups + ceil_div(p.last_page_len[i], KVC_KV_TILE) : 0));
-    double want = total_len > 0 ? (double)pol.target_workgroups * (double)kv_len[i] / (double)total_len /
-                                      ((double)c.num_heads * n_group)
-                                : 1.0;
+    const int32_t n_q = frames[i] * c.tokens_per_frame;
+    const int32_t nqt = (int32_t)ceil_div(n_q, KVC_Q_TILE);
+    const int32_t n_group = (int32_t)ceil_div(nqt, per_group);
+    double want = total_work > 0 ? (double)pol.target_workgroups * (double)frames[i] * (double)kv_len[i] /
+                                       total_work / ((double)c.num_heads * n_group)
+                                 : 1.0;
     int64_t ns = (int64_t)std::llround(want);
     ns = std::max<int64_t>(1, std::min<int64_t>(ns, std::min<int64_t>(max_splits, units)));
     p.n_split.push_back((int32_t)ns);
@@ -221,7 +227,7 @@ void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const P
     kvc_dev_stream rec;
     std::memset(&rec, 0, sizeof(rec));
     rec.q_row0 = p.qo_indptr[i];
-    rec.n_q = c.tokens_per_frame;
+    rec.n_q = n_q;
     rec.page0 = p.kv_indptr[i];
     rec.n_patch = p.n_patch_pages[i];
     rec.n_pages = p.kv_indptr[i + 1] - p.kv_indptr[i];
@@ -233,7 +239,8 @@ void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const P
     rec.ups = ups;
     rec.n_split = (int32_t)ns;
     rec.n_group = n_group;
-    rec.q_tile0 = i * nqt;
+    rec.q_tile0 = tiles;
+    tiles += nqt;
     rec.item0 = item;
     rec.n_items = c.num_heads * (int32_t)ns * n_group;
     item += rec.n_items;
@@ -241,7 +248,7 @@ void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const P
   }
   p.num_items = item;
   p.num_rows = p.qo_indptr.back();
-  p.num_tiles = n * nqt;
+  p.num_tiles = tiles;
   p.image[KVC_HDR_NUM_STREAMS] = n;
   p.image[KVC_HDR_NUM_ITEMS] = item;
   p.image[KVC_HDR_NUM_ROWS] = p.num_rows;

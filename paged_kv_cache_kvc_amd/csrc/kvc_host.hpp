@@ -25,12 +25,15 @@ struct Config {
   int32_t num_special_tokens = 0, special_row_offset = 0, page_size = 0;
   int32_t scale_frames = 0, sliding_window = 0, num_streams = 0;
   int32_t max_patch_pages = 0, max_special_pages = 0;
+  int32_t max_frames_per_step = 1;
 
   int32_t patch_tokens() const { return tokens_per_frame - num_special_tokens; }
   int32_t max_num_pages() const { return max_patch_pages + max_special_pages; }
-  int32_t rows_capacity() const { return num_streams * tokens_per_frame; }
+  int32_t rows_capacity() const { return num_streams * max_frames_per_step * tokens_per_frame; }
   // query tiles of KVC_Q_TILE rows over all streams (split partial outputs)
-  int32_t tiles_capacity() const { return num_streams * ((tokens_per_frame + KVC_Q_TILE - 1) / KVC_Q_TILE); }
+  int32_t tiles_capacity() const {
+    return num_streams * ((max_frames_per_step * tokens_per_frame + KVC_Q_TILE - 1) / KVC_Q_TILE);
+  }
 };
 
 // Result codes mirror kvc_status.
@@ -106,7 +109,10 @@ struct HostPlan {
 };
 
 // Plan the given streams (ascending) from the allocator's current lists.
-void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const PlanPolicy& pol, HostPlan* out);
+// frames[i]: frames streams[i] appended this step (its queries are
+// frames[i] * tokens_per_frame rows).
+void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const std::vector<int32_t>& frames,
+                const PlanPolicy& pol, HostPlan* out);
 
 // int32 entries of the device plan image for a configuration (upper bound).
 size_t plan_image_ints(const Config& c);

@@ -74,7 +74,8 @@ class Harness:
 
     def __init__(self, wl: syn.Workload, num_blocks: int = 1, q_scale: float = 1.0,
                  real_patch: Optional[Callable[[int, int], bool]] = None, orders=None,
-                 options: Optional[Dict[int, int]] = None, device="cuda", oracle_blocks: Sequence[int] = (0,)):
+                 options: Optional[Dict[int, int]] = None, device="cuda", oracle_blocks: Sequence[int] = (0,),
+                 max_frames_per_step: int = 1):
         import torch
         import paged_kv_cache_kvc_amd as kvc
         self.torch = torch
@@ -84,7 +85,8 @@ class Harness:
         self.q_scale = q_scale
         self.real_patch = real_patch or (lambda s, f: True)
         po, so = orders if orders is not None else free_orders(wl)
-        self.gpu = kvc.PagedKVCache(kvc.make_config(**cfg_args(wl, num_blocks)), device=device,
+        self.gpu = kvc.PagedKVCache(kvc.make_config(**cfg_args(wl, num_blocks),
+                                                    max_frames_per_step=max_frames_per_step), device=device,
                                     free_patch_order=po, free_special_order=so)
         for k, v in (options or {}).items():
             self.gpu.set_option(k, v)
@@ -115,16 +117,18 @@ class Harness:
     def active(self) -> List[int]:
         return [s for s in range(self.wl.num_streams) if self.global_step >= syn.stream_join_step(self.wl, s)]
 
-    def step(self, run: bool = True, check: bool = False, blocks_to_run: Optional[Sequence[int]] = None):
-        """One frame step for every active stream.  Returns a dict with the
-        GPU outputs (bits per block) and, when check, the oracle outputs and
-        plans."""
+    def step(self, run: bool = True, check: bool = False, blocks_to_run: Optional[Sequence[int]] = None,
+             nframes: Optional[Dict[int, int]] = None):
+        """One step for every active stream: one frame each, or nframes[s]
+        frames (a scale-phase step).  Returns a dict with the GPU outputs
+        (bits per block) and, when check, the oracle outputs and plans."""
         act = self.active()
         frames = {s: self.frame_of[s] for s in act}
+        nf = {s: (nframes or {}).get(s, 1) for s in act}
         kv_cache = {}
 
         def frame_kv(s, f, b):
-            key = (s, b)
+            key = (s, f, b)
             if key not in kv_cache:
                 kv_cache[key] = (self._frame(s, f, b, "k"), self._frame(s, f, b, "v"))
             return kv_cache[key]
@@ -134,28 +138,34 @@ class Harness:
         outs = {}
         for b in range(self.nb):
             for s in act:
-                k, v = frame_kv(s, frames[s], b)
-                self.to_dev(k, self.kbuf)
-                self.to_dev(v, self.vbuf)
-                self.gpu.append_frame(b, self.kbuf, self.vbuf, stream_id=s)
+                if nf[s] == 1:
+                    k, v = frame_kv(s, frames[s], b)
+                    self.to_dev(k, self.kbuf)
+                    self.to_dev(v, self.vbuf)
+                    self.gpu.append_frame(b, self.kbuf, self.vbuf, stream_id=s)
+                else:
+                    kvs = [frame_kv(s, frames[s] + j, b) for j in range(nf[s])]
+                    kd = self.to_dev(np.concatenate([x[0] for x in kvs]))
+                    vd = self.to_dev(np.concatenate([x[1] for x in kvs]))
+                    self.gpu.append_frames(b, kd, vd, num_frames=nf[s], stream_id=s)
             if b == 0:
                 for s in act:
                     self.gpu.evict_frames(s)
                 self.gpu.plan()           # a plan closes every step, run or not
             if run and b in run_blocks:
-                q = np.concatenate([self._frame(s, frames[s], b, "q") for s in act])
+                q = np.concatenate([self._frame(s, frames[s] + j, b, "q") for s in act for j in range(nf[s])])
                 qd = self.to_dev(q)
                 out = self.gpu.compute_attention(b, qd)
                 outs[b] = (q, out)
         # oracle replay (allocator always; pools only for its blocks)
-        ora_plan = self.ora.step(act, frame_kv)
+        ora_plan = self.ora.step(act, frame_kv, frames=[nf[s] for s in act])
         res["ora_plan"] = ora_plan
         res["gpu_plan"] = self.gpu.get_plan()
         res["out_bits"] = {b: out.view(self.torch.int16).cpu().numpy().view(np.uint16) for b, (q, out) in outs.items()}
         if check:
             res["ref"] = {b: self.ora.attend(ora_plan, b, q) for b, (q, out) in outs.items() if b in self.ora.pools}
         for s in act:
-            self.frame_of[s] += 1
+            self.frame_of[s] += nf[s]
         self.global_step += 1
         return res
 

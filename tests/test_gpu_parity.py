@@ -209,3 +209,27 @@ def test_fragmented_four_streams():
     compare_plan(res)
     st = check_close(res["out_bits"][0], res["ref"][0])
     log(f"frag: splits {res['gpu_plan']['n_splits']} {st}")
+
+
+def test_scale_phase_multi_frame_prefill():
+    """[p2] §Frame Processing Loop: the first S frames in one step (S*T
+    queries attending every token of those frames), then single-frame
+    streaming.  Outputs within tolerance, plans and pool bit-exact."""
+    _need_gpu()
+    wl = _base_small(H=4, frames=90)
+    S, T = wl.scale_frames, wl.tokens_per_frame
+    h = Harness(wl, num_blocks=2, max_frames_per_step=S, oracle_blocks=(0, 1))
+    res = h.step(check=True, nframes={0: S})
+    compare_plan(res)
+    assert list(res["gpu_plan"]["qo_indptr"]) == [0, S * T]
+    for b in (0, 1):
+        st = check_close(res["out_bits"][b], res["ref"][b])
+        log(f"scale-phase step block {b}: splits {res['gpu_plan']['n_splits']} {st}")
+    last = max(wl.frames) - S
+    for t in range(1, last + 1):
+        res = h.step(run=t in (1, 40, last), check=t in (1, last))
+        compare_plan(res)
+        if "ref" in res:
+            check_close(res["out_bits"][0], res["ref"][0])
+    assert h.frame_of[0] == max(wl.frames)
+    assert np.array_equal(h.pool_bits(0), h.ora.pools[0].data)

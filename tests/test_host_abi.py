@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, n), n
         assert n in kvc.SIGNATURES, n
     assert set(kvc.SIGNATURES) == set(names)
-    assert lib.kvc_abi_version() == 1
+    assert lib.kvc_abi_version() == kvc.ABI_VERSION == 2
 
 
 def cfg_of(wl: syn.Workload):
@@ -228,3 +228,63 @@ def test_split_policy_options():
     c.plan()
     assert c.get_plan()["n_splits"][0] == 1
     assert c.get_option(kvc.KVC_OPT_MAX_SPLITS) == 1
+
+
+def test_scale_phase_multi_frame_steps_match_oracle():
+    """A stream whose first step appends its S scale frames together ([p2]
+    §Frame Processing Loop), then streams one frame per step; a second stream
+    joins later with a 3-frame step.  Plans and counters bit-exact."""
+    wl = syn.WORKLOADS["base"]
+    c = cfg_of(wl)
+    c.num_streams = 2
+    c.max_patch_pages = 2 * (wl.scale_frames + wl.sliding_window + 16)
+    c.max_special_pages = 12
+    c.max_frames_per_step = wl.scale_frames
+    cache = kvc.PagedKVCache(c, metadata_only=True)
+    ocfg = ocfg_of(wl)
+    ocfg.num_streams, ocfg.max_patch_pages, ocfg.max_special_pages = 2, c.max_patch_pages, 12
+    ref = ko.AllocatorReplay(ocfg)
+    for step in range(120):
+        sched = {0: wl.scale_frames if step == 0 else 1}
+        if step >= 30:
+            sched[1] = 3 if step == 30 else 1
+        active = sorted(sched)
+        for s in active:
+            cache.append_frames(0, num_frames=sched[s], stream_id=s)
+            for _ in range(sched[s]):
+                ref.append_frame(s)
+        for s in active:
+            cache.evict_frames(s)
+            ref.evict_frames(s)
+        cache.plan()
+        ours = cache.get_plan()
+        compare_plans(ours, ref.plan(active, [sched[s] for s in active]), active)
+        for s in active:
+            st = cache.get_cache_stats(s)
+            theirs = ref.get_cache_stats(s)
+            assert {k: st[k] for k in theirs} == theirs
+
+
+def test_multi_frame_append_arguments_and_all_or_none():
+    c = tiny_cache(num_blocks=2, max_frames_per_step=4)
+    with pytest.raises(kvc.KvcError) as e:
+        c.append_frames(0, num_frames=5)              # above max_frames_per_step
+    assert e.value.status == kvc.KVC_ERR_ARG
+    with pytest.raises(kvc.KvcError) as e:
+        c.append_frames(0, num_frames=0)
+    assert e.value.status == kvc.KVC_ERR_ARG
+    c.append_frames(0, num_frames=3)
+    with pytest.raises(kvc.KvcError) as e:
+        c.append_frames(1, num_frames=2)              # differs from block 0
+    assert e.value.status == kvc.KVC_ERR_ARG
+    c.append_frames(1, num_frames=3)
+    c.plan()
+    assert list(c.get_plan()["qo_indptr"]) == [0, 3 * syn.WORKLOADS["tiny"].tokens_per_frame]
+    # 6 patch pages: 3 used, a 4-frame step cannot fit and must leave no trace
+    before = c.get_cache_stats()
+    with pytest.raises(kvc.KvcError) as e:
+        c.append_frames(0, num_frames=4)
+    assert e.value.status == kvc.KVC_ERR_POOL_EXHAUSTED
+    assert c.get_cache_stats() == before
+    c.append_frames(0, num_frames=3)                  # exactly fills the pool
+    assert c.get_cache_stats()["free_pages"] == 0

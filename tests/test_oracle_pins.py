@@ -133,6 +133,35 @@ def pin_sdpa(oracle=ko, seed=0):
         np.testing.assert_allclose(ours, ref, rtol=1e-12, atol=1e-12)
 
 
+def pin_scale_phase(oracle=ko, seed=5):
+    """[p2] §Frame Processing Loop: the scale phase runs one full attention
+    pass over several initialization frames.  A first step that appends F
+    frames and attends their F*T queries through the page table must equal
+    PyTorch SDPA over the concatenated tokens of those frames (every query
+    sees every token, its own frame's and the other frames' alike)."""
+    cfg = tiny_cfg(scale_frames=3)
+    T, H, D = cfg.tokens_per_frame, cfg.num_heads, cfg.head_dim
+    rng = np.random.default_rng(seed)
+    F = 3
+    qs = [rand_bits(rng, (T, H, D), 2.0) for _ in range(F)]
+    ks = [rand_bits(rng, (T, H, D)) for _ in range(F)]
+    vs = [rand_bits(rng, (T, H, D)) for _ in range(F)]
+    a = oracle.AllocatorReplay(cfg)
+    pool = oracle.SimulatedPool(cfg)
+    for f in range(F):
+        pool.write_frame(a.append_frame(0), ks[f], vs[f])
+    a.evict_frames(0)
+    plan = a.plan([0], frames=[F])
+    assert list(plan["qo_indptr"]) == [0, F * T]
+    k, v = oracle.gather_paged(cfg, pool, plan, 0)
+    assert k.shape[0] == F * T
+    ours = oracle.attention_fp64(np.concatenate(qs), k, v)
+    to = lambda b: torch.from_numpy(syn.bf16_bits_to_f32(b).astype(np.float64)).permute(1, 0, 2)[None]
+    ref = torch.nn.functional.scaled_dot_product_attention(to(np.concatenate(qs)), to(np.concatenate(ks)),
+                                                           to(np.concatenate(vs)))[0].permute(1, 0, 2).numpy()
+    np.testing.assert_allclose(ours, ref, rtol=1e-12, atol=1e-12)
+
+
 def pin_bruteforce(oracle=ko, seed=1):
     """Scalar loops straight from the definition of softmax attention."""
     rng = np.random.default_rng(seed)
@@ -215,6 +244,10 @@ def test_visible_set_and_order():
 
 def test_attention_matches_torch_sdpa():
     pin_sdpa()
+
+
+def test_scale_phase_multi_frame_step_is_dense_sdpa():
+    pin_scale_phase()
 
 
 def test_attention_bruteforce():
@@ -458,6 +491,11 @@ class _ScaleEvicted(ko.AllocatorReplay):
         return fs
 
 
+class _OneFramePerStep(ko.AllocatorReplay):
+    def plan(self, streams, frames=None):
+        return super().plan(streams)      # ignores the frames of a scale-phase step
+
+
 class _LifoSpecialReuse(ko.AllocatorReplay):
     def append_frame(self, stream):
         fs = super().append_frame(stream)
@@ -475,7 +513,7 @@ def _pins_fail(mutant, pins):
 
 
 ALL_PINS = [pin_worked_example, pin_special_closed_forms, pin_visible_set, pin_sdpa, pin_bruteforce,
-            pin_softmax_invariants, pin_paged_equals_dense]
+            pin_softmax_invariants, pin_paged_equals_dense, pin_scale_phase]
 
 
 @pytest.mark.parametrize("mutant", [
@@ -487,8 +525,9 @@ ALL_PINS = [pin_worked_example, pin_special_closed_forms, pin_visible_set, pin_s
     _Mutant(AllocatorReplay=_LastPageZeroWhenFull),
     _Mutant(AllocatorReplay=_ScaleEvicted),
     _Mutant(AllocatorReplay=_LifoSpecialReuse),
+    _Mutant(AllocatorReplay=_OneFramePerStep),
 ], ids=["no_scale", "values_are_keys", "wrong_softmax_axis", "window_off_by_one", "specials_first",
-        "last_page_zero", "scale_evicted", "special_count_drift"])
+        "last_page_zero", "scale_evicted", "special_count_drift", "one_frame_per_step"])
 def test_planted_mistake_is_caught(mutant):
     # OracleStream inside the mutant must use the mutant's allocator
     class _Stream(ko.OracleStream):
@@ -498,11 +537,11 @@ def test_planted_mistake_is_caught(mutant):
             self.pools = {b: ko.SimulatedPool(cfg) for b in blocks}
 
         def attend(self, plan, block, q_bits):
-            T = self.cfg.tokens_per_frame
+            qo = plan["qo_indptr"]
             outs = []
             for i in range(len(plan["last_page_len"])):
                 k, v = mutant.gather_paged(self.cfg, self.pools[block], plan, i)
-                outs.append(mutant.attention_fp64(q_bits[i * T:(i + 1) * T], k, v))
+                outs.append(mutant.attention_fp64(q_bits[qo[i]:qo[i + 1]], k, v))
             return np.concatenate(outs)
     mutant.OracleStream = _Stream
     assert _pins_fail(mutant, ALL_PINS)
