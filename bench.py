@@ -144,12 +144,93 @@ def cpu_baseline(wl, seconds):
     }
 
 
+def scale_phase(args, torch, syn, kvc, dev):
+    """The scale phase of the base shape: S = 8 frames appended in one step
+    to all 24 blocks, then paged attention of their 8 x 262 queries over
+    their 8 x 262 tokens for every block ([p2] "How LingBot-Map Uses
+    FlashInfer KV Cache for Streaming 3D Reconstruction" §Frame Processing
+    Loop).  Each timed step resets the host metadata first (the pools keep
+    their contents; only valid slots are read)."""
+    wl = syn.WORKLOADS["base"]
+    nb, T, H, D, S = wl.num_blocks, wl.tokens_per_frame, wl.num_heads, wl.head_dim, wl.scale_frames
+    K, W = args.steps, args.warmup
+    cfg = kvc.make_config(nb, H, D, T, wl.num_special_tokens, page_size=wl.page_size, scale_frames=S,
+                          sliding_window=wl.sliding_window, max_patch_pages=wl.max_patch_pages,
+                          max_special_pages=wl.max_special_pages, special_row_offset=wl.row_offset,
+                          max_frames_per_step=S)
+    cache = kvc.PagedKVCache(cfg, device=dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(wl.seed)
+    mk = lambda: torch.randn((nb, S * T, H, D), generator=g, device=dev).to(torch.bfloat16)
+    qb, kb, vb = mk(), mk(), mk()
+    ob = torch.empty((S * T, H, D), dtype=torch.bfloat16, device=dev)
+    hs = torch.cuda.current_stream(dev).cuda_stream
+
+    def step(run_profiled=False):
+        cache.reset()
+        for b in range(nb):
+            cache.raw_append_frames(b, kb[b].data_ptr(), vb[b].data_ptr(), S, 0, hs)
+            if b == 0:
+                cache.evict_frames(0)
+                cache.raw_plan(hs)
+            cache.raw_run(b, qb[b].data_ptr(), ob.data_ptr(), hs)
+
+    for _ in range(W):
+        step()
+    torch.cuda.synchronize()
+    progress(f"timing {K} scale-phase steps")
+    t0 = time.perf_counter()
+    for _ in range(K):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    value = K / wall
+    st = cache.get_cache_stats(0)
+    L = (st["scale_pages"] + st["live_pages"]) * wl.patch_tokens + st["special_tokens"]
+    flop = 4.0 * S * T * L * H * D
+    byts = 4.0 * L * H * D + 4.0 * S * T * H * D
+    # the kernels' durations from per-launch HIP events, attention launches repeated on the last plan
+    cache.set_option(kvc.KVC_OPT_PROFILE, 1)
+    for k in (kvc.KVC_KERNEL_ATTENTION, kvc.KVC_KERNEL_MERGE):
+        cache.profile_read(k, reset=True)
+    for _ in range(K):
+        for b in range(nb):
+            cache.raw_run(b, qb[b].data_ptr(), ob.data_ptr(), hs)
+    torch.cuda.synchronize()
+    cache.set_option(kvc.KVC_OPT_PROFILE, 0)
+    a_ms, a_n = cache.profile_read(kvc.KVC_KERNEL_ATTENTION)
+    m_ms, m_n = cache.profile_read(kvc.KVC_KERNEL_MERGE)
+    a_s = a_ms / 1e3 / max(a_n, 1)
+    tfl = flop / a_s / 1e12
+    gbs = byts / a_s / 1e9
+    bound = "hbm" if flop / byts < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9) else "mfma"
+    roof = ({"bound": "mfma", "achieved": tfl, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+             "frac": tfl / PEAK_BF16_TFLOPS, "traffic": None} if bound == "mfma" else
+            {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+             "traffic": None})
+    out = {
+        "metric": "scale-phase steps/sec (8 frames appended and attended in one step, all 24 blocks)",
+        "value": value, "unit": "scale-phase steps/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": 1e3 * wall / K, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": (f"scale: {nb} blocks, H={H}, D={D}, {S} frames of {wl.patch_tokens} patch + "
+                                f"{wl.num_special_tokens} special tokens in one step, page_size {wl.page_size}"),
+                   "num_blocks": nb, "query_rows": S * T, "visible_tokens": L, "num_heads": H, "head_dim": D},
+        "roofline": roof,
+        "attention": {"kernel": "attn_kernel", "launches": a_n, "avg_us": 1e6 * a_s, "tflops": tfl, "gbs": gbs,
+                      "alg_flop_per_launch": flop, "alg_bytes_per_launch": byts,
+                      "merge_avg_us": 1e3 * m_ms / max(m_n, 1), "merge_launches": m_n},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="base", choices=["base", "r518", "long", "frag"])
+    ap.add_argument("--workload", default="base", choices=["base", "r518", "long", "frag", "scale"],
+                    help="scale: the base shape's scale phase, its 8 first frames appended and attended in one step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--target-wgs", type=int, default=None)
@@ -182,6 +263,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": n, "launches": 5}), flush=True)
+        return
+    if args.workload == "scale":
+        scale_phase(args, torch, syn, kvc, dev)
         return
     wl = syn.WORKLOADS[args.workload]
     F = max(wl.frames)

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include <cmath>
+#include <algorithm>
 #include <cstring>
 #include <new>
 #include <string>
@@ -440,6 +441,7 @@ kvc_status kvc_run(kvc_ctx* c, int32_t block, const void* q, void* o, kvc_stream
     m.head_dim = cf.head_dim;
     m.tiles_cap = cf.tiles_capacity();
     m.num_tiles = c->plan.num_tiles;
+    m.max_split = *std::max_element(c->plan.n_split.begin(), c->plan.n_split.end());
     e = timed(c, KVC_KERNEL_MERGE, hs, [&] { return kvc::launch_merge(m, hs); });
     if (e) return hip_fail(c, e, "merge launch");
   }

@@ -49,6 +49,7 @@ struct MergeParams {
   const float* part_lse;
   void* o;
   int32_t num_heads, head_dim, tiles_cap, num_tiles;
+  int32_t max_split;        // largest split count over the planned streams
 };
 
 // Return 0 on success or the hipError_t value.

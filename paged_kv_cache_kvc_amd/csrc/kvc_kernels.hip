@@ -717,16 +717,19 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
 // ---------------------------------------------------------------------------
 // merge of KV splits
 // ---------------------------------------------------------------------------
-// One work-group of 16 waves per (query tile, head).  Wave w takes d block
-// w % DB and split group w / DB (splits g, g + SG, ...); each lane the 4
-// values it holds in every split's partial (the accumulator lane order).  A
-// group folds its splits with weights 2^(lse_c - its max); the groups are then
-// combined through LDS, in group order, so every sum has a fixed order.
+// One work-group of DB * SG waves per (query tile, head), SG = 1, 2, 4 ...
+// (at most 16 waves; the host picks SG from the largest split count).  Wave w
+// takes d block w % DB and split group w / DB (splits g, g + SG, ...); each
+// lane the 4 values it holds in every split's partial (the accumulator lane
+// order).  A group folds its splits with weights 2^(lse_c - its max); the
+// groups are then combined through LDS, in group order, so every sum has a
+// fixed order.
 template <int D>
 __global__ __launch_bounds__(1024) void merge_kernel(MergeParams p) {
   constexpr int DB = D / 16;
-  constexpr int SG = 16 / DB;     // split groups
-  __shared__ float xs[SG][DB][6][64];
+  constexpr int SGMAX = 16 / DB;
+  __shared__ float xs[SGMAX][DB][6][64];
+  const int SG = (int)(blockDim.x >> 6) / DB;   // split groups of this launch
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int db = wave % DB, sg = wave / DB;
@@ -763,11 +766,9 @@ __global__ __launch_bounds__(1024) void merge_kernel(MergeParams p) {
   __syncthreads();
   if (sg != 0) return;
   float M = -INFINITY;
-#pragma unroll
   for (int g = 0; g < SG; ++g) M = fmaxf(M, xs[g][db][0][lane]);
   f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
   float tw = 0.f;
-#pragma unroll
   for (int g = 0; g < SG; ++g) {
     const float wg = xs[g][db][1][lane] > 0.f ? __builtin_amdgcn_exp2f(xs[g][db][0][lane] - M) : 0.f;
     tw += wg * xs[g][db][1][lane];
@@ -815,15 +816,19 @@ int launch_attention(const AttnParams& p, int32_t grid, void* s) {
 int launch_merge(const MergeParams& p, void* s) {
   const hipStream_t hs = (hipStream_t)s;
   const int grid = p.num_tiles * p.num_heads;   // one work-group per (query tile, head)
+  const int db = p.head_dim / 16;
+  int sg = 1;
+  while (sg < 16 / db && sg < p.max_split) sg *= 2;
+  const int threads = 64 * db * sg;
   switch (p.head_dim) {
     case 32:
-      hipLaunchKernelGGL(merge_kernel<32>, dim3(grid), dim3(1024), 0, hs, p);
+      hipLaunchKernelGGL(merge_kernel<32>, dim3(grid), dim3(threads), 0, hs, p);
       break;
     case 64:
-      hipLaunchKernelGGL(merge_kernel<64>, dim3(grid), dim3(1024), 0, hs, p);
+      hipLaunchKernelGGL(merge_kernel<64>, dim3(grid), dim3(threads), 0, hs, p);
       break;
     case 128:
-      hipLaunchKernelGGL(merge_kernel<128>, dim3(grid), dim3(1024), 0, hs, p);
+      hipLaunchKernelGGL(merge_kernel<128>, dim3(grid), dim3(threads), 0, hs, p);
       break;
     default:
       return (int)hipErrorInvalidValue;
