@@ -119,7 +119,9 @@ typedef struct kvc_stats {
 enum {
   KVC_OPT_TARGET_WORKGROUPS = 1, /* attention work-groups the planner aims for per run (default 2 per CU) */
   KVC_OPT_MAX_SPLITS = 2,        /* cap on KV splits per stream; 1 disables split-KV (default 64, the maximum) */
-  KVC_OPT_PROFILE = 3            /* 1: time every attention/merge/append launch with HIP events */
+  KVC_OPT_PROFILE = 3,           /* 1: time every attention/merge/append launch with HIP events */
+  KVC_OPT_DEFER_EVICTION = 4     /* 1: hold evicted window pages back until the stream's next frame,
+                                    so that kvc_rollback can undo the latest frame (default 0) */
 };
 
 /* Kernels for kvc_profile_read. */
@@ -213,8 +215,22 @@ kvc_status kvc_append_frames(kvc_ctx* ctx, int32_t stream, int32_t block, const 
 
 /* [p5] §Sliding-Window Eviction Strategy: move the oldest live-window pages
  * beyond the window back to the free list (host metadata only; scale pages
- * are kept).  Idempotent within a step. */
+ * are kept).  Idempotent within a step.  With KVC_OPT_DEFER_EVICTION the
+ * pages leave the visible table but are held back (their contents intact)
+ * until the stream appends its next frame. */
 kvc_status kvc_evict(kvc_ctx* ctx, int32_t stream);
+
+/* Deferred eviction for frame rollback, as key-frame selection needs ([p2]
+ * §Scale Frames vs Sliding Window; [p4] §Summary): undo the stream's most
+ * recent frame.  Its patch page and the special pages it opened return to
+ * the front of the free lists, its special tokens are dropped, and window
+ * pages held back by the last eviction return to the front of the window
+ * until it is full; no device memory is touched.  The visible table is then
+ * the one before that frame, and the next frame reuses the freed page.
+ * Call between steps (after kvc_plan); the step's plan can no longer be run.
+ * Errors: KVC_ERR_ARG, KVC_ERR_STATE (deferred eviction off, mid-step, or no
+ * frame to undo: only the latest frame, once per append). */
+kvc_status kvc_rollback(kvc_ctx* ctx, int32_t stream);
 
 /* Build the step's plan ([p3] §Plan-Run Execution Workflow): for each stream
  * that appended block 0 this step, in ascending order, the visible page table

@@ -107,6 +107,10 @@ class _StreamState:
     special_tokens: int
     frame_count: int
     frames: List[FrameSlots]
+    # deferred eviction: window pages evicted since the last append (oldest
+    # first), out of the table but not yet free
+    held_back: List[int] = dataclasses.field(default_factory=list)
+    undoable: bool = False
 
 
 class AllocatorReplay:
@@ -132,6 +136,11 @@ class AllocatorReplay:
             if free_special_order is None else [int(x) for x in free_special_order]
         assert sorted(self._init_patch) == list(range(cfg.max_patch_pages))
         assert sorted(self._init_special) == list(range(cfg.max_patch_pages, cfg.max_num_pages))
+        # [p2] §Scale Frames vs Sliding Window mentions deferred eviction for
+        # frame rollback (key-frame selection) without its rules; the reading
+        # used here: evicted window pages are held back until the stream's
+        # next append, and only the latest frame can be undone, once.
+        self.defer_eviction = False
         self.reset()
 
     def reset(self):
@@ -156,8 +165,6 @@ class AllocatorReplay:
         cfg = self.cfg
         st = self.streams[stream]
         pg = cfg.page_size
-        if not self.free_patch_pages:
-            raise PoolExhausted("no free patch page")
         # special pages needed for this frame's tokens
         need = 0
         n = st.special_tokens
@@ -167,6 +174,11 @@ class AllocatorReplay:
             n += 1
         if need > len(self.free_special_pages):
             raise PoolExhausted("special pool exhausted")
+        if not self.free_patch_pages and not st.held_back:
+            raise PoolExhausted("no free patch page")
+        # the previous frame becomes final: its held-back pages are freed
+        self.free_patch_pages.extend(st.held_back)
+        st.held_back = []
         page = self.free_patch_pages.popleft()
         if len(st.scale_patch_pages) < cfg.scale_frames:
             st.scale_patch_pages.append(page)
@@ -181,6 +193,35 @@ class AllocatorReplay:
         st.frame_count += 1
         fs = FrameSlots(page, slots)
         st.frames.append(fs)
+        st.undoable = True
+        return fs
+
+    def rollback_frame(self, stream: int) -> FrameSlots:
+        """Undo the latest frame of the stream (deferred eviction only): the
+        page lists return to what they were before that frame's append, with
+        the pages it took back at the front of the free lists, and the
+        held-back window pages back at the front of the window until the
+        window is full again."""
+        st = self.streams[stream]
+        if not self.defer_eviction or not st.undoable or not st.frames:
+            raise RuntimeError("nothing to roll back")
+        fs = st.frames.pop()
+        opened = sorted({p for p, slot in fs.special if slot == 0}, key=st.all_special_pages.index)
+        for p in reversed(opened):
+            assert st.all_special_pages[-1] == p
+            st.all_special_pages.pop()
+            self.free_special_pages.appendleft(p)
+        st.special_tokens -= len(fs.special)
+        if st.live_window_patch_pages and st.live_window_patch_pages[-1] == fs.patch_page:
+            st.live_window_patch_pages.pop()
+        else:
+            assert st.scale_patch_pages[-1] == fs.patch_page
+            st.scale_patch_pages.pop()
+        self.free_patch_pages.appendleft(fs.patch_page)
+        while st.held_back and len(st.live_window_patch_pages) < self.cfg.sliding_window:
+            st.live_window_patch_pages.appendleft(st.held_back.pop())
+        st.frame_count -= 1
+        st.undoable = False
         return fs
 
     def evict_frames(self, stream: int) -> List[int]:
@@ -191,7 +232,10 @@ class AllocatorReplay:
         freed = []
         while len(st.live_window_patch_pages) > self.cfg.sliding_window:
             p = st.live_window_patch_pages.popleft()
-            self.free_patch_pages.append(p)
+            if self.defer_eviction:
+                st.held_back.append(p)
+            else:
+                self.free_patch_pages.append(p)
             freed.append(p)
         return freed
 

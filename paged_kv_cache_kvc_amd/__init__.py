@@ -34,6 +34,7 @@ KVC_ERR_UNSUPPORTED = -6
 KVC_OPT_TARGET_WORKGROUPS = 1
 KVC_OPT_MAX_SPLITS = 2
 KVC_OPT_PROFILE = 3
+KVC_OPT_DEFER_EVICTION = 4
 
 KVC_KERNEL_ATTENTION = 0
 KVC_KERNEL_MERGE = 1
@@ -80,6 +81,7 @@ SIGNATURES = {
     "kvc_append_frame": (_I32, [_P, _I32, _I32, _P, _P, _P]),
     "kvc_append_frames": (_I32, [_P, _I32, _I32, _P, _P, _I32, _P]),
     "kvc_evict": (_I32, [_P, _I32]),
+    "kvc_rollback": (_I32, [_P, _I32]),
     "kvc_plan": (_I32, [_P, _P]),
     "kvc_run": (_I32, [_P, _I32, _P, _P, _P]),
     "kvc_get_plan": (_I32, [_P, _PI32, _PI32, _PI32, _PI32, _PI32, _PI32, _PI32, _I32, _I32, _PI32, _PI32]),
@@ -250,6 +252,11 @@ class PagedKVCache:
         """Return live-window pages beyond the window to the free list (host
         metadata only, once per step; block_idx is accepted and ignored)."""
         self._check(self.lib.kvc_evict(self._ctx, stream_id), "evict_frames")
+
+    def rollback_frame(self, stream_id: int = 0):
+        """Undo the stream's most recent frame (deferred eviction must be on;
+        between steps, after plan)."""
+        self._check(self.lib.kvc_rollback(self._ctx, stream_id), "rollback_frame")
 
     def plan(self, stream=None):
         rc = self.lib.kvc_plan(self._ctx, None if self.metadata_only else self._stream(stream))

@@ -74,6 +74,7 @@ struct kvc_ctx {
   // per-step state
   bool planned = false;
   bool have_plan = false;
+  bool plan_stale = false;            // a rollback happened after this step's plan
   std::vector<uint8_t> advanced;      // [stream]: appended block 0 this step
   std::vector<uint8_t> block_done;    // [stream * num_blocks + block]
   std::vector<int32_t> nframes;       // [stream]: frames appended this step
@@ -354,6 +355,19 @@ kvc_status kvc_append_frame(kvc_ctx* c, int32_t stream, int32_t block, const voi
   return kvc_append_frames(c, stream, block, k, v, 1, hs);
 }
 
+kvc_status kvc_rollback(kvc_ctx* c, int32_t stream) {
+  if (!c) return KVC_ERR_ARG;
+  if (stream < 0 || stream >= c->cfg.num_streams) return fail(c, KVC_ERR_ARG, "stream out of range");
+  bool mid_step = false;
+  for (uint8_t a : c->advanced) mid_step = mid_step || a;
+  if (mid_step && !c->planned) return fail(c, KVC_ERR_STATE, "rollback inside a step (call it after kvc_plan)");
+  std::string why;
+  const int rc = c->alloc.rollback(stream, &why);
+  if (rc != kvc::OK) return fail(c, (kvc_status)rc, why);
+  c->plan_stale = true;
+  return KVC_OK;
+}
+
 kvc_status kvc_evict(kvc_ctx* c, int32_t stream) {
   if (!c) return KVC_ERR_ARG;
   if (stream < 0 || stream >= c->cfg.num_streams) return fail(c, KVC_ERR_ARG, "stream out of range");
@@ -373,6 +387,7 @@ kvc_status kvc_plan(kvc_ctx* c, kvc_stream_t hs) {
   if (streams.empty()) return fail(c, KVC_ERR_STATE, "no stream appended block 0 this step");
   kvc::build_plan(c->alloc, streams, frames, c->policy, &c->plan);
   c->planned = true;
+  c->plan_stale = false;
   c->have_plan = true;
   if (c->metadata_only) return KVC_OK;
 
@@ -402,6 +417,7 @@ kvc_status kvc_run(kvc_ctx* c, int32_t block, const void* q, void* o, kvc_stream
   if (!q || !o || ((uintptr_t)q & 15) || ((uintptr_t)o & 15)) return fail(c, KVC_ERR_ARG, "q and o must be 16-byte aligned");
   if (q == o) return fail(c, KVC_ERR_ARG, "o must not alias q");
   if (!c->planned) return fail(c, KVC_ERR_STATE, "run before plan in this step");
+  if (c->plan_stale) return fail(c, KVC_ERR_STATE, "a rollback since the plan: append and plan the next step first");
   for (int32_t s : c->plan.planned)
     if (!c->block_done[(size_t)s * cf.num_blocks + block])
       return fail(c, KVC_ERR_STATE, "a planned stream has not appended this block");
@@ -502,6 +518,10 @@ kvc_status kvc_set_option(kvc_ctx* c, int32_t option, int64_t value) {
       if (c->metadata_only && value) return fail(c, KVC_ERR_STATE, "metadata-only context has no kernels");
       c->profile = value != 0;
       return KVC_OK;
+    case KVC_OPT_DEFER_EVICTION:
+      if (value != 0 && value != 1) return fail(c, KVC_ERR_ARG, "defer eviction is 0 or 1");
+      c->alloc.set_defer_eviction(value != 0);
+      return KVC_OK;
     default:
       return fail(c, KVC_ERR_ARG, "unknown option");
   }
@@ -513,6 +533,7 @@ kvc_status kvc_get_option(const kvc_ctx* c, int32_t option, int64_t* value) {
     case KVC_OPT_TARGET_WORKGROUPS: *value = c->policy.target_workgroups; return KVC_OK;
     case KVC_OPT_MAX_SPLITS: *value = c->policy.max_splits; return KVC_OK;
     case KVC_OPT_PROFILE: *value = c->profile ? 1 : 0; return KVC_OK;
+    case KVC_OPT_DEFER_EVICTION: *value = c->alloc.defer_eviction() ? 1 : 0; return KVC_OK;
     default: return KVC_ERR_ARG;
   }
 }

@@ -94,7 +94,7 @@ int Allocator::append(int s, FrameSlots* out, std::string* why) {
   StreamState& st = streams_[s];
   const int64_t pg = cfg_.page_size;
   const int n_s = cfg_.num_special_tokens;
-  if (free_patch_.empty()) {
+  if (free_patch_.empty() && st.pending.empty()) {
     if (why) *why = "no free patch page (evict, or raise max_patch_pages)";
     return ERR_POOL;
   }
@@ -107,12 +107,19 @@ int Allocator::append(int s, FrameSlots* out, std::string* why) {
     return ERR_POOL;
   }
   FrameSlots fs;
+  // the previous frame is final now: release its held-back window pages
+  // (after the checks above, so that an error leaves the state unchanged;
+  // the checks count them as free)
+  for (int32_t p : st.pending) free_patch_.push_back(p);
+  st.pending.clear();
   fs.patch_page = free_patch_.front();
   free_patch_.pop_front();
-  if ((int32_t)st.scale_pages.size() < cfg_.scale_frames)
+  st.last_is_live = (int32_t)st.scale_pages.size() >= cfg_.scale_frames;
+  if (!st.last_is_live)
     st.scale_pages.push_back(fs.patch_page);
   else
     st.live_pages.push_back(fs.patch_page);
+  st.can_rollback = true;
   if (n_s > 0) {
     fs.sp_slot0 = (int32_t)(st.special_tokens % pg);
     if (fs.sp_slot0 != 0) fs.sp_pages[fs.n_sp_pages++] = st.special_pages.back();
@@ -134,11 +141,52 @@ int Allocator::evict(int s) {
   StreamState& st = streams_[s];
   int n = 0;
   while ((int32_t)st.live_pages.size() > cfg_.sliding_window) {
-    free_patch_.push_back(st.live_pages.front());
+    if (defer_)
+      st.pending.push_back(st.live_pages.front());
+    else
+      free_patch_.push_back(st.live_pages.front());
     st.live_pages.pop_front();
     ++n;
   }
   return n;
+}
+
+int Allocator::rollback(int s, std::string* why) {
+  StreamState& st = streams_[s];
+  if (!defer_) {
+    if (why) *why = "rollback needs deferred eviction (KVC_OPT_DEFER_EVICTION)";
+    return ERR_STATE;
+  }
+  if (!st.can_rollback || st.frame_count == 0) {
+    if (why) *why = "no frame to undo (only the most recent frame, once)";
+    return ERR_STATE;
+  }
+  const int64_t pg = cfg_.page_size;
+  const int n_s = cfg_.num_special_tokens;
+  // special pages this frame opened, newest first back to the front of the list
+  const int64_t before = st.special_tokens - n_s;
+  int opened = 0;
+  for (int j = 0; j < n_s; ++j)
+    if ((before + j) % pg == 0) ++opened;
+  for (int i = 0; i < opened; ++i) {
+    free_special_.push_front(st.special_pages.back());
+    st.special_pages.pop_back();
+  }
+  st.special_tokens = before;
+  if (st.last_is_live) {
+    free_patch_.push_front(st.live_pages.back());
+    st.live_pages.pop_back();
+  } else {
+    free_patch_.push_front(st.scale_pages.back());
+    st.scale_pages.pop_back();
+  }
+  while (!st.pending.empty() && (int32_t)st.live_pages.size() < cfg_.sliding_window) {
+    st.live_pages.push_front(st.pending.back());
+    st.pending.pop_back();
+  }
+  st.frame_count -= 1;
+  st.can_rollback = false;
+  return OK;
 }
 
 int32_t Allocator::last_page_len(int s) const {

@@ -57,6 +57,11 @@ struct StreamState {
   std::vector<int32_t> special_pages;  // append-only
   int64_t special_tokens = 0;
   int64_t frame_count = 0;
+  // deferred eviction: window pages evicted since the last frame's append,
+  // oldest first; out of the visible table but not yet free
+  std::vector<int32_t> pending;
+  bool last_is_live = false;   // the last frame's patch page went to the window
+  bool can_rollback = false;   // the last frame may still be undone
 };
 
 class Allocator {
@@ -65,8 +70,18 @@ class Allocator {
   int init(const Config& cfg, const std::vector<int32_t>& free_patch_order,
            const std::vector<int32_t>& free_special_order, std::string* why);
   void reset();
-  // Allocate one frame of `stream`; state is unchanged on error.
+  // Allocate one frame of `stream`; state is unchanged on error.  With
+  // deferred eviction, pages held back by the previous evict are released to
+  // the free list first (the previous frame can no longer be undone).
   int append(int stream, FrameSlots* out, std::string* why);
+  // Undo the stream's most recent frame (deferred eviction only): its patch
+  // page and the special pages it opened go back to the front of the free
+  // lists, its special tokens are dropped, and held-back window pages return
+  // to the front of the window until it is full again.  ERR_STATE when there
+  // is nothing to undo.
+  int rollback(int stream, std::string* why);
+  void set_defer_eviction(bool on) { defer_ = on; }
+  bool defer_eviction() const { return defer_; }
   // Free live-window pages beyond the window; returns the number freed.
   int evict(int stream);
 
@@ -84,6 +99,7 @@ class Allocator {
   std::vector<int32_t> init_patch_, init_special_;
   std::deque<int32_t> free_patch_, free_special_;
   std::vector<StreamState> streams_;
+  bool defer_ = false;
 };
 
 // Split / group policy of the attention launch.

@@ -95,6 +95,9 @@ class Harness:
                                    free_special_order=so)
         self.global_step = 0
         self.frame_of = [0] * wl.num_streams
+        # frames drawn but rolled back per stream: the oracle numbers frames by
+        # its allocator's count, the inputs are drawn by frame_of
+        self.skew = [0] * wl.num_streams
         T, H, D = wl.tokens_per_frame, wl.num_heads, wl.head_dim
         self.kbuf = torch.empty((T, H, D), dtype=torch.bfloat16, device=device)
         self.vbuf = torch.empty_like(self.kbuf)
@@ -158,7 +161,8 @@ class Harness:
                 out = self.gpu.compute_attention(b, qd)
                 outs[b] = (q, out)
         # oracle replay (allocator always; pools only for its blocks)
-        ora_plan = self.ora.step(act, frame_kv, frames=[nf[s] for s in act])
+        ora_plan = self.ora.step(act, lambda s, f, b: frame_kv(s, f + self.skew[s], b),
+                                 frames=[nf[s] for s in act])
         res["ora_plan"] = ora_plan
         res["gpu_plan"] = self.gpu.get_plan()
         res["out_bits"] = {b: out.view(self.torch.int16).cpu().numpy().view(np.uint16) for b, (q, out) in outs.items()}
@@ -168,6 +172,13 @@ class Harness:
             self.frame_of[s] += nf[s]
         self.global_step += 1
         return res
+
+    def rollback(self, s: int):
+        """Undo stream s's most recent frame on both sides.  The next frame
+        draws new inputs, so rows left behind by the undone frame would show."""
+        self.gpu.rollback_frame(s)
+        self.ora.alloc.rollback_frame(s)
+        self.skew[s] += 1
 
     def pool_bits(self, block: int) -> np.ndarray:
         return self.gpu.pools[block].view(self.torch.int16).cpu().numpy().view(np.uint16)

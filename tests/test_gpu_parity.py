@@ -233,3 +233,33 @@ def test_scale_phase_multi_frame_prefill():
             check_close(res["out_bits"][0], res["ref"][0])
     assert h.frame_of[0] == max(wl.frames)
     assert np.array_equal(h.pool_bits(0), h.ora.pools[0].data)
+
+
+def test_deferred_eviction_with_rollbacks():
+    """Frame rollback with deferred eviction ([p2] §Scale Frames vs Sliding
+    Window): every fourth frame is undone after its step; attention stays
+    within tolerance of the oracle replaying the same rules, the stale plan
+    cannot be run after a rollback, and the pool matches bit-exactly."""
+    _need_gpu()
+    import paged_kv_cache_kvc_amd as kvc
+    wl = _base_small(H=4, frames=100)
+    h = Harness(wl)
+    h.gpu.set_option(kvc.KVC_OPT_DEFER_EVICTION, 1)
+    h.ora.alloc.defer_eviction = True
+    rolled = 0
+    for t in range(max(wl.frames)):
+        res = h.step(run=t % 10 == 9 or t % 4 == 2, check=t % 20 == 19 or t in (2, 78))
+        compare_plan(res)
+        if "ref" in res:
+            st = check_close(res["out_bits"][0], res["ref"][0])
+            log(f"step {t} frames {h.gpu.get_cache_stats()['frame_count']} {st}")
+        if t % 4 == 2 and t < 90:
+            h.rollback(0)
+            rolled += 1
+            q = h.torch.zeros((wl.tokens_per_frame, wl.num_heads, wl.head_dim), dtype=h.torch.bfloat16,
+                              device=h.device)
+            with pytest.raises(kvc.KvcError) as e:
+                h.gpu.compute_attention(0, q)
+            assert e.value.status == kvc.KVC_ERR_STATE
+    assert h.gpu.get_cache_stats()["frame_count"] == max(wl.frames) - rolled
+    assert np.array_equal(h.pool_bits(0), h.ora.pools[0].data)

@@ -288,3 +288,64 @@ def test_multi_frame_append_arguments_and_all_or_none():
     assert c.get_cache_stats() == before
     c.append_frames(0, num_frames=3)                  # exactly fills the pool
     assert c.get_cache_stats()["free_pages"] == 0
+
+
+def test_deferred_eviction_and_rollback_match_oracle():
+    """Rollback with deferred eviction (the reading of [p2] §Scale Frames vs
+    Sliding Window): tables and counters bit-exact against the oracle's
+    replay of the same rules, through every step, with rollbacks at seeded
+    steps (scale frames included)."""
+    wl = syn.WORKLOADS["base"]
+    c = cfg_of(wl)
+    cache = kvc.PagedKVCache(c, metadata_only=True)
+    cache.set_option(kvc.KVC_OPT_DEFER_EVICTION, 1)
+    assert cache.get_option(kvc.KVC_OPT_DEFER_EVICTION) == 1
+    ref = ko.AllocatorReplay(ocfg_of(wl))
+    ref.defer_eviction = True
+    rng = np.random.default_rng(3)
+    rolled = 0
+    for step in range(150):
+        cache.append_frame(0)
+        ref.append_frame(0)
+        cache.evict_frames()
+        ref.evict_frames(0)
+        cache.plan()
+        compare_plans(cache.get_plan(), ref.plan([0]), [0])
+        if rng.random() < 0.3 or step in (3, 7, 8):
+            cache.rollback_frame(0)
+            ref.rollback_frame(0)
+            rolled += 1
+            with pytest.raises(kvc.KvcError) as e:
+                cache.rollback_frame(0)                   # only once per append
+            assert e.value.status == kvc.KVC_ERR_STATE
+        ours = cache.get_cache_stats(0)
+        theirs = ref.get_cache_stats(0)
+        assert {k: ours[k] for k in theirs} == theirs
+    assert rolled > 20 and ours["frame_count"] == 150 - rolled
+
+
+def test_rollback_errors():
+    c = tiny_cache(num_blocks=2)
+    c.append_frame(0)
+    c.append_frame(1)
+    c.evict_frames()
+    c.plan()
+    with pytest.raises(kvc.KvcError) as e:
+        c.rollback_frame(0)                               # deferred eviction off
+    assert e.value.status == kvc.KVC_ERR_STATE
+    c.set_option(kvc.KVC_OPT_DEFER_EVICTION, 1)
+    c.append_frame(0)
+    with pytest.raises(kvc.KvcError) as e:
+        c.rollback_frame(0)                               # inside a step
+    assert e.value.status == kvc.KVC_ERR_STATE
+    c.append_frame(1)
+    c.evict_frames()
+    c.plan()
+    before = c.get_cache_stats()
+    c.rollback_frame(0)
+    after = c.get_cache_stats()
+    assert after["frame_count"] == before["frame_count"] - 1
+    assert after["special_tokens"] == before["special_tokens"] - syn.WORKLOADS["tiny"].num_special_tokens
+    with pytest.raises(kvc.KvcError) as e:
+        c.set_option(kvc.KVC_OPT_DEFER_EVICTION, 2)
+    assert e.value.status == kvc.KVC_ERR_ARG

@@ -162,6 +162,35 @@ def pin_scale_phase(oracle=ko, seed=5):
     np.testing.assert_allclose(ours, ref, rtol=1e-12, atol=1e-12)
 
 
+def pin_rollback(oracle=ko, seed=7):
+    """Deferred eviction for frame rollback ([p2] §Scale Frames vs Sliding
+    Window): after undoing the latest frame, the paged view of the stream is
+    the dense history of the frames it kept, as if the undone frame had never
+    been appended; later frames stream on from there."""
+    cfg = tiny_cfg(max_patch_pages=8, max_special_pages=8)
+    T, H, D = cfg.tokens_per_frame, cfg.num_heads, cfg.head_dim
+    rng = np.random.default_rng(seed)
+    a = oracle.AllocatorReplay(cfg)
+    a.defer_eviction = True
+    pool = oracle.SimulatedPool(cfg)
+    kept = []
+    for i in range(24):
+        k, v = rand_bits(rng, (T, H, D)), rand_bits(rng, (T, H, D))
+        pool.write_frame(a.append_frame(0), k, v)
+        kept.append((k, v))
+        a.evict_frames(0)
+        if i % 3 == 2 and i < 20:
+            a.rollback_frame(0)
+            kept.pop()
+        plan = a.plan([0])
+        kp, vp = oracle.gather_paged(cfg, pool, plan, 0)
+        kd, vd = oracle.gather_dense(cfg, len(kept) - 1, lambda f: kept[f])
+        assert np.array_equal(kp, kd) and np.array_equal(vp, vd)
+        st = a.get_cache_stats(0)
+        assert st["frame_count"] == len(kept)
+        assert st["special_tokens"] == cfg.num_special_tokens * len(kept)
+
+
 def pin_bruteforce(oracle=ko, seed=1):
     """Scalar loops straight from the definition of softmax attention."""
     rng = np.random.default_rng(seed)
@@ -248,6 +277,10 @@ def test_attention_matches_torch_sdpa():
 
 def test_scale_phase_multi_frame_step_is_dense_sdpa():
     pin_scale_phase()
+
+
+def test_rollback_leaves_the_kept_frames_history():
+    pin_rollback()
 
 
 def test_attention_bruteforce():
@@ -496,6 +529,15 @@ class _OneFramePerStep(ko.AllocatorReplay):
         return super().plan(streams)      # ignores the frames of a scale-phase step
 
 
+class _RollbackKeepsHeldBack(ko.AllocatorReplay):
+    def rollback_frame(self, stream):
+        st = self.streams[stream]
+        held, st.held_back = st.held_back, []
+        fs = super().rollback_frame(stream)   # window not refilled
+        self.free_patch_pages.extend(held)
+        return fs
+
+
 class _LifoSpecialReuse(ko.AllocatorReplay):
     def append_frame(self, stream):
         fs = super().append_frame(stream)
@@ -513,7 +555,7 @@ def _pins_fail(mutant, pins):
 
 
 ALL_PINS = [pin_worked_example, pin_special_closed_forms, pin_visible_set, pin_sdpa, pin_bruteforce,
-            pin_softmax_invariants, pin_paged_equals_dense, pin_scale_phase]
+            pin_softmax_invariants, pin_paged_equals_dense, pin_scale_phase, pin_rollback]
 
 
 @pytest.mark.parametrize("mutant", [
@@ -526,8 +568,9 @@ ALL_PINS = [pin_worked_example, pin_special_closed_forms, pin_visible_set, pin_s
     _Mutant(AllocatorReplay=_ScaleEvicted),
     _Mutant(AllocatorReplay=_LifoSpecialReuse),
     _Mutant(AllocatorReplay=_OneFramePerStep),
+    _Mutant(AllocatorReplay=_RollbackKeepsHeldBack),
 ], ids=["no_scale", "values_are_keys", "wrong_softmax_axis", "window_off_by_one", "specials_first",
-        "last_page_zero", "scale_evicted", "special_count_drift", "one_frame_per_step"])
+        "last_page_zero", "scale_evicted", "special_count_drift", "one_frame_per_step", "rollback_no_refill"])
 def test_planted_mistake_is_caught(mutant):
     # OracleStream inside the mutant must use the mutant's allocator
     class _Stream(ko.OracleStream):
