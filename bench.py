@@ -144,6 +144,42 @@ def cpu_baseline(wl, seconds):
     }
 
 
+def achievable_peaks(torch, dev):
+    """Measured ceilings on this GPU, reported beside the spec-sheet peaks:
+    a 1 GiB device-to-device copy (bytes read + written per second) and a
+    large square bf16 matmul (torch, i.e. hipBLASLt)."""
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    reps = 10
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2.0 * n * reps / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del src, dst
+    m = 8192
+    a = torch.randn((m, m), device=dev, dtype=torch.bfloat16)
+    b = torch.randn((m, m), device=dev, dtype=torch.bfloat16)
+    c = torch.matmul(a, b)
+    torch.cuda.synchronize()
+    reps = 20
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(a, b, out=c)
+    e1.record()
+    torch.cuda.synchronize()
+    gemm_tfs = 2.0 * m ** 3 * reps / (e0.elapsed_time(e1) / 1e3) / 1e12
+    del a, b, c
+    torch.cuda.empty_cache()
+    return {"hbm_copy_GBs": copy_gbs, "bf16_gemm_TFLOPs": gemm_tfs,
+            "how": "1 GiB device copy x10 (read + write bytes); 8192^3 bf16 torch.matmul x20; HIP events"}
+
+
 def scale_phase(args, torch, syn, kvc, dev):
     """The scale phase of the base shape: S = 8 frames appended in one step
     to all 24 blocks, then paged attention of their 8 x 262 queries over
@@ -208,6 +244,7 @@ def scale_phase(args, torch, syn, kvc, dev):
              "frac": tfl / PEAK_BF16_TFLOPS, "traffic": None} if bound == "mfma" else
             {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
              "traffic": None})
+    peaks = achievable_peaks(torch, dev)
     out = {
         "metric": "scale-phase steps/sec (8 frames appended and attended in one step, all 24 blocks)",
         "value": value, "unit": "scale-phase steps/s", "n_gpus": 1, "steps": K, "warmup": W,
@@ -219,7 +256,9 @@ def scale_phase(args, torch, syn, kvc, dev):
         "roofline": roof,
         "attention": {"kernel": "attn_kernel", "launches": a_n, "avg_us": 1e6 * a_s, "tflops": tfl, "gbs": gbs,
                       "alg_flop_per_launch": flop, "alg_bytes_per_launch": byts,
-                      "merge_avg_us": 1e3 * m_ms / max(m_n, 1), "merge_launches": m_n},
+                      "merge_avg_us": 1e3 * m_ms / max(m_n, 1), "merge_launches": m_n,
+                      "frac_hbm_achievable": gbs / peaks["hbm_copy_GBs"],
+                      "frac_mfma_achievable": tfl / peaks["bf16_gemm_TFLOPs"], "achievable_peaks": peaks},
     }
     print(json.dumps(out), flush=True)
 
@@ -420,11 +459,15 @@ def main():
                     "frac": tfl / PEAK_BF16_TFLOPS}
         roof["traffic"] = traffic
         out["roofline"] = roof
+        peaks = achievable_peaks(torch, dev)
         out["attention"] = {
             "kernel": "attn_kernel", "launches": a_n, "avg_us": 1e3 * a_ms / max(a_n, 1),
             "tflops": tfl, "gbs": gbs, "frac_hbm": gbs / PEAK_HBM_GBS, "frac_mfma": tfl / PEAK_BF16_TFLOPS,
             "alg_bytes_per_launch": pb / max(a_n, 1), "alg_flop_per_launch": pf / max(a_n, 1),
             "merge_avg_us": 1e3 * m_ms / max(m_n, 1), "merge_launches": m_n,
+            "frac_hbm_achievable": gbs / peaks["hbm_copy_GBs"],
+            "frac_mfma_achievable": tfl / peaks["bf16_gemm_TFLOPs"],
+            "achievable_peaks": peaks,
             "timing": ("per-launch HIP events on the launch stream, around the attention launches of the "
                        "last timed step repeated K times (value is timed without per-launch events)"),
         }
