@@ -111,21 +111,28 @@ struct Shape {
 };
 
 // 16-byte chunk swizzle inside a K/V row of LDS (XORed into the chunk index).
-// Two read patterns must hit distinct banks (64 banks of 4 bytes):
-//  * K operand, ds_read_b128, 16 lanes per pass: one chunk of rows
-//    {8a + j : a, j in 0..3} (+ a multiple of 4): row bits 0, 1, 3, 4 vary;
-//  * V^T operand, ds_read_b64_tr_b16, 32 lanes per pass: the two chunks
-//    2 db + {0, 1} of rows {8 g + j : g in 0..1, j in 0..3}: row bits 0, 1, 3
-//    vary.
-// Rows of a 256-byte bank window that share their bank range (bit 0 for D=128,
-// none below) are separated by the chunk bits the swizzle assigns, so each
-// pattern maps its lanes one-to-one onto the banks.
+// The LDS has 64 banks of 4 bytes; a 64-lane read is served 256 bytes at a
+// time, by groups of lanes measured with the bank-conflict counters:
+//  * ds_read_b128 (K operand): lanes {8a .. 8a+7} together with
+//    {32+8a .. 32+8a+7}.  In such a group lane bits 0, 1, 2 and 5 vary, i.e.
+//    K row bits 0, 1, 3 and chunk bit 1; row bit 4 and the other chunk bits
+//    are fixed.
+//  * ds_read_b64_tr_b16 (V^T operand): lanes 0-31, then 32-63.  In a group
+//    lane bits 0-4 vary, i.e. V row bits 0, 1, 3, chunk bit 0 and the 8-byte
+//    half; row bit 4 is fixed.
+// A group must cover its 256-byte window one-to-one.  The bits of the window
+// address are the row bits below the window (none for D=128, bit 0 for
+// D=64, bits 0-1 for D=32) and the swizzled chunk, so the swizzle has to
+// make the remaining varying bits a bijection: for D=64 swizzle bits {0, 2}
+// over row bits {1, 3} (K) and {1, 2} over {1, 3} (V); for D=32 bit 0 and
+// bit 1 over row bit 3; for D=128 bits {0, 2, 3} (K) and {1, 2, 3} (V) over
+// row bits {0, 1, 3}.
 template <int D>
 __device__ __forceinline__ int swz(int row) {
   const int b0 = row & 1, b1 = (row >> 1) & 1, b3 = (row >> 3) & 1, b4 = (row >> 4) & 1;
-  if constexpr (D == 32) return b4 | (b3 << 1);
-  else if constexpr (D == 64) return b4 | (b1 << 1) | (b3 << 2);
-  else return b4 | (b0 << 1) | (b1 << 2) | (b3 << 3);
+  if constexpr (D == 32) return b3 | (b3 << 1);
+  else if constexpr (D == 64) return b1 | ((b1 ^ b3) << 1) | ((b3 ^ b4) << 2);
+  else return b3 | (b3 << 1) | (b0 << 2) | (b1 << 3);
 }
 
 // The ring of stages is filled by direct global->LDS loads that the kernel
@@ -264,9 +271,17 @@ struct Ops {
   }
 };
 
-// p = 2^(s * scale - ref) rounded to bf16 and packed in pairs (the P^T
-// operand), and the lane's sum of the rounded values (the same numbers the
-// P.V product uses).
+// p = 2^(s * scale - ref) packed in pairs as bf16 (the P^T operand), and the
+// lane's sum of the packed values (the same numbers the P.V product uses).
+// The bf16 value is the upper half of the float32 (rounded toward zero): one
+// byte permute per pair instead of a rounding conversion.  Its relative error
+// has the same spread as round-to-nearest (one bf16 ulp wide) and a mean of
+// half an ulp; numerator and denominator are sums over the same rounded
+// weights, so that mean cancels in the normalisation.
+__device__ __forceinline__ uint32_t pack_hi16(float lo, float hi) {
+  return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, hi), __builtin_bit_cast(uint32_t, lo), 0x07060302u);
+}
+
 template <int N>
 __device__ __forceinline__ float probs(const f32x4 (&s)[N], float sl, float nref, uint32_t (&pk)[2 * N]) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -276,13 +291,13 @@ __device__ __forceinline__ float probs(const f32x4 (&s)[N], float sl, float nref
   for (int i = 0; i < N; ++i)
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const bf16x2 v = {(__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[i][2 * h], sl, nref)),
-                        (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[i][2 * h + 1], sl, nref))};
-      pk[2 * i + h] = __builtin_bit_cast(uint32_t, v);
+      const uint32_t w = pack_hi16(__builtin_amdgcn_exp2f(__builtin_fmaf(s[i][2 * h], sl, nref)),
+                                   __builtin_amdgcn_exp2f(__builtin_fmaf(s[i][2 * h + 1], sl, nref)));
+      pk[2 * i + h] = w;
       if (h == 0)
-        a = __builtin_amdgcn_fdot2_f32_bf16(v, ones, a, false);
+        a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, a, false);
       else
-        b = __builtin_amdgcn_fdot2_f32_bf16(v, ones, b, false);
+        b = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, b, false);
     }
   return a + b;
 }
@@ -348,9 +363,10 @@ __device__ __forceinline__ float renorm(const f32x4 (&s)[N], float sl, bool& fre
 //   step 0: QK(s, own 1), PV(s-1, own 1), PV(s-1, shared) | probs(s, own 0)
 //   step 1: QK(s, shared), PV(s, own 0)                   | probs(s, own 1)
 //   step 2: QK(s+1, own 0)                                 | probs(s, shared)
-// K operands of stage s+1 are read from LDS after step 0 (stage s+1 is
-// published there), V operands of stage s after step 0, the shared block's K
-// of stage s+1 after step 1.  An MFMA result is read by the vector unit one
+// In step 0, after its MFMAs are issued, the V operands of stage s are read
+// from LDS, stage s+1 is published (barrier) and its K operands are read,
+// all ahead of the step's vector work; the shared block's K of stage s+1 is
+// read after step 1.  An MFMA result is read by the vector unit one
 // step after its MFMA at the earliest.  After the last stage the same code
 // reads a ring slot that holds no stage and computes a QK^T that is never
 // used; every LDS address stays inside the ring.
@@ -582,10 +598,12 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
       O::pv(vop, pb, o1);
     }
     O::qk(kop, q1, sc1);
-    float lt = probs<4>(sc0, sl, nref0, pk0);
-    asm volatile("" ::"v"(lt));   // keep the common path ahead of the branch, next to the MFMAs
-    if (fresh0 || __builtin_amdgcn_ballot_w64(lt > LAZY_SUM_LIMIT)) lt = renorm<4, DB>(sc0, sl, fresh0, ref0, nref0, l0, o0, pk0);
-    l0 += lt;
+    // The V operands of stage s (published one stage ago) and, once stage
+    // s+1 is published, its K operands are read before this step's vector
+    // work, which then covers their latency.  Every read of stage s-1 has
+    // completed (the products above consumed them) before the barrier lets
+    // the ring slot of stage s-1 be refilled.
+    read_v(s, vop);
     // publish stage s+1, refill the ring slot of stage s-1
     if (s + 2 < nstage)
       wait_vmcnt<LPW>();
@@ -598,7 +616,10 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
     vq1 = vq2;
     vq2 = en.z;
     read_k(s + 1, kop);
-    read_v(s, vop);
+    float lt = probs<4>(sc0, sl, nref0, pk0);
+    asm volatile("" ::"v"(lt));   // keep the common path ahead of the branch, next to the MFMAs
+    if (fresh0 || __builtin_amdgcn_ballot_w64(lt > LAZY_SUM_LIMIT)) lt = renorm<4, DB>(sc0, sl, fresh0, ref0, nref0, l0, o0, pk0);
+    l0 += lt;
 
     // ---- step 1: own tile 1 ----
     if (partial) mask_scores<4>(sc1, kb_own, valid, g4);
