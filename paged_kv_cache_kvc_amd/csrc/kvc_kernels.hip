@@ -738,74 +738,76 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
 // ---------------------------------------------------------------------------
 // merge of KV splits
 // ---------------------------------------------------------------------------
-// One work-group of DB * SG waves per (query tile, head), SG = 1, 2, 4 ...
-// (at most 16 waves; the host picks SG from the largest split count).  Wave w
-// takes d block w % DB and split group w / DB (splits g, g + SG, ...); each
-// lane the 4 values it holds in every split's partial (the accumulator lane
-// order).  A group folds its splits with weights 2^(lse_c - its max); the
-// groups are then combined through LDS, in group order, so every sum has a
-// fixed order.
+// One work-group of DB waves per (query tile, head) of a split stream, on the
+// XCD whose L2 holds most of its partials (the plan's merge order lists the
+// pairs of each XCD; work-group b runs on XCD b % 8).  Wave w takes d block w,
+// each lane the 4 values it holds in every split's partial (the accumulator
+// lane order).  The tile's entry in the plan's tile table gives its stream's
+// split count and output rows.  The partials and log-sum-exps of up to
+// MERGE_CHUNK splits are loaded together, then folded in split order with
+// weights 2^(lse_c - running max): one memory round trip per chunk, and every
+// sum in a fixed order.  Splits past the tile's own count (other streams may
+// have more) are loaded from the workspace but never used.
+constexpr int MERGE_CHUNK = 16;
+
 template <int D>
-__global__ __launch_bounds__(1024) void merge_kernel(MergeParams p) {
+__global__ __launch_bounds__(512) void merge_kernel(MergeParams p) {
   constexpr int DB = D / 16;
-  constexpr int SGMAX = 16 / DB;
-  __shared__ float xs[SGMAX][DB][6][64];
-  const int SG = (int)(blockDim.x >> 6) / DB;   // split groups of this launch
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int db = wave % DB, sg = wave / DB;
+  const int db = threadIdx.x >> 6;
   const int H = p.num_heads;
-  const int gt = blockIdx.x / H;          // global query tile
-  const int h = blockIdx.x - gt * H;
-  if (gt >= p.num_tiles) return;          // uniform over the work-group
-  const int nstreams = p.plan[KVC_HDR_NUM_STREAMS];
-  const kvc_dev_stream* recs = reinterpret_cast<const kvc_dev_stream*>(p.plan + KVC_PLAN_HEADER_INTS);
-  int si = 0;
-  while (si + 1 < nstreams && gt >= recs[si + 1].q_tile0) ++si;
-  const kvc_dev_stream st = recs[si];
-  const int nsp = st.n_split;
-  if (nsp <= 1) return;                   // uniform over the work-group
+  const int slot = blockIdx.x >> 3;
+  if (slot >= p.merge_slots) return;      // uniform over the work-group
+  const int pair = p.plan[p.merge_table + (blockIdx.x & (KVC_NUM_XCD - 1)) * p.merge_slots + slot];
+  if (pair < 0) return;
+  const int gt = pair / H;                // global query tile
+  const int h = pair - gt * H;
+  const i32x4 te = *reinterpret_cast<const i32x4*>(p.plan + p.tile_table + KVC_TILE_INTS * gt);
   const int r16 = lane & 15, g4 = lane >> 4;
   const size_t tstride = (size_t)H * p.tiles_cap;   // between splits, in tiles
   const size_t t0 = (size_t)h * p.tiles_cap + gt;
-  float m = -INFINITY;
-  for (int c = sg; c < nsp; c += SG) m = fmaxf(m, p.part_lse[(c * tstride + t0) * KVC_Q_TILE + r16]);
+  const uint16_t* po = static_cast<const uint16_t*>(p.part_o) + (t0 * DB + db) * 256 + lane * 4;
+  const float* pl = p.part_lse + t0 * KVC_Q_TILE + r16;
+  float m = -INFINITY, wsum = 0.f;
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  float wsum = 0.f;
-  for (int c = sg; c < nsp; c += SG) {
-    const size_t pt = c * tstride + t0;
-    const float w = __builtin_amdgcn_exp2f(p.part_lse[pt * KVC_Q_TILE + r16] - m);
-    const bf16x4 x =
-        *reinterpret_cast<const bf16x4*>(static_cast<const uint16_t*>(p.part_o) + (pt * DB + db) * 256 + lane * 4);
-    acc += w * f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
-    wsum += w;
-  }
-  xs[sg][db][0][lane] = m;
-  xs[sg][db][1][lane] = wsum;
+  for (int c0 = 0; c0 < p.max_split; c0 += MERGE_CHUNK) {
+    float lse[MERGE_CHUNK];
+    bf16x4 x[MERGE_CHUNK];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) xs[sg][db][2 + i][lane] = acc[i];
-  __syncthreads();
-  if (sg != 0) return;
-  float M = -INFINITY;
-  for (int g = 0; g < SG; ++g) M = fmaxf(M, xs[g][db][0][lane]);
-  f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
-  float tw = 0.f;
-  for (int g = 0; g < SG; ++g) {
-    const float wg = xs[g][db][1][lane] > 0.f ? __builtin_amdgcn_exp2f(xs[g][db][0][lane] - M) : 0.f;
-    tw += wg * xs[g][db][1][lane];
+    for (int j = 0; j < MERGE_CHUNK; ++j)
+      if (c0 + j < p.max_split) {
+        const size_t c = (size_t)(c0 + j) * tstride;
+        lse[j] = pl[c * KVC_Q_TILE];
+        x[j] = *reinterpret_cast<const bf16x4*>(po + c * DB * 256);
+      }
+    const int nsp = te.x;
+    if (nsp <= 1) return;                 // single split: attention wrote o itself
+    float mc = m;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) t[i] += wg * xs[g][db][2 + i][lane];
+    for (int j = 0; j < MERGE_CHUNK; ++j)
+      if (c0 + j < nsp) mc = fmaxf(mc, lse[j]);
+    if (mc == -INFINITY) continue;        // nothing of weight yet
+    const float sc = __builtin_amdgcn_exp2f(m - mc);   // 0 while m is -inf
+    acc *= sc;
+    wsum *= sc;
+#pragma unroll
+    for (int j = 0; j < MERGE_CHUNK; ++j)
+      if (c0 + j < nsp) {
+        const float w = __builtin_amdgcn_exp2f(lse[j] - mc);
+        acc += w * f32x4{(float)x[j][0], (float)x[j][1], (float)x[j][2], (float)x[j][3]};
+        wsum += w;
+      }
+    m = mc;
   }
-  const int row = KVC_Q_TILE * (gt - st.q_tile0) + r16;
-  if (row < st.n_q) {
-    const f32x4 v = t * (1.0f / tw);
+  if (r16 < te.z) {
+    const f32x4 v = acc * (1.0f / wsum);
     bf16x4 b;
     b[0] = (__bf16)v[0];
     b[1] = (__bf16)v[1];
     b[2] = (__bf16)v[2];
     b[3] = (__bf16)v[3];
-    *reinterpret_cast<bf16x4*>(static_cast<uint16_t*>(p.o) + ((size_t)(st.q_row0 + row) * H + h) * D + 16 * db +
-                               4 * g4) = b;
+    *reinterpret_cast<bf16x4*>(static_cast<uint16_t*>(p.o) + ((size_t)(te.y + r16) * H + h) * D + 16 * db + 4 * g4) =
+        b;
   }
 }
 
@@ -836,11 +838,9 @@ int launch_attention(const AttnParams& p, int32_t grid, void* s) {
 
 int launch_merge(const MergeParams& p, void* s) {
   const hipStream_t hs = (hipStream_t)s;
-  const int grid = p.num_tiles * p.num_heads;   // one work-group per (query tile, head)
-  const int db = p.head_dim / 16;
-  int sg = 1;
-  while (sg < 16 / db && sg < p.max_split) sg *= 2;
-  const int threads = 64 * db * sg;
+  const int grid = KVC_NUM_XCD * p.merge_slots;   // one work-group per merged (query tile, head)
+  if (grid == 0) return 0;
+  const int threads = 64 * (p.head_dim / 16);   // one wave per 16-row d block
   switch (p.head_dim) {
     case 32:
       hipLaunchKernelGGL(merge_kernel<32>, dim3(grid), dim3(threads), 0, hs, p);
