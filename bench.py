@@ -92,7 +92,8 @@ def cpu_baseline(wl, seconds):
     t = F - 1
     ocfg = ko.OracleConfig(num_heads=H, head_dim=D, tokens_per_frame=T, num_special_tokens=wl.num_special_tokens,
                            page_size=wl.page_size, scale_frames=wl.scale_frames, sliding_window=wl.sliding_window,
-                           max_patch_pages=wl.max_patch_pages, max_special_pages=wl.max_special_pages)
+                           max_patch_pages=wl.max_patch_pages, max_special_pages=wl.max_special_pages,
+                           dtype=wl.dtype)
     vis = set(ko.visible_frames(t, wl.scale_frames, wl.sliding_window))
     cache = {}
 
@@ -100,18 +101,18 @@ def cpu_baseline(wl, seconds):
         if f not in cache:
             args = (T, H, D, wl.num_special_tokens, wl.row_offset)
             real = f in vis
-            cache[f] = (syn.frame_tensor(wl.seed, 0, f, 0, "k", *args, patch_real=real),
-                        syn.frame_tensor(wl.seed, 0, f, 0, "v", *args, patch_real=real))
+            cache[f] = (syn.frame_tensor(wl.seed, 0, f, 0, "k", *args, patch_real=real, dtype=wl.dtype),
+                        syn.frame_tensor(wl.seed, 0, f, 0, "v", *args, patch_real=real, dtype=wl.dtype))
         return cache[f]
 
-    q = syn.frame_tensor(wl.seed, 0, t, 0, "q", T, H, D, wl.num_special_tokens, wl.row_offset)
+    q = syn.frame_tensor(wl.seed, 0, t, 0, "q", T, H, D, wl.num_special_tokens, wl.row_offset, dtype=wl.dtype)
     for f in range(F):
         frame_kv(f)
     blocks = 0
     t0 = time.perf_counter()
     while True:
         k, v = ko.gather_dense(ocfg, t, frame_kv)
-        ko.attention_fp64(q, k, v)
+        ko.attention_fp64(q, k, v, wl.dtype)
         blocks += 1
         el = time.perf_counter() - t0
         if el >= seconds and blocks >= 1:
@@ -193,13 +194,14 @@ def scale_phase(args, torch, syn, kvc, dev):
     cfg = kvc.make_config(nb, H, D, T, wl.num_special_tokens, page_size=wl.page_size, scale_frames=S,
                           sliding_window=wl.sliding_window, max_patch_pages=wl.max_patch_pages,
                           max_special_pages=wl.max_special_pages, special_row_offset=wl.row_offset,
-                          max_frames_per_step=S)
+                          max_frames_per_step=S, dtype=args.dtype)
     cache = kvc.PagedKVCache(cfg, device=dev)
+    el = cache.elem_dtype
     g = torch.Generator(device=dev)
     g.manual_seed(wl.seed)
-    mk = lambda: torch.randn((nb, S * T, H, D), generator=g, device=dev).to(torch.bfloat16)
+    mk = lambda: torch.randn((nb, S * T, H, D), generator=g, device=dev).to(el)
     qb, kb, vb = mk(), mk(), mk()
-    ob = torch.empty((S * T, H, D), dtype=torch.bfloat16, device=dev)
+    ob = torch.empty((S * T, H, D), dtype=el, device=dev)
     hs = torch.cuda.current_stream(dev).cuda_stream
 
     def step(run_profiled=False):
@@ -249,7 +251,7 @@ def scale_phase(args, torch, syn, kvc, dev):
         "metric": "scale-phase steps/sec (8 frames appended and attended in one step, all 24 blocks)",
         "value": value, "unit": "scale-phase steps/s", "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": 1e3 * wall / K, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic",
+        "dtype": args.dtype, "data": "synthetic",
         "config": {"workload": (f"scale: {nb} blocks, H={H}, D={D}, {S} frames of {wl.patch_tokens} patch + "
                                 f"{wl.num_special_tokens} special tokens in one step, page_size {wl.page_size}"),
                    "num_blocks": nb, "query_rows": S * T, "visible_tokens": L, "num_heads": H, "head_dim": D},
@@ -270,6 +272,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="base", choices=["base", "r518", "long", "frag", "scale"],
                     help="scale: the base shape's scale phase, its 8 first frames appended and attended in one step")
+    ap.add_argument("--dtype", default="bf16", choices=["bf16", "f16"],
+                    help="element type of the pools and of q, k, v, o")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--target-wgs", type=int, default=None)
@@ -317,7 +321,8 @@ def main():
 
     cfg = kvc.make_config(nb, H, D, T, wl.num_special_tokens, page_size=wl.page_size, scale_frames=wl.scale_frames,
                           sliding_window=wl.sliding_window, num_streams=ns, max_patch_pages=wl.max_patch_pages,
-                          max_special_pages=wl.max_special_pages, special_row_offset=wl.row_offset)
+                          max_special_pages=wl.max_special_pages, special_row_offset=wl.row_offset,
+                          dtype=args.dtype)
     po = so = None
     if wl.shuffle_free_lists:
         po = syn.free_list_order(wl.seed, wl.max_patch_pages, 0, 0)
@@ -335,10 +340,10 @@ def main():
 
     def bank(scale=1.0):
         x = torch.randn((ns, BANK, nb, T, H, D), generator=g, device=dev, dtype=torch.float32)
-        return x.mul_(scale).to(torch.bfloat16)
+        return x.mul_(scale).to(cache.elem_dtype)
     qb, kb, vb = bank(), bank(), bank()
-    ob = torch.empty((ns * T, H, D), dtype=torch.bfloat16, device=dev)
-    qcat = torch.empty((BANK, nb, ns * T, H, D), dtype=torch.bfloat16, device=dev)
+    ob = torch.empty((ns * T, H, D), dtype=cache.elem_dtype, device=dev)
+    qcat = torch.empty((BANK, nb, ns * T, H, D), dtype=cache.elem_dtype, device=dev)
     for s in range(ns):
         qcat[:, :, s * T:(s + 1) * T] = qb[s]
 
@@ -421,7 +426,7 @@ def main():
     out = {
         "metric": METRIC, "value": value, "unit": "frame-steps/s", "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": 1e3 * elapsed / K, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic",
+        "dtype": args.dtype, "data": "synthetic",
         "config": {"workload": (f"{wl.name}: {nb} blocks, H={H}, D={D}, {wl.patch_tokens} patch + "
                                 f"{wl.num_special_tokens} special tokens/frame, page_size {wl.page_size}, "
                                 f"scale {wl.scale_frames}, window {wl.sliding_window}, streams {ns} at "
@@ -474,7 +479,8 @@ def main():
     progress(json.dumps({k: out[k] for k in ("value", "ms_per_step")}))
     if not args.no_cpu_baseline:
         progress("timing the CPU oracle")
-        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+        import dataclasses
+        out["cpu_baseline"] = cpu_baseline(dataclasses.replace(wl, dtype=args.dtype), args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 2
+#define KVC_ABI_VERSION 3
 
 typedef struct kvc_ctx kvc_ctx;
 typedef void* kvc_stream_t;   /* hipStream_t */
@@ -101,7 +101,15 @@ typedef struct kvc_config {
   int32_t max_special_pages;   /* special pages shared by all streams, >= 0 */
   int32_t max_frames_per_step; /* most frames one stream appends in one step, 1..64: above 1 for the
                                   multi-frame scale phase ([p2] §Frame Processing Loop) */
+  int32_t dtype;               /* element type of the pools and of every k, v, q, o buffer:
+                                  KVC_DTYPE_BF16 (0) or KVC_DTYPE_F16 (1), the two 16-bit types the
+                                  paged kernels take natively ([p3] §Precision and Hardware
+                                  Utilization); below, "bf16" reads as this type */
 } kvc_config;
+
+/* Element types (kvc_config.dtype).  Both are 16-bit; arithmetic is MFMA on
+   the 16-bit values with float32 accumulation and softmax either way. */
+enum { KVC_DTYPE_BF16 = 0, KVC_DTYPE_F16 = 1 };
 
 /* [p3] §Inspecting Cache Statistics, plus the special-page counters. */
 typedef struct kvc_stats {

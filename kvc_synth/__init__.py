@@ -40,18 +40,43 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     return ((u + rounding) >> 16).astype(np.uint16)
 
 
+def f32_to_f16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to IEEE half (numpy's round to nearest even) and
+    return the 16-bit patterns as uint16."""
+    return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     """Exact widening of bf16 bit patterns to float32."""
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
+def bits_to_f32(b: np.ndarray, dtype: str = "bf16") -> np.ndarray:
+    """Exact widening of 16-bit patterns of the given element type ("bf16" or
+    "f16") to float32."""
+    if dtype == "bf16":
+        return bf16_bits_to_f32(b)
+    if dtype == "f16":
+        return np.ascontiguousarray(b, dtype=np.uint16).view(np.float16).astype(np.float32)
+    raise ValueError(f"unknown dtype {dtype}")
+
+
+def f32_to_bits(x: np.ndarray, dtype: str = "bf16") -> np.ndarray:
+    if dtype == "bf16":
+        return f32_to_bf16_bits(x)
+    if dtype == "f16":
+        return f32_to_f16_bits(x)
+    raise ValueError(f"unknown dtype {dtype}")
+
+
 def normal_bf16(seed: int, stream: int, frame: int, block: int, tensor: int, part: int,
-                shape, scale: float = 1.0) -> np.ndarray:
+                shape, scale: float = 1.0, dtype: str = "bf16") -> np.ndarray:
+    """Seeded N(0, scale^2) values rounded to the element type, as bits."""
     g = np.random.Generator(np.random.Philox(key=_key(seed, stream, frame, block, tensor, part)))
     x = g.standard_normal(shape, dtype=np.float32)
     if scale != 1.0:
         x = x * np.float32(scale)
-    return f32_to_bf16_bits(x)
+    return f32_to_bits(x, dtype)
 
 
 def special_rows(T: int, n_special: int, special_row_offset: int) -> np.ndarray:
@@ -67,8 +92,8 @@ def patch_rows(T: int, n_special: int, special_row_offset: int) -> np.ndarray:
 
 def frame_tensor(seed: int, stream: int, frame: int, block: int, which: str,
                  T: int, H: int, D: int, n_special: int, special_row_offset: int,
-                 scale: float = 1.0, patch_real: bool = True) -> np.ndarray:
-    """One frame's Q, K or V as bf16 bits, shape [T, H, D] (NHD).
+                 scale: float = 1.0, patch_real: bool = True, dtype: str = "bf16") -> np.ndarray:
+    """One frame's Q, K or V as 16-bit patterns of `dtype`, shape [T, H, D] (NHD).
 
     Patch rows and special rows are drawn from separate keys, so the special
     rows of any frame can be regenerated cheaply.  With patch_real=False the
@@ -79,18 +104,18 @@ def frame_tensor(seed: int, stream: int, frame: int, block: int, which: str,
     pr = patch_rows(T, n_special, special_row_offset)
     sr = special_rows(T, n_special, special_row_offset)
     if patch_real and len(pr):
-        out[pr] = normal_bf16(seed, stream, frame, block, t, PART_PATCH, (len(pr), H, D), scale)
+        out[pr] = normal_bf16(seed, stream, frame, block, t, PART_PATCH, (len(pr), H, D), scale, dtype)
     if len(sr):
-        out[sr] = normal_bf16(seed, stream, frame, block, t, PART_SPECIAL, (len(sr), H, D), scale)
+        out[sr] = normal_bf16(seed, stream, frame, block, t, PART_SPECIAL, (len(sr), H, D), scale, dtype)
     return out
 
 
 def special_part(seed: int, stream: int, frame: int, block: int, which: str,
-                 n_special: int, H: int, D: int, scale: float = 1.0) -> np.ndarray:
-    """Only the special rows of a frame, [n_special, H, D] bf16 bits (the same
+                 n_special: int, H: int, D: int, scale: float = 1.0, dtype: str = "bf16") -> np.ndarray:
+    """Only the special rows of a frame, [n_special, H, D] bits (the same
     values frame_tensor places at the special rows)."""
     return normal_bf16(seed, stream, frame, block, TENSOR_IDS[which], PART_SPECIAL,
-                       (n_special, H, D), scale)
+                       (n_special, H, D), scale, dtype)
 
 
 def free_list_order(seed: int, n: int, first_id: int, which: int) -> np.ndarray:
@@ -121,6 +146,7 @@ class Workload:
     max_special_pages: int
     shuffle_free_lists: bool = False
     special_row_offset: Optional[int] = None   # None: specials after the patches
+    dtype: str = "bf16"                         # element type: "bf16" or "f16"
 
     @property
     def tokens_per_frame(self) -> int:

@@ -56,7 +56,7 @@ from typing import Callable, Dict, List, Optional, Sequence, Tuple
 
 import numpy as np
 
-from kvc_synth import bf16_bits_to_f32, patch_rows, special_rows
+from kvc_synth import bits_to_f32, patch_rows, special_rows
 
 
 @dataclasses.dataclass
@@ -72,6 +72,7 @@ class OracleConfig:
     max_special_pages: int
     num_streams: int = 1
     special_row_offset: Optional[int] = None   # None: specials after patches
+    dtype: str = "bf16"                        # element type of K, V, Q: "bf16" or "f16"
 
     @property
     def patch_tokens(self) -> int:
@@ -375,18 +376,20 @@ def gather_paged(cfg: OracleConfig, pool: SimulatedPool, plan: Dict[str, np.ndar
     return np.concatenate(ks, axis=0), np.concatenate(vs, axis=0)
 
 
-def attention_fp64(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray) -> np.ndarray:
+def attention_fp64(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray, dtype: str = "bf16") -> np.ndarray:
     """Unmasked softmax attention of every query row over every given key,
-    per head, in float64 from the exact bf16 values:
+    per head, in float64 from the exact 16-bit values (bf16, or f16 for the
+    16-bit float the paged kernels also take natively, [p3] §Precision and
+    Hardware Utilization):
     O = softmax(Q K^T / sqrt(D)) V  ([p1] §Efficient Attention Masking and
     Padding: no boolean mask; [p5] §Kernel Dispatch and Sequence Lengths:
     exact weights over the valid tokens).
 
-    q_bits [T, H, D], k_bits and v_bits [L, H, D] (uint16 bf16 patterns).
+    q_bits [T, H, D], k_bits and v_bits [L, H, D] (uint16 patterns of dtype).
     Returns [T, H, D] float64."""
-    q = bf16_bits_to_f32(q_bits).astype(np.float64)
-    k = bf16_bits_to_f32(k_bits).astype(np.float64)
-    v = bf16_bits_to_f32(v_bits).astype(np.float64)
+    q = bits_to_f32(q_bits, dtype).astype(np.float64)
+    k = bits_to_f32(k_bits, dtype).astype(np.float64)
+    v = bits_to_f32(v_bits, dtype).astype(np.float64)
     T, H, D = q.shape
     out = np.empty((T, H, D), dtype=np.float64)
     scale = 1.0 / math.sqrt(D)
@@ -399,11 +402,11 @@ def attention_fp64(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray) -
     return out
 
 
-def lse_base2_fp64(q_bits: np.ndarray, k_bits: np.ndarray) -> np.ndarray:
+def lse_base2_fp64(q_bits: np.ndarray, k_bits: np.ndarray, dtype: str = "bf16") -> np.ndarray:
     """log2 of sum_j exp(q.k_j / sqrt(D)) per query row and head, [T, H]; used
     to check split-KV partial results."""
-    q = bf16_bits_to_f32(q_bits).astype(np.float64)
-    k = bf16_bits_to_f32(k_bits).astype(np.float64)
+    q = bits_to_f32(q_bits, dtype).astype(np.float64)
+    k = bits_to_f32(k_bits, dtype).astype(np.float64)
     T, H, D = q.shape
     out = np.empty((T, H), dtype=np.float64)
     for h in range(H):
@@ -458,5 +461,5 @@ class OracleStream:
         outs = []
         for i in range(len(plan["last_page_len"])):
             k, v = gather_paged(self.cfg, self.pools[block], plan, i)
-            outs.append(attention_fp64(q_bits[qo[i]:qo[i + 1]], k, v))
+            outs.append(attention_fp64(q_bits[qo[i]:qo[i + 1]], k, v, self.cfg.dtype))
         return np.concatenate(outs, axis=0)

@@ -35,13 +35,16 @@ KVC_OPT_TARGET_WORKGROUPS = 1
 KVC_OPT_MAX_SPLITS = 2
 KVC_OPT_PROFILE = 3
 KVC_OPT_DEFER_EVICTION = 4
+KVC_DTYPE_BF16 = 0
+KVC_DTYPE_F16 = 1
+DTYPES = {"bf16": KVC_DTYPE_BF16, "f16": KVC_DTYPE_F16}
 
 KVC_KERNEL_ATTENTION = 0
 KVC_KERNEL_MERGE = 1
 KVC_KERNEL_APPEND = 2
 
 MAX_SPLITS = 64
-ABI_VERSION = 2   # KVC_ABI_VERSION of include/kvc.h
+ABI_VERSION = 3   # KVC_ABI_VERSION of include/kvc.h
 
 
 class KvcError(RuntimeError):
@@ -54,7 +57,7 @@ class KvcConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "num_blocks", "num_heads", "head_dim", "tokens_per_frame", "num_special_tokens",
         "special_row_offset", "page_size", "scale_frames", "sliding_window", "num_streams",
-        "max_patch_pages", "max_special_pages", "max_frames_per_step")]
+        "max_patch_pages", "max_special_pages", "max_frames_per_step", "dtype")]
 
 
 class KvcStats(ctypes.Structure):
@@ -122,7 +125,7 @@ def _ceil_div(a, b):
 def make_config(num_blocks, num_heads, head_dim, tokens_per_frame, num_special_tokens=6, page_size=None,
                 scale_frames=8, sliding_window=64, num_streams=1, max_patch_pages=None,
                 max_special_pages=None, max_total_frames=None, special_row_offset=None,
-                max_frames_per_step=1) -> KvcConfig:
+                max_frames_per_step=1, dtype="bf16") -> KvcConfig:
     """Build a kvc_config.  Defaults follow [p2] §Initializing the Cache
     Manager: page_size = patch tokens, patch pages = S + W + 16 headroom per
     stream, special pages sized for max_total_frames."""
@@ -136,9 +139,11 @@ def make_config(num_blocks, num_heads, head_dim, tokens_per_frame, num_special_t
         max_special_pages = num_streams * _ceil_div(total * num_special_tokens, page_size)
     if special_row_offset is None:
         special_row_offset = P
+    if dtype not in DTYPES:
+        raise KvcError(KVC_ERR_ARG, f"dtype must be one of {sorted(DTYPES)}")
     return KvcConfig(num_blocks, num_heads, head_dim, tokens_per_frame, num_special_tokens, special_row_offset,
                      page_size, scale_frames, sliding_window, num_streams, max_patch_pages, max_special_pages,
-                     max_frames_per_step)
+                     max_frames_per_step, DTYPES[dtype])
 
 
 class PagedKVCache:
@@ -162,6 +167,7 @@ class PagedKVCache:
             return
         import torch
         self.torch = torch
+        self.elem_dtype = {KVC_DTYPE_BF16: torch.bfloat16, KVC_DTYPE_F16: torch.float16}[config.dtype]
         self.device = torch.device(device)
         if self.device.type == "cuda" and self.device.index is None:
             self.device = torch.device("cuda", torch.cuda.current_device())
@@ -173,7 +179,7 @@ class PagedKVCache:
         pages = config.max_patch_pages + config.max_special_pages
         shape = (pages, 2, config.page_size, config.num_heads, config.head_dim)
         with torch.cuda.device(self.device):
-            self.pools = [torch.empty(shape, dtype=torch.bfloat16, device=self.device)
+            self.pools = [torch.empty(shape, dtype=self.elem_dtype, device=self.device)
                           for _ in range(config.num_blocks)]
             self.workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=self.device)
             self.staging = torch.empty(st_bytes, dtype=torch.uint8, pin_memory=True)
@@ -203,9 +209,9 @@ class PagedKVCache:
 
     def _check_tensor(self, t, rows, name):
         c = self.cfg
-        if t.dtype != self.torch.bfloat16 or not t.is_contiguous() or t.device != self.device \
+        if t.dtype != self.elem_dtype or not t.is_contiguous() or t.device != self.device \
                 or tuple(t.shape) != (rows, c.num_heads, c.head_dim):
-            raise KvcError(KVC_ERR_ARG, f"{name} must be a contiguous bf16 [{rows}, {c.num_heads}, "
+            raise KvcError(KVC_ERR_ARG, f"{name} must be a contiguous {self.elem_dtype} [{rows}, {c.num_heads}, "
                                         f"{c.head_dim}] tensor on {self.device}")
 
     # -- the method ------------------------------------------------------

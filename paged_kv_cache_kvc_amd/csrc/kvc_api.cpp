@@ -35,6 +35,7 @@ kvc::Config to_cfg(const kvc_config& c) {
   k.max_patch_pages = c.max_patch_pages;
   k.max_special_pages = c.max_special_pages;
   k.max_frames_per_step = c.max_frames_per_step;
+  k.dtype = c.dtype;
   return k;
 }
 
@@ -443,6 +444,7 @@ kvc_status kvc_run(kvc_ctx* c, int32_t block, const void* q, void* o, kvc_stream
   a.div_page = kvc::make_fastdiv((uint32_t)cf.page_size);
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)cf.head_dim));
   a.num_items = c->plan.num_items;
+  a.dtype = cf.dtype;
   a.items_per_xcd = (c->plan.num_items + 7) / 8;
   const int32_t grid = 8 * a.items_per_xcd;
   int e = timed(c, KVC_KERNEL_ATTENTION, hs, [&] { return kvc::launch_attention(a, grid, hs); });
@@ -461,6 +463,7 @@ kvc_status kvc_run(kvc_ctx* c, int32_t block, const void* q, void* o, kvc_stream
     m.tile_table = c->plan.tile_table;
     m.merge_table = c->plan.merge_table;
     m.merge_slots = c->plan.merge_slots;
+    m.dtype = cf.dtype;
     e = timed(c, KVC_KERNEL_MERGE, hs, [&] { return kvc::launch_merge(m, hs); });
     if (e) return hip_fail(c, e, "merge launch");
   }

@@ -35,6 +35,7 @@ int validate(const Config& c, std::string* why) {
   if ((int64_t)c.num_heads * c.head_dim > 65536) return fail(ERR_UNSUPPORTED, "num_heads * head_dim above 65536");
   if (c.max_frames_per_step < 1 || c.max_frames_per_step > 64)
     return fail(ERR_ARG, "max_frames_per_step must be in [1, 64]");
+  if (c.dtype != 0 && c.dtype != 1) return fail(ERR_UNSUPPORTED, "dtype must be KVC_DTYPE_BF16 or KVC_DTYPE_F16");
   if ((int64_t)c.num_streams * c.max_frames_per_step * c.tokens_per_frame >= (int64_t)1 << 24)
     return fail(ERR_UNSUPPORTED, "too many query rows");
   return OK;

@@ -26,6 +26,7 @@ struct Config {
   int32_t scale_frames = 0, sliding_window = 0, num_streams = 0;
   int32_t max_patch_pages = 0, max_special_pages = 0;
   int32_t max_frames_per_step = 1;
+  int32_t dtype = 0;   // element type: 0 bfloat16, 1 float16
 
   int32_t patch_tokens() const { return tokens_per_frame - num_special_tokens; }
   int32_t max_num_pages() const { return max_patch_pages + max_special_pages; }

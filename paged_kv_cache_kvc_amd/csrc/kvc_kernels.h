@@ -41,6 +41,7 @@ struct AttnParams {
   FastDiv div_patch, div_page;
   float scale_log2;         // log2(e) / sqrt(D)
   int32_t num_items, items_per_xcd;
+  int32_t dtype;            // element type: 0 bfloat16, 1 float16
 };
 
 struct MergeParams {
@@ -53,6 +54,7 @@ struct MergeParams {
   int32_t tile_table;       // offset in ints of the plan's tile table
   int32_t merge_table;      // offset in ints of the plan's merge order
   int32_t merge_slots;      // merge slots per XCD
+  int32_t dtype;            // element type: 0 bfloat16, 1 float16
 };
 
 // Return 0 on success or the hipError_t value.

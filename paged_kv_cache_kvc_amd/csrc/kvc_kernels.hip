@@ -55,6 +55,69 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int KT = KVC_KV_TILE;
 
+// Element type of the pools, k, v, q, o and the split partials: E = 0
+// bfloat16, E = 1 float16.  Operands travel as raw 16-bit pairs (bf16x8
+// registers) and take their type only in the MFMA, the probability packing,
+// the row-sum dot product and the conversions to and from float32.
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+template <int E>
+struct El;
+
+template <>
+struct El<0> {
+  static __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  // bf16 pair of p (lo, hi): the upper halves of the float32 values (rounded
+  // toward zero), one byte permute per pair
+  static __device__ __forceinline__ uint32_t pack_p(float lo, float hi) {
+    return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, hi), __builtin_bit_cast(uint32_t, lo), 0x07060302u);
+  }
+  static __device__ __forceinline__ float dot_ones(uint32_t w, float acc) {
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, acc, false);
+  }
+  // round to nearest even
+  static __device__ __forceinline__ u32x2 cvt4(const f32x4& v) {
+    const bf16x4 b = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+    return __builtin_bit_cast(u32x2, b);
+  }
+  static __device__ __forceinline__ f32x4 widen4(const u32x2& x) {
+    const bf16x4 b = __builtin_bit_cast(bf16x4, x);
+    return f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
+  }
+};
+
+template <>
+struct El<1> {
+  static __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                   0, 0);
+  }
+  // f16 pair of p (lo, hi), rounded toward zero in one packing conversion;
+  // p <= 2^8 here, inside the f16 range
+  static __device__ __forceinline__ uint32_t pack_p(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+  }
+  static __device__ __forceinline__ float dot_ones(uint32_t w, float acc) {
+    const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), ones, acc, false);
+  }
+  static __device__ __forceinline__ u32x2 cvt4(const f32x4& v) {
+    typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+    const f16x4 b = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+    return __builtin_bit_cast(u32x2, b);
+  }
+  static __device__ __forceinline__ f32x4 widen4(const u32x2& x) {
+    typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+    const f16x4 b = __builtin_bit_cast(f16x4, x);
+    return f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
+  }
+};
+
 __device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
   return (__umulhi(n, f.mul) + n) >> f.shr;
 }
@@ -231,9 +294,10 @@ __device__ __forceinline__ float lane_swap_sum(float x) {
 // slot always takes the exact path.
 constexpr float LAZY_SUM_LIMIT = 256.0f;
 
-template <int D>
+template <int D, int E>
 struct Ops {
   using S = Shape<D>;
+  using T = El<E>;
   static constexpr int KS = S::KSTEPS;
   static constexpr int DB = S::DBLK;
 
@@ -241,17 +305,16 @@ struct Ops {
   static __device__ __forceinline__ void qk(const bf16x8 (&kop)[4][KS], const bf16x8 (&q)[KS], f32x4 (&s)[4]) {
 #pragma unroll
     for (int kbi = 0; kbi < 4; ++kbi) {
-      s[kbi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kbi][0], q[0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      s[kbi] = T::mfma(kop[kbi][0], q[0], f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-      for (int ks = 1; ks < KS; ++ks)
-        s[kbi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kbi][ks], q[ks], s[kbi], 0, 0, 0);
+      for (int ks = 1; ks < KS; ++ks) s[kbi] = T::mfma(kop[kbi][ks], q[ks], s[kbi]);
     }
   }
   // the same for one 16-kv block
   static __device__ __forceinline__ void qk1(const bf16x8 (&k)[KS], const bf16x8 (&q)[KS], f32x4 (&s)[1]) {
-    s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k[0], q[0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+    s[0] = T::mfma(k[0], q[0], f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-    for (int ks = 1; ks < KS; ++ks) s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k[ks], q[ks], s[0], 0, 0, 0);
+    for (int ks = 1; ks < KS; ++ks) s[0] = T::mfma(k[ks], q[ks], s[0]);
   }
   // O^T[D x 16 q] += V^T P^T over the stage's two 32-kv pairs
   static __device__ __forceinline__ void pv(const bf16x8 (&vop)[DB][2], const u32x4 (&pb)[2], f32x4 (&o)[DB]) {
@@ -259,45 +322,38 @@ struct Ops {
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int pp = 0; pp < 2; ++pp)
-        o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[db][pp], __builtin_bit_cast(bf16x8, pb[pp]), o[db], 0,
-                                                        0, 0);
+        o[db] = T::mfma(vop[db][pp], __builtin_bit_cast(bf16x8, pb[pp]), o[db]);
   }
   // ... over one pair
   template <int PP>
   static __device__ __forceinline__ void pv1(const bf16x8 (&vop)[DB][2], const u32x4& pb, f32x4 (&o)[DB]) {
 #pragma unroll
     for (int db = 0; db < DB; ++db)
-      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[db][PP], __builtin_bit_cast(bf16x8, pb), o[db], 0, 0, 0);
+      o[db] = T::mfma(vop[db][PP], __builtin_bit_cast(bf16x8, pb), o[db]);
   }
 };
 
-// p = 2^(s * scale - ref) packed in pairs as bf16 (the P^T operand), and the
-// lane's sum of the packed values (the same numbers the P.V product uses).
-// The bf16 value is the upper half of the float32 (rounded toward zero): one
-// byte permute per pair instead of a rounding conversion.  Its relative error
-// has the same spread as round-to-nearest (one bf16 ulp wide) and a mean of
-// half an ulp; numerator and denominator are sums over the same rounded
-// weights, so that mean cancels in the normalisation.
-__device__ __forceinline__ uint32_t pack_hi16(float lo, float hi) {
-  return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, hi), __builtin_bit_cast(uint32_t, lo), 0x07060302u);
-}
-
-template <int N>
+// p = 2^(s * scale - ref) packed in pairs in the element type (the P^T
+// operand), and the lane's sum of the packed values (the same numbers the P.V
+// product uses).  The packing rounds toward zero (for bf16 it keeps the upper
+// half of the float32: one byte permute per pair): its relative error has the
+// same spread as round-to-nearest (one ulp wide) and a mean of half an ulp,
+// and numerator and denominator are sums over the same rounded weights, so
+// that mean cancels in the normalisation.
+template <int N, int E>
 __device__ __forceinline__ float probs(const f32x4 (&s)[N], float sl, float nref, uint32_t (&pk)[2 * N]) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   float a = 0.f, b = 0.f;
 #pragma unroll
   for (int i = 0; i < N; ++i)
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const uint32_t w = pack_hi16(__builtin_amdgcn_exp2f(__builtin_fmaf(s[i][2 * h], sl, nref)),
-                                   __builtin_amdgcn_exp2f(__builtin_fmaf(s[i][2 * h + 1], sl, nref)));
+      const uint32_t w = El<E>::pack_p(__builtin_amdgcn_exp2f(__builtin_fmaf(s[i][2 * h], sl, nref)),
+                                       __builtin_amdgcn_exp2f(__builtin_fmaf(s[i][2 * h + 1], sl, nref)));
       pk[2 * i + h] = w;
       if (h == 0)
-        a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, a, false);
+        a = El<E>::dot_ones(w, a);
       else
-        b = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, b, false);
+        b = El<E>::dot_ones(w, b);
     }
   return a + b;
 }
@@ -324,7 +380,7 @@ __device__ __forceinline__ void mask_scores(f32x4 (&s)[N], const int (&boff)[N],
 // the same masked slots, so the maximum is -inf in all lanes or in none; a
 // fresh tile whose slots were all masked stays fresh.  Taken rarely; a few
 // wait states at both ends keep it clear of the MFMAs around it.
-template <int N, int DB>
+template <int N, int DB, int E>
 __device__ __forceinline__ float renorm(const f32x4 (&s)[N], float sl, bool& fresh, float& ref, float& nref,
                                         float& l, f32x4 (&o)[DB], uint32_t (&pk)[2 * N]) {
   asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
@@ -345,7 +401,7 @@ __device__ __forceinline__ float renorm(const f32x4 (&s)[N], float sl, bool& fre
   }
   ref += shift;
   nref = -ref;
-  const float lt = probs<N>(s, sl, nref, pk);
+  const float lt = probs<N, E>(s, sl, nref, pk);
   asm volatile("s_nop 3" ::: "memory");
   return lt;
 }
@@ -370,10 +426,10 @@ __device__ __forceinline__ float renorm(const f32x4 (&s)[N], float sl, bool& fre
 // step after its MFMA at the earliest.  After the last stage the same code
 // reads a ring slot that holds no stage and computes a QK^T that is never
 // used; every LDS address stays inside the ring.
-template <int D>
+template <int D, int E>
 __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams p) {
   using S = Shape<D>;
-  using O = Ops<D>;
+  using O = Ops<D, E>;
   constexpr int KS = S::KSTEPS;
   constexpr int DB = S::DBLK;
   constexpr int LPW = S::LOADS_PER_WAVE;
@@ -616,9 +672,9 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
     vq1 = vq2;
     vq2 = en.z;
     read_k(s + 1, kop);
-    float lt = probs<4>(sc0, sl, nref0, pk0);
+    float lt = probs<4, E>(sc0, sl, nref0, pk0);
     asm volatile("" ::"v"(lt));   // keep the common path ahead of the branch, next to the MFMAs
-    if (fresh0 || __builtin_amdgcn_ballot_w64(lt > LAZY_SUM_LIMIT)) lt = renorm<4, DB>(sc0, sl, fresh0, ref0, nref0, l0, o0, pk0);
+    if (fresh0 || __builtin_amdgcn_ballot_w64(lt > LAZY_SUM_LIMIT)) lt = renorm<4, DB, E>(sc0, sl, fresh0, ref0, nref0, l0, o0, pk0);
     l0 += lt;
 
     // ---- step 1: own tile 1 ----
@@ -628,18 +684,18 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
       u32x4 pb[2] = {u32x4{pk0[0], pk0[1], pk0[2], pk0[3]}, u32x4{pk0[4], pk0[5], pk0[6], pk0[7]}};
       O::pv(vop, pb, o0);
     }
-    lt = probs<4>(sc1, sl, nref1, pk1);
+    lt = probs<4, E>(sc1, sl, nref1, pk1);
     asm volatile("" ::"v"(lt));
-    if (fresh1 || __builtin_amdgcn_ballot_w64(lt > LAZY_SUM_LIMIT)) lt = renorm<4, DB>(sc1, sl, fresh1, ref1, nref1, l1, o1, pk1);
+    if (fresh1 || __builtin_amdgcn_ballot_w64(lt > LAZY_SUM_LIMIT)) lt = renorm<4, DB, E>(sc1, sl, fresh1, ref1, nref1, l1, o1, pk1);
     l1 += lt;
     read_ksh(s + 1, ksh);
 
     // ---- step 2: shared tile ----
     if (partial) mask_scores<1>(sc2, kb_sh, valid, g4);
     O::qk(kop, q0, sc0);
-    lt = probs<1>(sc2, sl, nref2, pk2);
+    lt = probs<1, E>(sc2, sl, nref2, pk2);
     asm volatile("" ::"v"(lt));
-    if (fresh2 || __builtin_amdgcn_ballot_w64(lt > LAZY_SUM_LIMIT)) lt = renorm<1, DB>(sc2, sl, fresh2, ref2, nref2, l2, o2, pk2);
+    if (fresh2 || __builtin_amdgcn_ballot_w64(lt > LAZY_SUM_LIMIT)) lt = renorm<1, DB, E>(sc2, sl, fresh2, ref2, nref2, l2, o2, pk2);
     l2 += lt;
     // P^T of the shared block: its 4 slots sit at positions 4*half..4*half+3
     // of the pair's operand; the other half is zero
@@ -666,15 +722,7 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
       const size_t pt = ((size_t)split * H + h) * p.tiles_cap + st.q_tile0 + tile;
       uint16_t* po = static_cast<uint16_t*>(p.part_o) + pt * DB * 256 + lane * 4;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const f32x4 v = o[db] * inv;
-        bf16x4 b;
-        b[0] = (__bf16)v[0];
-        b[1] = (__bf16)v[1];
-        b[2] = (__bf16)v[2];
-        b[3] = (__bf16)v[3];
-        *reinterpret_cast<bf16x4*>(po + db * 256) = b;
-      }
+      for (int db = 0; db < DB; ++db) *reinterpret_cast<u32x2*>(po + db * 256) = El<E>::cvt4(o[db] * inv);
       if (g4 == 0) p.part_lse[pt * KVC_Q_TILE + r16] = ref + __log2f(l);
       return;
     }
@@ -683,15 +731,7 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
     {
       uint16_t* orow = static_cast<uint16_t*>(p.o) + ((size_t)grow * H + h) * D;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const f32x4 v = o[db] * inv;
-        bf16x4 b;
-        b[0] = (__bf16)v[0];
-        b[1] = (__bf16)v[1];
-        b[2] = (__bf16)v[2];
-        b[3] = (__bf16)v[3];
-        *reinterpret_cast<bf16x4*>(orow + 16 * db + 4 * g4) = b;
-      }
+      for (int db = 0; db < DB; ++db) *reinterpret_cast<u32x2*>(orow + 16 * db + 4 * g4) = El<E>::cvt4(o[db] * inv);
     }
   };
   if (wave < n_own) store(t_lo + wave, ref0, lane_swap_sum(l0), o0);
@@ -750,7 +790,7 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
 // have more) are loaded from the workspace but never used.
 constexpr int MERGE_CHUNK = 16;
 
-template <int D>
+template <int D, int E>
 __global__ __launch_bounds__(512) void merge_kernel(MergeParams p) {
   constexpr int DB = D / 16;
   const int lane = threadIdx.x & 63;
@@ -772,13 +812,13 @@ __global__ __launch_bounds__(512) void merge_kernel(MergeParams p) {
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int c0 = 0; c0 < p.max_split; c0 += MERGE_CHUNK) {
     float lse[MERGE_CHUNK];
-    bf16x4 x[MERGE_CHUNK];
+    u32x2 x[MERGE_CHUNK];
 #pragma unroll
     for (int j = 0; j < MERGE_CHUNK; ++j)
       if (c0 + j < p.max_split) {
         const size_t c = (size_t)(c0 + j) * tstride;
         lse[j] = pl[c * KVC_Q_TILE];
-        x[j] = *reinterpret_cast<const bf16x4*>(po + c * DB * 256);
+        x[j] = *reinterpret_cast<const u32x2*>(po + c * DB * 256);
       }
     const int nsp = te.x;
     if (nsp <= 1) return;                 // single split: attention wrote o itself
@@ -794,20 +834,14 @@ __global__ __launch_bounds__(512) void merge_kernel(MergeParams p) {
     for (int j = 0; j < MERGE_CHUNK; ++j)
       if (c0 + j < nsp) {
         const float w = __builtin_amdgcn_exp2f(lse[j] - mc);
-        acc += w * f32x4{(float)x[j][0], (float)x[j][1], (float)x[j][2], (float)x[j][3]};
+        acc += w * El<E>::widen4(x[j]);
         wsum += w;
       }
     m = mc;
   }
   if (r16 < te.z) {
-    const f32x4 v = acc * (1.0f / wsum);
-    bf16x4 b;
-    b[0] = (__bf16)v[0];
-    b[1] = (__bf16)v[1];
-    b[2] = (__bf16)v[2];
-    b[3] = (__bf16)v[3];
-    *reinterpret_cast<bf16x4*>(static_cast<uint16_t*>(p.o) + ((size_t)(te.y + r16) * H + h) * D + 16 * db + 4 * g4) =
-        b;
+    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.o) + ((size_t)(te.y + r16) * H + h) * D + 16 * db + 4 * g4) =
+        El<E>::cvt4(acc * (1.0f / wsum));
   }
 }
 
@@ -818,17 +852,43 @@ int launch_append(const AppendParams& p, void* s) {
   return (int)hipGetLastError();
 }
 
-int launch_attention(const AttnParams& p, int32_t grid, void* s) {
-  const hipStream_t hs = (hipStream_t)s;
+// Instantiations by (D, element type).
+template <int E>
+static int launch_attention_e(const AttnParams& p, int32_t grid, hipStream_t hs) {
   switch (p.head_dim) {
     case 32:
-      hipLaunchKernelGGL((attn_kernel<32>), dim3(grid), dim3(256), 0, hs, p);
+      hipLaunchKernelGGL((attn_kernel<32, E>), dim3(grid), dim3(256), 0, hs, p);
       break;
     case 64:
-      hipLaunchKernelGGL((attn_kernel<64>), dim3(grid), dim3(256), 0, hs, p);
+      hipLaunchKernelGGL((attn_kernel<64, E>), dim3(grid), dim3(256), 0, hs, p);
       break;
     case 128:
-      hipLaunchKernelGGL((attn_kernel<128>), dim3(grid), dim3(256), 0, hs, p);
+      hipLaunchKernelGGL((attn_kernel<128, E>), dim3(grid), dim3(256), 0, hs, p);
+      break;
+    default:
+      return (int)hipErrorInvalidValue;
+  }
+  return (int)hipGetLastError();
+}
+
+int launch_attention(const AttnParams& p, int32_t grid, void* s) {
+  const hipStream_t hs = (hipStream_t)s;
+  if (p.dtype == 0) return launch_attention_e<0>(p, grid, hs);
+  if (p.dtype == 1) return launch_attention_e<1>(p, grid, hs);
+  return (int)hipErrorInvalidValue;
+}
+
+template <int E>
+static int launch_merge_e(const MergeParams& p, int grid, int threads, hipStream_t hs) {
+  switch (p.head_dim) {
+    case 32:
+      hipLaunchKernelGGL((merge_kernel<32, E>), dim3(grid), dim3(threads), 0, hs, p);
+      break;
+    case 64:
+      hipLaunchKernelGGL((merge_kernel<64, E>), dim3(grid), dim3(threads), 0, hs, p);
+      break;
+    case 128:
+      hipLaunchKernelGGL((merge_kernel<128, E>), dim3(grid), dim3(threads), 0, hs, p);
       break;
     default:
       return (int)hipErrorInvalidValue;
@@ -841,20 +901,9 @@ int launch_merge(const MergeParams& p, void* s) {
   const int grid = KVC_NUM_XCD * p.merge_slots;   // one work-group per merged (query tile, head)
   if (grid == 0) return 0;
   const int threads = 64 * (p.head_dim / 16);   // one wave per 16-row d block
-  switch (p.head_dim) {
-    case 32:
-      hipLaunchKernelGGL(merge_kernel<32>, dim3(grid), dim3(threads), 0, hs, p);
-      break;
-    case 64:
-      hipLaunchKernelGGL(merge_kernel<64>, dim3(grid), dim3(threads), 0, hs, p);
-      break;
-    case 128:
-      hipLaunchKernelGGL(merge_kernel<128>, dim3(grid), dim3(threads), 0, hs, p);
-      break;
-    default:
-      return (int)hipErrorInvalidValue;
-  }
-  return (int)hipGetLastError();
+  if (p.dtype == 0) return launch_merge_e<0>(p, grid, threads, hs);
+  if (p.dtype == 1) return launch_merge_e<1>(p, grid, threads, hs);
+  return (int)hipErrorInvalidValue;
 }
 
 }  // namespace kvc

@@ -17,7 +17,7 @@ def cfg_args(wl: syn.Workload, num_blocks: int):
                 tokens_per_frame=wl.tokens_per_frame, num_special_tokens=wl.num_special_tokens,
                 page_size=wl.page_size, scale_frames=wl.scale_frames, sliding_window=wl.sliding_window,
                 num_streams=wl.num_streams, max_patch_pages=wl.max_patch_pages,
-                max_special_pages=wl.max_special_pages, special_row_offset=wl.row_offset)
+                max_special_pages=wl.max_special_pages, special_row_offset=wl.row_offset, dtype=wl.dtype)
 
 
 def oracle_cfg(wl: syn.Workload) -> ko.OracleConfig:
@@ -25,7 +25,8 @@ def oracle_cfg(wl: syn.Workload) -> ko.OracleConfig:
                            num_special_tokens=wl.num_special_tokens, page_size=wl.page_size,
                            scale_frames=wl.scale_frames, sliding_window=wl.sliding_window,
                            max_patch_pages=wl.max_patch_pages, max_special_pages=wl.max_special_pages,
-                           num_streams=wl.num_streams, special_row_offset=wl.special_row_offset)
+                           num_streams=wl.num_streams, special_row_offset=wl.special_row_offset,
+                           dtype=wl.dtype)
 
 
 def free_orders(wl: syn.Workload, seed: Optional[int] = None):
@@ -47,14 +48,14 @@ def final_visible(wl: syn.Workload, stream: int, extra_steps: Sequence[int] = ()
     return out
 
 
-def bits_to_f32(bits: np.ndarray) -> np.ndarray:
-    return syn.bf16_bits_to_f32(bits)
+def bits_to_f32(bits: np.ndarray, dtype: str = "bf16") -> np.ndarray:
+    return syn.bits_to_f32(bits, dtype)
 
 
-def check_close(out_bits: np.ndarray, ref: np.ndarray, atol=1e-2, rtol=1e-2) -> Dict[str, float]:
+def check_close(out_bits: np.ndarray, ref: np.ndarray, atol=1e-2, rtol=1e-2, dtype: str = "bf16") -> Dict[str, float]:
     """The acceptance test: |o - o_ref| <= atol + rtol * |o_ref| elementwise;
     returns error statistics."""
-    o = bits_to_f32(out_bits).astype(np.float64)
+    o = bits_to_f32(out_bits, dtype).astype(np.float64)
     err = np.abs(o - ref)
     bound = atol + rtol * np.abs(ref)
     bad = err > bound
@@ -99,7 +100,7 @@ class Harness:
         # its allocator's count, the inputs are drawn by frame_of
         self.skew = [0] * wl.num_streams
         T, H, D = wl.tokens_per_frame, wl.num_heads, wl.head_dim
-        self.kbuf = torch.empty((T, H, D), dtype=torch.bfloat16, device=device)
+        self.kbuf = torch.empty((T, H, D), dtype=self.gpu.elem_dtype, device=device)
         self.vbuf = torch.empty_like(self.kbuf)
         self.device = device
 
@@ -108,10 +109,10 @@ class Harness:
         return syn.frame_tensor(wl.seed, s, f, b, which, wl.tokens_per_frame, wl.num_heads, wl.head_dim,
                                 wl.num_special_tokens, wl.row_offset,
                                 scale=self.q_scale if which == "q" else 1.0,
-                                patch_real=self.real_patch(s, f) or which == "q")
+                                patch_real=self.real_patch(s, f) or which == "q", dtype=wl.dtype)
 
     def to_dev(self, bits: np.ndarray, out=None):
-        t = self.torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(self.torch.bfloat16)
+        t = self.torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(self.gpu.elem_dtype)
         if out is None:
             return t.to(self.device)
         out.copy_(t)

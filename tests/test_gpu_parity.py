@@ -263,3 +263,43 @@ def test_deferred_eviction_with_rollbacks():
             assert e.value.status == kvc.KVC_ERR_STATE
     assert h.gpu.get_cache_stats()["frame_count"] == max(wl.frames) - rolled
     assert np.array_equal(h.pool_bits(0), h.ora.pools[0].data)
+
+
+def test_f16_pools_d32_d64_d128():
+    """IEEE-half pools and inputs ([p3] §Precision and Hardware Utilization:
+    the paged kernels take fp16 as well as bf16): the tiny stream at every
+    step (D=32, two blocks, pools bit-exact), the base shape with sharpened
+    queries split and unsplit (D=64), and D=128 over a shorter stream, each
+    against the oracle on the same f16 inputs."""
+    _need_gpu()
+    import dataclasses
+    import paged_kv_cache_kvc_amd as kvc
+    wl = dataclasses.replace(syn.WORKLOADS["tiny"], dtype="f16")
+    h = Harness(wl, num_blocks=2, oracle_blocks=(0, 1))
+    for t in range(max(wl.frames)):
+        res = h.step(check=True)
+        compare_plan(res)
+        for b in (0, 1):
+            st = check_close(res["out_bits"][b], res["ref"][b], dtype="f16")
+            assert np.array_equal(h.pool_bits(b), h.ora.pools[b].data), f"pool block {b} step {t}"
+    log(f"f16 tiny ok {st}")
+    wl = dataclasses.replace(_base_small(H=4, frames=80), dtype="f16")
+    outs = []
+    for opts in ({}, {kvc.KVC_OPT_MAX_SPLITS: 1}):
+        h = Harness(wl, q_scale=3.0, options=opts)
+        for t in range(max(wl.frames)):
+            res = h.step(run=t in (0, 79), check=t in (0, 79))
+            if t in (0, 79):
+                st = check_close(res["out_bits"][0], res["ref"][0], dtype="f16")
+        outs.append(syn.bits_to_f32(res["out_bits"][0], "f16"))
+        log(f"f16 base opts {opts} splits {res['gpu_plan']['n_splits']} {st}")
+        assert np.array_equal(h.pool_bits(0), h.ora.pools[0].data)
+    assert np.max(np.abs(outs[0] - outs[1])) <= 2 ** -7 * np.max(np.abs(outs[1])) + 1e-6
+    wl = dataclasses.replace(_base_small(H=2, frames=75), head_dim=128, dtype="f16")
+    h = Harness(wl)
+    for t in range(max(wl.frames)):
+        res = h.step(run=t in (3, 74), check=t in (3, 74))
+        if t in (3, 74):
+            compare_plan(res)
+            st = check_close(res["out_bits"][0], res["ref"][0], dtype="f16")
+            log(f"f16 D=128 step {t} splits {res['gpu_plan']['n_splits']} {st}")

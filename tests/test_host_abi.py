@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, n), n
         assert n in kvc.SIGNATURES, n
     assert set(kvc.SIGNATURES) == set(names)
-    assert lib.kvc_abi_version() == kvc.ABI_VERSION == 2
+    assert lib.kvc_abi_version() == kvc.ABI_VERSION == 3
 
 
 def cfg_of(wl: syn.Workload):
@@ -156,6 +156,14 @@ def test_bad_arguments_and_capacity():
     small = cfg_of(wl)
     small.max_patch_pages = wl.scale_frames + wl.sliding_window      # no room for the appended frame
     assert lib.kvc_create_metadata_only(ctypes.byref(small), None, None, ctypes.byref(ctx)) == kvc.KVC_ERR_CAPACITY
+    dt = cfg_of(wl)
+    dt.dtype = 2                                                      # neither bf16 nor f16
+    assert lib.kvc_create_metadata_only(ctypes.byref(dt), None, None, ctypes.byref(ctx)) == kvc.KVC_ERR_UNSUPPORTED
+    assert lib.kvc_pool_bytes(ctypes.byref(dt)) == 0
+    dt.dtype = kvc.KVC_DTYPE_F16                                      # same sizes as bf16
+    assert lib.kvc_pool_bytes(ctypes.byref(dt)) == lib.kvc_pool_bytes(ctypes.byref(good))
+    with pytest.raises(kvc.KvcError):
+        kvc.make_config(1, 2, 32, 22, dtype="fp8")
     pg = cfg_of(wl)
     pg.page_size = 15                                                 # < P
     assert lib.kvc_create_metadata_only(ctypes.byref(pg), None, None, ctypes.byref(ctx)) == kvc.KVC_ERR_ARG

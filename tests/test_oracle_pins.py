@@ -191,6 +191,21 @@ def pin_rollback(oracle=ko, seed=7):
         assert st["special_tokens"] == cfg.num_special_tokens * len(kept)
 
 
+def pin_f16_inputs(oracle=ko, seed=11):
+    """IEEE-half K/V/Q ([p3] §Precision and Hardware Utilization: the paged
+    kernels take fp16 as well as bf16): the oracle on f16 bit patterns equals
+    PyTorch SDPA in float64 over torch's own decoding of the same halves, and
+    differs from reading those bits as bf16."""
+    rng = np.random.default_rng(seed)
+    T, L, H, D = 9, 40, 2, 32
+    q, k, v = (syn.f32_to_f16_bits(rng.standard_normal(sh).astype(np.float32) * np.float32(sc))
+               for sh, sc in (((T, H, D), 1.5), ((L, H, D), 1.0), ((L, H, D), 1.0)))
+    ours = oracle.attention_fp64(q, k, v, "f16")
+    to = lambda b: torch.from_numpy(b.view(np.float16)).double().permute(1, 0, 2)[None]
+    ref = torch.nn.functional.scaled_dot_product_attention(to(q), to(k), to(v))[0].permute(1, 0, 2).numpy()
+    np.testing.assert_allclose(ours, ref, rtol=1e-12, atol=1e-12)
+
+
 def pin_bruteforce(oracle=ko, seed=1):
     """Scalar loops straight from the definition of softmax attention."""
     rng = np.random.default_rng(seed)
@@ -281,6 +296,10 @@ def test_scale_phase_multi_frame_step_is_dense_sdpa():
 
 def test_rollback_leaves_the_kept_frames_history():
     pin_rollback()
+
+
+def test_f16_inputs_match_torch_sdpa():
+    pin_f16_inputs()
 
 
 def test_attention_bruteforce():
@@ -466,7 +485,7 @@ class _Mutant:
         self.__dict__.update(overrides)
 
 
-def _no_scale(q_bits, k_bits, v_bits):
+def _no_scale(q_bits, k_bits, v_bits, dtype="bf16"):
     q = syn.bf16_bits_to_f32(q_bits).astype(np.float64)
     k = syn.bf16_bits_to_f32(k_bits).astype(np.float64)
     v = syn.bf16_bits_to_f32(v_bits).astype(np.float64)
@@ -478,11 +497,15 @@ def _no_scale(q_bits, k_bits, v_bits):
     return out
 
 
-def _values_are_keys(q_bits, k_bits, v_bits):
-    return ko.attention_fp64(q_bits, k_bits, k_bits)
+def _values_are_keys(q_bits, k_bits, v_bits, dtype="bf16"):
+    return ko.attention_fp64(q_bits, k_bits, k_bits, dtype)
 
 
-def _sum_over_queries(q_bits, k_bits, v_bits):
+def _f16_read_as_bf16(q_bits, k_bits, v_bits, dtype="bf16"):
+    return ko.attention_fp64(q_bits, k_bits, v_bits)   # ignores the element type
+
+
+def _sum_over_queries(q_bits, k_bits, v_bits, dtype="bf16"):
     q = syn.bf16_bits_to_f32(q_bits).astype(np.float64)
     k = syn.bf16_bits_to_f32(k_bits).astype(np.float64)
     v = syn.bf16_bits_to_f32(v_bits).astype(np.float64)
@@ -555,7 +578,7 @@ def _pins_fail(mutant, pins):
 
 
 ALL_PINS = [pin_worked_example, pin_special_closed_forms, pin_visible_set, pin_sdpa, pin_bruteforce,
-            pin_softmax_invariants, pin_paged_equals_dense, pin_scale_phase, pin_rollback]
+            pin_softmax_invariants, pin_paged_equals_dense, pin_scale_phase, pin_rollback, pin_f16_inputs]
 
 
 @pytest.mark.parametrize("mutant", [
@@ -569,8 +592,10 @@ ALL_PINS = [pin_worked_example, pin_special_closed_forms, pin_visible_set, pin_s
     _Mutant(AllocatorReplay=_LifoSpecialReuse),
     _Mutant(AllocatorReplay=_OneFramePerStep),
     _Mutant(AllocatorReplay=_RollbackKeepsHeldBack),
+    _Mutant(attention_fp64=_f16_read_as_bf16),
 ], ids=["no_scale", "values_are_keys", "wrong_softmax_axis", "window_off_by_one", "specials_first",
-        "last_page_zero", "scale_evicted", "special_count_drift", "one_frame_per_step", "rollback_no_refill"])
+        "last_page_zero", "scale_evicted", "special_count_drift", "one_frame_per_step", "rollback_no_refill",
+        "f16_read_as_bf16"])
 def test_planted_mistake_is_caught(mutant):
     # OracleStream inside the mutant must use the mutant's allocator
     class _Stream(ko.OracleStream):
@@ -584,7 +609,7 @@ def test_planted_mistake_is_caught(mutant):
             outs = []
             for i in range(len(plan["last_page_len"])):
                 k, v = mutant.gather_paged(self.cfg, self.pools[block], plan, i)
-                outs.append(mutant.attention_fp64(q_bits[qo[i]:qo[i + 1]], k, v))
+                outs.append(mutant.attention_fp64(q_bits[qo[i]:qo[i + 1]], k, v, self.cfg.dtype))
             return np.concatenate(outs)
     mutant.OracleStream = _Stream
     assert _pins_fail(mutant, ALL_PINS)
