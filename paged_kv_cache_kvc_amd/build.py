@@ -39,11 +39,31 @@ def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
-    out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
+    out = "\n".join(l for l in r.stdout.splitlines()
+                    if "packed-fp32-ops" not in l and "kernel-resource-usage" not in l)
     if r.returncode != 0:
         raise RuntimeError(f"build step failed ({r.returncode}): {' '.join(cmd)}\n{out}")
     if verbose and out.strip():
         print(out)
+    return r.stdout
+
+
+def check_no_scratch(remarks: str) -> None:
+    """The attention kernel counts its own direct-to-LDS loads with vmcnt
+    waits; a register spill inside its loop would add scratch loads to that
+    count (publishing a stage too early) or force a full drain.  Refuse any
+    build in which a kernel uses scratch memory."""
+    name = None
+    bad = []
+    for line in remarks.splitlines():
+        if "Function Name:" in line:
+            name = line.split("Function Name:")[1].split()[0]
+        elif "ScratchSize [bytes/lane]:" in line:
+            size = int(line.split("ScratchSize [bytes/lane]:")[1].split()[0])
+            if size:
+                bad.append(f"{name}: {size} bytes/lane")
+    if bad:
+        raise RuntimeError("kernels spill to scratch memory:\n  " + "\n  ".join(bad))
 
 
 def build(verbose: bool = False) -> str:
@@ -53,7 +73,11 @@ def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     objs = []
     o = os.path.join(BUILD, "kvc_kernels.o")
-    _run([hipcc, *HIP_FLAGS, "-c", os.path.join(CSRC, "kvc_kernels.hip"), "-o", o], verbose)
+    remarks = _run([hipcc, *HIP_FLAGS, "-Rpass-analysis=kernel-resource-usage", "-c",
+                    os.path.join(CSRC, "kvc_kernels.hip"), "-o", o], verbose)
+    if "ScratchSize" not in remarks:
+        raise RuntimeError("no kernel resource usage reported by hipcc")
+    check_no_scratch(remarks)
     objs.append(o)
     for src in ("kvc_host.cpp", "kvc_api.cpp"):
         o = os.path.join(BUILD, src.replace(".cpp", ".o"))

@@ -68,6 +68,7 @@ struct El;
 
 template <>
 struct El<0> {
+  static constexpr uint32_t ONE2 = 0x3f803f80u;   // two bf16 ones
   static __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
@@ -93,6 +94,7 @@ struct El<0> {
 
 template <>
 struct El<1> {
+  static constexpr uint32_t ONE2 = 0x3c003c00u;   // two f16 ones
   static __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
                                                    0, 0);
@@ -291,8 +293,11 @@ __device__ __forceinline__ float lane_swap_sum(float x) {
 // current ref; only when a lane's sum of those probabilities exceeds 2^8 (a
 // score more than a few units above ref, or an overflow to infinity) is it
 // redone against the exact column maximum.  A tile's first stage with a valid
-// slot always takes the exact path.
+// slot always takes the exact path.  The own tiles test the whole column's
+// sum over the stage (the four lane groups' 64 slots), against four times the
+// lane limit.
 constexpr float LAZY_SUM_LIMIT = 256.0f;
+constexpr float LAZY_COL_LIMIT = 4.0f * LAZY_SUM_LIMIT;
 
 template <int D, int E>
 struct Ops {
@@ -323,6 +328,13 @@ struct Ops {
 #pragma unroll
       for (int pp = 0; pp < 2; ++pp)
         o[db] = T::mfma(vop[db][pp], __builtin_bit_cast(bf16x8, pb[pp]), o[db]);
+  }
+  // Column sums of P^T over the stage (both pairs): the same product with an
+  // all-ones V^T, so every accumulator of a lane holds its query column's sum
+  // of the rounded probabilities the P.V product uses.
+  static __device__ __forceinline__ f32x4 colsum(const bf16x8& ones, const u32x4 (&pb)[2]) {
+    const f32x4 c = T::mfma(ones, __builtin_bit_cast(bf16x8, pb[0]), f32x4{0.f, 0.f, 0.f, 0.f});
+    return T::mfma(ones, __builtin_bit_cast(bf16x8, pb[1]), c);
   }
   // ... over one pair
   template <int PP>
@@ -356,6 +368,18 @@ __device__ __forceinline__ float probs(const f32x4 (&s)[N], float sl, float nref
         b = El<E>::dot_ones(w, b);
     }
   return a + b;
+}
+
+// The same packing without the lane sum (the own tiles take their sums from
+// the MFMA, colsum).
+template <int N, int E>
+__device__ __forceinline__ void probs_pack(const f32x4 (&s)[N], float sl, float nref, uint32_t (&pk)[2 * N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      pk[2 * i + h] = El<E>::pack_p(__builtin_amdgcn_exp2f(__builtin_fmaf(s[i][2 * h], sl, nref)),
+                                    __builtin_amdgcn_exp2f(__builtin_fmaf(s[i][2 * h + 1], sl, nref)));
 }
 
 // Slots of score block j held by lane group g4 are boff[j] + 8 g4 + i (boff
@@ -614,6 +638,11 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
   const int kb_sh[1] = {32 * shPP + 4 * shTT};
 
   bf16x8 kop[4][KS], ksh[KS], vop[DB][2];
+  // Own tiles' stage sums: by MFMA (colsum, an all-ones V^T operand) for
+  // bf16; for f16 the lane sums of the packing (the f16 build has no
+  // registers to spare for the sum accumulators)
+  constexpr bool MSUM = E == 0;
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{El<E>::ONE2, El<E>::ONE2, El<E>::ONE2, El<E>::ONE2});
   f32x4 sc0[4], sc1[4], sc2[1];
   uint32_t pk0[8], pk1[8], pk2[2];
   u32x4 pbsh = u32x4{0u, 0u, 0u, 0u};
@@ -672,27 +701,58 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
     vq1 = vq2;
     vq2 = en.z;
     read_k(s + 1, kop);
-    float lt = probs<4, E>(sc0, sl, nref0, pk0);
-    asm volatile("" ::"v"(lt));   // keep the common path ahead of the branch, next to the MFMAs
-    if (fresh0 || __builtin_amdgcn_ballot_w64(lt > LAZY_SUM_LIMIT)) lt = renorm<4, DB, E>(sc0, sl, fresh0, ref0, nref0, l0, o0, pk0);
-    l0 += lt;
+    f32x4 cs0;
+    float ls0;
+    if constexpr (MSUM) {
+      probs_pack<4, E>(sc0, sl, nref0, pk0);
+      cs0 = O::colsum(ones, {u32x4{pk0[0], pk0[1], pk0[2], pk0[3]}, u32x4{pk0[4], pk0[5], pk0[6], pk0[7]}});
+    } else {
+      ls0 = probs<4, E>(sc0, sl, nref0, pk0);
+    }
 
     // ---- step 1: own tile 1 ----
-    if (partial) mask_scores<4>(sc1, kb_own, valid, g4);
     O::qk1(ksh, q2, sc2);
+    // own tile 0: check its stage sum, then P.V
+    float lt;
+    if constexpr (MSUM) {
+      lt = cs0[0];
+      if (fresh0 || __builtin_amdgcn_ballot_w64(lt > LAZY_COL_LIMIT))
+        lt = lane_swap_sum(renorm<4, DB, E>(sc0, sl, fresh0, ref0, nref0, l0, o0, pk0));
+    } else {
+      lt = ls0;
+      if (fresh0 || __builtin_amdgcn_ballot_w64(lt > LAZY_SUM_LIMIT))
+        lt = renorm<4, DB, E>(sc0, sl, fresh0, ref0, nref0, l0, o0, pk0);
+    }
+    l0 += lt;
     {
       u32x4 pb[2] = {u32x4{pk0[0], pk0[1], pk0[2], pk0[3]}, u32x4{pk0[4], pk0[5], pk0[6], pk0[7]}};
       O::pv(vop, pb, o0);
     }
-    lt = probs<4, E>(sc1, sl, nref1, pk1);
-    asm volatile("" ::"v"(lt));
-    if (fresh1 || __builtin_amdgcn_ballot_w64(lt > LAZY_SUM_LIMIT)) lt = renorm<4, DB, E>(sc1, sl, fresh1, ref1, nref1, l1, o1, pk1);
-    l1 += lt;
+    if (partial) mask_scores<4>(sc1, kb_own, valid, g4);
+    f32x4 cs1;
+    float ls1;
+    if constexpr (MSUM) {
+      probs_pack<4, E>(sc1, sl, nref1, pk1);
+      cs1 = O::colsum(ones, {u32x4{pk1[0], pk1[1], pk1[2], pk1[3]}, u32x4{pk1[4], pk1[5], pk1[6], pk1[7]}});
+    } else {
+      ls1 = probs<4, E>(sc1, sl, nref1, pk1);
+    }
     read_ksh(s + 1, ksh);
 
     // ---- step 2: shared tile ----
-    if (partial) mask_scores<1>(sc2, kb_sh, valid, g4);
     O::qk(kop, q0, sc0);
+    // own tile 1: check its stage sum (its P.V follows in the next step 0)
+    if constexpr (MSUM) {
+      lt = cs1[0];
+      if (fresh1 || __builtin_amdgcn_ballot_w64(lt > LAZY_COL_LIMIT))
+        lt = lane_swap_sum(renorm<4, DB, E>(sc1, sl, fresh1, ref1, nref1, l1, o1, pk1));
+    } else {
+      lt = ls1;
+      if (fresh1 || __builtin_amdgcn_ballot_w64(lt > LAZY_SUM_LIMIT))
+        lt = renorm<4, DB, E>(sc1, sl, fresh1, ref1, nref1, l1, o1, pk1);
+    }
+    l1 += lt;
+    if (partial) mask_scores<1>(sc2, kb_sh, valid, g4);
     lt = probs<1, E>(sc2, sl, nref2, pk2);
     asm volatile("" ::"v"(lt));
     if (fresh2 || __builtin_amdgcn_ballot_w64(lt > LAZY_SUM_LIMIT)) lt = renorm<1, DB, E>(sc2, sl, fresh2, ref2, nref2, l2, o2, pk2);
@@ -734,8 +794,11 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
       for (int db = 0; db < DB; ++db) *reinterpret_cast<u32x2*>(orow + 16 * db + 4 * g4) = El<E>::cvt4(o[db] * inv);
     }
   };
-  if (wave < n_own) store(t_lo + wave, ref0, lane_swap_sum(l0), o0);
-  if (wave + 4 < n_own) store(t_lo + wave + 4, ref1, lane_swap_sum(l1), o1);
+  // with MSUM, l0 and l1 are whole column sums; otherwise, like l2, the lane
+  // group's share
+  const float lw0 = MSUM ? l0 : lane_swap_sum(l0), lw1 = MSUM ? l1 : lane_swap_sum(l1);
+  if (wave < n_own) store(t_lo + wave, ref0, lw0, o0);
+  if (wave + 4 < n_own) store(t_lo + wave + 4, ref1, lw1, o1);
 
   if (has_shared) {
     // merge the four waves' partial states of the shared tile (one split

@@ -357,3 +357,13 @@ def test_rollback_errors():
     with pytest.raises(kvc.KvcError) as e:
         c.set_option(kvc.KVC_OPT_DEFER_EVICTION, 2)
     assert e.value.status == kvc.KVC_ERR_ARG
+
+
+def test_build_refuses_kernels_that_spill():
+    """The attention loop counts its own direct-to-LDS loads with vmcnt waits,
+    so a build whose kernels use scratch memory is refused."""
+    from paged_kv_cache_kvc_amd import build as b
+    ok = ("k.hip:1:1: remark: Function Name: attn [-R]\nk.hip:1:1: remark:     ScratchSize [bytes/lane]: 0 [-R]\n")
+    b.check_no_scratch(ok)
+    with pytest.raises(RuntimeError, match="attn2: 216"):
+        b.check_no_scratch(ok + ok.replace("attn", "attn2").replace("]: 0", "]: 216"))
