@@ -29,6 +29,24 @@ def oracle_cfg(wl: syn.Workload) -> ko.OracleConfig:
                            dtype=wl.dtype)
 
 
+def edge_workloads() -> Dict[str, syn.Workload]:
+    """Degenerate shapes: frames without special tokens, the most special
+    tokens a frame may carry (64, spanning four 16-slot pages), one-token
+    frames on a single head at D=128, and the most frames one step may append
+    (64, a scale phase of 64 tiny frames followed by single frames)."""
+    W = syn.Workload
+    return {
+        "no_specials": W("no_specials", 1, 2, 64, 20, 0, 20, 2, 3, (10,), 21,
+                         max_patch_pages=2 + 3 + 1, max_special_pages=0),
+        "max_specials": W("max_specials", 1, 2, 32, 16, 64, 16, 1, 2, (6,), 22,
+                          max_patch_pages=1 + 2 + 1, max_special_pages=24),
+        "one_token": W("one_token", 1, 1, 128, 1, 0, 1, 1, 3, (8,), 23,
+                       max_patch_pages=1 + 3 + 1, max_special_pages=0),
+        "steps_of_64": W("steps_of_64", 1, 2, 32, 16, 6, 16, 8, 64, (74,), 24,
+                         max_patch_pages=8 + 64 + 1, max_special_pages=28),
+    }
+
+
 def free_orders(wl: syn.Workload, seed: Optional[int] = None):
     if seed is None:
         if not wl.shuffle_free_lists:

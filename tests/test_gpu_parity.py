@@ -303,3 +303,25 @@ def test_f16_pools_d32_d64_d128():
             compare_plan(res)
             st = check_close(res["out_bits"][0], res["ref"][0], dtype="f16")
             log(f"f16 D=128 step {t} splits {res['gpu_plan']['n_splits']} {st}")
+
+
+@pytest.mark.parametrize("name", ["no_specials", "max_specials", "one_token", "steps_of_64"])
+def test_degenerate_shapes(name):
+    """Frames without special tokens, 64 special tokens per frame over four
+    pages, one-token frames (one head, D=128, one-slot pages), and a first
+    step of 64 frames: page tables, pools (bit-exact) and attention against
+    the oracle at every step."""
+    _need_gpu()
+    from tests.stream_harness import edge_workloads
+    wl = edge_workloads()[name]
+    multi = 64 if name == "steps_of_64" else 1
+    h = Harness(wl, max_frames_per_step=multi)
+    done = 0
+    while done < max(wl.frames):
+        nf = multi if done == 0 else 1
+        res = h.step(check=True, nframes={0: nf})
+        compare_plan(res)
+        st = check_close(res["out_bits"][0], res["ref"][0])
+        assert np.array_equal(h.pool_bits(0), h.ora.pools[0].data), f"pool after {done} frames"
+        done += nf
+    log(f"{name}: {done} frames, splits {res['gpu_plan']['n_splits']} {st}")

@@ -89,6 +89,33 @@ def test_metadata_replay_matches_oracle_every_step(name):
     assert np.all(p["n_splits"] >= 1) and np.all(p["n_splits"] <= kvc.MAX_SPLITS)
 
 
+@pytest.mark.parametrize("name", ["no_specials", "max_specials", "one_token", "steps_of_64"])
+def test_metadata_replay_degenerate_shapes(name):
+    """Page tables and counters of the degenerate shapes against the oracle at
+    every step (the 64-frame shape appends its first 64 frames in one step)."""
+    from tests.stream_harness import cfg_args, edge_workloads
+    wl = edge_workloads()[name]
+    multi = 64 if name == "steps_of_64" else 1
+    cache = kvc.PagedKVCache(kvc.make_config(**cfg_args(wl, 1), max_frames_per_step=multi), metadata_only=True)
+    ref = ko.AllocatorReplay(ocfg_of(wl))
+    done = 0
+    while done < max(wl.frames):
+        nf = multi if done == 0 else 1
+        if nf > 1:
+            cache.append_frames(0, num_frames=nf)
+        else:
+            cache.append_frame(0)
+        for _ in range(nf):
+            ref.append_frame(0)
+        cache.evict_frames(0)
+        ref.evict_frames(0)
+        cache.plan()
+        compare_plans(cache.get_plan(), ref.plan([0], frames=[nf]), [0])
+        st, rs = cache.get_cache_stats(0), ref.get_cache_stats(0)
+        assert {k: st[k] for k in rs} == rs
+        done += nf
+
+
 def test_worked_example_through_abi():
     cfg = kvc.make_config(1, 16, 64, 262, 6, scale_frames=8, sliding_window=64, max_patch_pages=88,
                           max_total_frames=200)
