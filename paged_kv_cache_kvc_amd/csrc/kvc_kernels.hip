@@ -388,6 +388,8 @@ __device__ __forceinline__ void probs_pack(const f32x4 (&s)[N], float sl, float 
 // stay inside the (rarely taken) branch of a partial stage.
 template <int N>
 __device__ __forceinline__ void mask_scores(f32x4 (&s)[N], const int (&boff)[N], int valid, int g4) {
+  // rare branch: wait states first, clear of the MFMAs that wrote s
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
   int lim = valid - 8 * g4;
   asm volatile("" : "+v"(lim));
 #pragma unroll
@@ -670,26 +672,46 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
   read_ksh(0, ksh);
   O::qk(kop, q0, sc0);
 
+  // Stage 0's step 0 multiplies the zero P^T operands of "stage -1" with
+  // zero V^T operands: exact zeros, so the loop needs no first-stage branch.
+#pragma unroll
+  for (int db = 0; db < DB; ++db) vop[db][0] = vop[db][1] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+#pragma unroll
+  for (int i = 0; i < 8; ++i) pk1[i] = 0u;
+
   for (int s = 0; s < nstage; ++s) {
     const int valid = vq0;
     const bool partial = valid < KT;
     i32x4 en = unit_load(units + KVC_UNIT_INTS * min(s + 3, nstage - 1));
 
-    // ---- step 0: own tile 0 ----
+    // ---- step 0: MFMAs of own tile 1 and the shared tile | probabilities of own tile 0 ----
     if (partial) mask_scores<4>(sc0, kb_own, valid, g4);
-    if (s > 0) {
-      O::template pv1<0>(vop, pbsh, o2);
+    O::template pv1<0>(vop, pbsh, o2);
+    {
       u32x4 pb[2] = {u32x4{pk1[0], pk1[1], pk1[2], pk1[3]}, u32x4{pk1[4], pk1[5], pk1[6], pk1[7]}};
       O::pv(vop, pb, o1);
     }
     O::qk(kop, q1, sc1);
-    // The V operands of stage s (published one stage ago) and, once stage
-    // s+1 is published, its K operands are read before this step's vector
-    // work, which then covers their latency.  Every read of stage s-1 has
+    f32x4 cs0;
+    float ls0;
+    if constexpr (MSUM) {
+      probs_pack<4, E>(sc0, sl, nref0, pk0);
+      cs0 = O::colsum(ones, {u32x4{pk0[0], pk0[1], pk0[2], pk0[3]}, u32x4{pk0[4], pk0[5], pk0[6], pk0[7]}});
+    } else {
+      ls0 = probs<4, E>(sc0, sl, nref0, pk0);
+    }
+    // one MFMA, then two vector instructions, while both last
+#pragma unroll
+    for (int i = 0; i < 20; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+    }
+    // The V operands of stage s (published one stage ago) are read once the
+    // products above have consumed those of stage s-1; then stage s+1 is
+    // published and its K operands read.  Every read of stage s-1 has
     // completed (the products above consumed them) before the barrier lets
     // the ring slot of stage s-1 be refilled.
     read_v(s, vop);
-    // publish stage s+1, refill the ring slot of stage s-1
     if (s + 2 < nstage)
       wait_vmcnt<LPW>();
     else
@@ -701,18 +723,11 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
     vq1 = vq2;
     vq2 = en.z;
     read_k(s + 1, kop);
-    f32x4 cs0;
-    float ls0;
-    if constexpr (MSUM) {
-      probs_pack<4, E>(sc0, sl, nref0, pk0);
-      cs0 = O::colsum(ones, {u32x4{pk0[0], pk0[1], pk0[2], pk0[3]}, u32x4{pk0[4], pk0[5], pk0[6], pk0[7]}});
-    } else {
-      ls0 = probs<4, E>(sc0, sl, nref0, pk0);
-    }
 
-    // ---- step 1: own tile 1 ----
+    // ---- step 1: QK of the shared tile, P.V of own tile 0 | probabilities of own tile 1 ----
+    if (partial) mask_scores<4>(sc1, kb_own, valid, g4);
     O::qk1(ksh, q2, sc2);
-    // own tile 0: check its stage sum, then P.V
+    // own tile 0: check its stage sum before its P.V
     float lt;
     if constexpr (MSUM) {
       lt = cs0[0];
@@ -728,7 +743,6 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
       u32x4 pb[2] = {u32x4{pk0[0], pk0[1], pk0[2], pk0[3]}, u32x4{pk0[4], pk0[5], pk0[6], pk0[7]}};
       O::pv(vop, pb, o0);
     }
-    if (partial) mask_scores<4>(sc1, kb_own, valid, g4);
     f32x4 cs1;
     float ls1;
     if constexpr (MSUM) {
@@ -737,10 +751,25 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
     } else {
       ls1 = probs<4, E>(sc1, sl, nref1, pk1);
     }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+    }
     read_ksh(s + 1, ksh);
 
-    // ---- step 2: shared tile ----
+    // ---- step 2: QK of own tile 0 for stage s+1 | probabilities of the shared tile ----
+    if (partial) mask_scores<1>(sc2, kb_sh, valid, g4);
     O::qk(kop, q0, sc0);
+    float lt2 = probs<1, E>(sc2, sl, nref2, pk2);
+#pragma unroll
+    for (int i = 0; i < 7; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+    }
+    // keep the shared tile's probabilities here, beside the MFMAs above,
+    // rather than sunk past the branch below
+    asm volatile("" : "+v"(lt2));
     // own tile 1: check its stage sum (its P.V follows in the next step 0)
     if constexpr (MSUM) {
       lt = cs1[0];
@@ -752,11 +781,9 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
         lt = renorm<4, DB, E>(sc1, sl, fresh1, ref1, nref1, l1, o1, pk1);
     }
     l1 += lt;
-    if (partial) mask_scores<1>(sc2, kb_sh, valid, g4);
-    lt = probs<1, E>(sc2, sl, nref2, pk2);
-    asm volatile("" ::"v"(lt));
-    if (fresh2 || __builtin_amdgcn_ballot_w64(lt > LAZY_SUM_LIMIT)) lt = renorm<1, DB, E>(sc2, sl, fresh2, ref2, nref2, l2, o2, pk2);
-    l2 += lt;
+    if (fresh2 || __builtin_amdgcn_ballot_w64(lt2 > LAZY_SUM_LIMIT))
+      lt2 = renorm<1, DB, E>(sc2, sl, fresh2, ref2, nref2, l2, o2, pk2);
+    l2 += lt2;
     // P^T of the shared block: its 4 slots sit at positions 4*half..4*half+3
     // of the pair's operand; the other half is zero
     pbsh = shTT ? u32x4{0u, 0u, pk2[0], pk2[1]} : u32x4{pk2[0], pk2[1], 0u, 0u};
