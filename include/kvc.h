@@ -125,7 +125,9 @@ typedef struct kvc_stats {
 
 /* Tunables for kvc_set_option / kvc_get_option. */
 enum {
-  KVC_OPT_TARGET_WORKGROUPS = 1, /* attention work-groups the planner aims for per run (default 2 per CU) */
+  KVC_OPT_TARGET_WORKGROUPS = 1, /* attention work-groups the planner fills per run without exceeding it
+                                    (default: what the device holds at once, 2 per CU for head_dim <= 64,
+                                    1 per CU for 128) */
   KVC_OPT_MAX_SPLITS = 2,        /* cap on KV splits per stream; 1 disables split-KV (default 64, the maximum) */
   KVC_OPT_PROFILE = 3,           /* 1: time every attention/merge/append launch with HIP events */
   KVC_OPT_DEFER_EVICTION = 4     /* 1: hold evicted window pages back until the stream's next frame,

@@ -168,6 +168,12 @@ size_t kvc_staging_bytes(const kvc_config* cfg) {
   return 2 * layout_of(c).plan_bytes;
 }
 
+// Attention work-groups the device holds at once: two per CU up to D = 64
+// (registers and LDS of two fit), one at D = 128.
+static int32_t resident_workgroups(const kvc::Config& c, int cu_count) {
+  return (c.head_dim <= 64 ? 2 : 1) * cu_count;
+}
+
 static kvc_status create_common(const kvc_config* cfg, const int32_t* fpo, const int32_t* fso, kvc_ctx** out,
                                 kvc_ctx** made) {
   if (!cfg || !out) return KVC_ERR_ARG;
@@ -202,7 +208,7 @@ kvc_status kvc_create_metadata_only(const kvc_config* cfg, const int32_t* fpo, c
   const kvc_status rc = create_common(cfg, fpo, fso, out, &x);
   if (rc != KVC_OK) return rc;
   x->metadata_only = true;
-  x->policy.target_workgroups = 2 * x->cu_count;
+  x->policy.target_workgroups = resident_workgroups(x->cfg, x->cu_count);
   *out = x;
   return KVC_OK;
 }
@@ -230,7 +236,7 @@ kvc_status kvc_create(const kvc_config* cfg, void* const* pools, void* workspace
     delete x;
     return KVC_ERR_HIP;
   }
-  x->policy.target_workgroups = 2 * x->cu_count;
+  x->policy.target_workgroups = resident_workgroups(x->cfg, x->cu_count);
   for (int b = 0; b < x->cfg.num_blocks; ++b) {
     if (hipMemset(x->pools[b], 0, pb) != hipSuccess) {
       delete x;

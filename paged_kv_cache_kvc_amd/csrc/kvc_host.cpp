@@ -243,34 +243,62 @@ void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const s
   }
 
   // Work decomposition: each work item is (stream, head, KV split, query
-  // group).  Query groups hold at most KVC_ATTN_WAVES * tiles_per_wave tiles;
-  // KV splits share the target work-group count in proportion to each
-  // stream's visible length, in whole KVC_KV_TILE units.
+  // group).  Query groups hold at most KVC_ATTN_WAVES * tiles_per_wave tiles.
+  // Every work-group costs the same per 64-slot unit, so a launch takes as
+  // long as its longest split times the number of rounds in which the
+  // work-groups run.  The target work-group count is what the device holds
+  // at once (one round); the split counts start from each stream's share of
+  // it, in proportion to queries x visible tokens, rounded down, and then the
+  // stream whose splits are longest gains a split while the whole launch
+  // still fits in one round.
   const int32_t per_group = kvc_group_tiles(c.head_dim);
-  // work is proportional to queries x visible tokens
   double total_work = 0;
   for (int i = 0; i < n; ++i) total_work += (double)frames[i] * (double)kv_len[i];
   const int32_t max_splits = std::max(1, std::min<int32_t>(pol.max_splits, KVC_MAX_SPLITS));
+  const int32_t upp = (int32_t)ceil_div(std::max(1, P), KVC_KV_TILE);
+  const int32_t ups = (int32_t)ceil_div(c.page_size, KVC_KV_TILE);
+  std::vector<int64_t> units(n), groups(n), nsplit(n), cap(n);
+  int64_t items_total = 0;
+  for (int i = 0; i < n; ++i) {
+    const int32_t n_patch = p.n_patch_pages[i];
+    const int32_t n_special = p.kv_indptr[i + 1] - p.kv_indptr[i] - n_patch;
+    units[i] = std::max<int64_t>(
+        1, (int64_t)n_patch * upp +
+               (n_special > 0 ? (int64_t)(n_special - 1) * ups + ceil_div(p.last_page_len[i], KVC_KV_TILE) : 0));
+    const int32_t nqt = (int32_t)ceil_div(frames[i] * c.tokens_per_frame, KVC_Q_TILE);
+    groups[i] = (int64_t)c.num_heads * ceil_div(nqt, per_group);
+    cap[i] = std::min<int64_t>(max_splits, units[i]);
+    const double want = total_work > 0 ? (double)pol.target_workgroups * (double)frames[i] * (double)kv_len[i] /
+                                             total_work / (double)groups[i]
+                                       : 1.0;
+    nsplit[i] = std::max<int64_t>(1, std::min<int64_t>((int64_t)std::floor(want), cap[i]));
+    items_total += groups[i] * nsplit[i];
+  }
+  for (;;) {
+    int best = -1;
+    int64_t best_len = 0;
+    for (int i = 0; i < n; ++i) {
+      if (nsplit[i] >= cap[i] || items_total + groups[i] > pol.target_workgroups) continue;
+      const int64_t len = ceil_div(units[i], nsplit[i]);
+      if (len > best_len) {
+        best = i;
+        best_len = len;
+      }
+    }
+    // a split that does not shorten the longest split of its stream gains nothing
+    if (best < 0 || ceil_div(units[best], nsplit[best] + 1) >= best_len) break;
+    ++nsplit[best];
+    items_total += groups[best];
+  }
 
   p.image.assign(KVC_PLAN_HEADER_INTS + (size_t)KVC_STREAM_REC_INTS * n + p.kv_indices.size(), 0);
   int32_t item = 0, tiles = 0;
   p.any_split = false;
-  const int32_t upp = (int32_t)ceil_div(std::max(1, P), KVC_KV_TILE);
-  const int32_t ups = (int32_t)ceil_div(c.page_size, KVC_KV_TILE);
   for (int i = 0; i < n; ++i) {
-    const int32_t n_patch = p.n_patch_pages[i];
-    const int32_t n_special = p.kv_indptr[i + 1] - p.kv_indptr[i] - n_patch;
-    const int64_t units = std::max<int64_t>(
-        1, (int64_t)n_patch * upp +
-               (n_special > 0 ? (int64_t)(n_special - 1) * ups + ceil_div(p.last_page_len[i], KVC_KV_TILE) : 0));
     const int32_t n_q = frames[i] * c.tokens_per_frame;
     const int32_t nqt = (int32_t)ceil_div(n_q, KVC_Q_TILE);
     const int32_t n_group = (int32_t)ceil_div(nqt, per_group);
-    double want = total_work > 0 ? (double)pol.target_workgroups * (double)frames[i] * (double)kv_len[i] /
-                                       total_work / ((double)c.num_heads * n_group)
-                                 : 1.0;
-    int64_t ns = (int64_t)std::llround(want);
-    ns = std::max<int64_t>(1, std::min<int64_t>(ns, std::min<int64_t>(max_splits, units)));
+    const int64_t ns = nsplit[i];
     p.n_split.push_back((int32_t)ns);
     if (ns > 1) p.any_split = true;
 
@@ -284,7 +312,7 @@ void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const s
     rec.last_len = p.last_page_len[i];
     rec.kv_len = (int32_t)kv_len[i];
     rec.unit0 = 0;   // set below, once the page tables are in place
-    rec.n_units = (int32_t)units;
+    rec.n_units = (int32_t)units[i];
     rec.upp = upp;
     rec.ups = ups;
     rec.n_split = (int32_t)ns;
