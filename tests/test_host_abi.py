@@ -265,6 +265,47 @@ def test_split_policy_options():
     assert c.get_option(kvc.KVC_OPT_MAX_SPLITS) == 1
 
 
+@pytest.mark.parametrize("name", ["base", "r518", "frag"])
+def test_split_counts_fill_one_round(name):
+    """The planner's split counts keep every attention work-group of a run
+    resident at once (at most the target count, which defaults to what the
+    device holds: 2 per CU up to D = 64, 1 at D = 128), and no stream could
+    take one more split that shortens its longest split and still fit."""
+    wl = syn.WORKLOADS[name]
+    c = kvc.PagedKVCache(cfg_of(wl), metadata_only=True)
+    F = max(wl.frames)
+    starts = [F - f for f in wl.frames]
+    for t in range(F):
+        act = [s for s in range(len(wl.frames)) if t >= starts[s]]
+        for s in act:
+            c.append_frame(0, stream_id=s)
+        for s in act:
+            c.evict_frames(stream_id=s)
+        c.plan()
+    p = c.get_plan()
+    target = c.get_option(kvc.KVC_OPT_TARGET_WORKGROUPS)
+    assert target == (2 if wl.head_dim <= 64 else 1) * 256   # the CU count a metadata-only context assumes
+    P = wl.tokens_per_frame - wl.num_special_tokens
+    ceil = lambda a, b: -(-a // b)
+    units, groups = [], []
+    for i in range(len(p["planned"])):
+        n_pages = int(p["kv_indptr"][i + 1] - p["kv_indptr"][i])
+        n_patch = int(p["n_patch_pages"][i])
+        n_sp = n_pages - n_patch
+        u = n_patch * ceil(P, 64)
+        if n_sp:
+            u += (n_sp - 1) * ceil(wl.page_size, 64) + ceil(int(p["last_page_len"][i]), 64)
+        units.append(u)
+        rows = int(p["qo_indptr"][i + 1] - p["qo_indptr"][i])
+        groups.append(wl.num_heads * ceil(ceil(rows, 16), 9))
+    ns = [int(x) for x in p["n_splits"]]
+    items = sum(g * n for g, n in zip(groups, ns))
+    assert items <= target
+    for i, (u, g, n) in enumerate(zip(units, groups, ns)):
+        if n < min(kvc.MAX_SPLITS, u) and ceil(u, n + 1) < ceil(u, n):
+            assert items + g > target, (name, i, ns)
+
+
 def test_scale_phase_multi_frame_steps_match_oracle():
     """A stream whose first step appends its S scale frames together ([p2]
     §Frame Processing Loop), then streams one frame per step; a second stream
