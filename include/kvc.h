@@ -260,6 +260,10 @@ kvc_status kvc_plan(kvc_ctx* ctx, kvc_stream_t hip_stream);
  *   o: device [R, H, D] bf16, written; must not overlap q.
  * Each stream's queries attend only to its own visible tokens.  Launches the
  * attention kernel and, when a stream's KV is split, the merge kernel.
+ * Every run and plan of one context uses the same workspace (plan buffers and
+ * split partials), so they must execute in call order on the device: issue
+ * them on one HIP stream, or order the streams with events.  Runs of different
+ * contexts are independent.
  * Errors: KVC_ERR_ARG, KVC_ERR_STATE (not planned, or a planned stream has
  * not appended this block), KVC_ERR_HIP. */
 kvc_status kvc_run(kvc_ctx* ctx, int32_t block, const void* q, void* o, kvc_stream_t hip_stream);
