@@ -466,7 +466,6 @@ kvc_status kvc_run(kvc_ctx* c, int32_t block, const void* q, void* o, kvc_stream
     m.tiles_cap = cf.tiles_capacity();
     m.num_tiles = c->plan.num_tiles;
     m.max_split = *std::max_element(c->plan.n_split.begin(), c->plan.n_split.end());
-    m.tile_table = c->plan.tile_table;
     m.merge_table = c->plan.merge_table;
     m.merge_slots = c->plan.merge_slots;
     m.dtype = cf.dtype;

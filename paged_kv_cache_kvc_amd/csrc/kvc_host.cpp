@@ -2,6 +2,7 @@
 #include "kvc_host.hpp"
 
 #include <algorithm>
+#include <array>
 #include <cmath>
 #include <cstring>
 
@@ -208,8 +209,8 @@ static size_t max_units(const Config& c) {
 
 size_t plan_image_ints(const Config& c) {
   return KVC_PLAN_HEADER_INTS + (size_t)KVC_STREAM_REC_INTS * c.num_streams + (size_t)c.max_num_pages() + 4 +
-         (size_t)KVC_UNIT_INTS * max_units(c) + 4 + (size_t)KVC_TILE_INTS * c.tiles_capacity() +
-         (size_t)KVC_NUM_XCD * c.tiles_capacity() * c.num_heads;
+         (size_t)KVC_UNIT_INTS * max_units(c) + 4 +
+         (size_t)KVC_MERGE_INTS * KVC_NUM_XCD * c.tiles_capacity() * c.num_heads;
 }
 
 void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const std::vector<int32_t>& frames,
@@ -372,30 +373,13 @@ void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const s
     at += (size_t)KVC_UNIT_INTS * r.n_units;
   }
 
-  // Tile table: what the split merge needs of each query tile, so that it
-  // reads one entry instead of searching the stream records.
-  at = (p.image.size() + 3) & ~(size_t)3;
-  p.tile_table = (int32_t)at;
-  p.image[KVC_HDR_TILE_TABLE] = p.tile_table;
-  p.image.resize(at + (size_t)KVC_TILE_INTS * p.num_tiles, 0);
-  for (int i = 0, t0 = 0; i < n; ++i) {   // tiles follow the streams' order (q_tile0)
-    const int32_t n_q = p.qo_indptr[i + 1] - p.qo_indptr[i];
-    const int32_t nqt = (int32_t)ceil_div(n_q, KVC_Q_TILE);
-    for (int32_t t = 0; t < nqt; ++t) {
-      int32_t* e = &p.image[at + (size_t)KVC_TILE_INTS * (t0 + t)];
-      e[0] = p.n_split[i];
-      e[1] = p.qo_indptr[i] + KVC_Q_TILE * t;
-      e[2] = std::min<int32_t>(KVC_Q_TILE, n_q - KVC_Q_TILE * t);
-      e[3] = 0;
-    }
-    t0 += nqt;
-  }
-
   // Merge order: the attention work-group of item i runs on XCD
   // i / items_per_xcd (the kernel gives each XCD a contiguous item range), so
   // the split partials of a (tile, head) sit in that XCD's L2.  Each pair is
-  // merged on the XCD that ran its middle split.
-  std::vector<std::vector<int32_t>> bucket(KVC_NUM_XCD);
+  // merged on the XCD that ran its middle split.  An entry carries what the
+  // merge needs of its tile (split count and output rows), so that the merge
+  // reads one entry before its partials.
+  std::vector<std::vector<std::array<int32_t, KVC_MERGE_INTS>>> bucket(KVC_NUM_XCD);
   const int32_t ipx = (p.num_items + KVC_NUM_XCD - 1) / KVC_NUM_XCD;
   for (int i = 0, t0 = 0; i < n; ++i) {
     const int32_t n_q = p.qo_indptr[i + 1] - p.qo_indptr[i];
@@ -408,7 +392,9 @@ void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const s
         while ((grp + 1) * nqt / r.n_group <= t) ++grp;   // the query group holding tile t
         for (int32_t h = 0; h < c.num_heads; ++h) {
           const int32_t item = r.item0 + (h * r.n_split + r.n_split / 2) * r.n_group + grp;
-          bucket[std::min(item / std::max(1, ipx), KVC_NUM_XCD - 1)].push_back((t0 + t) * c.num_heads + h);
+          bucket[std::min(item / std::max(1, ipx), KVC_NUM_XCD - 1)].push_back(
+              {(t0 + t) * c.num_heads + h, r.n_split, p.qo_indptr[i] + KVC_Q_TILE * t,
+               std::min<int32_t>(KVC_Q_TILE, n_q - KVC_Q_TILE * t)});
         }
       }
     }
@@ -416,13 +402,20 @@ void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const s
   }
   size_t slots = 0;
   for (const auto& b : bucket) slots = std::max(slots, b.size());
-  p.merge_table = (int32_t)p.image.size();
+  at = (p.image.size() + 3) & ~(size_t)3;
+  p.merge_table = (int32_t)at;
   p.merge_slots = (int32_t)slots;
   p.image[KVC_HDR_MERGE_TABLE] = p.merge_table;
   p.image[KVC_HDR_MERGE_SLOTS] = p.merge_slots;
-  p.image.resize(p.image.size() + KVC_NUM_XCD * slots, -1);
+  p.image.resize(at + (size_t)KVC_MERGE_INTS * KVC_NUM_XCD * slots, 0);
   for (int x = 0; x < KVC_NUM_XCD; ++x)
-    std::copy(bucket[x].begin(), bucket[x].end(), p.image.begin() + p.merge_table + (size_t)x * slots);
+    for (size_t k = 0; k < slots; ++k) {
+      int32_t* e = &p.image[at + (size_t)KVC_MERGE_INTS * (x * slots + k)];
+      if (k < bucket[x].size())
+        std::copy(bucket[x][k].begin(), bucket[x][k].end(), e);
+      else
+        e[0] = -1;
+    }
 }
 
 }  // namespace kvc

@@ -51,7 +51,6 @@ struct MergeParams {
   void* o;
   int32_t num_heads, head_dim, tiles_cap, num_tiles;
   int32_t max_split;        // largest split count over the planned streams
-  int32_t tile_table;       // offset in ints of the plan's tile table
   int32_t merge_table;      // offset in ints of the plan's merge order
   int32_t merge_slots;      // merge slots per XCD
   int32_t dtype;            // element type: 0 bfloat16, 1 float16

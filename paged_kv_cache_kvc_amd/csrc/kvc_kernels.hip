@@ -881,19 +881,22 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
 // smallest of 2, 4, 8 that covers the plan's largest split count, else 8: a
 // larger chunk holds more registers, and the occupancy it costs outweighs the
 // round trips it saves (measured: 16 splits merge faster in two chunks of 8).
-template <int D, int E, int MERGE_CHUNK>
-__global__ __launch_bounds__(512) void merge_kernel(MergeParams p) {
+template <int D, int E, int MERGE_CHUNK, int HALVES>
+__global__ __launch_bounds__(64 * (D / 16) * HALVES) void merge_kernel(MergeParams p) {
   constexpr int DB = D / 16;
   const int lane = threadIdx.x & 63;
-  const int db = threadIdx.x >> 6;
+  const int wv = threadIdx.x >> 6;
+  const int db = wv % DB, half = wv / DB;
   const int H = p.num_heads;
   const int slot = blockIdx.x >> 3;
   if (slot >= p.merge_slots) return;      // uniform over the work-group
-  const int pair = p.plan[p.merge_table + (blockIdx.x & (KVC_NUM_XCD - 1)) * p.merge_slots + slot];
+  // {tile * H + head, splits, first output row, valid rows}
+  const i32x4 te = *reinterpret_cast<const i32x4*>(
+      p.plan + p.merge_table + KVC_MERGE_INTS * ((blockIdx.x & (KVC_NUM_XCD - 1)) * p.merge_slots + slot));
+  const int pair = te.x;
   if (pair < 0) return;
   const int gt = pair / H;                // global query tile
   const int h = pair - gt * H;
-  const i32x4 te = *reinterpret_cast<const i32x4*>(p.plan + p.tile_table + KVC_TILE_INTS * gt);
   const int r16 = lane & 15, g4 = lane >> 4;
   const size_t tstride = (size_t)H * p.tiles_cap;   // between splits, in tiles
   const size_t t0 = (size_t)h * p.tiles_cap + gt;
@@ -901,7 +904,9 @@ __global__ __launch_bounds__(512) void merge_kernel(MergeParams p) {
   const float* pl = p.part_lse + t0 * KVC_Q_TILE + r16;
   float m = -INFINITY, wsum = 0.f;
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int c0 = 0; c0 < p.max_split; c0 += MERGE_CHUNK) {
+  // With two halves, the waves of half 1 fold the odd chunks, those of half 0
+  // the even ones; both load in the same round trip.
+  for (int c0 = half * MERGE_CHUNK; c0 < p.max_split; c0 += HALVES * MERGE_CHUNK) {
     float lse[MERGE_CHUNK];
     u32x2 x[MERGE_CHUNK];
 #pragma unroll
@@ -911,8 +916,8 @@ __global__ __launch_bounds__(512) void merge_kernel(MergeParams p) {
         lse[j] = pl[c * KVC_Q_TILE];
         x[j] = *reinterpret_cast<const u32x2*>(po + c * DB * 256);
       }
-    const int nsp = te.x;
-    if (nsp <= 1) return;                 // single split: attention wrote o itself
+    const int nsp = te.y;
+    if (HALVES == 1 && nsp <= 1) return;  // single split: attention wrote o itself
     float mc = m;
 #pragma unroll
     for (int j = 0; j < MERGE_CHUNK; ++j)
@@ -930,8 +935,30 @@ __global__ __launch_bounds__(512) void merge_kernel(MergeParams p) {
       }
     m = mc;
   }
-  if (r16 < te.z) {
-    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.o) + ((size_t)(te.y + r16) * H + h) * D + 16 * db + 4 * g4) =
+  if constexpr (HALVES == 2) {
+    if (te.y <= 1) return;                // uniform: attention wrote o itself
+    // half 1 hands its fold to half 0 through LDS: (m, wsum, acc) per lane
+    __shared__ float xs[DB * 64 * 6];
+    float* x = xs + (db * 64 + lane) * 6;
+    if (half == 1) {
+      x[0] = m;
+      x[1] = wsum;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[2 + i] = acc[i];
+    }
+    __syncthreads();
+    if (half == 1) return;
+    const float m1 = x[0];
+    const float mm = fmaxf(m, m1);
+    if (mm != -INFINITY) {
+      const float a0 = __builtin_amdgcn_exp2f(m - mm), a1 = __builtin_amdgcn_exp2f(m1 - mm);
+      wsum = wsum * a0 + x[1] * a1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = acc[i] * a0 + x[2 + i] * a1;
+    }
+  }
+  if (r16 < te.w) {
+    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.o) + ((size_t)(te.z + r16) * H + h) * D + 16 * db + 4 * g4) =
         El<E>::cvt4(acc * (1.0f / wsum));
   }
 }
@@ -969,17 +996,17 @@ int launch_attention(const AttnParams& p, int32_t grid, void* s) {
   return (int)hipErrorInvalidValue;
 }
 
-template <int E, int CH>
-static int launch_merge_ec(const MergeParams& p, int grid, int threads, hipStream_t hs) {
+template <int E, int CH, int HV>
+static int launch_merge_ec(const MergeParams& p, int grid, hipStream_t hs) {
   switch (p.head_dim) {
     case 32:
-      hipLaunchKernelGGL((merge_kernel<32, E, CH>), dim3(grid), dim3(threads), 0, hs, p);
+      hipLaunchKernelGGL((merge_kernel<32, E, CH, HV>), dim3(grid), dim3(64 * 2 * HV), 0, hs, p);
       break;
     case 64:
-      hipLaunchKernelGGL((merge_kernel<64, E, CH>), dim3(grid), dim3(threads), 0, hs, p);
+      hipLaunchKernelGGL((merge_kernel<64, E, CH, HV>), dim3(grid), dim3(64 * 4 * HV), 0, hs, p);
       break;
     case 128:
-      hipLaunchKernelGGL((merge_kernel<128, E, CH>), dim3(grid), dim3(threads), 0, hs, p);
+      hipLaunchKernelGGL((merge_kernel<128, E, CH, HV>), dim3(grid), dim3(64 * 8 * HV), 0, hs, p);
       break;
     default:
       return (int)hipErrorInvalidValue;
@@ -987,20 +1014,23 @@ static int launch_merge_ec(const MergeParams& p, int grid, int threads, hipStrea
   return (int)hipGetLastError();
 }
 
+// Chunk: the smallest of 2, 4, 8 that covers the largest split count, else
+// 8.  Beyond one chunk, a second set of waves takes every other chunk.
 template <int E>
-static int launch_merge_e(const MergeParams& p, int grid, int threads, hipStream_t hs) {
-  if (p.max_split <= 2) return launch_merge_ec<E, 2>(p, grid, threads, hs);
-  if (p.max_split <= 4) return launch_merge_ec<E, 4>(p, grid, threads, hs);
-  return launch_merge_ec<E, 8>(p, grid, threads, hs);
+static int launch_merge_e(const MergeParams& p, int grid, hipStream_t hs) {
+  if (p.max_split <= 2) return launch_merge_ec<E, 2, 1>(p, grid, hs);
+  if (p.max_split <= 4) return launch_merge_ec<E, 4, 1>(p, grid, hs);
+  if (p.max_split <= 8) return launch_merge_ec<E, 8, 1>(p, grid, hs);
+  return launch_merge_ec<E, 8, 2>(p, grid, hs);
 }
 
 int launch_merge(const MergeParams& p, void* s) {
   const hipStream_t hs = (hipStream_t)s;
   const int grid = KVC_NUM_XCD * p.merge_slots;   // one work-group per merged (query tile, head)
   if (grid == 0) return 0;
-  const int threads = 64 * (p.head_dim / 16);   // one wave per 16-row d block
-  if (p.dtype == 0) return launch_merge_e<0>(p, grid, threads, hs);
-  if (p.dtype == 1) return launch_merge_e<1>(p, grid, threads, hs);
+  // one wave per 16-row d block (and per half of the chunks)
+  if (p.dtype == 0) return launch_merge_e<0>(p, grid, hs);
+  if (p.dtype == 1) return launch_merge_e<1>(p, grid, hs);
   return (int)hipErrorInvalidValue;
 }
 

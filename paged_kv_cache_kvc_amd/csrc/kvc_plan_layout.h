@@ -13,13 +13,12 @@
 //   [aligned to 4 ints, + 4 * total units)         unit tables: per stream, per
 //                                                  64-slot work unit in table order,
 //                                                  {K byte offset lo, hi, valid slots, 0}
-//   [aligned to 4 ints, + 4 * total query tiles)   tile table: per query tile of
-//                                                  every stream, in output order,
-//                                                  {KV splits, first output row,
-//                                                  valid rows, 0}
-//   [+ 8 * merge slots per XCD)                    merge order: for each of the 8
-//                                                  XCDs, the (tile * H + head) pairs
-//                                                  to merge there, -1 padded
+//   [aligned to 4 ints, + 4 * 8 * merge slots)     merge order: for each of the 8
+//                                                  XCDs, the (query tile, head)
+//                                                  pairs of split streams to merge
+//                                                  there, {tile * H + head, KV
+//                                                  splits, first output row, valid
+//                                                  rows}, padded with pair -1
 #ifndef KVC_PLAN_LAYOUT_H
 #define KVC_PLAN_LAYOUT_H
 
@@ -50,13 +49,13 @@
 #define KVC_HDR_NUM_ROWS 2
 #define KVC_HDR_ANY_SPLIT 3
 #define KVC_HDR_NUM_TILES 4
-#define KVC_HDR_TILE_TABLE 5   // offset in ints of the tile table from the plan start
+#define KVC_HDR_UNUSED 5
 #define KVC_HDR_MERGE_TABLE 6  // offset in ints of the merge order
 #define KVC_HDR_MERGE_SLOTS 7  // merge slots per XCD (the merge grid is 8 times this)
 // XCDs of the device; work-groups are dispatched to them round-robin.
 #define KVC_NUM_XCD 8
-// Ints per tile-table entry.
-#define KVC_TILE_INTS 4
+// Ints per merge-order entry.
+#define KVC_MERGE_INTS 4
 
 typedef struct kvc_dev_stream {
   int32_t q_row0;     // first query/output row of this stream
