@@ -249,9 +249,9 @@ void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const s
   // long as its longest split times the number of rounds in which the
   // work-groups run.  The target work-group count is what the device holds
   // at once (one round); the split counts start from each stream's share of
-  // it, in proportion to queries x visible tokens, rounded down, and then the
-  // stream whose splits are longest gains a split while the whole launch
-  // still fits in one round.
+  // it, in proportion to queries x visible tokens, rounded down; then the
+  // stream whose splits are longest gains a split while that shortens them
+  // and the whole launch still fits in one round.
   const int32_t per_group = kvc_group_tiles(c.head_dim);
   double total_work = 0;
   for (int i = 0; i < n; ++i) total_work += (double)frames[i] * (double)kv_len[i];
@@ -275,19 +275,16 @@ void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const s
     nsplit[i] = std::max<int64_t>(1, std::min<int64_t>((int64_t)std::floor(want), cap[i]));
     items_total += groups[i] * nsplit[i];
   }
+  // The launch lasts as long as the longest split: only that stream's splits
+  // are worth adding, and once it cannot gain one (at its cap, over the
+  // target, or no shorter for it), no other split would shorten the launch.
   for (;;) {
-    int best = -1;
-    int64_t best_len = 0;
-    for (int i = 0; i < n; ++i) {
-      if (nsplit[i] >= cap[i] || items_total + groups[i] > pol.target_workgroups) continue;
-      const int64_t len = ceil_div(units[i], nsplit[i]);
-      if (len > best_len) {
-        best = i;
-        best_len = len;
-      }
-    }
-    // a split that does not shorten the longest split of its stream gains nothing
-    if (best < 0 || ceil_div(units[best], nsplit[best] + 1) >= best_len) break;
+    int best = 0;
+    for (int i = 1; i < n; ++i)
+      if (ceil_div(units[i], nsplit[i]) > ceil_div(units[best], nsplit[best])) best = i;
+    if (nsplit[best] >= cap[best] || items_total + groups[best] > pol.target_workgroups ||
+        ceil_div(units[best], nsplit[best] + 1) >= ceil_div(units[best], nsplit[best]))
+      break;
     ++nsplit[best];
     items_total += groups[best];
   }

@@ -269,8 +269,9 @@ def test_split_policy_options():
 def test_split_counts_fill_one_round(name):
     """The planner's split counts keep every attention work-group of a run
     resident at once (at most the target count, which defaults to what the
-    device holds: 2 per CU up to D = 64, 1 at D = 128), and no stream could
-    take one more split that shortens its longest split and still fit."""
+    device holds: 2 per CU up to D = 64, 1 at D = 128), and the stream with
+    the longest splits, which sets the launch's length, could not take one
+    more split that shortens them and still fit."""
     wl = syn.WORKLOADS[name]
     c = kvc.PagedKVCache(cfg_of(wl), metadata_only=True)
     F = max(wl.frames)
@@ -301,9 +302,11 @@ def test_split_counts_fill_one_round(name):
     ns = [int(x) for x in p["n_splits"]]
     items = sum(g * n for g, n in zip(groups, ns))
     assert items <= target
-    for i, (u, g, n) in enumerate(zip(units, groups, ns)):
-        if n < min(kvc.MAX_SPLITS, u) and ceil(u, n + 1) < ceil(u, n):
-            assert items + g > target, (name, i, ns)
+    lens = [ceil(u, n) for u, n in zip(units, ns)]
+    i = lens.index(max(lens))
+    u, g, n = units[i], groups[i], ns[i]
+    if n < min(kvc.MAX_SPLITS, u) and ceil(u, n + 1) < ceil(u, n):
+        assert items + g > target, (name, i, ns)
 
 
 def test_scale_phase_multi_frame_steps_match_oracle():
