@@ -870,17 +870,20 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
 // ---------------------------------------------------------------------------
 // One work-group of DB waves per (query tile, head) of a split stream, on the
 // XCD whose L2 holds most of its partials (the plan's merge order lists the
-// pairs of each XCD; work-group b runs on XCD b % 8).  Wave w takes d block w,
-// each lane the 4 values it holds in every split's partial (the accumulator
-// lane order).  The tile's entry in the plan's tile table gives its stream's
-// split count and output rows.  The partials and log-sum-exps of up to
-// MERGE_CHUNK splits are loaded together, then folded in split order with
+// pairs of each XCD; work-group b runs on XCD b % 8).  Wave w takes d block
+// w % DB, each lane the 4 values it holds in every split's partial (the
+// accumulator lane order).  The pair's merge-order entry also gives its
+// stream's split count and output rows.  The partials and log-sum-exps of up
+// to MERGE_CHUNK splits are loaded together, then folded in split order with
 // weights 2^(lse_c - running max): one memory round trip per chunk, and every
 // sum in a fixed order.  Splits past the tile's own count (other streams may
 // have more) are loaded from the workspace but never used.  The chunk is the
 // smallest of 2, 4, 8 that covers the plan's largest split count, else 8: a
 // larger chunk holds more registers, and the occupancy it costs outweighs the
 // round trips it saves (measured: 16 splits merge faster in two chunks of 8).
+// With more than one chunk, HALVES = 2 doubles the waves: the second set
+// folds the odd chunks in the same round trip as the first set's even ones,
+// and the two folds are combined through LDS (fixed order again).
 template <int D, int E, int MERGE_CHUNK, int HALVES>
 __global__ __launch_bounds__(64 * (D / 16) * HALVES) void merge_kernel(MergeParams p) {
   constexpr int DB = D / 16;
