@@ -445,11 +445,13 @@ __device__ __forceinline__ float renorm(const f32x4 (&s)[N], float sl, bool& fre
 //   step 0: QK(s, own 1), PV(s-1, own 1), PV(s-1, shared) | probs(s, own 0)
 //   step 1: QK(s, shared), PV(s, own 0)                   | probs(s, own 1)
 //   step 2: QK(s+1, own 0)                                 | probs(s, shared)
-// In step 0, after its MFMAs are issued, the V operands of stage s are read
-// from LDS, stage s+1 is published (barrier) and its K operands are read,
-// all ahead of the step's vector work; the shared block's K of stage s+1 is
-// read after step 1.  An MFMA result is read by the vector unit one
-// step after its MFMA at the earliest.  After the last stage the same code
+// Each step is one straight-line block in which scheduling groups interleave
+// the MFMAs with the vector work; the rare branches (partial-stage masking,
+// the exact renormalisation) sit between the blocks.  After step 0, the V
+// operands of stage s are read from LDS, stage s+1 is published (barrier)
+// and its K operands are read, ahead of steps 1 and 2; the shared block's K
+// of stage s+1 is read after step 1.  An MFMA result is read by the vector
+// unit one step after its MFMA at the earliest.  After the last stage the same code
 // reads a ring slot that holds no stage and computes a QK^T that is never
 // used; every LDS address stays inside the ring.
 template <int D, int E>
