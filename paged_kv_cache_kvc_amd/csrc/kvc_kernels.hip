@@ -407,7 +407,7 @@ __device__ __forceinline__ void mask_scores(f32x4 (&s)[N], const int (&boff)[N],
 // fresh tile whose slots were all masked stays fresh.  Taken rarely; a few
 // wait states at both ends keep it clear of the MFMAs around it.
 template <int N, int DB, int E>
-__device__ __forceinline__ float renorm(const f32x4 (&s)[N], float sl, bool& fresh, float& ref, float& nref,
+__device__ __forceinline__ float renorm(const f32x4 (&s)[N], float sl, int& fresh, float& ref, float& nref,
                                         float& l, f32x4 (&o)[DB], uint32_t (&pk)[2 * N]) {
   asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
   float m = s[0][0];
@@ -416,8 +416,9 @@ __device__ __forceinline__ float renorm(const f32x4 (&s)[N], float sl, bool& fre
 #pragma unroll
     for (int i = 0; i < 4; ++i) m = max2(m, s[j][i]);
   m = __builtin_fmaf(lane_swap_max(m), sl, nref);
-  const bool first = fresh;
-  fresh = fresh && __builtin_amdgcn_ballot_w64(m == -INFINITY) != 0;
+  const bool first = fresh != 0;
+  // uniform: kept in a scalar register
+  fresh = __builtin_amdgcn_readfirstlane((int)(first && __builtin_amdgcn_ballot_w64(m == -INFINITY) != 0));
   const float shift = first ? (m == -INFINITY ? 0.0f : m) : fmaxf(m, 0.0f);
   if (!first) {
     const float alpha = __builtin_amdgcn_exp2f(-shift);
@@ -531,7 +532,7 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
   // not set)
   float ref0 = 0.f, ref1 = 0.f, ref2 = 0.f;
   float nref0 = 0.f, nref1 = 0.f, nref2 = 0.f;
-  bool fresh0 = true, fresh1 = true, fresh2 = true;
+  int fresh0 = 1, fresh1 = 1, fresh2 = 1;
   float l0 = 0.f, l1 = 0.f, l2 = 0.f;
   f32x4 o0[DB], o1[DB], o2[DB];
 #pragma unroll
@@ -646,7 +647,9 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
   // bf16; for f16 the lane sums of the packing (the f16 build has no
   // registers to spare for the sum accumulators)
   constexpr bool MSUM = E == 0;
-  const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{El<E>::ONE2, El<E>::ONE2, El<E>::ONE2, El<E>::ONE2});
+  bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{El<E>::ONE2, El<E>::ONE2, El<E>::ONE2, El<E>::ONE2});
+  // held in vector registers for the whole loop, not rebuilt before each use
+  asm volatile("" : "+v"(ones));
   f32x4 sc0[4], sc1[4], sc2[1];
   uint32_t pk0[8], pk1[8], pk2[2];
   u32x4 pbsh = u32x4{0u, 0u, 0u, 0u};
