@@ -643,10 +643,7 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
   const int kb_sh[1] = {32 * shPP + 4 * shTT};
 
   bf16x8 kop[4][KS], ksh[KS], vop[DB][2];
-  // Own tiles' stage sums: by MFMA (colsum, an all-ones V^T operand) for
-  // bf16; for f16 the lane sums of the packing (the f16 build has no
-  // registers to spare for the sum accumulators)
-  constexpr bool MSUM = E == 0;
+  // Own tiles' stage sums: by MFMA (colsum, an all-ones V^T operand)
   bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{El<E>::ONE2, El<E>::ONE2, El<E>::ONE2, El<E>::ONE2});
   // held in vector registers for the whole loop, not rebuilt before each use
   asm volatile("" : "+v"(ones));
@@ -697,14 +694,9 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
       O::pv(vop, pb, o1);
     }
     O::qk(kop, q1, sc1);
-    f32x4 cs0;
-    float ls0;
-    if constexpr (MSUM) {
-      probs_pack<4, E>(sc0, sl, nref0, pk0);
-      cs0 = O::colsum(ones, {u32x4{pk0[0], pk0[1], pk0[2], pk0[3]}, u32x4{pk0[4], pk0[5], pk0[6], pk0[7]}});
-    } else {
-      ls0 = probs<4, E>(sc0, sl, nref0, pk0);
-    }
+    probs_pack<4, E>(sc0, sl, nref0, pk0);
+    const f32x4 cs0 =
+        O::colsum(ones, {u32x4{pk0[0], pk0[1], pk0[2], pk0[3]}, u32x4{pk0[4], pk0[5], pk0[6], pk0[7]}});
     // one MFMA, then two vector instructions, while both last
 #pragma unroll
     for (int i = 0; i < 20; ++i) {
@@ -733,29 +725,17 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
     if (partial) mask_scores<4>(sc1, kb_own, valid, g4);
     O::qk1(ksh, q2, sc2);
     // own tile 0: check its stage sum before its P.V
-    float lt;
-    if constexpr (MSUM) {
-      lt = cs0[0];
-      if (fresh0 || __builtin_amdgcn_ballot_w64(lt > LAZY_COL_LIMIT))
-        lt = lane_swap_sum(renorm<4, DB, E>(sc0, sl, fresh0, ref0, nref0, l0, o0, pk0));
-    } else {
-      lt = ls0;
-      if (fresh0 || __builtin_amdgcn_ballot_w64(lt > LAZY_SUM_LIMIT))
-        lt = renorm<4, DB, E>(sc0, sl, fresh0, ref0, nref0, l0, o0, pk0);
-    }
+    float lt = cs0[0];
+    if (fresh0 || __builtin_amdgcn_ballot_w64(lt > LAZY_COL_LIMIT))
+      lt = lane_swap_sum(renorm<4, DB, E>(sc0, sl, fresh0, ref0, nref0, l0, o0, pk0));
     l0 += lt;
     {
       u32x4 pb[2] = {u32x4{pk0[0], pk0[1], pk0[2], pk0[3]}, u32x4{pk0[4], pk0[5], pk0[6], pk0[7]}};
       O::pv(vop, pb, o0);
     }
-    f32x4 cs1;
-    float ls1;
-    if constexpr (MSUM) {
-      probs_pack<4, E>(sc1, sl, nref1, pk1);
-      cs1 = O::colsum(ones, {u32x4{pk1[0], pk1[1], pk1[2], pk1[3]}, u32x4{pk1[4], pk1[5], pk1[6], pk1[7]}});
-    } else {
-      ls1 = probs<4, E>(sc1, sl, nref1, pk1);
-    }
+    probs_pack<4, E>(sc1, sl, nref1, pk1);
+    const f32x4 cs1 =
+        O::colsum(ones, {u32x4{pk1[0], pk1[1], pk1[2], pk1[3]}, u32x4{pk1[4], pk1[5], pk1[6], pk1[7]}});
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -776,15 +756,9 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
     // rather than sunk past the branch below
     asm volatile("" : "+v"(lt2));
     // own tile 1: check its stage sum (its P.V follows in the next step 0)
-    if constexpr (MSUM) {
-      lt = cs1[0];
-      if (fresh1 || __builtin_amdgcn_ballot_w64(lt > LAZY_COL_LIMIT))
-        lt = lane_swap_sum(renorm<4, DB, E>(sc1, sl, fresh1, ref1, nref1, l1, o1, pk1));
-    } else {
-      lt = ls1;
-      if (fresh1 || __builtin_amdgcn_ballot_w64(lt > LAZY_SUM_LIMIT))
-        lt = renorm<4, DB, E>(sc1, sl, fresh1, ref1, nref1, l1, o1, pk1);
-    }
+    lt = cs1[0];
+    if (fresh1 || __builtin_amdgcn_ballot_w64(lt > LAZY_COL_LIMIT))
+      lt = lane_swap_sum(renorm<4, DB, E>(sc1, sl, fresh1, ref1, nref1, l1, o1, pk1));
     l1 += lt;
     if (fresh2 || __builtin_amdgcn_ballot_w64(lt2 > LAZY_SUM_LIMIT))
       lt2 = renorm<1, DB, E>(sc2, sl, fresh2, ref2, nref2, l2, o2, pk2);
@@ -826,11 +800,10 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
       for (int db = 0; db < DB; ++db) *reinterpret_cast<u32x2*>(orow + 16 * db + 4 * g4) = El<E>::cvt4(o[db] * inv);
     }
   };
-  // with MSUM, l0 and l1 are whole column sums; otherwise, like l2, the lane
-  // group's share
-  const float lw0 = MSUM ? l0 : lane_swap_sum(l0), lw1 = MSUM ? l1 : lane_swap_sum(l1);
-  if (wave < n_own) store(t_lo + wave, ref0, lw0, o0);
-  if (wave + 4 < n_own) store(t_lo + wave + 4, ref1, lw1, o1);
+  // l0 and l1 are whole column sums (the column-sum MFMAs); l2 is the lane
+  // group's share, summed in the shared tile's merge below
+  if (wave < n_own) store(t_lo + wave, ref0, l0, o0);
+  if (wave + 4 < n_own) store(t_lo + wave + 4, ref1, l1, o1);
 
   if (has_shared) {
     // merge the four waves' partial states of the shared tile (one split
