@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 3
+#define KVC_ABI_VERSION 4
 
 typedef struct kvc_ctx kvc_ctx;
 typedef void* kvc_stream_t;   /* hipStream_t */
@@ -279,6 +279,13 @@ kvc_status kvc_get_plan(const kvc_ctx* ctx, int32_t* planned_streams, int32_t* k
                         int32_t* kv_indices, int32_t* last_page_len, int32_t* n_patch_pages,
                         int32_t* qo_indptr, int32_t* n_splits, int32_t capacity_streams,
                         int32_t capacity_indices, int32_t* num_planned, int32_t* num_indices);
+
+/* Shape of the current plan's attention launch (for tests and tuning):
+ *   work_items:  attention work-groups, (stream, head, KV split, query group);
+ *   group_tiles: query tiles of 16 rows per query group, 9 when the four waves
+ *                of a work-group share a ninth tile, else 8.
+ * Either pointer may be NULL.  Errors: KVC_ERR_ARG, KVC_ERR_STATE (no plan). */
+kvc_status kvc_get_plan_shape(const kvc_ctx* ctx, int32_t* work_items, int32_t* group_tiles);
 
 /* [p3] §Inspecting Cache Statistics for one stream. */
 kvc_status kvc_get_stats(const kvc_ctx* ctx, int32_t stream, kvc_stats* out);

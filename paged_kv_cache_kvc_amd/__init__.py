@@ -44,7 +44,7 @@ KVC_KERNEL_MERGE = 1
 KVC_KERNEL_APPEND = 2
 
 MAX_SPLITS = 64
-ABI_VERSION = 3   # KVC_ABI_VERSION of include/kvc.h
+ABI_VERSION = 4   # KVC_ABI_VERSION of include/kvc.h
 
 
 class KvcError(RuntimeError):
@@ -88,6 +88,7 @@ SIGNATURES = {
     "kvc_plan": (_I32, [_P, _P]),
     "kvc_run": (_I32, [_P, _I32, _P, _P, _P]),
     "kvc_get_plan": (_I32, [_P, _PI32, _PI32, _PI32, _PI32, _PI32, _PI32, _PI32, _I32, _I32, _PI32, _PI32]),
+    "kvc_get_plan_shape": (_I32, [_P, _PI32, _PI32]),
     "kvc_get_stats": (_I32, [_P, _I32, ctypes.POINTER(KvcStats)]),
     "kvc_set_option": (_I32, [_P, _I32, ctypes.c_int64]),
     "kvc_get_option": (_I32, [_P, _I32, ctypes.POINTER(ctypes.c_int64)]),
@@ -311,6 +312,14 @@ class PagedKVCache:
                                           ptr["n_splits"], ns, max(nidx, 1), None, None), "get_plan")
         arrs["kv_indices"] = arrs["kv_indices"][:nidx]
         return arrs
+
+    def get_plan_shape(self) -> Dict[str, int]:
+        """Attention work-groups of the current plan and query tiles per group."""
+        items = ctypes.c_int32()
+        tiles = ctypes.c_int32()
+        self._check(self.lib.kvc_get_plan_shape(self._ctx, ctypes.byref(items), ctypes.byref(tiles)),
+                    "get_plan_shape")
+        return {"work_items": items.value, "group_tiles": tiles.value}
 
     def set_option(self, option: int, value: int):
         self._check(self.lib.kvc_set_option(self._ctx, option, value), "set_option")

@@ -452,6 +452,7 @@ kvc_status kvc_run(kvc_ctx* c, int32_t block, const void* q, void* o, kvc_stream
   a.num_items = c->plan.num_items;
   a.dtype = cf.dtype;
   a.items_per_xcd = (c->plan.num_items + 7) / 8;
+  a.shared_tile = c->plan.shared_tile ? 1 : 0;
   const int32_t grid = 8 * a.items_per_xcd;
   int e = timed(c, KVC_KERNEL_ATTENTION, hs, [&] { return kvc::launch_attention(a, grid, hs); });
   if (e) return hip_fail(c, e, "attention launch");
@@ -496,6 +497,14 @@ kvc_status kvc_get_plan(const kvc_ctx* c, int32_t* planned, int32_t* kv_indptr, 
   if (n_patch_pages) std::copy(p.n_patch_pages.begin(), p.n_patch_pages.end(), n_patch_pages);
   if (qo_indptr) std::copy(p.qo_indptr.begin(), p.qo_indptr.end(), qo_indptr);
   if (n_splits) std::copy(p.n_split.begin(), p.n_split.end(), n_splits);
+  return KVC_OK;
+}
+
+kvc_status kvc_get_plan_shape(const kvc_ctx* c, int32_t* work_items, int32_t* group_tiles) {
+  if (!c) return KVC_ERR_ARG;
+  if (!c->have_plan) return fail(const_cast<kvc_ctx*>(c), KVC_ERR_STATE, "no plan");
+  if (work_items) *work_items = c->plan.num_items;
+  if (group_tiles) *group_tiles = kvc_group_tiles(c->plan.shared_tile ? 1 : 0);
   return KVC_OK;
 }
 

@@ -244,7 +244,8 @@ void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const s
   }
 
   // Work decomposition: each work item is (stream, head, KV split, query
-  // group).  Query groups hold at most KVC_ATTN_WAVES * tiles_per_wave tiles.
+  // group).  Query groups hold at most KVC_ATTN_WAVES * KVC_TILES_PER_WAVE
+  // tiles, plus a ninth shared by the waves when the launch uses one.
   // Every work-group costs the same per 64-slot unit, so a launch takes as
   // long as its longest split times the number of rounds in which the
   // work-groups run.  The target work-group count is what the device holds
@@ -252,42 +253,73 @@ void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const s
   // it, in proportion to queries x visible tokens, rounded down; then the
   // stream whose splits are longest gains a split while that shortens them
   // and the whole launch still fits in one round.
-  const int32_t per_group = kvc_group_tiles(c.head_dim);
   double total_work = 0;
   for (int i = 0; i < n; ++i) total_work += (double)frames[i] * (double)kv_len[i];
   const int32_t max_splits = std::max(1, std::min<int32_t>(pol.max_splits, KVC_MAX_SPLITS));
   const int32_t upp = (int32_t)ceil_div(std::max(1, P), KVC_KV_TILE);
   const int32_t ups = (int32_t)ceil_div(c.page_size, KVC_KV_TILE);
-  std::vector<int64_t> units(n), groups(n), nsplit(n), cap(n);
-  int64_t items_total = 0;
+  std::vector<int64_t> units(n), cap(n);
   for (int i = 0; i < n; ++i) {
     const int32_t n_patch = p.n_patch_pages[i];
     const int32_t n_special = p.kv_indptr[i + 1] - p.kv_indptr[i] - n_patch;
     units[i] = std::max<int64_t>(
         1, (int64_t)n_patch * upp +
                (n_special > 0 ? (int64_t)(n_special - 1) * ups + ceil_div(p.last_page_len[i], KVC_KV_TILE) : 0));
-    const int32_t nqt = (int32_t)ceil_div(frames[i] * c.tokens_per_frame, KVC_Q_TILE);
-    groups[i] = (int64_t)c.num_heads * ceil_div(nqt, per_group);
     cap[i] = std::min<int64_t>(max_splits, units[i]);
-    const double want = total_work > 0 ? (double)pol.target_workgroups * (double)frames[i] * (double)kv_len[i] /
-                                             total_work / (double)groups[i]
-                                       : 1.0;
-    nsplit[i] = std::max<int64_t>(1, std::min<int64_t>((int64_t)std::floor(want), cap[i]));
-    items_total += groups[i] * nsplit[i];
   }
-  // The launch lasts as long as the longest split: only that stream's splits
-  // are worth adding, and once it cannot gain one (at its cap, over the
-  // target, or no shorter for it), no other split would shorten the launch.
-  for (;;) {
-    int best = 0;
-    for (int i = 1; i < n; ++i)
-      if (ceil_div(units[i], nsplit[i]) > ceil_div(units[best], nsplit[best])) best = i;
-    if (nsplit[best] >= cap[best] || items_total + groups[best] > pol.target_workgroups ||
-        ceil_div(units[best], nsplit[best] + 1) >= ceil_div(units[best], nsplit[best]))
-      break;
-    ++nsplit[best];
-    items_total += groups[best];
-  }
+  // Split counts for one query grouping (groups of at most per_group tiles);
+  // returns the launch's estimated length in tile-steps per wave.
+  struct Choice {
+    std::vector<int64_t> groups, nsplit;
+    double cost;
+  };
+  auto choose = [&](int32_t per_group) {
+    Choice ch;
+    ch.groups.resize(n);
+    ch.nsplit.resize(n);
+    int64_t items_total = 0;
+    for (int i = 0; i < n; ++i) {
+      const int32_t nqt = (int32_t)ceil_div(frames[i] * c.tokens_per_frame, KVC_Q_TILE);
+      ch.groups[i] = (int64_t)c.num_heads * ceil_div(nqt, per_group);
+      const double want = total_work > 0 ? (double)pol.target_workgroups * (double)frames[i] * (double)kv_len[i] /
+                                               total_work / (double)ch.groups[i]
+                                         : 1.0;
+      ch.nsplit[i] = std::max<int64_t>(1, std::min<int64_t>((int64_t)std::floor(want), cap[i]));
+      items_total += ch.groups[i] * ch.nsplit[i];
+    }
+    // The launch lasts as long as the longest split: only that stream's
+    // splits are worth adding, and once it cannot gain one (at its cap, over
+    // the target, or no shorter for it), no other split would shorten the
+    // launch.
+    auto longest = [&]() {
+      int best = 0;
+      for (int i = 1; i < n; ++i)
+        if (ceil_div(units[i], ch.nsplit[i]) > ceil_div(units[best], ch.nsplit[best])) best = i;
+      return best;
+    };
+    for (;;) {
+      const int best = longest();
+      if (ch.nsplit[best] >= cap[best] || items_total + ch.groups[best] > pol.target_workgroups ||
+          ceil_div(units[best], ch.nsplit[best] + 1) >= ceil_div(units[best], ch.nsplit[best]))
+        break;
+      ++ch.nsplit[best];
+      items_total += ch.groups[best];
+    }
+    // per stage, a wave does 2 tiles plus a quarter of the shared one
+    const double per_stage = per_group > KVC_ATTN_WAVES * KVC_TILES_PER_WAVE ? 2.25 : 2.0;
+    const int64_t rounds = std::max<int64_t>(1, ceil_div(items_total, std::max(1, pol.target_workgroups)));
+    const int b = longest();
+    ch.cost = (double)ceil_div(units[b], ch.nsplit[b]) * per_stage * (double)rounds;
+    return ch;
+  };
+  // Query groups of 9 tiles (the ninth shared by the four waves) or of 8:
+  // the shared tile packs 17 tiles into two groups, but costs every stage a
+  // quarter tile per wave; take the grouping with the shorter launch.
+  const Choice with_shared = choose(kvc_group_tiles(1)), without = choose(kvc_group_tiles(0));
+  p.shared_tile = !(without.cost < with_shared.cost);
+  const Choice& ch = p.shared_tile ? with_shared : without;
+  const int32_t per_group = kvc_group_tiles(p.shared_tile ? 1 : 0);
+  const std::vector<int64_t>& nsplit = ch.nsplit;
 
   p.image.assign(KVC_PLAN_HEADER_INTS + (size_t)KVC_STREAM_REC_INTS * n + p.kv_indices.size(), 0);
   int32_t item = 0, tiles = 0;
@@ -330,6 +362,7 @@ void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const s
   p.image[KVC_HDR_NUM_ROWS] = p.num_rows;
   p.image[KVC_HDR_ANY_SPLIT] = p.any_split ? 1 : 0;
   p.image[KVC_HDR_NUM_TILES] = p.num_tiles;
+  p.image[KVC_HDR_SHARED_TILE] = p.shared_tile ? 1 : 0;
   std::copy(p.kv_indices.begin(), p.kv_indices.end(),
             p.image.begin() + KVC_PLAN_HEADER_INTS + (size_t)KVC_STREAM_REC_INTS * n);
 

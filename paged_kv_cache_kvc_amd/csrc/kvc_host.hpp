@@ -122,6 +122,7 @@ struct HostPlan {
   int32_t num_items = 0;
   int32_t num_rows = 0;
   int32_t num_tiles = 0;
+  bool shared_tile = true;             // query groups with a shared ninth tile (else up to 8 tiles)
   int32_t merge_table = 0;             // offset in ints of the merge order in image
   int32_t merge_slots = 0;             // merge slots per XCD
   bool any_split = false;

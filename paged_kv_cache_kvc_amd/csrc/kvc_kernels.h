@@ -41,6 +41,7 @@ struct AttnParams {
   FastDiv div_patch, div_page;
   float scale_log2;         // log2(e) / sqrt(D)
   int32_t num_items, items_per_xcd;
+  int32_t shared_tile;      // 1: query groups of up to 9 tiles, the ninth shared by the waves; 0: up to 8
   int32_t dtype;            // element type: 0 bfloat16, 1 float16
 };
 

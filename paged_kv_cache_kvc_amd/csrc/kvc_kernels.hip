@@ -455,7 +455,7 @@ __device__ __forceinline__ float renorm(const f32x4 (&s)[N], float sl, int& fres
 // unit one step after its MFMA at the earliest.  After the last stage the same code
 // reads a ring slot that holds no stage and computes a QK^T that is never
 // used; every LDS address stays inside the ring.
-template <int D, int E>
+template <int D, int E, bool SH>
 __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams p) {
   using S = Shape<D>;
   using O = Ops<D, E>;
@@ -494,7 +494,7 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
   const int t_lo = grp * nqt / st.n_group;
   const int t_hi = (grp + 1) * nqt / st.n_group;
   const int ntile = t_hi - t_lo;
-  const bool has_shared = ntile == 4 * 2 + 1;
+  const bool has_shared = SH && ntile == 4 * 2 + 1;
   const int n_own = has_shared ? 8 : ntile;
   const int u0 = split * st.n_units / st.n_split;
   const int u1 = (split + 1) * st.n_units / st.n_split;
@@ -525,7 +525,7 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
   bf16x8 q0[KS], q1[KS], q2[KS];
   load_q(t_lo + wave, wave < n_own, q0);
   load_q(t_lo + wave + 4, wave + 4 < n_own, q1);
-  load_q(t_hi - 1, has_shared, q2);
+  if constexpr (SH) load_q(t_hi - 1, has_shared, q2);
 
   // softmax state of tiles own 0, own 1, shared
   // ref of each tile and its negation; fresh: no valid slot seen yet (ref
@@ -671,7 +671,7 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
     wait_vmcnt<0>();
   block_barrier();
   read_k(0, kop);
-  read_ksh(0, ksh);
+  if constexpr (SH) read_ksh(0, ksh);
   O::qk(kop, q0, sc0);
 
   // Stage 0's step 0 multiplies the zero P^T operands of "stage -1" with
@@ -688,7 +688,7 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
 
     // ---- step 0: MFMAs of own tile 1 and the shared tile | probabilities of own tile 0 ----
     if (partial) mask_scores<4>(sc0, kb_own, valid, g4);
-    O::template pv1<0>(vop, pbsh, o2);
+    if constexpr (SH) O::template pv1<0>(vop, pbsh, o2);
     {
       u32x4 pb[2] = {u32x4{pk1[0], pk1[1], pk1[2], pk1[3]}, u32x4{pk1[4], pk1[5], pk1[6], pk1[7]}};
       O::pv(vop, pb, o1);
@@ -699,7 +699,7 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
         O::colsum(ones, {u32x4{pk0[0], pk0[1], pk0[2], pk0[3]}, u32x4{pk0[4], pk0[5], pk0[6], pk0[7]}});
     // one MFMA, then two vector instructions, while both last
 #pragma unroll
-    for (int i = 0; i < 20; ++i) {
+    for (int i = 0; i < (SH ? 20 : 16); ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
     }
@@ -723,7 +723,7 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
 
     // ---- step 1: QK of the shared tile, P.V of own tile 0 | probabilities of own tile 1 ----
     if (partial) mask_scores<4>(sc1, kb_own, valid, g4);
-    O::qk1(ksh, q2, sc2);
+    if constexpr (SH) O::qk1(ksh, q2, sc2);
     // own tile 0: check its stage sum before its P.V
     float lt = cs0[0];
     if (fresh0 || __builtin_amdgcn_ballot_w64(lt > LAZY_COL_LIMIT))
@@ -741,33 +741,40 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
     }
-    read_ksh(s + 1, ksh);
+    if constexpr (SH) read_ksh(s + 1, ksh);
 
     // ---- step 2: QK of own tile 0 for stage s+1 | probabilities of the shared tile ----
-    if (partial) mask_scores<1>(sc2, kb_sh, valid, g4);
-    O::qk(kop, q0, sc0);
-    float lt2 = probs<1, E>(sc2, sl, nref2, pk2);
-#pragma unroll
-    for (int i = 0; i < 7; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+    if constexpr (SH) {
+      if (partial) mask_scores<1>(sc2, kb_sh, valid, g4);
     }
-    // keep the shared tile's probabilities here, beside the MFMAs above,
-    // rather than sunk past the branch below
-    asm volatile("" : "+v"(lt2));
+    O::qk(kop, q0, sc0);
+    float lt2 = 0.f;
+    if constexpr (SH) {
+      lt2 = probs<1, E>(sc2, sl, nref2, pk2);
+#pragma unroll
+      for (int i = 0; i < 7; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+      }
+      // keep the shared tile's probabilities here, beside the MFMAs above,
+      // rather than sunk past the branch below
+      asm volatile("" : "+v"(lt2));
+    }
     // own tile 1: check its stage sum (its P.V follows in the next step 0)
     lt = cs1[0];
     if (fresh1 || __builtin_amdgcn_ballot_w64(lt > LAZY_COL_LIMIT))
       lt = lane_swap_sum(renorm<4, DB, E>(sc1, sl, fresh1, ref1, nref1, l1, o1, pk1));
     l1 += lt;
-    if (fresh2 || __builtin_amdgcn_ballot_w64(lt2 > LAZY_SUM_LIMIT))
-      lt2 = renorm<1, DB, E>(sc2, sl, fresh2, ref2, nref2, l2, o2, pk2);
-    l2 += lt2;
-    // P^T of the shared block: its 4 slots sit at positions 4*half..4*half+3
-    // of the pair's operand; the other half is zero
-    pbsh = shTT ? u32x4{0u, 0u, pk2[0], pk2[1]} : u32x4{pk2[0], pk2[1], 0u, 0u};
+    if constexpr (SH) {
+      if (fresh2 || __builtin_amdgcn_ballot_w64(lt2 > LAZY_SUM_LIMIT))
+        lt2 = renorm<1, DB, E>(sc2, sl, fresh2, ref2, nref2, l2, o2, pk2);
+      l2 += lt2;
+      // P^T of the shared block: its 4 slots sit at positions 4*half..4*half+3
+      // of the pair's operand; the other half is zero
+      pbsh = shTT ? u32x4{0u, 0u, pk2[0], pk2[1]} : u32x4{pk2[0], pk2[1], 0u, 0u};
+    }
   }
-  O::template pv1<0>(vop, pbsh, o2);
+  if constexpr (SH) O::template pv1<0>(vop, pbsh, o2);
   {
     u32x4 pb[2] = {u32x4{pk1[0], pk1[1], pk1[2], pk1[3]}, u32x4{pk1[4], pk1[5], pk1[6], pk1[7]}};
     O::pv(vop, pb, o1);
@@ -952,22 +959,27 @@ int launch_append(const AppendParams& p, void* s) {
 }
 
 // Instantiations by (D, element type).
-template <int E>
-static int launch_attention_e(const AttnParams& p, int32_t grid, hipStream_t hs) {
+template <int E, bool SH>
+static int launch_attention_es(const AttnParams& p, int32_t grid, hipStream_t hs) {
   switch (p.head_dim) {
     case 32:
-      hipLaunchKernelGGL((attn_kernel<32, E>), dim3(grid), dim3(256), 0, hs, p);
+      hipLaunchKernelGGL((attn_kernel<32, E, SH>), dim3(grid), dim3(256), 0, hs, p);
       break;
     case 64:
-      hipLaunchKernelGGL((attn_kernel<64, E>), dim3(grid), dim3(256), 0, hs, p);
+      hipLaunchKernelGGL((attn_kernel<64, E, SH>), dim3(grid), dim3(256), 0, hs, p);
       break;
     case 128:
-      hipLaunchKernelGGL((attn_kernel<128, E>), dim3(grid), dim3(256), 0, hs, p);
+      hipLaunchKernelGGL((attn_kernel<128, E, SH>), dim3(grid), dim3(256), 0, hs, p);
       break;
     default:
       return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();
+}
+
+template <int E>
+static int launch_attention_e(const AttnParams& p, int32_t grid, hipStream_t hs) {
+  return p.shared_tile ? launch_attention_es<E, true>(p, grid, hs) : launch_attention_es<E, false>(p, grid, hs);
 }
 
 int launch_attention(const AttnParams& p, int32_t grid, void* s) {

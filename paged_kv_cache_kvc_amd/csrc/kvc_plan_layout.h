@@ -49,7 +49,7 @@
 #define KVC_HDR_NUM_ROWS 2
 #define KVC_HDR_ANY_SPLIT 3
 #define KVC_HDR_NUM_TILES 4
-#define KVC_HDR_UNUSED 5
+#define KVC_HDR_SHARED_TILE 5  // 1: query groups of up to 9 tiles (a shared ninth); 0: up to 8
 #define KVC_HDR_MERGE_TABLE 6  // offset in ints of the merge order
 #define KVC_HDR_MERGE_SLOTS 7  // merge slots per XCD (the merge grid is 8 times this)
 // XCDs of the device; work-groups are dispatched to them round-robin.
@@ -77,13 +77,11 @@ typedef struct kvc_dev_stream {
 } kvc_dev_stream;
 
 // Query tiles (of KVC_Q_TILE rows) one wave owns.  A query group spans at
-// most KVC_ATTN_WAVES * this many tiles plus one tile shared by all waves.
-static inline int kvc_tiles_per_wave(int head_dim) {
-  (void)head_dim;
-  return 2;
-}
-static inline int kvc_group_tiles(int head_dim) {
-  return KVC_ATTN_WAVES * kvc_tiles_per_wave(head_dim) + 1;
+// most KVC_ATTN_WAVES * this many tiles, plus one tile shared by all waves
+// when the launch uses shared tiles.
+#define KVC_TILES_PER_WAVE 2
+static inline int kvc_group_tiles(int shared_tile) {
+  return KVC_ATTN_WAVES * KVC_TILES_PER_WAVE + (shared_tile ? 1 : 0);
 }
 
 #endif

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, n), n
         assert n in kvc.SIGNATURES, n
     assert set(kvc.SIGNATURES) == set(names)
-    assert lib.kvc_abi_version() == kvc.ABI_VERSION == 3
+    assert lib.kvc_abi_version() == kvc.ABI_VERSION == 4
 
 
 def cfg_of(wl: syn.Workload):
@@ -265,13 +265,7 @@ def test_split_policy_options():
     assert c.get_option(kvc.KVC_OPT_MAX_SPLITS) == 1
 
 
-@pytest.mark.parametrize("name", ["base", "r518", "frag"])
-def test_split_counts_fill_one_round(name):
-    """The planner's split counts keep every attention work-group of a run
-    resident at once (at most the target count, which defaults to what the
-    device holds: 2 per CU up to D = 64, 1 at D = 128), and the stream with
-    the longest splits, which sets the launch's length, could not take one
-    more split that shortens them and still fit."""
+def _plan_at_measured_step(name):
     wl = syn.WORKLOADS[name]
     c = kvc.PagedKVCache(cfg_of(wl), metadata_only=True)
     F = max(wl.frames)
@@ -283,12 +277,13 @@ def test_split_counts_fill_one_round(name):
         for s in act:
             c.evict_frames(stream_id=s)
         c.plan()
-    p = c.get_plan()
-    target = c.get_option(kvc.KVC_OPT_TARGET_WORKGROUPS)
-    assert target == (2 if wl.head_dim <= 64 else 1) * 256   # the CU count a metadata-only context assumes
+    return wl, c
+
+
+def _units_and_qtiles(wl, p):
     P = wl.tokens_per_frame - wl.num_special_tokens
     ceil = lambda a, b: -(-a // b)
-    units, groups = [], []
+    units, qtiles = [], []
     for i in range(len(p["planned"])):
         n_pages = int(p["kv_indptr"][i + 1] - p["kv_indptr"][i])
         n_patch = int(p["n_patch_pages"][i])
@@ -297,16 +292,47 @@ def test_split_counts_fill_one_round(name):
         if n_sp:
             u += (n_sp - 1) * ceil(wl.page_size, 64) + ceil(int(p["last_page_len"][i]), 64)
         units.append(u)
-        rows = int(p["qo_indptr"][i + 1] - p["qo_indptr"][i])
-        groups.append(wl.num_heads * ceil(ceil(rows, 16), 9))
+        qtiles.append(ceil(int(p["qo_indptr"][i + 1] - p["qo_indptr"][i]), 16))
+    return units, qtiles
+
+
+@pytest.mark.parametrize("name", ["base", "r518", "frag"])
+def test_split_counts_fill_one_round(name):
+    """The planner's split counts keep every attention work-group of a run
+    resident at once (at most the target count, which defaults to what the
+    device holds: 2 per CU up to D = 64, 1 at D = 128), and the stream with
+    the longest splits, which sets the launch's length, could not take one
+    more split that shortens them and still fit."""
+    wl, c = _plan_at_measured_step(name)
+    p = c.get_plan()
+    shape = c.get_plan_shape()
+    target = c.get_option(kvc.KVC_OPT_TARGET_WORKGROUPS)
+    assert target == (2 if wl.head_dim <= 64 else 1) * 256   # the CU count a metadata-only context assumes
+    ceil = lambda a, b: -(-a // b)
+    units, qtiles = _units_and_qtiles(wl, p)
+    groups = [wl.num_heads * ceil(q, shape["group_tiles"]) for q in qtiles]
     ns = [int(x) for x in p["n_splits"]]
     items = sum(g * n for g, n in zip(groups, ns))
-    assert items <= target
+    assert items == shape["work_items"] <= target
     lens = [ceil(u, n) for u, n in zip(units, ns)]
     i = lens.index(max(lens))
     u, g, n = units[i], groups[i], ns[i]
     if n < min(kvc.MAX_SPLITS, u) and ceil(u, n + 1) < ceil(u, n):
         assert items + g > target, (name, i, ns)
+
+
+def test_query_grouping_choice():
+    """Groups of 9 query tiles (the ninth shared by the four waves, a quarter
+    tile more per wave and stage) against groups of 8: the 262-query frame
+    (17 tiles) keeps the shared tile, the 1005-query frame of the 999-patch
+    workload (63 tiles) takes groups of 8, which fill all 512 work-groups with
+    4 splits instead of 448 and drop the quarter tile."""
+    _, c = _plan_at_measured_step("base")
+    assert c.get_plan_shape() == {"work_items": 512, "group_tiles": 9}
+    assert list(c.get_plan()["n_splits"]) == [16]
+    _, c = _plan_at_measured_step("r518")
+    assert c.get_plan_shape() == {"work_items": 512, "group_tiles": 8}
+    assert list(c.get_plan()["n_splits"]) == [4]
 
 
 def test_scale_phase_multi_frame_steps_match_oracle():
