@@ -287,6 +287,13 @@ kvc_status kvc_get_plan(const kvc_ctx* ctx, int32_t* planned_streams, int32_t* k
  * Either pointer may be NULL.  Errors: KVC_ERR_ARG, KVC_ERR_STATE (no plan). */
 kvc_status kvc_get_plan_shape(const kvc_ctx* ctx, int32_t* work_items, int32_t* group_tiles);
 
+/* Copy the current plan's device image (the int32 buffer that kvc_plan
+ * uploads and the kernels read; layout in kvc_plan_layout.h of the sources)
+ * to buf, for host-side checks.  capacity: ints available in buf (buf may be
+ * NULL to query the size); n_ints receives the image's size.
+ * Errors: KVC_ERR_ARG (capacity short), KVC_ERR_STATE (no plan). */
+kvc_status kvc_get_plan_image(const kvc_ctx* ctx, int32_t* buf, int32_t capacity, int32_t* n_ints);
+
 /* [p3] §Inspecting Cache Statistics for one stream. */
 kvc_status kvc_get_stats(const kvc_ctx* ctx, int32_t stream, kvc_stats* out);
 

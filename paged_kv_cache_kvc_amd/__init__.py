@@ -89,6 +89,7 @@ SIGNATURES = {
     "kvc_run": (_I32, [_P, _I32, _P, _P, _P]),
     "kvc_get_plan": (_I32, [_P, _PI32, _PI32, _PI32, _PI32, _PI32, _PI32, _PI32, _I32, _I32, _PI32, _PI32]),
     "kvc_get_plan_shape": (_I32, [_P, _PI32, _PI32]),
+    "kvc_get_plan_image": (_I32, [_P, _PI32, _I32, _PI32]),
     "kvc_get_stats": (_I32, [_P, _I32, ctypes.POINTER(KvcStats)]),
     "kvc_set_option": (_I32, [_P, _I32, ctypes.c_int64]),
     "kvc_get_option": (_I32, [_P, _I32, ctypes.POINTER(ctypes.c_int64)]),
@@ -320,6 +321,15 @@ class PagedKVCache:
         self._check(self.lib.kvc_get_plan_shape(self._ctx, ctypes.byref(items), ctypes.byref(tiles)),
                     "get_plan_shape")
         return {"work_items": items.value, "group_tiles": tiles.value}
+
+    def get_plan_image(self) -> np.ndarray:
+        """The int32 plan image that kvc_plan uploads for the kernels."""
+        n = ctypes.c_int32()
+        self._check(self.lib.kvc_get_plan_image(self._ctx, None, 0, ctypes.byref(n)), "get_plan_image")
+        buf = np.zeros(max(n.value, 1), np.int32)
+        self._check(self.lib.kvc_get_plan_image(self._ctx, buf.ctypes.data_as(_PI32), buf.size, ctypes.byref(n)),
+                    "get_plan_image")
+        return buf[:n.value]
 
     def set_option(self, option: int, value: int):
         self._check(self.lib.kvc_set_option(self._ctx, option, value), "set_option")

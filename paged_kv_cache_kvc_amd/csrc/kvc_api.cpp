@@ -508,6 +508,19 @@ kvc_status kvc_get_plan_shape(const kvc_ctx* c, int32_t* work_items, int32_t* gr
   return KVC_OK;
 }
 
+kvc_status kvc_get_plan_image(const kvc_ctx* c, int32_t* buf, int32_t capacity, int32_t* n_ints) {
+  if (!c) return KVC_ERR_ARG;
+  kvc_ctx* m = const_cast<kvc_ctx*>(c);
+  if (!c->have_plan) return fail(m, KVC_ERR_STATE, "no plan");
+  const int32_t n = (int32_t)c->plan.image.size();
+  if (n_ints) *n_ints = n;
+  if (buf) {
+    if (capacity < n) return fail(m, KVC_ERR_ARG, "capacity too small");
+    std::copy(c->plan.image.begin(), c->plan.image.end(), buf);
+  }
+  return KVC_OK;
+}
+
 kvc_status kvc_get_stats(const kvc_ctx* c, int32_t stream, kvc_stats* out) {
   if (!c || !out) return KVC_ERR_ARG;
   if (stream < 0 || stream >= c->cfg.num_streams) return KVC_ERR_ARG;

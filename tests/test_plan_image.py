@@ -1,0 +1,194 @@
+"""Host-side checks of the device plan image: the int32 buffer that kvc_plan
+uploads and the attention and merge kernels read without checks of their own
+(the layout of paged_kv_cache_kvc_amd/csrc/kvc_plan_layout.h, restated here).
+
+Each plan is decoded independently of the planner and checked against the
+public plan (page tables, last-page lengths, query rows) and the pool
+geometry: every work unit lies inside one visible page of its own stream, in
+table order, within that page's valid slots, and the units add up to the
+visible length; the splits of every work item tile the units; the merge order
+lists each (query tile, head) of a split stream exactly once, on the XCD of
+its middle split, with the tile's split count and output rows."""
+import math
+
+import numpy as np
+import pytest
+
+import kvc_synth as syn
+import paged_kv_cache_kvc_amd as kvc
+from tests.stream_harness import edge_workloads
+from tests.test_host_abi import cfg_of, free_orders
+
+HEADER, REC, UNIT, MERGE, KV_TILE, Q_TILE, XCD, WAVES = 8, 16, 4, 4, 64, 16, 8, 4
+REC_FIELDS = ("q_row0", "n_q", "page0", "n_patch", "n_pages", "last_len", "kv_len", "unit0", "n_units",
+              "n_split", "n_group", "item0", "n_items", "upp", "ups", "q_tile0")
+
+
+def check_image(wl, c):
+    img = c.get_plan_image().astype(np.int64)
+    plan = c.get_plan()
+    shape = c.get_plan_shape()
+    H, D, pg = wl.num_heads, wl.head_dim, wl.page_size
+    P = wl.tokens_per_frame - wl.num_special_tokens
+    slot_bytes = H * D * 2
+    page_bytes = 2 * pg * slot_bytes
+    n_streams, n_items, n_rows, any_split, n_tiles, shared, merge_at, merge_slots = (int(x) for x in img[:HEADER])
+    n = len(plan["planned"])
+    assert n_streams == n
+    assert shared == (1 if shape["group_tiles"] == 9 else 0)
+    assert n_items == shape["work_items"]
+    assert n_rows == plan["qo_indptr"][-1]
+    recs = [dict(zip(REC_FIELDS, (int(x) for x in img[HEADER + REC * i: HEADER + REC * (i + 1)]))) for i in range(n)]
+    tables_at = HEADER + REC * n
+    assert np.array_equal(img[tables_at: tables_at + len(plan["kv_indices"])], plan["kv_indices"])
+    item = tiles = 0
+    split_streams = set()
+    for i, r in enumerate(recs):
+        assert r["q_row0"] == plan["qo_indptr"][i] and r["n_q"] == plan["qo_indptr"][i + 1] - plan["qo_indptr"][i]
+        assert r["page0"] == plan["kv_indptr"][i]
+        assert r["n_pages"] == plan["kv_indptr"][i + 1] - plan["kv_indptr"][i]
+        assert r["n_patch"] == plan["n_patch_pages"][i] and r["last_len"] == plan["last_page_len"][i]
+        assert r["n_split"] == plan["n_splits"][i]
+        # units: in table order, page by page, 64-slot chunks of each page's valid slots
+        pages = plan["kv_indices"][r["page0"]: r["page0"] + r["n_pages"]]
+        expect = []
+        for pi, page in enumerate(pages):
+            length = r["last_len"] if pi == r["n_pages"] - 1 else (P if pi < r["n_patch"] else pg)
+            expect += [(int(page), s0, min(KV_TILE, length - s0)) for s0 in range(0, length, KV_TILE)]
+        assert r["n_units"] == len(expect) >= 1
+        assert r["unit0"] % 4 == 0
+        got = []
+        for u in range(r["n_units"]):
+            lo, hi, valid, pad = (int(x) for x in img[r["unit0"] + UNIT * u: r["unit0"] + UNIT * (u + 1)])
+            off = (lo & 0xFFFFFFFF) | (hi << 32)
+            page, rem = divmod(off, page_bytes)
+            slot, byte = divmod(rem, slot_bytes)
+            assert byte == 0 and slot < pg and pad == 0     # a K row of head 0, V at + pg rows
+            got.append((page, slot, valid))
+        assert got == expect
+        assert sum(v for _, _, v in got) == r["kv_len"]
+        # work items: heads x splits x query groups, every split non-empty
+        nqt = math.ceil(r["n_q"] / Q_TILE)
+        assert r["n_group"] == math.ceil(nqt / shape["group_tiles"])
+        assert all((g + 1) * nqt // r["n_group"] - g * nqt // r["n_group"] <= shape["group_tiles"]
+                   for g in range(r["n_group"]))
+        assert 1 <= r["n_split"] <= min(kvc.MAX_SPLITS, r["n_units"])
+        bounds = [s * r["n_units"] // r["n_split"] for s in range(r["n_split"] + 1)]
+        assert all(b1 > b0 for b0, b1 in zip(bounds, bounds[1:])) and bounds[-1] == r["n_units"]
+        assert r["item0"] == item and r["n_items"] == H * r["n_split"] * r["n_group"]
+        assert r["q_tile0"] == tiles
+        item += r["n_items"]
+        tiles += nqt
+        if r["n_split"] > 1:
+            split_streams.add(i)
+    assert item == n_items and tiles == n_tiles and any_split == (1 if split_streams else 0)
+    # merge order
+    assert merge_at % 4 == 0 and len(img) == merge_at + MERGE * XCD * merge_slots
+    ipx = -(-n_items // XCD)
+    seen = {}
+    for x in range(XCD):
+        for k in range(merge_slots):
+            e = [int(v) for v in img[merge_at + MERGE * (x * merge_slots + k): merge_at + MERGE * (x * merge_slots + k + 1)]]
+            if e[0] < 0:
+                continue
+            assert e[0] not in seen
+            seen[e[0]] = (x, e[1:])
+    want = {}
+    for i in split_streams:
+        r = recs[i]
+        nqt = math.ceil(r["n_q"] / Q_TILE)
+        for t in range(nqt):
+            grp = next(g for g in range(r["n_group"]) if t < (g + 1) * nqt // r["n_group"])
+            for h in range(H):
+                mid = r["item0"] + (h * r["n_split"] + r["n_split"] // 2) * r["n_group"] + grp
+                want[(r["q_tile0"] + t) * H + h] = (min(mid // max(1, ipx), XCD - 1),
+                                                    [r["n_split"], r["q_row0"] + Q_TILE * t,
+                                                     min(Q_TILE, r["n_q"] - Q_TILE * t)])
+    assert seen == want
+
+
+def stream_and_check(wl, steps_to_check, nframes=None):
+    fp, fs = free_orders(wl)
+    c = kvc.PagedKVCache(cfg_of(wl), metadata_only=True, free_patch_order=fp, free_special_order=fs) \
+        if fp is not None else kvc.PagedKVCache(cfg_of(wl), metadata_only=True)
+    F = max(wl.frames)
+    starts = [F - f for f in wl.frames]
+    for t in range(F):
+        act = [s for s in range(len(wl.frames)) if t >= starts[s]]
+        for s in act:
+            c.append_frame(0, stream_id=s)
+        for s in act:
+            c.evict_frames(stream_id=s)
+        c.plan()
+        if t in steps_to_check or t == F - 1:
+            check_image(wl, c)
+    return c
+
+
+@pytest.mark.parametrize("name", ["tiny", "base", "r518", "frag"])
+def test_plan_image_workloads(name):
+    wl = syn.WORKLOADS[name]
+    F = max(wl.frames)
+    stream_and_check(wl, set(range(F)) if name == "tiny" else {0, 1, wl.scale_frames, F // 2})
+
+
+def test_plan_image_long_stream_tail():
+    """10 000 frames: 235 special pages, the split bounds over 1228 units."""
+    stream_and_check(syn.WORKLOADS["long"], {9998})
+
+
+@pytest.mark.parametrize("name", sorted(edge_workloads()))
+def test_plan_image_degenerate_shapes(name):
+    wl = edge_workloads()[name]
+    cfg = kvc.make_config(wl.num_blocks, wl.num_heads, wl.head_dim, wl.tokens_per_frame, wl.num_special_tokens,
+                          page_size=wl.page_size, scale_frames=wl.scale_frames, sliding_window=wl.sliding_window,
+                          num_streams=wl.num_streams, max_patch_pages=wl.max_patch_pages,
+                          max_special_pages=wl.max_special_pages, special_row_offset=wl.row_offset,
+                          max_frames_per_step=64)
+    c = kvc.PagedKVCache(cfg, metadata_only=True)
+    done, first = 0, True
+    while done < max(wl.frames):
+        nf = min(64 if (first and name == "steps_of_64") else 1, max(wl.frames) - done)
+        if nf > 1:
+            c.append_frames(0, num_frames=nf)
+        else:
+            c.append_frame(0)
+        c.evict_frames()
+        c.plan()
+        check_image(wl, c)
+        done += nf
+        first = False
+
+
+def test_plan_image_check_catches_corruption():
+    """The decoder above rejects a corrupted image: a unit moved by one slot,
+    a valid count off by one, a work-item range shifted, a merge entry's
+    rows or split count changed, a tile missing from the merge order."""
+    wl = syn.WORKLOADS["tiny"]
+    c = stream_and_check(wl, set())
+    good = c.get_plan_image()
+    plan = c.get_plan()
+    n = len(plan["planned"])
+    rec0 = HEADER
+    unit0 = int(good[rec0 + REC_FIELDS.index("unit0")])
+    merge_at, merge_slots = int(good[6]), int(good[7])
+    first_merge = next(merge_at + MERGE * k for k in range(XCD * merge_slots) if good[merge_at + MERGE * k] >= 0)
+    slot_bytes = wl.num_heads * wl.head_dim * 2
+
+    def corrupt(i, delta):
+        bad = good.copy()
+        bad[i] += delta
+        return bad
+
+    cases = [corrupt(unit0, slot_bytes), corrupt(unit0 + 2, -1), corrupt(rec0 + REC_FIELDS.index("item0"), 1),
+             corrupt(first_merge + 1, 1), corrupt(first_merge + 2, 16)]
+    missing = good.copy()
+    missing[first_merge] = -1
+    cases.append(missing)
+    assert n == 1 and plan["n_splits"][0] > 1
+    for bad in cases:
+        c.get_plan_image = lambda bad=bad: bad
+        with pytest.raises(AssertionError):
+            check_image(wl, c)
+    c.get_plan_image = lambda: good
+    check_image(wl, c)
