@@ -446,8 +446,6 @@ kvc_status kvc_run(kvc_ctx* c, int32_t block, const void* q, void* o, kvc_stream
   a.page_size = cf.page_size;
   a.patch_tokens = cf.patch_tokens();
   a.tiles_cap = cf.tiles_capacity();
-  a.div_patch = kvc::make_fastdiv((uint32_t)std::max(1, cf.patch_tokens()));
-  a.div_page = kvc::make_fastdiv((uint32_t)cf.page_size);
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)cf.head_dim));
   a.num_items = c->plan.num_items;
   a.dtype = cf.dtype;

@@ -8,14 +8,6 @@
 
 namespace kvc {
 
-// Exact unsigned division n / d for 0 <= n < 2^31 by a multiply-high:
-// q = (umulhi(n, mul) + n) >> shr, with shr = ceil(log2 d) and
-// mul = ceil(2^(32+shr) / d) - 2^32.
-struct FastDiv {
-  uint32_t div, mul, shr;
-};
-FastDiv make_fastdiv(uint32_t d);
-
 struct AppendParams {
   void* pool;               // this block's pool
   const void* k;            // [T, H, D] bf16
@@ -38,7 +30,6 @@ struct AttnParams {
   void* part_o;
   float* part_lse;
   int32_t num_heads, head_dim, page_size, patch_tokens, tiles_cap;
-  FastDiv div_patch, div_page;
   float scale_log2;         // log2(e) / sqrt(D)
   int32_t num_items, items_per_xcd;
   int32_t shared_tile;      // 1: query groups of up to 9 tiles, the ninth shared by the waves; 0: up to 8

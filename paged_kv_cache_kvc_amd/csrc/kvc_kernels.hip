@@ -34,17 +34,6 @@
 
 namespace kvc {
 
-FastDiv make_fastdiv(uint32_t d) {
-  FastDiv f;
-  f.div = d;
-  uint32_t s = 0;
-  while ((1ull << s) < d) ++s;
-  f.shr = s;
-  const uint64_t m = ((1ull << (32 + s)) + d - 1) / d;
-  f.mul = (uint32_t)(m - (1ull << 32));
-  return f;
-}
-
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -119,10 +108,6 @@ struct El<1> {
     return f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
   }
 };
-
-__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
-  return (__umulhi(n, f.mul) + n) >> f.shr;
-}
 
 // ---------------------------------------------------------------------------
 // append
@@ -238,7 +223,6 @@ __device__ __forceinline__ void load_lds16(const void* base, uint32_t offset, ui
 // compiler's own max so that its hazard tracking sees the MFMA results these
 // read (an opaque instruction reading an MFMA accumulator too early would see
 // a partially written register).
-__device__ __forceinline__ float max3(float a, float b, float c) { return __builtin_fmaxf(__builtin_fmaxf(a, b), c); }
 __device__ __forceinline__ float max2(float a, float b) { return __builtin_fmaxf(a, b); }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* generic) {
