@@ -112,6 +112,8 @@ def test_base_full_size_parity_and_pool():
             for b in (0, 1):
                 st = check_close(res["out_bits"][b], res["ref"][b])
             log(f"base step {t}: splits {res['gpu_plan']['n_splits']} {st}")
+    # the launch timed by bench.py: query groups of 9 tiles, the ninth shared
+    assert h.gpu.get_plan_shape() == {"work_items": 512, "group_tiles": 9}
     for b in (0, 1):
         assert np.array_equal(h.pool_bits(b), h.ora.pools[b].data)
     # deterministic: same inputs, same bits
@@ -153,6 +155,8 @@ def test_r518_padded_pages_and_poisoned_slots():
             compare_plan(res)
             st = check_close(res["out_bits"][0], res["ref"][0])
             log(f"r518 step {t}: splits {res['gpu_plan']['n_splits']} {st}")
+    # the full-size step runs the kernel without a shared tile (groups of 8)
+    assert h.gpu.get_plan_shape() == {"work_items": 512, "group_tiles": 8}
     before = res["out_bits"][0]
     plan = res["gpu_plan"]
     pool = h.gpu.pools[0]
