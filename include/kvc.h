@@ -79,7 +79,8 @@ enum {
   KVC_ERR_POOL_EXHAUSTED = -3,  /* no free patch page, or the special pool is full ([p2] §Patch Stream and Special Stream) */
   KVC_ERR_CAPACITY = -4,        /* configuration cannot hold the steady state */
   KVC_ERR_HIP = -5,             /* a HIP runtime call failed */
-  KVC_ERR_UNSUPPORTED = -6      /* shape outside what the kernels are built for */
+  KVC_ERR_UNSUPPORTED = -6,     /* shape outside what the kernels are built for */
+  KVC_ERR_HOST_ALLOC = -7       /* the library could not allocate host memory for a context */
 };
 
 /* Sizing and shape of one cache ([p2] §Initializing the Cache Manager;
@@ -173,7 +174,7 @@ size_t kvc_staging_bytes(const kvc_config* cfg);
  *   out:        receives the context.
  * Errors: KVC_ERR_ARG, KVC_ERR_CAPACITY (max_patch_pages too small),
  * KVC_ERR_UNSUPPORTED (head_dim, or a shape the kernels do not cover),
- * KVC_ERR_HIP. */
+ * KVC_ERR_HOST_ALLOC, KVC_ERR_HIP. */
 kvc_status kvc_create(const kvc_config* cfg, void* const* pools, void* workspace, void* staging,
                       const int32_t* free_patch_order, const int32_t* free_special_order,
                       kvc_ctx** out);
@@ -189,7 +190,9 @@ kvc_status kvc_destroy(kvc_ctx* ctx);
 
 /* [p5] §Resetting for New Sequences: clear page lists and counters and keep
  * the buffers (pool contents are left as they are; only valid visible slots
- * are ever read). */
+ * are ever read).  Every per-step state is cleared too: the step in progress
+ * is dropped, kvc_get_plan has no plan, and the next call must be a block-0
+ * append. */
 kvc_status kvc_reset(kvc_ctx* ctx);
 
 /* Write one frame's K and V for one block ([p5] §Frame Appending Without
@@ -249,7 +252,9 @@ kvc_status kvc_rollback(kvc_ctx* ctx, int32_t stream);
  * query row ranges and the split-KV work list; then one asynchronous copy of
  * the plan from pinned staging to the workspace on hip_stream.
  * Errors: KVC_ERR_STATE (no stream appended, or already planned this step),
- * KVC_ERR_HIP. */
+ * KVC_ERR_CAPACITY (a planned stream holds more than scale_frames +
+ * sliding_window patch pages, i.e. kvc_evict was skipped: the plan would not
+ * fit the plan buffer; nothing changes), KVC_ERR_HIP. */
 kvc_status kvc_plan(kvc_ctx* ctx, kvc_stream_t hip_stream);
 
 /* Paged attention for one block with the step's plan ([p2] §Attention Kernel

@@ -43,9 +43,9 @@ the design notes of the repository):
 
 Parity pins: every function here is pinned by the CPU tests (worked example of
 [p3] §Inspecting Cache Statistics, closed forms, invariants, PyTorch's
-scaled_dot_product_attention as a second routine, brute force on tiny inputs,
-paged-vs-dense identity and page-ID permutation invariance).  No function is
-parity unpinned.
+scaled_dot_product_attention and logsumexp as second routines, brute force on
+tiny inputs, the split-KV merge identity, paged-vs-dense identity and page-ID
+permutation invariance), and planted mistakes in each are caught by some pin.
 """
 from __future__ import annotations
 
@@ -403,8 +403,12 @@ def attention_fp64(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray, d
 
 
 def lse_base2_fp64(q_bits: np.ndarray, k_bits: np.ndarray, dtype: str = "bf16") -> np.ndarray:
-    """log2 of sum_j exp(q.k_j / sqrt(D)) per query row and head, [T, H]; used
-    to check split-KV partial results."""
+    """log2 of sum_j exp(q.k_j / sqrt(D)) per query row and head, [T, H]: the
+    normaliser of the softmax over the given keys, in base 2.  Attention over
+    chunks of the keys, each weighted by 2^(lse_chunk - lse_all), sums to the
+    attention over all of them, which is what a split-KV partial result must
+    carry ([p5] §Kernel Dispatch and Sequence Lengths: exact weights over the
+    valid tokens, whatever the split)."""
     q = bits_to_f32(q_bits, dtype).astype(np.float64)
     k = bits_to_f32(k_bits, dtype).astype(np.float64)
     T, H, D = q.shape

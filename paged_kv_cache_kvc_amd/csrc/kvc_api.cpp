@@ -143,6 +143,7 @@ const char* kvc_status_string(kvc_status s) {
     case KVC_ERR_CAPACITY: return "capacity too small";
     case KVC_ERR_HIP: return "HIP runtime error";
     case KVC_ERR_UNSUPPORTED: return "unsupported shape";
+    case KVC_ERR_HOST_ALLOC: return "host memory allocation failed";
     default: return "unknown status";
   }
 }
@@ -174,8 +175,23 @@ static int32_t resident_workgroups(const kvc::Config& c, int cu_count) {
   return (c.head_dim <= 64 ? 2 : 1) * cu_count;
 }
 
+static kvc_status create_common_impl(const kvc_config* cfg, const int32_t* fpo, const int32_t* fso, kvc_ctx** out,
+                                     kvc_ctx** made);
+
+// Host allocations (page lists, plan vectors) can throw std::bad_alloc; no
+// exception may cross the C ABI, so the entry points that allocate turn it
+// into KVC_ERR_HOST_ALLOC.
 static kvc_status create_common(const kvc_config* cfg, const int32_t* fpo, const int32_t* fso, kvc_ctx** out,
                                 kvc_ctx** made) {
+  try {
+    return create_common_impl(cfg, fpo, fso, out, made);
+  } catch (const std::bad_alloc&) {
+    return KVC_ERR_HOST_ALLOC;
+  }
+}
+
+static kvc_status create_common_impl(const kvc_config* cfg, const int32_t* fpo, const int32_t* fso, kvc_ctx** out,
+                                     kvc_ctx** made) {
   if (!cfg || !out) return KVC_ERR_ARG;
   *out = nullptr;
   kvc::Config c = to_cfg(*cfg);
@@ -183,22 +199,27 @@ static kvc_status create_common(const kvc_config* cfg, const int32_t* fpo, const
   const int v = kvc::validate(c, &why);
   if (v != kvc::OK) return (kvc_status)v;
   kvc_ctx* x = new (std::nothrow) kvc_ctx();
-  if (!x) return KVC_ERR_ARG;
-  x->cfg = c;
-  std::vector<int32_t> fp, fs;
-  if (fpo) fp.assign(fpo, fpo + c.max_patch_pages);
-  if (fso) fs.assign(fso, fso + c.max_special_pages);
-  if (fso && c.max_special_pages == 0) fs.clear();
-  const int rc = x->alloc.init(c, fp, fs, &why);
-  if (rc != kvc::OK) {
+  if (!x) return KVC_ERR_HOST_ALLOC;
+  try {
+    x->cfg = c;
+    std::vector<int32_t> fp, fs;
+    if (fpo) fp.assign(fpo, fpo + c.max_patch_pages);
+    if (fso) fs.assign(fso, fso + c.max_special_pages);
+    if (fso && c.max_special_pages == 0) fs.clear();
+    const int rc = x->alloc.init(c, fp, fs, &why);
+    if (rc != kvc::OK) {
+      delete x;
+      return (kvc_status)rc;
+    }
+    x->advanced.assign(c.num_streams, 0);
+    x->block_done.assign((size_t)c.num_streams * c.num_blocks, 0);
+    x->slots.assign((size_t)c.num_streams * c.max_frames_per_step, kvc::FrameSlots());
+    x->nframes.assign(c.num_streams, 0);
+    x->lay = layout_of(c);
+  } catch (const std::bad_alloc&) {
     delete x;
-    return (kvc_status)rc;
+    return KVC_ERR_HOST_ALLOC;
   }
-  x->advanced.assign(c.num_streams, 0);
-  x->block_done.assign((size_t)c.num_streams * c.num_blocks, 0);
-  x->slots.assign((size_t)c.num_streams * c.max_frames_per_step, kvc::FrameSlots());
-  x->nframes.assign(c.num_streams, 0);
-  x->lay = layout_of(c);
   *made = x;
   return KVC_OK;
 }
@@ -276,17 +297,34 @@ kvc_status kvc_destroy(kvc_ctx* c) {
 kvc_status kvc_reset(kvc_ctx* c) {
   if (!c) return KVC_ERR_ARG;
   c->alloc.reset();
+  // every per-step field: the next call must be a block-0 append
   c->planned = false;
   c->have_plan = false;
+  c->plan_stale = false;
   std::fill(c->advanced.begin(), c->advanced.end(), 0);
   std::fill(c->block_done.begin(), c->block_done.end(), 0);
+  std::fill(c->nframes.begin(), c->nframes.end(), 0);
+  std::fill(c->slots.begin(), c->slots.end(), kvc::FrameSlots());
+  c->plan = kvc::HostPlan();
   c->err.clear();
   return KVC_OK;
 }
 
+static kvc_status append_frames_impl(kvc_ctx* c, int32_t stream, int32_t block, const void* k, const void* v,
+                                     int32_t num_frames, kvc_stream_t hs);
+
 kvc_status kvc_append_frames(kvc_ctx* c, int32_t stream, int32_t block, const void* k, const void* v,
                              int32_t num_frames, kvc_stream_t hs) {
   if (!c) return KVC_ERR_ARG;
+  try {
+    return append_frames_impl(c, stream, block, k, v, num_frames, hs);
+  } catch (const std::bad_alloc&) {
+    return fail(c, KVC_ERR_HOST_ALLOC, "host allocation failed");
+  }
+}
+
+static kvc_status append_frames_impl(kvc_ctx* c, int32_t stream, int32_t block, const void* k, const void* v,
+                                     int32_t num_frames, kvc_stream_t hs) {
   const kvc::Config& cf = c->cfg;
   if (stream < 0 || stream >= cf.num_streams) return fail(c, KVC_ERR_ARG, "stream out of range");
   if (block < 0 || block >= cf.num_blocks) return fail(c, KVC_ERR_ARG, "block out of range");
@@ -382,8 +420,18 @@ kvc_status kvc_evict(kvc_ctx* c, int32_t stream) {
   return KVC_OK;
 }
 
+static kvc_status plan_impl(kvc_ctx* c, kvc_stream_t hs);
+
 kvc_status kvc_plan(kvc_ctx* c, kvc_stream_t hs) {
   if (!c) return KVC_ERR_ARG;
+  try {
+    return plan_impl(c, hs);
+  } catch (const std::bad_alloc&) {
+    return fail(c, KVC_ERR_HOST_ALLOC, "host allocation failed");
+  }
+}
+
+static kvc_status plan_impl(kvc_ctx* c, kvc_stream_t hs) {
   if (c->planned) return fail(c, KVC_ERR_STATE, "already planned this step");
   std::vector<int32_t> streams, frames;
   for (int s = 0; s < c->cfg.num_streams; ++s)
@@ -392,7 +440,17 @@ kvc_status kvc_plan(kvc_ctx* c, kvc_stream_t hs) {
       frames.push_back(c->nframes[s]);
     }
   if (streams.empty()) return fail(c, KVC_ERR_STATE, "no stream appended block 0 this step");
-  kvc::build_plan(c->alloc, streams, frames, c->policy, &c->plan);
+  kvc::HostPlan next;
+  kvc::build_plan(c->alloc, streams, frames, c->policy, &next);
+  // The device plan buffer (and its staging half) holds plan_image_ints ints,
+  // enough while every planned stream sees at most scale_frames +
+  // sliding_window patch pages.  A stream whose window was not evicted can
+  // exceed it; refuse such a plan rather than overrun the buffers.
+  if (next.image.size() > kvc::plan_image_ints(c->cfg))
+    return fail(c, KVC_ERR_CAPACITY,
+                "plan larger than the plan buffer: a planned stream holds more than scale_frames + "
+                "sliding_window patch pages (call kvc_evict before kvc_plan)");
+  c->plan = std::move(next);
   c->planned = true;
   c->plan_stale = false;
   c->have_plan = true;
@@ -404,6 +462,7 @@ kvc_status kvc_plan(kvc_ctx* c, kvc_stream_t hs) {
     if (e != hipSuccess) return hip_fail(c, e, "plan staging wait");
   }
   const size_t bytes = c->plan.image.size() * sizeof(int32_t);
+  if (bytes > c->lay.plan_bytes) return fail(c, KVC_ERR_CAPACITY, "plan image exceeds the plan buffer");
   char* host = c->staging + b * c->lay.plan_bytes;
   std::memcpy(host, c->plan.image.data(), bytes);
   char* dev = c->workspace + (b ? c->lay.plan1 : c->lay.plan0);

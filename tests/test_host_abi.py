@@ -231,6 +231,67 @@ def test_patch_pool_exhaustion_without_eviction():
     assert e.value.status == kvc.KVC_ERR_POOL_EXHAUSTED
 
 
+def test_plan_without_eviction_is_refused_not_overrun():
+    """A stream that keeps appending without kvc_evict holds more window pages
+    than the plan buffer is sized for (scale_frames + sliding_window per
+    stream).  kvc_plan must refuse that plan with KVC_ERR_CAPACITY before
+    anything is copied, and leave the step open; evicting then lets the same
+    step plan."""
+    wl = syn.WORKLOADS["base"]
+    cfg = kvc.make_config(1, wl.num_heads, wl.head_dim, wl.tokens_per_frame, wl.num_special_tokens,
+                          page_size=wl.page_size, scale_frames=wl.scale_frames, sliding_window=wl.sliding_window,
+                          max_patch_pages=4000, max_special_pages=60)
+    c = kvc.PagedKVCache(cfg, metadata_only=True)
+    refused = None
+    for f in range(2000):
+        c.append_frame(0)
+        try:
+            c.plan()
+        except kvc.KvcError as e:
+            assert e.status == kvc.KVC_ERR_CAPACITY
+            refused = f
+            break
+    assert refused is not None and refused > wl.scale_frames + wl.sliding_window
+    # the step is still open: evicting and planning it succeeds
+    with pytest.raises(kvc.KvcError) as e2:
+        c.append_frame(0)
+    assert e2.value.status == kvc.KVC_ERR_STATE
+    c.evict_frames()
+    c.plan()
+    p = c.get_plan()
+    assert p["n_patch_pages"][0] == wl.scale_frames + wl.sliding_window
+    img = c.get_plan_image()
+    assert img.size > 0
+
+
+def test_reset_clears_every_per_step_state():
+    """kvc_reset in the middle of a step drops the step: no plan is left, a
+    block-1 append or a plan is out of order, and a multi-frame count of the
+    dropped step does not constrain the next one."""
+    base = syn.WORKLOADS["base"]
+    cfg = kvc.make_config(2, 2, 32, base.tokens_per_frame, base.num_special_tokens, page_size=base.page_size,
+                          scale_frames=2, sliding_window=4, max_patch_pages=2 + 4 + 8, max_special_pages=8,
+                          max_frames_per_step=4)
+    c = kvc.PagedKVCache(cfg, metadata_only=True)
+    c.append_frames(0, num_frames=3)
+    c.reset()
+    with pytest.raises(kvc.KvcError) as e:
+        c.get_plan()
+    assert e.value.status == kvc.KVC_ERR_STATE
+    with pytest.raises(kvc.KvcError) as e:
+        c.append_frames(1, num_frames=3)
+    assert e.value.status == kvc.KVC_ERR_STATE
+    with pytest.raises(kvc.KvcError) as e:
+        c.plan()
+    assert e.value.status == kvc.KVC_ERR_STATE
+    c.append_frames(0, num_frames=2)
+    c.append_frames(1, num_frames=2)
+    c.evict_frames()
+    c.plan()
+    assert list(c.get_plan()["qo_indptr"]) == [0, 2 * base.tokens_per_frame]
+    assert c.get_cache_stats()["frame_count"] == 2
+
+
 def test_reset_replays_like_fresh():
     c = tiny_cache()
     plans = []

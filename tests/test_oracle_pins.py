@@ -223,6 +223,39 @@ def pin_bruteforce(oracle=ko, seed=1):
                 assert abs(o - out[i, h, d]) < 1e-12
 
 
+def pin_lse_base2(oracle=ko, seed=3):
+    """lse_base2_fp64 = log2 sum_j exp(q.k_j / sqrt(D)): a scalar loop from the
+    definition on tiny inputs, PyTorch's logsumexp in float64 divided by ln 2
+    as a second routine, and the split-KV identity it exists for: attention
+    over chunks of the keys, merged with weights 2^(lse_c - lse), equals
+    attention over all keys, and log2 of the sum of 2^lse_c equals lse."""
+    import torch
+    rng = np.random.default_rng(seed)
+    T, L, H, D = 3, 7, 2, 4
+    q, k = rand_bits(rng, (T, H, D), 2.0), rand_bits(rng, (L, H, D))
+    Q, K = (syn.bf16_bits_to_f32(x).astype(float).tolist() for x in (q, k))
+    lse = oracle.lse_base2_fp64(q, k)
+    assert lse.shape == (T, H)
+    for i in range(T):
+        for h in range(H):
+            z = sum(math.exp(sum(Q[i][h][d] * K[j][h][d] for d in range(D)) / math.sqrt(D)) for j in range(L))
+            assert abs(math.log2(z) - lse[i, h]) < 1e-12
+    T, L, H, D = 6, 50, 3, 32
+    q, k, v = rand_bits(rng, (T, H, D), 1.5), rand_bits(rng, (L, H, D)), rand_bits(rng, (L, H, D))
+    qd, kd = (torch.from_numpy(syn.bf16_bits_to_f32(x).astype(np.float64)) for x in (q, k))
+    s = torch.einsum("thd,lhd->thl", qd, kd) / math.sqrt(D)
+    ref = (torch.logsumexp(s, dim=2) / math.log(2.0)).numpy()
+    np.testing.assert_allclose(oracle.lse_base2_fp64(q, k), ref, rtol=0, atol=1e-12)
+    full = oracle.attention_fp64(q, k, v)
+    lse = oracle.lse_base2_fp64(q, k)
+    cuts = [0, 11, 12, 30, 50]
+    parts = [(oracle.attention_fp64(q, k[a:b], v[a:b]), oracle.lse_base2_fp64(q, k[a:b]))
+             for a, b in zip(cuts[:-1], cuts[1:])]
+    merged = sum(o * np.exp2(l - lse)[:, :, None] for o, l in parts)
+    np.testing.assert_allclose(merged, full, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(np.log2(sum(np.exp2(l) for _, l in parts)), lse, rtol=0, atol=1e-12)
+
+
 def pin_softmax_invariants(oracle=ko, seed=2):
     rng = np.random.default_rng(seed)
     T, L, H, D = 9, 40, 2, 32
@@ -304,6 +337,10 @@ def test_f16_inputs_match_torch_sdpa():
 
 def test_attention_bruteforce():
     pin_bruteforce()
+
+
+def test_lse_base2_definition_and_split_identity():
+    pin_lse_base2()
 
 
 def test_softmax_invariants():
@@ -568,6 +605,28 @@ class _LifoSpecialReuse(ko.AllocatorReplay):
         return fs
 
 
+def _lse_natural_log(q_bits, k_bits, dtype="bf16"):
+    return ko.lse_base2_fp64(q_bits, k_bits, dtype) * math.log(2.0)    # forgets the base change
+
+
+def _lse_max_only(q_bits, k_bits, dtype="bf16"):
+    q = syn.bf16_bits_to_f32(q_bits).astype(np.float64)
+    k = syn.bf16_bits_to_f32(k_bits).astype(np.float64)
+    return np.stack([((q[:, h] @ k[:, h].T) / math.sqrt(q.shape[2])).max(1) for h in range(q.shape[1])],
+                    1) / math.log(2.0)
+
+
+def _lse_unscaled(q_bits, k_bits, dtype="bf16"):
+    q = syn.bf16_bits_to_f32(q_bits).astype(np.float64)
+    k = syn.bf16_bits_to_f32(k_bits).astype(np.float64)
+    out = np.empty(q.shape[:2])
+    for h in range(q.shape[1]):
+        s = q[:, h] @ k[:, h].T                   # no 1/sqrt(D)
+        m = s.max(1)
+        out[:, h] = (m + np.log(np.exp(s - m[:, None]).sum(1))) / math.log(2.0)
+    return out
+
+
 def _pins_fail(mutant, pins):
     for pin in pins:
         try:
@@ -578,7 +637,8 @@ def _pins_fail(mutant, pins):
 
 
 ALL_PINS = [pin_worked_example, pin_special_closed_forms, pin_visible_set, pin_sdpa, pin_bruteforce,
-            pin_softmax_invariants, pin_paged_equals_dense, pin_scale_phase, pin_rollback, pin_f16_inputs]
+            pin_softmax_invariants, pin_paged_equals_dense, pin_scale_phase, pin_rollback, pin_f16_inputs,
+            pin_lse_base2]
 
 
 @pytest.mark.parametrize("mutant", [
@@ -593,9 +653,12 @@ ALL_PINS = [pin_worked_example, pin_special_closed_forms, pin_visible_set, pin_s
     _Mutant(AllocatorReplay=_OneFramePerStep),
     _Mutant(AllocatorReplay=_RollbackKeepsHeldBack),
     _Mutant(attention_fp64=_f16_read_as_bf16),
+    _Mutant(lse_base2_fp64=_lse_natural_log),
+    _Mutant(lse_base2_fp64=_lse_max_only),
+    _Mutant(lse_base2_fp64=_lse_unscaled),
 ], ids=["no_scale", "values_are_keys", "wrong_softmax_axis", "window_off_by_one", "specials_first",
         "last_page_zero", "scale_evicted", "special_count_drift", "one_frame_per_step", "rollback_no_refill",
-        "f16_read_as_bf16"])
+        "f16_read_as_bf16", "lse_natural_log", "lse_max_only", "lse_unscaled"])
 def test_planted_mistake_is_caught(mutant):
     # OracleStream inside the mutant must use the mutant's allocator
     class _Stream(ko.OracleStream):
