@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 4
+#define KVC_ABI_VERSION 5
 
 typedef struct kvc_ctx kvc_ctx;
 typedef void* kvc_stream_t;   /* hipStream_t */
@@ -272,6 +272,30 @@ kvc_status kvc_plan(kvc_ctx* ctx, kvc_stream_t hip_stream);
  * Errors: KVC_ERR_ARG, KVC_ERR_STATE (not planned, or a planned stream has
  * not appended this block), KVC_ERR_HIP. */
 kvc_status kvc_run(kvc_ctx* ctx, int32_t block, const void* q, void* o, kvc_stream_t hip_stream);
+
+/* Size of the static device scratch behind kvc_run_no_alloc, per device. */
+#define KVC_NO_ALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* For callers that cannot allocate device memory while they run attention:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  kvc_run with the split-KV partial outputs (the per-split
+ * normalised outputs and log-sum-exps that the attention kernel writes and the
+ * merge kernel reads back) kept in a static device array of
+ * KVC_NO_ALLOC_SCRATCH_BYTES that the library holds on each device it runs on
+ * until the process ends, instead of in the context's workspace.  Arguments,
+ * call order and results are those of kvc_run; the plan still comes from the
+ * context's workspace.  Nothing is allocated: no hipMalloc, no hipFree, no
+ * allocating library call (the device address of the array is looked up once
+ * per device, on the first call made with that device current).
+ * Every call on one device shares that device's array, and it keeps the last
+ * call's contents (nothing in it needs to start at zero: every partial is
+ * written before it is read).  Calls that overlap on one device (on different
+ * streams, or from different contexts at the same time) race on the array;
+ * calls issued in order on one stream do not.
+ * Errors: as kvc_run, and KVC_ERR_CAPACITY when the step's plan needs more
+ * partial-output space than the array holds (splits x heads x query tiles of
+ * the configuration); nothing is launched then. */
+kvc_status kvc_run_no_alloc(kvc_ctx* ctx, int32_t block, const void* q, void* o, kvc_stream_t hip_stream);
 
 /* Copy the current plan to host arrays (for bit-exact checks).
  *   planned_streams[capacity_streams], kv_indptr[capacity_streams + 1],

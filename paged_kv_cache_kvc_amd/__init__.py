@@ -30,6 +30,8 @@ KVC_ERR_POOL_EXHAUSTED = -3
 KVC_ERR_CAPACITY = -4
 KVC_ERR_HIP = -5
 KVC_ERR_UNSUPPORTED = -6
+KVC_ERR_HOST_ALLOC = -7
+NO_ALLOC_SCRATCH_BYTES = 64 << 20   # KVC_NO_ALLOC_SCRATCH_BYTES of include/kvc.h
 
 KVC_OPT_TARGET_WORKGROUPS = 1
 KVC_OPT_MAX_SPLITS = 2
@@ -44,7 +46,7 @@ KVC_KERNEL_MERGE = 1
 KVC_KERNEL_APPEND = 2
 
 MAX_SPLITS = 64
-ABI_VERSION = 4   # KVC_ABI_VERSION of include/kvc.h
+ABI_VERSION = 5   # KVC_ABI_VERSION of include/kvc.h
 
 
 class KvcError(RuntimeError):
@@ -87,6 +89,7 @@ SIGNATURES = {
     "kvc_rollback": (_I32, [_P, _I32]),
     "kvc_plan": (_I32, [_P, _P]),
     "kvc_run": (_I32, [_P, _I32, _P, _P, _P]),
+    "kvc_run_no_alloc": (_I32, [_P, _I32, _P, _P, _P]),
     "kvc_get_plan": (_I32, [_P, _PI32, _PI32, _PI32, _PI32, _PI32, _PI32, _PI32, _I32, _I32, _PI32, _PI32]),
     "kvc_get_plan_shape": (_I32, [_P, _PI32, _PI32]),
     "kvc_get_plan_image": (_I32, [_P, _PI32, _I32, _PI32]),
@@ -271,18 +274,24 @@ class PagedKVCache:
         self._check(rc, "plan")
         self._planned = True
 
-    def compute_attention(self, block_idx: int, q, out=None, stream=None):
+    def compute_attention(self, block_idx: int, q, out=None, stream=None, no_alloc: bool = False):
         """Paged attention of the step's queries q [R, H, D] for one block;
-        plans first when called for block 0 of an unplanned step."""
+        plans first when called for block 0 of an unplanned step.  no_alloc
+        runs kvc_run_no_alloc (split partials in the library's static device
+        scratch); out must then be given, since allocating it would defeat
+        the purpose."""
         if block_idx == 0 and not self._planned:
             self.plan(stream)
         rows = q.shape[0]
         self._check_tensor(q, rows, "q")
         if out is None:
+            if no_alloc:
+                raise KvcError(KVC_ERR_ARG, "no_alloc needs a preallocated out")
             out = self.torch.empty_like(q)
         else:
             self._check_tensor(out, rows, "out")
-        rc = self.lib.kvc_run(self._ctx, block_idx, q.data_ptr(), out.data_ptr(), self._stream(stream))
+        fn = self.lib.kvc_run_no_alloc if no_alloc else self.lib.kvc_run
+        rc = fn(self._ctx, block_idx, q.data_ptr(), out.data_ptr(), self._stream(stream))
         self._check(rc, "compute_attention")
         return out
 

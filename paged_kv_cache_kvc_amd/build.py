@@ -31,6 +31,7 @@ HIP_FLAGS = [
     "-fno-honor-nans",
 ]
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
+HIP_FLAGS.append(f"-I{INCLUDE}")
 CXX_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-Wall", "-Wextra", "-Wno-unused-parameter",
              "-D__HIP_PLATFORM_AMD__", f"-I{ROCM}/include", f"-I{INCLUDE}"]
 

@@ -475,8 +475,9 @@ static kvc_status plan_impl(kvc_ctx* c, kvc_stream_t hs) {
   return KVC_OK;
 }
 
-kvc_status kvc_run(kvc_ctx* c, int32_t block, const void* q, void* o, kvc_stream_t hs) {
-  if (!c) return KVC_ERR_ARG;
+// Checks and launches of one block's attention (and merge), with the split
+// partials at lse / po.  `partials` says where they live, for messages.
+static kvc_status check_run(kvc_ctx* c, int32_t block, const void* q, const void* o) {
   if (c->metadata_only) return fail(c, KVC_ERR_STATE, "metadata-only context cannot run");
   const kvc::Config& cf = c->cfg;
   if (block < 0 || block >= cf.num_blocks) return fail(c, KVC_ERR_ARG, "block out of range");
@@ -488,9 +489,13 @@ kvc_status kvc_run(kvc_ctx* c, int32_t block, const void* q, void* o, kvc_stream
     if (!c->block_done[(size_t)s * cf.num_blocks + block])
       return fail(c, KVC_ERR_STATE, "a planned stream has not appended this block");
 
+  return KVC_OK;
+}
+
+static kvc_status launch_run(kvc_ctx* c, int32_t block, const void* q, void* o, kvc_stream_t hs, float* lse,
+                             void* po) {
+  const kvc::Config& cf = c->cfg;
   const int32_t* dplan = reinterpret_cast<const int32_t*>(c->workspace + (c->plan_buf ? c->lay.plan1 : c->lay.plan0));
-  float* lse = reinterpret_cast<float*>(c->workspace + c->lay.lse);
-  void* po = c->workspace + c->lay.part_o;
 
   kvc::AttnParams a;
   std::memset(&a, 0, sizeof(a));
@@ -531,6 +536,43 @@ kvc_status kvc_run(kvc_ctx* c, int32_t block, const void* q, void* o, kvc_stream
     if (e) return hip_fail(c, e, "merge launch");
   }
   return KVC_OK;
+}
+
+kvc_status kvc_run(kvc_ctx* c, int32_t block, const void* q, void* o, kvc_stream_t hs) {
+  if (!c) return KVC_ERR_ARG;
+  const kvc_status rc = check_run(c, block, q, o);
+  if (rc != KVC_OK) return rc;
+  return launch_run(c, block, q, o, hs, reinterpret_cast<float*>(c->workspace + c->lay.lse),
+                    c->workspace + c->lay.part_o);
+}
+
+// Bytes of split partials one plan writes, laid out as in the workspace
+// ([split][head][query tile] lse rows, then the outputs), for the plan's
+// largest split count rather than the workspace's maximum.
+static void partial_extent(const kvc::Config& cf, int32_t max_split, size_t* lse_bytes, size_t* total) {
+  const size_t rows = (size_t)cf.tiles_capacity() * KVC_Q_TILE;
+  *lse_bytes = align_up((size_t)max_split * rows * cf.num_heads * sizeof(float), 256);
+  *total = *lse_bytes + (size_t)max_split * rows * cf.num_heads * cf.head_dim * sizeof(uint16_t);
+}
+
+kvc_status kvc_run_no_alloc(kvc_ctx* c, int32_t block, const void* q, void* o, kvc_stream_t hs) {
+  if (!c) return KVC_ERR_ARG;
+  const kvc_status rc = check_run(c, block, q, o);
+  if (rc != KVC_OK) return rc;
+  char* base = nullptr;
+  size_t cap = 0;
+  const int e = kvc::no_alloc_scratch(reinterpret_cast<void**>(&base), &cap);
+  if (e) return hip_fail(c, e, "static scratch address");
+  const int32_t max_split = *std::max_element(c->plan.n_split.begin(), c->plan.n_split.end());
+  size_t lse_bytes = 0, need = 0;
+  partial_extent(c->cfg, max_split, &lse_bytes, &need);
+  if (need > cap)
+    return fail(c, KVC_ERR_CAPACITY,
+                "the step's split partials need " + std::to_string(need) + " bytes, above the static scratch's " +
+                    std::to_string(cap) + " (fewer splits via KVC_OPT_MAX_SPLITS, or kvc_run)");
+  // with max_split splits the partial tiles are indexed exactly as in the
+  // workspace layout, only with the plan's split count as the extent
+  return launch_run(c, block, q, o, hs, reinterpret_cast<float*>(base), base + lse_bytes);
 }
 
 kvc_status kvc_get_plan(const kvc_ctx* c, int32_t* planned, int32_t* kv_indptr, int32_t* kv_indices,

@@ -2,6 +2,7 @@
 #ifndef KVC_KERNELS_H
 #define KVC_KERNELS_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #include "kvc_plan_layout.h"
@@ -52,6 +53,9 @@ struct MergeParams {
 int launch_append(const AppendParams& p, void* hip_stream);
 int launch_attention(const AttnParams& p, int32_t grid, void* hip_stream);
 int launch_merge(const MergeParams& p, void* hip_stream);
+// Device address and size of the static scratch of kvc_run_no_alloc on the
+// current device (looked up once per device); 0 or the hipError_t value.
+int no_alloc_scratch(void** ptr, size_t* bytes);
 
 }  // namespace kvc
 

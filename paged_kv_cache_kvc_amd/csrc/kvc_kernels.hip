@@ -30,6 +30,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
+#include "kvc.h"
 #include "kvc_kernels.h"
 
 namespace kvc {
@@ -936,6 +939,38 @@ __global__ __launch_bounds__(64 * (D / 16) * HALVES) void merge_kernel(MergePara
 }
 
 }  // namespace
+
+// ---------------------------------------------------------------------------
+// static scratch of kvc_run_no_alloc
+// ---------------------------------------------------------------------------
+// Split partial outputs of kvc_run_no_alloc.  In host code `scratch` names a
+// host-side stand-in, not device memory: its device address (one per device,
+// each device holding its own copy) comes from hipGetSymbolAddress, and only
+// that address is handed to kernels.
+static __device__ __align__(256) uint8_t scratch[KVC_NO_ALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void* scratch_addr[kMaxDevices] = {};
+}  // namespace
+
+int no_alloc_scratch(void** ptr, size_t* bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (!scratch_addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return (int)e;
+    scratch_addr[dev] = p;
+  }
+  *ptr = scratch_addr[dev];
+  *bytes = KVC_NO_ALLOC_SCRATCH_BYTES;
+  return 0;
+}
 
 int launch_append(const AppendParams& p, void* s) {
   hipLaunchKernelGGL(append_kernel, dim3(p.T), dim3(256), 0, (hipStream_t)s, p);
