@@ -254,7 +254,8 @@ kvc_status kvc_rollback(kvc_ctx* ctx, int32_t stream);
  * Errors: KVC_ERR_STATE (no stream appended, or already planned this step),
  * KVC_ERR_CAPACITY (a planned stream holds more than scale_frames +
  * sliding_window patch pages, i.e. kvc_evict was skipped: the plan would not
- * fit the plan buffer; nothing changes), KVC_ERR_HIP. */
+ * fit the plan buffer; or a planned stream sees more than 2^21 tokens, beyond
+ * 64 KV splits of 512 work units of 64 slots; nothing changes), KVC_ERR_HIP. */
 kvc_status kvc_plan(kvc_ctx* ctx, kvc_stream_t hip_stream);
 
 /* Paged attention for one block with the step's plan ([p2] §Attention Kernel
@@ -310,11 +311,14 @@ kvc_status kvc_get_plan(const kvc_ctx* ctx, int32_t* planned_streams, int32_t* k
                         int32_t capacity_indices, int32_t* num_planned, int32_t* num_indices);
 
 /* Shape of the current plan's attention launch (for tests and tuning):
- *   work_items:  attention work-groups, (stream, head, KV split, query group);
- *   group_tiles: query tiles of 16 rows per query group, 9 when the four waves
- *                of a work-group share a ninth tile, else 8.
+ *   work_items: attention work-groups, (stream, head, KV split, query group);
+ *   group_rows: most query rows one work-group covers.  head_dim 32 and 64:
+ *               4 waves x 2 tiles x 32 rows = 256, plus 16 when the launch
+ *               lets a group carry a tail of up to 16 rows shared by the
+ *               waves (272); head_dim 128: 8 tiles x 16 rows = 128, or 144
+ *               with a ninth tile shared by the waves.
  * Either pointer may be NULL.  Errors: KVC_ERR_ARG, KVC_ERR_STATE (no plan). */
-kvc_status kvc_get_plan_shape(const kvc_ctx* ctx, int32_t* work_items, int32_t* group_tiles);
+kvc_status kvc_get_plan_shape(const kvc_ctx* ctx, int32_t* work_items, int32_t* group_rows);
 
 /* Copy the current plan's device image (the int32 buffer that kvc_plan
  * uploads and the kernels read; layout in kvc_plan_layout.h of the sources)

@@ -324,12 +324,12 @@ class PagedKVCache:
         return arrs
 
     def get_plan_shape(self) -> Dict[str, int]:
-        """Attention work-groups of the current plan and query tiles per group."""
+        """Attention work-groups of the current plan and query rows per group."""
         items = ctypes.c_int32()
-        tiles = ctypes.c_int32()
-        self._check(self.lib.kvc_get_plan_shape(self._ctx, ctypes.byref(items), ctypes.byref(tiles)),
+        rows = ctypes.c_int32()
+        self._check(self.lib.kvc_get_plan_shape(self._ctx, ctypes.byref(items), ctypes.byref(rows)),
                     "get_plan_shape")
-        return {"work_items": items.value, "group_tiles": tiles.value}
+        return {"work_items": items.value, "group_rows": rows.value}
 
     def get_plan_image(self) -> np.ndarray:
         """The int32 plan image that kvc_plan uploads for the kernels."""

@@ -73,13 +73,14 @@ def build(verbose: bool = False) -> str:
     cxx = shutil.which("g++") or "g++"
     os.makedirs(BUILD, exist_ok=True)
     objs = []
-    o = os.path.join(BUILD, "kvc_kernels.o")
-    remarks = _run([hipcc, *HIP_FLAGS, "-Rpass-analysis=kernel-resource-usage", "-c",
-                    os.path.join(CSRC, "kvc_kernels.hip"), "-o", o], verbose)
-    if "ScratchSize" not in remarks:
-        raise RuntimeError("no kernel resource usage reported by hipcc")
-    check_no_scratch(remarks)
-    objs.append(o)
+    for src in ("kvc_kernels.hip", "kvc_attn.hip"):
+        o = os.path.join(BUILD, src.replace(".hip", ".o"))
+        remarks = _run([hipcc, *HIP_FLAGS, "-Rpass-analysis=kernel-resource-usage", "-c",
+                        os.path.join(CSRC, src), "-o", o], verbose)
+        if "ScratchSize" not in remarks:
+            raise RuntimeError(f"no kernel resource usage reported by hipcc for {src}")
+        check_no_scratch(remarks)
+        objs.append(o)
     for src in ("kvc_host.cpp", "kvc_api.cpp"):
         o = os.path.join(BUILD, src.replace(".cpp", ".o"))
         _run([cxx, *CXX_FLAGS, "-c", os.path.join(CSRC, src), "-o", o], verbose)

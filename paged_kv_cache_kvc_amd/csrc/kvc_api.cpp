@@ -50,8 +50,8 @@ Layout layout_of(const kvc::Config& c) {
   l.plan0 = 0;
   l.plan1 = l.plan_bytes;
   l.lse = 2 * l.plan_bytes;
-  // partial outputs are stored per query tile of KVC_Q_TILE rows
-  const size_t rows = (size_t)c.tiles_capacity() * KVC_Q_TILE;
+  // partial outputs are stored per query tile of KVC_Q_TILE32 rows
+  const size_t rows = (size_t)c.tiles_capacity() * KVC_Q_TILE32;
   l.part_o = l.lse + align_up((size_t)KVC_MAX_SPLITS * rows * c.num_heads * sizeof(float), 256);
   l.total = l.part_o + align_up((size_t)KVC_MAX_SPLITS * rows * c.num_heads * c.head_dim * sizeof(uint16_t), 256);
   return l;
@@ -169,10 +169,12 @@ size_t kvc_staging_bytes(const kvc_config* cfg) {
   return 2 * layout_of(c).plan_bytes;
 }
 
-// Attention work-groups the device holds at once: two per CU up to D = 64
-// (registers and LDS of two fit), one at D = 128.
+// Attention work-groups the device holds at once: one per CU (the 32x32
+// kernel of head_dim 32 and 64 holds a 6-stage LDS ring and one wave per
+// SIMD; the 16x16 kernel of head_dim 128 one work-group's registers).
 static int32_t resident_workgroups(const kvc::Config& c, int cu_count) {
-  return (c.head_dim <= 64 ? 2 : 1) * cu_count;
+  (void)c;
+  return cu_count;
 }
 
 static kvc_status create_common_impl(const kvc_config* cfg, const int32_t* fpo, const int32_t* fso, kvc_ctx** out,
@@ -450,6 +452,13 @@ static kvc_status plan_impl(kvc_ctx* c, kvc_stream_t hs) {
     return fail(c, KVC_ERR_CAPACITY,
                 "plan larger than the plan buffer: a planned stream holds more than scale_frames + "
                 "sliding_window patch pages (call kvc_evict before kvc_plan)");
+  // The split partial buffers hold KVC_MAX_SPLITS splits; up to head_dim 64
+  // a split covers at most KVC_MAX_SPLIT_STAGES units (its LDS entry table).
+  for (int32_t ns : next.n_split)
+    if (ns > KVC_MAX_SPLITS)
+      return fail(c, KVC_ERR_CAPACITY,
+                  "a planned stream sees more than " + std::to_string(KVC_MAX_SPLITS * KVC_MAX_SPLIT_STAGES * 64) +
+                      " tokens (64 splits of 512 units of 64 slots)");
   c->plan = std::move(next);
   c->planned = true;
   c->plan_stale = false;
@@ -516,7 +525,9 @@ static kvc_status launch_run(kvc_ctx* c, int32_t block, const void* q, void* o, 
   a.items_per_xcd = (c->plan.num_items + 7) / 8;
   a.shared_tile = c->plan.shared_tile ? 1 : 0;
   const int32_t grid = 8 * a.items_per_xcd;
-  int e = timed(c, KVC_KERNEL_ATTENTION, hs, [&] { return kvc::launch_attention(a, grid, hs); });
+  int e = timed(c, KVC_KERNEL_ATTENTION, hs, [&] {
+    return cf.tiles32() ? kvc::launch_attention32(a, grid, hs) : kvc::launch_attention(a, grid, hs);
+  });
   if (e) return hip_fail(c, e, "attention launch");
   if (c->plan.any_split) {
     kvc::MergeParams m;
@@ -550,7 +561,7 @@ kvc_status kvc_run(kvc_ctx* c, int32_t block, const void* q, void* o, kvc_stream
 // ([split][head][query tile] lse rows, then the outputs), for the plan's
 // largest split count rather than the workspace's maximum.
 static void partial_extent(const kvc::Config& cf, int32_t max_split, size_t* lse_bytes, size_t* total) {
-  const size_t rows = (size_t)cf.tiles_capacity() * KVC_Q_TILE;
+  const size_t rows = (size_t)cf.tiles_capacity() * KVC_Q_TILE32;
   *lse_bytes = align_up((size_t)max_split * rows * cf.num_heads * sizeof(float), 256);
   *total = *lse_bytes + (size_t)max_split * rows * cf.num_heads * cf.head_dim * sizeof(uint16_t);
 }
@@ -599,11 +610,16 @@ kvc_status kvc_get_plan(const kvc_ctx* c, int32_t* planned, int32_t* kv_indptr, 
   return KVC_OK;
 }
 
-kvc_status kvc_get_plan_shape(const kvc_ctx* c, int32_t* work_items, int32_t* group_tiles) {
+kvc_status kvc_get_plan_shape(const kvc_ctx* c, int32_t* work_items, int32_t* group_rows) {
   if (!c) return KVC_ERR_ARG;
   if (!c->have_plan) return fail(const_cast<kvc_ctx*>(c), KVC_ERR_STATE, "no plan");
   if (work_items) *work_items = c->plan.num_items;
-  if (group_tiles) *group_tiles = kvc_group_tiles(c->plan.shared_tile ? 1 : 0);
+  if (group_rows) {
+    if (c->cfg.tiles32())
+      *group_rows = KVC_ATTN32_WAVES * 2 * KVC_Q_TILE32 + (c->plan.shared_tile ? KVC_TAIL_ROWS : 0);
+    else
+      *group_rows = kvc_group_tiles(c->plan.shared_tile ? 1 : 0) * KVC_Q_TILE;
+  }
   return KVC_OK;
 }
 

@@ -1,0 +1,798 @@
+// Paged prefill attention for head_dim 32 and 64 on gfx950 (MI355X), with
+// 32x32x16 MFMAs.
+//
+// What it computes: for every planned stream, head and query row of the step,
+// o = softmax(q K^T / sqrt(D)) V over the stream's valid visible tokens,
+// unmasked, K and V gathered through the page table ([p2] "How LingBot-Map
+// Uses FlashInfer KV Cache for Streaming 3D Reconstruction" §Attention Kernel
+// Execution; [p1] "How FlashInfer KV Cache Attention Accelerates Streaming 3D
+// Reconstruction Over SDPA" §Efficient Attention Masking and Padding: lengths
+// delimit the valid tokens).  With split-KV each split writes its normalised
+// partial output and log-sum-exp; the merge kernel combines them.
+//
+// Work item = (stream, head, KV split, query group).  A work-group of 4 waves
+// (one per SIMD) streams its split's K/V through a ring of LDS stages of 64
+// slots of one page, loaded by direct global-to-LDS loads.  A query group is
+// up to 8 tiles of 32 queries: wave w owns tiles w (A) and w + 4 (B).  When
+// the stream's rows leave a remainder of at most 16, those rows form a tail
+// tile of 16 queries shared by the four waves: in every stage wave w takes
+// its slots 16w .. 16w + 15 (16x16 MFMAs), and the four partial softmax
+// states are merged at the end.
+//
+// Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16: kv
+// slots on the rows, queries on the columns, so a lane's accumulators belong
+// to one query (lane n and n + 32 hold its 64 slots, 32 each).  K rows are
+// read in an order (bits 2 and 3 of the row swapped) that makes each lane's
+// 8 consecutive accumulators the 8 consecutive slots the P.V product wants
+// from that lane, so the probabilities pack straight into the P^T operand of
+// O^T = V^T P^T.  V^T comes from row-major V by transposing LDS reads.
+//
+// Each stage runs two steps; each pairs one tile's softmax (vector unit) with
+// the other tile's MFMAs:
+//   step X: QK(B, s), PV(B, s-1), tail QK(s), tail PV(s-1) | softmax(A, s)
+//   step Y: QK(A, s+1), PV(A, s)                           | softmax(B, s), tail softmax(s)
+// Between them one barrier publishes stage s+1 and frees the ring slot of
+// stage s-1; V(s) and K(s+1) are then read from LDS into registers, where they
+// serve both tiles.  Probability row sums come from MFMAs against a 0/1 mask
+// operand (below), a step before the lazy check that reads them.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvc_device.h"
+#include "kvc_kernels.h"
+
+namespace kvc {
+
+namespace {
+
+using namespace dev;
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+template <int E>
+struct M32;
+
+template <>
+struct M32<0> {
+  static __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mfma16x16(const bf16x4& a, const bf16x4& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+  }
+};
+
+template <>
+struct M32<1> {
+  static __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                  0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mfma16x16(const bf16x4& a, const bf16x4& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a), __builtin_bit_cast(f16x4, b), c, 0,
+                                                 0, 0);
+  }
+};
+
+template <int D>
+struct Shape32 {
+  static constexpr int ROW_BYTES = D * 2;
+  static constexpr int KS = D / 16;                    // k-steps of S^T = K Q^T (32x32x16)
+  static constexpr int DB = D / 32;                    // 32-row blocks of O^T
+  static constexpr int TKS = D / 32;                   // tail: k-steps of 16x16x32
+  static constexpr int TDB = D / 16;                   // tail: 16-row blocks of O^T
+  static constexpr int HALF = KVC_KV_TILE * ROW_BYTES; // K (or V) part of a stage
+  static constexpr int STAGE = 2 * HALF;
+  static constexpr int NSTAGE = 6;                     // ring stages; NSTAGE - 2 are loaded ahead
+  static constexpr int LOADS = STAGE / 1024;           // 1 KiB direct-to-LDS loads per stage
+  static constexpr int LPW = LOADS / KVC_ATTN32_WAVES;
+};
+
+// 16-byte chunk swizzle inside a K/V row of LDS, XORed into the chunk index.
+// A 64-lane LDS read is served 256 bytes at a time: a ds_read_b128 by lanes
+// {8a .. 8a+7} with {32+8a .. 32+8a+7}, a ds_read_b64_tr_b16 by lanes 0-31,
+// then 32-63.  In a K read group the rows vary in bits 0, 1, 3 (bits 2 and 3
+// of the lane's row are swapped) and the chunk in bit 0; in a V read group
+// the rows vary in bits 0, 1 and the chunk in bits 0, 1 plus the 8-byte
+// half.  Row bit 0 picks the 128-byte half of the window (D = 64) or rows
+// bits 0-1 its 64-byte quarter (D = 32); the swizzle maps the remaining
+// varying bits one-to-one onto the chunk bits: D = 64: chunk ^= (row1 << 2)
+// | (row3 << 1) | row2; D = 32: chunk ^= (row3 << 1) | row2 (row2 spreads the
+// tail's K reads).
+template <int D>
+__device__ __forceinline__ int swz32(int row) {
+  const int b1 = (row >> 1) & 1, b2 = (row >> 2) & 1, b3 = (row >> 3) & 1;
+  if constexpr (D == 64) return (b1 << 2) | (b3 << 1) | b2;
+  else return (b3 << 1) | b2;
+}
+
+// K row read by lane row m of a 32-slot block: m with bits 2 and 3 swapped.
+// Accumulator element e = 4i + j of lane (n, h) then holds slot
+// 16 (i >> 1) + 8h + 4 (i & 1) + j of the block: elements 8u .. 8u + 7 are
+// slots 16u + 8h .. 16u + 8h + 7, one lane's share of P.V k-step u.
+__device__ __forceinline__ int kperm(int m) { return (m & 0x13) | ((m >> 1) & 0x4) | ((m << 1) & 0x8); }
+
+// Row sums of P^T over one 16-slot k-step by a 16x16x32 MFMA: its B operand
+// is the P^T register as is, which that MFMA reads as lanes {n16, n16 + 16,
+// n16 + 32, n16 + 48} x 8 values: queries n16 and n16 + 16, each from both
+// halves.  The A operand row m selects the lanes of query n16 + 16 ((m / 4)
+// odd) or n16 ((m / 4) even), so result row 4g + j (held by lane 16g + n16)
+// is the sum for query n16 + 16 (g & 1): the lane's own query.  Lane l's A
+// operand is 8 ones when bit 2 of l equals bit 4, else zeros.
+template <int E>
+__device__ __forceinline__ bf16x8 rowsum_mask(int lane) {
+  const uint32_t w = (((lane >> 2) & 1) == ((lane >> 4) & 1)) ? El<E>::ONE2 : 0u;
+  return __builtin_bit_cast(bf16x8, u32x4{w, w, w, w});
+}
+
+// Probabilities of a 32x32 tile: p = 2^(s * scale - ref), packed in pairs to
+// the element type (rounded toward zero) as the four P^T operands.
+template <int E>
+__device__ __forceinline__ void probs32(const f32x16 (&s)[2], float sl, float nref, u32x4 (&pk)[4]) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int e = 8 * (t & 1) + 2 * k;
+      pk[t][k] = El<E>::pack_p(__builtin_amdgcn_exp2f(__builtin_fmaf(s[t >> 1][e], sl, nref)),
+                               __builtin_amdgcn_exp2f(__builtin_fmaf(s[t >> 1][e + 1], sl, nref)));
+    }
+}
+
+// Slot (within the stage) of element e of block sb for lane half h.
+__device__ __forceinline__ int slot32(int sb, int e, int h) {
+  return 32 * sb + 16 * (e >> 3) + 8 * h + 4 * ((e >> 2) & 1) + (e & 3);
+}
+
+// Rare branch: scores of slots at or past `valid` become -inf.  Wait states
+// first, clear of the MFMAs that wrote s.
+__device__ __forceinline__ void mask32(f32x16 (&s)[2], int valid, int h) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  int lim = valid;
+  asm volatile("" : "+v"(lim));
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      if (slot32(sb, e, h) >= lim) s[sb][e] = -INFINITY;
+}
+
+__device__ __forceinline__ void mask16(f32x4& s, int valid, int slot0) {
+  asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+  int lim = valid - slot0;
+  asm volatile("" : "+v"(lim));
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (j >= lim) s[j] = -INFINITY;
+}
+
+// Exact path of a 32x32 tile (rare): column maximum of s * scale - ref over
+// the stage (the lane's 32 slots and those of lane ^ 32), ref moved up to it
+// (set, while the tile has seen no valid slot, `fresh`), the running sum and
+// output scaled by 2^-(shift), and the probabilities recomputed.  Returns the
+// column sum of the recomputed (rounded) probabilities.
+template <int DB, int E>
+__device__ __forceinline__ float renorm32(const f32x16 (&s)[2], float sl, int& fresh, float& ref, float& nref,
+                                          float& l, f32x16 (&o)[DB], u32x4 (&pk)[4]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  float m = s[0][0];
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) m = max2(m, s[sb][e]);
+  {
+    uint32_t a = __builtin_bit_cast(uint32_t, m), b = a;
+    swap32(a, b);
+    m = max2(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+  }
+  m = __builtin_fmaf(m, sl, nref);
+  const bool first = fresh != 0;
+  fresh = __builtin_amdgcn_readfirstlane((int)(first && __builtin_amdgcn_ballot_w64(m == -INFINITY) != 0));
+  const float shift = first ? (m == -INFINITY ? 0.0f : m) : fmaxf(m, 0.0f);
+  // (one block of four accumulators, one k-step of probabilities at a
+  // time: this branch runs while every value of the hot loop is live)
+  if (!first) {
+    const float alpha = __builtin_amdgcn_exp2f(-shift);
+    l *= alpha;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[db][4 * q4 + j] *= alpha;
+      }
+  }
+  ref += shift;
+  nref = -ref;
+  float a = 0.f, b = 0.f;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int e = 8 * (t & 1) + 2 * k;
+      pk[t][k] = El<E>::pack_p(__builtin_amdgcn_exp2f(__builtin_fmaf(s[t >> 1][e], sl, nref)),
+                               __builtin_amdgcn_exp2f(__builtin_fmaf(s[t >> 1][e + 1], sl, nref)));
+    }
+    a = El<E>::dot_ones(pk[t][0], a);
+    b = El<E>::dot_ones(pk[t][1], b);
+    a = El<E>::dot_ones(pk[t][2], a);
+    b = El<E>::dot_ones(pk[t][3], b);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  float sum = a + b;
+  {
+    uint32_t x = __builtin_bit_cast(uint32_t, sum), y = x;
+    swap32(x, y);
+    sum = __builtin_bit_cast(float, x) + __builtin_bit_cast(float, y);
+  }
+  asm volatile("s_nop 3" ::: "memory");
+  return sum;
+}
+
+// The same for the tail's 16x16 block (4 slots per lane; a column's 16
+// slots sit in lanes l, l ^ 16, l ^ 32, l ^ 48).  Returns the lane's sum.
+template <int TDB, int E>
+__device__ __forceinline__ float renorm16(const f32x4& s, float sl, int& fresh, float& ref, float& nref, float& l,
+                                          f32x4 (&o)[TDB], u32x2& pk) {
+  asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+  float m = max2(max2(s[0], s[1]), max2(s[2], s[3]));
+  m = __builtin_fmaf(lane_swap_max(m), sl, nref);
+  const bool first = fresh != 0;
+  fresh = __builtin_amdgcn_readfirstlane((int)(first && __builtin_amdgcn_ballot_w64(m == -INFINITY) != 0));
+  const float shift = first ? (m == -INFINITY ? 0.0f : m) : fmaxf(m, 0.0f);
+  if (!first) {
+    const float alpha = __builtin_amdgcn_exp2f(-shift);
+    l *= alpha;
+#pragma unroll
+    for (int db = 0; db < TDB; ++db) o[db] *= alpha;
+  }
+  ref += shift;
+  nref = -ref;
+  pk[0] = El<E>::pack_p(__builtin_amdgcn_exp2f(__builtin_fmaf(s[0], sl, nref)),
+                        __builtin_amdgcn_exp2f(__builtin_fmaf(s[1], sl, nref)));
+  pk[1] = El<E>::pack_p(__builtin_amdgcn_exp2f(__builtin_fmaf(s[2], sl, nref)),
+                        __builtin_amdgcn_exp2f(__builtin_fmaf(s[3], sl, nref)));
+  const float lt = El<E>::dot_ones(pk[1], El<E>::dot_ones(pk[0], 0.f));
+  asm volatile("s_nop 3" ::: "memory");
+  return lt;
+}
+
+// Barrier that first waits for the wave's LDS reads: after it, other waves'
+// direct-to-LDS loads may refill the ring slot those reads came from.
+__device__ __forceinline__ void ring_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <int D, int E, bool TAIL>
+__global__ __launch_bounds__(64 * KVC_ATTN32_WAVES, 1) void attn32_kernel(AttnParams p) {
+  using S = Shape32<D>;
+  using MM = M32<E>;
+  constexpr int KS = S::KS, DB = S::DB, TKS = S::TKS, TDB = S::TDB, LPW = S::LPW, NST = S::NSTAGE;
+  // LDS: the ring of K/V stages; each wave's query operands in register
+  // order (tile A, tile B, tail: one 1 KiB block per k-step, lane l at 16 l,
+  // so every read is one conflict-free 1 KiB row); the split's unit entries.
+  constexpr int QBLK = 2 * KS + (TAIL ? TKS : 0);
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[NST * S::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t qlds[KVC_ATTN32_WAVES * QBLK * 1024];
+  __shared__ int2 elds[KVC_MAX_SPLIT_STAGES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int n = lane & 31, h = lane >> 5;       // 32x32 layouts: query column, lane half
+  const int r16 = lane & 15, g4 = lane >> 4;    // 16x16 layouts
+
+  // XCD-aware item order: work-groups go round-robin over the 8 XCDs; each
+  // XCD takes a contiguous item range, so one head's splits share an L2.
+  const int bid = blockIdx.x;
+  const int item = (bid & 7) * p.items_per_xcd + (bid >> 3);
+  if (item >= p.num_items) return;
+
+  const int nstreams = p.plan[KVC_HDR_NUM_STREAMS];
+  const kvc_dev_stream* recs = reinterpret_cast<const kvc_dev_stream*>(p.plan + KVC_PLAN_HEADER_INTS);
+  int si = 0;
+  while (si + 1 < nstreams && item >= recs[si + 1].item0) ++si;
+  const kvc_dev_stream st = recs[si];
+
+  int local = item - st.item0;
+  const int grp = local % st.n_group;
+  local /= st.n_group;
+  const int split = local % st.n_split;
+  const int hd = local / st.n_split;
+
+  // tiles of 32 rows of this group, and the tail (16 rows) if this group has it
+  const int t_lo = grp * st.n_t32 / st.n_group;
+  const int t_hi = (grp + 1) * st.n_t32 / st.n_group;
+  const int ntile = t_hi - t_lo;
+  const bool has_tail = TAIL && st.tail != 0 && grp == st.n_group - 1;
+  const int u0 = split * st.n_units / st.n_split;
+  const int u1 = (split + 1) * st.n_units / st.n_split;
+  const int nstage = u1 - u0;
+  const int H = p.num_heads;
+  const uint32_t slot_bytes = (uint32_t)H * D * 2;
+  const int32_t* units = p.plan + st.unit0 + KVC_UNIT_INTS * u0;
+  const uint64_t head_off = (uint64_t)hd * D * 2;
+  const float sl = p.scale_log2;
+
+  // This split's unit entries (the host planner resolved pages, chunks and
+  // valid lengths), copied once to LDS; each stage reads its own entry from
+  // there, so the stage loop issues no global memory operation besides its
+  // direct-to-LDS loads (whose completion it counts with vmcnt).
+  for (int u = tid; u < nstage; u += 64 * KVC_ATTN32_WAVES)
+    elds[u] = *reinterpret_cast<const int2*>(units + KVC_UNIT_INTS * u);
+  // entry of stage i (uniform): slot index of its first K row, valid slots
+  auto stage_entry = [&](int i) {
+    const int2 e = elds[i];
+    return int2{__builtin_amdgcn_readfirstlane(e.x), __builtin_amdgcn_readfirstlane(e.y)};
+  };
+  auto stage_entry_valid = [&](int i) { return __builtin_amdgcn_readfirstlane(elds[i].y); };
+
+  // ---- query operands (B of S^T = K Q^T), staged in LDS ----
+  // tile: lane (n, h) holds q[row n][16 ks + 8h .. + 8) for each k-step
+  uint8_t* qw = qlds + wv * QBLK * 1024 + lane * 16;
+  auto stage_q32 = [&](int tile, bool ok, int blk0) {
+    const int row = 32 * tile + n;
+    ok = ok && row < st.n_q;
+    const uint16_t* qr = static_cast<const uint16_t*>(p.q) + ((size_t)(st.q_row0 + (ok ? row : 0)) * H + hd) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 v = *reinterpret_cast<const u32x4*>(qr + 16 * ks + 8 * h);
+      if (!ok) v = u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(qw + (blk0 + ks) * 1024) = v;
+    }
+  };
+  stage_q32(t_lo + wv, wv < ntile, 0);
+  stage_q32(t_lo + wv + 4, wv + 4 < ntile, KS);
+  const int tail_row0 = 32 * st.n_t32;
+  if constexpr (TAIL) {
+    // tail: lane (r16, g4) holds q[row r16][32 tks + 8 g4 .. + 8)
+    const int row = tail_row0 + r16;
+    const bool ok = has_tail && row < st.n_q;
+    const uint16_t* qr = static_cast<const uint16_t*>(p.q) + ((size_t)(st.q_row0 + (ok ? row : 0)) * H + hd) * D;
+#pragma unroll
+    for (int k = 0; k < TKS; ++k) {
+      u32x4 v = *reinterpret_cast<const u32x4*>(qr + 32 * k + 8 * g4);
+      if (!ok) v = u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(qw + (2 * KS + k) * 1024) = v;
+    }
+  }
+  auto read_q = [&](int blk) { return *reinterpret_cast<const bf16x8*>(qw + blk * 1024); };
+
+  // ---- softmax state: ref (log2 units) and its negation, running sum, and
+  // fresh (no valid slot seen yet) per tile ----
+  float refA = 0.f, refB = 0.f, refT = 0.f, nrefA = 0.f, nrefB = 0.f, nrefT = 0.f;
+  float lA = 0.f, lB = 0.f, lT = 0.f;
+  int freshA = 1, freshB = 1, freshT = 1;
+  f32x16 oA[DB], oB[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) oA[db][e] = oB[db][e] = 0.f;
+  f32x4 oT[TDB];
+#pragma unroll
+  for (int db = 0; db < TDB; ++db) oT[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // ---- direct global -> LDS loads of one stage (K rows, then V rows) ----
+  // Load instruction j of the wave fills 1 KiB at LDS byte 1024 * (wave *
+  // LPW + j) of the stage, lane l writing [16 l, 16 l + 16); the lane fetches
+  // the logical chunk the swizzle places there.  In a partial stage, rows
+  // past the valid count re-read the last valid row (finite; masked later).
+  const uint8_t* pool = static_cast<const uint8_t*>(p.pool);
+  const uint64_t v_half = (uint64_t)p.page_size * slot_bytes;
+  // Load instruction i of a stage (K: i < LOADS / 2, V: the rest) covers
+  // rows RPL (i % (LOADS / 2)) .. + RPL - 1 of its half; lane l writes chunk
+  // l % CPR of row RPL (i % ...) + l / CPR.  The swizzle depends on row bits
+  // 1-3.  With D = 32 (RPL = 16) they all come from l / CPR; with D = 64
+  // (RPL = 8) bit 3 is the parity of the load's row block, which is that of
+  // the wave's load index j (LPW and LOADS / 2 are even).  So one per-lane
+  // offset per block parity serves every load, and the row offset
+  // RPL (i % ...) joins the (scalar) base address.
+  constexpr int CPR = S::ROW_BYTES / 16, RPL = 1024 / S::ROW_BYTES;
+  static_assert(RPL % 16 == 0 || (RPL == 8 && LPW % 2 == 0 && (S::LOADS / 2) % 2 == 0), "load row blocks");
+  const int lrow0 = lane / CPR;
+  const uint32_t lofs0 = (uint32_t)lrow0 * slot_bytes + (uint32_t)(((lane % CPR) ^ swz32<D>(lrow0)) << 4);
+  const uint32_t lofs1 =
+      RPL == 8 ? (uint32_t)lrow0 * slot_bytes + (uint32_t)(((lane % CPR) ^ swz32<D>(lrow0 + 8)) << 4) : lofs0;
+  const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(lds_addr(ring));
+  auto issue = [&](int sidx) {
+    const int2 e = stage_entry(sidx);
+    const uint64_t koff = (uint64_t)(uint32_t)e.x * slot_bytes + head_off;
+    const int valid = e.y;
+    const uint32_t slot = ring_lds + (uint32_t)(sidx % NST) * S::STAGE;
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {
+      const int inst = wv * LPW + j;
+      const int kv = inst >= S::LOADS / 2 ? 1 : 0;
+      const int blk = inst - kv * (S::LOADS / 2);
+      int row0 = RPL * blk;                       // first row of this load (uniform)
+      const uint32_t lofs = (j & 1) ? lofs1 : lofs0;
+      uint32_t o = lofs;
+      // partial stage (rare): rows past the valid count re-read the last valid
+      // row.  The offset is an unsigned 32-bit addend of the scalar base, so
+      // the row is measured from the unit's first row, never below it.
+      if (__builtin_expect(valid < KVC_KV_TILE, 0)) {
+        const int row = row0 + lrow0;
+        o = lofs + (uint32_t)(min(row, valid - 1) - lrow0) * slot_bytes;
+        row0 = 0;
+      }
+      load_lds16(pool + koff + (kv ? v_half : 0) + (uint64_t)row0 * slot_bytes, o,
+                 __builtin_amdgcn_readfirstlane(slot + (uint32_t)(kv * S::HALF + blk * 1024)));
+    }
+  };
+
+  // ---- LDS operand offsets (per lane; stage base added at the read) ----
+  uint32_t kofs[KS];          // K rows (A of S^T): row kperm(n) of each 32-slot block, chunk 2ks + h
+  {
+    const int row = kperm(n);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      kofs[ks] = (uint32_t)(row * S::ROW_BYTES + (((2 * ks + h) ^ swz32<D>(row)) << 4));
+  }
+  uint32_t vofs[DB][2];       // V^T (A of O^T) by transposing reads: k-step 0; + 16 rows per k-step
+  {
+    const int g = lane >> 4, s = lane & 15;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr) {
+        const int row = 8 * (g >> 1) + 4 * rr + (s >> 2);
+        const int c = 4 * db + 2 * (g & 1) + ((s & 3) >> 1);
+        vofs[db][rr] = (uint32_t)(S::HALF + row * S::ROW_BYTES + ((c ^ swz32<D>(row)) << 4) + 8 * (s & 1));
+      }
+  }
+  uint32_t tkofs[TKS], tvofs[TDB];   // tail: K rows 16w + r16; V^T rows 16w + 4 g4 + s / 4
+  if constexpr (TAIL) {
+    const int row = 16 * wv + r16;
+#pragma unroll
+    for (int k = 0; k < TKS; ++k)
+      tkofs[k] = (uint32_t)(row * S::ROW_BYTES + (((4 * k + g4) ^ swz32<D>(row)) << 4));
+    const int s = lane & 15;
+    const int vrow = 16 * wv + 4 * g4 + (s >> 2);
+#pragma unroll
+    for (int db = 0; db < TDB; ++db) {
+      const int c = 2 * db + ((s & 3) >> 1);
+      tvofs[db] = (uint32_t)(S::HALF + vrow * S::ROW_BYTES + ((c ^ swz32<D>(vrow)) << 4) + 8 * (s & 1));
+    }
+  }
+
+  bf16x8 kop[2][KS], vop[4][DB];
+  bf16x8 tk[TKS];
+  bf16x4 tv[TDB];
+  auto read_k = [&](int sidx) {
+    const uint8_t* b = ring + (sidx % NST) * S::STAGE;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        kop[sb][ks] = *reinterpret_cast<const bf16x8*>(b + kofs[ks] + 32 * sb * S::ROW_BYTES);
+  };
+  // tail operands of step X: K(s) and V(s-1) (both ring slots still hold
+  // their stages until the barrier that follows step X)
+  auto read_tail = [&](int s) {
+    const uint8_t* bk = ring + (s % NST) * S::STAGE;
+    const uint8_t* bv = ring + ((s + NST - 1) % NST) * S::STAGE;
+#pragma unroll
+    for (int k = 0; k < TKS; ++k) tk[k] = *reinterpret_cast<const bf16x8*>(bk + tkofs[k]);
+#pragma unroll
+    for (int db = 0; db < TDB; ++db) tv[db] = __builtin_bit_cast(bf16x4, ds_read_tr16(bv + tvofs[db]));
+  };
+  auto read_v = [&](int sidx) {
+    const uint8_t* b = ring + (sidx % NST) * S::STAGE;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const i16x4 x0 = ds_read_tr16(b + vofs[db][0] + 16 * t * S::ROW_BYTES);
+        const i16x4 x1 = ds_read_tr16(b + vofs[db][1] + 16 * t * S::ROW_BYTES);
+        vop[t][db] = __builtin_bit_cast(
+            bf16x8, (short __attribute__((ext_vector_type(8)))){x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]});
+      }
+  };
+
+  const bf16x8 mask = rowsum_mask<E>(lane);
+  auto qk32 = [&](int qblk0, f32x16 (&s)[2]) {
+    bf16x8 q[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) q[ks] = read_q(qblk0 + ks);
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      s[sb] = MM::mfma32(kop[sb][0], q[0], f32x16{});
+#pragma unroll
+      for (int ks = 1; ks < KS; ++ks) s[sb] = MM::mfma32(kop[sb][ks], q[ks], s[sb]);
+    }
+  };
+  auto pv32 = [&](const u32x4 (&pk)[4], f32x16 (&o)[DB]) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] = MM::mfma32(vop[t][db], __builtin_bit_cast(bf16x8, pk[t]), o[db]);
+  };
+  auto rowsum = [&](const u32x4 (&pk)[4]) {
+    f32x4 r = El<E>::mfma(mask, __builtin_bit_cast(bf16x8, pk[0]), f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+    for (int t = 1; t < 4; ++t) r = El<E>::mfma(mask, __builtin_bit_cast(bf16x8, pk[t]), r);
+    return r;
+  };
+  auto qk16 = [&](f32x4& s) {
+    s = El<E>::mfma(tk[0], read_q(2 * KS), f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+    for (int k = 1; k < TKS; ++k) s = El<E>::mfma(tk[k], read_q(2 * KS + k), s);
+  };
+  auto pv16 = [&](const u32x2& pk) {
+#pragma unroll
+    for (int db = 0; db < TDB; ++db) oT[db] = MM::mfma16x16(tv[db], __builtin_bit_cast(bf16x4, pk), oT[db]);
+  };
+
+  f32x16 sA[2], sB[2];
+  u32x4 pA[4], pB[4];
+  f32x4 rsA, rsB, sT;
+  u32x2 pT = u32x2{0u, 0u};
+  float ltT = 0.f;
+
+  // ---- prologue: the first NST - 1 stages loaded, stage 0 published ----
+  __syncthreads();   // unit entries and query operands staged
+  {
+    const int pre = min(nstage, NST - 1);
+    for (int i = 0; i < pre; ++i) issue(i);
+    switch (pre) {   // stage 0 complete: the later stages' loads may still fly
+      case 5: wait_vmcnt<4 * LPW>(); break;
+      case 4: wait_vmcnt<3 * LPW>(); break;
+      case 3: wait_vmcnt<2 * LPW>(); break;
+      case 2: wait_vmcnt<1 * LPW>(); break;
+      default: wait_vmcnt<0>(); break;
+    }
+  }
+  block_barrier();
+  read_k(0);
+  qk32(0, sA);
+  {
+    const int v0 = stage_entry_valid(0);
+    if (v0 < KVC_KV_TILE) mask32(sA, v0, h);
+  }
+  // "stage -1" of tile B and of the tail: all slots masked, zero operands;
+  // their first checks take the exact path and leave them fresh and empty
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sB[sb][e] = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    pB[t] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int db = 0; db < DB; ++db) vop[t][db] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+  }
+  rsB = f32x4{0.f, 0.f, 0.f, 0.f};
+  sT = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+
+  for (int s = 0; s < nstage; ++s) {
+    const int valid = stage_entry_valid(s);
+
+    // ---- step X: check of B (stage s-1) and of the tail (stage s-1) ----
+    {
+      float cs = rsB[0];
+      if (__builtin_expect(freshB || __builtin_amdgcn_ballot_w64(cs > LAZY_COL_LIMIT), 0))
+        cs = renorm32<DB, E>(sB, sl, freshB, refB, nrefB, lB, oB, pB);
+      lB += cs;
+    }
+    if constexpr (TAIL) {
+      float lt = ltT;
+      if (__builtin_expect(freshT || __builtin_amdgcn_ballot_w64(lt > LAZY_SUM_LIMIT), 0))
+        lt = renorm16<TDB, E>(sT, sl, freshT, refT, nrefT, lT, oT, pT);
+      lT += lt;
+    }
+    // MFMAs: QK(B, s), tail QK(s), PV(B, s-1), tail PV(s-1) | softmax(A, s)
+    if constexpr (TAIL) {
+      read_tail(s);
+      if (s == 0) {
+#pragma unroll
+        for (int db = 0; db < TDB; ++db) tv[db] = __builtin_bit_cast(bf16x4, u32x2{0u, 0u});
+      }
+    }
+    qk32(KS, sB);
+    if constexpr (TAIL) qk16(sT);
+    pv32(pB, oB);
+    if constexpr (TAIL) pv16(pT);
+    probs32<E>(sA, sl, nrefA, pA);
+    rsA = rowsum(pA);
+#pragma unroll
+    for (int i = 0; i < (TAIL ? 26 : 20); ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+    }
+
+    // ---- stage s+1 published, slot of stage s-1 free; V(s) and K(s+1) read ----
+    {
+      const int ahead = min(nstage - 2 - s, NST - 3);   // stages after s+1 whose loads may fly
+      switch (ahead) {
+        case 3: wait_vmcnt<3 * LPW>(); break;
+        case 2: wait_vmcnt<2 * LPW>(); break;
+        case 1: wait_vmcnt<1 * LPW>(); break;
+        default: wait_vmcnt<0>(); break;
+      }
+    }
+    ring_barrier();
+    if (s + NST - 1 < nstage) issue(s + NST - 1);
+    read_v(s);
+    read_k(s + 1);
+
+    // ---- step Y: check of A (stage s) ----
+    if (__builtin_expect(valid < KVC_KV_TILE, 0)) {
+      mask32(sB, valid, h);
+      if constexpr (TAIL) mask16(sT, valid, 16 * wv + 4 * g4);
+    }
+    {
+      float cs = rsA[0];
+      if (__builtin_expect(freshA || __builtin_amdgcn_ballot_w64(cs > LAZY_COL_LIMIT), 0))
+        cs = renorm32<DB, E>(sA, sl, freshA, refA, nrefA, lA, oA, pA);
+      lA += cs;
+    }
+    // MFMAs: QK(A, s+1), PV(A, s) | softmax(B, s), tail softmax(s)
+    qk32(0, sA);
+    pv32(pA, oA);
+    probs32<E>(sB, sl, nrefB, pB);
+    rsB = rowsum(pB);
+    if constexpr (TAIL) {
+      pT[0] = El<E>::pack_p(__builtin_amdgcn_exp2f(__builtin_fmaf(sT[0], sl, nrefT)),
+                            __builtin_amdgcn_exp2f(__builtin_fmaf(sT[1], sl, nrefT)));
+      pT[1] = El<E>::pack_p(__builtin_amdgcn_exp2f(__builtin_fmaf(sT[2], sl, nrefT)),
+                            __builtin_amdgcn_exp2f(__builtin_fmaf(sT[3], sl, nrefT)));
+      ltT = El<E>::dot_ones(pT[1], El<E>::dot_ones(pT[0], 0.f));
+    }
+#pragma unroll
+    for (int i = 0; i < 20; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, TAIL ? 4 : 3, 0);
+    }
+    // the next stage's A scores need masking before its softmax (step X)
+    if (s + 1 < nstage) {
+      const int vn = stage_entry_valid(s + 1);
+      if (__builtin_expect(vn < KVC_KV_TILE, 0)) mask32(sA, vn, h);
+    }
+  }
+
+  // ---- drain: check and P.V of B and of the tail for the last stage ----
+  {
+    float cs = rsB[0];
+    if (__builtin_expect(freshB || __builtin_amdgcn_ballot_w64(cs > LAZY_COL_LIMIT), 0))
+      cs = renorm32<DB, E>(sB, sl, freshB, refB, nrefB, lB, oB, pB);
+    lB += cs;
+  }
+  pv32(pB, oB);
+  if constexpr (TAIL) {
+    {
+      const uint8_t* bv = ring + ((nstage - 1) % NST) * S::STAGE;
+#pragma unroll
+      for (int db = 0; db < TDB; ++db) tv[db] = __builtin_bit_cast(bf16x4, ds_read_tr16(bv + tvofs[db]));
+    }
+    float lt = ltT;
+    if (__builtin_expect(freshT || __builtin_amdgcn_ballot_w64(lt > LAZY_SUM_LIMIT), 0))
+      lt = renorm16<TDB, E>(sT, sl, freshT, refT, nrefT, lT, oT, pT);
+    lT += lt;
+    pv16(pT);
+  }
+  // the epilogue reads the accumulators the last MFMAs wrote
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+
+  // ---- epilogue ----
+  // 32x32 tiles: lane (n, h) holds O^T[32 db + 8 i + 4 h + j][query n] in
+  // element 4 i + j of block db.
+  auto store32 = [&](int tile, float ref, float l, const f32x16 (&o)[DB]) {
+    const float inv = 1.0f / l;
+    const int row = 32 * tile + n;
+    if (st.n_split > 1) {
+      // normalised partial output (a convex combination of V rows, rounded
+      // to the element type) in the accumulator's lane order, and its
+      // log-sum-exp; rows past the stream's queries are stored too (never merged)
+      const size_t pt = ((size_t)split * H + hd) * p.tiles_cap + st.q_tile0 + tile;
+      uint16_t* po = static_cast<uint16_t*>(p.part_o) + pt * (size_t)(DB * 4 * 256) + lane * 4;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f32x4 v = f32x4{o[db][4 * i], o[db][4 * i + 1], o[db][4 * i + 2], o[db][4 * i + 3]} * inv;
+          *reinterpret_cast<u32x2*>(po + (db * 4 + i) * 256) = El<E>::cvt4(v);
+        }
+      if (h == 0) p.part_lse[pt * 32 + n] = ref + __log2f(l);
+      return;
+    }
+    if (row >= st.n_q) return;
+    uint16_t* orow = static_cast<uint16_t*>(p.o) + ((size_t)(st.q_row0 + row) * H + hd) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x4 v = f32x4{o[db][4 * i], o[db][4 * i + 1], o[db][4 * i + 2], o[db][4 * i + 3]} * inv;
+        *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * i + 4 * h) = El<E>::cvt4(v);
+      }
+  };
+  if (wv < ntile) store32(t_lo + wv, refA, lA, oA);
+  if (wv + 4 < ntile) store32(t_lo + wv + 4, refB, lB, oB);
+
+  if constexpr (TAIL) {
+    if (has_tail) {
+      // merge the four waves' states of the tail (weights 2^(ref_w - max ref));
+      // a wave whose slots were all masked has l = 0
+      constexpr int NV = TDB * 4 + 2;
+      float* xs = reinterpret_cast<float*>(ring);
+      const float lsum_w = lane_swap_sum(lT);
+      __syncthreads();   // every wave is done with the ring
+#pragma unroll
+      for (int db = 0; db < TDB; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xs[(wv * 64 + lane) * NV + 4 * db + j] = oT[db][j];
+      xs[(wv * 64 + lane) * NV + TDB * 4] = lsum_w > 0.0f ? refT : -INFINITY;
+      xs[(wv * 64 + lane) * NV + TDB * 4 + 1] = lsum_w;
+      __syncthreads();
+      if (wv == 0) {
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < KVC_ATTN32_WAVES; ++w) M = fmaxf(M, xs[(w * 64 + lane) * NV + TDB * 4]);
+        float lsum = 0.f;
+        f32x4 o[TDB];
+#pragma unroll
+        for (int db = 0; db < TDB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < KVC_ATTN32_WAVES; ++w) {
+          const float* x = xs + (w * 64 + lane) * NV;
+          const float wt = __builtin_amdgcn_exp2f(x[TDB * 4] - M);
+          lsum += wt * x[TDB * 4 + 1];
+#pragma unroll
+          for (int db = 0; db < TDB; ++db)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) o[db][j] += wt * x[4 * db + j];
+        }
+        const float inv = 1.0f / lsum;
+        // lane (r16, g4) holds O^T[16 db + 4 g4 + j][tail query r16]
+        if (st.n_split > 1) {
+          // stored as rows 0-15 of the 32-row tile after the full ones, in
+          // the 32x32 accumulator lane order the merge reads
+          const size_t pt = ((size_t)split * H + hd) * p.tiles_cap + st.q_tile0 + st.n_t32;
+          uint16_t* po = static_cast<uint16_t*>(p.part_o) + pt * (size_t)(DB * 4 * 256);
+#pragma unroll
+          for (int db = 0; db < TDB; ++db) {
+            const int d = 16 * db + 4 * g4;
+            const int b32 = d >> 5, i = (d & 31) >> 3, hh = (d >> 2) & 1;
+            *reinterpret_cast<u32x2*>(po + (b32 * 4 + i) * 256 + (32 * hh + r16) * 4) = El<E>::cvt4(o[db] * inv);
+          }
+          if (g4 == 0) p.part_lse[pt * 32 + r16] = M + __log2f(lsum);
+        } else {
+          const int row = tail_row0 + r16;
+          if (row < st.n_q) {
+            uint16_t* orow = static_cast<uint16_t*>(p.o) + ((size_t)(st.q_row0 + row) * H + hd) * D;
+#pragma unroll
+            for (int db = 0; db < TDB; ++db)
+              *reinterpret_cast<u32x2*>(orow + 16 * db + 4 * g4) = El<E>::cvt4(o[db] * inv);
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int E, bool TAIL>
+int launch32_et(const AttnParams& p, int32_t grid, hipStream_t hs) {
+  switch (p.head_dim) {
+    case 32:
+      hipLaunchKernelGGL((attn32_kernel<32, E, TAIL>), dim3(grid), dim3(64 * KVC_ATTN32_WAVES), 0, hs, p);
+      break;
+    case 64:
+      hipLaunchKernelGGL((attn32_kernel<64, E, TAIL>), dim3(grid), dim3(64 * KVC_ATTN32_WAVES), 0, hs, p);
+      break;
+    default:
+      return (int)hipErrorInvalidValue;
+  }
+  return (int)hipGetLastError();
+}
+
+}  // namespace
+
+int launch_attention32(const AttnParams& p, int32_t grid, void* s) {
+  const hipStream_t hs = (hipStream_t)s;
+  if (p.dtype == 0) return p.shared_tile ? launch32_et<0, true>(p, grid, hs) : launch32_et<0, false>(p, grid, hs);
+  if (p.dtype == 1) return p.shared_tile ? launch32_et<1, true>(p, grid, hs) : launch32_et<1, false>(p, grid, hs);
+  return (int)hipErrorInvalidValue;
+}
+
+}  // namespace kvc

@@ -244,15 +244,14 @@ void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const s
   }
 
   // Work decomposition: each work item is (stream, head, KV split, query
-  // group).  Query groups hold at most KVC_ATTN_WAVES * KVC_TILES_PER_WAVE
-  // tiles, plus a ninth shared by the waves when the launch uses one.
-  // Every work-group costs the same per 64-slot unit, so a launch takes as
-  // long as its longest split times the number of rounds in which the
-  // work-groups run.  The target work-group count is what the device holds
-  // at once (one round); the split counts start from each stream's share of
-  // it, in proportion to queries x visible tokens, rounded down; then the
-  // stream whose splits are longest gains a split while that shortens them
-  // and the whole launch still fits in one round.
+  // group), one work-group.  Every work-group costs about the same per 64-slot
+  // unit, its busiest wave's share, so a launch takes as long as its longest
+  // split (in units times that per-unit cost) times the number of rounds in
+  // which the work-groups run.  The target work-group count is what the
+  // device holds at once (one round); the split counts start from each
+  // stream's share of it, in proportion to queries x visible tokens, rounded
+  // down; then the stream whose splits take longest gains a split while that
+  // shortens them and the whole launch still fits in one round.
   double total_work = 0;
   for (int i = 0; i < n; ++i) total_work += (double)frames[i] * (double)kv_len[i];
   const int32_t max_splits = std::max(1, std::min<int32_t>(pol.max_splits, KVC_MAX_SPLITS));
@@ -267,26 +266,75 @@ void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const s
                (n_special > 0 ? (int64_t)(n_special - 1) * ups + ceil_div(p.last_page_len[i], KVC_KV_TILE) : 0));
     cap[i] = std::min<int64_t>(max_splits, units[i]);
   }
-  // Split counts for one query grouping (groups of at most per_group tiles);
-  // returns the launch's estimated length in tile-steps per wave.
+  // The 32x32 kernel stages a split's unit entries in LDS: at most
+  // KVC_MAX_SPLIT_STAGES units per split.
+  std::vector<int64_t> min_split(n, 1);
+  if (c.tiles32())
+    for (int i = 0; i < n; ++i) {
+      min_split[i] = ceil_div(units[i], KVC_MAX_SPLIT_STAGES);
+      cap[i] = std::max(cap[i], min_split[i]);
+    }
+  // A query grouping: per stream, its groups, (32x32 kernel) full 32-row
+  // tiles and tail, and the per-unit cost of its busiest wave in 16x64
+  // tile-steps.
+  struct Grouping {
+    std::vector<int64_t> n_group, n_t32, tail;
+    std::vector<double> per_unit;
+    bool variant = false;
+  };
+  auto grouping = [&](bool variant) {
+    Grouping g;
+    g.variant = variant;
+    g.n_group.resize(n);
+    g.n_t32.assign(n, 0);
+    g.tail.assign(n, 0);
+    g.per_unit.resize(n);
+    for (int i = 0; i < n; ++i) {
+      const int64_t n_q = (int64_t)frames[i] * c.tokens_per_frame;
+      if (c.tiles32()) {
+        // variant: rows past the last full 32-row tile, if at most 16, form a
+        // tail that the four waves share (a quarter of its slots each)
+        const int64_t rem = n_q % KVC_Q_TILE32;
+        const bool tail = variant && rem >= 1 && rem <= KVC_TAIL_ROWS;
+        const int64_t nt = tail ? n_q / KVC_Q_TILE32 : ceil_div(n_q, KVC_Q_TILE32);
+        const int64_t per = KVC_ATTN32_WAVES * 2;
+        g.n_group[i] = std::max<int64_t>(1, ceil_div(nt, per));
+        g.n_t32[i] = nt;
+        g.tail[i] = tail ? 1 : 0;
+        // wave w owns tiles w and w + 4 of its group: 2 tile-steps each, plus
+        // a quarter tile-step of the tail in every group of a tail launch
+        const int64_t kmax = ceil_div(nt, g.n_group[i]);
+        g.per_unit[i] = (kmax > 0 ? 2.0 : 0.0) + (kmax > KVC_ATTN32_WAVES ? 2.0 : 0.0) + (variant ? 0.25 : 0.0);
+      } else {
+        // 16x16 kernel: groups of 8 tiles of 16 rows, or 9 with the ninth
+        // shared by the four waves (a quarter tile-step each per stage)
+        const int64_t nqt = ceil_div(n_q, KVC_Q_TILE);
+        g.n_group[i] = ceil_div(nqt, kvc_group_tiles(variant ? 1 : 0));
+        g.per_unit[i] = variant ? 2.25 : 2.0;
+      }
+    }
+    return g;
+  };
   struct Choice {
-    std::vector<int64_t> groups, nsplit;
+    Grouping g;
+    std::vector<int64_t> nsplit;
     double cost;
   };
-  auto choose = [&](int32_t per_group) {
+  auto choose = [&](const Grouping& g) {
     Choice ch;
-    ch.groups.resize(n);
+    ch.g = g;
     ch.nsplit.resize(n);
+    std::vector<int64_t> items(n);
     int64_t items_total = 0;
     for (int i = 0; i < n; ++i) {
-      const int32_t nqt = (int32_t)ceil_div(frames[i] * c.tokens_per_frame, KVC_Q_TILE);
-      ch.groups[i] = (int64_t)c.num_heads * ceil_div(nqt, per_group);
+      items[i] = (int64_t)c.num_heads * g.n_group[i];
       const double want = total_work > 0 ? (double)pol.target_workgroups * (double)frames[i] * (double)kv_len[i] /
-                                               total_work / (double)ch.groups[i]
+                                               total_work / (double)items[i]
                                          : 1.0;
-      ch.nsplit[i] = std::max<int64_t>(1, std::min<int64_t>((int64_t)std::floor(want), cap[i]));
-      items_total += ch.groups[i] * ch.nsplit[i];
+      ch.nsplit[i] = std::max<int64_t>(min_split[i], std::min<int64_t>((int64_t)std::floor(want), cap[i]));
+      items_total += items[i] * ch.nsplit[i];
     }
+    auto length = [&](int i, int64_t ns) { return (double)ceil_div(units[i], ns) * g.per_unit[i]; };
     // The launch lasts as long as the longest split: only that stream's
     // splits are worth adding, and once it cannot gain one (at its cap, over
     // the target, or no shorter for it), no other split would shorten the
@@ -294,31 +342,27 @@ void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const s
     auto longest = [&]() {
       int best = 0;
       for (int i = 1; i < n; ++i)
-        if (ceil_div(units[i], ch.nsplit[i]) > ceil_div(units[best], ch.nsplit[best])) best = i;
+        if (length(i, ch.nsplit[i]) > length(best, ch.nsplit[best])) best = i;
       return best;
     };
     for (;;) {
-      const int best = longest();
-      if (ch.nsplit[best] >= cap[best] || items_total + ch.groups[best] > pol.target_workgroups ||
-          ceil_div(units[best], ch.nsplit[best] + 1) >= ceil_div(units[best], ch.nsplit[best]))
+      const int b = longest();
+      if (ch.nsplit[b] >= cap[b] || items_total + items[b] > pol.target_workgroups ||
+          ceil_div(units[b], ch.nsplit[b] + 1) >= ceil_div(units[b], ch.nsplit[b]))
         break;
-      ++ch.nsplit[best];
-      items_total += ch.groups[best];
+      ++ch.nsplit[b];
+      items_total += items[b];
     }
-    // per stage, a wave does 2 tiles plus a quarter of the shared one
-    const double per_stage = per_group > KVC_ATTN_WAVES * KVC_TILES_PER_WAVE ? 2.25 : 2.0;
     const int64_t rounds = std::max<int64_t>(1, ceil_div(items_total, std::max(1, pol.target_workgroups)));
     const int b = longest();
-    ch.cost = (double)ceil_div(units[b], ch.nsplit[b]) * per_stage * (double)rounds;
+    ch.cost = length(b, ch.nsplit[b]) * (double)rounds;
     return ch;
   };
-  // Query groups of 9 tiles (the ninth shared by the four waves) or of 8:
-  // the shared tile packs 17 tiles into two groups, but costs every stage a
-  // quarter tile per wave; take the grouping with the shorter launch.
-  const Choice with_shared = choose(kvc_group_tiles(1)), without = choose(kvc_group_tiles(0));
-  p.shared_tile = !(without.cost < with_shared.cost);
-  const Choice& ch = p.shared_tile ? with_shared : without;
-  const int32_t per_group = kvc_group_tiles(p.shared_tile ? 1 : 0);
+  // Take the grouping variant (a shared tail / a shared ninth tile) when it
+  // gives the shorter launch.
+  const Choice with_variant = choose(grouping(true)), without = choose(grouping(false));
+  p.shared_tile = !(without.cost < with_variant.cost);
+  const Choice& ch = p.shared_tile ? with_variant : without;
   const std::vector<int64_t>& nsplit = ch.nsplit;
 
   p.image.assign(KVC_PLAN_HEADER_INTS + (size_t)KVC_STREAM_REC_INTS * n + p.kv_indices.size(), 0);
@@ -326,8 +370,7 @@ void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const s
   p.any_split = false;
   for (int i = 0; i < n; ++i) {
     const int32_t n_q = frames[i] * c.tokens_per_frame;
-    const int32_t nqt = (int32_t)ceil_div(n_q, KVC_Q_TILE);
-    const int32_t n_group = (int32_t)ceil_div(nqt, per_group);
+    const int32_t n_group = (int32_t)ch.g.n_group[i];
     const int64_t ns = nsplit[i];
     p.n_split.push_back((int32_t)ns);
     if (ns > 1) p.any_split = true;
@@ -348,7 +391,9 @@ void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const s
     rec.n_split = (int32_t)ns;
     rec.n_group = n_group;
     rec.q_tile0 = tiles;
-    tiles += nqt;
+    rec.n_t32 = (int32_t)ch.g.n_t32[i];
+    rec.tail = (int32_t)ch.g.tail[i];
+    tiles += (int32_t)ceil_div(n_q, KVC_Q_TILE32);
     rec.item0 = item;
     rec.n_items = c.num_heads * (int32_t)ns * n_group;
     item += rec.n_items;
@@ -371,7 +416,6 @@ void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const s
   // page last_page_len ([p1] "How FlashInfer KV Cache Attention Accelerates
   // Streaming 3D Reconstruction Over SDPA" §Efficient Attention Masking and
   // Padding: lengths, not masks, delimit the valid tokens).
-  const uint64_t slot_bytes = (uint64_t)c.num_heads * c.head_dim * 2;
   size_t at = (p.image.size() + 3) & ~(size_t)3;
   for (int i = 0; i < n; ++i) {
     kvc_dev_stream* rec = reinterpret_cast<kvc_dev_stream*>(&p.image[KVC_PLAN_HEADER_INTS + (size_t)KVC_STREAM_REC_INTS * i]);
@@ -393,11 +437,13 @@ void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const s
         cu = u - patch_units - pj * r.ups;
       }
       const int32_t len = pi == r.n_pages - 1 ? r.last_len : (pi < r.n_patch ? P : c.page_size);
-      const uint64_t off = ((uint64_t)idx[pi] * 2 * c.page_size + (uint64_t)KVC_KV_TILE * cu) * slot_bytes;
+      // slot index of the unit's first K row in the block's pool [pages][2][page_size]
+      // (below 2^32: validate keeps pages * page_size below 2^31)
+      const uint32_t slot = (uint32_t)idx[pi] * 2u * (uint32_t)c.page_size + (uint32_t)KVC_KV_TILE * (uint32_t)cu;
       int32_t* e = &p.image[at + (size_t)KVC_UNIT_INTS * u];
-      e[0] = (int32_t)(uint32_t)off;
-      e[1] = (int32_t)(uint32_t)(off >> 32);
-      e[2] = std::min<int32_t>(KVC_KV_TILE, len - KVC_KV_TILE * cu);
+      e[0] = (int32_t)slot;
+      e[1] = std::min<int32_t>(KVC_KV_TILE, len - KVC_KV_TILE * cu);
+      e[2] = 0;
       e[3] = 0;
     }
     at += (size_t)KVC_UNIT_INTS * r.n_units;
@@ -405,30 +451,37 @@ void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const s
 
   // Merge order: the attention work-group of item i runs on XCD
   // i / items_per_xcd (the kernel gives each XCD a contiguous item range), so
-  // the split partials of a (tile, head) sit in that XCD's L2.  Each pair is
-  // merged on the XCD that ran its middle split.  An entry carries what the
-  // merge needs of its tile (split count and output rows), so that the merge
-  // reads one entry before its partials.
+  // the split partials of a (tile, head) sit in that XCD's L2.  Each pair of
+  // a 32-row tile and a head is merged on the XCD that ran its middle split.
+  // An entry carries what the merge needs of its tile (split count and output
+  // rows), so that the merge reads one entry before its partials.
   std::vector<std::vector<std::array<int32_t, KVC_MERGE_INTS>>> bucket(KVC_NUM_XCD);
   const int32_t ipx = (p.num_items + KVC_NUM_XCD - 1) / KVC_NUM_XCD;
-  for (int i = 0, t0 = 0; i < n; ++i) {
+  for (int i = 0; i < n; ++i) {
     const int32_t n_q = p.qo_indptr[i + 1] - p.qo_indptr[i];
-    const int32_t nqt = (int32_t)ceil_div(n_q, KVC_Q_TILE);
+    const int32_t ntile = (int32_t)ceil_div(n_q, KVC_Q_TILE32);
     kvc_dev_stream r;
     std::memcpy(&r, &p.image[KVC_PLAN_HEADER_INTS + (size_t)KVC_STREAM_REC_INTS * i], sizeof(r));
-    if (r.n_split > 1) {
-      for (int32_t t = 0; t < nqt; ++t) {
-        int32_t grp = 0;
-        while ((grp + 1) * nqt / r.n_group <= t) ++grp;   // the query group holding tile t
-        for (int32_t h = 0; h < c.num_heads; ++h) {
-          const int32_t item = r.item0 + (h * r.n_split + r.n_split / 2) * r.n_group + grp;
-          bucket[std::min(item / std::max(1, ipx), KVC_NUM_XCD - 1)].push_back(
-              {(t0 + t) * c.num_heads + h, r.n_split, p.qo_indptr[i] + KVC_Q_TILE * t,
-               std::min<int32_t>(KVC_Q_TILE, n_q - KVC_Q_TILE * t)});
-        }
+    if (r.n_split <= 1) continue;
+    for (int32_t t = 0; t < ntile; ++t) {
+      // the query group holding (the first rows of) tile t
+      int32_t grp = 0;
+      if (c.tiles32()) {
+        if (t >= r.n_t32)
+          grp = r.n_group - 1;   // the tail
+        else
+          while ((grp + 1) * r.n_t32 / r.n_group <= t) ++grp;
+      } else {
+        const int32_t nqt = (int32_t)ceil_div(n_q, KVC_Q_TILE);
+        while ((grp + 1) * nqt / r.n_group <= 2 * t) ++grp;
+      }
+      for (int32_t h = 0; h < c.num_heads; ++h) {
+        const int32_t it = r.item0 + (h * r.n_split + r.n_split / 2) * r.n_group + grp;
+        bucket[std::min(it / std::max(1, ipx), KVC_NUM_XCD - 1)].push_back(
+            {(r.q_tile0 + t) * c.num_heads + h, r.n_split, p.qo_indptr[i] + KVC_Q_TILE32 * t,
+             std::min<int32_t>(KVC_Q_TILE32, n_q - KVC_Q_TILE32 * t)});
       }
     }
-    t0 += nqt;
   }
   size_t slots = 0;
   for (const auto& b : bucket) slots = std::max(slots, b.size());

@@ -31,10 +31,12 @@ struct Config {
   int32_t patch_tokens() const { return tokens_per_frame - num_special_tokens; }
   int32_t max_num_pages() const { return max_patch_pages + max_special_pages; }
   int32_t rows_capacity() const { return num_streams * max_frames_per_step * tokens_per_frame; }
-  // query tiles of KVC_Q_TILE rows over all streams (split partial outputs)
+  // query tiles of KVC_Q_TILE32 rows over all streams (split partial outputs)
   int32_t tiles_capacity() const {
-    return num_streams * ((max_frames_per_step * tokens_per_frame + KVC_Q_TILE - 1) / KVC_Q_TILE);
+    return num_streams * ((max_frames_per_step * tokens_per_frame + KVC_Q_TILE32 - 1) / KVC_Q_TILE32);
   }
+  // the 32x32 attention kernel serves head_dim 32 and 64, the 16x16 one 128
+  bool tiles32() const { return head_dim <= 64; }
 };
 
 // Result codes mirror kvc_status.
@@ -122,7 +124,8 @@ struct HostPlan {
   int32_t num_items = 0;
   int32_t num_rows = 0;
   int32_t num_tiles = 0;
-  bool shared_tile = true;             // query groups with a shared ninth tile (else up to 8 tiles)
+  bool shared_tile = true;             // launch variant (KVC_HDR_SHARED_TILE): 32x32 kernel: groups may carry a
+                                       // 16-row tail; 16x16 kernel: groups with a shared ninth tile
   int32_t merge_table = 0;             // offset in ints of the merge order in image
   int32_t merge_slots = 0;             // merge slots per XCD
   bool any_split = false;

@@ -24,16 +24,17 @@ struct AttnParams {
   const void* pool;
   const void* q;            // [R, H, D] bf16
   void* o;                  // [R, H, D] bf16
-  // Split partial outputs, per query tile of 16 rows, in the lane order of the
-  // MFMA accumulators so that each store instruction writes 512 contiguous
-  // bytes: part_o[split][head][tile][d block of 16][lane][4] bf16 (normalised;
-  // lane = 16 * (d%16)/4 + row%16), part_lse[split][head][tile][16] float.
+  // Split partial outputs, per query tile of 32 rows, in the lane order of the
+  // 32x32 MFMA accumulators so that each store instruction of that kernel
+  // writes 512 contiguous bytes: part_o[split][head][tile][d / 32][(d % 32) / 8]
+  // [lane][4] bf16 (normalised; lane = 32 * ((d % 8) / 4) + row % 32, the last
+  // index d % 4), part_lse[split][head][tile][32] float (base-2 log-sum-exp).
   void* part_o;
   float* part_lse;
-  int32_t num_heads, head_dim, page_size, patch_tokens, tiles_cap;
+  int32_t num_heads, head_dim, page_size, patch_tokens, tiles_cap;   // tiles_cap: 32-row tiles
   float scale_log2;         // log2(e) / sqrt(D)
   int32_t num_items, items_per_xcd;
-  int32_t shared_tile;      // 1: query groups of up to 9 tiles, the ninth shared by the waves; 0: up to 8
+  int32_t shared_tile;      // launch variant, as KVC_HDR_SHARED_TILE of the plan
   int32_t dtype;            // element type: 0 bfloat16, 1 float16
 };
 
@@ -51,7 +52,8 @@ struct MergeParams {
 
 // Return 0 on success or the hipError_t value.
 int launch_append(const AppendParams& p, void* hip_stream);
-int launch_attention(const AttnParams& p, int32_t grid, void* hip_stream);
+int launch_attention(const AttnParams& p, int32_t grid, void* hip_stream);     // 16x16 kernel, head_dim 128
+int launch_attention32(const AttnParams& p, int32_t grid, void* hip_stream);   // 32x32 kernel, head_dim 32, 64
 int launch_merge(const MergeParams& p, void* hip_stream);
 // Device address and size of the static scratch of kvc_run_no_alloc on the
 // current device (looked up once per device); 0 or the hipError_t value.

@@ -33,84 +33,14 @@
 #include <mutex>
 
 #include "kvc.h"
+#include "kvc_device.h"
 #include "kvc_kernels.h"
 
 namespace kvc {
 
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-constexpr int KT = KVC_KV_TILE;
-
-// Element type of the pools, k, v, q, o and the split partials: E = 0
-// bfloat16, E = 1 float16.  Operands travel as raw 16-bit pairs (bf16x8
-// registers) and take their type only in the MFMA, the probability packing,
-// the row-sum dot product and the conversions to and from float32.
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-template <int E>
-struct El;
-
-template <>
-struct El<0> {
-  static constexpr uint32_t ONE2 = 0x3f803f80u;   // two bf16 ones
-  static __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-  }
-  // bf16 pair of p (lo, hi): the upper halves of the float32 values (rounded
-  // toward zero), one byte permute per pair
-  static __device__ __forceinline__ uint32_t pack_p(float lo, float hi) {
-    return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, hi), __builtin_bit_cast(uint32_t, lo), 0x07060302u);
-  }
-  static __device__ __forceinline__ float dot_ones(uint32_t w, float acc) {
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, acc, false);
-  }
-  // round to nearest even
-  static __device__ __forceinline__ u32x2 cvt4(const f32x4& v) {
-    const bf16x4 b = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
-    return __builtin_bit_cast(u32x2, b);
-  }
-  static __device__ __forceinline__ f32x4 widen4(const u32x2& x) {
-    const bf16x4 b = __builtin_bit_cast(bf16x4, x);
-    return f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
-  }
-};
-
-template <>
-struct El<1> {
-  static constexpr uint32_t ONE2 = 0x3c003c00u;   // two f16 ones
-  static __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
-                                                   0, 0);
-  }
-  // f16 pair of p (lo, hi), rounded toward zero in one packing conversion;
-  // p <= 2^8 here, inside the f16 range
-  static __device__ __forceinline__ uint32_t pack_p(float lo, float hi) {
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
-  }
-  static __device__ __forceinline__ float dot_ones(uint32_t w, float acc) {
-    const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), ones, acc, false);
-  }
-  static __device__ __forceinline__ u32x2 cvt4(const f32x4& v) {
-    typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-    const f16x4 b = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
-    return __builtin_bit_cast(u32x2, b);
-  }
-  static __device__ __forceinline__ f32x4 widen4(const u32x2& x) {
-    typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-    const f16x4 b = __builtin_bit_cast(f16x4, x);
-    return f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
-  }
-};
+using namespace dev;
 
 // ---------------------------------------------------------------------------
 // append
@@ -187,104 +117,6 @@ __device__ __forceinline__ int swz(int row) {
   else if constexpr (D == 64) return b1 | ((b1 ^ b3) << 1) | ((b3 ^ b4) << 2);
   else return b3 | (b3 << 1) | (b0 << 2) | (b1 << 3);
 }
-
-// The ring of stages is filled by direct global->LDS loads that the kernel
-// issues, waits for and publishes itself: the compiler would otherwise treat
-// every LDS read as depending on every load in flight and drain the ring at
-// each barrier.  Completion is tracked with vmcnt (vector memory operations
-// retire in issue order), then a barrier makes a stage visible to all waves.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
-
-// One work-unit entry of the plan (16 bytes at a wave-uniform address) read
-// into scalar registers.  The load completes asynchronously: unit_wait must
-// run before the value is used (it names the registers, so every use follows
-// it).  Scalar loads share the lgkm counter with LDS reads; an extra scalar
-// load in flight only makes the compiler's own LDS waits stricter.
-typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ i32x4 unit_load(const int32_t* entry) {
-  i32x4 e;
-  asm volatile("s_load_dwordx4 %0, %1, 0x0" : "=s"(e) : "s"(entry) : "memory");
-  return e;
-}
-__device__ __forceinline__ void unit_wait(i32x4& e) { asm volatile("s_waitcnt lgkmcnt(0)" : "+s"(e)::"memory"); }
-
-// 16 bytes from base + offset (per lane) to LDS byte address
-// lds_base + 16 * lane.  base is wave-uniform (scalar registers).
-__device__ __forceinline__ void load_lds16(const void* base, uint32_t offset, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(offset), "s"(base),
-               "s"(lds_base)
-               : "memory", "m0");
-}
-
-// Maximum of scores (never NaN: masked slots are -inf).  Written with the
-// compiler's own max so that its hazard tracking sees the MFMA results these
-// read (an opaque instruction reading an MFMA accumulator too early would see
-// a partially written register).
-__device__ __forceinline__ float max2(float a, float b) { return __builtin_fmaxf(a, b); }
-
-__device__ __forceinline__ uint32_t lds_addr(const void* generic) {
-  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)generic;
-}
-
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ i16x4 ds_read_tr16(const uint8_t* lds_generic) {
-  const lds_i16x4* p = (const lds_i16x4*)(__attribute__((address_space(3))) const uint8_t*)lds_generic;
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
-}
-
-// Exchange with the lane 32 (or 16) apart: after the swap, each lane holds
-// its own value and its partner's in (a, b).  Issued directly because the
-// compiler builtin's second result is not usable.
-__device__ __forceinline__ void swap32(uint32_t& a, uint32_t& b) {
-  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
-}
-__device__ __forceinline__ void swap16(uint32_t& a, uint32_t& b) {
-  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
-}
-
-// max / sum over lanes l, l^16, l^32, l^48: the four lane groups that hold
-// one query column of an MFMA accumulator
-__device__ __forceinline__ float lane_swap_max(float x) {
-  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
-  swap32(a, b);
-  x = max2(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
-  a = __builtin_bit_cast(uint32_t, x);
-  b = a;
-  swap16(a, b);
-  return max2(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
-}
-
-__device__ __forceinline__ float lane_swap_sum(float x) {
-  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
-  swap32(a, b);
-  x = __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
-  a = __builtin_bit_cast(uint32_t, x);
-  b = a;
-  swap16(a, b);
-  return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
-}
-
-// Lazy renormalisation.  Each query tile keeps a reference value ref in log2
-// units (the running maximum as last renormalised); a stage's probabilities
-// are p = 2^(s * scale - ref), with scale = log2(e)/sqrt(D) applied in fp32 to
-// the exact MFMA scores.  The stage is first exponentiated against the
-// current ref; only when a lane's sum of those probabilities exceeds 2^8 (a
-// score more than a few units above ref, or an overflow to infinity) is it
-// redone against the exact column maximum.  A tile's first stage with a valid
-// slot always takes the exact path.  The own tiles test the whole column's
-// sum over the stage (the four lane groups' 64 slots), against four times the
-// lane limit.
-constexpr float LAZY_SUM_LIMIT = 256.0f;
-constexpr float LAZY_COL_LIMIT = 4.0f * LAZY_SUM_LIMIT;
 
 template <int D, int E>
 struct Ops {
@@ -547,8 +379,8 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
   // LDS byte address of the ring (uniform)
   const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(lds_addr(ring));
   auto issue = [&](int sidx, const i32x4& e) {
-    const uint64_t koff = ((uint64_t)(uint32_t)e.x | ((uint64_t)(uint32_t)e.y << 32)) + head_off;
-    const int valid = e.z;
+    const uint64_t koff = (uint64_t)(uint32_t)e.x * slot_bytes + head_off;
+    const int valid = e.y;
     const uint32_t slot = ring_lds + (uint32_t)(sidx % S::NSTAGE) * S::STAGE_BYTES;
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
@@ -649,7 +481,7 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
   issue(0, e0);
   if (nstage > 1) issue(1, e1);
   if (nstage > 2) issue(2, e2);
-  int vq0 = e0.z, vq1 = e1.z, vq2 = e2.z;
+  int vq0 = e0.y, vq1 = e1.y, vq2 = e2.y;
   if (nstage >= 3)
     wait_vmcnt<2 * LPW>();
   else if (nstage == 2)
@@ -705,7 +537,7 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
     if (s + 3 < nstage) issue(s + 3, en);
     vq0 = vq1;
     vq1 = vq2;
-    vq2 = en.z;
+    vq2 = en.y;
     read_k(s + 1, kop);
 
     // ---- step 1: QK of the shared tile, P.V of own tile 0 | probabilities of own tile 1 ----
@@ -778,12 +610,22 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
     if (st.n_split > 1) {
       // normalised partial output, rounded to bf16 (a convex combination of
       // V rows, so within V's range), and its log-sum-exp in float32; rows
-      // past the stream's queries are stored too (finite; never merged)
-      const size_t pt = ((size_t)split * H + h) * p.tiles_cap + st.q_tile0 + tile;
-      uint16_t* po = static_cast<uint16_t*>(p.part_o) + pt * DB * 256 + lane * 4;
+      // past the stream's queries are stored too (finite; never merged).
+      // The layout is that of the 32x32 kernel's accumulators (per 32-row
+      // tile): this 16-row tile is half `tile & 1` of 32-row tile tile / 2,
+      // and lane (r16, g4)'s four values of d block db are d = 16 db + 4 g4
+      // .. + 3, i.e. 32-lane row 16 (tile & 1) + r16 of slice (d / 32,
+      // (d % 32) / 8), lane half (d / 4) & 1.
+      const size_t pt = ((size_t)split * H + h) * p.tiles_cap + st.q_tile0 + (tile >> 1);
+      const int r32 = 16 * (tile & 1) + r16;
+      uint16_t* po = static_cast<uint16_t*>(p.part_o) + pt * (size_t)(D / 32 * 4 * 256);
 #pragma unroll
-      for (int db = 0; db < DB; ++db) *reinterpret_cast<u32x2*>(po + db * 256) = El<E>::cvt4(o[db] * inv);
-      if (g4 == 0) p.part_lse[pt * KVC_Q_TILE + r16] = ref + __log2f(l);
+      for (int db = 0; db < DB; ++db) {
+        const int d = 16 * db + 4 * g4;
+        *reinterpret_cast<u32x2*>(po + ((d >> 5) * 4 + ((d & 31) >> 3)) * 256 + (32 * ((d >> 2) & 1) + r32) * 4) =
+            El<E>::cvt4(o[db] * inv);
+      }
+      if (g4 == 0) p.part_lse[pt * KVC_Q_TILE32 + r32] = ref + __log2f(l);
       return;
     }
     if (row >= st.n_q) return;
@@ -840,28 +682,22 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
 // ---------------------------------------------------------------------------
 // merge of KV splits
 // ---------------------------------------------------------------------------
-// One work-group of DB waves per (query tile, head) of a split stream, on the
-// XCD whose L2 holds most of its partials (the plan's merge order lists the
-// pairs of each XCD; work-group b runs on XCD b % 8).  Wave w takes d block
-// w % DB, each lane the 4 values it holds in every split's partial (the
-// accumulator lane order).  The pair's merge-order entry also gives its
-// stream's split count and output rows.  The partials and log-sum-exps of up
-// to MERGE_CHUNK splits are loaded together, then folded in split order with
-// weights 2^(lse_c - running max): one memory round trip per chunk, and every
-// sum in a fixed order.  Splits past the tile's own count (other streams may
-// have more) are loaded from the workspace but never used.  The chunk is the
-// smallest of 2, 4, 8 that covers the plan's largest split count, else 8: a
-// larger chunk holds more registers, and the occupancy it costs outweighs the
-// round trips it saves (measured: 16 splits merge faster in two chunks of 8).
-// With more than one chunk, HALVES = 2 doubles the waves: the second set
-// folds the odd chunks in the same round trip as the first set's even ones,
-// and the two folds are combined through LDS (fixed order again).
-template <int D, int E, int MERGE_CHUNK, int HALVES>
-__global__ __launch_bounds__(64 * (D / 16) * HALVES) void merge_kernel(MergeParams p) {
-  constexpr int DB = D / 16;
+// One work-group per (32-row query tile, head) of a split stream, on the XCD
+// whose L2 holds most of its partials (the plan's merge order lists the
+// pairs of each XCD; work-group b runs on XCD b % 8).  The partials are laid
+// out per tile as D / 32 x 4 slices of 64 lanes x 4 values (the 32x32
+// accumulator order); wave w takes slice w, each lane the 4 values it holds
+// in every split: row n = lane % 32, d = 32 (w / 4) + 8 (w % 4) + 4 (lane / 32)
+// .. + 3.  The pair's merge-order entry gives its stream's split count and
+// output rows.  The partials and log-sum-exps of up to CH splits are loaded
+// together, then folded in split order with weights 2^(lse_c - running max):
+// one memory round trip per chunk, and every sum in a fixed order.  Splits
+// past the tile's own count (other streams may have more) are never loaded.
+template <int D, int E, int CH>
+__global__ __launch_bounds__(64 * (D / 32) * 4) void merge_kernel(MergeParams p) {
+  constexpr int SLICES = D / 32 * 4;
   const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
-  const int db = wv % DB, half = wv / DB;
+  const int w = threadIdx.x >> 6;
   const int H = p.num_heads;
   const int slot = blockIdx.x >> 3;
   if (slot >= p.merge_slots) return;      // uniform over the work-group
@@ -870,70 +706,46 @@ __global__ __launch_bounds__(64 * (D / 16) * HALVES) void merge_kernel(MergePara
       p.plan + p.merge_table + KVC_MERGE_INTS * ((blockIdx.x & (KVC_NUM_XCD - 1)) * p.merge_slots + slot));
   const int pair = te.x;
   if (pair < 0) return;
-  const int gt = pair / H;                // global query tile
+  const int gt = pair / H;                // global 32-row tile
   const int h = pair - gt * H;
-  const int r16 = lane & 15, g4 = lane >> 4;
+  const int nsp = te.y;
+  const int n = lane & 31, hh = lane >> 5;
   const size_t tstride = (size_t)H * p.tiles_cap;   // between splits, in tiles
   const size_t t0 = (size_t)h * p.tiles_cap + gt;
-  const uint16_t* po = static_cast<const uint16_t*>(p.part_o) + (t0 * DB + db) * 256 + lane * 4;
-  const float* pl = p.part_lse + t0 * KVC_Q_TILE + r16;
+  const uint16_t* po = static_cast<const uint16_t*>(p.part_o) + (t0 * SLICES + w) * 256 + lane * 4;
+  const float* pl = p.part_lse + t0 * KVC_Q_TILE32 + n;
   float m = -INFINITY, wsum = 0.f;
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  // With two halves, the waves of half 1 fold the odd chunks, those of half 0
-  // the even ones; both load in the same round trip.
-  for (int c0 = half * MERGE_CHUNK; c0 < p.max_split; c0 += HALVES * MERGE_CHUNK) {
-    float lse[MERGE_CHUNK];
-    u32x2 x[MERGE_CHUNK];
+  for (int c0 = 0; c0 < nsp; c0 += CH) {
+    float lse[CH];
+    u32x2 x[CH];
 #pragma unroll
-    for (int j = 0; j < MERGE_CHUNK; ++j)
-      if (c0 + j < p.max_split) {
+    for (int j = 0; j < CH; ++j)
+      if (c0 + j < nsp) {
         const size_t c = (size_t)(c0 + j) * tstride;
-        lse[j] = pl[c * KVC_Q_TILE];
-        x[j] = *reinterpret_cast<const u32x2*>(po + c * DB * 256);
+        lse[j] = pl[c * KVC_Q_TILE32];
+        x[j] = *reinterpret_cast<const u32x2*>(po + c * SLICES * 256);
       }
-    const int nsp = te.y;
-    if (HALVES == 1 && nsp <= 1) return;  // single split: attention wrote o itself
     float mc = m;
 #pragma unroll
-    for (int j = 0; j < MERGE_CHUNK; ++j)
+    for (int j = 0; j < CH; ++j)
       if (c0 + j < nsp) mc = fmaxf(mc, lse[j]);
     if (mc == -INFINITY) continue;        // nothing of weight yet
     const float sc = __builtin_amdgcn_exp2f(m - mc);   // 0 while m is -inf
     acc *= sc;
     wsum *= sc;
 #pragma unroll
-    for (int j = 0; j < MERGE_CHUNK; ++j)
+    for (int j = 0; j < CH; ++j)
       if (c0 + j < nsp) {
-        const float w = __builtin_amdgcn_exp2f(lse[j] - mc);
-        acc += w * El<E>::widen4(x[j]);
-        wsum += w;
+        const float wt = __builtin_amdgcn_exp2f(lse[j] - mc);
+        acc += wt * El<E>::widen4(x[j]);
+        wsum += wt;
       }
     m = mc;
   }
-  if constexpr (HALVES == 2) {
-    if (te.y <= 1) return;                // uniform: attention wrote o itself
-    // half 1 hands its fold to half 0 through LDS: (m, wsum, acc) per lane
-    __shared__ float xs[DB * 64 * 6];
-    float* x = xs + (db * 64 + lane) * 6;
-    if (half == 1) {
-      x[0] = m;
-      x[1] = wsum;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) x[2 + i] = acc[i];
-    }
-    __syncthreads();
-    if (half == 1) return;
-    const float m1 = x[0];
-    const float mm = fmaxf(m, m1);
-    if (mm != -INFINITY) {
-      const float a0 = __builtin_amdgcn_exp2f(m - mm), a1 = __builtin_amdgcn_exp2f(m1 - mm);
-      wsum = wsum * a0 + x[1] * a1;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = acc[i] * a0 + x[2 + i] * a1;
-    }
-  }
-  if (r16 < te.w) {
-    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.o) + ((size_t)(te.z + r16) * H + h) * D + 16 * db + 4 * g4) =
+  if (n < te.w) {
+    const int d = 32 * (w >> 2) + 8 * (w & 3) + 4 * hh;
+    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.o) + ((size_t)(te.z + n) * H + h) * D + d) =
         El<E>::cvt4(acc * (1.0f / wsum));
   }
 }
@@ -977,22 +789,12 @@ int launch_append(const AppendParams& p, void* s) {
   return (int)hipGetLastError();
 }
 
-// Instantiations by (D, element type).
+// Instantiations by (D, element type).  The 16x16 attention kernel serves
+// head_dim 128; 32 and 64 go to the 32x32 kernel (kvc_attn.hip).
 template <int E, bool SH>
 static int launch_attention_es(const AttnParams& p, int32_t grid, hipStream_t hs) {
-  switch (p.head_dim) {
-    case 32:
-      hipLaunchKernelGGL((attn_kernel<32, E, SH>), dim3(grid), dim3(256), 0, hs, p);
-      break;
-    case 64:
-      hipLaunchKernelGGL((attn_kernel<64, E, SH>), dim3(grid), dim3(256), 0, hs, p);
-      break;
-    case 128:
-      hipLaunchKernelGGL((attn_kernel<128, E, SH>), dim3(grid), dim3(256), 0, hs, p);
-      break;
-    default:
-      return (int)hipErrorInvalidValue;
-  }
+  if (p.head_dim != 128) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL((attn_kernel<128, E, SH>), dim3(grid), dim3(256), 0, hs, p);
   return (int)hipGetLastError();
 }
 
@@ -1008,17 +810,17 @@ int launch_attention(const AttnParams& p, int32_t grid, void* s) {
   return (int)hipErrorInvalidValue;
 }
 
-template <int E, int CH, int HV>
+template <int E, int CH>
 static int launch_merge_ec(const MergeParams& p, int grid, hipStream_t hs) {
   switch (p.head_dim) {
     case 32:
-      hipLaunchKernelGGL((merge_kernel<32, E, CH, HV>), dim3(grid), dim3(64 * 2 * HV), 0, hs, p);
+      hipLaunchKernelGGL((merge_kernel<32, E, CH>), dim3(grid), dim3(64 * 4), 0, hs, p);
       break;
     case 64:
-      hipLaunchKernelGGL((merge_kernel<64, E, CH, HV>), dim3(grid), dim3(64 * 4 * HV), 0, hs, p);
+      hipLaunchKernelGGL((merge_kernel<64, E, CH>), dim3(grid), dim3(64 * 8), 0, hs, p);
       break;
     case 128:
-      hipLaunchKernelGGL((merge_kernel<128, E, CH, HV>), dim3(grid), dim3(64 * 8 * HV), 0, hs, p);
+      hipLaunchKernelGGL((merge_kernel<128, E, CH>), dim3(grid), dim3(64 * 16), 0, hs, p);
       break;
     default:
       return (int)hipErrorInvalidValue;
@@ -1026,21 +828,19 @@ static int launch_merge_ec(const MergeParams& p, int grid, hipStream_t hs) {
   return (int)hipGetLastError();
 }
 
-// Chunk: the smallest of 2, 4, 8 that covers the largest split count, else
-// 8.  Beyond one chunk, a second set of waves takes every other chunk.
+// Chunk: the smallest of 4, 8, 16 that covers the largest split count, else
+// 16 (two or more round trips).
 template <int E>
 static int launch_merge_e(const MergeParams& p, int grid, hipStream_t hs) {
-  if (p.max_split <= 2) return launch_merge_ec<E, 2, 1>(p, grid, hs);
-  if (p.max_split <= 4) return launch_merge_ec<E, 4, 1>(p, grid, hs);
-  if (p.max_split <= 8) return launch_merge_ec<E, 8, 1>(p, grid, hs);
-  return launch_merge_ec<E, 8, 2>(p, grid, hs);
+  if (p.max_split <= 4) return launch_merge_ec<E, 4>(p, grid, hs);
+  if (p.max_split <= 8) return launch_merge_ec<E, 8>(p, grid, hs);
+  return launch_merge_ec<E, 16>(p, grid, hs);
 }
 
 int launch_merge(const MergeParams& p, void* s) {
   const hipStream_t hs = (hipStream_t)s;
   const int grid = KVC_NUM_XCD * p.merge_slots;   // one work-group per merged (query tile, head)
   if (grid == 0) return 0;
-  // one wave per 16-row d block (and per half of the chunks)
   if (p.dtype == 0) return launch_merge_e<0>(p, grid, hs);
   if (p.dtype == 1) return launch_merge_e<1>(p, grid, hs);
   return (int)hipErrorInvalidValue;

@@ -49,10 +49,10 @@ static void check_plan(const Config& c, const Allocator& a, const HostPlan& p, c
     int64_t slots = 0;
     for (int32_t u = 0; u < r.n_units; ++u) {
       const int32_t* e = &p.image[(size_t)r.unit0 + (size_t)KVC_UNIT_INTS * u];
-      const uint64_t off = (uint64_t)(uint32_t)e[0] | ((uint64_t)(uint32_t)e[1] << 32);
-      const int32_t valid = e[2];
-      CHECK(off % slot_bytes == 0, "%s: unit %d offset not slot-aligned", where.c_str(), u);
-      const uint64_t slot = off / slot_bytes;                 // slot index in [page][kv][slot]
+      const uint64_t slot = (uint32_t)e[0];                   // slot index in [page][kv][slot]
+      const int32_t valid = e[1];
+      CHECK(e[2] == 0 && e[3] == 0, "%s: unit %d padding", where.c_str(), u);
+      const uint64_t off = slot * slot_bytes;
       const uint64_t page = slot / (2 * (uint64_t)c.page_size);
       const uint64_t in_page = slot % (2 * (uint64_t)c.page_size);
       CHECK(page < (uint64_t)c.max_num_pages(), "%s: unit %d page %llu out of pool", where.c_str(), u,

@@ -160,8 +160,8 @@ def test_r518_padded_pages_and_poisoned_slots():
             compare_plan(res)
             st = check_close(res["out_bits"][0], res["ref"][0])
             log(f"r518 step {t}: splits {res['gpu_plan']['n_splits']} {st}")
-    # the full-size step runs the kernel without a shared tile (groups of 8)
-    assert h.gpu.get_plan_shape() == {"work_items": 512, "group_tiles": 8}
+    # the full-size step runs the 32x32 kernel without a tail (4 groups of 8 tiles)
+    assert h.gpu.get_plan_shape() == {"work_items": 256, "group_rows": 256}
     before = res["out_bits"][0]
     plan = res["gpu_plan"]
     pool = h.gpu.pools[0]

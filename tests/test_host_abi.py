@@ -357,42 +357,60 @@ def _units_and_qtiles(wl, p):
     return units, qtiles
 
 
+def _groups_of_plan(c, n):
+    """Per stream (n_group, n_t32) from the plan image's stream records
+    (20 ints each after an 8-int header; n_group at 10, n_t32 at 16)."""
+    img = c.get_plan_image()
+    recs = [img[8 + 20 * i: 8 + 20 * (i + 1)] for i in range(n)]
+    return [int(r[10]) for r in recs], [int(r[16]) for r in recs], int(img[5])
+
+
 @pytest.mark.parametrize("name", ["base", "r518", "frag"])
 def test_split_counts_fill_one_round(name):
     """The planner's split counts keep every attention work-group of a run
-    resident at once (at most the target count, which defaults to what the
-    device holds: 2 per CU up to D = 64, 1 at D = 128), and the stream with
-    the longest splits, which sets the launch's length, could not take one
-    more split that shortens them and still fit."""
+    resident at once (at most the target count, which defaults to one per
+    CU), and the stream with the longest splits (units per split times its
+    busiest wave's tile-steps per unit), which sets the launch's length,
+    could not take one more split that shortens them and still fit."""
     wl, c = _plan_at_measured_step(name)
     p = c.get_plan()
     shape = c.get_plan_shape()
     target = c.get_option(kvc.KVC_OPT_TARGET_WORKGROUPS)
-    assert target == (2 if wl.head_dim <= 64 else 1) * 256   # the CU count a metadata-only context assumes
+    assert target == 256   # the CU count a metadata-only context assumes
     ceil = lambda a, b: -(-a // b)
-    units, qtiles = _units_and_qtiles(wl, p)
-    groups = [wl.num_heads * ceil(q, shape["group_tiles"]) for q in qtiles]
+    units, _ = _units_and_qtiles(wl, p)
+    n_group, n_t32, shared = _groups_of_plan(c, len(units))
+    heads = [wl.num_heads * g for g in n_group]
     ns = [int(x) for x in p["n_splits"]]
-    items = sum(g * n for g, n in zip(groups, ns))
+    items = sum(g * n for g, n in zip(heads, ns))
     assert items == shape["work_items"] <= target
-    lens = [ceil(u, n) for u, n in zip(units, ns)]
+
+    def per_unit(i):
+        if wl.head_dim > 64:
+            return 2.25 if shared else 2.0
+        kmax = ceil(n_t32[i], n_group[i])
+        return 2.0 * (kmax > 0) + 2.0 * (kmax > 4) + 0.25 * shared
+
+    lens = [ceil(u, n) * per_unit(i) for i, (u, n) in enumerate(zip(units, ns))]
     i = lens.index(max(lens))
-    u, g, n = units[i], groups[i], ns[i]
+    u, g, n = units[i], heads[i], ns[i]
     if n < min(kvc.MAX_SPLITS, u) and ceil(u, n + 1) < ceil(u, n):
         assert items + g > target, (name, i, ns)
 
 
 def test_query_grouping_choice():
-    """Groups of 9 query tiles (the ninth shared by the four waves, a quarter
-    tile more per wave and stage) against groups of 8: the 262-query frame
-    (17 tiles) keeps the shared tile, the 1005-query frame of the 999-patch
-    workload (63 tiles) takes groups of 8, which fill all 512 work-groups with
-    4 splits instead of 448 and drop the quarter tile."""
+    """A group of the 32x32 kernel is 4 waves x 2 tiles of 32 rows, plus, in
+    a launch of the shared variant, a 16-row tail that the waves share (a
+    quarter tile-step more per wave and unit).  The 262-query frame (8 full
+    tiles and 6 rows) takes the tail: one group per head, 16 splits over 256
+    work-groups, where 9 tiles would need two groups and half the splits.
+    The 1005-query frame of the 999-patch workload (31 tiles and 13 rows)
+    rounds up to 32 tiles: 4 groups of 8, 4 splits, no tail."""
     _, c = _plan_at_measured_step("base")
-    assert c.get_plan_shape() == {"work_items": 512, "group_tiles": 9}
+    assert c.get_plan_shape() == {"work_items": 256, "group_rows": 272}
     assert list(c.get_plan()["n_splits"]) == [16]
     _, c = _plan_at_measured_step("r518")
-    assert c.get_plan_shape() == {"work_items": 512, "group_tiles": 8}
+    assert c.get_plan_shape() == {"work_items": 256, "group_rows": 256}
     assert list(c.get_plan()["n_splits"]) == [4]
 
 

@@ -19,23 +19,51 @@ import paged_kv_cache_kvc_amd as kvc
 from tests.stream_harness import edge_workloads
 from tests.test_host_abi import cfg_of, free_orders
 
-HEADER, REC, UNIT, MERGE, KV_TILE, Q_TILE, XCD, WAVES = 8, 16, 4, 4, 64, 16, 8, 4
+HEADER, REC, UNIT, MERGE, KV_TILE, XCD = 8, 20, 4, 4, 64, 8
+Q_TILE32, TAIL_ROWS, WAVES32, Q_TILE16 = 32, 16, 4, 16
 REC_FIELDS = ("q_row0", "n_q", "page0", "n_patch", "n_pages", "last_len", "kv_len", "unit0", "n_units",
-              "n_split", "n_group", "item0", "n_items", "upp", "ups", "q_tile0")
+              "n_split", "n_group", "item0", "n_items", "upp", "ups", "q_tile0", "n_t32", "tail",
+              "reserved0", "reserved1")
+
+
+def expected_grouping(wl, n_q, shared):
+    """(n_group, n_t32, tail) of a stream with n_q query rows.  Up to D = 64
+    a group is 4 waves x 2 tiles of 32 rows; with the shared variant, rows
+    past the last full tile form a 16-row tail of the last group when there
+    are at most 16 of them.  At D = 128 a group is 8 tiles of 16 rows, or 9
+    with the shared variant."""
+    if wl.head_dim <= 64:
+        rem = n_q % Q_TILE32
+        tail = 1 if shared and 1 <= rem <= TAIL_ROWS else 0
+        nt = n_q // Q_TILE32 if tail else -(-n_q // Q_TILE32)
+        return max(1, -(-nt // (2 * WAVES32))), nt, tail
+    return -(-(-(-n_q // Q_TILE16)) // (9 if shared else 8)), 0, 0
+
+
+def merge_group(wl, r, t):
+    """The query group that computes (the first rows of) 32-row tile t."""
+    if wl.head_dim <= 64:
+        if t >= r["n_t32"]:
+            return r["n_group"] - 1
+        return next(g for g in range(r["n_group"]) if t < (g + 1) * r["n_t32"] // r["n_group"])
+    nqt = -(-r["n_q"] // Q_TILE16)
+    return next(g for g in range(r["n_group"]) if 2 * t < (g + 1) * nqt // r["n_group"])
 
 
 def check_image(wl, c):
     img = c.get_plan_image().astype(np.int64)
     plan = c.get_plan()
     shape = c.get_plan_shape()
-    H, D, pg = wl.num_heads, wl.head_dim, wl.page_size
+    H, pg = wl.num_heads, wl.page_size
     P = wl.tokens_per_frame - wl.num_special_tokens
-    slot_bytes = H * D * 2
-    page_bytes = 2 * pg * slot_bytes
     n_streams, n_items, n_rows, any_split, n_tiles, shared, merge_at, merge_slots = (int(x) for x in img[:HEADER])
     n = len(plan["planned"])
     assert n_streams == n
-    assert shared == (1 if shape["group_tiles"] == 9 else 0)
+    assert shared in (0, 1)
+    if wl.head_dim <= 64:
+        assert shape["group_rows"] == 2 * WAVES32 * Q_TILE32 + (TAIL_ROWS if shared else 0)
+    else:
+        assert shape["group_rows"] == (9 if shared else 8) * Q_TILE16
     assert n_items == shape["work_items"]
     assert n_rows == plan["qo_indptr"][-1]
     recs = [dict(zip(REC_FIELDS, (int(x) for x in img[HEADER + REC * i: HEADER + REC * (i + 1)]))) for i in range(n)]
@@ -49,6 +77,7 @@ def check_image(wl, c):
         assert r["n_pages"] == plan["kv_indptr"][i + 1] - plan["kv_indptr"][i]
         assert r["n_patch"] == plan["n_patch_pages"][i] and r["last_len"] == plan["last_page_len"][i]
         assert r["n_split"] == plan["n_splits"][i]
+        assert r["reserved0"] == r["reserved1"] == 0
         # units: in table order, page by page, 64-slot chunks of each page's valid slots
         pages = plan["kv_indices"][r["page0"]: r["page0"] + r["n_pages"]]
         expect = []
@@ -59,30 +88,32 @@ def check_image(wl, c):
         assert r["unit0"] % 4 == 0
         got = []
         for u in range(r["n_units"]):
-            lo, hi, valid, pad = (int(x) for x in img[r["unit0"] + UNIT * u: r["unit0"] + UNIT * (u + 1)])
-            off = (lo & 0xFFFFFFFF) | (hi << 32)
-            page, rem = divmod(off, page_bytes)
-            slot, byte = divmod(rem, slot_bytes)
-            assert byte == 0 and slot < pg and pad == 0     # a K row of head 0, V at + pg rows
-            got.append((page, slot, valid))
+            slot, valid, z0, z1 = (int(x) for x in img[r["unit0"] + UNIT * u: r["unit0"] + UNIT * (u + 1)])
+            page, s = divmod(slot & 0xFFFFFFFF, 2 * pg)   # pool rows [page][K, V][page_size]
+            assert s < pg and z0 == z1 == 0
+            got.append((page, s, valid))
         assert got == expect
         assert sum(v for _, _, v in got) == r["kv_len"]
         # work items: heads x splits x query groups, every split non-empty
-        nqt = math.ceil(r["n_q"] / Q_TILE)
-        assert r["n_group"] == math.ceil(nqt / shape["group_tiles"])
-        assert all((g + 1) * nqt // r["n_group"] - g * nqt // r["n_group"] <= shape["group_tiles"]
-                   for g in range(r["n_group"]))
-        assert 1 <= r["n_split"] <= min(kvc.MAX_SPLITS, r["n_units"])
+        assert (r["n_group"], r["n_t32"], r["tail"]) == expected_grouping(wl, r["n_q"], shared)
+        if wl.head_dim <= 64:
+            assert all((g + 1) * r["n_t32"] // r["n_group"] - g * r["n_t32"] // r["n_group"] <= 2 * WAVES32
+                       for g in range(r["n_group"]))
+            assert 32 * r["n_t32"] + (TAIL_ROWS if r["tail"] else 0) >= r["n_q"] > 32 * r["n_t32"] - 32
+        assert 1 <= r["n_split"] <= r["n_units"]
+        assert r["n_split"] <= kvc.MAX_SPLITS or -(-r["n_units"] // kvc.MAX_SPLITS) > 512
+        if wl.head_dim <= 64:
+            assert -(-r["n_units"] // r["n_split"]) <= 512   # a split's entries fit the kernel's LDS table
         bounds = [s * r["n_units"] // r["n_split"] for s in range(r["n_split"] + 1)]
         assert all(b1 > b0 for b0, b1 in zip(bounds, bounds[1:])) and bounds[-1] == r["n_units"]
         assert r["item0"] == item and r["n_items"] == H * r["n_split"] * r["n_group"]
         assert r["q_tile0"] == tiles
         item += r["n_items"]
-        tiles += nqt
+        tiles += -(-r["n_q"] // Q_TILE32)
         if r["n_split"] > 1:
             split_streams.add(i)
     assert item == n_items and tiles == n_tiles and any_split == (1 if split_streams else 0)
-    # merge order
+    # merge order: one entry per (32-row tile, head) of a split stream
     assert merge_at % 4 == 0 and len(img) == merge_at + MERGE * XCD * merge_slots
     ipx = -(-n_items // XCD)
     seen = {}
@@ -96,14 +127,13 @@ def check_image(wl, c):
     want = {}
     for i in split_streams:
         r = recs[i]
-        nqt = math.ceil(r["n_q"] / Q_TILE)
-        for t in range(nqt):
-            grp = next(g for g in range(r["n_group"]) if t < (g + 1) * nqt // r["n_group"])
+        for t in range(-(-r["n_q"] // Q_TILE32)):
+            grp = merge_group(wl, r, t)
             for h in range(H):
                 mid = r["item0"] + (h * r["n_split"] + r["n_split"] // 2) * r["n_group"] + grp
                 want[(r["q_tile0"] + t) * H + h] = (min(mid // max(1, ipx), XCD - 1),
-                                                    [r["n_split"], r["q_row0"] + Q_TILE * t,
-                                                     min(Q_TILE, r["n_q"] - Q_TILE * t)])
+                                                    [r["n_split"], r["q_row0"] + Q_TILE32 * t,
+                                                     min(Q_TILE32, r["n_q"] - Q_TILE32 * t)])
     assert seen == want
 
 
@@ -173,14 +203,13 @@ def test_plan_image_check_catches_corruption():
     unit0 = int(good[rec0 + REC_FIELDS.index("unit0")])
     merge_at, merge_slots = int(good[6]), int(good[7])
     first_merge = next(merge_at + MERGE * k for k in range(XCD * merge_slots) if good[merge_at + MERGE * k] >= 0)
-    slot_bytes = wl.num_heads * wl.head_dim * 2
 
     def corrupt(i, delta):
         bad = good.copy()
         bad[i] += delta
         return bad
 
-    cases = [corrupt(unit0, slot_bytes), corrupt(unit0 + 2, -1), corrupt(rec0 + REC_FIELDS.index("item0"), 1),
+    cases = [corrupt(unit0, 1), corrupt(unit0 + 2, -1), corrupt(rec0 + REC_FIELDS.index("item0"), 1),
              corrupt(first_merge + 1, 1), corrupt(first_merge + 2, 16)]
     missing = good.copy()
     missing[first_merge] = -1
