@@ -84,9 +84,12 @@ struct Shape32 {
   static constexpr int TDB = D / 16;                   // tail: 16-row blocks of O^T
   static constexpr int HALF = KVC_KV_TILE * ROW_BYTES; // K (or V) part of a stage
   static constexpr int STAGE = 2 * HALF;
-  static constexpr int NSTAGE = 6;                     // ring stages; NSTAGE - 2 are loaded ahead
+  static constexpr int NSTAGE = 128 * 1024 / STAGE;    // ring of 128 KiB: 8 stages (D = 64), 16 (D = 32);
+                                                       // NSTAGE - 2 stay in flight
   static constexpr int LOADS = STAGE / 1024;           // 1 KiB direct-to-LDS loads per stage
   static constexpr int LPW = LOADS / KVC_ATTN32_WAVES;
+  static constexpr int QT = 32 * ROW_BYTES / 1024;     // loads per 32-row query tile
+  static constexpr int TQ = 16 * ROW_BYTES / 1024;     // loads per 16-row tail
 };
 
 // 16-byte chunk swizzle inside a K/V row of LDS, XORed into the chunk index.
@@ -261,21 +264,36 @@ __device__ __forceinline__ float renorm16(const f32x4& s, float sl, int& fresh, 
 }
 
 // Barrier that first waits for the wave's LDS reads: after it, other waves'
-// direct-to-LDS loads may refill the ring slot those reads came from.
+// direct-to-LDS loads may refill the ring slots those reads came from.
 __device__ __forceinline__ void ring_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Wait until at most `a` stages (LPW loads each) of the wave's direct-to-LDS
+// loads are outstanding (a <= A; vmcnt takes an immediate).
+template <int LPW, int A>
+__device__ __forceinline__ void wait_ahead(int a) {
+  if constexpr (A == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (a >= A)
+      wait_vmcnt<A * LPW>();
+    else
+      wait_ahead<LPW, A - 1>(a);
+  }
+}
 
 template <int D, int E, bool TAIL>
 __global__ __launch_bounds__(64 * KVC_ATTN32_WAVES, 1) void attn32_kernel(AttnParams p) {
   using S = Shape32<D>;
   using MM = M32<E>;
   constexpr int KS = S::KS, DB = S::DB, TKS = S::TKS, TDB = S::TDB, LPW = S::LPW, NST = S::NSTAGE;
-  // LDS: the ring of K/V stages; each wave's query operands in register
-  // order (tile A, tile B, tail: one 1 KiB block per k-step, lane l at 16 l,
-  // so every read is one conflict-free 1 KiB row); the split's unit entries.
-  constexpr int QBLK = 2 * KS + (TAIL ? TKS : 0);
+  // LDS: the ring of K/V stages and the split's unit entries.  Before the
+  // loop the last three ring slots stage the query operands: per wave its
+  // tiles A and B and a copy of the tail, row-major.
+  constexpr int QW = (2 * S::QT + (TAIL ? S::TQ : 0)) * 1024;
+  static_assert(KVC_ATTN32_WAVES * QW <= 3 * S::STAGE, "query staging fits three ring slots");
+  constexpr int P0 = NST - 3;   // stages loaded before the query operands are read
   __shared__ __attribute__((aligned(1024))) uint8_t ring[NST * S::STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t qlds[KVC_ATTN32_WAVES * QBLK * 1024];
-  __shared__ int2 elds[KVC_MAX_SPLIT_STAGES];
+  __shared__ __attribute__((aligned(1024))) int4 elds[KVC_MAX_SPLIT_STAGES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -316,63 +334,21 @@ __global__ __launch_bounds__(64 * KVC_ATTN32_WAVES, 1) void attn32_kernel(AttnPa
   const uint64_t head_off = (uint64_t)hd * D * 2;
   const float sl = p.scale_log2;
 
-  // This split's unit entries (the host planner resolved pages, chunks and
-  // valid lengths), copied once to LDS; each stage reads its own entry from
-  // there, so the stage loop issues no global memory operation besides its
+  // Unit entries (the host planner resolved pages, chunks and valid
+  // lengths): those of the first stages by scalar loads, ahead of every
+  // other memory operation; all of them copied to LDS by direct loads for the
+  // stage loop, which then issues no global memory operation besides its
   // direct-to-LDS loads (whose completion it counts with vmcnt).
-  for (int u = tid; u < nstage; u += 64 * KVC_ATTN32_WAVES)
-    elds[u] = *reinterpret_cast<const int2*>(units + KVC_UNIT_INTS * u);
+  int2 e_first[P0];
+#pragma unroll
+  for (int i = 0; i < P0; ++i)
+    e_first[i] = i < nstage ? int2{units[KVC_UNIT_INTS * i], units[KVC_UNIT_INTS * i + 1]} : int2{0, KVC_KV_TILE};
   // entry of stage i (uniform): slot index of its first K row, valid slots
   auto stage_entry = [&](int i) {
-    const int2 e = elds[i];
+    const int4 e = elds[i];
     return int2{__builtin_amdgcn_readfirstlane(e.x), __builtin_amdgcn_readfirstlane(e.y)};
   };
   auto stage_entry_valid = [&](int i) { return __builtin_amdgcn_readfirstlane(elds[i].y); };
-
-  // ---- query operands (B of S^T = K Q^T), staged in LDS ----
-  // tile: lane (n, h) holds q[row n][16 ks + 8h .. + 8) for each k-step
-  uint8_t* qw = qlds + wv * QBLK * 1024 + lane * 16;
-  auto stage_q32 = [&](int tile, bool ok, int blk0) {
-    const int row = 32 * tile + n;
-    ok = ok && row < st.n_q;
-    const uint16_t* qr = static_cast<const uint16_t*>(p.q) + ((size_t)(st.q_row0 + (ok ? row : 0)) * H + hd) * D;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      u32x4 v = *reinterpret_cast<const u32x4*>(qr + 16 * ks + 8 * h);
-      if (!ok) v = u32x4{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(qw + (blk0 + ks) * 1024) = v;
-    }
-  };
-  stage_q32(t_lo + wv, wv < ntile, 0);
-  stage_q32(t_lo + wv + 4, wv + 4 < ntile, KS);
-  const int tail_row0 = 32 * st.n_t32;
-  if constexpr (TAIL) {
-    // tail: lane (r16, g4) holds q[row r16][32 tks + 8 g4 .. + 8)
-    const int row = tail_row0 + r16;
-    const bool ok = has_tail && row < st.n_q;
-    const uint16_t* qr = static_cast<const uint16_t*>(p.q) + ((size_t)(st.q_row0 + (ok ? row : 0)) * H + hd) * D;
-#pragma unroll
-    for (int k = 0; k < TKS; ++k) {
-      u32x4 v = *reinterpret_cast<const u32x4*>(qr + 32 * k + 8 * g4);
-      if (!ok) v = u32x4{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(qw + (2 * KS + k) * 1024) = v;
-    }
-  }
-  auto read_q = [&](int blk) { return *reinterpret_cast<const bf16x8*>(qw + blk * 1024); };
-
-  // ---- softmax state: ref (log2 units) and its negation, running sum, and
-  // fresh (no valid slot seen yet) per tile ----
-  float refA = 0.f, refB = 0.f, refT = 0.f, nrefA = 0.f, nrefB = 0.f, nrefT = 0.f;
-  float lA = 0.f, lB = 0.f, lT = 0.f;
-  int freshA = 1, freshB = 1, freshT = 1;
-  f32x16 oA[DB], oB[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) oA[db][e] = oB[db][e] = 0.f;
-  f32x4 oT[TDB];
-#pragma unroll
-  for (int db = 0; db < TDB; ++db) oT[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // ---- direct global -> LDS loads of one stage (K rows, then V rows) ----
   // Load instruction j of the wave fills 1 KiB at LDS byte 1024 * (wave *
@@ -396,31 +372,73 @@ __global__ __launch_bounds__(64 * KVC_ATTN32_WAVES, 1) void attn32_kernel(AttnPa
   const uint32_t lofs1 =
       RPL == 8 ? (uint32_t)lrow0 * slot_bytes + (uint32_t)(((lane % CPR) ^ swz32<D>(lrow0 + 8)) << 4) : lofs0;
   const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(lds_addr(ring));
-  auto issue = [&](int sidx) {
-    const int2 e = stage_entry(sidx);
-    const uint64_t koff = (uint64_t)(uint32_t)e.x * slot_bytes + head_off;
+  // per load j of this wave: offset of its first row from the unit's first K
+  // row (K or V half) and its LDS offset in a stage (uniform)
+  uint64_t jofs[LPW];
+  uint32_t jlds[LPW];
+  int jrow[LPW];
+#pragma unroll
+  for (int j = 0; j < LPW; ++j) {
+    const int inst = wv * LPW + j;
+    const int kv = inst >= S::LOADS / 2 ? 1 : 0;
+    const int blk = inst - kv * (S::LOADS / 2);
+    jrow[j] = RPL * blk;
+    jofs[j] = (kv ? v_half : 0) + (uint64_t)(RPL * blk) * slot_bytes;
+    jlds[j] = (uint32_t)(kv * S::HALF + blk * 1024);
+  }
+  auto issue_e = [&](int sidx, int2 e) {
+    const uint8_t* ubase = pool + (uint64_t)(uint32_t)e.x * slot_bytes + head_off;
     const int valid = e.y;
     const uint32_t slot = ring_lds + (uint32_t)(sidx % NST) * S::STAGE;
+    if (__builtin_expect(valid >= KVC_KV_TILE, 1)) {
 #pragma unroll
-    for (int j = 0; j < LPW; ++j) {
-      const int inst = wv * LPW + j;
-      const int kv = inst >= S::LOADS / 2 ? 1 : 0;
-      const int blk = inst - kv * (S::LOADS / 2);
-      int row0 = RPL * blk;                       // first row of this load (uniform)
-      const uint32_t lofs = (j & 1) ? lofs1 : lofs0;
-      uint32_t o = lofs;
-      // partial stage (rare): rows past the valid count re-read the last valid
-      // row.  The offset is an unsigned 32-bit addend of the scalar base, so
-      // the row is measured from the unit's first row, never below it.
-      if (__builtin_expect(valid < KVC_KV_TILE, 0)) {
-        const int row = row0 + lrow0;
-        o = lofs + (uint32_t)(min(row, valid - 1) - lrow0) * slot_bytes;
-        row0 = 0;
+      for (int j = 0; j < LPW; ++j) load_lds16(ubase + jofs[j], (j & 1) ? lofs1 : lofs0, slot + jlds[j]);
+    } else {
+      // partial stage (rare): rows past the valid count re-read the last
+      // valid row.  The offset is an unsigned 32-bit addend of the scalar
+      // base, so the row is measured from the unit's first row, never below it.
+#pragma unroll
+      for (int j = 0; j < LPW; ++j) {
+        const int row = jrow[j] + lrow0;
+        const uint32_t o = ((j & 1) ? lofs1 : lofs0) + (uint32_t)(min(row, valid - 1) - lrow0) * slot_bytes;
+        load_lds16(ubase + (jofs[j] - (uint64_t)jrow[j] * slot_bytes), o, slot + jlds[j]);
       }
-      load_lds16(pool + koff + (kv ? v_half : 0) + (uint64_t)row0 * slot_bytes, o,
-                 __builtin_amdgcn_readfirstlane(slot + (uint32_t)(kv * S::HALF + blk * 1024)));
     }
   };
+  auto issue = [&](int sidx) { issue_e(sidx, stage_entry(sidx)); };
+
+  // ---- prologue loads, in the order the vmcnt accounting assumes ----
+  // (1) query rows (RPL per load, row-major) into the staging slots; rows
+  // past the stream's queries repeat its last row (their columns are never
+  // stored)
+  const uint32_t qlds = ring_lds + (uint32_t)((NST - 3) * S::STAGE + wv * QW);
+  const uint8_t* qsrc = static_cast<const uint8_t*>(p.q) + ((size_t)st.q_row0 * H + hd) * D * 2;
+  auto q_dma = [&](int row0, int nload, uint32_t lds0) {
+    const int r0 = min(row0, st.n_q - 1);
+#pragma unroll
+    for (int i = 0; i < nload; ++i) {
+      const int row = min(row0 + RPL * i + lrow0, st.n_q - 1);
+      load_lds16(qsrc + (size_t)r0 * slot_bytes, (uint32_t)(row - r0) * slot_bytes + (uint32_t)((lane % CPR) << 4),
+                 __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(i * 1024)));
+    }
+  };
+  q_dma(32 * (t_lo + wv), S::QT, qlds);
+  q_dma(32 * (t_lo + wv + 4), S::QT, qlds + S::QT * 1024);
+  if constexpr (TAIL) q_dma(32 * st.n_t32, S::TQ, qlds + 2 * S::QT * 1024);
+  // (2) unit entries, 64 per load, by the waves in turn (lanes past the
+  // split's count repeat its last entry)
+  {
+    const uint32_t elds_lds = __builtin_amdgcn_readfirstlane(lds_addr(elds));
+    const int nblk = (nstage + 63) / 64;
+    for (int b = wv; b < nblk; b += KVC_ATTN32_WAVES)
+      load_lds16(units, (uint32_t)min(64 * b + lane, nstage - 1) * 16,
+                 __builtin_amdgcn_readfirstlane(elds_lds + (uint32_t)(b * 1024)));
+  }
+  // (3) the first stages
+  const int pre = min(nstage, P0);
+#pragma unroll
+  for (int i = 0; i < P0; ++i)
+    if (i < pre) issue_e(i, e_first[i]);
 
   // ---- LDS operand offsets (per lane; stage base added at the read) ----
   uint32_t kofs[KS];          // K rows (A of S^T): row kperm(n) of each 32-slot block, chunk 2ks + h
@@ -468,87 +486,102 @@ __global__ __launch_bounds__(64 * KVC_ATTN32_WAVES, 1) void attn32_kernel(AttnPa
       for (int ks = 0; ks < KS; ++ks)
         kop[sb][ks] = *reinterpret_cast<const bf16x8*>(b + kofs[ks] + 32 * sb * S::ROW_BYTES);
   };
-  // tail operands of step X: K(s) and V(s-1) (both ring slots still hold
-  // their stages until the barrier that follows step X)
-  auto read_tail = [&](int s) {
-    const uint8_t* bk = ring + (s % NST) * S::STAGE;
-    const uint8_t* bv = ring + ((s + NST - 1) % NST) * S::STAGE;
-#pragma unroll
-    for (int k = 0; k < TKS; ++k) tk[k] = *reinterpret_cast<const bf16x8*>(bk + tkofs[k]);
-#pragma unroll
-    for (int db = 0; db < TDB; ++db) tv[db] = __builtin_bit_cast(bf16x4, ds_read_tr16(bv + tvofs[db]));
-  };
-  auto read_v = [&](int sidx) {
+  // one operand register of K (i = sb * KS + ks) or of V^T (i = t * DB + db)
+  auto read_k1 = [&](int sidx, int i) {
     const uint8_t* b = ring + (sidx % NST) * S::STAGE;
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const i16x4 x0 = ds_read_tr16(b + vofs[db][0] + 16 * t * S::ROW_BYTES);
-        const i16x4 x1 = ds_read_tr16(b + vofs[db][1] + 16 * t * S::ROW_BYTES);
-        vop[t][db] = __builtin_bit_cast(
-            bf16x8, (short __attribute__((ext_vector_type(8)))){x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]});
-      }
+    kop[i / KS][i % KS] = *reinterpret_cast<const bf16x8*>(b + kofs[i % KS] + 32 * (i / KS) * S::ROW_BYTES);
   };
-
-  const bf16x8 mask = rowsum_mask<E>(lane);
-  auto qk32 = [&](int qblk0, f32x16 (&s)[2]) {
-    bf16x8 q[KS];
+  auto read_v1 = [&](int sidx, int i) {
+    const uint8_t* b = ring + (sidx % NST) * S::STAGE;
+    const int t = i / DB, db = i % DB;
+    const i16x4 x0 = ds_read_tr16(b + vofs[db][0] + 16 * t * S::ROW_BYTES);
+    const i16x4 x1 = ds_read_tr16(b + vofs[db][1] + 16 * t * S::ROW_BYTES);
+    vop[t][db] = __builtin_bit_cast(
+        bf16x8, (short __attribute__((ext_vector_type(8)))){x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]});
+  };
+  // tail operands: its 16 K rows of stage s, its 16 V rows of stage s
+  auto read_tk = [&](int s) {
+    const uint8_t* b = ring + (s % NST) * S::STAGE;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) q[ks] = read_q(qblk0 + ks);
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      s[sb] = MM::mfma32(kop[sb][0], q[0], f32x16{});
-#pragma unroll
-      for (int ks = 1; ks < KS; ++ks) s[sb] = MM::mfma32(kop[sb][ks], q[ks], s[sb]);
+    for (int k = 0; k < TKS; ++k) tk[k] = *reinterpret_cast<const bf16x8*>(b + tkofs[k]);
+  };
+  auto read_tv1 = [&](int s, int i) {   // i < TDB; more than TDB does nothing
+    if (i < TDB) {
+      const uint8_t* b = ring + (s % NST) * S::STAGE;
+      tv[i] = __builtin_bit_cast(bf16x4, ds_read_tr16(b + tvofs[i]));
     }
   };
-  auto pv32 = [&](const u32x4 (&pk)[4], f32x16 (&o)[DB]) {
+
+
+  // ---- softmax state: ref (log2 units) and its negation, running sum, and
+  // fresh (no valid slot seen yet) per tile ----
+  float refA = 0.f, refB = 0.f, refT = 0.f, nrefA = 0.f, nrefB = 0.f, nrefT = 0.f;
+  float lA = 0.f, lB = 0.f, lT = 0.f;
+  int freshA = 1, freshB = 1, freshT = 1;
+  f32x16 oA[DB], oB[DB];
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] = MM::mfma32(vop[t][db], __builtin_bit_cast(bf16x8, pk[t]), o[db]);
-  };
+    for (int e = 0; e < 16; ++e) oA[db][e] = oB[db][e] = 0.f;
+  f32x4 oT[TDB];
+#pragma unroll
+  for (int db = 0; db < TDB; ++db) oT[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const bf16x8 mask = rowsum_mask<E>(lane);
+  f32x16 sA[2], sB[2];
+  u32x4 pA[4], pB[4];
+  f32x4 rsA, rsB, sT;
+  u32x2 pT = u32x2{0u, 0u};
+  float ltT = 0.f;
   auto rowsum = [&](const u32x4 (&pk)[4]) {
     f32x4 r = El<E>::mfma(mask, __builtin_bit_cast(bf16x8, pk[0]), f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
     for (int t = 1; t < 4; ++t) r = El<E>::mfma(mask, __builtin_bit_cast(bf16x8, pk[t]), r);
     return r;
   };
-  auto qk16 = [&](f32x4& s) {
-    s = El<E>::mfma(tk[0], read_q(2 * KS), f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-    for (int k = 1; k < TKS; ++k) s = El<E>::mfma(tk[k], read_q(2 * KS + k), s);
-  };
-  auto pv16 = [&](const u32x2& pk) {
-#pragma unroll
-    for (int db = 0; db < TDB; ++db) oT[db] = MM::mfma16x16(tv[db], __builtin_bit_cast(bf16x4, pk), oT[db]);
+  // chunk c (0..15) of a 32x32 tile's probabilities: P^T operand t = c / 4, pair c % 4
+  auto prob_chunk = [&](const f32x16 (&s)[2], float nref, u32x4 (&pk)[4], int c) {
+    const int t = c >> 2, k = c & 3, e = 8 * (t & 1) + 2 * k;
+    pk[t][k] = El<E>::pack_p(__builtin_amdgcn_exp2f(__builtin_fmaf(s[t >> 1][e], sl, nref)),
+                             __builtin_amdgcn_exp2f(__builtin_fmaf(s[t >> 1][e + 1], sl, nref)));
   };
 
-  f32x16 sA[2], sB[2];
-  u32x4 pA[4], pB[4];
-  f32x4 rsA, rsB, sT;
-  u32x2 pT = u32x2{0u, 0u};
-  float ltT = 0.f;
-
-  // ---- prologue: the first NST - 1 stages loaded, stage 0 published ----
-  __syncthreads();   // unit entries and query operands staged
+  // ---- prologue: query operands and stage 0 ----
+  wait_ahead<LPW, P0 - 1>(pre - 1);   // queries, entries and stage 0 landed (own loads)
+  block_barrier();                    // ... and everyone's
+  bf16x8 qA[KS], qB[KS], qT[TKS];
   {
-    const int pre = min(nstage, NST - 1);
-    for (int i = 0; i < pre; ++i) issue(i);
-    switch (pre) {   // stage 0 complete: the later stages' loads may still fly
-      case 5: wait_vmcnt<4 * LPW>(); break;
-      case 4: wait_vmcnt<3 * LPW>(); break;
-      case 3: wait_vmcnt<2 * LPW>(); break;
-      case 2: wait_vmcnt<1 * LPW>(); break;
-      default: wait_vmcnt<0>(); break;
+    // tile: lane (n, h) holds q[row n][16 ks + 8h .. + 8); tail: lane (r16,
+    // g4) holds q[row r16][32 k + 8 g4 .. + 8)
+    const uint8_t* qw = ring + (NST - 3) * S::STAGE + wv * QW;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qA[ks] = *reinterpret_cast<const bf16x8*>(qw + n * S::ROW_BYTES + (2 * ks + h) * 16);
+      qB[ks] = *reinterpret_cast<const bf16x8*>(qw + S::QT * 1024 + n * S::ROW_BYTES + (2 * ks + h) * 16);
+    }
+    if constexpr (TAIL) {
+#pragma unroll
+      for (int k = 0; k < TKS; ++k)
+        qT[k] = *reinterpret_cast<const bf16x8*>(qw + 2 * S::QT * 1024 + r16 * S::ROW_BYTES + (4 * k + g4) * 16);
     }
   }
-  block_barrier();
   read_k(0);
-  qk32(0, sA);
+  if constexpr (TAIL) {
+    read_tk(0);
+#pragma unroll
+    for (int db = 0; db < TDB; ++db) tv[db] = __builtin_bit_cast(bf16x4, u32x2{0u, 0u});
+  }
+  // every wave has its query operands: the staging slots take stages P0 ..
+  ring_barrier();
+  for (int i = P0; i < min(nstage, NST - 1); ++i) issue(i);
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb) {
+    sA[sb] = MM::mfma32(kop[sb][0], qA[0], f32x16{});
+#pragma unroll
+    for (int ks = 1; ks < KS; ++ks) sA[sb] = MM::mfma32(kop[sb][ks], qA[ks], sA[sb]);
+  }
   {
-    const int v0 = stage_entry_valid(0);
+    const int v0 = e_first[0].y;
     if (v0 < KVC_KV_TILE) mask32(sA, v0, h);
   }
   // "stage -1" of tile B and of the tail: all slots masked, zero operands;
@@ -566,10 +599,25 @@ __global__ __launch_bounds__(64 * KVC_ATTN32_WAVES, 1) void attn32_kernel(AttnPa
   rsB = f32x4{0.f, 0.f, 0.f, 0.f};
   sT = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 
+  // ---- stage loop ----
+  // Top of iteration s: kop = K(s), vop = V(s-1), tk = K(s) and tv = V(s-1)
+  // of the tail, sA = scores of tile A for stage s (masked), pB / rsB = tile
+  // B's probabilities of stage s-1 and their sums, sT = the tail's scores
+  // of stage s-1 (masked), pT / ltT its probabilities and lane sums.  The
+  // unit entries of stage s (its valid count) and of stage s + NST - 1 (its
+  // loads) were read from LDS during the previous iteration.
+  int4 e_valid = elds[0];
+  int4 e_issue = elds[min(NST - 1, KVC_MAX_SPLIT_STAGES - 1)];
   for (int s = 0; s < nstage; ++s) {
-    const int valid = stage_entry_valid(s);
+    // stage s+1 published; the ring slot of stage s-1 (read by every wave in
+    // iteration s-1) refilled with stage s + NST - 1
+    wait_ahead<LPW, NST - 3>(min(nstage - 2 - s, NST - 3));
+    ring_barrier();
+    if (s + NST - 1 < nstage)
+      issue_e(s + NST - 1, int2{__builtin_amdgcn_readfirstlane(e_issue.x), __builtin_amdgcn_readfirstlane(e_issue.y)});
+    const int valid = __builtin_amdgcn_readfirstlane(e_valid.y);
 
-    // ---- step X: check of B (stage s-1) and of the tail (stage s-1) ----
+    // ---- step X: checks of B and of the tail (stage s-1) ----
     {
       float cs = rsB[0];
       if (__builtin_expect(freshB || __builtin_amdgcn_ballot_w64(cs > LAZY_COL_LIMIT), 0))
@@ -582,42 +630,72 @@ __global__ __launch_bounds__(64 * KVC_ATTN32_WAVES, 1) void attn32_kernel(AttnPa
         lt = renorm16<TDB, E>(sT, sl, freshT, refT, nrefT, lT, oT, pT);
       lT += lt;
     }
-    // MFMAs: QK(B, s), tail QK(s), PV(B, s-1), tail PV(s-1) | softmax(A, s)
-    if constexpr (TAIL) {
-      read_tail(s);
-      if (s == 0) {
-#pragma unroll
-        for (int db = 0; db < TDB; ++db) tv[db] = __builtin_bit_cast(bf16x4, u32x2{0u, 0u});
-      }
-    }
-    qk32(KS, sB);
-    if constexpr (TAIL) qk16(sT);
-    pv32(pB, oB);
-    if constexpr (TAIL) pv16(pT);
-    probs32<E>(sA, sl, nrefA, pA);
-    rsA = rowsum(pA);
-#pragma unroll
-    for (int i = 0; i < (TAIL ? 26 : 20); ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
-    }
-
-    // ---- stage s+1 published, slot of stage s-1 free; V(s) and K(s+1) read ----
+    // MFMAs QK(B, s), tail QK(s), PV(B, s-1), tail PV(s-1) and A's row sums,
+    // each followed by its share of tile A's probabilities (softmax(A, s));
+    // K(s+1) is read into kop during PV(B, s-1), V(s) into vop after it, a
+    // register or two at a time so that the LDS reads overlap the MFMAs
     {
-      const int ahead = min(nstage - 2 - s, NST - 3);   // stages after s+1 whose loads may fly
-      switch (ahead) {
-        case 3: wait_vmcnt<3 * LPW>(); break;
-        case 2: wait_vmcnt<2 * LPW>(); break;
-        case 1: wait_vmcnt<1 * LPW>(); break;
-        default: wait_vmcnt<0>(); break;
+      constexpr int NM = 2 * KS + (TAIL ? TKS : 0) + 4 * DB + (TAIL ? TDB : 0);
+      constexpr int NV = (TAIL ? TDB : 0) + 4;   // MFMAs that V(s)'s reads are spread over
+      int m = 0;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+          sB[sb] = MM::mfma32(kop[sb][ks], qB[ks], ks == 0 ? f32x16{} : sB[sb]);
+#pragma unroll
+          for (int c = 16 * m / NM; c < 16 * (m + 1) / NM; ++c) prob_chunk(sA, nrefA, pA, c);
+          ++m;
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      if constexpr (TAIL) {
+#pragma unroll
+        for (int k = 0; k < TKS; ++k) {
+          sT = El<E>::mfma(tk[k], qT[k], k == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sT);
+#pragma unroll
+          for (int c = 16 * m / NM; c < 16 * (m + 1) / NM; ++c) prob_chunk(sA, nrefA, pA, c);
+          ++m;
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const int j = t * DB + db;
+          oB[db] = MM::mfma32(vop[t][db], __builtin_bit_cast(bf16x8, pB[t]), oB[db]);
+#pragma unroll
+          for (int c = 16 * m / NM; c < 16 * (m + 1) / NM; ++c) prob_chunk(sA, nrefA, pA, c);
+#pragma unroll
+          for (int i = 2 * KS * j / (4 * DB); i < 2 * KS * (j + 1) / (4 * DB); ++i) read_k1(s + 1, i);
+          ++m;
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      int mv = 0;
+      if constexpr (TAIL) {
+#pragma unroll
+        for (int db = 0; db < TDB; ++db) {
+          oT[db] = MM::mfma16x16(tv[db], __builtin_bit_cast(bf16x4, pT), oT[db]);
+#pragma unroll
+          for (int c = 16 * m / NM; c < 16 * (m + 1) / NM; ++c) prob_chunk(sA, nrefA, pA, c);
+#pragma unroll
+          for (int i = 4 * DB * mv / NV; i < 4 * DB * (mv + 1) / NV; ++i) read_v1(s, i);
+          ++m;
+          ++mv;
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        rsA = El<E>::mfma(mask, __builtin_bit_cast(bf16x8, pA[t]), t == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : rsA);
+#pragma unroll
+        for (int i = 4 * DB * mv / NV; i < 4 * DB * (mv + 1) / NV; ++i) read_v1(s, i);
+        ++mv;
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    ring_barrier();
-    if (s + NST - 1 < nstage) issue(s + NST - 1);
-    read_v(s);
-    read_k(s + 1);
 
-    // ---- step Y: check of A (stage s) ----
+    // ---- step Y: masks of B and the tail (stage s), check of A (stage s) ----
     if (__builtin_expect(valid < KVC_KV_TILE, 0)) {
       mask32(sB, valid, h);
       if constexpr (TAIL) mask16(sT, valid, 16 * wv + 4 * g4);
@@ -628,26 +706,58 @@ __global__ __launch_bounds__(64 * KVC_ATTN32_WAVES, 1) void attn32_kernel(AttnPa
         cs = renorm32<DB, E>(sA, sl, freshA, refA, nrefA, lA, oA, pA);
       lA += cs;
     }
-    // MFMAs: QK(A, s+1), PV(A, s) | softmax(B, s), tail softmax(s)
-    qk32(0, sA);
-    pv32(pA, oA);
-    probs32<E>(sB, sl, nrefB, pB);
-    rsB = rowsum(pB);
-    if constexpr (TAIL) {
-      pT[0] = El<E>::pack_p(__builtin_amdgcn_exp2f(__builtin_fmaf(sT[0], sl, nrefT)),
-                            __builtin_amdgcn_exp2f(__builtin_fmaf(sT[1], sl, nrefT)));
-      pT[1] = El<E>::pack_p(__builtin_amdgcn_exp2f(__builtin_fmaf(sT[2], sl, nrefT)),
-                            __builtin_amdgcn_exp2f(__builtin_fmaf(sT[3], sl, nrefT)));
-      ltT = El<E>::dot_ones(pT[1], El<E>::dot_ones(pT[0], 0.f));
-    }
+    // MFMAs QK(A, s+1), PV(A, s), each followed by its share of tile B's
+    // probabilities (softmax(B, s)); then B's row sums with the tail's
+    // softmax(s) and the tail operands of the next iteration; the entries of
+    // the next iteration
+    {
+      constexpr int NM = 2 * KS + 4 * DB;
+      int m = 0;
 #pragma unroll
-    for (int i = 0; i < 20; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, TAIL ? 4 : 3, 0);
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+          sA[sb] = MM::mfma32(kop[sb][ks], qA[ks], ks == 0 ? f32x16{} : sA[sb]);
+#pragma unroll
+          for (int c = 16 * m / NM; c < 16 * (m + 1) / NM; ++c) prob_chunk(sB, nrefB, pB, c);
+          ++m;
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      e_valid = elds[min(s + 1, KVC_MAX_SPLIT_STAGES - 1)];
+      e_issue = elds[min(s + NST, KVC_MAX_SPLIT_STAGES - 1)];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          oA[db] = MM::mfma32(vop[t][db], __builtin_bit_cast(bf16x8, pA[t]), oA[db]);
+#pragma unroll
+          for (int c = 16 * m / NM; c < 16 * (m + 1) / NM; ++c) prob_chunk(sB, nrefB, pB, c);
+          ++m;
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        rsB = El<E>::mfma(mask, __builtin_bit_cast(bf16x8, pB[t]), t == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : rsB);
+        if constexpr (TAIL) {
+          if (t == 0) {
+            pT[0] = El<E>::pack_p(__builtin_amdgcn_exp2f(__builtin_fmaf(sT[0], sl, nrefT)),
+                                  __builtin_amdgcn_exp2f(__builtin_fmaf(sT[1], sl, nrefT)));
+            read_tk(s + 1);
+          } else if (t == 1) {
+            pT[1] = El<E>::pack_p(__builtin_amdgcn_exp2f(__builtin_fmaf(sT[2], sl, nrefT)),
+                                  __builtin_amdgcn_exp2f(__builtin_fmaf(sT[3], sl, nrefT)));
+            ltT = El<E>::dot_ones(pT[1], El<E>::dot_ones(pT[0], 0.f));
+          } else {
+            read_tv1(s, 2 * t - 4);
+            read_tv1(s, 2 * t - 3);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     // the next stage's A scores need masking before its softmax (step X)
     if (s + 1 < nstage) {
-      const int vn = stage_entry_valid(s + 1);
+      const int vn = __builtin_amdgcn_readfirstlane(e_valid.y);
       if (__builtin_expect(vn < KVC_KV_TILE, 0)) mask32(sA, vn, h);
     }
   }
@@ -659,18 +769,17 @@ __global__ __launch_bounds__(64 * KVC_ATTN32_WAVES, 1) void attn32_kernel(AttnPa
       cs = renorm32<DB, E>(sB, sl, freshB, refB, nrefB, lB, oB, pB);
     lB += cs;
   }
-  pv32(pB, oB);
-  if constexpr (TAIL) {
-    {
-      const uint8_t* bv = ring + ((nstage - 1) % NST) * S::STAGE;
 #pragma unroll
-      for (int db = 0; db < TDB; ++db) tv[db] = __builtin_bit_cast(bf16x4, ds_read_tr16(bv + tvofs[db]));
-    }
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oB[db] = MM::mfma32(vop[t][db], __builtin_bit_cast(bf16x8, pB[t]), oB[db]);
+  if constexpr (TAIL) {
     float lt = ltT;
     if (__builtin_expect(freshT || __builtin_amdgcn_ballot_w64(lt > LAZY_SUM_LIMIT), 0))
       lt = renorm16<TDB, E>(sT, sl, freshT, refT, nrefT, lT, oT, pT);
     lT += lt;
-    pv16(pT);
+#pragma unroll
+    for (int db = 0; db < TDB; ++db) oT[db] = MM::mfma16x16(tv[db], __builtin_bit_cast(bf16x4, pT), oT[db]);
   }
   // the epilogue reads the accumulators the last MFMAs wrote
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
@@ -758,7 +867,7 @@ __global__ __launch_bounds__(64 * KVC_ATTN32_WAVES, 1) void attn32_kernel(AttnPa
           }
           if (g4 == 0) p.part_lse[pt * 32 + r16] = M + __log2f(lsum);
         } else {
-          const int row = tail_row0 + r16;
+          const int row = 32 * st.n_t32 + r16;
           if (row < st.n_q) {
             uint16_t* orow = static_cast<uint16_t*>(p.o) + ((size_t)(st.q_row0 + row) * H + hd) * D;
 #pragma unroll
