@@ -616,7 +616,7 @@ kvc_status kvc_get_plan_shape(const kvc_ctx* c, int32_t* work_items, int32_t* gr
   if (work_items) *work_items = c->plan.num_items;
   if (group_rows) {
     if (c->cfg.tiles32())
-      *group_rows = KVC_ATTN32_WAVES * 2 * KVC_Q_TILE32 + (c->plan.shared_tile ? KVC_TAIL_ROWS : 0);
+      *group_rows = KVC_GROUP_TILES32 * KVC_Q_TILE32 + (c->plan.shared_tile ? KVC_TAIL_ROWS : 0);
     else
       *group_rows = kvc_group_tiles(c->plan.shared_tile ? 1 : 0) * KVC_Q_TILE;
   }

@@ -263,6 +263,11 @@ __device__ __forceinline__ float renorm16(const f32x4& s, float sl, int& fresh, 
   return lt;
 }
 
+template <bool B>
+struct Flag {
+  static constexpr bool value = B;
+};
+
 // Barrier that first waits for the wave's LDS reads: after it, other waves'
 // direct-to-LDS loads may refill the ring slots those reads came from.
 __device__ __forceinline__ void ring_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
@@ -285,12 +290,13 @@ template <int D, int E, bool TAIL>
 __global__ __launch_bounds__(64 * KVC_ATTN32_WAVES, 1) void attn32_kernel(AttnParams p) {
   using S = Shape32<D>;
   using MM = M32<E>;
+  constexpr int NW = KVC_ATTN32_WAVES;
   constexpr int KS = S::KS, DB = S::DB, TKS = S::TKS, TDB = S::TDB, LPW = S::LPW, NST = S::NSTAGE;
   // LDS: the ring of K/V stages and the split's unit entries.  Before the
   // loop the last three ring slots stage the query operands: per wave its
-  // tiles A and B and a copy of the tail, row-major.
-  constexpr int QW = (2 * S::QT + (TAIL ? S::TQ : 0)) * 1024;
-  static_assert(KVC_ATTN32_WAVES * QW <= 3 * S::STAGE, "query staging fits three ring slots");
+  // tile (and, for the tail waves, a copy of the tail), row-major.
+  constexpr int QW = (S::QT + (TAIL ? S::TQ : 0)) * 1024;
+  static_assert(NW * QW <= 3 * S::STAGE, "query staging fits three ring slots");
   constexpr int P0 = NST - 3;   // stages loaded before the query operands are read
   __shared__ __attribute__((aligned(1024))) uint8_t ring[NST * S::STAGE];
   __shared__ __attribute__((aligned(1024))) int4 elds[KVC_MAX_SPLIT_STAGES];
@@ -301,6 +307,11 @@ __global__ __launch_bounds__(64 * KVC_ATTN32_WAVES, 1) void attn32_kernel(AttnPa
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   const int n = lane & 31, h = lane >> 5;       // 32x32 layouts: query column, lane half
   const int r16 = lane & 15, g4 = lane >> 4;    // 16x16 layouts
+  // Waves w and w + 4 share a SIMD.  A lead wave (w < 4) does QK, softmax
+  // and P.V of stage s in iteration s; its lag partner does the softmax and
+  // P.V of stage s - 1, then QK of stage s: while one runs MFMAs the other
+  // runs the vector unit.  The lead waves also share the tail.
+  const bool lead = wv < KVC_TAIL_WAVES;
 
   // XCD-aware item order: work-groups go round-robin over the 8 XCDs; each
   // XCD takes a contiguous item range, so one head's splits share an L2.
@@ -320,10 +331,12 @@ __global__ __launch_bounds__(64 * KVC_ATTN32_WAVES, 1) void attn32_kernel(AttnPa
   const int split = local % st.n_split;
   const int hd = local / st.n_split;
 
-  // tiles of 32 rows of this group, and the tail (16 rows) if this group has it
+  // tiles of 32 rows of this group (one per wave), and the tail (16 rows) if
+  // this group has it
   const int t_lo = grp * st.n_t32 / st.n_group;
   const int t_hi = (grp + 1) * st.n_t32 / st.n_group;
   const int ntile = t_hi - t_lo;
+  const int tile = t_lo + wv;
   const bool has_tail = TAIL && st.tail != 0 && grp == st.n_group - 1;
   const int u0 = split * st.n_units / st.n_split;
   const int u1 = (split + 1) * st.n_units / st.n_split;
@@ -343,18 +356,15 @@ __global__ __launch_bounds__(64 * KVC_ATTN32_WAVES, 1) void attn32_kernel(AttnPa
 #pragma unroll
   for (int i = 0; i < P0; ++i)
     e_first[i] = i < nstage ? int2{units[KVC_UNIT_INTS * i], units[KVC_UNIT_INTS * i + 1]} : int2{0, KVC_KV_TILE};
-  // entry of stage i (uniform): slot index of its first K row, valid slots
   auto stage_entry = [&](int i) {
     const int4 e = elds[i];
     return int2{__builtin_amdgcn_readfirstlane(e.x), __builtin_amdgcn_readfirstlane(e.y)};
   };
-  auto stage_entry_valid = [&](int i) { return __builtin_amdgcn_readfirstlane(elds[i].y); };
 
   // ---- direct global -> LDS loads of one stage (K rows, then V rows) ----
   // Load instruction j of the wave fills 1 KiB at LDS byte 1024 * (wave *
   // LPW + j) of the stage, lane l writing [16 l, 16 l + 16); the lane fetches
-  // the logical chunk the swizzle places there.  In a partial stage, rows
-  // past the valid count re-read the last valid row (finite; masked later).
+  // the logical chunk the swizzle places there.
   const uint8_t* pool = static_cast<const uint8_t*>(p.pool);
   const uint64_t v_half = (uint64_t)p.page_size * slot_bytes;
   // Load instruction i of a stage (K: i < LOADS / 2, V: the rest) covers
@@ -386,26 +396,21 @@ __global__ __launch_bounds__(64 * KVC_ATTN32_WAVES, 1) void attn32_kernel(AttnPa
     jofs[j] = (kv ? v_half : 0) + (uint64_t)(RPL * blk) * slot_bytes;
     jlds[j] = (uint32_t)(kv * S::HALF + blk * 1024);
   }
+  // load j of a stage whose unit starts at ubase, into the ring slot at LDS
+  // byte `slot`: rows past the valid count (a partial stage) re-read the last
+  // valid row.  The offset is an unsigned 32-bit addend of the scalar base
+  // (the unit's first row of the K or V half), so rows are measured from the
+  // unit's first row, never below it.
   auto issue_e = [&](int sidx, int2 e) {
     const uint8_t* ubase = pool + (uint64_t)(uint32_t)e.x * slot_bytes + head_off;
-    const int valid = e.y;
     const uint32_t slot = ring_lds + (uint32_t)(sidx % NST) * S::STAGE;
-    if (__builtin_expect(valid >= KVC_KV_TILE, 1)) {
 #pragma unroll
-      for (int j = 0; j < LPW; ++j) load_lds16(ubase + jofs[j], (j & 1) ? lofs1 : lofs0, slot + jlds[j]);
-    } else {
-      // partial stage (rare): rows past the valid count re-read the last
-      // valid row.  The offset is an unsigned 32-bit addend of the scalar
-      // base, so the row is measured from the unit's first row, never below it.
-#pragma unroll
-      for (int j = 0; j < LPW; ++j) {
-        const int row = jrow[j] + lrow0;
-        const uint32_t o = ((j & 1) ? lofs1 : lofs0) + (uint32_t)(min(row, valid - 1) - lrow0) * slot_bytes;
-        load_lds16(ubase + (jofs[j] - (uint64_t)jrow[j] * slot_bytes), o, slot + jlds[j]);
-      }
+    for (int j = 0; j < LPW; ++j) {
+      const uint32_t o =
+          ((j & 1) ? lofs1 : lofs0) + (uint32_t)(min(jrow[j] + lrow0, e.y - 1) - lrow0) * slot_bytes;
+      load_lds16(ubase + (jofs[j] - (uint64_t)jrow[j] * slot_bytes), o, slot + jlds[j]);
     }
   };
-  auto issue = [&](int sidx) { issue_e(sidx, stage_entry(sidx)); };
 
   // ---- prologue loads, in the order the vmcnt accounting assumes ----
   // (1) query rows (RPL per load, row-major) into the staging slots; rows
@@ -419,20 +424,19 @@ __global__ __launch_bounds__(64 * KVC_ATTN32_WAVES, 1) void attn32_kernel(AttnPa
     for (int i = 0; i < nload; ++i) {
       const int row = min(row0 + RPL * i + lrow0, st.n_q - 1);
       load_lds16(qsrc + (size_t)r0 * slot_bytes, (uint32_t)(row - r0) * slot_bytes + (uint32_t)((lane % CPR) << 4),
-                 __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(i * 1024)));
+                 lds0 + (uint32_t)(i * 1024));
     }
   };
-  q_dma(32 * (t_lo + wv), S::QT, qlds);
-  q_dma(32 * (t_lo + wv + 4), S::QT, qlds + S::QT * 1024);
-  if constexpr (TAIL) q_dma(32 * st.n_t32, S::TQ, qlds + 2 * S::QT * 1024);
+  q_dma(32 * tile, S::QT, qlds);
+  if constexpr (TAIL)
+    if (lead) q_dma(32 * st.n_t32, S::TQ, qlds + S::QT * 1024);
   // (2) unit entries, 64 per load, by the waves in turn (lanes past the
   // split's count repeat its last entry)
   {
     const uint32_t elds_lds = __builtin_amdgcn_readfirstlane(lds_addr(elds));
     const int nblk = (nstage + 63) / 64;
-    for (int b = wv; b < nblk; b += KVC_ATTN32_WAVES)
-      load_lds16(units, (uint32_t)min(64 * b + lane, nstage - 1) * 16,
-                 __builtin_amdgcn_readfirstlane(elds_lds + (uint32_t)(b * 1024)));
+    for (int b = wv; b < nblk; b += NW)
+      load_lds16(units, (uint32_t)min(64 * b + lane, nstage - 1) * 16, elds_lds + (uint32_t)(b * 1024));
   }
   // (3) the first stages
   const int pre = min(nstage, P0);
@@ -460,14 +464,14 @@ __global__ __launch_bounds__(64 * KVC_ATTN32_WAVES, 1) void attn32_kernel(AttnPa
         vofs[db][rr] = (uint32_t)(S::HALF + row * S::ROW_BYTES + ((c ^ swz32<D>(row)) << 4) + 8 * (s & 1));
       }
   }
-  uint32_t tkofs[TKS], tvofs[TDB];   // tail: K rows 16w + r16; V^T rows 16w + 4 g4 + s / 4
+  uint32_t tkofs[TKS], tvofs[TDB];   // tail (lead waves): K rows 16w + r16; V^T rows 16w + 4 g4 + s / 4
   if constexpr (TAIL) {
-    const int row = 16 * wv + r16;
+    const int row = 16 * (wv & 3) + r16;
 #pragma unroll
     for (int k = 0; k < TKS; ++k)
       tkofs[k] = (uint32_t)(row * S::ROW_BYTES + (((4 * k + g4) ^ swz32<D>(row)) << 4));
     const int s = lane & 15;
-    const int vrow = 16 * wv + 4 * g4 + (s >> 2);
+    const int vrow = 16 * (wv & 3) + 4 * g4 + (s >> 2);
 #pragma unroll
     for (int db = 0; db < TDB; ++db) {
       const int c = 2 * db + ((s & 3) >> 1);
@@ -486,308 +490,203 @@ __global__ __launch_bounds__(64 * KVC_ATTN32_WAVES, 1) void attn32_kernel(AttnPa
       for (int ks = 0; ks < KS; ++ks)
         kop[sb][ks] = *reinterpret_cast<const bf16x8*>(b + kofs[ks] + 32 * sb * S::ROW_BYTES);
   };
-  // one operand register of K (i = sb * KS + ks) or of V^T (i = t * DB + db)
-  auto read_k1 = [&](int sidx, int i) {
+  auto read_v = [&](int sidx) {
     const uint8_t* b = ring + (sidx % NST) * S::STAGE;
-    kop[i / KS][i % KS] = *reinterpret_cast<const bf16x8*>(b + kofs[i % KS] + 32 * (i / KS) * S::ROW_BYTES);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const i16x4 x0 = ds_read_tr16(b + vofs[db][0] + 16 * t * S::ROW_BYTES);
+        const i16x4 x1 = ds_read_tr16(b + vofs[db][1] + 16 * t * S::ROW_BYTES);
+        vop[t][db] = __builtin_bit_cast(
+            bf16x8, (short __attribute__((ext_vector_type(8)))){x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]});
+      }
   };
-  auto read_v1 = [&](int sidx, int i) {
+  auto read_tail = [&](int sidx) {
     const uint8_t* b = ring + (sidx % NST) * S::STAGE;
-    const int t = i / DB, db = i % DB;
-    const i16x4 x0 = ds_read_tr16(b + vofs[db][0] + 16 * t * S::ROW_BYTES);
-    const i16x4 x1 = ds_read_tr16(b + vofs[db][1] + 16 * t * S::ROW_BYTES);
-    vop[t][db] = __builtin_bit_cast(
-        bf16x8, (short __attribute__((ext_vector_type(8)))){x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]});
-  };
-  // tail operands: its 16 K rows of stage s, its 16 V rows of stage s
-  auto read_tk = [&](int s) {
-    const uint8_t* b = ring + (s % NST) * S::STAGE;
 #pragma unroll
     for (int k = 0; k < TKS; ++k) tk[k] = *reinterpret_cast<const bf16x8*>(b + tkofs[k]);
-  };
-  auto read_tv1 = [&](int s, int i) {   // i < TDB; more than TDB does nothing
-    if (i < TDB) {
-      const uint8_t* b = ring + (s % NST) * S::STAGE;
-      tv[i] = __builtin_bit_cast(bf16x4, ds_read_tr16(b + tvofs[i]));
-    }
+#pragma unroll
+    for (int db = 0; db < TDB; ++db) tv[db] = __builtin_bit_cast(bf16x4, ds_read_tr16(b + tvofs[db]));
   };
 
-
-  // ---- softmax state: ref (log2 units) and its negation, running sum, and
-  // fresh (no valid slot seen yet) per tile ----
-  float refA = 0.f, refB = 0.f, refT = 0.f, nrefA = 0.f, nrefB = 0.f, nrefT = 0.f;
-  float lA = 0.f, lB = 0.f, lT = 0.f;
-  int freshA = 1, freshB = 1, freshT = 1;
-  f32x16 oA[DB], oB[DB];
+  // ---- softmax state of the wave's tile and (lead waves) of its tail block:
+  // ref (log2 units) and its negation, running sum, fresh (no valid slot
+  // seen yet) ----
+  float ref = 0.f, nref = 0.f, l = 0.f, refT = 0.f, nrefT = 0.f, lT = 0.f;
+  int fresh = 1, freshT = 1;
+  f32x16 o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) oA[db][e] = oB[db][e] = 0.f;
+    for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
   f32x4 oT[TDB];
 #pragma unroll
   for (int db = 0; db < TDB; ++db) oT[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const bf16x8 mask = rowsum_mask<E>(lane);
-  f32x16 sA[2], sB[2];
-  u32x4 pA[4], pB[4];
-  f32x4 rsA, rsB, sT;
+  f32x16 sc[2];
+  u32x4 pk[4];
+  f32x4 sT;
   u32x2 pT = u32x2{0u, 0u};
-  float ltT = 0.f;
-  auto rowsum = [&](const u32x4 (&pk)[4]) {
+
+  // the tile's probabilities in 16 chunks (chunk c: P^T operand t = c / 4,
+  // pair c % 4), software-pipelined over three steps so that each result is
+  // used one step after it was computed: step c packs chunk c-1, takes exp2
+  // of chunk c and scales chunk c+1
+  auto softmax = [&]() {
+    float f0, f1, x0 = 0.f, x1 = 0.f;
+    auto scale = [&](int c) {
+      const int t = c >> 2, e = 8 * (t & 1) + 2 * (c & 3);
+      f0 = __builtin_fmaf(sc[t >> 1][e], sl, nref);
+      f1 = __builtin_fmaf(sc[t >> 1][e + 1], sl, nref);
+    };
+    scale(0);
+#pragma unroll
+    for (int c = 0; c <= 16; ++c) {
+      if (c > 0) pk[(c - 1) >> 2][(c - 1) & 3] = El<E>::pack_p(x0, x1);
+      if (c < 16) {
+        x0 = __builtin_amdgcn_exp2f(f0);
+        x1 = __builtin_amdgcn_exp2f(f1);
+      }
+      if (c + 1 < 16) scale(c + 1);
+    }
+  };
+  auto rowsum = [&]() {
     f32x4 r = El<E>::mfma(mask, __builtin_bit_cast(bf16x8, pk[0]), f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
     for (int t = 1; t < 4; ++t) r = El<E>::mfma(mask, __builtin_bit_cast(bf16x8, pk[t]), r);
     return r;
   };
-  // chunk c (0..15) of a 32x32 tile's probabilities: P^T operand t = c / 4, pair c % 4
-  auto prob_chunk = [&](const f32x16 (&s)[2], float nref, u32x4 (&pk)[4], int c) {
-    const int t = c >> 2, k = c & 3, e = 8 * (t & 1) + 2 * k;
-    pk[t][k] = El<E>::pack_p(__builtin_amdgcn_exp2f(__builtin_fmaf(s[t >> 1][e], sl, nref)),
-                             __builtin_amdgcn_exp2f(__builtin_fmaf(s[t >> 1][e + 1], sl, nref)));
+  // lazy check of the tile (column sums of the probabilities with the current
+  // ref; the exact path when a sum is too large or the tile is fresh)
+  auto check = [&](const f32x4& rs) {
+    float cs = rs[0];
+    if (__builtin_expect(fresh || __builtin_amdgcn_ballot_w64(cs > LAZY_COL_LIMIT), 0))
+      cs = renorm32<DB, E>(sc, sl, fresh, ref, nref, l, o, pk);
+    l += cs;
   };
-
+  bf16x8 qv[KS], qT[TKS];
+  auto qk = [&]() {
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      sc[sb] = MM::mfma32(kop[sb][0], qv[0], f32x16{});
+#pragma unroll
+      for (int ks = 1; ks < KS; ++ks) sc[sb] = MM::mfma32(kop[sb][ks], qv[ks], sc[sb]);
+    }
+  };
+  auto pv = [&]() {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] = MM::mfma32(vop[t][db], __builtin_bit_cast(bf16x8, pk[t]), o[db]);
+  };
   // ---- prologue: query operands and stage 0 ----
   wait_ahead<LPW, P0 - 1>(pre - 1);   // queries, entries and stage 0 landed (own loads)
   block_barrier();                    // ... and everyone's
-  bf16x8 qA[KS], qB[KS], qT[TKS];
   {
     // tile: lane (n, h) holds q[row n][16 ks + 8h .. + 8); tail: lane (r16,
     // g4) holds q[row r16][32 k + 8 g4 .. + 8)
     const uint8_t* qw = ring + (NST - 3) * S::STAGE + wv * QW;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      qA[ks] = *reinterpret_cast<const bf16x8*>(qw + n * S::ROW_BYTES + (2 * ks + h) * 16);
-      qB[ks] = *reinterpret_cast<const bf16x8*>(qw + S::QT * 1024 + n * S::ROW_BYTES + (2 * ks + h) * 16);
-    }
+    for (int ks = 0; ks < KS; ++ks)
+      qv[ks] = *reinterpret_cast<const bf16x8*>(qw + n * S::ROW_BYTES + (2 * ks + h) * 16);
     if constexpr (TAIL) {
 #pragma unroll
       for (int k = 0; k < TKS; ++k)
-        qT[k] = *reinterpret_cast<const bf16x8*>(qw + 2 * S::QT * 1024 + r16 * S::ROW_BYTES + (4 * k + g4) * 16);
+        qT[k] = *reinterpret_cast<const bf16x8*>(qw + S::QT * 1024 + r16 * S::ROW_BYTES + (4 * k + g4) * 16);
     }
-  }
-  read_k(0);
-  if constexpr (TAIL) {
-    read_tk(0);
-#pragma unroll
-    for (int db = 0; db < TDB; ++db) tv[db] = __builtin_bit_cast(bf16x4, u32x2{0u, 0u});
   }
   // every wave has its query operands: the staging slots take stages P0 ..
   ring_barrier();
-  for (int i = P0; i < min(nstage, NST - 1); ++i) issue(i);
-#pragma unroll
-  for (int sb = 0; sb < 2; ++sb) {
-    sA[sb] = MM::mfma32(kop[sb][0], qA[0], f32x16{});
-#pragma unroll
-    for (int ks = 1; ks < KS; ++ks) sA[sb] = MM::mfma32(kop[sb][ks], qA[ks], sA[sb]);
-  }
-  {
-    const int v0 = e_first[0].y;
-    if (v0 < KVC_KV_TILE) mask32(sA, v0, h);
-  }
-  // "stage -1" of tile B and of the tail: all slots masked, zero operands;
-  // their first checks take the exact path and leave them fresh and empty
+  for (int i = P0; i < min(nstage, NST - 1); ++i) issue_e(i, stage_entry(i));
+  // the lag waves start with "stage -1": all slots masked, zero operands; its
+  // check takes the exact path and leaves the tile fresh and empty
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) sB[sb][e] = -INFINITY;
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    pB[t] = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int db = 0; db < DB; ++db) vop[t][db] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-  }
-  rsB = f32x4{0.f, 0.f, 0.f, 0.f};
-  sT = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-
-  // ---- stage loop ----
-  // Top of iteration s: kop = K(s), vop = V(s-1), tk = K(s) and tv = V(s-1)
-  // of the tail, sA = scores of tile A for stage s (masked), pB / rsB = tile
-  // B's probabilities of stage s-1 and their sums, sT = the tail's scores
-  // of stage s-1 (masked), pT / ltT its probabilities and lane sums.  The
-  // unit entries of stage s (its valid count) and of stage s + NST - 1 (its
-  // loads) were read from LDS during the previous iteration.
-  int4 e_valid = elds[0];
-  int4 e_issue = elds[min(NST - 1, KVC_MAX_SPLIT_STAGES - 1)];
-  for (int s = 0; s < nstage; ++s) {
-    // stage s+1 published; the ring slot of stage s-1 (read by every wave in
-    // iteration s-1) refilled with stage s + NST - 1
-    wait_ahead<LPW, NST - 3>(min(nstage - 2 - s, NST - 3));
-    ring_barrier();
-    if (s + NST - 1 < nstage)
-      issue_e(s + NST - 1, int2{__builtin_amdgcn_readfirstlane(e_issue.x), __builtin_amdgcn_readfirstlane(e_issue.y)});
-    const int valid = __builtin_amdgcn_readfirstlane(e_valid.y);
-
-    // ---- step X: checks of B and of the tail (stage s-1) ----
-    {
-      float cs = rsB[0];
-      if (__builtin_expect(freshB || __builtin_amdgcn_ballot_w64(cs > LAZY_COL_LIMIT), 0))
-        cs = renorm32<DB, E>(sB, sl, freshB, refB, nrefB, lB, oB, pB);
-      lB += cs;
-    }
-    if constexpr (TAIL) {
-      float lt = ltT;
-      if (__builtin_expect(freshT || __builtin_amdgcn_ballot_w64(lt > LAZY_SUM_LIMIT), 0))
-        lt = renorm16<TDB, E>(sT, sl, freshT, refT, nrefT, lT, oT, pT);
-      lT += lt;
-    }
-    // MFMAs QK(B, s), tail QK(s), PV(B, s-1), tail PV(s-1) and A's row sums,
-    // each followed by its share of tile A's probabilities (softmax(A, s));
-    // K(s+1) is read into kop during PV(B, s-1), V(s) into vop after it, a
-    // register or two at a time so that the LDS reads overlap the MFMAs
-    {
-      constexpr int NM = 2 * KS + (TAIL ? TKS : 0) + 4 * DB + (TAIL ? TDB : 0);
-      constexpr int NV = (TAIL ? TDB : 0) + 4;   // MFMAs that V(s)'s reads are spread over
-      int m = 0;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-          sB[sb] = MM::mfma32(kop[sb][ks], qB[ks], ks == 0 ? f32x16{} : sB[sb]);
-#pragma unroll
-          for (int c = 16 * m / NM; c < 16 * (m + 1) / NM; ++c) prob_chunk(sA, nrefA, pA, c);
-          ++m;
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      if constexpr (TAIL) {
-#pragma unroll
-        for (int k = 0; k < TKS; ++k) {
-          sT = El<E>::mfma(tk[k], qT[k], k == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sT);
-#pragma unroll
-          for (int c = 16 * m / NM; c < 16 * (m + 1) / NM; ++c) prob_chunk(sA, nrefA, pA, c);
-          ++m;
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const int j = t * DB + db;
-          oB[db] = MM::mfma32(vop[t][db], __builtin_bit_cast(bf16x8, pB[t]), oB[db]);
-#pragma unroll
-          for (int c = 16 * m / NM; c < 16 * (m + 1) / NM; ++c) prob_chunk(sA, nrefA, pA, c);
-#pragma unroll
-          for (int i = 2 * KS * j / (4 * DB); i < 2 * KS * (j + 1) / (4 * DB); ++i) read_k1(s + 1, i);
-          ++m;
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      int mv = 0;
-      if constexpr (TAIL) {
-#pragma unroll
-        for (int db = 0; db < TDB; ++db) {
-          oT[db] = MM::mfma16x16(tv[db], __builtin_bit_cast(bf16x4, pT), oT[db]);
-#pragma unroll
-          for (int c = 16 * m / NM; c < 16 * (m + 1) / NM; ++c) prob_chunk(sA, nrefA, pA, c);
-#pragma unroll
-          for (int i = 4 * DB * mv / NV; i < 4 * DB * (mv + 1) / NV; ++i) read_v1(s, i);
-          ++m;
-          ++mv;
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        rsA = El<E>::mfma(mask, __builtin_bit_cast(bf16x8, pA[t]), t == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : rsA);
-#pragma unroll
-        for (int i = 4 * DB * mv / NV; i < 4 * DB * (mv + 1) / NV; ++i) read_v1(s, i);
-        ++mv;
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-
-    // ---- step Y: masks of B and the tail (stage s), check of A (stage s) ----
-    if (__builtin_expect(valid < KVC_KV_TILE, 0)) {
-      mask32(sB, valid, h);
-      if constexpr (TAIL) mask16(sT, valid, 16 * wv + 4 * g4);
-    }
-    {
-      float cs = rsA[0];
-      if (__builtin_expect(freshA || __builtin_amdgcn_ballot_w64(cs > LAZY_COL_LIMIT), 0))
-        cs = renorm32<DB, E>(sA, sl, freshA, refA, nrefA, lA, oA, pA);
-      lA += cs;
-    }
-    // MFMAs QK(A, s+1), PV(A, s), each followed by its share of tile B's
-    // probabilities (softmax(B, s)); then B's row sums with the tail's
-    // softmax(s) and the tail operands of the next iteration; the entries of
-    // the next iteration
-    {
-      constexpr int NM = 2 * KS + 4 * DB;
-      int m = 0;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-          sA[sb] = MM::mfma32(kop[sb][ks], qA[ks], ks == 0 ? f32x16{} : sA[sb]);
-#pragma unroll
-          for (int c = 16 * m / NM; c < 16 * (m + 1) / NM; ++c) prob_chunk(sB, nrefB, pB, c);
-          ++m;
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      e_valid = elds[min(s + 1, KVC_MAX_SPLIT_STAGES - 1)];
-      e_issue = elds[min(s + NST, KVC_MAX_SPLIT_STAGES - 1)];
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          oA[db] = MM::mfma32(vop[t][db], __builtin_bit_cast(bf16x8, pA[t]), oA[db]);
-#pragma unroll
-          for (int c = 16 * m / NM; c < 16 * (m + 1) / NM; ++c) prob_chunk(sB, nrefB, pB, c);
-          ++m;
-          __builtin_amdgcn_sched_barrier(0);
-        }
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        rsB = El<E>::mfma(mask, __builtin_bit_cast(bf16x8, pB[t]), t == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : rsB);
-        if constexpr (TAIL) {
-          if (t == 0) {
-            pT[0] = El<E>::pack_p(__builtin_amdgcn_exp2f(__builtin_fmaf(sT[0], sl, nrefT)),
-                                  __builtin_amdgcn_exp2f(__builtin_fmaf(sT[1], sl, nrefT)));
-            read_tk(s + 1);
-          } else if (t == 1) {
-            pT[1] = El<E>::pack_p(__builtin_amdgcn_exp2f(__builtin_fmaf(sT[2], sl, nrefT)),
-                                  __builtin_amdgcn_exp2f(__builtin_fmaf(sT[3], sl, nrefT)));
-            ltT = El<E>::dot_ones(pT[1], El<E>::dot_ones(pT[0], 0.f));
-          } else {
-            read_tv1(s, 2 * t - 4);
-            read_tv1(s, 2 * t - 3);
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    // the next stage's A scores need masking before its softmax (step X)
-    if (s + 1 < nstage) {
-      const int vn = __builtin_amdgcn_readfirstlane(e_valid.y);
-      if (__builtin_expect(vn < KVC_KV_TILE, 0)) mask32(sA, vn, h);
-    }
-  }
-
-  // ---- drain: check and P.V of B and of the tail for the last stage ----
-  {
-    float cs = rsB[0];
-    if (__builtin_expect(freshB || __builtin_amdgcn_ballot_w64(cs > LAZY_COL_LIMIT), 0))
-      cs = renorm32<DB, E>(sB, sl, freshB, refB, nrefB, lB, oB, pB);
-    lB += cs;
-  }
+    for (int e = 0; e < 16; ++e) sc[sb][e] = -INFINITY;
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int db = 0; db < DB; ++db) oB[db] = MM::mfma32(vop[t][db], __builtin_bit_cast(bf16x8, pB[t]), oB[db]);
-  if constexpr (TAIL) {
-    float lt = ltT;
-    if (__builtin_expect(freshT || __builtin_amdgcn_ballot_w64(lt > LAZY_SUM_LIMIT), 0))
-      lt = renorm16<TDB, E>(sT, sl, freshT, refT, nrefT, lT, oT, pT);
-    lT += lt;
+    for (int db = 0; db < DB; ++db) vop[t][db] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+
+  // ---- stage loop: iteration s consumes ring slot s, published by the
+  // barrier at its top, and refills the slot of stage s - 1 with stage
+  // s + NST - 1 (two loops, with and without those loads) ----
+  int4 e_next = elds[min(NST - 1, KVC_MAX_SPLIT_STAGES - 1)];
+  int4 e_cur = elds[0];
+  auto stage_body = [&](int s, auto issue_tag) {
+    constexpr bool do_issue = decltype(issue_tag)::value;
+    wait_ahead<LPW, NST - 2>(min(nstage - 1 - s, NST - 2));
+    ring_barrier();
+    if constexpr (do_issue)
+      issue_e(s + NST - 1, int2{__builtin_amdgcn_readfirstlane(e_next.x), __builtin_amdgcn_readfirstlane(e_next.y)});
+    const int valid = __builtin_amdgcn_readfirstlane(e_cur.y);
+    e_cur = elds[min(s + 1, KVC_MAX_SPLIT_STAGES - 1)];
+    e_next = elds[min(s + NST, KVC_MAX_SPLIT_STAGES - 1)];
+    if (lead) {
+      read_k(s);
+      read_v(s);
+      if constexpr (TAIL) read_tail(s);
+      qk();
+      if constexpr (TAIL) {
+        sT = El<E>::mfma(tk[0], qT[0], f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-    for (int db = 0; db < TDB; ++db) oT[db] = MM::mfma16x16(tv[db], __builtin_bit_cast(bf16x4, pT), oT[db]);
+        for (int k = 1; k < TKS; ++k) sT = El<E>::mfma(tk[k], qT[k], sT);
+      }
+      if (__builtin_expect(valid < KVC_KV_TILE, 0)) {
+        mask32(sc, valid, h);
+        if constexpr (TAIL) mask16(sT, valid, 16 * wv + 4 * g4);
+      }
+      softmax();
+      const f32x4 rs = rowsum();
+      if constexpr (TAIL) {
+        pT[0] = El<E>::pack_p(__builtin_amdgcn_exp2f(__builtin_fmaf(sT[0], sl, nrefT)),
+                              __builtin_amdgcn_exp2f(__builtin_fmaf(sT[1], sl, nrefT)));
+        pT[1] = El<E>::pack_p(__builtin_amdgcn_exp2f(__builtin_fmaf(sT[2], sl, nrefT)),
+                              __builtin_amdgcn_exp2f(__builtin_fmaf(sT[3], sl, nrefT)));
+        float lt = El<E>::dot_ones(pT[1], El<E>::dot_ones(pT[0], 0.f));
+        if (__builtin_expect(freshT || __builtin_amdgcn_ballot_w64(lt > LAZY_SUM_LIMIT), 0))
+          lt = renorm16<TDB, E>(sT, sl, freshT, refT, nrefT, lT, oT, pT);
+        lT += lt;
+      }
+      check(rs);
+      pv();
+      if constexpr (TAIL) {
+#pragma unroll
+        for (int db = 0; db < TDB; ++db) oT[db] = MM::mfma16x16(tv[db], __builtin_bit_cast(bf16x4, pT), oT[db]);
+      }
+    } else {
+      // stage s - 1: scores in sc, V in vop
+      softmax();
+      check(rowsum());
+      pv();
+      // stage s: V into vop for the next iteration, scores into sc
+      read_k(s);
+      read_v(s);
+      qk();
+      if (__builtin_expect(valid < KVC_KV_TILE, 0)) mask32(sc, valid, h);
+    }
+  };
+  {
+    int s = 0;
+    for (; s + NST - 1 < nstage; ++s) stage_body(s, Flag<true>{});
+    for (; s < nstage; ++s) stage_body(s, Flag<false>{});
+  }
+  // ---- drain: the lag waves' last stage ----
+  if (!lead) {
+    softmax();
+    check(rowsum());
+    pv();
   }
   // the epilogue reads the accumulators the last MFMAs wrote
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 
   // ---- epilogue ----
-  // 32x32 tiles: lane (n, h) holds O^T[32 db + 8 i + 4 h + j][query n] in
-  // element 4 i + j of block db.
-  auto store32 = [&](int tile, float ref, float l, const f32x16 (&o)[DB]) {
+  // lane (n, h) holds O^T[32 db + 8 i + 4 h + j][query n] in element 4 i + j
+  // of block db.
+  if (wv < ntile) {
     const float inv = 1.0f / l;
     const int row = 32 * tile + n;
     if (st.n_split > 1) {
@@ -804,53 +703,52 @@ __global__ __launch_bounds__(64 * KVC_ATTN32_WAVES, 1) void attn32_kernel(AttnPa
           *reinterpret_cast<u32x2*>(po + (db * 4 + i) * 256) = El<E>::cvt4(v);
         }
       if (h == 0) p.part_lse[pt * 32 + n] = ref + __log2f(l);
-      return;
+    } else if (row < st.n_q) {
+      uint16_t* orow = static_cast<uint16_t*>(p.o) + ((size_t)(st.q_row0 + row) * H + hd) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f32x4 v = f32x4{o[db][4 * i], o[db][4 * i + 1], o[db][4 * i + 2], o[db][4 * i + 3]} * inv;
+          *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * i + 4 * h) = El<E>::cvt4(v);
+        }
     }
-    if (row >= st.n_q) return;
-    uint16_t* orow = static_cast<uint16_t*>(p.o) + ((size_t)(st.q_row0 + row) * H + hd) * D;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const f32x4 v = f32x4{o[db][4 * i], o[db][4 * i + 1], o[db][4 * i + 2], o[db][4 * i + 3]} * inv;
-        *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * i + 4 * h) = El<E>::cvt4(v);
-      }
-  };
-  if (wv < ntile) store32(t_lo + wv, refA, lA, oA);
-  if (wv + 4 < ntile) store32(t_lo + wv + 4, refB, lB, oB);
+  }
 
   if constexpr (TAIL) {
     if (has_tail) {
-      // merge the four waves' states of the tail (weights 2^(ref_w - max ref));
-      // a wave whose slots were all masked has l = 0
+      // merge the lead waves' states of the tail (weights 2^(ref_w - max
+      // ref)); a wave whose slots were all masked has l = 0
       constexpr int NV = TDB * 4 + 2;
       float* xs = reinterpret_cast<float*>(ring);
       const float lsum_w = lane_swap_sum(lT);
       __syncthreads();   // every wave is done with the ring
+      if (lead) {
 #pragma unroll
-      for (int db = 0; db < TDB; ++db)
+        for (int db = 0; db < TDB; ++db)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) xs[(wv * 64 + lane) * NV + 4 * db + j] = oT[db][j];
-      xs[(wv * 64 + lane) * NV + TDB * 4] = lsum_w > 0.0f ? refT : -INFINITY;
-      xs[(wv * 64 + lane) * NV + TDB * 4 + 1] = lsum_w;
+          for (int j = 0; j < 4; ++j) xs[(wv * 64 + lane) * NV + 4 * db + j] = oT[db][j];
+        xs[(wv * 64 + lane) * NV + TDB * 4] = lsum_w > 0.0f ? refT : -INFINITY;
+        xs[(wv * 64 + lane) * NV + TDB * 4 + 1] = lsum_w;
+      }
       __syncthreads();
       if (wv == 0) {
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < KVC_ATTN32_WAVES; ++w) M = fmaxf(M, xs[(w * 64 + lane) * NV + TDB * 4]);
+        for (int w = 0; w < KVC_TAIL_WAVES; ++w) M = fmaxf(M, xs[(w * 64 + lane) * NV + TDB * 4]);
         float lsum = 0.f;
-        f32x4 o[TDB];
+        f32x4 ot[TDB];
 #pragma unroll
-        for (int db = 0; db < TDB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int db = 0; db < TDB; ++db) ot[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int w = 0; w < KVC_ATTN32_WAVES; ++w) {
+        for (int w = 0; w < KVC_TAIL_WAVES; ++w) {
           const float* x = xs + (w * 64 + lane) * NV;
           const float wt = __builtin_amdgcn_exp2f(x[TDB * 4] - M);
           lsum += wt * x[TDB * 4 + 1];
 #pragma unroll
           for (int db = 0; db < TDB; ++db)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) o[db][j] += wt * x[4 * db + j];
+            for (int j = 0; j < 4; ++j) ot[db][j] += wt * x[4 * db + j];
         }
         const float inv = 1.0f / lsum;
         // lane (r16, g4) holds O^T[16 db + 4 g4 + j][tail query r16]
@@ -863,7 +761,7 @@ __global__ __launch_bounds__(64 * KVC_ATTN32_WAVES, 1) void attn32_kernel(AttnPa
           for (int db = 0; db < TDB; ++db) {
             const int d = 16 * db + 4 * g4;
             const int b32 = d >> 5, i = (d & 31) >> 3, hh = (d >> 2) & 1;
-            *reinterpret_cast<u32x2*>(po + (b32 * 4 + i) * 256 + (32 * hh + r16) * 4) = El<E>::cvt4(o[db] * inv);
+            *reinterpret_cast<u32x2*>(po + (b32 * 4 + i) * 256 + (32 * hh + r16) * 4) = El<E>::cvt4(ot[db] * inv);
           }
           if (g4 == 0) p.part_lse[pt * 32 + r16] = M + __log2f(lsum);
         } else {
@@ -872,7 +770,7 @@ __global__ __launch_bounds__(64 * KVC_ATTN32_WAVES, 1) void attn32_kernel(AttnPa
             uint16_t* orow = static_cast<uint16_t*>(p.o) + ((size_t)(st.q_row0 + row) * H + hd) * D;
 #pragma unroll
             for (int db = 0; db < TDB; ++db)
-              *reinterpret_cast<u32x2*>(orow + 16 * db + 4 * g4) = El<E>::cvt4(o[db] * inv);
+              *reinterpret_cast<u32x2*>(orow + 16 * db + 4 * g4) = El<E>::cvt4(ot[db] * inv);
           }
         }
       }

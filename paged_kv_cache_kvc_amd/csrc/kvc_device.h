@@ -112,10 +112,15 @@ __device__ __forceinline__ i32x4 unit_load(const int32_t* entry) {
 __device__ __forceinline__ void unit_wait(i32x4& e) { asm volatile("s_waitcnt lgkmcnt(0)" : "+s"(e)::"memory"); }
 
 // 16 bytes from base + offset (per lane) to LDS byte address
-// lds_base + 16 * lane.  base is wave-uniform (scalar registers).
+// lds_base + 16 * lane.  base and lds_base are wave-uniform; they are read
+// from the first lane so that they always sit in scalar registers.
 __device__ __forceinline__ void load_lds16(const void* base, uint32_t offset, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(offset), "s"(base),
-               "s"(lds_base)
+  const uint64_t b = (uint64_t)base;
+  const uint64_t sb = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(b >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  const uint32_t sl = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_base);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(offset), "s"((const void*)sb),
+               "s"(sl)
                : "memory", "m0");
 }
 

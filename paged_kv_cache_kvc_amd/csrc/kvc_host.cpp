@@ -297,14 +297,14 @@ void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const s
         const int64_t rem = n_q % KVC_Q_TILE32;
         const bool tail = variant && rem >= 1 && rem <= KVC_TAIL_ROWS;
         const int64_t nt = tail ? n_q / KVC_Q_TILE32 : ceil_div(n_q, KVC_Q_TILE32);
-        const int64_t per = KVC_ATTN32_WAVES * 2;
-        g.n_group[i] = std::max<int64_t>(1, ceil_div(nt, per));
+        g.n_group[i] = std::max<int64_t>(1, ceil_div(nt, KVC_GROUP_TILES32));
         g.n_t32[i] = nt;
         g.tail[i] = tail ? 1 : 0;
-        // wave w owns tiles w and w + 4 of its group: 2 tile-steps each, plus
-        // a quarter tile-step of the tail in every group of a tail launch
+        // wave w owns tile w of its group and waves w and w + 4 share a SIMD:
+        // 2 tile-steps each, plus a quarter tile-step of the tail in every
+        // group of a tail launch
         const int64_t kmax = ceil_div(nt, g.n_group[i]);
-        g.per_unit[i] = (kmax > 0 ? 2.0 : 0.0) + (kmax > KVC_ATTN32_WAVES ? 2.0 : 0.0) + (variant ? 0.25 : 0.0);
+        g.per_unit[i] = (kmax > 0 ? 2.0 : 0.0) + (kmax > KVC_TAIL_WAVES ? 2.0 : 0.0) + (variant ? 0.25 : 0.0);
       } else {
         // 16x16 kernel: groups of 8 tiles of 16 rows, or 9 with the ninth
         // shared by the four waves (a quarter tile-step each per stage)

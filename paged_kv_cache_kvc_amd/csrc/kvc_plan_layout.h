@@ -35,11 +35,14 @@
 // 16x16 attention kernel (head_dim 128).
 #define KVC_Q_TILE 16
 #define KVC_ATTN_WAVES 4
-// The 32x32 attention kernel (head_dim 32 and 64): query tiles of 32 rows,
-// 4 waves of two tiles each, and a tail tile of up to 16 rows shared by the
-// waves.  Split partial outputs of both kernels are stored per 32-row tile.
+// The 32x32 attention kernel (head_dim 32 and 64): query groups of 8 tiles
+// of 32 rows, one per wave of an 8-wave work-group, and a tail tile of up to
+// 16 rows shared by the first 4 waves.  Split partial outputs of both
+// kernels are stored per 32-row tile.
 #define KVC_Q_TILE32 32
-#define KVC_ATTN32_WAVES 4
+#define KVC_ATTN32_WAVES 8
+#define KVC_GROUP_TILES32 8
+#define KVC_TAIL_WAVES 4
 #define KVC_TAIL_ROWS 16
 // Upper bound of KV splits per stream (sizes the partial-output workspace).
 #define KVC_MAX_SPLITS 64
