@@ -49,7 +49,7 @@ def progress(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-KERNEL_SOURCES = ("kvc_kernels.hip", "kvc_kernels.h", "kvc_plan_layout.h")
+KERNEL_SOURCES = ("kvc_kernels.hip", "kvc_attn.hip", "kvc_device.h", "kvc_kernels.h", "kvc_plan_layout.h")
 
 
 def kernel_source_hash():
@@ -61,11 +61,17 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload):
+def attention_kernel_name(head_dim):
+    """The attention kernel that serves a head size: the 32x32 kernel up to
+    64, the 16x16 one at 128."""
+    return "attn32_kernel" if head_dim <= 64 else "attn_kernel"
+
+
+def read_traffic(workload, head_dim):
     """HBM bytes per attention launch from the committed rocprofv3 counter
     summary (FETCH_SIZE and WRITE_SIZE, calibrated against a plain copy), or
     None when it is missing or was taken on other kernel source."""
-    p = os.path.join(ROOT, "profiles", f"attn_kernel_{workload}_hbm_traffic.md")
+    p = os.path.join(ROOT, "profiles", f"{attention_kernel_name(head_dim)}_{workload}_hbm_traffic.md")
     if not os.path.exists(p):
         return None
     fields = {}
@@ -259,7 +265,7 @@ def scale_phase(args, torch, syn, kvc, dev):
                                 f"{wl.num_special_tokens} special tokens in one step, page_size {wl.page_size}"),
                    "num_blocks": nb, "query_rows": S * T, "visible_tokens": L, "num_heads": H, "head_dim": D},
         "roofline": roof,
-        "attention": {"kernel": "attn_kernel", "launches": a_n, "avg_us": 1e3 * a_ms / max(a_n, 1),
+        "attention": {"kernel": attention_kernel_name(wl.head_dim), "launches": a_n, "avg_us": 1e3 * a_ms / max(a_n, 1),
                       "attention_plus_merge_us": 1e6 * a_s, "tflops": tfl, "gbs": gbs,
                       "alg_flop_per_launch": flop, "alg_bytes_per_launch": byts,
                       "merge_avg_us": 1e3 * m_ms / max(m_n, 1), "merge_launches": m_n,
@@ -469,7 +475,7 @@ def main():
         gbs_step = pb / K / step_s / 1e9
         tfl_step = pf / K / step_s / 1e12
         bound = "hbm" if pf / pb < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9) else "mfma"
-        traffic = read_traffic(wl.name)
+        traffic = read_traffic(wl.name, D)
         if bound == "hbm":
             roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
                     "frac_attention_kernel_only": gbs_a / PEAK_HBM_GBS, "frac_whole_step": gbs_step / PEAK_HBM_GBS}
@@ -482,7 +488,7 @@ def main():
         out["roofline"] = roof
         peaks = achievable_peaks(torch, dev)
         out["attention"] = {
-            "kernel": "attn_kernel", "launches": a_n, "avg_us": 1e3 * a_ms / max(a_n, 1),
+            "kernel": attention_kernel_name(D), "launches": a_n, "avg_us": 1e3 * a_ms / max(a_n, 1),
             "tflops": tfl_a, "gbs": gbs_a, "frac_hbm": gbs_a / PEAK_HBM_GBS, "frac_mfma": tfl_a / PEAK_BF16_TFLOPS,
             "alg_bytes_per_launch": pb / max(a_n, 1), "alg_flop_per_launch": pf / max(a_n, 1),
             "merge_avg_us": 1e3 * m_ms / max(m_n, 1), "merge_launches": m_n,
