@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 5
+#define KVC_ABI_VERSION 6
 
 typedef struct kvc_ctx kvc_ctx;
 typedef void* kvc_stream_t;   /* hipStream_t */
@@ -326,6 +326,24 @@ kvc_status kvc_get_plan_shape(const kvc_ctx* ctx, int32_t* work_items, int32_t* 
  * NULL to query the size); n_ints receives the image's size.
  * Errors: KVC_ERR_ARG (capacity short), KVC_ERR_STATE (no plan). */
 kvc_status kvc_get_plan_image(const kvc_ctx* ctx, int32_t* buf, int32_t capacity, int32_t* n_ints);
+
+/* Copy the split partial results that the latest kvc_run wrote (for tests
+ * of the split-KV decomposition; [p5] "How Paged KV Cache Attention Achieves
+ * Stable Inference in Ling-Bot-Map" §Kernel Dispatch and Sequence Lengths:
+ * the splits of a row must combine to the exact softmax over its valid
+ * tokens).  Waits for hip_stream, then copies device to host:
+ *   lse: float [KVC_MAX_SPLITS][H][tiles][32], the base-2 log-sum-exp of the
+ *        scores (q.k / sqrt(D)) of each query row over the split's tokens;
+ *   o:   element type [KVC_MAX_SPLITS][H][tiles][D/32][4][64][4], the split's
+ *        normalised output, element (d, row) at [d/32][(d%32)/8]
+ *        [32 ((d%8)/4) + row][d%4] of its 32-row tile,
+ * with tiles = num_streams * ceil(max_frames_per_step * tokens_per_frame / 32)
+ * and a stream's tiles from its first (the plan's query tiles in order).
+ * Only the splits and tiles of split streams in the current plan hold
+ * values.  Either pointer may be NULL; n_lse / n_o receive the element counts.
+ * Errors: KVC_ERR_ARG (capacity short), KVC_ERR_STATE (no plan), KVC_ERR_HIP. */
+kvc_status kvc_get_split_partials(const kvc_ctx* ctx, float* lse, int64_t capacity_lse, uint16_t* o,
+                                  int64_t capacity_o, int64_t* n_lse, int64_t* n_o, kvc_stream_t hip_stream);
 
 /* [p3] §Inspecting Cache Statistics for one stream. */
 kvc_status kvc_get_stats(const kvc_ctx* ctx, int32_t stream, kvc_stats* out);

@@ -46,7 +46,7 @@ KVC_KERNEL_MERGE = 1
 KVC_KERNEL_APPEND = 2
 
 MAX_SPLITS = 64
-ABI_VERSION = 5   # KVC_ABI_VERSION of include/kvc.h
+ABI_VERSION = 6   # KVC_ABI_VERSION of include/kvc.h
 
 
 class KvcError(RuntimeError):
@@ -93,6 +93,9 @@ SIGNATURES = {
     "kvc_get_plan": (_I32, [_P, _PI32, _PI32, _PI32, _PI32, _PI32, _PI32, _PI32, _I32, _I32, _PI32, _PI32]),
     "kvc_get_plan_shape": (_I32, [_P, _PI32, _PI32]),
     "kvc_get_plan_image": (_I32, [_P, _PI32, _I32, _PI32]),
+    "kvc_get_split_partials": (_I32, [_P, ctypes.POINTER(ctypes.c_float), ctypes.c_int64,
+                                      ctypes.POINTER(ctypes.c_uint16), ctypes.c_int64,
+                                      ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64), _P]),
     "kvc_get_stats": (_I32, [_P, _I32, ctypes.POINTER(KvcStats)]),
     "kvc_set_option": (_I32, [_P, _I32, ctypes.c_int64]),
     "kvc_get_option": (_I32, [_P, _I32, ctypes.POINTER(ctypes.c_int64)]),
@@ -330,6 +333,24 @@ class PagedKVCache:
         self._check(self.lib.kvc_get_plan_shape(self._ctx, ctypes.byref(items), ctypes.byref(rows)),
                     "get_plan_shape")
         return {"work_items": items.value, "group_rows": rows.value}
+
+    def get_split_partials(self, stream=None):
+        """The split partials of the latest run: (lse [MAX_SPLITS, H, tiles, 32]
+        float32 base-2 log-sum-exps, o [MAX_SPLITS, H, tiles, D/32, 4, 64, 4]
+        raw 16-bit normalised outputs); see kvc_get_split_partials."""
+        nl, no = ctypes.c_int64(), ctypes.c_int64()
+        self._check(self.lib.kvc_get_split_partials(self._ctx, None, 0, None, 0, ctypes.byref(nl), ctypes.byref(no),
+                                                    None), "get_split_partials")
+        lse = np.zeros(nl.value, np.float32)
+        o = np.zeros(no.value, np.uint16)
+        hs = self._stream(stream)
+        self._check(self.lib.kvc_get_split_partials(self._ctx, lse.ctypes.data_as(ctypes.POINTER(ctypes.c_float)),
+                                                    lse.size, o.ctypes.data_as(ctypes.POINTER(ctypes.c_uint16)),
+                                                    o.size, ctypes.byref(nl), ctypes.byref(no), hs),
+                    "get_split_partials")
+        H, D = self.cfg.num_heads, self.cfg.head_dim
+        tiles = nl.value // (MAX_SPLITS * H * 32)
+        return lse.reshape(MAX_SPLITS, H, tiles, 32), o.reshape(MAX_SPLITS, H, tiles, D // 32, 4, 64, 4)
 
     def get_plan_image(self) -> np.ndarray:
         """The int32 plan image that kvc_plan uploads for the kernels."""

@@ -636,6 +636,27 @@ kvc_status kvc_get_plan_image(const kvc_ctx* c, int32_t* buf, int32_t capacity, 
   return KVC_OK;
 }
 
+kvc_status kvc_get_split_partials(const kvc_ctx* c, float* lse, int64_t cap_lse, uint16_t* o, int64_t cap_o,
+                                  int64_t* n_lse, int64_t* n_o, kvc_stream_t hs) {
+  if (!c) return KVC_ERR_ARG;
+  kvc_ctx* m = const_cast<kvc_ctx*>(c);
+  if (!c->have_plan) return fail(m, KVC_ERR_STATE, "no plan");
+  const size_t rows = (size_t)c->cfg.tiles_capacity() * KVC_Q_TILE32;
+  const int64_t nl = (int64_t)KVC_MAX_SPLITS * (int64_t)rows * c->cfg.num_heads;
+  const int64_t no = nl * c->cfg.head_dim;
+  if (n_lse) *n_lse = nl;
+  if (n_o) *n_o = no;
+  if ((lse && cap_lse < nl) || (o && cap_o < no)) return fail(m, KVC_ERR_ARG, "capacity too small");
+  if (c->metadata_only) return fail(m, KVC_ERR_STATE, "metadata-only context has no device buffers");
+  hipError_t e = hipStreamSynchronize((hipStream_t)hs);
+  if (e == hipSuccess && lse)
+    e = hipMemcpy(lse, c->workspace + c->lay.lse, (size_t)nl * sizeof(float), hipMemcpyDeviceToHost);
+  if (e == hipSuccess && o)
+    e = hipMemcpy(o, c->workspace + c->lay.part_o, (size_t)no * sizeof(uint16_t), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(m, e, "copy of the split partials");
+  return KVC_OK;
+}
+
 kvc_status kvc_get_stats(const kvc_ctx* c, int32_t stream, kvc_stats* out) {
   if (!c || !out) return KVC_ERR_ARG;
   if (stream < 0 || stream >= c->cfg.num_streams) return KVC_ERR_ARG;

@@ -231,6 +231,7 @@ class Harness:
         res["ora_plan"] = ora_plan
         res["gpu_plan"] = self.gpu.get_plan()
         res["out_bits"] = {b: out.view(self.torch.int16).cpu().numpy().view(np.uint16) for b, (q, out) in outs.items()}
+        res["q_bits"] = {b: q for b, (q, out) in outs.items()}
         if check:
             res["ref"] = {b: self.ora.attend(ora_plan, b, q) for b, (q, out) in outs.items() if b in self.ora.pools}
         for s in act:
