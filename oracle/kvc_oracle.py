@@ -39,13 +39,18 @@ the design notes of the repository):
   * several streams share one pool per block and one pair of free lists and
     advance in ascending stream order inside a step; each stream attends only
     to its own pages (batch-prefill semantics of [p1] §Plan Reuse and Kernel
-    Optimization).
+    Optimization);
+  * the rotary embedding turns interleaved pairs (2i, 2i+1) of each head by
+    angles from caller-supplied cos/sin tables [T, D/2] (the pages give no
+    frequencies), computed in float64 and rounded once to the element type.
 
 Parity pins: every function here is pinned by the CPU tests (worked example of
 [p3] §Inspecting Cache Statistics, closed forms, invariants, PyTorch's
 scaled_dot_product_attention and logsumexp as second routines, brute force on
 tiny inputs, the split-KV merge identity, paged-vs-dense identity and page-ID
-permutation invariance), and planted mistakes in each are caught by some pin.
+permutation invariance; for the rotary embedding: brute-force nearest
+rounding, the identity and quarter-turn rotations, complex multiplication,
+norm preservation, composition and the relative-position identity), and planted mistakes in each are caught by some pin.
 """
 from __future__ import annotations
 
@@ -418,6 +423,49 @@ def lse_base2_fp64(q_bits: np.ndarray, k_bits: np.ndarray, dtype: str = "bf16") 
         m = s.max(axis=1)
         out[:, h] = (m + np.log(np.exp(s - m[:, None]).sum(axis=1))) / math.log(2.0)
     return out
+
+
+def round_to_elem(x: np.ndarray, dtype: str = "bf16") -> np.ndarray:
+    """float64 values rounded to the nearest 16-bit value of the element type
+    (ties to even), as uint16 bit patterns.  bf16: 8 significant bits and the
+    float32 exponent range; the values here are finite and, when non-zero,
+    normal."""
+    x = np.asarray(x, dtype=np.float64)
+    if dtype == "f16":
+        return x.astype(np.float16).view(np.uint16)
+    m, e = np.frexp(x)                                  # x = m 2^e, 0.5 <= |m| < 1
+    r = np.rint(m * 256.0) * np.exp2(e.astype(np.float64) - 8.0)   # 8 significant bits, ties to even
+    return (r.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def rope_rotate_fp64(x_bits: np.ndarray, cos: np.ndarray, sin: np.ndarray, dtype: str = "bf16") -> np.ndarray:
+    """Rotary position embedding applied to query or key rows before they
+    enter the cache ([p2] "How LingBot-Map Uses FlashInfer KV Cache for
+    Streaming 3D Reconstruction" §3D RoPE Position Encoding and its FAQ on
+    temporal information: positions are baked into q and k, so attention
+    needs no position lookup).  The pages name a 3-D rotary embedding but give
+    no frequency definition, so the angles are the caller's: cos and sin
+    [T, D/2] hold, for row t and pair i, the cosine and sine of the angle by
+    which elements (2i, 2i+1) of every head of that row turn (the pair read
+    as one complex number, multiplied by cos + i sin):
+        (a, b) -> (a cos - b sin, a sin + b cos),
+    in float64 from the exact 16-bit inputs and the tables' values.
+    x_bits [T, H, D]; returns float64 [T, H, D], not rounded."""
+    x = bits_to_f32(x_bits, dtype).astype(np.float64)
+    T, H, D = x.shape
+    c = np.asarray(cos, dtype=np.float64).reshape(T, 1, D // 2)
+    s = np.asarray(sin, dtype=np.float64).reshape(T, 1, D // 2)
+    a, b = x[:, :, 0::2], x[:, :, 1::2]
+    out = np.empty_like(x)
+    out[:, :, 0::2] = a * c - b * s
+    out[:, :, 1::2] = a * s + b * c
+    return out
+
+
+def rope_fp64(x_bits: np.ndarray, cos: np.ndarray, sin: np.ndarray, dtype: str = "bf16") -> np.ndarray:
+    """The rotated rows as they are stored: rope_rotate_fp64 rounded once to
+    the element type.  Returns uint16 bits [T, H, D]."""
+    return round_to_elem(rope_rotate_fp64(x_bits, cos, sin, dtype), dtype)
 
 
 def pool_bytes(cfg: OracleConfig, num_blocks: int) -> int:

@@ -511,6 +511,135 @@ def test_reset_replays_identically():
 
 
 # --------------------------------------------------------------------------
+# rotary embedding pins ([p2] "How LingBot-Map Uses FlashInfer KV Cache for
+# Streaming 3D Reconstruction" §3D RoPE Position Encoding): rounding by brute
+# force over every 16-bit pattern, rotations with known results, complex
+# multiplication as a second routine, and the two properties that make a
+# rotary embedding one (norm preservation, relative position)
+# --------------------------------------------------------------------------
+
+def _elem_table(dtype):
+    """Every finite non-negative value of the element type, ascending, with
+    its bit pattern."""
+    bits = np.arange(0x8000, dtype=np.uint32)
+    if dtype == "bf16":
+        with np.errstate(invalid="ignore"):
+            vals = (bits << 16).view(np.float32).astype(np.float64)
+    else:
+        vals = bits.astype(np.uint16).view(np.float16).astype(np.float64)
+    ok = np.isfinite(vals)
+    return vals[ok], bits[ok].astype(np.uint16)
+
+
+def _nearest_elem(x, dtype):
+    """IEEE round-to-nearest-even by search: the closest table value, the one
+    with an even bit pattern when two are equally close."""
+    vals, bits = _elem_table(dtype)
+    ax = np.abs(np.asarray(x, dtype=np.float64)).ravel()
+    hi = np.clip(np.searchsorted(vals, ax), 1, len(vals) - 1)
+    lo = hi - 1
+    dlo, dhi = ax - vals[lo], vals[hi] - ax
+    pick = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(bits[lo] % 2 == 0, lo, hi)))
+    out = bits[pick] | np.where(np.signbit(np.asarray(x, dtype=np.float64).ravel()), 0x8000, 0).astype(np.uint16)
+    return out.reshape(np.shape(x))
+
+
+def _rope_inputs(seed, T=6, H=3, D=16, dtype="bf16"):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, H, D)) * 2.0
+    bits = _nearest_elem(x, dtype)
+    theta = rng.uniform(-4 * math.pi, 4 * math.pi, (T, D // 2))
+    return bits, theta
+
+
+def pin_round_to_elem(oracle=ko, seed=13):
+    """round_to_elem is IEEE nearest-even, found by brute force: random values
+    over 60 binades, exact midpoints between neighbours (ties to the even
+    pattern), and values a hair past a midpoint, where rounding first to
+    float32 and then to bf16 would land on the tie and round the wrong way."""
+    rng = np.random.default_rng(seed)
+    for dtype, emax in (("bf16", 30), ("f16", 14)):
+        vals, _ = _elem_table(dtype)
+        x = rng.choice([-1.0, 1.0], 4000) * np.exp2(rng.uniform(-emax, emax, 4000))
+        normal = vals[(vals >= 2.0 ** -emax) & (vals < 2.0 ** emax)]
+        i = rng.integers(0, len(normal) - 1, 2000)
+        mid = 0.5 * (normal[i] + normal[i + 1])                     # exact in float64
+        hair = mid + np.ldexp(np.abs(mid), -40) * rng.choice([-1.0, 1.0], 2000)
+        for xs in (x, mid, -mid, hair, -hair, normal[i], -normal[i]):
+            got = oracle.round_to_elem(xs, dtype)
+            assert got.dtype == np.uint16 and np.array_equal(got, _nearest_elem(xs, dtype)), dtype
+
+
+def pin_rope_known_rotations(oracle=ko, seed=17):
+    """R_0 = I leaves every bit unchanged; a quarter turn maps (a, b) to
+    (-b, a) and a half turn to (-a, -b), exactly, for both element types;
+    rope_fp64 is the rotation rounded once to the nearest element value."""
+    for dtype in ("bf16", "f16"):
+        bits, theta = _rope_inputs(seed, dtype=dtype)
+        x = syn.bits_to_f32(bits, dtype).astype(np.float64)
+        one, zero = np.ones_like(theta), np.zeros_like(theta)
+        assert np.array_equal(oracle.rope_fp64(bits, one, zero, dtype), bits)
+        quarter = oracle.rope_rotate_fp64(bits, zero, one, dtype)
+        assert np.array_equal(quarter[..., 0::2], -x[..., 1::2]) and np.array_equal(quarter[..., 1::2], x[..., 0::2])
+        half = oracle.rope_rotate_fp64(bits, -one, zero, dtype)
+        assert np.array_equal(half, -x)
+        c, s = np.cos(theta), np.sin(theta)
+        assert np.array_equal(oracle.rope_fp64(bits, c, s, dtype),
+                              _nearest_elem(oracle.rope_rotate_fp64(bits, c, s, dtype), dtype))
+
+
+def pin_rope_complex(oracle=ko, seed=19):
+    """Each pair (x[2i], x[2i+1]) read as a complex number and multiplied by
+    cos(theta) + i sin(theta), with NumPy's complex arithmetic."""
+    bits, theta = _rope_inputs(seed, T=9, H=4, D=32)
+    x = syn.bits_to_f32(bits, "bf16").astype(np.float64)
+    z = (x[..., 0::2] + 1j * x[..., 1::2]) * (np.cos(theta) + 1j * np.sin(theta))[:, None, :]
+    got = oracle.rope_rotate_fp64(bits, np.cos(theta), np.sin(theta))
+    assert np.allclose(got[..., 0::2], z.real, rtol=0, atol=1e-14)
+    assert np.allclose(got[..., 1::2], z.imag, rtol=0, atol=1e-14)
+
+
+def pin_rope_norm_and_relative_position(oracle=ko, seed=23, D=32, base=10000.0):
+    """With angles theta[t, i] = p_t * w_i (one frequency per pair), the
+    rotation keeps every pair's length, and the score of a rotated query
+    against a rotated key depends only on the position difference:
+    <R(p) q, R(p') k> = <q, R(p' - p) k>."""
+    rng = np.random.default_rng(seed)
+    T, H = 12, 3
+    w = base ** (-np.arange(D // 2) * 2.0 / D)
+    pq, pk = rng.integers(0, 5000, T), rng.integers(0, 5000, T)
+    qb = _nearest_elem(rng.standard_normal((T, H, D)), "bf16")
+    kb = _nearest_elem(rng.standard_normal((T, H, D)), "bf16")
+
+    def rot(bits, pos):
+        ang = pos[:, None] * w[None, :]
+        return oracle.rope_rotate_fp64(bits, np.cos(ang), np.sin(ang))
+    q = syn.bits_to_f32(qb, "bf16").astype(np.float64)
+    rq = rot(qb, pq)
+    n0 = q[..., 0::2] ** 2 + q[..., 1::2] ** 2
+    assert np.allclose(rq[..., 0::2] ** 2 + rq[..., 1::2] ** 2, n0, rtol=1e-13, atol=0)
+    lhs = np.einsum("thd,thd->th", rq, rot(kb, pk))
+    rhs = np.einsum("thd,thd->th", q, rot(kb, pk - pq))
+    assert np.allclose(lhs, rhs, rtol=0, atol=1e-9)
+
+
+def test_round_to_elem_is_nearest_even():
+    pin_round_to_elem()
+
+
+def test_rope_known_rotations():
+    pin_rope_known_rotations()
+
+
+def test_rope_is_complex_multiplication():
+    pin_rope_complex()
+
+
+def test_rope_norm_and_relative_position():
+    pin_rope_norm_and_relative_position()
+
+
+# --------------------------------------------------------------------------
 # planted mistakes: each must be caught by at least one pin
 # --------------------------------------------------------------------------
 
@@ -627,6 +756,65 @@ def _lse_unscaled(q_bits, k_bits, dtype="bf16"):
     return out
 
 
+def _rope_parts(x_bits, cos, sin, dtype):
+    x = syn.bits_to_f32(x_bits, dtype).astype(np.float64)
+    T, H, D = x.shape
+    return x, np.asarray(cos, np.float64).reshape(T, 1, D // 2), np.asarray(sin, np.float64).reshape(T, 1, D // 2)
+
+
+def _rope_sign_slip(x_bits, cos, sin, dtype="bf16"):
+    x, c, s = _rope_parts(x_bits, cos, sin, dtype)
+    out = np.empty_like(x)
+    out[..., 0::2] = x[..., 0::2] * c + x[..., 1::2] * s      # + where - belongs
+    out[..., 1::2] = x[..., 0::2] * s + x[..., 1::2] * c
+    return out
+
+
+def _rope_dropped_term(x_bits, cos, sin, dtype="bf16"):
+    x, c, s = _rope_parts(x_bits, cos, sin, dtype)
+    out = np.empty_like(x)
+    out[..., 0::2] = x[..., 0::2] * c - x[..., 1::2] * s
+    out[..., 1::2] = x[..., 1::2] * c                         # a sin dropped
+    return out
+
+
+def _rope_rotate_half(x_bits, cos, sin, dtype="bf16"):
+    x, c, s = _rope_parts(x_bits, cos, sin, dtype)
+    h = x.shape[2] // 2
+    a, b = x[..., :h], x[..., h:]                             # pairs (i, i + D/2)
+    return np.concatenate([a * c - b * s, a * s + b * c], axis=2)
+
+
+def _rope_inverse(x_bits, cos, sin, dtype="bf16"):
+    x, c, s = _rope_parts(x_bits, cos, sin, dtype)
+    out = np.empty_like(x)
+    out[..., 0::2] = x[..., 0::2] * c + x[..., 1::2] * s      # turns by -theta
+    out[..., 1::2] = -x[..., 0::2] * s + x[..., 1::2] * c
+    return out
+
+
+def _round_truncates(x, dtype="bf16"):
+    if dtype == "f16":
+        return ko.round_to_elem(x, dtype)
+    return (np.asarray(x, np.float64).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _round_via_f32(x, dtype="bf16"):
+    if dtype == "f16":
+        return ko.round_to_elem(x, dtype)
+    return ko.round_to_elem(np.asarray(x, np.float64).astype(np.float32).astype(np.float64), dtype)
+
+
+def _round_ties_away(x, dtype="bf16"):
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    r = np.trunc(m * (256.0 if dtype == "bf16" else 2048.0) + np.copysign(0.5, m))
+    r = r * np.exp2(e.astype(np.float64) - (8.0 if dtype == "bf16" else 11.0))
+    if dtype == "f16":
+        return r.astype(np.float16).view(np.uint16)
+    return (r.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
 def _pins_fail(mutant, pins):
     for pin in pins:
         try:
@@ -638,7 +826,8 @@ def _pins_fail(mutant, pins):
 
 ALL_PINS = [pin_worked_example, pin_special_closed_forms, pin_visible_set, pin_sdpa, pin_bruteforce,
             pin_softmax_invariants, pin_paged_equals_dense, pin_scale_phase, pin_rollback, pin_f16_inputs,
-            pin_lse_base2]
+            pin_lse_base2, pin_round_to_elem, pin_rope_known_rotations, pin_rope_complex,
+            pin_rope_norm_and_relative_position]
 
 
 @pytest.mark.parametrize("mutant", [
@@ -656,9 +845,18 @@ ALL_PINS = [pin_worked_example, pin_special_closed_forms, pin_visible_set, pin_s
     _Mutant(lse_base2_fp64=_lse_natural_log),
     _Mutant(lse_base2_fp64=_lse_max_only),
     _Mutant(lse_base2_fp64=_lse_unscaled),
+    _Mutant(rope_rotate_fp64=_rope_sign_slip),
+    _Mutant(rope_rotate_fp64=_rope_dropped_term),
+    _Mutant(rope_rotate_fp64=_rope_rotate_half),
+    _Mutant(rope_rotate_fp64=_rope_inverse),
+    _Mutant(round_to_elem=_round_truncates),
+    _Mutant(round_to_elem=_round_via_f32),
+    _Mutant(round_to_elem=_round_ties_away),
 ], ids=["no_scale", "values_are_keys", "wrong_softmax_axis", "window_off_by_one", "specials_first",
         "last_page_zero", "scale_evicted", "special_count_drift", "one_frame_per_step", "rollback_no_refill",
-        "f16_read_as_bf16", "lse_natural_log", "lse_max_only", "lse_unscaled"])
+        "f16_read_as_bf16", "lse_natural_log", "lse_max_only", "lse_unscaled", "rope_sign_slip",
+        "rope_dropped_term", "rope_rotate_half", "rope_inverse", "round_truncates", "round_via_f32",
+        "round_ties_away"])
 def test_planted_mistake_is_caught(mutant):
     # OracleStream inside the mutant must use the mutant's allocator
     class _Stream(ko.OracleStream):
