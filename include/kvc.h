@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 6
+#define KVC_ABI_VERSION 7
 
 typedef struct kvc_ctx kvc_ctx;
 typedef void* kvc_stream_t;   /* hipStream_t */
@@ -130,13 +130,14 @@ enum {
                                     (default: what the device holds at once, 2 per CU for head_dim <= 64,
                                     1 per CU for 128) */
   KVC_OPT_MAX_SPLITS = 2,        /* cap on KV splits per stream; 1 disables split-KV (default 64, the maximum) */
-  KVC_OPT_PROFILE = 3,           /* 1: time every attention/merge/append launch with HIP events */
+  KVC_OPT_PROFILE = 3,           /* 1: time every attention/merge/append/rope launch with HIP events */
   KVC_OPT_DEFER_EVICTION = 4     /* 1: hold evicted window pages back until the stream's next frame,
                                     so that kvc_rollback can undo the latest frame (default 0) */
 };
 
 /* Kernels for kvc_profile_read. */
-enum { KVC_KERNEL_ATTENTION = 0, KVC_KERNEL_MERGE = 1, KVC_KERNEL_APPEND = 2 };
+enum { KVC_KERNEL_ATTENTION = 0, KVC_KERNEL_MERGE = 1, KVC_KERNEL_APPEND = 2, KVC_KERNEL_ROPE = 3 };
+#define KVC_NUM_KERNELS 4
 
 int32_t kvc_abi_version(void);
 const char* kvc_status_string(kvc_status status);
@@ -147,9 +148,9 @@ const char* kvc_status_string(kvc_status status);
 size_t kvc_pool_bytes(const kvc_config* cfg);
 
 /* Bytes of device workspace the caller allocates for kvc_create: two plan
- * buffers and the split-KV partial outputs (normalised bf16 outputs and float32
- * log-sum-exps), sized for the maximum
- * split count.  Returns 0 for an invalid configuration. */
+ * buffers, the split-KV partial outputs (normalised bf16 outputs and float32
+ * log-sum-exps) sized for the maximum split count, and the rotated query rows
+ * of kvc_run_rope.  Returns 0 for an invalid configuration. */
 size_t kvc_workspace_bytes(const kvc_config* cfg);
 
 /* Bytes of pinned (page-locked) host staging for the per-step plan upload,
@@ -226,6 +227,25 @@ kvc_status kvc_append_frame(kvc_ctx* ctx, int32_t stream, int32_t block, const v
 kvc_status kvc_append_frames(kvc_ctx* ctx, int32_t stream, int32_t block, const void* k, const void* v,
                              int32_t num_frames, kvc_stream_t hip_stream);
 
+/* kvc_append_frames with the rotary position embedding applied to K on its
+ * way into the pool ([p2] "How LingBot-Map Uses FlashInfer KV Cache for
+ * Streaming 3D Reconstruction" §3D RoPE Position Encoding and its FAQ on
+ * temporal information: positions are baked into q and k before the cache,
+ * so attention needs no position lookup).  The pages give no frequencies, so
+ * the angles are the caller's:
+ *   rope_cos, rope_sin: device float32 [num_frames * T, D/2], contiguous,
+ *   16-byte aligned; entry (t, i) is the cosine (sine) of the angle by which
+ *   elements (2i, 2i+1) of every head of k row t turn:
+ *     (a, b) -> (a cos - b sin, a sin + b cos).
+ * The rotation is computed in float64 (both products are exact there) and
+ * rounded once to the element type, nearest even.  V is stored as it is.
+ * Nothing is written to k, v or the tables.  Errors: as kvc_append_frames,
+ * and KVC_ERR_ARG for a null or misaligned table (a metadata-only context
+ * takes none). */
+kvc_status kvc_append_frames_rope(kvc_ctx* ctx, int32_t stream, int32_t block, const void* k, const void* v,
+                                  int32_t num_frames, const float* rope_cos, const float* rope_sin,
+                                  kvc_stream_t hip_stream);
+
 /* [p5] §Sliding-Window Eviction Strategy: move the oldest live-window pages
  * beyond the window back to the free list (host metadata only; scale pages
  * are kept).  Idempotent within a step.  With KVC_OPT_DEFER_EVICTION the
@@ -273,6 +293,16 @@ kvc_status kvc_plan(kvc_ctx* ctx, kvc_stream_t hip_stream);
  * Errors: KVC_ERR_ARG, KVC_ERR_STATE (not planned, or a planned stream has
  * not appended this block), KVC_ERR_HIP. */
 kvc_status kvc_run(kvc_ctx* ctx, int32_t block, const void* q, void* o, kvc_stream_t hip_stream);
+
+/* kvc_run with the rotary position embedding applied to the queries first
+ * (the same section as kvc_append_frames_rope, the same arithmetic):
+ *   rope_cos, rope_sin: device float32 [R, D/2], contiguous, 16-byte aligned,
+ *   rows in q's order.
+ * One pass writes the rotated rows into the workspace (q itself is not
+ * changed), then attention runs on them as kvc_run does.  Errors: as kvc_run,
+ * and KVC_ERR_ARG for a null or misaligned table. */
+kvc_status kvc_run_rope(kvc_ctx* ctx, int32_t block, const void* q, const float* rope_cos,
+                        const float* rope_sin, void* o, kvc_stream_t hip_stream);
 
 /* Size of the static device scratch behind kvc_run_no_alloc, per device. */
 #define KVC_NO_ALLOC_SCRATCH_BYTES ((size_t)64 << 20)

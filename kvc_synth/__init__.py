@@ -128,6 +128,37 @@ def free_list_order(seed: int, n: int, first_id: int, which: int) -> np.ndarray:
     return ids[g.permutation(n)].astype(np.int32)
 
 
+def rope_tables(frame0: int, num_frames: int, T: int, D: int, n_special: int, special_row_offset: int,
+                base: float = 100.0):
+    """Caller-side rotary tables for the rows of frames frame0 ..
+    frame0 + num_frames - 1 (global frame indices), as the caller of a
+    rotary embedding would build them: float32 cos and sin [num_frames * T,
+    D/2].  A stand-in for a 3-D layout: the D/2 pairs are split into three
+    bands that turn with the frame index, the patch's row and its column on a
+    near-square grid of the frame's patches (special tokens sit at row and
+    column 0); band j of size m has frequencies base^(-i/m), i < m.  These are
+    inputs, drawn the same way for both sides; no randomness is involved."""
+    half = D // 2
+    m = half // 3
+    sizes = (half - 2 * m, m, m)
+    P = T - n_special
+    width = max(1, int(np.ceil(np.sqrt(max(P, 1)))))
+    rows = np.arange(T)
+    is_special = (rows >= special_row_offset) & (rows < special_row_offset + n_special)
+    patch_idx = np.where(rows < special_row_offset, rows, rows - n_special)
+    py = np.where(is_special, 0, patch_idx // width).astype(np.float64)
+    px = np.where(is_special, 0, patch_idx % width).astype(np.float64)
+    cos = np.empty((num_frames * T, half), np.float32)
+    sin = np.empty_like(cos)
+    for f in range(num_frames):
+        pos = (np.full(T, float(frame0 + f)), py, px)
+        ang = np.concatenate([pos[j][:, None] * base ** (-np.arange(sizes[j]) / max(sizes[j], 1))[None, :]
+                              for j in range(3)], axis=1)
+        cos[f * T:(f + 1) * T] = np.cos(ang)
+        sin[f * T:(f + 1) * T] = np.sin(ang)
+    return cos, sin
+
+
 @dataclasses.dataclass(frozen=True)
 class Workload:
     """Shape of one synthetic frame stream workload."""

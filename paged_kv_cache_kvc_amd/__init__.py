@@ -44,9 +44,10 @@ DTYPES = {"bf16": KVC_DTYPE_BF16, "f16": KVC_DTYPE_F16}
 KVC_KERNEL_ATTENTION = 0
 KVC_KERNEL_MERGE = 1
 KVC_KERNEL_APPEND = 2
+KVC_KERNEL_ROPE = 3
 
 MAX_SPLITS = 64
-ABI_VERSION = 6   # KVC_ABI_VERSION of include/kvc.h
+ABI_VERSION = 7   # KVC_ABI_VERSION of include/kvc.h
 
 
 class KvcError(RuntimeError):
@@ -85,11 +86,13 @@ SIGNATURES = {
     "kvc_reset": (_I32, [_P]),
     "kvc_append_frame": (_I32, [_P, _I32, _I32, _P, _P, _P]),
     "kvc_append_frames": (_I32, [_P, _I32, _I32, _P, _P, _I32, _P]),
+    "kvc_append_frames_rope": (_I32, [_P, _I32, _I32, _P, _P, _I32, _P, _P, _P]),
     "kvc_evict": (_I32, [_P, _I32]),
     "kvc_rollback": (_I32, [_P, _I32]),
     "kvc_plan": (_I32, [_P, _P]),
     "kvc_run": (_I32, [_P, _I32, _P, _P, _P]),
     "kvc_run_no_alloc": (_I32, [_P, _I32, _P, _P, _P]),
+    "kvc_run_rope": (_I32, [_P, _I32, _P, _P, _P, _P, _P]),
     "kvc_get_plan": (_I32, [_P, _PI32, _PI32, _PI32, _PI32, _PI32, _PI32, _PI32, _I32, _I32, _PI32, _PI32]),
     "kvc_get_plan_shape": (_I32, [_P, _PI32, _PI32]),
     "kvc_get_plan_image": (_I32, [_P, _PI32, _I32, _PI32]),
@@ -222,10 +225,28 @@ class PagedKVCache:
             raise KvcError(KVC_ERR_ARG, f"{name} must be a contiguous {self.elem_dtype} [{rows}, {c.num_heads}, "
                                         f"{c.head_dim}] tensor on {self.device}")
 
+    def _check_tables(self, rope, rows):
+        """Rotary tables (cos, sin): contiguous float32 [rows, D/2] tensors on
+        this device, 16-byte aligned."""
+        half = self.cfg.head_dim // 2
+        if not isinstance(rope, (tuple, list)) or len(rope) != 2:
+            raise KvcError(KVC_ERR_ARG, "rope must be a pair (cos, sin)")
+        for name, t in zip(("cos", "sin"), rope):
+            if t.dtype != self.torch.float32 or not t.is_contiguous() or t.device != self.device \
+                    or tuple(t.shape) != (rows, half) or t.data_ptr() % 16:
+                raise KvcError(KVC_ERR_ARG, f"rope {name} must be a contiguous 16-byte aligned float32 "
+                                            f"[{rows}, {half}] tensor on {self.device}")
+        return rope[0].data_ptr(), rope[1].data_ptr()
+
     # -- the method ------------------------------------------------------
-    def append_frame(self, block_idx: int, k=None, v=None, stream_id: int = 0, stream=None):
+    def append_frame(self, block_idx: int, k=None, v=None, stream_id: int = 0, stream=None, rope=None):
         """Write one frame's K and V ([T, H, D] bf16) of one block; at block 0
-        this also allocates the frame's patch page and special slots."""
+        this also allocates the frame's patch page and special slots.  rope =
+        (cos, sin), float32 [T, D/2] each, turns K by those angles on the way
+        into the pool (kvc_append_frames_rope)."""
+        if rope is not None:
+            self.append_frames(block_idx, k, v, 1, stream_id, stream, rope)
+            return
         if self.metadata_only:
             rc = self.lib.kvc_append_frame(self._ctx, stream_id, block_idx, None, None, None)
         else:
@@ -239,13 +260,16 @@ class PagedKVCache:
             self._planned = False
 
     def append_frames(self, block_idx: int, k=None, v=None, num_frames: Optional[int] = None, stream_id: int = 0,
-                      stream=None):
+                      stream=None, rope=None):
         """Write several frames' K and V ([F, T, H, D] or [F*T, H, D] bf16) of
         one block in one step (the scale phase); at block 0 this also
-        allocates the F frames, all or none."""
+        allocates the F frames, all or none.  rope = (cos, sin), float32
+        [F*T, D/2] each, turns K by those angles on the way into the pool."""
         if self.metadata_only:
             if num_frames is None:
                 raise KvcError(KVC_ERR_ARG, "num_frames is required without tensors")
+            if rope is not None:
+                raise KvcError(KVC_ERR_ARG, "a metadata-only cache takes no rotary tables")
             rc = self.lib.kvc_append_frames(self._ctx, stream_id, block_idx, None, None, num_frames, None)
         else:
             T = self.cfg.tokens_per_frame
@@ -256,8 +280,13 @@ class PagedKVCache:
             v2 = v.reshape(F * T, *v.shape[-2:])
             self._check_tensor(k2, F * T, "k")
             self._check_tensor(v2, F * T, "v")
-            rc = self.lib.kvc_append_frames(self._ctx, stream_id, block_idx, k2.data_ptr(), v2.data_ptr(), F,
-                                            self._stream(stream))
+            if rope is None:
+                rc = self.lib.kvc_append_frames(self._ctx, stream_id, block_idx, k2.data_ptr(), v2.data_ptr(), F,
+                                                self._stream(stream))
+            else:
+                cp, sp = self._check_tables(rope, F * T)
+                rc = self.lib.kvc_append_frames_rope(self._ctx, stream_id, block_idx, k2.data_ptr(), v2.data_ptr(),
+                                                     F, cp, sp, self._stream(stream))
         self._check(rc, "append_frames")
         if block_idx == 0:
             self._planned = False
@@ -277,12 +306,13 @@ class PagedKVCache:
         self._check(rc, "plan")
         self._planned = True
 
-    def compute_attention(self, block_idx: int, q, out=None, stream=None, no_alloc: bool = False):
+    def compute_attention(self, block_idx: int, q, out=None, stream=None, no_alloc: bool = False, rope=None):
         """Paged attention of the step's queries q [R, H, D] for one block;
         plans first when called for block 0 of an unplanned step.  no_alloc
         runs kvc_run_no_alloc (split partials in the library's static device
         scratch); out must then be given, since allocating it would defeat
-        the purpose."""
+        the purpose.  rope = (cos, sin), float32 [R, D/2] each, turns the
+        queries by those angles first (kvc_run_rope)."""
         if block_idx == 0 and not self._planned:
             self.plan(stream)
         rows = q.shape[0]
@@ -293,6 +323,14 @@ class PagedKVCache:
             out = self.torch.empty_like(q)
         else:
             self._check_tensor(out, rows, "out")
+        if rope is not None:
+            if no_alloc:
+                raise KvcError(KVC_ERR_ARG, "the rotary embedding runs through the workspace, not no_alloc")
+            cp, sp = self._check_tables(rope, rows)
+            rc = self.lib.kvc_run_rope(self._ctx, block_idx, q.data_ptr(), cp, sp, out.data_ptr(),
+                                       self._stream(stream))
+            self._check(rc, "compute_attention")
+            return out
         fn = self.lib.kvc_run_no_alloc if no_alloc else self.lib.kvc_run
         rc = fn(self._ctx, block_idx, q.data_ptr(), out.data_ptr(), self._stream(stream))
         self._check(rc, "compute_attention")

@@ -39,9 +39,10 @@ kvc::Config to_cfg(const kvc_config& c) {
   return k;
 }
 
-// Workspace layout: [plan 0][plan 1][partial lse][partial o], 256-byte aligned.
+// Workspace layout: [plan 0][plan 1][partial lse][partial o][rotated q],
+// 256-byte aligned.
 struct Layout {
-  size_t plan_bytes, plan0, plan1, lse, part_o, total;
+  size_t plan_bytes, plan0, plan1, lse, part_o, q_rot, total;
 };
 
 Layout layout_of(const kvc::Config& c) {
@@ -53,7 +54,9 @@ Layout layout_of(const kvc::Config& c) {
   // partial outputs are stored per query tile of KVC_Q_TILE32 rows
   const size_t rows = (size_t)c.tiles_capacity() * KVC_Q_TILE32;
   l.part_o = l.lse + align_up((size_t)KVC_MAX_SPLITS * rows * c.num_heads * sizeof(float), 256);
-  l.total = l.part_o + align_up((size_t)KVC_MAX_SPLITS * rows * c.num_heads * c.head_dim * sizeof(uint16_t), 256);
+  l.q_rot = l.part_o + align_up((size_t)KVC_MAX_SPLITS * rows * c.num_heads * c.head_dim * sizeof(uint16_t), 256);
+  // the step's query rows after the rotary embedding of kvc_run_rope
+  l.total = l.q_rot + align_up(rows * c.num_heads * c.head_dim * sizeof(uint16_t), 256);
   return l;
 }
 
@@ -89,10 +92,10 @@ struct kvc_ctx {
   int cu_count = 256;
 
   bool profile = false;
-  std::vector<EventPair> pending[3];
+  std::vector<EventPair> pending[KVC_NUM_KERNELS];
   std::vector<hipEvent_t> spare;
-  double prof_ms[3] = {0, 0, 0};
-  int64_t prof_n[3] = {0, 0, 0};
+  double prof_ms[KVC_NUM_KERNELS] = {};
+  int64_t prof_n[KVC_NUM_KERNELS] = {};
 
   std::string err;
 };
@@ -170,7 +173,7 @@ size_t kvc_staging_bytes(const kvc_config* cfg) {
 }
 
 // Attention work-groups the device holds at once: one per CU (the 32x32
-// kernel of head_dim 32 and 64 holds a 6-stage LDS ring and one wave per
+// kernel of head_dim 32 and 64 holds a 128 KiB LDS ring and two waves per
 // SIMD; the 16x16 kernel of head_dim 128 one work-group's registers).
 static int32_t resident_workgroups(const kvc::Config& c, int cu_count) {
   (void)c;
@@ -284,7 +287,7 @@ kvc_status kvc_destroy(kvc_ctx* c) {
         (void)hipEventSynchronize(c->staging_done[i]);
         (void)hipEventDestroy(c->staging_done[i]);
       }
-    for (int k = 0; k < 3; ++k)
+    for (int k = 0; k < KVC_NUM_KERNELS; ++k)
       for (auto& e : c->pending[k]) {
         (void)hipEventSynchronize(e.stop);
         (void)hipEventDestroy(e.start);
@@ -313,29 +316,47 @@ kvc_status kvc_reset(kvc_ctx* c) {
 }
 
 static kvc_status append_frames_impl(kvc_ctx* c, int32_t stream, int32_t block, const void* k, const void* v,
-                                     int32_t num_frames, kvc_stream_t hs);
+                                     int32_t num_frames, const float* rope_cos, const float* rope_sin, bool rope,
+                                     kvc_stream_t hs);
 
 kvc_status kvc_append_frames(kvc_ctx* c, int32_t stream, int32_t block, const void* k, const void* v,
                              int32_t num_frames, kvc_stream_t hs) {
   if (!c) return KVC_ERR_ARG;
   try {
-    return append_frames_impl(c, stream, block, k, v, num_frames, hs);
+    return append_frames_impl(c, stream, block, k, v, num_frames, nullptr, nullptr, false, hs);
   } catch (const std::bad_alloc&) {
     return fail(c, KVC_ERR_HOST_ALLOC, "host allocation failed");
   }
 }
 
+kvc_status kvc_append_frames_rope(kvc_ctx* c, int32_t stream, int32_t block, const void* k, const void* v,
+                                  int32_t num_frames, const float* rope_cos, const float* rope_sin,
+                                  kvc_stream_t hs) {
+  if (!c) return KVC_ERR_ARG;
+  try {
+    return append_frames_impl(c, stream, block, k, v, num_frames, rope_cos, rope_sin, true, hs);
+  } catch (const std::bad_alloc&) {
+    return fail(c, KVC_ERR_HOST_ALLOC, "host allocation failed");
+  }
+}
+
+static bool table_ok(const float* t) { return t && ((uintptr_t)t & 15) == 0; }
+
 static kvc_status append_frames_impl(kvc_ctx* c, int32_t stream, int32_t block, const void* k, const void* v,
-                                     int32_t num_frames, kvc_stream_t hs) {
+                                     int32_t num_frames, const float* rope_cos, const float* rope_sin, bool rope,
+                                     kvc_stream_t hs) {
   const kvc::Config& cf = c->cfg;
   if (stream < 0 || stream >= cf.num_streams) return fail(c, KVC_ERR_ARG, "stream out of range");
   if (block < 0 || block >= cf.num_blocks) return fail(c, KVC_ERR_ARG, "block out of range");
   if (num_frames < 1 || num_frames > cf.max_frames_per_step)
     return fail(c, KVC_ERR_ARG, "num_frames must be in [1, max_frames_per_step]");
   if (c->metadata_only) {
-    if (k || v) return fail(c, KVC_ERR_ARG, "metadata-only context takes k = v = NULL");
+    if (k || v || rope_cos || rope_sin)
+      return fail(c, KVC_ERR_ARG, "metadata-only context takes k = v = NULL and no rotary tables");
   } else if (!k || !v || ((uintptr_t)k & 15) || ((uintptr_t)v & 15)) {
     return fail(c, KVC_ERR_ARG, "k and v must be 16-byte aligned device pointers");
+  } else if (rope && (!table_ok(rope_cos) || !table_ok(rope_sin))) {
+    return fail(c, KVC_ERR_ARG, "rope_cos and rope_sin must be 16-byte aligned device pointers");
   }
   const size_t bd = (size_t)stream * cf.num_blocks + block;
   kvc::FrameSlots* fs = &c->slots[(size_t)stream * cf.max_frames_per_step];
@@ -376,12 +397,19 @@ static kvc_status append_frames_impl(kvc_ctx* c, int32_t stream, int32_t block, 
   if (c->metadata_only) return KVC_OK;
 
   const size_t frame_bytes = (size_t)cf.tokens_per_frame * cf.num_heads * cf.head_dim * 2;
+  const size_t frame_table = (size_t)cf.tokens_per_frame * (cf.head_dim / 2);
   for (int32_t f = 0; f < num_frames; ++f) {
     kvc::AppendParams p;
     std::memset(&p, 0, sizeof(p));
     p.pool = c->pools[block];
     p.k = static_cast<const char*>(k) + f * frame_bytes;
     p.v = static_cast<const char*>(v) + f * frame_bytes;
+    if (rope) {
+      p.rope_cos = rope_cos + f * frame_table;
+      p.rope_sin = rope_sin + f * frame_table;
+    }
+    p.head_dim = cf.head_dim;
+    p.dtype = cf.dtype;
     p.T = cf.tokens_per_frame;
     p.row_elems = cf.num_heads * cf.head_dim;
     p.special_row_offset = cf.special_row_offset;
@@ -557,6 +585,32 @@ kvc_status kvc_run(kvc_ctx* c, int32_t block, const void* q, void* o, kvc_stream
                     c->workspace + c->lay.part_o);
 }
 
+kvc_status kvc_run_rope(kvc_ctx* c, int32_t block, const void* q, const float* rope_cos, const float* rope_sin,
+                        void* o, kvc_stream_t hs) {
+  if (!c) return KVC_ERR_ARG;
+  kvc_status rc = check_run(c, block, q, o);
+  if (rc != KVC_OK) return rc;
+  if (!table_ok(rope_cos) || !table_ok(rope_sin))
+    return fail(c, KVC_ERR_ARG, "rope_cos and rope_sin must be 16-byte aligned device pointers");
+  const kvc::Config& cf = c->cfg;
+  void* qr = c->workspace + c->lay.q_rot;
+  kvc::RopeParams r;
+  std::memset(&r, 0, sizeof(r));
+  r.x = q;
+  r.y = qr;
+  r.cos = rope_cos;
+  r.sin = rope_sin;
+  r.row_elems = cf.num_heads * cf.head_dim;
+  r.head_dim = cf.head_dim;
+  r.dtype = cf.dtype;
+  r.chunks = (int64_t)c->plan.qo_indptr.back() * (r.row_elems / 8);
+  if (r.chunks >= ((int64_t)1 << 31)) return fail(c, KVC_ERR_UNSUPPORTED, "more than 2^31 query chunks");
+  const int e = timed(c, KVC_KERNEL_ROPE, hs, [&] { return kvc::launch_rope(r, hs); });
+  if (e) return hip_fail(c, e, "rope launch");
+  return launch_run(c, block, qr, o, hs, reinterpret_cast<float*>(c->workspace + c->lay.lse),
+                    c->workspace + c->lay.part_o);
+}
+
 // Bytes of split partials one plan writes, laid out as in the workspace
 // ([split][head][query tile] lse rows, then the outputs), for the plan's
 // largest split count rather than the workspace's maximum.
@@ -708,7 +762,7 @@ kvc_status kvc_get_option(const kvc_ctx* c, int32_t option, int64_t* value) {
 }
 
 kvc_status kvc_profile_read(kvc_ctx* c, int32_t kernel, double* total_ms, int64_t* launches, int32_t reset) {
-  if (!c || kernel < 0 || kernel > 2) return KVC_ERR_ARG;
+  if (!c || kernel < 0 || kernel >= KVC_NUM_KERNELS) return KVC_ERR_ARG;
   for (auto& ev : c->pending[kernel]) {
     hipError_t e = hipEventSynchronize(ev.stop);
     if (e != hipSuccess) return hip_fail(c, e, "profile event");

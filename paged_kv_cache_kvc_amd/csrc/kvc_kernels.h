@@ -17,6 +17,22 @@ struct AppendParams {
   int32_t special_row_offset, n_special, page_size;
   int32_t patch_page, sp_slot0, n_sp_pages;
   int32_t sp_pages[KVC_MAX_APPEND_SPECIAL_PAGES];
+  // rotary embedding of K: float32 [T, D/2] cos and sin of this frame's
+  // rows, 16-byte aligned, or both null to store K as it is
+  const float* rope_cos;
+  const float* rope_sin;
+  int32_t head_dim;
+  int32_t dtype;            // element type: 0 bfloat16, 1 float16
+};
+
+struct RopeParams {
+  const void* x;            // [rows, H, D] 16-bit elements
+  void* y;                  // same shape, written; must not overlap x
+  const float* cos;         // [rows, D/2] float32, 16-byte aligned
+  const float* sin;
+  int64_t chunks;           // rows * H * D / 8
+  int32_t row_elems, head_dim;
+  int32_t dtype;
 };
 
 struct AttnParams {
@@ -52,6 +68,7 @@ struct MergeParams {
 
 // Return 0 on success or the hipError_t value.
 int launch_append(const AppendParams& p, void* hip_stream);
+int launch_rope(const RopeParams& p, void* hip_stream);
 int launch_attention(const AttnParams& p, int32_t grid, void* hip_stream);     // 16x16 kernel, head_dim 128
 int launch_attention32(const AttnParams& p, int32_t grid, void* hip_stream);   // 32x32 kernel, head_dim 32, 64
 int launch_merge(const MergeParams& p, void* hip_stream);

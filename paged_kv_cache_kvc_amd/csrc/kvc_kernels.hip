@@ -12,6 +12,10 @@
 //                    Cache for Streaming 3D Reconstruction" §Attention Kernel
 //                    Execution; [p5] §Kernel Dispatch and Sequence Lengths).
 //   merge_kernel   - combines the KV splits of a row in fixed split order.
+//   rope_kernel    - rotary position embedding of the step's query rows with
+//                    caller tables ([p2] §3D RoPE Position Encoding); the
+//                    key rows are turned inside append_kernel on their way to
+//                    the pool.
 //
 // Layouts: pool [pages, 2, page_size, H, D] bf16 (NHD inside a page, [p1]
 // "How FlashInfer KV Cache Attention Accelerates Streaming 3D Reconstruction
@@ -43,8 +47,69 @@ namespace {
 using namespace dev;
 
 // ---------------------------------------------------------------------------
+// rotary position embedding
+// ---------------------------------------------------------------------------
+// Positions are applied to q and k before the cache, so attention needs no
+// position lookup ([p2] "How LingBot-Map Uses FlashInfer KV Cache for
+// Streaming 3D Reconstruction" §3D RoPE Position Encoding and its FAQ on
+// temporal information).  The pages give no frequencies: the caller passes
+// float32 tables cos, sin [rows, D/2], entry (t, i) turning elements
+// (2i, 2i+1) of every head of row t as (a, b) -> (a c - b s, a s + b c).
+//
+// The rotation is computed in float64.  A product of a 16-bit element and a
+// float32 table value has at most 35 significant bits, so both products are
+// exact there and the only roundings are the sum's (to float64) and the final
+// one to the element type, done as a single rounding to nearest even: the
+// value is first narrowed to float32 toward zero with the discarded bits
+// kept as a sticky last bit (round to odd, 24 >= 11 + 2 bits), which a
+// second rounding to 8 or 11 bits cannot tell from the float64 value.
+__device__ __forceinline__ float f64_to_f32_odd(double x) {
+  const float t = __double2float_rz(x);
+  return __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, t) | ((double)t != x ? 1u : 0u));
+}
+
+template <int E>
+__device__ __forceinline__ double elem_to_f64(uint32_t w, int half);
+template <>
+__device__ __forceinline__ double elem_to_f64<0>(uint32_t w, int half) {
+  return (double)__builtin_bit_cast(float, half ? (w & 0xFFFF0000u) : (w << 16));
+}
+template <>
+__device__ __forceinline__ double elem_to_f64<1>(uint32_t w, int half) {
+  return (double)(float)__builtin_bit_cast(_Float16, (uint16_t)(half ? (w >> 16) : (w & 0xFFFFu)));
+}
+
+template <int E>
+__device__ __forceinline__ uint32_t f64_to_elem(double x);
+template <>
+__device__ __forceinline__ uint32_t f64_to_elem<0>(double x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, f64_to_f32_odd(x));
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+template <>
+__device__ __forceinline__ uint32_t f64_to_elem<1>(double x) {
+  return __builtin_bit_cast(uint16_t, (_Float16)f64_to_f32_odd(x));
+}
+
+// One 16-byte chunk: four (even, odd) pairs, each 32-bit word one pair.
+template <int E>
+__device__ __forceinline__ u32x4 rope_chunk(const u32x4& x, const f32x4& c, const f32x4& s) {
+  u32x4 y;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const double a = elem_to_f64<E>(x[j], 0), b = elem_to_f64<E>(x[j], 1);
+    const double cj = (double)c[j], sj = (double)s[j];
+    y[j] = f64_to_elem<E>(a * cj - b * sj) | (f64_to_elem<E>(a * sj + b * cj) << 16);
+  }
+  return y;
+}
+
+// ---------------------------------------------------------------------------
 // append
 // ---------------------------------------------------------------------------
+// ROPE: -1 copies K as it is; 0 (bf16) or 1 (f16) turns it by row r of the
+// tables on the way.
+template <int ROPE>
 __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
   const int r = blockIdx.x;
   const int off = p.special_row_offset;
@@ -69,11 +134,33 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
   u32x4* dk = reinterpret_cast<u32x4*>(pool + (((size_t)page * 2 + 0) * p.page_size + slot) * p.row_elems);
   u32x4* dv = reinterpret_cast<u32x4*>(pool + (((size_t)page * 2 + 1) * p.page_size + slot) * p.row_elems);
   for (int i = threadIdx.x; i < 2 * chunks; i += blockDim.x) {
-    if (i < chunks)
-      dk[i] = sk[i];
-    else
+    if (i < chunks) {
+      if constexpr (ROPE >= 0) {
+        // pairs (8i mod D)/2 .. +4 of this row's table entries
+        const size_t t = (size_t)r * (p.head_dim >> 1) + (((i << 3) & (p.head_dim - 1)) >> 1);
+        dk[i] = rope_chunk<ROPE>(sk[i], *reinterpret_cast<const f32x4*>(p.rope_cos + t),
+                                 *reinterpret_cast<const f32x4*>(p.rope_sin + t));
+      } else {
+        dk[i] = sk[i];
+      }
+    } else {
       dv[i - chunks] = sv[i - chunks];
+    }
   }
+}
+
+// Query rows [rows, H, D] -> rotated rows, one 16-byte chunk per thread.
+template <int E>
+__global__ __launch_bounds__(256) void rope_kernel(RopeParams p) {
+  const uint32_t i = blockIdx.x * 256u + threadIdx.x;   // chunks < 2^31, checked by the host
+  if (i >= (uint32_t)p.chunks) return;
+  const uint32_t cpr = (uint32_t)p.row_elems >> 3;
+  const uint32_t row = i / cpr;
+  const uint32_t e0 = (i - row * cpr) << 3;
+  const size_t t = (size_t)row * (uint32_t)(p.head_dim >> 1) + ((e0 & (uint32_t)(p.head_dim - 1)) >> 1);
+  reinterpret_cast<u32x4*>(p.y)[i] =
+      rope_chunk<E>(reinterpret_cast<const u32x4*>(p.x)[i], *reinterpret_cast<const f32x4*>(p.cos + t),
+                    *reinterpret_cast<const f32x4*>(p.sin + t));
 }
 
 // ---------------------------------------------------------------------------
@@ -785,7 +872,28 @@ int no_alloc_scratch(void** ptr, size_t* bytes) {
 }
 
 int launch_append(const AppendParams& p, void* s) {
-  hipLaunchKernelGGL(append_kernel, dim3(p.T), dim3(256), 0, (hipStream_t)s, p);
+  const hipStream_t hs = (hipStream_t)s;
+  if (!p.rope_cos)
+    hipLaunchKernelGGL(append_kernel<-1>, dim3(p.T), dim3(256), 0, hs, p);
+  else if (p.dtype == 0)
+    hipLaunchKernelGGL(append_kernel<0>, dim3(p.T), dim3(256), 0, hs, p);
+  else if (p.dtype == 1)
+    hipLaunchKernelGGL(append_kernel<1>, dim3(p.T), dim3(256), 0, hs, p);
+  else
+    return (int)hipErrorInvalidValue;
+  return (int)hipGetLastError();
+}
+
+int launch_rope(const RopeParams& p, void* s) {
+  const hipStream_t hs = (hipStream_t)s;
+  if (p.chunks == 0) return 0;
+  const dim3 grid((unsigned)((p.chunks + 255) / 256));
+  if (p.dtype == 0)
+    hipLaunchKernelGGL(rope_kernel<0>, grid, dim3(256), 0, hs, p);
+  else if (p.dtype == 1)
+    hipLaunchKernelGGL(rope_kernel<1>, grid, dim3(256), 0, hs, p);
+  else
+    return (int)hipErrorInvalidValue;
   return (int)hipGetLastError();
 }
 

@@ -135,12 +135,14 @@ class Harness:
     blocks: how many block pools to exercise (block b draws its inputs with
     block index b).  real_patch(stream, frame) says whether a frame's patch
     rows are drawn (else zero; only for frames never visible at a checked
-    step)."""
+    step).  rope: K is appended through kvc_append_frames_rope and q run
+    through kvc_run_rope with the tables of kvc_synth.rope_tables for each
+    frame; the oracle sees rope_fp64 of the same rows."""
 
     def __init__(self, wl: syn.Workload, num_blocks: int = 1, q_scale: float = 1.0,
                  real_patch: Optional[Callable[[int, int], bool]] = None, orders=None,
                  options: Optional[Dict[int, int]] = None, device="cuda", oracle_blocks: Sequence[int] = (0,),
-                 max_frames_per_step: int = 1):
+                 max_frames_per_step: int = 1, rope: bool = False):
         import torch
         import paged_kv_cache_kvc_amd as kvc
         self.torch = torch
@@ -167,6 +169,16 @@ class Harness:
         self.kbuf = torch.empty((T, H, D), dtype=self.gpu.elem_dtype, device=device)
         self.vbuf = torch.empty_like(self.kbuf)
         self.device = device
+        self.rope = rope
+
+    def tables(self, f: int, n: int = 1):
+        """Rotary tables (float32 cos, sin [n * T, D/2]) of drawn frames f ..
+        f + n - 1."""
+        wl = self.wl
+        return syn.rope_tables(f, n, wl.tokens_per_frame, wl.head_dim, wl.num_special_tokens, wl.row_offset)
+
+    def tables_dev(self, tabs):
+        return tuple(self.torch.from_numpy(t).to(self.device) for t in tabs)
 
     def _frame(self, s, f, b, which):
         wl = self.wl
@@ -201,21 +213,28 @@ class Harness:
                 kv_cache[key] = (self._frame(s, f, b, "k"), self._frame(s, f, b, "v"))
             return kv_cache[key]
 
+        def frame_kv_oracle(s, f, b):
+            k, v = frame_kv(s, f, b)
+            if self.rope:
+                k = ko.rope_fp64(k, *self.tables(f), self.wl.dtype)
+            return k, v
+
         res = {"active": act, "frames": frames}
         run_blocks = list(range(self.nb)) if blocks_to_run is None else list(blocks_to_run)
         outs = {}
         for b in range(self.nb):
             for s in act:
+                rope = self.tables_dev(self.tables(frames[s], nf[s])) if self.rope else None
                 if nf[s] == 1:
                     k, v = frame_kv(s, frames[s], b)
                     self.to_dev(k, self.kbuf)
                     self.to_dev(v, self.vbuf)
-                    self.gpu.append_frame(b, self.kbuf, self.vbuf, stream_id=s)
+                    self.gpu.append_frame(b, self.kbuf, self.vbuf, stream_id=s, rope=rope)
                 else:
                     kvs = [frame_kv(s, frames[s] + j, b) for j in range(nf[s])]
                     kd = self.to_dev(np.concatenate([x[0] for x in kvs]))
                     vd = self.to_dev(np.concatenate([x[1] for x in kvs]))
-                    self.gpu.append_frames(b, kd, vd, num_frames=nf[s], stream_id=s)
+                    self.gpu.append_frames(b, kd, vd, num_frames=nf[s], stream_id=s, rope=rope)
             if b == 0:
                 for s in act:
                     self.gpu.evict_frames(s)
@@ -223,10 +242,16 @@ class Harness:
             if run and b in run_blocks:
                 q = np.concatenate([self._frame(s, frames[s] + j, b, "q") for s in act for j in range(nf[s])])
                 qd = self.to_dev(q)
-                out = self.gpu.compute_attention(b, qd)
+                if self.rope:
+                    tabs = [np.concatenate(x) for x in zip(*(self.tables(frames[s], nf[s]) for s in act))]
+                    out = self.gpu.compute_attention(b, qd, rope=self.tables_dev(tabs))
+                    res.setdefault("q_raw", {})[b] = q
+                    q = ko.rope_fp64(q, *tabs, self.wl.dtype)
+                else:
+                    out = self.gpu.compute_attention(b, qd)
                 outs[b] = (q, out)
         # oracle replay (allocator always; pools only for its blocks)
-        ora_plan = self.ora.step(act, lambda s, f, b: frame_kv(s, f + self.skew[s], b),
+        ora_plan = self.ora.step(act, lambda s, f, b: frame_kv_oracle(s, f + self.skew[s], b),
                                  frames=[nf[s] for s in act])
         res["ora_plan"] = ora_plan
         res["gpu_plan"] = self.gpu.get_plan()

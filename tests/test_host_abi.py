@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, n), n
         assert n in kvc.SIGNATURES, n
     assert set(kvc.SIGNATURES) == set(names)
-    assert lib.kvc_abi_version() == kvc.ABI_VERSION == 6
+    assert lib.kvc_abi_version() == kvc.ABI_VERSION == 7
 
 
 def cfg_of(wl: syn.Workload):
@@ -472,6 +472,32 @@ def test_multi_frame_append_arguments_and_all_or_none():
     assert c.get_cache_stats() == before
     c.append_frames(0, num_frames=3)                  # exactly fills the pool
     assert c.get_cache_stats()["free_pages"] == 0
+
+
+def test_rope_entry_points_on_metadata_only_context():
+    """kvc_append_frames_rope follows kvc_append_frames' allocation and call
+    order (a metadata-only context takes no tables); kvc_run_rope refuses to
+    run without device buffers; the rope launch has its own profile slot."""
+    lib = kvc.load_library()
+    c = tiny_cache(num_blocks=2)
+    fake = ctypes.c_void_p(16)
+    rc = lib.kvc_append_frames_rope(c._ctx, 0, 0, None, None, 1, fake, fake, None)
+    assert rc == kvc.KVC_ERR_ARG                       # tables on a metadata-only context
+    assert lib.kvc_append_frames_rope(c._ctx, 0, 0, None, None, 1, None, None, None) == kvc.KVC_OK
+    assert lib.kvc_append_frames_rope(c._ctx, 0, 0, None, None, 1, None, None, None) == kvc.KVC_ERR_STATE
+    assert lib.kvc_append_frames_rope(c._ctx, 0, 1, None, None, 2, None, None, None) == kvc.KVC_ERR_ARG
+    assert lib.kvc_append_frames_rope(c._ctx, 0, 1, None, None, 1, None, None, None) == kvc.KVC_OK
+    with pytest.raises(kvc.KvcError) as e:
+        c.append_frames(0, num_frames=1, rope=(None, None))
+    assert e.value.status == kvc.KVC_ERR_ARG
+    assert lib.kvc_evict(c._ctx, 0) == kvc.KVC_OK
+    assert lib.kvc_plan(c._ctx, None) == kvc.KVC_OK
+    assert lib.kvc_run_rope(c._ctx, 0, fake, fake, fake, ctypes.c_void_p(4096), None) == kvc.KVC_ERR_STATE
+    assert c.get_cache_stats()["frame_count"] == 1
+    ms, n = ctypes.c_double(), ctypes.c_int64()
+    assert lib.kvc_profile_read(c._ctx, kvc.KVC_KERNEL_ROPE, ctypes.byref(ms), ctypes.byref(n), 0) == kvc.KVC_OK
+    assert n.value == 0
+    assert lib.kvc_profile_read(c._ctx, kvc.KVC_KERNEL_ROPE + 1, None, None, 0) == kvc.KVC_ERR_ARG
 
 
 def test_deferred_eviction_and_rollback_match_oracle():
