@@ -49,11 +49,19 @@ def _run(cmd, verbose):
     return r.stdout
 
 
+# Kernels that read unit entries with scalar loads issued in inline asm
+# (unit_load): the compiler takes those registers as written at the asm, so
+# an SGPR spill or copy of them before the matching wait would capture values
+# still in flight.  No such kernel may spill SGPRs.
+ASM_SCALAR_LOAD_KERNELS = ("attn_kernel",)
+
+
 def check_no_scratch(remarks: str) -> None:
-    """The attention kernel counts its own direct-to-LDS loads with vmcnt
-    waits; a register spill inside its loop would add scratch loads to that
+    """The attention kernels count their own direct-to-LDS loads with vmcnt
+    waits; a register spill inside their loops would add scratch loads to that
     count (publishing a stage too early) or force a full drain.  Refuse any
-    build in which a kernel uses scratch memory."""
+    build in which a kernel uses scratch memory, or in which a kernel of
+    ASM_SCALAR_LOAD_KERNELS spills SGPRs."""
     name = None
     bad = []
     for line in remarks.splitlines():
@@ -62,9 +70,13 @@ def check_no_scratch(remarks: str) -> None:
         elif "ScratchSize [bytes/lane]:" in line:
             size = int(line.split("ScratchSize [bytes/lane]:")[1].split()[0])
             if size:
-                bad.append(f"{name}: {size} bytes/lane")
+                bad.append(f"{name}: {size} bytes/lane of scratch")
+        elif "SGPRs Spill:" in line:
+            n = int(line.split("SGPRs Spill:")[1].split()[0])
+            if n and name and any(k in name for k in ASM_SCALAR_LOAD_KERNELS):
+                bad.append(f"{name}: {n} SGPRs spilled in a kernel with asm scalar loads")
     if bad:
-        raise RuntimeError("kernels spill to scratch memory:\n  " + "\n  ".join(bad))
+        raise RuntimeError("kernels spill registers:\n  " + "\n  ".join(bad))
 
 
 def build(verbose: bool = False) -> str:

@@ -552,6 +552,9 @@ static kvc_status launch_run(kvc_ctx* c, int32_t block, const void* q, void* o, 
   a.dtype = cf.dtype;
   a.items_per_xcd = (c->plan.num_items + 7) / 8;
   a.shared_tile = c->plan.shared_tile ? 1 : 0;
+  a.num_streams = (int32_t)c->plan.planned.size();
+  if (a.num_streams <= KVC_ARG_STREAMS)
+    std::memcpy(a.recs, c->plan.image.data() + KVC_PLAN_HEADER_INTS, (size_t)a.num_streams * sizeof(kvc_dev_stream));
   const int32_t grid = 8 * a.items_per_xcd;
   int e = timed(c, KVC_KERNEL_ATTENTION, hs, [&] {
     return cf.tiles32() ? kvc::launch_attention32(a, grid, hs) : kvc::launch_attention(a, grid, hs);

@@ -319,11 +319,7 @@ __global__ __launch_bounds__(64 * KVC_ATTN32_WAVES, 1) void attn32_kernel(AttnPa
   const int item = (bid & 7) * p.items_per_xcd + (bid >> 3);
   if (item >= p.num_items) return;
 
-  const int nstreams = p.plan[KVC_HDR_NUM_STREAMS];
-  const kvc_dev_stream* recs = reinterpret_cast<const kvc_dev_stream*>(p.plan + KVC_PLAN_HEADER_INTS);
-  int si = 0;
-  while (si + 1 < nstreams && item >= recs[si + 1].item0) ++si;
-  const kvc_dev_stream st = recs[si];
+  const kvc_dev_stream st = stream_of_item(p, item);
 
   int local = item - st.item0;
   const int grp = local % st.n_group;
@@ -616,8 +612,9 @@ __global__ __launch_bounds__(64 * KVC_ATTN32_WAVES, 1) void attn32_kernel(AttnPa
   // s + NST - 1 (two loops, with and without those loads) ----
   int4 e_next = elds[min(NST - 1, KVC_MAX_SPLIT_STAGES - 1)];
   int4 e_cur = elds[0];
-  auto stage_body = [&](int s, auto issue_tag) {
+  auto stage_body = [&](int s, auto issue_tag, auto lead_tag) {
     constexpr bool do_issue = decltype(issue_tag)::value;
+    constexpr bool is_lead = decltype(lead_tag)::value;
     wait_ahead<LPW, NST - 2>(min(nstage - 1 - s, NST - 2));
     ring_barrier();
     if constexpr (do_issue)
@@ -625,7 +622,7 @@ __global__ __launch_bounds__(64 * KVC_ATTN32_WAVES, 1) void attn32_kernel(AttnPa
     const int valid = __builtin_amdgcn_readfirstlane(e_cur.y);
     e_cur = elds[min(s + 1, KVC_MAX_SPLIT_STAGES - 1)];
     e_next = elds[min(s + NST, KVC_MAX_SPLIT_STAGES - 1)];
-    if (lead) {
+    if constexpr (is_lead) {
       read_k(s);
       read_v(s);
       if constexpr (TAIL) read_tail(s);
@@ -669,10 +666,17 @@ __global__ __launch_bounds__(64 * KVC_ATTN32_WAVES, 1) void attn32_kernel(AttnPa
       if (__builtin_expect(valid < KVC_KV_TILE, 0)) mask32(sc, valid, h);
     }
   };
-  {
+  // one loop per role: each keeps its loop-carried accumulators in its own
+  // registers (a shared loop with a role branch inside made the compiler
+  // copy the output accumulators between the branches every stage)
+  if (lead) {
     int s = 0;
-    for (; s + NST - 1 < nstage; ++s) stage_body(s, Flag<true>{});
-    for (; s < nstage; ++s) stage_body(s, Flag<false>{});
+    for (; s + NST - 1 < nstage; ++s) stage_body(s, Flag<true>{}, Flag<true>{});
+    for (; s < nstage; ++s) stage_body(s, Flag<false>{}, Flag<true>{});
+  } else {
+    int s = 0;
+    for (; s + NST - 1 < nstage; ++s) stage_body(s, Flag<true>{}, Flag<false>{});
+    for (; s < nstage; ++s) stage_body(s, Flag<false>{}, Flag<false>{});
   }
   // ---- drain: the lag waves' last stage ----
   if (!lead) {

@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kvc_kernels.h"
 #include "kvc_plan_layout.h"
 
 namespace kvc {
@@ -105,8 +106,11 @@ __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "
 // load in flight only makes the compiler's own LDS waits stricter.
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ i32x4 unit_load(const int32_t* entry) {
+  const uint64_t b = (uint64_t)entry;
+  const uint64_t sb = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(b >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
   i32x4 e;
-  asm volatile("s_load_dwordx4 %0, %1, 0x0" : "=s"(e) : "s"(entry) : "memory");
+  asm volatile("s_load_dwordx4 %0, %1, 0x0" : "=s"(e) : "s"((const int32_t*)sb) : "memory");
   return e;
 }
 __device__ __forceinline__ void unit_wait(i32x4& e) { asm volatile("s_waitcnt lgkmcnt(0)" : "+s"(e)::"memory"); }
@@ -173,6 +177,28 @@ __device__ __forceinline__ float lane_swap_sum(float x) {
   b = a;
   swap16(a, b);
   return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+}
+
+// The stream record of an attention work item: the stream is the last one
+// whose first item is at most `item` (item0 ascends over the streams).  Taken
+// from the launch arguments when the plan has at most KVC_ARG_STREAMS
+// streams, so that the work-group's first memory round trip is the one for
+// its unit entries; else read from the plan.
+__device__ __forceinline__ kvc_dev_stream stream_of_item(const AttnParams& p, int item) {
+  const int nstreams = p.num_streams;
+  kvc_dev_stream st;
+  if (nstreams <= KVC_ARG_STREAMS) {
+    st = p.recs[0];
+#pragma unroll
+    for (int i = 1; i < KVC_ARG_STREAMS; ++i)
+      if (i < nstreams && item >= p.recs[i].item0) st = p.recs[i];
+  } else {
+    const kvc_dev_stream* recs = reinterpret_cast<const kvc_dev_stream*>(p.plan + KVC_PLAN_HEADER_INTS);
+    int si = 0;
+    while (si + 1 < nstreams && item >= recs[si + 1].item0) ++si;
+    st = recs[si];
+  }
+  return st;
 }
 
 // Lazy renormalisation.  Each query tile keeps a reference value ref in log2

@@ -52,6 +52,11 @@ struct AttnParams {
   int32_t num_items, items_per_xcd;
   int32_t shared_tile;      // launch variant, as KVC_HDR_SHARED_TILE of the plan
   int32_t dtype;            // element type: 0 bfloat16, 1 float16
+  // The plan's stream count and, when it is at most KVC_ARG_STREAMS, copies
+  // of its stream records (the 32x32 kernel then starts its unit-entry loads
+  // without first loading the plan's header and records)
+  int32_t num_streams;
+  kvc_dev_stream recs[KVC_ARG_STREAMS];
 };
 
 struct MergeParams {

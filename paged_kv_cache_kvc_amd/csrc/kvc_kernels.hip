@@ -384,11 +384,7 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
   const int item = (bid & 7) * p.items_per_xcd + (bid >> 3);
   if (item >= p.num_items) return;
 
-  const int nstreams = p.plan[KVC_HDR_NUM_STREAMS];
-  const kvc_dev_stream* recs = reinterpret_cast<const kvc_dev_stream*>(p.plan + KVC_PLAN_HEADER_INTS);
-  int si = 0;
-  while (si + 1 < nstreams && item >= recs[si + 1].item0) ++si;
-  const kvc_dev_stream st = recs[si];
+  const kvc_dev_stream st = stream_of_item(p, item);
 
   int local = item - st.item0;
   const int grp = local % st.n_group;

@@ -94,6 +94,9 @@ typedef struct kvc_dev_stream {
   int32_t reserved0, reserved1;
 } kvc_dev_stream;
 
+// Stream records the attention launch also passes by value.
+#define KVC_ARG_STREAMS 4
+
 // Query tiles (of KVC_Q_TILE rows) one wave owns.  A query group spans at
 // most KVC_ATTN_WAVES * this many tiles, plus one tile shared by all waves
 // when the launch uses shared tiles.

@@ -569,3 +569,9 @@ def test_build_refuses_kernels_that_spill():
     b.check_no_scratch(ok)
     with pytest.raises(RuntimeError, match="attn2: 216"):
         b.check_no_scratch(ok + ok.replace("attn", "attn2").replace("]: 0", "]: 216"))
+    # SGPR spills: refused in the kernel whose unit entries come from asm
+    # scalar loads, accepted elsewhere
+    spill = "k.hip:1:1: remark: Function Name: {} [-R]\nk.hip:1:1: remark:     SGPRs Spill: 15 [-R]\n"
+    b.check_no_scratch(spill.format("_ZN3kvc13attn32_kernelILi64E"))
+    with pytest.raises(RuntimeError, match="SGPRs spilled"):
+        b.check_no_scratch(spill.format("_ZN3kvc11attn_kernelILi128E"))
