@@ -251,6 +251,26 @@ def test_scale_phase_multi_frame_prefill():
     assert np.array_equal(h.pool_bits(0), h.ora.pools[0].data)
 
 
+def test_scale_phase_full_heads():
+    """The 8-frame scale step at the full H=16, D=64 shape: 2096 queries over
+    2096 tokens in 144 work-groups (9 query groups of 8 tiles per head, one
+    split: a second split would need a second round of work-groups and a
+    merge, which measured slower); output against the oracle, pool
+    bit-exact."""
+    _need_gpu()
+    import dataclasses
+    wl = dataclasses.replace(syn.WORKLOADS["base"], frames=(12,))
+    S = wl.scale_frames
+    h = Harness(wl, max_frames_per_step=S)
+    res = h.step(check=True, nframes={0: S})
+    compare_plan(res)
+    assert list(res["gpu_plan"]["n_splits"]) == [1]
+    assert h.gpu.get_plan_shape()["work_items"] == 144
+    st = check_close(res["out_bits"][0], res["ref"][0])
+    log(f"scale step H=16: {st}")
+    assert np.array_equal(h.pool_bits(0), h.ora.pools[0].data)
+
+
 def test_deferred_eviction_with_rollbacks():
     """Frame rollback with deferred eviction ([p2] §Scale Frames vs Sliding
     Window): every fourth frame is undone after its step; attention stays
