@@ -51,13 +51,19 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
+# Bit-pattern array type of each element type.
+BITS_DTYPE = {"bf16": np.uint16, "f16": np.uint16, "f32": np.uint32}
+
+
 def bits_to_f32(b: np.ndarray, dtype: str = "bf16") -> np.ndarray:
-    """Exact widening of 16-bit patterns of the given element type ("bf16" or
-    "f16") to float32."""
+    """Exact widening of the bit patterns of the given element type ("bf16",
+    "f16" or "f32") to float32."""
     if dtype == "bf16":
         return bf16_bits_to_f32(b)
     if dtype == "f16":
         return np.ascontiguousarray(b, dtype=np.uint16).view(np.float16).astype(np.float32)
+    if dtype == "f32":
+        return np.ascontiguousarray(b, dtype=np.uint32).view(np.float32)
     raise ValueError(f"unknown dtype {dtype}")
 
 
@@ -66,6 +72,8 @@ def f32_to_bits(x: np.ndarray, dtype: str = "bf16") -> np.ndarray:
         return f32_to_bf16_bits(x)
     if dtype == "f16":
         return f32_to_f16_bits(x)
+    if dtype == "f32":
+        return np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).copy()
     raise ValueError(f"unknown dtype {dtype}")
 
 
@@ -93,14 +101,14 @@ def patch_rows(T: int, n_special: int, special_row_offset: int) -> np.ndarray:
 def frame_tensor(seed: int, stream: int, frame: int, block: int, which: str,
                  T: int, H: int, D: int, n_special: int, special_row_offset: int,
                  scale: float = 1.0, patch_real: bool = True, dtype: str = "bf16") -> np.ndarray:
-    """One frame's Q, K or V as 16-bit patterns of `dtype`, shape [T, H, D] (NHD).
+    """One frame's Q, K or V as bit patterns of `dtype`, shape [T, H, D] (NHD).
 
     Patch rows and special rows are drawn from separate keys, so the special
     rows of any frame can be regenerated cheaply.  With patch_real=False the
     patch rows are zero (used for frames whose patch page is evicted before
     any checked step, so a long stream need not draw them)."""
     t = TENSOR_IDS[which]
-    out = np.zeros((T, H, D), dtype=np.uint16)
+    out = np.zeros((T, H, D), dtype=BITS_DTYPE[dtype])
     pr = patch_rows(T, n_special, special_row_offset)
     sr = special_rows(T, n_special, special_row_offset)
     if patch_real and len(pr):
@@ -177,7 +185,7 @@ class Workload:
     max_special_pages: int
     shuffle_free_lists: bool = False
     special_row_offset: Optional[int] = None   # None: specials after the patches
-    dtype: str = "bf16"                         # element type: "bf16" or "f16"
+    dtype: str = "bf16"                         # element type: "bf16", "f16" or "f32"
 
     @property
     def tokens_per_frame(self) -> int:

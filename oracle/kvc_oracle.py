@@ -61,7 +61,7 @@ from typing import Callable, Dict, List, Optional, Sequence, Tuple
 
 import numpy as np
 
-from kvc_synth import bits_to_f32, patch_rows, special_rows
+from kvc_synth import BITS_DTYPE, bits_to_f32, patch_rows, special_rows
 
 
 @dataclasses.dataclass
@@ -77,7 +77,7 @@ class OracleConfig:
     max_special_pages: int
     num_streams: int = 1
     special_row_offset: Optional[int] = None   # None: specials after patches
-    dtype: str = "bf16"                        # element type of K, V, Q: "bf16" or "f16"
+    dtype: str = "bf16"                        # element type of K, V, Q: "bf16", "f16" or "f32"
 
     @property
     def patch_tokens(self) -> int:
@@ -305,14 +305,15 @@ class AllocatorReplay:
 
 
 class SimulatedPool:
-    """One block's page pool [max_num_pages, 2, page_size, H, D] of bf16 bit
-    patterns ([p1] §Paged KV Cache Memory Layout; [p5] §Core Implementation
+    """One block's page pool [max_num_pages, 2, page_size, H, D] of element
+    bit patterns (uint16 for bf16 and f16, uint32 for f32) ([p1] §Paged KV
+    Cache Memory Layout; [p5] §Core Implementation
     Mechanics: dimension 1 is 0 = K, 1 = V; NHD inside a page), zero at start."""
 
     def __init__(self, cfg: OracleConfig):
         self.cfg = cfg
         self.data = np.zeros((cfg.max_num_pages, 2, cfg.page_size, cfg.num_heads, cfg.head_dim),
-                             dtype=np.uint16)
+                             dtype=BITS_DTYPE[cfg.dtype])
 
     def write_frame(self, slots: FrameSlots, k_bits: np.ndarray, v_bits: np.ndarray):
         """[p5] §Frame Appending Without Dispatch Overhead: patch rows go to the
@@ -383,14 +384,15 @@ def gather_paged(cfg: OracleConfig, pool: SimulatedPool, plan: Dict[str, np.ndar
 
 def attention_fp64(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray, dtype: str = "bf16") -> np.ndarray:
     """Unmasked softmax attention of every query row over every given key,
-    per head, in float64 from the exact 16-bit values (bf16, or f16 for the
-    16-bit float the paged kernels also take natively, [p3] §Precision and
-    Hardware Utilization):
+    per head, in float64 from the exact input values (bf16; f16, the 16-bit
+    float the paged kernels also take natively, [p3] §Precision and Hardware
+    Utilization; or f32, the full-precision pool of [p3] FAQ on fp32 and [p4]
+    §Memory Management and Debugging):
     O = softmax(Q K^T / sqrt(D)) V  ([p1] §Efficient Attention Masking and
     Padding: no boolean mask; [p5] §Kernel Dispatch and Sequence Lengths:
     exact weights over the valid tokens).
 
-    q_bits [T, H, D], k_bits and v_bits [L, H, D] (uint16 patterns of dtype).
+    q_bits [T, H, D], k_bits and v_bits [L, H, D] (bit patterns of dtype).
     Returns [T, H, D] float64."""
     q = bits_to_f32(q_bits, dtype).astype(np.float64)
     k = bits_to_f32(k_bits, dtype).astype(np.float64)
@@ -426,13 +428,15 @@ def lse_base2_fp64(q_bits: np.ndarray, k_bits: np.ndarray, dtype: str = "bf16") 
 
 
 def round_to_elem(x: np.ndarray, dtype: str = "bf16") -> np.ndarray:
-    """float64 values rounded to the nearest 16-bit value of the element type
-    (ties to even), as uint16 bit patterns.  bf16: 8 significant bits and the
-    float32 exponent range; the values here are finite and, when non-zero,
-    normal."""
+    """float64 values rounded to the nearest value of the element type (ties
+    to even), as bit patterns (uint16; uint32 for f32).  bf16: 8 significant
+    bits and the float32 exponent range; the values here are finite and, when
+    non-zero, normal."""
     x = np.asarray(x, dtype=np.float64)
     if dtype == "f16":
         return x.astype(np.float16).view(np.uint16)
+    if dtype == "f32":
+        return x.astype(np.float32).view(np.uint32)
     m, e = np.frexp(x)                                  # x = m 2^e, 0.5 <= |m| < 1
     r = np.rint(m * 256.0) * np.exp2(e.astype(np.float64) - 8.0)   # 8 significant bits, ties to even
     return (r.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
@@ -464,7 +468,7 @@ def rope_rotate_fp64(x_bits: np.ndarray, cos: np.ndarray, sin: np.ndarray, dtype
 
 def rope_fp64(x_bits: np.ndarray, cos: np.ndarray, sin: np.ndarray, dtype: str = "bf16") -> np.ndarray:
     """The rotated rows as they are stored: rope_rotate_fp64 rounded once to
-    the element type.  Returns uint16 bits [T, H, D]."""
+    the element type.  Returns bit patterns [T, H, D]."""
     return round_to_elem(rope_rotate_fp64(x_bits, cos, sin, dtype), dtype)
 
 

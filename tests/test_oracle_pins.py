@@ -206,6 +206,43 @@ def pin_f16_inputs(oracle=ko, seed=11):
     np.testing.assert_allclose(ours, ref, rtol=1e-12, atol=1e-12)
 
 
+def pin_f32_inputs(oracle=ko, seed=12):
+    """float32 K/V/Q (a full-precision pool): the oracle on f32 bit patterns
+    equals PyTorch SDPA in float64 over the same float32 values, and differs
+    from reading the high halves of those bits as bf16."""
+    rng = np.random.default_rng(seed)
+    T, L, H, D = 7, 33, 2, 32
+    q, k, v = (syn.f32_to_bits(rng.standard_normal(sh).astype(np.float32) * np.float32(sc), "f32")
+               for sh, sc in (((T, H, D), 1.5), ((L, H, D), 1.0), ((L, H, D), 1.0)))
+    assert q.dtype == np.uint32
+    ours = oracle.attention_fp64(q, k, v, "f32")
+    to = lambda b: torch.from_numpy(b.view(np.float32)).double().permute(1, 0, 2)[None]
+    ref = torch.nn.functional.scaled_dot_product_attention(to(q), to(k), to(v))[0].permute(1, 0, 2).numpy()
+    np.testing.assert_allclose(ours, ref, rtol=1e-12, atol=1e-12)
+
+
+def pin_round_to_f32(oracle=ko, seed=14):
+    """round_to_elem for f32 is nearest-even: every result is one of the two
+    float32 neighbours of the value (found with nextafter), the nearer one;
+    exact midpoints go to the even pattern, and values a hair past a
+    midpoint to the far side."""
+    rng = np.random.default_rng(seed)
+    a = (rng.standard_normal(3000) * np.exp2(rng.uniform(-40, 40, 3000))).astype(np.float32)
+    b = np.nextafter(a, np.float32(np.inf))
+    mid = 0.5 * (a.astype(np.float64) + b.astype(np.float64))       # exact in float64
+    up = mid + np.abs(mid) * 2.0 ** -45
+    x = mid + (b.astype(np.float64) - a.astype(np.float64)) * rng.uniform(-0.49, 0.49, 3000)
+    got = oracle.round_to_elem(x, "f32").view(np.float32)
+    lo, hi = np.minimum(a, b), np.maximum(a, b)
+    d_lo, d_hi = np.abs(x - lo), np.abs(x - hi)
+    want = np.where(d_lo < d_hi, lo, hi)
+    assert np.array_equal(got, want.astype(np.float32))
+    tie = oracle.round_to_elem(mid, "f32")
+    even = np.where(a.view(np.uint32) % 2 == 0, a, b).view(np.uint32)
+    assert np.array_equal(tie, even)
+    assert np.array_equal(oracle.round_to_elem(up, "f32").view(np.float32), np.where(up > mid, hi, lo))
+
+
 def pin_bruteforce(oracle=ko, seed=1):
     """Scalar loops straight from the definition of softmax attention."""
     rng = np.random.default_rng(seed)
@@ -333,6 +370,14 @@ def test_rollback_leaves_the_kept_frames_history():
 
 def test_f16_inputs_match_torch_sdpa():
     pin_f16_inputs()
+
+
+def test_f32_inputs_match_torch_sdpa():
+    pin_f32_inputs()
+
+
+def test_round_to_f32_is_nearest_even():
+    pin_round_to_f32()
 
 
 def test_attention_bruteforce():
@@ -547,7 +592,7 @@ def _nearest_elem(x, dtype):
 def _rope_inputs(seed, T=6, H=3, D=16, dtype="bf16"):
     rng = np.random.default_rng(seed)
     x = rng.standard_normal((T, H, D)) * 2.0
-    bits = _nearest_elem(x, dtype)
+    bits = syn.f32_to_bits(x.astype(np.float32), "f32") if dtype == "f32" else _nearest_elem(x, dtype)
     theta = rng.uniform(-4 * math.pi, 4 * math.pi, (T, D // 2))
     return bits, theta
 
@@ -572,9 +617,10 @@ def pin_round_to_elem(oracle=ko, seed=13):
 
 def pin_rope_known_rotations(oracle=ko, seed=17):
     """R_0 = I leaves every bit unchanged; a quarter turn maps (a, b) to
-    (-b, a) and a half turn to (-a, -b), exactly, for both element types;
-    rope_fp64 is the rotation rounded once to the nearest element value."""
-    for dtype in ("bf16", "f16"):
+    (-b, a) and a half turn to (-a, -b), exactly, for every element type;
+    rope_fp64 is the rotation rounded once to the nearest element value (the
+    16-bit types by brute force here, f32 through pin_round_to_f32)."""
+    for dtype in ("bf16", "f16", "f32"):
         bits, theta = _rope_inputs(seed, dtype=dtype)
         x = syn.bits_to_f32(bits, dtype).astype(np.float64)
         one, zero = np.ones_like(theta), np.zeros_like(theta)
@@ -584,8 +630,9 @@ def pin_rope_known_rotations(oracle=ko, seed=17):
         half = oracle.rope_rotate_fp64(bits, -one, zero, dtype)
         assert np.array_equal(half, -x)
         c, s = np.cos(theta), np.sin(theta)
-        assert np.array_equal(oracle.rope_fp64(bits, c, s, dtype),
-                              _nearest_elem(oracle.rope_rotate_fp64(bits, c, s, dtype), dtype))
+        if dtype != "f32":
+            assert np.array_equal(oracle.rope_fp64(bits, c, s, dtype),
+                                  _nearest_elem(oracle.rope_rotate_fp64(bits, c, s, dtype), dtype))
 
 
 def pin_rope_complex(oracle=ko, seed=19):
@@ -793,6 +840,22 @@ def _rope_inverse(x_bits, cos, sin, dtype="bf16"):
     return out
 
 
+def _f32_read_as_bf16(q_bits, k_bits, v_bits, dtype="bf16"):
+    if dtype != "f32":
+        return ko.attention_fp64(q_bits, k_bits, v_bits, dtype)
+    hi = lambda b: (np.asarray(b, np.uint32) >> 16).astype(np.uint16)
+    return ko.attention_fp64(hi(q_bits), hi(k_bits), hi(v_bits), "bf16")
+
+
+def _round_f32_truncates(x, dtype="bf16"):
+    if dtype != "f32":
+        return ko.round_to_elem(x, dtype)
+    x = np.asarray(x, np.float64)
+    r = x.astype(np.float32)
+    over = np.abs(r.astype(np.float64)) > np.abs(x)
+    return np.where(over, np.nextafter(r, np.float32(0)), r).astype(np.float32).view(np.uint32)
+
+
 def _round_truncates(x, dtype="bf16"):
     if dtype == "f16":
         return ko.round_to_elem(x, dtype)
@@ -826,7 +889,7 @@ def _pins_fail(mutant, pins):
 
 ALL_PINS = [pin_worked_example, pin_special_closed_forms, pin_visible_set, pin_sdpa, pin_bruteforce,
             pin_softmax_invariants, pin_paged_equals_dense, pin_scale_phase, pin_rollback, pin_f16_inputs,
-            pin_lse_base2, pin_round_to_elem, pin_rope_known_rotations, pin_rope_complex,
+            pin_lse_base2, pin_f32_inputs, pin_round_to_f32, pin_round_to_elem, pin_rope_known_rotations, pin_rope_complex,
             pin_rope_norm_and_relative_position]
 
 
@@ -852,11 +915,13 @@ ALL_PINS = [pin_worked_example, pin_special_closed_forms, pin_visible_set, pin_s
     _Mutant(round_to_elem=_round_truncates),
     _Mutant(round_to_elem=_round_via_f32),
     _Mutant(round_to_elem=_round_ties_away),
+    _Mutant(attention_fp64=_f32_read_as_bf16),
+    _Mutant(round_to_elem=_round_f32_truncates),
 ], ids=["no_scale", "values_are_keys", "wrong_softmax_axis", "window_off_by_one", "specials_first",
         "last_page_zero", "scale_evicted", "special_count_drift", "one_frame_per_step", "rollback_no_refill",
         "f16_read_as_bf16", "lse_natural_log", "lse_max_only", "lse_unscaled", "rope_sign_slip",
         "rope_dropped_term", "rope_rotate_half", "rope_inverse", "round_truncates", "round_via_f32",
-        "round_ties_away"])
+        "round_ties_away", "f32_read_as_bf16", "round_f32_truncates"])
 def test_planted_mistake_is_caught(mutant):
     # OracleStream inside the mutant must use the mutant's allocator
     class _Stream(ko.OracleStream):
