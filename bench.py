@@ -41,7 +41,17 @@ if ROOT not in sys.path:
 
 METRIC = "frame-steps/sec (all blocks) + attn TFLOP/s & HBM GB/s vs MI355X peak"
 PEAK_HBM_GBS = 8000.0
-PEAK_BF16_TFLOPS = 2500.0
+PEAK_BF16_TFLOPS = 2500.0   # dense bf16 / fp16 MFMA
+PEAK_F32_TFLOPS = 157.3     # dense fp32 MFMA
+
+
+def elem_bytes(dtype):
+    return 4 if dtype == "f32" else 2
+
+
+def mfma_peak(dtype):
+    """Dense MFMA peak (TFLOP/s) of the type the attention computes in."""
+    return PEAK_F32_TFLOPS if dtype == "f32" else PEAK_BF16_TFLOPS
 BANK = 8
 
 
@@ -61,17 +71,20 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def attention_kernel_name(head_dim):
-    """The attention kernel that serves a head size: the 32x32 kernel up to
-    64, the 16x16 one at 128."""
+def attention_kernel_name(head_dim, dtype="bf16"):
+    """The attention kernel that serves a head size and element type: for the
+    16-bit types the 32x32 kernel up to 64 and the 16x16 one at 128; the
+    float32 kernel for float32 pools."""
+    if dtype == "f32":
+        return "attn_f32_kernel"
     return "attn32_kernel" if head_dim <= 64 else "attn_kernel"
 
 
-def read_traffic(workload, head_dim):
+def read_traffic(workload, head_dim, dtype="bf16"):
     """HBM bytes per attention launch from the committed rocprofv3 counter
     summary (FETCH_SIZE and WRITE_SIZE, calibrated against a plain copy), or
     None when it is missing or was taken on other kernel source."""
-    p = os.path.join(ROOT, "profiles", f"{attention_kernel_name(head_dim)}_{workload}_hbm_traffic.md")
+    p = os.path.join(ROOT, "profiles", f"{attention_kernel_name(head_dim, dtype)}_{workload}_hbm_traffic.md")
     if not os.path.exists(p):
         return None
     fields = {}
@@ -233,8 +246,10 @@ def scale_phase(args, torch, syn, kvc, dev):
     value = K / wall
     st = cache.get_cache_stats(0)
     L = (st["scale_pages"] + st["live_pages"]) * wl.patch_tokens + st["special_tokens"]
+    eb = elem_bytes(args.dtype)
+    peak_mfma = mfma_peak(args.dtype)
     flop = 4.0 * S * T * L * H * D
-    byts = 4.0 * L * H * D + 4.0 * S * T * H * D
+    byts = 2.0 * eb * L * H * D + 2.0 * eb * S * T * H * D
     # the kernels' durations from per-launch HIP events, attention launches repeated on the last plan
     cache.set_option(kvc.KVC_OPT_PROFILE, 1)
     for k in (kvc.KVC_KERNEL_ATTENTION, kvc.KVC_KERNEL_MERGE):
@@ -250,9 +265,9 @@ def scale_phase(args, torch, syn, kvc, dev):
     a_s = (a_ms + m_ms) / 1e3 / max(a_n, 1)
     tfl = flop / a_s / 1e12
     gbs = byts / a_s / 1e9
-    bound = "hbm" if flop / byts < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9) else "mfma"
-    roof = ({"bound": "mfma", "achieved": tfl, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-             "frac": tfl / PEAK_BF16_TFLOPS, "traffic": None} if bound == "mfma" else
+    bound = "hbm" if flop / byts < peak_mfma * 1e12 / (PEAK_HBM_GBS * 1e9) else "mfma"
+    roof = ({"bound": "mfma", "achieved": tfl, "peak": peak_mfma, "unit": "TFLOP/s",
+             "frac": tfl / peak_mfma, "traffic": None} if bound == "mfma" else
             {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
              "traffic": None})
     peaks = achievable_peaks(torch, dev)
@@ -265,7 +280,7 @@ def scale_phase(args, torch, syn, kvc, dev):
                                 f"{wl.num_special_tokens} special tokens in one step, page_size {wl.page_size}"),
                    "num_blocks": nb, "query_rows": S * T, "visible_tokens": L, "num_heads": H, "head_dim": D},
         "roofline": roof,
-        "attention": {"kernel": attention_kernel_name(wl.head_dim), "launches": a_n, "avg_us": 1e3 * a_ms / max(a_n, 1),
+        "attention": {"kernel": attention_kernel_name(wl.head_dim, args.dtype), "launches": a_n, "avg_us": 1e3 * a_ms / max(a_n, 1),
                       "attention_plus_merge_us": 1e6 * a_s, "tflops": tfl, "gbs": gbs,
                       "alg_flop_per_launch": flop, "alg_bytes_per_launch": byts,
                       "merge_avg_us": 1e3 * m_ms / max(m_n, 1), "merge_launches": m_n,
@@ -282,7 +297,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="base", choices=["base", "r518", "long", "frag", "scale"],
                     help="scale: the base shape's scale phase, its 8 first frames appended and attended in one step")
-    ap.add_argument("--dtype", default="bf16", choices=["bf16", "f16"],
+    ap.add_argument("--dtype", default="bf16", choices=["bf16", "f16", "f32"],
                     help="element type of the pools and of q, k, v, o")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -323,6 +338,8 @@ def main():
     wl = syn.WORKLOADS[args.workload]
     F = max(wl.frames)
     K, W = args.steps, args.warmup
+    eb = elem_bytes(args.dtype)
+    peak_mfma = mfma_peak(args.dtype)
     if K < 1 or W < 0 or K + W > F:
         print(f"need 1 <= steps and steps + warmup <= {F}", file=sys.stderr)
         sys.exit(2)
@@ -410,7 +427,7 @@ def main():
             st = cache.get_cache_stats(s)
             L = (st["scale_pages"] + st["live_pages"]) * wl.patch_tokens + st["special_tokens"]
             fl += 4.0 * T * L * H * D
-            by += 4.0 * L * H * D + 4.0 * T * H * D   # K and V (bf16) read once, Q read, O written
+            by += 2.0 * eb * L * H * D + 2.0 * eb * T * H * D   # K and V read once, Q read, O written
         return fl, by
 
     # Timed region 1: K whole steps with no per-launch events (the events
@@ -474,22 +491,22 @@ def main():
         step_s = elapsed / K
         gbs_step = pb / K / step_s / 1e9
         tfl_step = pf / K / step_s / 1e12
-        bound = "hbm" if pf / pb < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9) else "mfma"
-        traffic = read_traffic(wl.name, D)
+        bound = "hbm" if pf / pb < peak_mfma * 1e12 / (PEAK_HBM_GBS * 1e9) else "mfma"
+        traffic = read_traffic(wl.name, D, args.dtype)
         if bound == "hbm":
             roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
                     "frac_attention_kernel_only": gbs_a / PEAK_HBM_GBS, "frac_whole_step": gbs_step / PEAK_HBM_GBS}
         else:
-            roof = {"bound": "mfma", "achieved": tfl, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                    "frac": tfl / PEAK_BF16_TFLOPS, "frac_attention_kernel_only": tfl_a / PEAK_BF16_TFLOPS,
-                    "frac_whole_step": tfl_step / PEAK_BF16_TFLOPS}
+            roof = {"bound": "mfma", "achieved": tfl, "peak": peak_mfma, "unit": "TFLOP/s",
+                    "frac": tfl / peak_mfma, "frac_attention_kernel_only": tfl_a / peak_mfma,
+                    "frac_whole_step": tfl_step / peak_mfma}
         roof["traffic"] = traffic
         roof["time"] = "attention + merge kernels, per block (HIP events)"
         out["roofline"] = roof
         peaks = achievable_peaks(torch, dev)
         out["attention"] = {
-            "kernel": attention_kernel_name(D), "launches": a_n, "avg_us": 1e3 * a_ms / max(a_n, 1),
-            "tflops": tfl_a, "gbs": gbs_a, "frac_hbm": gbs_a / PEAK_HBM_GBS, "frac_mfma": tfl_a / PEAK_BF16_TFLOPS,
+            "kernel": attention_kernel_name(D, args.dtype), "launches": a_n, "avg_us": 1e3 * a_ms / max(a_n, 1),
+            "tflops": tfl_a, "gbs": gbs_a, "frac_hbm": gbs_a / PEAK_HBM_GBS, "frac_mfma": tfl_a / peak_mfma,
             "alg_bytes_per_launch": pb / max(a_n, 1), "alg_flop_per_launch": pf / max(a_n, 1),
             "merge_avg_us": 1e3 * m_ms / max(m_n, 1), "merge_launches": m_n,
             "attention_plus_merge_us": 1e6 * am_s / max(a_n, 1),

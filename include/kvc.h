@@ -105,12 +105,18 @@ typedef struct kvc_config {
   int32_t dtype;               /* element type of the pools and of every k, v, q, o buffer:
                                   KVC_DTYPE_BF16 (0) or KVC_DTYPE_F16 (1), the two 16-bit types the
                                   paged kernels take natively ([p3] §Precision and Hardware
-                                  Utilization); below, "bf16" reads as this type */
+                                  Utilization), or KVC_DTYPE_F32 (2), the full-precision pool ([p3]
+                                  FAQ on fp32 precision; [p4] §Memory Management and Debugging);
+                                  below, "bf16" reads as this type */
 } kvc_config;
 
-/* Element types (kvc_config.dtype).  Both are 16-bit; arithmetic is MFMA on
-   the 16-bit values with float32 accumulation and softmax either way. */
-enum { KVC_DTYPE_BF16 = 0, KVC_DTYPE_F16 = 1 };
+/* Element types (kvc_config.dtype).  With the 16-bit types arithmetic is
+   MFMA on the 16-bit values with float32 accumulation and softmax, and the
+   probabilities are rounded to the element type for the P.V product.  With
+   float32, products, sums and the softmax are float32 throughout (float32
+   MFMA, probabilities not rounded), every element takes 4 bytes, and
+   attention runs without KV splits. */
+enum { KVC_DTYPE_BF16 = 0, KVC_DTYPE_F16 = 1, KVC_DTYPE_F32 = 2 };
 
 /* [p3] §Inspecting Cache Statistics, plus the special-page counters. */
 typedef struct kvc_stats {

@@ -39,7 +39,8 @@ KVC_OPT_PROFILE = 3
 KVC_OPT_DEFER_EVICTION = 4
 KVC_DTYPE_BF16 = 0
 KVC_DTYPE_F16 = 1
-DTYPES = {"bf16": KVC_DTYPE_BF16, "f16": KVC_DTYPE_F16}
+KVC_DTYPE_F32 = 2
+DTYPES = {"bf16": KVC_DTYPE_BF16, "f16": KVC_DTYPE_F16, "f32": KVC_DTYPE_F32}
 
 KVC_KERNEL_ATTENTION = 0
 KVC_KERNEL_MERGE = 1
@@ -178,7 +179,8 @@ class PagedKVCache:
             return
         import torch
         self.torch = torch
-        self.elem_dtype = {KVC_DTYPE_BF16: torch.bfloat16, KVC_DTYPE_F16: torch.float16}[config.dtype]
+        self.elem_dtype = {KVC_DTYPE_BF16: torch.bfloat16, KVC_DTYPE_F16: torch.float16,
+                           KVC_DTYPE_F32: torch.float32}[config.dtype]
         self.device = torch.device(device)
         if self.device.type == "cuda" and self.device.index is None:
             self.device = torch.device("cuda", torch.cuda.current_device())

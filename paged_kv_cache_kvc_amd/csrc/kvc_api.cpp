@@ -56,7 +56,7 @@ Layout layout_of(const kvc::Config& c) {
   l.part_o = l.lse + align_up((size_t)KVC_MAX_SPLITS * rows * c.num_heads * sizeof(float), 256);
   l.q_rot = l.part_o + align_up((size_t)KVC_MAX_SPLITS * rows * c.num_heads * c.head_dim * sizeof(uint16_t), 256);
   // the step's query rows after the rotary embedding of kvc_run_rope
-  l.total = l.q_rot + align_up(rows * c.num_heads * c.head_dim * sizeof(uint16_t), 256);
+  l.total = l.q_rot + align_up(rows * c.num_heads * c.head_dim * (size_t)c.elem_bytes(), 256);
   return l;
 }
 
@@ -155,7 +155,7 @@ size_t kvc_pool_bytes(const kvc_config* cfg) {
   if (!cfg) return 0;
   const kvc::Config c = to_cfg(*cfg);
   if (kvc::validate(c, nullptr) != kvc::OK) return 0;
-  return (size_t)c.max_num_pages() * 2 * c.page_size * c.num_heads * c.head_dim * 2;
+  return (size_t)c.max_num_pages() * 2 * c.page_size * c.num_heads * c.head_dim * c.elem_bytes();
 }
 
 size_t kvc_workspace_bytes(const kvc_config* cfg) {
@@ -396,7 +396,7 @@ static kvc_status append_frames_impl(kvc_ctx* c, int32_t stream, int32_t block, 
   c->block_done[bd] = 1;
   if (c->metadata_only) return KVC_OK;
 
-  const size_t frame_bytes = (size_t)cf.tokens_per_frame * cf.num_heads * cf.head_dim * 2;
+  const size_t frame_bytes = (size_t)cf.tokens_per_frame * cf.num_heads * cf.head_dim * cf.elem_bytes();
   const size_t frame_table = (size_t)cf.tokens_per_frame * (cf.head_dim / 2);
   for (int32_t f = 0; f < num_frames; ++f) {
     kvc::AppendParams p;
@@ -412,6 +412,7 @@ static kvc_status append_frames_impl(kvc_ctx* c, int32_t stream, int32_t block, 
     p.dtype = cf.dtype;
     p.T = cf.tokens_per_frame;
     p.row_elems = cf.num_heads * cf.head_dim;
+    p.elem_bytes = cf.elem_bytes();
     p.special_row_offset = cf.special_row_offset;
     p.n_special = cf.num_special_tokens;
     p.page_size = cf.page_size;
@@ -557,6 +558,7 @@ static kvc_status launch_run(kvc_ctx* c, int32_t block, const void* q, void* o, 
     std::memcpy(a.recs, c->plan.image.data() + KVC_PLAN_HEADER_INTS, (size_t)a.num_streams * sizeof(kvc_dev_stream));
   const int32_t grid = 8 * a.items_per_xcd;
   int e = timed(c, KVC_KERNEL_ATTENTION, hs, [&] {
+    if (cf.fp32()) return kvc::launch_attention_f32(a, hs);
     return cf.tiles32() ? kvc::launch_attention32(a, grid, hs) : kvc::launch_attention(a, grid, hs);
   });
   if (e) return hip_fail(c, e, "attention launch");
@@ -606,7 +608,7 @@ kvc_status kvc_run_rope(kvc_ctx* c, int32_t block, const void* q, const float* r
   r.row_elems = cf.num_heads * cf.head_dim;
   r.head_dim = cf.head_dim;
   r.dtype = cf.dtype;
-  r.chunks = (int64_t)c->plan.qo_indptr.back() * (r.row_elems / 8);
+  r.chunks = (int64_t)c->plan.qo_indptr.back() * r.row_elems * cf.elem_bytes() / 16;
   if (r.chunks >= ((int64_t)1 << 31)) return fail(c, KVC_ERR_UNSUPPORTED, "more than 2^31 query chunks");
   const int e = timed(c, KVC_KERNEL_ROPE, hs, [&] { return kvc::launch_rope(r, hs); });
   if (e) return hip_fail(c, e, "rope launch");
@@ -672,7 +674,9 @@ kvc_status kvc_get_plan_shape(const kvc_ctx* c, int32_t* work_items, int32_t* gr
   if (!c->have_plan) return fail(const_cast<kvc_ctx*>(c), KVC_ERR_STATE, "no plan");
   if (work_items) *work_items = c->plan.num_items;
   if (group_rows) {
-    if (c->cfg.tiles32())
+    if (c->cfg.fp32())
+      *group_rows = KVC_F32_ROWS;
+    else if (c->cfg.tiles32())
       *group_rows = KVC_GROUP_TILES32 * KVC_Q_TILE32 + (c->plan.shared_tile ? KVC_TAIL_ROWS : 0);
     else
       *group_rows = kvc_group_tiles(c->plan.shared_tile ? 1 : 0) * KVC_Q_TILE;

@@ -36,7 +36,8 @@ int validate(const Config& c, std::string* why) {
   if ((int64_t)c.num_heads * c.head_dim > 65536) return fail(ERR_UNSUPPORTED, "num_heads * head_dim above 65536");
   if (c.max_frames_per_step < 1 || c.max_frames_per_step > 64)
     return fail(ERR_ARG, "max_frames_per_step must be in [1, 64]");
-  if (c.dtype != 0 && c.dtype != 1) return fail(ERR_UNSUPPORTED, "dtype must be KVC_DTYPE_BF16 or KVC_DTYPE_F16");
+  if (c.dtype < 0 || c.dtype > 2)
+    return fail(ERR_UNSUPPORTED, "dtype must be KVC_DTYPE_BF16, KVC_DTYPE_F16 or KVC_DTYPE_F32");
   if ((int64_t)c.num_streams * c.max_frames_per_step * c.tokens_per_frame >= (int64_t)1 << 24)
     return fail(ERR_UNSUPPORTED, "too many query rows");
   return OK;
@@ -254,7 +255,8 @@ void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const s
   // shortens them and the whole launch still fits in one round.
   double total_work = 0;
   for (int i = 0; i < n; ++i) total_work += (double)frames[i] * (double)kv_len[i];
-  const int32_t max_splits = std::max(1, std::min<int32_t>(pol.max_splits, KVC_MAX_SPLITS));
+  // (the float32 kernel runs without splits)
+  const int32_t max_splits = c.fp32() ? 1 : std::max(1, std::min<int32_t>(pol.max_splits, KVC_MAX_SPLITS));
   const int32_t upp = (int32_t)ceil_div(std::max(1, P), KVC_KV_TILE);
   const int32_t ups = (int32_t)ceil_div(c.page_size, KVC_KV_TILE);
   std::vector<int64_t> units(n), cap(n);
@@ -291,7 +293,11 @@ void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const s
     g.per_unit.resize(n);
     for (int i = 0; i < n; ++i) {
       const int64_t n_q = (int64_t)frames[i] * c.tokens_per_frame;
-      if (c.tiles32()) {
+      if (c.fp32()) {
+        // float32 kernel: one work-group wave per 16-row query tile
+        g.n_group[i] = ceil_div(n_q, KVC_F32_ROWS);
+        g.per_unit[i] = 1.0;
+      } else if (c.tiles32()) {
         // variant: rows past the last full 32-row tile, if at most 16, form a
         // tail that the four waves share (a quarter of its slots each)
         const int64_t rem = n_q % KVC_Q_TILE32;
@@ -361,7 +367,7 @@ void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const s
   // Take the grouping variant (a shared tail / a shared ninth tile) when it
   // gives the shorter launch.
   const Choice with_variant = choose(grouping(true)), without = choose(grouping(false));
-  p.shared_tile = !(without.cost < with_variant.cost);
+  p.shared_tile = !c.fp32() && !(without.cost < with_variant.cost);
   const Choice& ch = p.shared_tile ? with_variant : without;
   const std::vector<int64_t>& nsplit = ch.nsplit;
 

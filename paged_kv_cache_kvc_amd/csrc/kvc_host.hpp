@@ -26,7 +26,7 @@ struct Config {
   int32_t scale_frames = 0, sliding_window = 0, num_streams = 0;
   int32_t max_patch_pages = 0, max_special_pages = 0;
   int32_t max_frames_per_step = 1;
-  int32_t dtype = 0;   // element type: 0 bfloat16, 1 float16
+  int32_t dtype = 0;   // element type: 0 bfloat16, 1 float16, 2 float32
 
   int32_t patch_tokens() const { return tokens_per_frame - num_special_tokens; }
   int32_t max_num_pages() const { return max_patch_pages + max_special_pages; }
@@ -35,8 +35,13 @@ struct Config {
   int32_t tiles_capacity() const {
     return num_streams * ((max_frames_per_step * tokens_per_frame + KVC_Q_TILE32 - 1) / KVC_Q_TILE32);
   }
-  // the 32x32 attention kernel serves head_dim 32 and 64, the 16x16 one 128
-  bool tiles32() const { return head_dim <= 64; }
+  int32_t elem_bytes() const { return dtype == 2 ? 4 : 2; }
+  // float32 pools have an attention kernel of their own (one wave per 16
+  // query rows, no split)
+  bool fp32() const { return dtype == 2; }
+  // of the 16-bit kernels, the 32x32 one serves head_dim 32 and 64, the
+  // 16x16 one 128
+  bool tiles32() const { return head_dim <= 64 && !fp32(); }
 };
 
 // Result codes mirror kvc_status.

@@ -11,9 +11,10 @@ namespace kvc {
 
 struct AppendParams {
   void* pool;               // this block's pool
-  const void* k;            // [T, H, D] bf16
+  const void* k;            // [T, H, D] of the element type
   const void* v;
   int32_t T, row_elems;     // row_elems = H * D
+  int32_t elem_bytes;       // 2 (bf16, f16) or 4 (float32)
   int32_t special_row_offset, n_special, page_size;
   int32_t patch_page, sp_slot0, n_sp_pages;
   int32_t sp_pages[KVC_MAX_APPEND_SPECIAL_PAGES];
@@ -22,15 +23,15 @@ struct AppendParams {
   const float* rope_cos;
   const float* rope_sin;
   int32_t head_dim;
-  int32_t dtype;            // element type: 0 bfloat16, 1 float16
+  int32_t dtype;            // element type: 0 bfloat16, 1 float16, 2 float32
 };
 
 struct RopeParams {
-  const void* x;            // [rows, H, D] 16-bit elements
+  const void* x;            // [rows, H, D] elements of the element type
   void* y;                  // same shape, written; must not overlap x
   const float* cos;         // [rows, D/2] float32, 16-byte aligned
   const float* sin;
-  int64_t chunks;           // rows * H * D / 8
+  int64_t chunks;           // 16-byte chunks: rows * H * D * elem bytes / 16
   int32_t row_elems, head_dim;
   int32_t dtype;
 };
@@ -76,6 +77,7 @@ int launch_append(const AppendParams& p, void* hip_stream);
 int launch_rope(const RopeParams& p, void* hip_stream);
 int launch_attention(const AttnParams& p, int32_t grid, void* hip_stream);     // 16x16 kernel, head_dim 128
 int launch_attention32(const AttnParams& p, int32_t grid, void* hip_stream);   // 32x32 kernel, head_dim 32, 64
+int launch_attention_f32(const AttnParams& p, void* hip_stream);               // float32 pools, every head_dim
 int launch_merge(const MergeParams& p, void* hip_stream);
 // Device address and size of the static scratch of kvc_run_no_alloc on the
 // current device (looked up once per device); 0 or the hipError_t value.

@@ -12,6 +12,8 @@
 //                    Cache for Streaming 3D Reconstruction" §Attention Kernel
 //                    Execution; [p5] §Kernel Dispatch and Sequence Lengths).
 //   merge_kernel   - combines the KV splits of a row in fixed split order.
+//   attn_f32_kernel - paged attention on float32 pools (float32 MFMA,
+//                    probabilities not rounded), one wave per 16 queries.
 //   rope_kernel    - rotary position embedding of the step's query rows with
 //                    caller tables ([p2] §3D RoPE Position Encoding); the
 //                    key rows are turned inside append_kernel on their way to
@@ -78,6 +80,11 @@ template <>
 __device__ __forceinline__ double elem_to_f64<1>(uint32_t w, int half) {
   return (double)(float)__builtin_bit_cast(_Float16, (uint16_t)(half ? (w >> 16) : (w & 0xFFFFu)));
 }
+// float32: one element per word (`half` unused)
+template <>
+__device__ __forceinline__ double elem_to_f64<2>(uint32_t w, int half) {
+  return (double)__builtin_bit_cast(float, w);
+}
 
 template <int E>
 __device__ __forceinline__ uint32_t f64_to_elem(double x);
@@ -90,18 +97,53 @@ template <>
 __device__ __forceinline__ uint32_t f64_to_elem<1>(double x) {
   return __builtin_bit_cast(uint16_t, (_Float16)f64_to_f32_odd(x));
 }
+template <>
+__device__ __forceinline__ uint32_t f64_to_elem<2>(double x) {
+  return __builtin_bit_cast(uint32_t, (float)x);   // one rounding to nearest even
+}
 
-// One 16-byte chunk: four (even, odd) pairs, each 32-bit word one pair.
+// One 16-byte chunk: four (even, odd) pairs of 16-bit elements, each 32-bit
+// word one pair; or, for float32 (E = 2), two pairs in words (0, 1), (2, 3).
+// c and s hold the chunk's pairs' table entries (two used for float32).
 template <int E>
 __device__ __forceinline__ u32x4 rope_chunk(const u32x4& x, const f32x4& c, const f32x4& s) {
   u32x4 y;
+  if constexpr (E == 2) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const double a = elem_to_f64<E>(x[j], 0), b = elem_to_f64<E>(x[j], 1);
-    const double cj = (double)c[j], sj = (double)s[j];
-    y[j] = f64_to_elem<E>(a * cj - b * sj) | (f64_to_elem<E>(a * sj + b * cj) << 16);
+    for (int j = 0; j < 2; ++j) {
+      const double a = elem_to_f64<E>(x[2 * j], 0), b = elem_to_f64<E>(x[2 * j + 1], 0);
+      const double cj = (double)c[j], sj = (double)s[j];
+      y[2 * j] = f64_to_elem<E>(a * cj - b * sj);
+      y[2 * j + 1] = f64_to_elem<E>(a * sj + b * cj);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const double a = elem_to_f64<E>(x[j], 0), b = elem_to_f64<E>(x[j], 1);
+      const double cj = (double)c[j], sj = (double)s[j];
+      y[j] = f64_to_elem<E>(a * cj - b * sj) | (f64_to_elem<E>(a * sj + b * cj) << 16);
+    }
   }
   return y;
+}
+
+// Table entries of the pairs of 16-byte chunk i of a row (elements 16 / elem
+// bytes per chunk): four for 16-bit elements, two for float32.
+template <int E>
+__device__ __forceinline__ void rope_entries(const float* cos_row, const float* sin_row, uint32_t i, int head_dim,
+                                             f32x4& c, f32x4& s) {
+  constexpr uint32_t EPC = E == 2 ? 4 : 8;   // elements per chunk
+  const uint32_t pair0 = ((i * EPC) & (uint32_t)(head_dim - 1)) >> 1;
+  if constexpr (E == 2) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    const f32x2 c2 = *reinterpret_cast<const f32x2*>(cos_row + pair0);
+    const f32x2 s2 = *reinterpret_cast<const f32x2*>(sin_row + pair0);
+    c = f32x4{c2[0], c2[1], 0.f, 0.f};
+    s = f32x4{s2[0], s2[1], 0.f, 0.f};
+  } else {
+    c = *reinterpret_cast<const f32x4*>(cos_row + pair0);
+    s = *reinterpret_cast<const f32x4*>(sin_row + pair0);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -126,20 +168,21 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
     page = p.patch_page;
     slot = r < off ? r : r - p.n_special;
   }
-  const int chunks = p.row_elems >> 3;   // 16-byte chunks per row; H*D is a multiple of 32
-  const size_t row_off = (size_t)r * p.row_elems;
-  const u32x4* sk = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.k) + row_off);
-  const u32x4* sv = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.v) + row_off);
-  uint16_t* pool = static_cast<uint16_t*>(p.pool);
-  u32x4* dk = reinterpret_cast<u32x4*>(pool + (((size_t)page * 2 + 0) * p.page_size + slot) * p.row_elems);
-  u32x4* dv = reinterpret_cast<u32x4*>(pool + (((size_t)page * 2 + 1) * p.page_size + slot) * p.row_elems);
+  const size_t row_bytes = (size_t)p.row_elems * p.elem_bytes;
+  const int chunks = (int)(row_bytes >> 4);   // 16-byte chunks per row; H*D is a multiple of 32
+  const u32x4* sk = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(p.k) + (size_t)r * row_bytes);
+  const u32x4* sv = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(p.v) + (size_t)r * row_bytes);
+  uint8_t* pool = static_cast<uint8_t*>(p.pool);
+  u32x4* dk = reinterpret_cast<u32x4*>(pool + (((size_t)page * 2 + 0) * p.page_size + slot) * row_bytes);
+  u32x4* dv = reinterpret_cast<u32x4*>(pool + (((size_t)page * 2 + 1) * p.page_size + slot) * row_bytes);
   for (int i = threadIdx.x; i < 2 * chunks; i += blockDim.x) {
     if (i < chunks) {
       if constexpr (ROPE >= 0) {
-        // pairs (8i mod D)/2 .. +4 of this row's table entries
-        const size_t t = (size_t)r * (p.head_dim >> 1) + (((i << 3) & (p.head_dim - 1)) >> 1);
-        dk[i] = rope_chunk<ROPE>(sk[i], *reinterpret_cast<const f32x4*>(p.rope_cos + t),
-                                 *reinterpret_cast<const f32x4*>(p.rope_sin + t));
+        // this row's table entries of the chunk's pairs
+        const size_t t = (size_t)r * (p.head_dim >> 1);
+        f32x4 c, s;
+        rope_entries<ROPE>(p.rope_cos + t, p.rope_sin + t, (uint32_t)i, p.head_dim, c, s);
+        dk[i] = rope_chunk<ROPE>(sk[i], c, s);
       } else {
         dk[i] = sk[i];
       }
@@ -154,13 +197,12 @@ template <int E>
 __global__ __launch_bounds__(256) void rope_kernel(RopeParams p) {
   const uint32_t i = blockIdx.x * 256u + threadIdx.x;   // chunks < 2^31, checked by the host
   if (i >= (uint32_t)p.chunks) return;
-  const uint32_t cpr = (uint32_t)p.row_elems >> 3;
+  const uint32_t cpr = (uint32_t)p.row_elems / (E == 2 ? 4u : 8u);   // chunks per row
   const uint32_t row = i / cpr;
-  const uint32_t e0 = (i - row * cpr) << 3;
-  const size_t t = (size_t)row * (uint32_t)(p.head_dim >> 1) + ((e0 & (uint32_t)(p.head_dim - 1)) >> 1);
-  reinterpret_cast<u32x4*>(p.y)[i] =
-      rope_chunk<E>(reinterpret_cast<const u32x4*>(p.x)[i], *reinterpret_cast<const f32x4*>(p.cos + t),
-                    *reinterpret_cast<const f32x4*>(p.sin + t));
+  const size_t t = (size_t)row * (uint32_t)(p.head_dim >> 1);
+  f32x4 c, s;
+  rope_entries<E>(p.cos + t, p.sin + t, i - row * cpr, p.head_dim, c, s);
+  reinterpret_cast<u32x4*>(p.y)[i] = rope_chunk<E>(reinterpret_cast<const u32x4*>(p.x)[i], c, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -763,6 +805,164 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
 }
 
 // ---------------------------------------------------------------------------
+// attention on float32 pools
+// ---------------------------------------------------------------------------
+// The full-precision variant ([p3] FAQ on fp32 precision; [p4] §Memory
+// Management and Debugging): K, V, Q and O in float32, products and sums in
+// float32 on v_mfma_f32_16x16x4_f32, the online softmax in float32 (exact:
+// the running maximum moves at every stage) and the probabilities not
+// rounded.  Work item = (stream, head, 16-query tile), one work-group of
+// F32_WAVES waves: wave w takes units w, w + F32_WAVES, ... of the stream, and
+// the waves' softmax states are merged through LDS at the end (no split
+// across work-groups, hence no merge launch).
+//
+// Scores are transposed, S^T = K Q^T, per 16-slot block b of a unit: kv on
+// the rows, queries on the columns.  The contraction index d is assigned to
+// (k-step ks, lane group g = l / 16) as d = (D / 4) g + ks, so each lane reads
+// a contiguous quarter of a K row and of its query row.  Lane l then holds
+// the scores of query l % 16 with slots 16 b + 4 g + j (j = 0..3), and
+// O^T = V^T P^T takes k-step (b, j) with lane group g contributing slot
+// 16 b + 4 g + j: the B operand is the lane's own probability j.
+constexpr int F32_WAVES = 8;
+
+template <int D>
+__global__ __launch_bounds__(64 * F32_WAVES) void attn_f32_kernel(AttnParams p) {
+  constexpr int KQ = D / 4;    // contraction steps per block = floats per lane quarter
+  constexpr int DB = D / 16;   // 16-row blocks of O^T
+  constexpr int NV = 4 * DB + 2;   // floats per lane of a wave's state: O^T, max, sum
+  __shared__ float xs[F32_WAVES * 64 * NV];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int item = blockIdx.x;
+  const kvc_dev_stream st = stream_of_item(p, item);
+  const int local = item - st.item0;
+  const int tile = local % st.n_group;   // groups of one 16-row tile; one split
+  const int hd = local / st.n_group;
+  const int H = p.num_heads;
+  const int n = lane & 15, g = lane >> 4;
+  const size_t slot_elems = (size_t)H * D;
+  const float sl = p.scale_log2;
+
+  float qv[KQ];
+  {
+    const int row = min(16 * tile + n, st.n_q - 1);
+    const f32x4* qp = reinterpret_cast<const f32x4*>(static_cast<const float*>(p.q) +
+                                                     ((size_t)(st.q_row0 + row) * H + hd) * D + KQ * g);
+#pragma unroll
+    for (int i = 0; i < KQ / 4; ++i) {
+      const f32x4 x = qp[i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) qv[4 * i + j] = x[j];
+    }
+  }
+  f32x4 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, l = 0.f;   // running maximum of s * scale (log2 units) and sum
+
+  const float* pool = static_cast<const float*>(p.pool);
+  const int32_t* units = p.plan + st.unit0;
+  for (int u = wv; u < st.n_units; u += F32_WAVES) {
+    const uint32_t slot = (uint32_t)__builtin_amdgcn_readfirstlane(units[KVC_UNIT_INTS * u]);
+    const int valid = __builtin_amdgcn_readfirstlane(units[KVC_UNIT_INTS * u + 1]);
+    const float* kb = pool + (size_t)slot * slot_elems + (size_t)hd * D;   // K of the unit's first slot
+    const float* vb = kb + (size_t)p.page_size * slot_elems;              // its V
+    f32x4 sc[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      // rows past the valid count re-read the last valid one (masked below)
+      const f32x4* kp = reinterpret_cast<const f32x4*>(kb + (size_t)min(16 * b + n, valid - 1) * slot_elems + KQ * g);
+      float kq[KQ];
+#pragma unroll
+      for (int i = 0; i < KQ / 4; ++i) {
+        const f32x4 x = kp[i];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) kq[4 * i + j] = x[j];
+      }
+      sc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KQ; ++ks) sc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(kq[ks], qv[ks], sc[b], 0, 0, 0);
+    }
+    // scores in log2 units; slots at or past `valid` masked
+    float mx = -INFINITY;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float x = 16 * b + 4 * g + j < valid ? sc[b][j] * sl : -INFINITY;
+        sc[b][j] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mn = fmaxf(m, mx);
+    // nothing valid seen yet: keep everything at zero
+    const float alpha = mn == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m - mn);
+    float rs = 0.f;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float e = mn == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(sc[b][j] - mn);
+        sc[b][j] = e;
+        rs += e;
+      }
+    rs += __shfl_xor(rs, 16);
+    rs += __shfl_xor(rs, 32);
+    l = l * alpha + rs;
+    m = mn;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] *= alpha;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float* vr = vb + (size_t)min(16 * b + 4 * g + j, valid - 1) * slot_elems;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          o[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(vr[16 * db + n], sc[b][j], o[db], 0, 0, 0);
+      }
+  }
+  // merge the waves' states (weights 2^(m_w - max m); a wave that saw no
+  // valid slot has m = -inf and weighs nothing)
+  {
+    float* x = xs + (wv * 64 + lane) * NV;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[4 * db + r] = o[db][r];
+    x[4 * DB] = m;
+    x[4 * DB + 1] = l;
+  }
+  __syncthreads();
+  if (wv != 0) return;
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < F32_WAVES; ++w) M = fmaxf(M, xs[(w * 64 + lane) * NV + 4 * DB]);
+  float lsum = 0.f;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int w = 0; w < F32_WAVES; ++w) {
+    const float* x = xs + (w * 64 + lane) * NV;
+    const float wt = x[4 * DB] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(x[4 * DB] - M);
+    lsum += wt * x[4 * DB + 1];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[db][r] += wt * x[4 * db + r];
+  }
+  // lane l holds O^T[16 db + 4 g + r][query n] in element r of block db
+  const int row = 16 * tile + n;
+  if (row < st.n_q) {
+    const float inv = 1.0f / lsum;
+    float* orow = static_cast<float*>(p.o) + ((size_t)(st.q_row0 + row) * H + hd) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4*>(orow + 16 * db + 4 * g) = o[db] * inv;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // merge of KV splits
 // ---------------------------------------------------------------------------
 // One work-group per (32-row query tile, head) of a split stream, on the XCD
@@ -875,6 +1075,8 @@ int launch_append(const AppendParams& p, void* s) {
     hipLaunchKernelGGL(append_kernel<0>, dim3(p.T), dim3(256), 0, hs, p);
   else if (p.dtype == 1)
     hipLaunchKernelGGL(append_kernel<1>, dim3(p.T), dim3(256), 0, hs, p);
+  else if (p.dtype == 2)
+    hipLaunchKernelGGL(append_kernel<2>, dim3(p.T), dim3(256), 0, hs, p);
   else
     return (int)hipErrorInvalidValue;
   return (int)hipGetLastError();
@@ -888,6 +1090,8 @@ int launch_rope(const RopeParams& p, void* s) {
     hipLaunchKernelGGL(rope_kernel<0>, grid, dim3(256), 0, hs, p);
   else if (p.dtype == 1)
     hipLaunchKernelGGL(rope_kernel<1>, grid, dim3(256), 0, hs, p);
+  else if (p.dtype == 2)
+    hipLaunchKernelGGL(rope_kernel<2>, grid, dim3(256), 0, hs, p);
   else
     return (int)hipErrorInvalidValue;
   return (int)hipGetLastError();
@@ -912,6 +1116,26 @@ int launch_attention(const AttnParams& p, int32_t grid, void* s) {
   if (p.dtype == 0) return launch_attention_e<0>(p, grid, hs);
   if (p.dtype == 1) return launch_attention_e<1>(p, grid, hs);
   return (int)hipErrorInvalidValue;
+}
+
+int launch_attention_f32(const AttnParams& p, void* s) {
+  const hipStream_t hs = (hipStream_t)s;
+  const dim3 grid((unsigned)p.num_items), block(64 * F32_WAVES);
+  if (p.num_items == 0) return 0;
+  switch (p.head_dim) {
+    case 32:
+      hipLaunchKernelGGL(attn_f32_kernel<32>, grid, block, 0, hs, p);
+      break;
+    case 64:
+      hipLaunchKernelGGL(attn_f32_kernel<64>, grid, block, 0, hs, p);
+      break;
+    case 128:
+      hipLaunchKernelGGL(attn_f32_kernel<128>, grid, block, 0, hs, p);
+      break;
+    default:
+      return (int)hipErrorInvalidValue;
+  }
+  return (int)hipGetLastError();
 }
 
 template <int E, int CH>

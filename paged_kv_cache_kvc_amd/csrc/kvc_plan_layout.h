@@ -44,6 +44,8 @@
 #define KVC_GROUP_TILES32 8
 #define KVC_TAIL_WAVES 4
 #define KVC_TAIL_ROWS 16
+// Query rows per work item (one wave) of the float32 attention kernel.
+#define KVC_F32_ROWS 16
 // Upper bound of KV splits per stream (sizes the partial-output workspace).
 #define KVC_MAX_SPLITS 64
 // Ints per work-unit entry: slot index of the unit's first K row in the

@@ -89,15 +89,32 @@ REL_RMS_BOUND = 2.0 ** -6       # ||o - o_ref|| / ||o_ref||, bf16
 MAX_OVER_STD_BOUND = 0.25       # max |o - o_ref| / std(o_ref), bf16
 # f16 keeps 3 more significant bits: every term above shrinks by 8
 BOUNDS = {"bf16": (REL_RMS_BOUND, MAX_OVER_STD_BOUND), "f16": (REL_RMS_BOUND / 8, MAX_OVER_STD_BOUND / 8)}
+# float32 pools: nothing is rounded to 16 bits; what remains is float32
+# arithmetic (products and sums in the MFMA, 2^-24 relative per operation,
+# growing with the square root of the terms summed) and the exponential's
+# ulp error: about 2^-20 relative to the output, bounded here with a margin
+# of 16x.  The elementwise test uses ELEMENT_TOL["f32"].
+BOUNDS["f32"] = (2.0 ** -16, 2.0 ** -12)
+ELEMENT_TOL = {"bf16": (1e-2, 1e-2), "f16": (1e-2, 1e-2), "f32": (1e-5, 1e-4)}
 
 
-def check_close(out_bits: np.ndarray, ref: np.ndarray, atol=1e-2, rtol=1e-2, dtype: str = "bf16",
+def np_bits(dtype: str):
+    """numpy and torch integer types of the element type's bit patterns."""
+    import torch
+    return (np.uint32, torch.int32, np.int32) if dtype == "f32" else (np.uint16, torch.int16, np.int16)
+
+
+def check_close(out_bits: np.ndarray, ref: np.ndarray, atol=None, rtol=None, dtype: str = "bf16",
                 rel_rms_bound: Optional[float] = None, max_over_std_bound: Optional[float] = None
                 ) -> Dict[str, float]:
     """The acceptance test: |o - o_ref| <= atol + rtol * |o_ref| elementwise
     (the stated tolerance), and the relative RMS error and the largest error
     over the output's standard deviation within the rounding-model bounds
     above; returns error statistics."""
+    if atol is None:
+        atol = ELEMENT_TOL[dtype][0]
+    if rtol is None:
+        rtol = ELEMENT_TOL[dtype][1]
     if rel_rms_bound is None:
         rel_rms_bound = BOUNDS[dtype][0]
     if max_over_std_bound is None:
@@ -188,7 +205,7 @@ class Harness:
                                 patch_real=self.real_patch(s, f) or which == "q", dtype=wl.dtype)
 
     def to_dev(self, bits: np.ndarray, out=None):
-        t = self.torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(self.gpu.elem_dtype)
+        t = self.torch.from_numpy(np.ascontiguousarray(bits).view(np_bits(self.wl.dtype)[2])).view(self.gpu.elem_dtype)
         if out is None:
             return t.to(self.device)
         out.copy_(t)
@@ -255,7 +272,8 @@ class Harness:
                                  frames=[nf[s] for s in act])
         res["ora_plan"] = ora_plan
         res["gpu_plan"] = self.gpu.get_plan()
-        res["out_bits"] = {b: out.view(self.torch.int16).cpu().numpy().view(np.uint16) for b, (q, out) in outs.items()}
+        nb, tb, _ = np_bits(self.wl.dtype)
+        res["out_bits"] = {b: out.view(tb).cpu().numpy().view(nb) for b, (q, out) in outs.items()}
         res["q_bits"] = {b: q for b, (q, out) in outs.items()}
         if check:
             res["ref"] = {b: self.ora.attend(ora_plan, b, q) for b, (q, out) in outs.items() if b in self.ora.pools}
@@ -272,4 +290,5 @@ class Harness:
         self.skew[s] += 1
 
     def pool_bits(self, block: int) -> np.ndarray:
-        return self.gpu.pools[block].view(self.torch.int16).cpu().numpy().view(np.uint16)
+        nb, tb, _ = np_bits(self.wl.dtype)
+        return self.gpu.pools[block].view(tb).cpu().numpy().view(nb)

@@ -184,11 +184,14 @@ def test_bad_arguments_and_capacity():
     small.max_patch_pages = wl.scale_frames + wl.sliding_window      # no room for the appended frame
     assert lib.kvc_create_metadata_only(ctypes.byref(small), None, None, ctypes.byref(ctx)) == kvc.KVC_ERR_CAPACITY
     dt = cfg_of(wl)
-    dt.dtype = 2                                                      # neither bf16 nor f16
+    dt.dtype = 3                                                      # none of bf16, f16, f32
     assert lib.kvc_create_metadata_only(ctypes.byref(dt), None, None, ctypes.byref(ctx)) == kvc.KVC_ERR_UNSUPPORTED
     assert lib.kvc_pool_bytes(ctypes.byref(dt)) == 0
     dt.dtype = kvc.KVC_DTYPE_F16                                      # same sizes as bf16
     assert lib.kvc_pool_bytes(ctypes.byref(dt)) == lib.kvc_pool_bytes(ctypes.byref(good))
+    dt.dtype = kvc.KVC_DTYPE_F32                                      # 4-byte elements
+    assert lib.kvc_pool_bytes(ctypes.byref(dt)) == 2 * lib.kvc_pool_bytes(ctypes.byref(good))
+    assert lib.kvc_workspace_bytes(ctypes.byref(dt)) > lib.kvc_workspace_bytes(ctypes.byref(good))
     with pytest.raises(kvc.KvcError):
         kvc.make_config(1, 2, 32, 22, dtype="fp8")
     pg = cfg_of(wl)
@@ -396,6 +399,24 @@ def test_split_counts_fill_one_round(name):
     u, g, n = units[i], heads[i], ns[i]
     if n < min(kvc.MAX_SPLITS, u) and ceil(u, n + 1) < ceil(u, n):
         assert items + g > target, (name, i, ns)
+
+
+def test_f32_plan_has_no_splits():
+    """Float32 pools: one work item (one wave) per 16-query tile and head,
+    no KV split, hence no merge order; the 262-query frame of the base
+    workload makes 17 tiles x 16 heads = 272 items."""
+    wl = syn.WORKLOADS["base"]
+    cfg = cfg_of(wl)
+    cfg.dtype = kvc.KVC_DTYPE_F32
+    c = kvc.PagedKVCache(cfg, metadata_only=True)
+    for _ in range(80):
+        c.append_frame(0)
+        c.evict_frames()
+        c.plan()
+    assert list(c.get_plan()["n_splits"]) == [1]
+    assert c.get_plan_shape() == {"work_items": 272, "group_rows": 16}
+    img = c.get_plan_image()
+    assert img[3] == 0 and img[5] == 0 and img[7] == 0   # no split, no shared tile, no merge slots
 
 
 def test_query_grouping_choice():
