@@ -71,20 +71,22 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def attention_kernel_name(head_dim, dtype="bf16"):
-    """The attention kernel that serves a head size and element type: for the
-    16-bit types the 32x32 kernel up to 64 and the 16x16 one at 128; the
-    float32 kernel for float32 pools."""
+def attention_kernel_name(cache, dtype="bf16"):
+    """The attention kernel of the cache's current plan: the float32 kernel
+    for float32 pools; for the 16-bit types the 32x32 kernel (groups of 256
+    or 272 query rows: head_dim 32, and 64 unless the planner took the other)
+    or the 16x16 one (groups of 128 or 144 rows: head_dim 128, and 64 where
+    fewer query tiles would leave compute units idle)."""
     if dtype == "f32":
         return "attn_f32_kernel"
-    return "attn32_kernel" if head_dim <= 64 else "attn_kernel"
+    return "attn32_kernel" if cache.get_plan_shape()["group_rows"] >= 256 else "attn_kernel"
 
 
-def read_traffic(workload, head_dim, dtype="bf16"):
+def read_traffic(workload, kernel):
     """HBM bytes per attention launch from the committed rocprofv3 counter
     summary (FETCH_SIZE and WRITE_SIZE, calibrated against a plain copy), or
     None when it is missing or was taken on other kernel source."""
-    p = os.path.join(ROOT, "profiles", f"{attention_kernel_name(head_dim, dtype)}_{workload}_hbm_traffic.md")
+    p = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_traffic.md")
     if not os.path.exists(p):
         return None
     fields = {}
@@ -217,6 +219,8 @@ def scale_phase(args, torch, syn, kvc, dev):
                           max_special_pages=wl.max_special_pages, special_row_offset=wl.row_offset,
                           max_frames_per_step=S, dtype=args.dtype)
     cache = kvc.PagedKVCache(cfg, device=dev)
+    if args.query_tile:
+        cache.set_option(kvc.KVC_OPT_QUERY_TILE, args.query_tile)
     el = cache.elem_dtype
     g = torch.Generator(device=dev)
     g.manual_seed(wl.seed)
@@ -280,7 +284,7 @@ def scale_phase(args, torch, syn, kvc, dev):
                                 f"{wl.num_special_tokens} special tokens in one step, page_size {wl.page_size}"),
                    "num_blocks": nb, "query_rows": S * T, "visible_tokens": L, "num_heads": H, "head_dim": D},
         "roofline": roof,
-        "attention": {"kernel": attention_kernel_name(wl.head_dim, args.dtype), "launches": a_n, "avg_us": 1e3 * a_ms / max(a_n, 1),
+        "attention": {"kernel": attention_kernel_name(cache, args.dtype), "launches": a_n, "avg_us": 1e3 * a_ms / max(a_n, 1),
                       "attention_plus_merge_us": 1e6 * a_s, "tflops": tfl, "gbs": gbs,
                       "alg_flop_per_launch": flop, "alg_bytes_per_launch": byts,
                       "merge_avg_us": 1e3 * m_ms / max(m_n, 1), "merge_launches": m_n,
@@ -303,6 +307,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--target-wgs", type=int, default=None)
     ap.add_argument("--max-splits", type=int, default=None)
+    ap.add_argument("--query-tile", type=int, default=0, choices=[0, 16, 32],
+                    help="head_dim 64: query rows per MFMA tile (0: the planner's choice)")
     ap.add_argument("--no-profile", action="store_true", help="time without per-launch HIP events")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times (HBM counter calibration)")
@@ -359,6 +365,8 @@ def main():
         cache.set_option(kvc.KVC_OPT_TARGET_WORKGROUPS, args.target_wgs)
     if args.max_splits:
         cache.set_option(kvc.KVC_OPT_MAX_SPLITS, args.max_splits)
+    if args.query_tile:
+        cache.set_option(kvc.KVC_OPT_QUERY_TILE, args.query_tile)
 
     # device-resident input bank: [stream][bank][block] frames
     progress(f"workload {wl.name}: generating input bank")
@@ -492,7 +500,8 @@ def main():
         gbs_step = pb / K / step_s / 1e9
         tfl_step = pf / K / step_s / 1e12
         bound = "hbm" if pf / pb < peak_mfma * 1e12 / (PEAK_HBM_GBS * 1e9) else "mfma"
-        traffic = read_traffic(wl.name, D, args.dtype)
+        kname = attention_kernel_name(cache, args.dtype)
+        traffic = read_traffic(wl.name, kname)
         if bound == "hbm":
             roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
                     "frac_attention_kernel_only": gbs_a / PEAK_HBM_GBS, "frac_whole_step": gbs_step / PEAK_HBM_GBS}
@@ -505,7 +514,7 @@ def main():
         out["roofline"] = roof
         peaks = achievable_peaks(torch, dev)
         out["attention"] = {
-            "kernel": attention_kernel_name(D, args.dtype), "launches": a_n, "avg_us": 1e3 * a_ms / max(a_n, 1),
+            "kernel": kname, "launches": a_n, "avg_us": 1e3 * a_ms / max(a_n, 1),
             "tflops": tfl_a, "gbs": gbs_a, "frac_hbm": gbs_a / PEAK_HBM_GBS, "frac_mfma": tfl_a / peak_mfma,
             "alg_bytes_per_launch": pb / max(a_n, 1), "alg_flop_per_launch": pf / max(a_n, 1),
             "merge_avg_us": 1e3 * m_ms / max(m_n, 1), "merge_launches": m_n,

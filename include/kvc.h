@@ -133,12 +133,17 @@ typedef struct kvc_stats {
 /* Tunables for kvc_set_option / kvc_get_option. */
 enum {
   KVC_OPT_TARGET_WORKGROUPS = 1, /* attention work-groups the planner fills per run without exceeding it
-                                    (default: what the device holds at once, 2 per CU for head_dim <= 64,
-                                    1 per CU for 128) */
+                                    (default: the device's compute-unit count, one resident work-group
+                                    each; the 16-row kernel at head_dim 64 holds two per CU and fills
+                                    twice this) */
   KVC_OPT_MAX_SPLITS = 2,        /* cap on KV splits per stream; 1 disables split-KV (default 64, the maximum) */
   KVC_OPT_PROFILE = 3,           /* 1: time every attention/merge/append/rope launch with HIP events */
-  KVC_OPT_DEFER_EVICTION = 4     /* 1: hold evicted window pages back until the stream's next frame,
+  KVC_OPT_DEFER_EVICTION = 4,    /* 1: hold evicted window pages back until the stream's next frame,
                                     so that kvc_rollback can undo the latest frame (default 0) */
+  KVC_OPT_QUERY_TILE = 5         /* query rows per MFMA tile of the 16-bit attention kernel at head_dim 64:
+                                    0 = the planner's choice (default), 16 or 32 = that kernel always.
+                                    head_dim 32 has only the 32-row kernel, 128 only the 16-row one and
+                                    float32 pools their own: there the setting is ignored */
 };
 
 /* Kernels for kvc_profile_read. */
@@ -348,11 +353,14 @@ kvc_status kvc_get_plan(const kvc_ctx* ctx, int32_t* planned_streams, int32_t* k
 
 /* Shape of the current plan's attention launch (for tests and tuning):
  *   work_items: attention work-groups, (stream, head, KV split, query group);
- *   group_rows: most query rows one work-group covers.  head_dim 32 and 64:
+ *   group_rows: most query rows one work-group covers.  The 32-row kernel
+ *               (head_dim 32, and 64 unless the plan takes the 16-row one):
  *               4 waves x 2 tiles x 32 rows = 256, plus 16 when the launch
  *               lets a group carry a tail of up to 16 rows shared by the
- *               waves (272); head_dim 128: 8 tiles x 16 rows = 128, or 144
- *               with a ninth tile shared by the waves.
+ *               waves (272); the 16-row kernel (head_dim 128, and 64 where
+ *               the planner or KVC_OPT_QUERY_TILE picks it): 8 tiles x 16
+ *               rows = 128, or 144 with a ninth tile shared by the waves
+ *               (head_dim 128 only); float32 pools: 16.
  * Either pointer may be NULL.  Errors: KVC_ERR_ARG, KVC_ERR_STATE (no plan). */
 kvc_status kvc_get_plan_shape(const kvc_ctx* ctx, int32_t* work_items, int32_t* group_rows);
 

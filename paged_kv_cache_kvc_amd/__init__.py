@@ -37,6 +37,7 @@ KVC_OPT_TARGET_WORKGROUPS = 1
 KVC_OPT_MAX_SPLITS = 2
 KVC_OPT_PROFILE = 3
 KVC_OPT_DEFER_EVICTION = 4
+KVC_OPT_QUERY_TILE = 5
 KVC_DTYPE_BF16 = 0
 KVC_DTYPE_F16 = 1
 KVC_DTYPE_F32 = 2

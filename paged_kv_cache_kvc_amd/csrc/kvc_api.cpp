@@ -559,7 +559,8 @@ static kvc_status launch_run(kvc_ctx* c, int32_t block, const void* q, void* o, 
   const int32_t grid = 8 * a.items_per_xcd;
   int e = timed(c, KVC_KERNEL_ATTENTION, hs, [&] {
     if (cf.fp32()) return kvc::launch_attention_f32(a, hs);
-    return cf.tiles32() ? kvc::launch_attention32(a, grid, hs) : kvc::launch_attention(a, grid, hs);
+    return cf.tiles32() && !c->plan.tiles16 ? kvc::launch_attention32(a, grid, hs)
+                                            : kvc::launch_attention(a, grid, hs);
   });
   if (e) return hip_fail(c, e, "attention launch");
   if (c->plan.any_split) {
@@ -676,7 +677,7 @@ kvc_status kvc_get_plan_shape(const kvc_ctx* c, int32_t* work_items, int32_t* gr
   if (group_rows) {
     if (c->cfg.fp32())
       *group_rows = KVC_F32_ROWS;
-    else if (c->cfg.tiles32())
+    else if (c->cfg.tiles32() && !c->plan.tiles16)
       *group_rows = KVC_GROUP_TILES32 * KVC_Q_TILE32 + (c->plan.shared_tile ? KVC_TAIL_ROWS : 0);
     else
       *group_rows = kvc_group_tiles(c->plan.shared_tile ? 1 : 0) * KVC_Q_TILE;
@@ -752,6 +753,10 @@ kvc_status kvc_set_option(kvc_ctx* c, int32_t option, int64_t value) {
       if (value != 0 && value != 1) return fail(c, KVC_ERR_ARG, "defer eviction is 0 or 1");
       c->alloc.set_defer_eviction(value != 0);
       return KVC_OK;
+    case KVC_OPT_QUERY_TILE:
+      if (value != 0 && value != 16 && value != 32) return fail(c, KVC_ERR_ARG, "query tile is 0, 16 or 32");
+      c->policy.query_tile = (int32_t)value;
+      return KVC_OK;
     default:
       return fail(c, KVC_ERR_ARG, "unknown option");
   }
@@ -764,6 +769,7 @@ kvc_status kvc_get_option(const kvc_ctx* c, int32_t option, int64_t* value) {
     case KVC_OPT_MAX_SPLITS: *value = c->policy.max_splits; return KVC_OK;
     case KVC_OPT_PROFILE: *value = c->profile ? 1 : 0; return KVC_OK;
     case KVC_OPT_DEFER_EVICTION: *value = c->alloc.defer_eviction() ? 1 : 0; return KVC_OK;
+    case KVC_OPT_QUERY_TILE: *value = c->policy.query_tile; return KVC_OK;
     default: return KVC_ERR_ARG;
   }
 }

@@ -270,11 +270,11 @@ void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const s
   }
   // The 32x32 kernel stages a split's unit entries in LDS: at most
   // KVC_MAX_SPLIT_STAGES units per split.
-  std::vector<int64_t> min_split(n, 1);
+  std::vector<int64_t> min_split32(n, 1), cap32 = cap;
   if (c.tiles32())
     for (int i = 0; i < n; ++i) {
-      min_split[i] = ceil_div(units[i], KVC_MAX_SPLIT_STAGES);
-      cap[i] = std::max(cap[i], min_split[i]);
+      min_split32[i] = ceil_div(units[i], KVC_MAX_SPLIT_STAGES);
+      cap32[i] = std::max(cap[i], min_split32[i]);
     }
   // A query grouping: per stream, its groups, (32x32 kernel) full 32-row
   // tiles and tail, and the per-unit cost of its busiest wave in 16x64
@@ -283,10 +283,12 @@ void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const s
     std::vector<int64_t> n_group, n_t32, tail;
     std::vector<double> per_unit;
     bool variant = false;
+    bool k32 = false;   // the 32x32 kernel
   };
-  auto grouping = [&](bool variant) {
+  auto grouping = [&](bool variant, bool k32) {
     Grouping g;
     g.variant = variant;
+    g.k32 = k32;
     g.n_group.resize(n);
     g.n_t32.assign(n, 0);
     g.tail.assign(n, 0);
@@ -297,7 +299,7 @@ void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const s
         // float32 kernel: one work-group wave per 16-row query tile
         g.n_group[i] = ceil_div(n_q, KVC_F32_ROWS);
         g.per_unit[i] = 1.0;
-      } else if (c.tiles32()) {
+      } else if (k32) {
         // variant: rows past the last full 32-row tile, if at most 16, form a
         // tail that the four waves share (a quarter of its slots each)
         const int64_t rem = n_q % KVC_Q_TILE32;
@@ -325,19 +327,24 @@ void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const s
     Grouping g;
     std::vector<int64_t> nsplit;
     double cost;
+    double length;         // per-unit cost times units of the longest split
+    int64_t items_total;   // work-groups of the launch
   };
-  auto choose = [&](const Grouping& g) {
+  // target: the work-groups the device holds at once for the kernel
+  auto choose = [&](const Grouping& g, int64_t target) {
     Choice ch;
     ch.g = g;
     ch.nsplit.resize(n);
     std::vector<int64_t> items(n);
     int64_t items_total = 0;
+    const std::vector<int64_t>& min_split = g.k32 ? min_split32 : std::vector<int64_t>(n, 1);
+    const std::vector<int64_t>& capk = g.k32 ? cap32 : cap;
     for (int i = 0; i < n; ++i) {
       items[i] = (int64_t)c.num_heads * g.n_group[i];
-      const double want = total_work > 0 ? (double)pol.target_workgroups * (double)frames[i] * (double)kv_len[i] /
+      const double want = total_work > 0 ? (double)target * (double)frames[i] * (double)kv_len[i] /
                                                total_work / (double)items[i]
                                          : 1.0;
-      ch.nsplit[i] = std::max<int64_t>(min_split[i], std::min<int64_t>((int64_t)std::floor(want), cap[i]));
+      ch.nsplit[i] = std::max<int64_t>(min_split[i], std::min<int64_t>((int64_t)std::floor(want), capk[i]));
       items_total += items[i] * ch.nsplit[i];
     }
     auto length = [&](int i, int64_t ns) { return (double)ceil_div(units[i], ns) * g.per_unit[i]; };
@@ -353,22 +360,51 @@ void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const s
     };
     for (;;) {
       const int b = longest();
-      if (ch.nsplit[b] >= cap[b] || items_total + items[b] > pol.target_workgroups ||
+      if (ch.nsplit[b] >= capk[b] || items_total + items[b] > target ||
           ceil_div(units[b], ch.nsplit[b] + 1) >= ceil_div(units[b], ch.nsplit[b]))
         break;
       ++ch.nsplit[b];
       items_total += items[b];
     }
-    const int64_t rounds = std::max<int64_t>(1, ceil_div(items_total, std::max(1, pol.target_workgroups)));
+    const int64_t rounds = std::max<int64_t>(1, ceil_div(items_total, std::max<int64_t>(1, target)));
     const int b = longest();
-    ch.cost = length(b, ch.nsplit[b]) * (double)rounds;
+    ch.length = length(b, ch.nsplit[b]);
+    ch.items_total = items_total;
+    ch.cost = ch.length * (double)rounds;
     return ch;
   };
   // Take the grouping variant (a shared tail / a shared ninth tile) when it
-  // gives the shorter launch.
-  const Choice with_variant = choose(grouping(true)), without = choose(grouping(false));
-  p.shared_tile = !c.fp32() && !(without.cost < with_variant.cost);
-  const Choice& ch = p.shared_tile ? with_variant : without;
+  // gives the shorter launch.  At head_dim 64 the 16x16 kernel (up to two
+  // work-groups of four waves per CU) competes with the 32x32 one (one of
+  // eight, two waves per SIMD).  Its cost is per SIMD too: its per-wave cost
+  // times the work-groups that the busiest CU runs (the two resident ones
+  // share its SIMDs).  It wins where the 32x32 kernel's groups of 8 tiles of
+  // 32 rows spill past one round of work-groups while its own groups of 128
+  // rows spread more evenly, as for a multi-frame step over many heads.
+  // Only its plain grouping is offered (its shared-tile form does not fit
+  // the registers at head_dim 64).
+  constexpr double KVC_TILES16_COST = 1.0;   // relative cost of its tile-step
+  const int32_t tgt = std::max(1, pol.target_workgroups);
+  const bool k32 = c.tiles32();
+  Choice ch = choose(grouping(true, k32), tgt);
+  p.shared_tile = !c.fp32();
+  {
+    Choice cand = choose(grouping(false, k32), tgt);
+    if (cand.cost < ch.cost) {
+      ch = std::move(cand);
+      p.shared_tile = false;
+    }
+  }
+  p.tiles16 = false;
+  if (k32 && c.head_dim == 64 && pol.query_tile != 32) {
+    Choice cand = choose(grouping(false, false), 2 * (int64_t)tgt);
+    cand.cost = cand.length * (double)ceil_div(cand.items_total, (int64_t)tgt) * KVC_TILES16_COST;
+    if (pol.query_tile == 16 || cand.cost < ch.cost) {
+      ch = std::move(cand);
+      p.shared_tile = false;
+      p.tiles16 = true;
+    }
+  }
   const std::vector<int64_t>& nsplit = ch.nsplit;
 
   p.image.assign(KVC_PLAN_HEADER_INTS + (size_t)KVC_STREAM_REC_INTS * n + p.kv_indices.size(), 0);
@@ -413,7 +449,7 @@ void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const s
   p.image[KVC_HDR_NUM_ROWS] = p.num_rows;
   p.image[KVC_HDR_ANY_SPLIT] = p.any_split ? 1 : 0;
   p.image[KVC_HDR_NUM_TILES] = p.num_tiles;
-  p.image[KVC_HDR_SHARED_TILE] = p.shared_tile ? 1 : 0;
+  p.image[KVC_HDR_SHARED_TILE] = (p.shared_tile ? 1 : 0) | (p.tiles16 ? KVC_VARIANT_TILES16 : 0);
   std::copy(p.kv_indices.begin(), p.kv_indices.end(),
             p.image.begin() + KVC_PLAN_HEADER_INTS + (size_t)KVC_STREAM_REC_INTS * n);
 
@@ -472,7 +508,7 @@ void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const s
     for (int32_t t = 0; t < ntile; ++t) {
       // the query group holding (the first rows of) tile t
       int32_t grp = 0;
-      if (c.tiles32()) {
+      if (k32 && !p.tiles16) {
         if (t >= r.n_t32)
           grp = r.n_group - 1;   // the tail
         else

@@ -114,6 +114,9 @@ class Allocator {
 struct PlanPolicy {
   int32_t target_workgroups = 512;
   int32_t max_splits = KVC_MAX_SPLITS;
+  // head_dim 64, 16-bit pools: 0 = the kernel whose launch the cost model
+  // finds shorter, 16 / 32 = the 16x16 / 32x32 kernel always
+  int32_t query_tile = 0;
 };
 
 // Host image of one step's plan.
@@ -131,6 +134,7 @@ struct HostPlan {
   int32_t num_tiles = 0;
   bool shared_tile = true;             // launch variant (KVC_HDR_SHARED_TILE): 32x32 kernel: groups may carry a
                                        // 16-row tail; 16x16 kernel: groups with a shared ninth tile
+  bool tiles16 = false;                // head_dim 64 served by the 16x16 kernel (KVC_VARIANT_TILES16)
   int32_t merge_table = 0;             // offset in ints of the merge order in image
   int32_t merge_slots = 0;             // merge slots per XCD
   bool any_split = false;

@@ -1098,11 +1098,19 @@ int launch_rope(const RopeParams& p, void* s) {
 }
 
 // Instantiations by (D, element type).  The 16x16 attention kernel serves
-// head_dim 128; 32 and 64 go to the 32x32 kernel (kvc_attn.hip).
+// head_dim 128, and 64 where the plan picks it (the multi-frame scale step);
+// otherwise 32 and 64 go to the 32x32 kernel (kvc_attn.hip).
 template <int E, bool SH>
 static int launch_attention_es(const AttnParams& p, int32_t grid, hipStream_t hs) {
-  if (p.head_dim != 128) return (int)hipErrorInvalidValue;
-  hipLaunchKernelGGL((attn_kernel<128, E, SH>), dim3(grid), dim3(256), 0, hs, p);
+  if (p.head_dim == 128)
+    hipLaunchKernelGGL((attn_kernel<128, E, SH>), dim3(grid), dim3(256), 0, hs, p);
+  else if constexpr (!SH) {
+    // head_dim 64 in 16-row tiles (two work-groups per CU) for plans with few
+    // query tiles; the shared-tile form does not fit the registers there
+    if (p.head_dim != 64) return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL((attn_kernel<64, E, false>), dim3(grid), dim3(256), 0, hs, p);
+  } else
+    return (int)hipErrorInvalidValue;
   return (int)hipGetLastError();
 }
 

@@ -65,8 +65,11 @@
 #define KVC_HDR_NUM_ROWS 2
 #define KVC_HDR_ANY_SPLIT 3
 #define KVC_HDR_NUM_TILES 4
-#define KVC_HDR_SHARED_TILE 5  // launch variant: 32x32 kernel: 1 = query groups may carry a shared 16-row
-                               // tail; 16x16 kernel: 1 = groups of up to 9 tiles (a shared ninth), 0 = 8
+#define KVC_HDR_SHARED_TILE 5  // launch variant: bit 0: 32x32 kernel: query groups may carry a shared
+                               // 16-row tail; 16x16 kernel: groups of up to 9 tiles (a shared ninth)
+                               // instead of 8; bit 1 (KVC_VARIANT_TILES16): head_dim 64 served by the
+                               // 16x16 kernel
+#define KVC_VARIANT_TILES16 2
 #define KVC_HDR_MERGE_TABLE 6  // offset in ints of the merge order
 #define KVC_HDR_MERGE_SLOTS 7  // merge slots per XCD (the merge grid is 8 times this)
 // XCDs of the device; work-groups are dispatched to them round-robin.

@@ -252,16 +252,17 @@ def test_scale_phase_multi_frame_prefill():
 
 
 def test_scale_phase_full_heads():
-    """The 8-frame scale step at the full H=16, D=64 shape: 2096 queries over
-    2096 tokens in 144 work-groups (9 query groups of 8 tiles per head, one
-    split: a second split would need a second round of work-groups and a
-    merge, which measured slower); output against the oracle, pool
-    bit-exact."""
+    """The 8-frame scale step at the full H=16, D=64 shape on the 32x32
+    kernel: 2096 queries over 2096 tokens in 144 work-groups (9 query groups
+    of 8 tiles of 32 rows per head, one split: a second split would need a
+    second round of work-groups and a merge); output against the oracle,
+    pool bit-exact."""
     _need_gpu()
     import dataclasses
+    import paged_kv_cache_kvc_amd as kvc
     wl = dataclasses.replace(syn.WORKLOADS["base"], frames=(12,))
     S = wl.scale_frames
-    h = Harness(wl, max_frames_per_step=S)
+    h = Harness(wl, max_frames_per_step=S, options={kvc.KVC_OPT_QUERY_TILE: 32})
     res = h.step(check=True, nframes={0: S})
     compare_plan(res)
     assert list(res["gpu_plan"]["n_splits"]) == [1]

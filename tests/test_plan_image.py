@@ -9,6 +9,7 @@ table order, within that page's valid slots, and the units add up to the
 visible length; the splits of every work item tile the units; the merge order
 lists each (query tile, head) of a split stream exactly once, on the XCD of
 its middle split, with the tile's split count and output rows."""
+import dataclasses
 import math
 
 import numpy as np
@@ -26,13 +27,14 @@ REC_FIELDS = ("q_row0", "n_q", "page0", "n_patch", "n_pages", "last_len", "kv_le
               "reserved0", "reserved1")
 
 
-def expected_grouping(wl, n_q, shared):
-    """(n_group, n_t32, tail) of a stream with n_q query rows.  Up to D = 64
-    a group is 4 waves x 2 tiles of 32 rows; with the shared variant, rows
-    past the last full tile form a 16-row tail of the last group when there
-    are at most 16 of them.  At D = 128 a group is 8 tiles of 16 rows, or 9
-    with the shared variant."""
-    if wl.head_dim <= 64:
+def expected_grouping(wl, n_q, shared, k32):
+    """(n_group, n_t32, tail) of a stream with n_q query rows.  With the
+    32x32 kernel (D = 32 or 64) a group is 4 waves x 2 tiles of 32 rows; with
+    the shared variant, rows past the last full tile form a 16-row tail of
+    the last group when there are at most 16 of them.  With the 16x16 kernel
+    (D = 128, or D = 64 when the plan takes it) a group is 8 tiles of 16
+    rows, or 9 with the shared variant."""
+    if k32:
         rem = n_q % Q_TILE32
         tail = 1 if shared and 1 <= rem <= TAIL_ROWS else 0
         nt = n_q // Q_TILE32 if tail else -(-n_q // Q_TILE32)
@@ -40,9 +42,9 @@ def expected_grouping(wl, n_q, shared):
     return -(-(-(-n_q // Q_TILE16)) // (9 if shared else 8)), 0, 0
 
 
-def merge_group(wl, r, t):
+def merge_group(r, t, k32):
     """The query group that computes (the first rows of) 32-row tile t."""
-    if wl.head_dim <= 64:
+    if k32:
         if t >= r["n_t32"]:
             return r["n_group"] - 1
         return next(g for g in range(r["n_group"]) if t < (g + 1) * r["n_t32"] // r["n_group"])
@@ -59,8 +61,13 @@ def check_image(wl, c):
     n_streams, n_items, n_rows, any_split, n_tiles, shared, merge_at, merge_slots = (int(x) for x in img[:HEADER])
     n = len(plan["planned"])
     assert n_streams == n
-    assert shared in (0, 1)
-    if wl.head_dim <= 64:
+    # bit 0: the shared variant; bit 1: the 16x16 kernel at head_dim 64
+    tiles16 = bool(shared & 2)
+    shared &= 1
+    assert img[5] in (0, 1, 2)
+    assert not tiles16 or wl.head_dim == 64
+    k32 = wl.head_dim <= 64 and not tiles16
+    if k32:
         assert shape["group_rows"] == 2 * WAVES32 * Q_TILE32 + (TAIL_ROWS if shared else 0)
     else:
         assert shape["group_rows"] == (9 if shared else 8) * Q_TILE16
@@ -95,14 +102,14 @@ def check_image(wl, c):
         assert got == expect
         assert sum(v for _, _, v in got) == r["kv_len"]
         # work items: heads x splits x query groups, every split non-empty
-        assert (r["n_group"], r["n_t32"], r["tail"]) == expected_grouping(wl, r["n_q"], shared)
-        if wl.head_dim <= 64:
+        assert (r["n_group"], r["n_t32"], r["tail"]) == expected_grouping(wl, r["n_q"], shared, k32)
+        if k32:
             assert all((g + 1) * r["n_t32"] // r["n_group"] - g * r["n_t32"] // r["n_group"] <= 2 * WAVES32
                        for g in range(r["n_group"]))
             assert 32 * r["n_t32"] + (TAIL_ROWS if r["tail"] else 0) >= r["n_q"] > 32 * r["n_t32"] - 32
         assert 1 <= r["n_split"] <= r["n_units"]
         assert r["n_split"] <= kvc.MAX_SPLITS or -(-r["n_units"] // kvc.MAX_SPLITS) > 512
-        if wl.head_dim <= 64:
+        if k32:
             assert -(-r["n_units"] // r["n_split"]) <= 512   # a split's entries fit the kernel's LDS table
         bounds = [s * r["n_units"] // r["n_split"] for s in range(r["n_split"] + 1)]
         assert all(b1 > b0 for b0, b1 in zip(bounds, bounds[1:])) and bounds[-1] == r["n_units"]
@@ -128,7 +135,7 @@ def check_image(wl, c):
     for i in split_streams:
         r = recs[i]
         for t in range(-(-r["n_q"] // Q_TILE32)):
-            grp = merge_group(wl, r, t)
+            grp = merge_group(r, t, k32)
             for h in range(H):
                 mid = r["item0"] + (h * r["n_split"] + r["n_split"] // 2) * r["n_group"] + grp
                 want[(r["q_tile0"] + t) * H + h] = (min(mid // max(1, ipx), XCD - 1),
@@ -220,4 +227,60 @@ def test_plan_image_check_catches_corruption():
         with pytest.raises(AssertionError):
             check_image(wl, c)
     c.get_plan_image = lambda: good
+    check_image(wl, c)
+
+
+@pytest.mark.parametrize("tile", [16, 32])
+@pytest.mark.parametrize("name", ["base", "tiny"])
+def test_plan_image_forced_query_tile(name, tile):
+    """KVC_OPT_QUERY_TILE fixes the head_dim 64 kernel: the image carries the
+    16x16 bit exactly when 16 is asked for, over a scale step and steady
+    steps."""
+    wl = syn.WORKLOADS[name]
+    c = kvc.PagedKVCache(cfg_of(wl), metadata_only=True)
+    c.set_option(kvc.KVC_OPT_QUERY_TILE, tile)
+    assert c.get_option(kvc.KVC_OPT_QUERY_TILE) == tile
+    for t in range(wl.scale_frames + 3):
+        c.append_frame(0)
+        c.evict_frames()
+        c.plan()
+        check_image(wl, c)
+        img = c.get_plan_image()
+        assert bool(img[5] & 2) == (tile == 16 and wl.head_dim == 64)
+        assert c.get_plan_shape()["group_rows"] == (128 if tile == 16 and wl.head_dim == 64 else 256 + 16 * (img[5] & 1))
+    with pytest.raises(kvc.KvcError):
+        c.set_option(kvc.KVC_OPT_QUERY_TILE, 64)
+
+
+@pytest.mark.parametrize("heads,hist,nf,rows", [(16, 0, 8, 256), (32, 0, 8, 128), (16, 64, 1, 272),
+                                                (8, 8, 1, 128), (2, 120, 1, 256)])
+def test_planner_kernel_choice_head_dim_64(heads, hist, nf, rows):
+    """The planner's choice between the two head_dim 64 kernels on a 256-CU
+    target, at shapes where the faster one was measured: the 32x32 kernel for
+    the one-frame steady state and the 16-head scale step; the 16x16 kernel
+    for the 32-head scale step (the 32x32 kernel's 288 groups need a second
+    round on 32 CUs) and for the short first steps over 8 heads.  The image
+    is decoded and checked at every shape."""
+    wl = dataclasses.replace(syn.WORKLOADS["base"], num_heads=heads)
+    cfg = kvc.make_config(1, heads, 64, wl.tokens_per_frame, wl.num_special_tokens, page_size=wl.page_size,
+                          scale_frames=wl.scale_frames, sliding_window=wl.sliding_window,
+                          max_patch_pages=wl.max_patch_pages, max_special_pages=wl.max_special_pages,
+                          special_row_offset=wl.row_offset, max_frames_per_step=8)
+    c = kvc.PagedKVCache(cfg, metadata_only=True)
+    c.set_option(kvc.KVC_OPT_TARGET_WORKGROUPS, 256)
+    if hist:
+        c.append_frames(0, num_frames=wl.scale_frames)
+        c.evict_frames()
+        c.plan()
+        for _ in range(hist - wl.scale_frames):
+            c.append_frame(0)
+            c.evict_frames()
+            c.plan()
+    if nf > 1:
+        c.append_frames(0, num_frames=nf)
+    else:
+        c.append_frame(0)
+    c.evict_frames()
+    c.plan()
+    assert c.get_plan_shape()["group_rows"] == rows
     check_image(wl, c)
