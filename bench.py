@@ -307,6 +307,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--target-wgs", type=int, default=None)
     ap.add_argument("--max-splits", type=int, default=None)
+    ap.add_argument("--append", default="fused", choices=["fused", "separate"],
+                    help="timed steps: kvc_run_append per block (appends ride on the attention and merge "
+                         "launches) or kvc_append_frame + kvc_run")
     ap.add_argument("--query-tile", type=int, default=0, choices=[0, 16, 32],
                     help="head_dim 64: query rows per MFMA tile (0: the planner's choice)")
     ap.add_argument("--no-profile", action="store_true", help="time without per-launch HIP events")
@@ -382,7 +385,10 @@ def main():
     for s in range(ns):
         qcat[:, :, s * T:(s + 1) * T] = qb[s]
 
-    hs = torch.cuda.current_stream(dev).cuda_stream
+    hs_obj = torch.cuda.current_stream(dev)
+    hs = hs_obj.cuda_stream
+    if args.append == "fused":
+        cache.set_option(kvc.KVC_OPT_FUSED_APPEND, 1)
     frame_of = [0] * ns
     gstep = [0]
 
@@ -395,9 +401,13 @@ def main():
 
     def step(run):
         act = active()
+        fuse = run and args.append == "fused"
         for s in act:
-            kp, vp = kv_ptrs(s, 0)
-            cache.raw_append(0, kp, vp, s, hs)
+            if fuse:
+                cache.append_frames(0, num_frames=1, stream_id=s, stream=hs_obj, defer=True)
+            else:
+                kp, vp = kv_ptrs(s, 0)
+                cache.raw_append(0, kp, vp, s, hs)
         for s in act:
             cache.evict_frames(s)
         cache.raw_plan(hs)          # a plan closes every step, timed or not
@@ -405,11 +415,17 @@ def main():
             if len(act) != ns:
                 raise RuntimeError("timed steps must advance every stream")
             qf = qcat[frame_of[0] % BANK]
-            cache.raw_run(0, qf[0].data_ptr(), ob.data_ptr(), hs)
-        for b in range(1, nb):
-            for s in act:
-                kp, vp = kv_ptrs(s, b)
-                cache.raw_append(b, kp, vp, s, hs)
+        for b in range(nb):
+            if fuse:
+                # the appends of this block ride on its attention and merge launches
+                ptrs = [kv_ptrs(s, b) for s in range(ns)]
+                cache.raw_run_append(b, [x[0] for x in ptrs], [x[1] for x in ptrs], qf[b].data_ptr(),
+                                     ob.data_ptr(), hs)
+                continue
+            if b > 0:
+                for s in act:
+                    kp, vp = kv_ptrs(s, b)
+                    cache.raw_append(b, kp, vp, s, hs)
             if run:
                 cache.raw_run(b, qf[b].data_ptr(), ob.data_ptr(), hs)
         for s in act:

@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 7
+#define KVC_ABI_VERSION 8
 
 typedef struct kvc_ctx kvc_ctx;
 typedef void* kvc_stream_t;   /* hipStream_t */
@@ -140,10 +140,14 @@ enum {
   KVC_OPT_PROFILE = 3,           /* 1: time every attention/merge/append/rope launch with HIP events */
   KVC_OPT_DEFER_EVICTION = 4,    /* 1: hold evicted window pages back until the stream's next frame,
                                     so that kvc_rollback can undo the latest frame (default 0) */
-  KVC_OPT_QUERY_TILE = 5         /* query rows per MFMA tile of the 16-bit attention kernel at head_dim 64:
+  KVC_OPT_QUERY_TILE = 5,        /* query rows per MFMA tile of the 16-bit attention kernel at head_dim 64:
                                     0 = the planner's choice (default), 16 or 32 = that kernel always.
                                     head_dim 32 has only the 32-row kernel, 128 only the 16-row one and
                                     float32 pools their own: there the setting is ignored */
+  KVC_OPT_FUSED_APPEND = 6       /* 1: plans from the next kvc_plan on are built for kvc_run_append (the
+                                    step's own rows form work units of their own); an append with
+                                    k = v = NULL then defers its copy to that block's kvc_run_append
+                                    (default 0; 0 is refused while a deferred append is pending) */
 };
 
 /* Kernels for kvc_profile_read. */
@@ -216,9 +220,13 @@ kvc_status kvc_reset(kvc_ctx* ctx);
  * page whenever the tail page is full.  Blocks >= 1 reuse that page and those
  * slots.  One kernel launch writes the patch rows to slots [0, P) of the page
  * and each special row to its slot; pad slots are never written.
+ * With KVC_OPT_FUSED_APPEND on a device context, k = v = NULL does the
+ * bookkeeping (and at block 0 the allocation) without the copy, which the
+ * block's kvc_run_append then makes.
  * Errors: KVC_ERR_ARG, KVC_ERR_STATE (block >= 1 before block 0 of the step,
- * or a block appended twice in one step), KVC_ERR_POOL_EXHAUSTED (block 0
- * only; nothing changes), KVC_ERR_HIP. */
+ * a block appended twice in one step, or a new step while an append of the
+ * last one is still deferred), KVC_ERR_POOL_EXHAUSTED (block 0 only; nothing
+ * changes), KVC_ERR_HIP. */
 kvc_status kvc_append_frame(kvc_ctx* ctx, int32_t stream, int32_t block, const void* k, const void* v,
                             kvc_stream_t hip_stream);
 
@@ -304,6 +312,31 @@ kvc_status kvc_plan(kvc_ctx* ctx, kvc_stream_t hip_stream);
  * Errors: KVC_ERR_ARG, KVC_ERR_STATE (not planned, or a planned stream has
  * not appended this block), KVC_ERR_HIP. */
 kvc_status kvc_run(kvc_ctx* ctx, int32_t block, const void* q, void* o, kvc_stream_t hip_stream);
+
+/* The append of this step's frames for one block and its attention, fused
+ * ([p5] "How Paged KV Cache Attention Achieves Stable Inference in
+ * Ling-Bot-Map" §Frame Appending Without Dispatch Overhead; [p2] "How
+ * LingBot-Map Uses FlashInfer KV Cache for Streaming 3D Reconstruction"
+ * §Attention Kernel Execution): the result and the pool afterwards are those
+ * of kvc_append_frames of every planned stream followed by kvc_run.  Needs a
+ * plan built with KVC_OPT_FUSED_APPEND; at block 0 the planned streams have
+ * appended with k = v = NULL (deferred), at blocks >= 1 they may have or not.
+ *   k, v: host arrays of num_streams device pointers, indexed by stream id;
+ *         entry s of a planned stream is its [num_frames, T, H, D] rows as
+ *         kvc_append_frames takes them (other entries are not read).  They
+ *         must stay unchanged until the launches on hip_stream complete.
+ *   q, o: as kvc_run.
+ * With the 32-row kernel (head_dim 32, 64), a split plan and at most 4
+ * planned streams, the attention kernel reads the step's own rows straight
+ * from k and v (the plan gives them work units of their own) and the merge
+ * launch also copies them into the pool: two launches instead of the
+ * append's, the attention's and the merge's.  Otherwise the appends are
+ * launched, then the run, with the same result.
+ * Errors: KVC_ERR_ARG, KVC_ERR_STATE (not planned; the plan built without
+ * the option; a planned stream already appended this block with data, or
+ * has not appended block 0), KVC_ERR_HIP. */
+kvc_status kvc_run_append(kvc_ctx* ctx, int32_t block, const void* const* k, const void* const* v, const void* q,
+                          void* o, kvc_stream_t hip_stream);
 
 /* kvc_run with the rotary position embedding applied to the queries first
  * (the same section as kvc_append_frames_rope, the same arithmetic):

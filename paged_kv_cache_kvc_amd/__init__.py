@@ -38,6 +38,7 @@ KVC_OPT_MAX_SPLITS = 2
 KVC_OPT_PROFILE = 3
 KVC_OPT_DEFER_EVICTION = 4
 KVC_OPT_QUERY_TILE = 5
+KVC_OPT_FUSED_APPEND = 6
 KVC_DTYPE_BF16 = 0
 KVC_DTYPE_F16 = 1
 KVC_DTYPE_F32 = 2
@@ -49,7 +50,7 @@ KVC_KERNEL_APPEND = 2
 KVC_KERNEL_ROPE = 3
 
 MAX_SPLITS = 64
-ABI_VERSION = 7   # KVC_ABI_VERSION of include/kvc.h
+ABI_VERSION = 8   # KVC_ABI_VERSION of include/kvc.h
 
 
 class KvcError(RuntimeError):
@@ -94,6 +95,7 @@ SIGNATURES = {
     "kvc_plan": (_I32, [_P, _P]),
     "kvc_run": (_I32, [_P, _I32, _P, _P, _P]),
     "kvc_run_no_alloc": (_I32, [_P, _I32, _P, _P, _P]),
+    "kvc_run_append": (_I32, [_P, _I32, ctypes.POINTER(_P), ctypes.POINTER(_P), _P, _P, _P]),
     "kvc_run_rope": (_I32, [_P, _I32, _P, _P, _P, _P, _P]),
     "kvc_get_plan": (_I32, [_P, _PI32, _PI32, _PI32, _PI32, _PI32, _PI32, _PI32, _I32, _I32, _PI32, _PI32]),
     "kvc_get_plan_shape": (_I32, [_P, _PI32, _PI32]),
@@ -263,11 +265,22 @@ class PagedKVCache:
             self._planned = False
 
     def append_frames(self, block_idx: int, k=None, v=None, num_frames: Optional[int] = None, stream_id: int = 0,
-                      stream=None, rope=None):
+                      stream=None, rope=None, defer: bool = False):
         """Write several frames' K and V ([F, T, H, D] or [F*T, H, D] bf16) of
         one block in one step (the scale phase); at block 0 this also
         allocates the F frames, all or none.  rope = (cos, sin), float32
-        [F*T, D/2] each, turns K by those angles on the way into the pool."""
+        [F*T, D/2] each, turns K by those angles on the way into the pool.
+        defer = True (KVC_OPT_FUSED_APPEND) does the bookkeeping only: the
+        block's append_run makes the copy."""
+        if defer:
+            if num_frames is None or k is not None or v is not None or rope is not None:
+                raise KvcError(KVC_ERR_ARG, "a deferred append takes num_frames and no tensors")
+            rc = self.lib.kvc_append_frames(self._ctx, stream_id, block_idx, None, None, num_frames,
+                                            self._stream(stream))
+            self._check(rc, "append_frames")
+            if block_idx == 0:
+                self._planned = False
+            return
         if self.metadata_only:
             if num_frames is None:
                 raise KvcError(KVC_ERR_ARG, "num_frames is required without tensors")
@@ -338,6 +351,47 @@ class PagedKVCache:
         rc = fn(self._ctx, block_idx, q.data_ptr(), out.data_ptr(), self._stream(stream))
         self._check(rc, "compute_attention")
         return out
+
+    def append_run(self, block_idx: int, ks, vs, q, out=None, stream=None):
+        """kvc_run_append: this step's appends of one block and its attention.
+        ks, vs: {stream id: [F*T, H, D] (or [F, T, H, D]) rows} of the planned
+        streams; q, out as compute_attention.  Plans first when called for
+        block 0 of an unplanned step."""
+        if block_idx == 0 and not self._planned:
+            self.plan(stream)
+        rows = q.shape[0]
+        self._check_tensor(q, rows, "q")
+        if out is None:
+            out = self.torch.empty_like(q)
+        else:
+            self._check_tensor(out, rows, "out")
+        n = self.cfg.num_streams
+        kp = (_P * n)()
+        vp = (_P * n)()
+        T = self.cfg.tokens_per_frame
+        for s, kt in ks.items():
+            vt = vs[s]
+            k2 = kt.reshape(-1, *kt.shape[-2:])
+            v2 = vt.reshape(-1, *vt.shape[-2:])
+            if k2.shape[0] % T:
+                raise KvcError(KVC_ERR_ARG, f"stream {s}: rows not a whole number of frames")
+            self._check_tensor(k2, k2.shape[0], "k")
+            self._check_tensor(v2, v2.shape[0], "v")
+            kp[s] = k2.data_ptr()
+            vp[s] = v2.data_ptr()
+        rc = self.lib.kvc_run_append(self._ctx, block_idx, kp, vp, q.data_ptr(), out.data_ptr(), self._stream(stream))
+        self._check(rc, "append_run")
+        return out
+
+    def raw_run_append(self, block_idx: int, k_ptrs, v_ptrs, q_ptr: int, o_ptr: int, hip_stream: int):
+        """kvc_run_append on raw addresses: k_ptrs / v_ptrs per stream id
+        (num_streams entries, 0 where a stream is not planned)."""
+        n = self.cfg.num_streams
+        kp = (_P * n)(*k_ptrs)
+        vp = (_P * n)(*v_ptrs)
+        rc = self.lib.kvc_run_append(self._ctx, block_idx, kp, vp, q_ptr, o_ptr, hip_stream)
+        if rc:
+            self._check(rc, "append_run")
 
     def reset(self):
         self._check(self.lib.kvc_reset(self._ctx), "reset")

@@ -318,6 +318,16 @@ kvc_status kvc_reset(kvc_ctx* c) {
 static kvc_status append_frames_impl(kvc_ctx* c, int32_t stream, int32_t block, const void* k, const void* v,
                                      int32_t num_frames, const float* rope_cos, const float* rope_sin, bool rope,
                                      kvc_stream_t hs);
+static kvc_status launch_appends(kvc_ctx* c, int32_t stream, int32_t block, const void* k, const void* v,
+                                 int32_t num_frames, const float* rope_cos, const float* rope_sin, bool rope,
+                                 kvc_stream_t hs);
+
+// Some block's append of this step waits for its kvc_run_append.
+static bool deferred_pending(const kvc_ctx* c) {
+  for (uint8_t d : c->block_done)
+    if (d == 2) return true;
+  return false;
+}
 
 kvc_status kvc_append_frames(kvc_ctx* c, int32_t stream, int32_t block, const void* k, const void* v,
                              int32_t num_frames, kvc_stream_t hs) {
@@ -350,9 +360,15 @@ static kvc_status append_frames_impl(kvc_ctx* c, int32_t stream, int32_t block, 
   if (block < 0 || block >= cf.num_blocks) return fail(c, KVC_ERR_ARG, "block out of range");
   if (num_frames < 1 || num_frames > cf.max_frames_per_step)
     return fail(c, KVC_ERR_ARG, "num_frames must be in [1, max_frames_per_step]");
+  // k = v = NULL on a device context: the copy is deferred to this block's
+  // kvc_run_append (KVC_OPT_FUSED_APPEND only)
+  const bool deferred = !c->metadata_only && !k && !v && !rope;
   if (c->metadata_only) {
     if (k || v || rope_cos || rope_sin)
       return fail(c, KVC_ERR_ARG, "metadata-only context takes k = v = NULL and no rotary tables");
+  } else if (deferred) {
+    if (!c->policy.fused)
+      return fail(c, KVC_ERR_ARG, "k = v = NULL defers the copy, which needs KVC_OPT_FUSED_APPEND");
   } else if (!k || !v || ((uintptr_t)k & 15) || ((uintptr_t)v & 15)) {
     return fail(c, KVC_ERR_ARG, "k and v must be 16-byte aligned device pointers");
   } else if (rope && (!table_ok(rope_cos) || !table_ok(rope_sin))) {
@@ -363,6 +379,8 @@ static kvc_status append_frames_impl(kvc_ctx* c, int32_t stream, int32_t block, 
   if (block == 0) {
     // kvc_plan ends a step; the first block-0 append after it starts the next.
     const bool new_step = c->planned;
+    if (new_step && deferred_pending(c))
+      return fail(c, KVC_ERR_STATE, "a deferred append of the last step was not completed by kvc_run_append");
     if (!new_step && c->advanced[stream])
       return fail(c, KVC_ERR_STATE, "stream already appended block 0 this step (kvc_plan ends a step)");
     std::string why;
@@ -393,9 +411,17 @@ static kvc_status append_frames_impl(kvc_ctx* c, int32_t stream, int32_t block, 
     if (num_frames != c->nframes[stream])
       return fail(c, KVC_ERR_ARG, "num_frames differs from this step's block-0 append");
   }
-  c->block_done[bd] = 1;
-  if (c->metadata_only) return KVC_OK;
+  c->block_done[bd] = deferred ? 2 : 1;
+  if (c->metadata_only || deferred) return KVC_OK;
+  return launch_appends(c, stream, block, k, v, num_frames, rope_cos, rope_sin, rope, hs);
+}
 
+// The append kernels of one stream's frames of this step into a block's pool.
+static kvc_status launch_appends(kvc_ctx* c, int32_t stream, int32_t block, const void* k, const void* v,
+                                 int32_t num_frames, const float* rope_cos, const float* rope_sin, bool rope,
+                                 kvc_stream_t hs) {
+  const kvc::Config& cf = c->cfg;
+  const kvc::FrameSlots* fs = &c->slots[(size_t)stream * cf.max_frames_per_step];
   const size_t frame_bytes = (size_t)cf.tokens_per_frame * cf.num_heads * cf.head_dim * cf.elem_bytes();
   const size_t frame_table = (size_t)cf.tokens_per_frame * (cf.head_dim / 2);
   for (int32_t f = 0; f < num_frames; ++f) {
@@ -437,6 +463,8 @@ kvc_status kvc_rollback(kvc_ctx* c, int32_t stream) {
   bool mid_step = false;
   for (uint8_t a : c->advanced) mid_step = mid_step || a;
   if (mid_step && !c->planned) return fail(c, KVC_ERR_STATE, "rollback inside a step (call it after kvc_plan)");
+  if (deferred_pending(c))
+    return fail(c, KVC_ERR_STATE, "rollback with a deferred append pending (complete it with kvc_run_append)");
   std::string why;
   const int rc = c->alloc.rollback(stream, &why);
   if (rc != kvc::OK) return fail(c, (kvc_status)rc, why);
@@ -471,8 +499,10 @@ static kvc_status plan_impl(kvc_ctx* c, kvc_stream_t hs) {
       frames.push_back(c->nframes[s]);
     }
   if (streams.empty()) return fail(c, KVC_ERR_STATE, "no stream appended block 0 this step");
+  std::vector<const kvc::FrameSlots*> fslots;
+  for (int32_t s : streams) fslots.push_back(&c->slots[(size_t)s * c->cfg.max_frames_per_step]);
   kvc::HostPlan next;
-  kvc::build_plan(c->alloc, streams, frames, c->policy, &next);
+  kvc::build_plan(c->alloc, streams, frames, fslots, c->policy, &next);
   // The device plan buffer (and its staging half) holds plan_image_ints ints,
   // enough while every planned stream sees at most scale_frames +
   // sliding_window patch pages.  A stream whose window was not evicted can
@@ -523,15 +553,22 @@ static kvc_status check_run(kvc_ctx* c, int32_t block, const void* q, const void
   if (q == o) return fail(c, KVC_ERR_ARG, "o must not alias q");
   if (!c->planned) return fail(c, KVC_ERR_STATE, "run before plan in this step");
   if (c->plan_stale) return fail(c, KVC_ERR_STATE, "a rollback since the plan: append and plan the next step first");
-  for (int32_t s : c->plan.planned)
-    if (!c->block_done[(size_t)s * cf.num_blocks + block])
-      return fail(c, KVC_ERR_STATE, "a planned stream has not appended this block");
-
+  for (int32_t s : c->plan.planned) {
+    const uint8_t d = c->block_done[(size_t)s * cf.num_blocks + block];
+    if (d == 2) return fail(c, KVC_ERR_STATE, "a planned stream deferred this block's append: use kvc_run_append");
+    if (d != 1) return fail(c, KVC_ERR_STATE, "a planned stream has not appended this block");
+  }
   return KVC_OK;
 }
 
+// Inputs of a fused run: per planned stream (plan order) its k and v rows.
+struct FusedInputs {
+  const void* k[KVC_ARG_STREAMS];
+  const void* v[KVC_ARG_STREAMS];
+};
+
 static kvc_status launch_run(kvc_ctx* c, int32_t block, const void* q, void* o, kvc_stream_t hs, float* lse,
-                             void* po) {
+                             void* po, const FusedInputs* fin = nullptr) {
   const kvc::Config& cf = c->cfg;
   const int32_t* dplan = reinterpret_cast<const int32_t*>(c->workspace + (c->plan_buf ? c->lay.plan1 : c->lay.plan0));
 
@@ -556,6 +593,13 @@ static kvc_status launch_run(kvc_ctx* c, int32_t block, const void* q, void* o, 
   a.num_streams = (int32_t)c->plan.planned.size();
   if (a.num_streams <= KVC_ARG_STREAMS)
     std::memcpy(a.recs, c->plan.image.data() + KVC_PLAN_HEADER_INTS, (size_t)a.num_streams * sizeof(kvc_dev_stream));
+  if (fin) {
+    a.fused = 1;
+    for (int i = 0; i < a.num_streams; ++i) {
+      a.kin[i] = fin->k[i];
+      a.vin[i] = fin->v[i];
+    }
+  }
   const int32_t grid = 8 * a.items_per_xcd;
   int e = timed(c, KVC_KERNEL_ATTENTION, hs, [&] {
     if (cf.fp32()) return kvc::launch_attention_f32(a, hs);
@@ -565,6 +609,7 @@ static kvc_status launch_run(kvc_ctx* c, int32_t block, const void* q, void* o, 
   if (e) return hip_fail(c, e, "attention launch");
   if (c->plan.any_split) {
     kvc::MergeParams m;
+    std::memset(&m, 0, sizeof(m));
     m.plan = dplan;
     m.part_o = po;
     m.part_lse = lse;
@@ -577,6 +622,23 @@ static kvc_status launch_run(kvc_ctx* c, int32_t block, const void* q, void* o, 
     m.merge_table = c->plan.merge_table;
     m.merge_slots = c->plan.merge_slots;
     m.dtype = cf.dtype;
+    if (fin) {
+      // the copy of the step's rows into the pool rides on the merge launch
+      m.copy_rows = c->plan.num_rows;
+      m.row_bytes = cf.num_heads * cf.head_dim * cf.elem_bytes();
+      const int64_t copies = (int64_t)m.copy_rows * 2 * (m.row_bytes / 16);
+      const int64_t per_wg = (int64_t)KVC_COPY_PER * 64 * (cf.head_dim / 32) * 4;
+      m.copy_wgs = (int32_t)((copies + per_wg - 1) / per_wg);
+      m.copy_table = c->plan.copy_table;
+      m.page_size = cf.page_size;
+      m.num_streams = a.num_streams;
+      for (int i = 0; i <= a.num_streams; ++i) m.row0[i] = c->plan.qo_indptr[i];
+      m.pool = c->pools[block];
+      for (int i = 0; i < a.num_streams; ++i) {
+        m.kin[i] = fin->k[i];
+        m.vin[i] = fin->v[i];
+      }
+    }
     e = timed(c, KVC_KERNEL_MERGE, hs, [&] { return kvc::launch_merge(m, hs); });
     if (e) return hip_fail(c, e, "merge launch");
   }
@@ -589,6 +651,49 @@ kvc_status kvc_run(kvc_ctx* c, int32_t block, const void* q, void* o, kvc_stream
   if (rc != KVC_OK) return rc;
   return launch_run(c, block, q, o, hs, reinterpret_cast<float*>(c->workspace + c->lay.lse),
                     c->workspace + c->lay.part_o);
+}
+
+kvc_status kvc_run_append(kvc_ctx* c, int32_t block, const void* const* k, const void* const* v, const void* q,
+                          void* o, kvc_stream_t hs) {
+  if (!c) return KVC_ERR_ARG;
+  const kvc::Config& cf = c->cfg;
+  if (c->metadata_only) return fail(c, KVC_ERR_STATE, "metadata-only context cannot run");
+  if (block < 0 || block >= cf.num_blocks) return fail(c, KVC_ERR_ARG, "block out of range");
+  if (!k || !v) return fail(c, KVC_ERR_ARG, "k and v must be arrays of num_streams device pointers");
+  if (!q || !o || ((uintptr_t)q & 15) || ((uintptr_t)o & 15)) return fail(c, KVC_ERR_ARG, "q and o must be 16-byte aligned");
+  if (q == o) return fail(c, KVC_ERR_ARG, "o must not alias q");
+  if (!c->planned) return fail(c, KVC_ERR_STATE, "run before plan in this step");
+  if (c->plan_stale) return fail(c, KVC_ERR_STATE, "a rollback since the plan: append and plan the next step first");
+  if (!c->plan.fused) return fail(c, KVC_ERR_STATE, "the plan was built without KVC_OPT_FUSED_APPEND");
+  for (int32_t s : c->plan.planned) {
+    const uint8_t d = c->block_done[(size_t)s * cf.num_blocks + block];
+    if (d == 1) return fail(c, KVC_ERR_STATE, "a planned stream already appended this block (use kvc_run)");
+    if (d == 0 && block == 0) return fail(c, KVC_ERR_STATE, "block 0 is appended (or deferred) before the plan");
+    if (!k[s] || !v[s] || ((uintptr_t)k[s] & 15) || ((uintptr_t)v[s] & 15))
+      return fail(c, KVC_ERR_ARG, "k[s] and v[s] of a planned stream must be 16-byte aligned device pointers");
+  }
+  for (int32_t s : c->plan.planned) c->block_done[(size_t)s * cf.num_blocks + block] = 1;
+  float* lse = reinterpret_cast<float*>(c->workspace + c->lay.lse);
+  char* po = c->workspace + c->lay.part_o;
+  const int n = (int)c->plan.planned.size();
+  // One attention launch reading the own rows from k / v and one merge
+  // launch that also copies them into the pool: 32x32 kernel, split plans,
+  // at most KVC_ARG_STREAMS streams.  Otherwise the appends, then the run.
+  if (!cf.fp32() && cf.tiles32() && !c->plan.tiles16 && c->plan.any_split && n <= KVC_ARG_STREAMS) {
+    FusedInputs fin;
+    std::memset(&fin, 0, sizeof(fin));
+    for (int i = 0; i < n; ++i) {
+      fin.k[i] = k[c->plan.planned[i]];
+      fin.v[i] = v[c->plan.planned[i]];
+    }
+    return launch_run(c, block, q, o, hs, lse, po, &fin);
+  }
+  for (int i = 0; i < n; ++i) {
+    const int32_t s = c->plan.planned[i];
+    const kvc_status rc = launch_appends(c, s, block, k[s], v[s], c->nframes[s], nullptr, nullptr, false, hs);
+    if (rc != KVC_OK) return rc;
+  }
+  return launch_run(c, block, q, o, hs, lse, po);
 }
 
 kvc_status kvc_run_rope(kvc_ctx* c, int32_t block, const void* q, const float* rope_cos, const float* rope_sin,
@@ -757,6 +862,11 @@ kvc_status kvc_set_option(kvc_ctx* c, int32_t option, int64_t value) {
       if (value != 0 && value != 16 && value != 32) return fail(c, KVC_ERR_ARG, "query tile is 0, 16 or 32");
       c->policy.query_tile = (int32_t)value;
       return KVC_OK;
+    case KVC_OPT_FUSED_APPEND:
+      if (value != 0 && value != 1) return fail(c, KVC_ERR_ARG, "fused append is 0 or 1");
+      if (!value && deferred_pending(c)) return fail(c, KVC_ERR_STATE, "a deferred append is pending");
+      c->policy.fused = value != 0;
+      return KVC_OK;
     default:
       return fail(c, KVC_ERR_ARG, "unknown option");
   }
@@ -770,6 +880,7 @@ kvc_status kvc_get_option(const kvc_ctx* c, int32_t option, int64_t* value) {
     case KVC_OPT_PROFILE: *value = c->profile ? 1 : 0; return KVC_OK;
     case KVC_OPT_DEFER_EVICTION: *value = c->alloc.defer_eviction() ? 1 : 0; return KVC_OK;
     case KVC_OPT_QUERY_TILE: *value = c->policy.query_tile; return KVC_OK;
+    case KVC_OPT_FUSED_APPEND: *value = c->policy.fused ? 1 : 0; return KVC_OK;
     default: return KVC_ERR_ARG;
   }
 }

@@ -348,14 +348,17 @@ __global__ __launch_bounds__(64 * KVC_ATTN32_WAVES, 1) void attn32_kernel(AttnPa
   // other memory operation; all of them copied to LDS by direct loads for the
   // stage loop, which then issues no global memory operation besides its
   // direct-to-LDS loads (whose completion it counts with vmcnt).
-  int2 e_first[P0];
+  int4 e_first[P0];
 #pragma unroll
   for (int i = 0; i < P0; ++i)
-    e_first[i] = i < nstage ? int2{units[KVC_UNIT_INTS * i], units[KVC_UNIT_INTS * i + 1]} : int2{0, KVC_KV_TILE};
-  auto stage_entry = [&](int i) {
-    const int4 e = elds[i];
-    return int2{__builtin_amdgcn_readfirstlane(e.x), __builtin_amdgcn_readfirstlane(e.y)};
+    e_first[i] = i < nstage ? int4{units[KVC_UNIT_INTS * i], units[KVC_UNIT_INTS * i + 1],
+                                   units[KVC_UNIT_INTS * i + 2], 0}
+                            : int4{0, KVC_KV_TILE, 0, 0};
+  auto uniform_entry = [](const int4& e) {
+    return int4{__builtin_amdgcn_readfirstlane(e.x), __builtin_amdgcn_readfirstlane(e.y),
+                __builtin_amdgcn_readfirstlane(e.z), 0};
   };
+  auto stage_entry = [&](int i) { return uniform_entry(elds[i]); };
 
   // ---- direct global -> LDS loads of one stage (K rows, then V rows) ----
   // Load instruction j of the wave fills 1 KiB at LDS byte 1024 * (wave *
@@ -363,6 +366,24 @@ __global__ __launch_bounds__(64 * KVC_ATTN32_WAVES, 1) void attn32_kernel(AttnPa
   // the logical chunk the swizzle places there.
   const uint8_t* pool = static_cast<const uint8_t*>(p.pool);
   const uint64_t v_half = (uint64_t)p.page_size * slot_bytes;
+  // Fused append: units of the step's own rows (entry z = 1 + input row)
+  // are read from the caller's k and v of the item's stream, whose rows have
+  // the pool's row layout; V is vin - kin bytes past K there.
+  const uint8_t* kin = nullptr;
+  uint64_t vin_delta = 0;
+  const bool fused = p.fused != 0;
+  if (fused) {
+    const void* kb = p.kin[0];
+    const void* vb = p.vin[0];
+#pragma unroll
+    for (int i = 1; i < KVC_ARG_STREAMS; ++i)
+      if (i < p.num_streams && item >= p.recs[i].item0) {
+        kb = p.kin[i];
+        vb = p.vin[i];
+      }
+    kin = static_cast<const uint8_t*>(kb);
+    vin_delta = (uint64_t)(uintptr_t)vb - (uint64_t)(uintptr_t)kb;
+  }
   // Load instruction i of a stage (K: i < LOADS / 2, V: the rest) covers
   // rows RPL (i % (LOADS / 2)) .. + RPL - 1 of its half; lane l writes chunk
   // l % CPR of row RPL (i % ...) + l / CPR.  The swizzle depends on row bits
@@ -378,9 +399,11 @@ __global__ __launch_bounds__(64 * KVC_ATTN32_WAVES, 1) void attn32_kernel(AttnPa
   const uint32_t lofs1 =
       RPL == 8 ? (uint32_t)lrow0 * slot_bytes + (uint32_t)(((lane % CPR) ^ swz32<D>(lrow0 + 8)) << 4) : lofs0;
   const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(lds_addr(ring));
-  // per load j of this wave: offset of its first row from the unit's first K
-  // row (K or V half) and its LDS offset in a stage (uniform)
-  uint64_t jofs[LPW];
+  // per load j of this wave: its first row in the unit, its half (all the
+  // wave's loads are K loads or all V loads) and its LDS offset in a stage
+  // (uniform)
+  static_assert((S::LOADS / 2) % LPW == 0, "a wave's loads stay in one half");
+  const bool wave_v = wv * LPW >= S::LOADS / 2;
   uint32_t jlds[LPW];
   int jrow[LPW];
 #pragma unroll
@@ -389,7 +412,6 @@ __global__ __launch_bounds__(64 * KVC_ATTN32_WAVES, 1) void attn32_kernel(AttnPa
     const int kv = inst >= S::LOADS / 2 ? 1 : 0;
     const int blk = inst - kv * (S::LOADS / 2);
     jrow[j] = RPL * blk;
-    jofs[j] = (kv ? v_half : 0) + (uint64_t)(RPL * blk) * slot_bytes;
     jlds[j] = (uint32_t)(kv * S::HALF + blk * 1024);
   }
   // load j of a stage whose unit starts at ubase, into the ring slot at LDS
@@ -397,14 +419,17 @@ __global__ __launch_bounds__(64 * KVC_ATTN32_WAVES, 1) void attn32_kernel(AttnPa
   // valid row.  The offset is an unsigned 32-bit addend of the scalar base
   // (the unit's first row of the K or V half), so rows are measured from the
   // unit's first row, never below it.
-  auto issue_e = [&](int sidx, int2 e) {
-    const uint8_t* ubase = pool + (uint64_t)(uint32_t)e.x * slot_bytes + head_off;
+  auto issue_e = [&](int sidx, int4 e) {
+    const bool in = fused && e.z != 0;
+    const uint8_t* kbase = in ? kin + (uint64_t)(uint32_t)(e.z - 1) * slot_bytes
+                              : pool + (uint64_t)(uint32_t)e.x * slot_bytes;
+    const uint8_t* ubase = kbase + head_off + (wave_v ? (in ? vin_delta : v_half) : 0);
     const uint32_t slot = ring_lds + (uint32_t)(sidx % NST) * S::STAGE;
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
       const uint32_t o =
           ((j & 1) ? lofs1 : lofs0) + (uint32_t)(min(jrow[j] + lrow0, e.y - 1) - lrow0) * slot_bytes;
-      load_lds16(ubase + (jofs[j] - (uint64_t)jrow[j] * slot_bytes), o, slot + jlds[j]);
+      load_lds16(ubase, o, slot + jlds[j]);
     }
   };
 
@@ -618,7 +643,7 @@ __global__ __launch_bounds__(64 * KVC_ATTN32_WAVES, 1) void attn32_kernel(AttnPa
     wait_ahead<LPW, NST - 2>(min(nstage - 1 - s, NST - 2));
     ring_barrier();
     if constexpr (do_issue)
-      issue_e(s + NST - 1, int2{__builtin_amdgcn_readfirstlane(e_next.x), __builtin_amdgcn_readfirstlane(e_next.y)});
+      issue_e(s + NST - 1, uniform_entry(e_next));
     const int valid = __builtin_amdgcn_readfirstlane(e_cur.y);
     e_cur = elds[min(s + 1, KVC_MAX_SPLIT_STAGES - 1)];
     e_next = elds[min(s + NST, KVC_MAX_SPLIT_STAGES - 1)];

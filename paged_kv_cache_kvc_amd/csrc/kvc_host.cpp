@@ -209,13 +209,71 @@ static size_t max_units(const Config& c) {
 }
 
 size_t plan_image_ints(const Config& c) {
+  // fused plans: at most two more units per own frame and one per stream
+  // (the cuts at the special row offset and at each frame's specials), and
+  // one pool row per input row
+  const size_t own = (size_t)c.num_streams * c.max_frames_per_step;
   return KVC_PLAN_HEADER_INTS + (size_t)KVC_STREAM_REC_INTS * c.num_streams + (size_t)c.max_num_pages() + 4 +
-         (size_t)KVC_UNIT_INTS * max_units(c) + 4 +
-         (size_t)KVC_MERGE_INTS * KVC_NUM_XCD * c.tiles_capacity() * c.num_heads;
+         (size_t)KVC_UNIT_INTS * (max_units(c) + 2 * own + c.num_streams) + 4 +
+         (size_t)KVC_MERGE_INTS * KVC_NUM_XCD * c.tiles_capacity() * c.num_heads + 4 + own * c.tokens_per_frame;
 }
 
+uint32_t input_row_slot(const Config& c, const FrameSlots& fs, int32_t t) {
+  const int32_t off = c.special_row_offset, ns = c.num_special_tokens;
+  if (t >= off && t < off + ns) {
+    const int32_t pos = fs.sp_slot0 + (t - off);
+    const int32_t idx = pos / c.page_size;
+    return (uint32_t)fs.sp_pages[idx] * 2u * (uint32_t)c.page_size + (uint32_t)(pos - idx * c.page_size);
+  }
+  return (uint32_t)fs.patch_page * 2u * (uint32_t)c.page_size + (uint32_t)(t < off ? t : t - ns);
+}
+
+namespace {
+
+struct Unit {
+  uint32_t slot;   // pool row of the unit's first K row
+  int32_t valid;   // rows
+  int32_t src;     // fused plans: 1 + the input row of its first row (rows consecutive), 0: pool only
+};
+
+// Work units of one stream: 64-slot chunks of each visible page's valid
+// slots, in table order.  With `own` (fused plans: the pool row -> input
+// row map of the step's own frames, over the pages they touch) a chunk is
+// further cut into runs of rows that are either all older (src 0) or all
+// own with consecutive input rows.
+void stream_units(const Config& c, const int32_t* idx, int32_t n_pages, int32_t n_patch, int32_t last_len,
+                  const std::vector<std::pair<int32_t, std::vector<int32_t>>>* own, std::vector<Unit>* out) {
+  const int32_t P = c.patch_tokens();
+  out->clear();
+  for (int32_t pi = 0; pi < n_pages; ++pi) {
+    const int32_t len = pi == n_pages - 1 ? last_len : (pi < n_patch ? P : c.page_size);
+    const uint32_t base = (uint32_t)idx[pi] * 2u * (uint32_t)c.page_size;
+    const std::vector<int32_t>* rows = nullptr;
+    if (own)
+      for (const auto& pr : *own)
+        if (pr.first == idx[pi]) rows = &pr.second;
+    for (int32_t a = 0; a < len; a += KVC_KV_TILE) {
+      const int32_t b = std::min<int32_t>(len, a + KVC_KV_TILE);
+      if (!rows) {
+        out->push_back({base + (uint32_t)a, b - a, 0});
+        continue;
+      }
+      int32_t s0 = a;
+      while (s0 < b) {
+        const int32_t r0 = (*rows)[s0];
+        int32_t s1 = s0 + 1;
+        while (s1 < b && (r0 < 0 ? (*rows)[s1] < 0 : (*rows)[s1] == r0 + (s1 - s0))) ++s1;
+        out->push_back({base + (uint32_t)s0, s1 - s0, r0 < 0 ? 0 : r0 + 1});
+        s0 = s1;
+      }
+    }
+  }
+}
+
+}  // namespace
+
 void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const std::vector<int32_t>& frames,
-                const PlanPolicy& pol, HostPlan* out) {
+                const std::vector<const FrameSlots*>& fslots, const PlanPolicy& pol, HostPlan* out) {
   const Config& c = a.config();
   HostPlan& p = *out;
   const int n = (int)streams.size();
@@ -259,13 +317,30 @@ void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const s
   const int32_t max_splits = c.fp32() ? 1 : std::max(1, std::min<int32_t>(pol.max_splits, KVC_MAX_SPLITS));
   const int32_t upp = (int32_t)ceil_div(std::max(1, P), KVC_KV_TILE);
   const int32_t ups = (int32_t)ceil_div(c.page_size, KVC_KV_TILE);
+  // the streams' unit lists (fused plans: cut at the own frames' row runs)
+  p.fused = pol.fused;
+  std::vector<std::vector<Unit>> ulist(n);
   std::vector<int64_t> units(n), cap(n);
   for (int i = 0; i < n; ++i) {
-    const int32_t n_patch = p.n_patch_pages[i];
-    const int32_t n_special = p.kv_indptr[i + 1] - p.kv_indptr[i] - n_patch;
-    units[i] = std::max<int64_t>(
-        1, (int64_t)n_patch * upp +
-               (n_special > 0 ? (int64_t)(n_special - 1) * ups + ceil_div(p.last_page_len[i], KVC_KV_TILE) : 0));
+    std::vector<std::pair<int32_t, std::vector<int32_t>>> own;
+    if (p.fused) {
+      // input row of every pool slot the step's own frames write, per page
+      for (int32_t f = 0; f < frames[i]; ++f)
+        for (int32_t t = 0; t < c.tokens_per_frame; ++t) {
+          const uint32_t slot = input_row_slot(c, fslots[i][f], t);
+          const int32_t page = (int32_t)(slot / (2u * (uint32_t)c.page_size));
+          const int32_t j = (int32_t)(slot - (uint32_t)page * 2u * (uint32_t)c.page_size);
+          auto it = std::find_if(own.begin(), own.end(), [&](const auto& pr) { return pr.first == page; });
+          if (it == own.end()) {
+            own.emplace_back(page, std::vector<int32_t>(c.page_size, -1));
+            it = own.end() - 1;
+          }
+          it->second[j] = f * c.tokens_per_frame + t;
+        }
+    }
+    stream_units(c, &p.kv_indices[p.kv_indptr[i]], p.kv_indptr[i + 1] - p.kv_indptr[i], p.n_patch_pages[i],
+                 p.last_page_len[i], p.fused ? &own : nullptr, &ulist[i]);
+    units[i] = (int64_t)ulist[i].size();
     cap[i] = std::min<int64_t>(max_splits, units[i]);
   }
   // The 32x32 kernel stages a split's unit entries in LDS: at most
@@ -453,11 +528,14 @@ void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const s
   std::copy(p.kv_indices.begin(), p.kv_indices.end(),
             p.image.begin() + KVC_PLAN_HEADER_INTS + (size_t)KVC_STREAM_REC_INTS * n);
 
-  // Unit tables: unit u of a stream is the 64-slot chunk cu of visible page
-  // pi.  Patch pages hold P valid slots, special pages page_size, the last
-  // page last_page_len ([p1] "How FlashInfer KV Cache Attention Accelerates
-  // Streaming 3D Reconstruction Over SDPA" §Efficient Attention Masking and
-  // Padding: lengths, not masks, delimit the valid tokens).
+  // Unit tables: the 64-slot chunks of each visible page's valid slots, in
+  // table order.  Patch pages hold P valid slots, special pages page_size,
+  // the last page last_page_len ([p1] "How FlashInfer KV Cache Attention
+  // Accelerates Streaming 3D Reconstruction Over SDPA" §Efficient Attention
+  // Masking and Padding: lengths, not masks, delimit the valid tokens).  An
+  // entry holds the slot index of the unit's first K row in the block's pool
+  // [pages][2][page_size] (below 2^32: validate keeps pages * page_size below
+  // 2^31), its valid rows and, in fused plans, 1 + its first input row.
   size_t at = (p.image.size() + 3) & ~(size_t)3;
   for (int i = 0; i < n; ++i) {
     kvc_dev_stream* rec = reinterpret_cast<kvc_dev_stream*>(&p.image[KVC_PLAN_HEADER_INTS + (size_t)KVC_STREAM_REC_INTS * i]);
@@ -466,26 +544,12 @@ void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const s
     r.unit0 = (int32_t)at;
     std::memcpy(rec, &r, sizeof(r));
     p.image.resize(at + (size_t)KVC_UNIT_INTS * r.n_units, 0);
-    const int32_t* idx = &p.kv_indices[p.kv_indptr[i]];
-    const int32_t patch_units = r.n_patch * r.upp;
     for (int32_t u = 0; u < r.n_units; ++u) {
-      int32_t pi, cu;
-      if (u < patch_units) {
-        pi = u / r.upp;
-        cu = u - pi * r.upp;
-      } else {
-        const int32_t pj = (u - patch_units) / r.ups;
-        pi = r.n_patch + pj;
-        cu = u - patch_units - pj * r.ups;
-      }
-      const int32_t len = pi == r.n_pages - 1 ? r.last_len : (pi < r.n_patch ? P : c.page_size);
-      // slot index of the unit's first K row in the block's pool [pages][2][page_size]
-      // (below 2^32: validate keeps pages * page_size below 2^31)
-      const uint32_t slot = (uint32_t)idx[pi] * 2u * (uint32_t)c.page_size + (uint32_t)KVC_KV_TILE * (uint32_t)cu;
+      const Unit& un = ulist[i][u];
       int32_t* e = &p.image[at + (size_t)KVC_UNIT_INTS * u];
-      e[0] = (int32_t)slot;
-      e[1] = std::min<int32_t>(KVC_KV_TILE, len - KVC_KV_TILE * cu);
-      e[2] = 0;
+      e[0] = (int32_t)un.slot;
+      e[1] = un.valid;
+      e[2] = un.src;
       e[3] = 0;
     }
     at += (size_t)KVC_UNIT_INTS * r.n_units;
@@ -541,6 +605,20 @@ void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const s
       else
         e[0] = -1;
     }
+
+  // Fused plans: the pool row of each input row (rows in query order: the
+  // streams' own frames concatenated), for the copy into the pool.
+  p.copy_table = 0;
+  if (p.fused) {
+    at = (p.image.size() + 3) & ~(size_t)3;
+    p.copy_table = (int32_t)at;
+    p.image.resize(at + (size_t)p.num_rows, 0);
+    for (int i = 0; i < n; ++i)
+      for (int32_t f = 0; f < frames[i]; ++f)
+        for (int32_t t = 0; t < c.tokens_per_frame; ++t)
+          p.image[at + (size_t)p.qo_indptr[i] + (size_t)f * c.tokens_per_frame + t] =
+              (int32_t)input_row_slot(c, fslots[i][f], t);
+  }
 }
 
 }  // namespace kvc

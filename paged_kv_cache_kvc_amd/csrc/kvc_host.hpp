@@ -117,6 +117,11 @@ struct PlanPolicy {
   // head_dim 64, 16-bit pools: 0 = the kernel whose launch the cost model
   // finds shorter, 16 / 32 = the 16x16 / 32x32 kernel always
   int32_t query_tile = 0;
+  // Fused append: the work units of the step's own frames are cut where
+  // their input rows stop being consecutive (so that a unit can be read
+  // from the caller's k / v rows instead of the pool), and the plan carries
+  // the pool row of every input row (the copy that the merge launch makes).
+  bool fused = false;
 };
 
 // Host image of one step's plan.
@@ -138,13 +143,21 @@ struct HostPlan {
   int32_t merge_table = 0;             // offset in ints of the merge order in image
   int32_t merge_slots = 0;             // merge slots per XCD
   bool any_split = false;
+  bool fused = false;                  // built with PlanPolicy::fused
+  int32_t copy_table = 0;              // fused: offset in ints of the input rows' pool rows
 };
 
 // Plan the given streams (ascending) from the allocator's current lists.
 // frames[i]: frames streams[i] appended this step (its queries are
-// frames[i] * tokens_per_frame rows).
+// frames[i] * tokens_per_frame rows).  slots[i]: the placement of those
+// frames (read only with PlanPolicy::fused).
 void build_plan(const Allocator& a, const std::vector<int32_t>& streams, const std::vector<int32_t>& frames,
-                const PlanPolicy& pol, HostPlan* out);
+                const std::vector<const FrameSlots*>& slots, const PlanPolicy& pol, HostPlan* out);
+
+// Pool row (the K row; V is page_size rows further) that input row t of
+// frame fs takes: the frame's patch page for patch rows, its special slots
+// for the special rows [special_row_offset, + num_special_tokens).
+uint32_t input_row_slot(const Config& c, const FrameSlots& fs, int32_t t);
 
 // int32 entries of the device plan image for a configuration (upper bound).
 size_t plan_image_ints(const Config& c);

@@ -58,6 +58,12 @@ struct AttnParams {
   // without first loading the plan's header and records)
   int32_t num_streams;
   kvc_dev_stream recs[KVC_ARG_STREAMS];
+  // Fused append (32x32 kernel, at most KVC_ARG_STREAMS streams): 1 when the
+  // units of the step's own rows are read from kin / vin (per stream, in
+  // plan order: the frames' rows in query order) instead of the pool
+  int32_t fused;
+  const void* kin[KVC_ARG_STREAMS];
+  const void* vin[KVC_ARG_STREAMS];
 };
 
 struct MergeParams {
@@ -70,7 +76,20 @@ struct MergeParams {
   int32_t merge_table;      // offset in ints of the plan's merge order
   int32_t merge_slots;      // merge slots per XCD
   int32_t dtype;            // element type: 0 bfloat16, 1 float16
+  // Fused append: after the KVC_NUM_XCD * merge_slots merge work-groups,
+  // copy_wgs work-groups copy the step's input rows (copy_rows of them, the
+  // streams' own frames in query order, stream i's from row row0[i]) into
+  // the pool, at the K rows the plan's copy table gives (V page_size rows
+  // further); row_bytes = H * D * element size
+  int32_t copy_wgs, copy_rows, copy_table, page_size, row_bytes, num_streams;
+  int32_t row0[KVC_ARG_STREAMS + 1];
+  void* pool;
+  const void* kin[KVC_ARG_STREAMS];
+  const void* vin[KVC_ARG_STREAMS];
 };
+
+// Copies per thread of the merge launch's copy work-groups (fused append).
+#define KVC_COPY_PER 4
 
 // Return 0 on success or the hipError_t value.
 int launch_append(const AppendParams& p, void* hip_stream);

@@ -976,14 +976,54 @@ __global__ __launch_bounds__(64 * F32_WAVES) void attn_f32_kernel(AttnParams p) 
 // together, then folded in split order with weights 2^(lse_c - running max):
 // one memory round trip per chunk, and every sum in a fixed order.  Splits
 // past the tile's own count (other streams may have more) are never loaded.
+// Fused append: the step's input rows into the pool, 16 bytes per thread
+// and copy, COPY_PER copies per thread with their loads issued together.
+// Copy q of the launch is chunk q % cpr of the K (q / cpr even) or V half of
+// input row q / (2 cpr).
+constexpr int COPY_PER = KVC_COPY_PER;
+__device__ __forceinline__ void copy_own_rows(const MergeParams& p, int wg, int nthreads) {
+  const uint32_t cpr = (uint32_t)p.row_bytes >> 4;
+  const uint32_t total = (uint32_t)p.copy_rows * 2u * cpr;
+  const uint32_t q0 = (uint32_t)wg * (uint32_t)nthreads * COPY_PER + threadIdx.x;
+  u32x4 x[COPY_PER];
+  u32x4* dst[COPY_PER];
+#pragma unroll
+  for (int k = 0; k < COPY_PER; ++k) {
+    const uint32_t q = q0 + (uint32_t)(k * nthreads);
+    dst[k] = nullptr;
+    if (q < total) {
+      const uint32_t row = q / (2u * cpr);
+      const uint32_t rem = q - row * 2u * cpr;
+      const bool vh = rem >= cpr;
+      const uint32_t ch = vh ? rem - cpr : rem;
+      int si = 0;
+#pragma unroll
+      for (int i = 1; i < KVC_ARG_STREAMS; ++i)
+        if (i < p.num_streams && (int)row >= p.row0[i]) si = i;
+      const uint8_t* src = static_cast<const uint8_t*>(vh ? p.vin[si] : p.kin[si]) +
+                           (size_t)(row - (uint32_t)p.row0[si]) * p.row_bytes + 16u * ch;
+      const uint32_t kslot = (uint32_t)p.plan[p.copy_table + row];
+      dst[k] = reinterpret_cast<u32x4*>(static_cast<uint8_t*>(p.pool) +
+                                        ((size_t)kslot + (vh ? (size_t)p.page_size : 0)) * p.row_bytes + 16u * ch);
+      x[k] = *reinterpret_cast<const u32x4*>(src);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < COPY_PER; ++k)
+    if (dst[k]) *dst[k] = x[k];
+}
+
 template <int D, int E, int CH>
 __global__ __launch_bounds__(64 * (D / 32) * 4) void merge_kernel(MergeParams p) {
   constexpr int SLICES = D / 32 * 4;
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int H = p.num_heads;
+  if ((int)blockIdx.x >= KVC_NUM_XCD * p.merge_slots) {   // uniform over the work-group
+    copy_own_rows(p, (int)blockIdx.x - KVC_NUM_XCD * p.merge_slots, 64 * (D / 32) * 4);
+    return;
+  }
   const int slot = blockIdx.x >> 3;
-  if (slot >= p.merge_slots) return;      // uniform over the work-group
   // {tile * H + head, splits, first output row, valid rows}
   const i32x4 te = *reinterpret_cast<const i32x4*>(
       p.plan + p.merge_table + KVC_MERGE_INTS * ((blockIdx.x & (KVC_NUM_XCD - 1)) * p.merge_slots + slot));
@@ -1175,7 +1215,8 @@ static int launch_merge_e(const MergeParams& p, int grid, hipStream_t hs) {
 
 int launch_merge(const MergeParams& p, void* s) {
   const hipStream_t hs = (hipStream_t)s;
-  const int grid = KVC_NUM_XCD * p.merge_slots;   // one work-group per merged (query tile, head)
+  // one work-group per merged (query tile, head), then the copy work-groups
+  const int grid = KVC_NUM_XCD * p.merge_slots + p.copy_wgs;
   if (grid == 0) return 0;
   if (p.dtype == 0) return launch_merge_e<0>(p, grid, hs);
   if (p.dtype == 1) return launch_merge_e<1>(p, grid, hs);

@@ -7,10 +7,13 @@
 //   defer_eviction rollback_every n_streams frames_0 .. frames_{n-1}
 // and replays every step of it: block-0 appends (frames_per_first_step frames
 // in each stream's first step), evictions, a plan per step, rollbacks every
-// rollback_every-th step when defer_eviction is 1.  Each plan is checked: the
-// image fits plan_image_ints, every unit entry addresses a whole unit inside
-// the pool and inside its page, unit slot counts sum to the visible token
-// count, and the free lists plus the tables conserve every page ID.
+// rollback_every-th step when defer_eviction is 1; every other step's plan is
+// built for the fused append.  Each plan is checked: the image fits
+// plan_image_ints, every unit entry addresses a whole unit inside the pool
+// and inside its page, unit slot counts sum to the visible token count, and
+// the free lists plus the tables conserve every page ID.  In fused plans a
+// unit read from the input covers input rows inside the step's frames, and
+// the copy table sends each of those rows to the unit's own pool row.
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -51,7 +54,14 @@ static void check_plan(const Config& c, const Allocator& a, const HostPlan& p, c
       const int32_t* e = &p.image[(size_t)r.unit0 + (size_t)KVC_UNIT_INTS * u];
       const uint64_t slot = (uint32_t)e[0];                   // slot index in [page][kv][slot]
       const int32_t valid = e[1];
-      CHECK(e[2] == 0 && e[3] == 0, "%s: unit %d padding", where.c_str(), u);
+      CHECK(e[3] == 0 && (p.fused ? e[2] >= 0 : e[2] == 0), "%s: unit %d padding", where.c_str(), u);
+      if (p.fused && e[2] > 0) {
+        const int32_t n_rows = p.qo_indptr[i + 1] - p.qo_indptr[i];
+        CHECK(e[2] - 1 + valid <= n_rows, "%s: unit %d input rows past the step's frames", where.c_str(), u);
+        for (int32_t k = 0; k < valid && e[2] - 1 + k < n_rows; ++k)
+          CHECK((uint32_t)p.image[(size_t)p.copy_table + p.qo_indptr[i] + e[2] - 1 + k] == (uint32_t)e[0] + (uint32_t)k,
+                "%s: unit %d row %d is not copied to its pool row", where.c_str(), u, k);
+      }
       const uint64_t off = slot * slot_bytes;
       const uint64_t page = slot / (2 * (uint64_t)c.page_size);
       const uint64_t in_page = slot % (2 * (uint64_t)c.page_size);
@@ -114,23 +124,27 @@ int main() {
     std::vector<int64_t> done(ns, 0);
     PlanPolicy pol;
     HostPlan plan;
+    std::vector<std::vector<FrameSlots>> fsl(ns);
     for (int64_t g = 0; g < total; ++g) {
       std::vector<int32_t> streams, nf;
+      std::vector<const FrameSlots*> slots;
       for (int s = 0; s < ns; ++s) {
         if (g < total - frames[s] || done[s] >= frames[s]) continue;
         const int k = done[s] == 0 ? (int)std::min<int64_t>(first_frames, frames[s]) : 1;
-        FrameSlots fs;
+        fsl[s].assign(k, FrameSlots());
         for (int j = 0; j < k; ++j) {
-          const int rc = a.append(s, &fs, &why);
+          const int rc = a.append(s, &fsl[s][j], &why);
           CHECK(rc == OK, "%s: append step %lld stream %d: %s", name.c_str(), (long long)g, s, why.c_str());
         }
         done[s] += k;
         streams.push_back(s);
         nf.push_back(k);
+        slots.push_back(fsl[s].data());
       }
       for (int32_t s : streams) a.evict(s);
       if (streams.empty()) continue;
-      build_plan(a, streams, nf, pol, &plan);
+      pol.fused = g % 2 == 1;
+      build_plan(a, streams, nf, slots, pol, &plan);
       ++plans;
       check_plan(c, a, plan, name + " step " + std::to_string(g));
       if (defer && roll_every > 0 && g % roll_every == roll_every - 1) {

@@ -154,12 +154,14 @@ class Harness:
     rows are drawn (else zero; only for frames never visible at a checked
     step).  rope: K is appended through kvc_append_frames_rope and q run
     through kvc_run_rope with the tables of kvc_synth.rope_tables for each
-    frame; the oracle sees rope_fp64 of the same rows."""
+    frame; the oracle sees rope_fp64 of the same rows.  fused: plans built
+    with KVC_OPT_FUSED_APPEND; every block that runs defers its appends and
+    runs through kvc_run_append, the others append with their rows."""
 
     def __init__(self, wl: syn.Workload, num_blocks: int = 1, q_scale: float = 1.0,
                  real_patch: Optional[Callable[[int, int], bool]] = None, orders=None,
                  options: Optional[Dict[int, int]] = None, device="cuda", oracle_blocks: Sequence[int] = (0,),
-                 max_frames_per_step: int = 1, rope: bool = False):
+                 max_frames_per_step: int = 1, rope: bool = False, fused: bool = False):
         import torch
         import paged_kv_cache_kvc_amd as kvc
         self.torch = torch
@@ -172,6 +174,10 @@ class Harness:
         self.gpu = kvc.PagedKVCache(kvc.make_config(**cfg_args(wl, num_blocks),
                                                     max_frames_per_step=max_frames_per_step), device=device,
                                     free_patch_order=po, free_special_order=so)
+        assert not (fused and rope), "the fused append takes no rotary tables"
+        self.fused = fused
+        if fused:
+            self.gpu.set_option(kvc.KVC_OPT_FUSED_APPEND, 1)
         for k, v in (options or {}).items():
             self.gpu.set_option(k, v)
         self.ocfg = oracle_cfg(wl)
@@ -240,9 +246,16 @@ class Harness:
         run_blocks = list(range(self.nb)) if blocks_to_run is None else list(blocks_to_run)
         outs = {}
         for b in range(self.nb):
+            fuse_b = self.fused and run and b in run_blocks
+            kin, vin = {}, {}
             for s in act:
                 rope = self.tables_dev(self.tables(frames[s], nf[s])) if self.rope else None
-                if nf[s] == 1:
+                if fuse_b:
+                    kvs = [frame_kv(s, frames[s] + j, b) for j in range(nf[s])]
+                    kin[s] = self.to_dev(np.concatenate([x[0] for x in kvs]))
+                    vin[s] = self.to_dev(np.concatenate([x[1] for x in kvs]))
+                    self.gpu.append_frames(b, num_frames=nf[s], stream_id=s, defer=True)
+                elif nf[s] == 1:
                     k, v = frame_kv(s, frames[s], b)
                     self.to_dev(k, self.kbuf)
                     self.to_dev(v, self.vbuf)
@@ -264,6 +277,8 @@ class Harness:
                     out = self.gpu.compute_attention(b, qd, rope=self.tables_dev(tabs))
                     res.setdefault("q_raw", {})[b] = q
                     q = ko.rope_fp64(q, *tabs, self.wl.dtype)
+                elif fuse_b:
+                    out = self.gpu.append_run(b, kin, vin, qd)
                 else:
                     out = self.gpu.compute_attention(b, qd)
                 outs[b] = (q, out)

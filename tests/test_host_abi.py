@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, n), n
         assert n in kvc.SIGNATURES, n
     assert set(kvc.SIGNATURES) == set(names)
-    assert lib.kvc_abi_version() == kvc.ABI_VERSION == 7
+    assert lib.kvc_abi_version() == kvc.ABI_VERSION == 8
 
 
 def cfg_of(wl: syn.Workload):

@@ -52,7 +52,7 @@ def merge_group(r, t, k32):
     return next(g for g in range(r["n_group"]) if 2 * t < (g + 1) * nqt // r["n_group"])
 
 
-def check_image(wl, c):
+def check_image(wl, c, fused=False):
     img = c.get_plan_image().astype(np.int64)
     plan = c.get_plan()
     shape = c.get_plan_shape()
@@ -78,6 +78,7 @@ def check_image(wl, c):
     assert np.array_equal(img[tables_at: tables_at + len(plan["kv_indices"])], plan["kv_indices"])
     item = tiles = 0
     split_streams = set()
+    fused_units = []
     for i, r in enumerate(recs):
         assert r["q_row0"] == plan["qo_indptr"][i] and r["n_q"] == plan["qo_indptr"][i + 1] - plan["qo_indptr"][i]
         assert r["page0"] == plan["kv_indptr"][i]
@@ -91,15 +92,29 @@ def check_image(wl, c):
         for pi, page in enumerate(pages):
             length = r["last_len"] if pi == r["n_pages"] - 1 else (P if pi < r["n_patch"] else pg)
             expect += [(int(page), s0, min(KV_TILE, length - s0)) for s0 in range(0, length, KV_TILE)]
-        assert r["n_units"] == len(expect) >= 1
+        assert (r["n_units"] >= len(expect) if fused else r["n_units"] == len(expect)) and len(expect) >= 1
         assert r["unit0"] % 4 == 0
-        got = []
+        got, srcs = [], []
         for u in range(r["n_units"]):
             slot, valid, z0, z1 = (int(x) for x in img[r["unit0"] + UNIT * u: r["unit0"] + UNIT * (u + 1)])
             page, s = divmod(slot & 0xFFFFFFFF, 2 * pg)   # pool rows [page][K, V][page_size]
-            assert s < pg and z0 == z1 == 0
+            assert s < pg and z1 == 0 and (z0 >= 0 if fused else z0 == 0)
             got.append((page, s, valid))
-        assert got == expect
+            srcs.append(z0)
+        if fused:
+            # the 64-slot chunks, each cut into runs: the units tile every
+            # chunk in order and none leaves its chunk
+            joined = []
+            for (page, s, valid) in got:
+                assert valid >= 1 and s // KV_TILE == (s + valid - 1) // KV_TILE
+                if joined and joined[-1][0] == page and joined[-1][1] + joined[-1][2] == s and s % KV_TILE:
+                    joined[-1] = (page, joined[-1][1], joined[-1][2] + valid)
+                else:
+                    joined.append((page, s, valid))
+            assert joined == expect
+            fused_units.append((i, got, srcs))
+        else:
+            assert got == expect
         assert sum(v for _, _, v in got) == r["kv_len"]
         # work items: heads x splits x query groups, every split non-empty
         assert (r["n_group"], r["n_t32"], r["tail"]) == expected_grouping(wl, r["n_q"], shared, k32)
@@ -121,7 +136,12 @@ def check_image(wl, c):
             split_streams.add(i)
     assert item == n_items and tiles == n_tiles and any_split == (1 if split_streams else 0)
     # merge order: one entry per (32-row tile, head) of a split stream
-    assert merge_at % 4 == 0 and len(img) == merge_at + MERGE * XCD * merge_slots
+    merge_end = merge_at + MERGE * XCD * merge_slots
+    if fused:
+        check_copy_table(wl, c, img, recs, fused_units, -(-merge_end // 4) * 4, n_rows)
+    else:
+        assert len(img) == merge_end
+    assert merge_at % 4 == 0
     ipx = -(-n_items // XCD)
     seen = {}
     for x in range(XCD):
@@ -142,6 +162,48 @@ def check_image(wl, c):
                                                     [r["n_split"], r["q_row0"] + Q_TILE32 * t,
                                                      min(Q_TILE32, r["n_q"] - Q_TILE32 * t)])
     assert seen == want
+
+
+def check_copy_table(wl, c, img, recs, fused_units, at, n_rows):
+    """Fused plans: after the merge order, the pool K row of every input row
+    (the step's own frames, in query order).  Restated from the placement
+    rules: frame f's patch row t (t outside the special rows) goes to slot
+    t or t - n_s of the frame's patch page, which is the f-th of the last F
+    patch pages of the table; its k-th special row to special position
+    total - F n_s + f n_s + k of the stream's special pages.  A unit read
+    from the input covers consecutive input rows whose pool rows are the
+    unit's own; every other unit holds none of those pool rows."""
+    assert len(img) == at + n_rows
+    copy = img[at:].astype(np.int64) & 0xFFFFFFFF
+    plan = c.get_plan()
+    pg, T, ns, off = wl.page_size, wl.tokens_per_frame, wl.num_special_tokens, wl.row_offset
+    for i, r in enumerate(recs):
+        F = r["n_q"] // T
+        pages = plan["kv_indices"][r["page0"]: r["page0"] + r["n_pages"]]
+        sp_pages = pages[r["n_patch"]:]
+        total_sp = sum(pg for _ in sp_pages[:-1]) + (r["last_len"] if len(sp_pages) else 0)
+        own = copy[r["q_row0"]: r["q_row0"] + r["n_q"]]
+        for f in range(F):
+            patch_page = int(pages[r["n_patch"] - F + f])
+            for t in range(T):
+                if off <= t < off + ns:
+                    pos = total_sp - F * ns + f * ns + (t - off)
+                    want = int(sp_pages[pos // pg]) * 2 * pg + pos % pg
+                else:
+                    want = patch_page * 2 * pg + (t if t < off else t - ns)
+                assert own[f * T + t] == want, (i, f, t)
+        own_rows = {int(x): k for k, x in enumerate(own)}
+        assert len(own_rows) == r["n_q"]
+        for (si, got, srcs) in fused_units:
+            if si != i:
+                continue
+            for (page, s, valid), z in zip(got, srcs):
+                slot = page * 2 * pg + s
+                if z:
+                    assert z - 1 + valid <= r["n_q"]
+                    assert all(own[z - 1 + k] == slot + k for k in range(valid))
+                else:
+                    assert all(slot + k not in own_rows for k in range(valid))
 
 
 def stream_and_check(wl, steps_to_check, nframes=None):
@@ -284,3 +346,68 @@ def test_planner_kernel_choice_head_dim_64(heads, hist, nf, rows):
     c.plan()
     assert c.get_plan_shape()["group_rows"] == rows
     check_image(wl, c)
+
+
+def _mid_specials():
+    """Specials in the middle of the frame (rows 17..21 of 45): the patch
+    rows of a frame are not consecutive in the input there."""
+    return syn.Workload("mid_specials", 1, 2, 32, 40, 5, 64, 2, 6, (30,), 31,
+                        max_patch_pages=2 + 6 + 1, max_special_pages=8, special_row_offset=17)
+
+
+@pytest.mark.parametrize("name", ["tiny", "base", "r518", "mid_specials", "max_specials", "no_specials",
+                                  "steps_of_64"])
+def test_plan_image_fused_append(name):
+    """Plans built for the fused append (KVC_OPT_FUSED_APPEND): the own
+    frames' units and the copy table, on a scale step and single-frame
+    steps."""
+    wl = {"mid_specials": _mid_specials(), **edge_workloads()}.get(name) or syn.WORKLOADS[name]
+    first = min(wl.scale_frames, 8) if name != "steps_of_64" else 64
+    cfg = kvc.make_config(wl.num_blocks, wl.num_heads, wl.head_dim, wl.tokens_per_frame, wl.num_special_tokens,
+                          page_size=wl.page_size, scale_frames=wl.scale_frames, sliding_window=wl.sliding_window,
+                          num_streams=wl.num_streams, max_patch_pages=wl.max_patch_pages,
+                          max_special_pages=wl.max_special_pages, special_row_offset=wl.row_offset,
+                          max_frames_per_step=max(first, 1))
+    c = kvc.PagedKVCache(cfg, metadata_only=True)
+    c.set_option(kvc.KVC_OPT_FUSED_APPEND, 1)
+    F = min(max(wl.frames), 80)
+    done = 0
+    while done < F:
+        nf = first if done == 0 and first > 1 else 1
+        nf = min(nf, F - done)
+        if nf > 1:
+            c.append_frames(0, num_frames=nf)
+        else:
+            c.append_frame(0)
+        c.evict_frames()
+        c.plan()
+        if done < 3 or done % 7 == 0 or done + nf == F:
+            check_image(wl, c, fused=True)
+        done += nf
+
+
+def test_plan_image_fused_check_catches_corruption():
+    """The fused decoder rejects a copy table entry moved by one row and an
+    input row of a unit moved by one."""
+    wl = syn.WORKLOADS["tiny"]
+    c = kvc.PagedKVCache(cfg_of(wl), metadata_only=True)
+    c.set_option(kvc.KVC_OPT_FUSED_APPEND, 1)
+    for _ in range(3):
+        c.append_frame(0)
+        c.evict_frames()
+        c.plan()
+    good = c.get_plan_image()
+    check_image(wl, c, fused=True)
+    n = len(c.get_plan()["planned"])
+    rec0 = HEADER
+    unit0, nu = int(good[rec0 + REC_FIELDS.index("unit0")]), int(good[rec0 + REC_FIELDS.index("n_units")])
+    own = next(u for u in range(nu) if good[unit0 + UNIT * u + 2] > 0)
+    bad1 = good.copy()
+    bad1[-1] += 1
+    bad2 = good.copy()
+    bad2[unit0 + UNIT * own + 2] += 1
+    assert n == 1
+    for bad in (bad1, bad2):
+        c.get_plan_image = lambda bad=bad: bad
+        with pytest.raises(AssertionError):
+            check_image(wl, c, fused=True)
