@@ -286,7 +286,9 @@ __device__ __forceinline__ void wait_ahead(int a) {
   }
 }
 
-template <int D, int E, bool TAIL>
+// FUSED: launched by kvc_run_append (p.fused = 1): units whose entry z is
+// nonzero are read from the caller's k and v.
+template <int D, int E, bool TAIL, bool FUSED>
 __global__ __launch_bounds__(64 * KVC_ATTN32_WAVES, 1) void attn32_kernel(AttnParams p) {
   using S = Shape32<D>;
   using MM = M32<E>;
@@ -352,11 +354,11 @@ __global__ __launch_bounds__(64 * KVC_ATTN32_WAVES, 1) void attn32_kernel(AttnPa
 #pragma unroll
   for (int i = 0; i < P0; ++i)
     e_first[i] = i < nstage ? int4{units[KVC_UNIT_INTS * i], units[KVC_UNIT_INTS * i + 1],
-                                   units[KVC_UNIT_INTS * i + 2], 0}
+                                   FUSED ? units[KVC_UNIT_INTS * i + 2] : 0, 0}
                             : int4{0, KVC_KV_TILE, 0, 0};
   auto uniform_entry = [](const int4& e) {
     return int4{__builtin_amdgcn_readfirstlane(e.x), __builtin_amdgcn_readfirstlane(e.y),
-                __builtin_amdgcn_readfirstlane(e.z), 0};
+                FUSED ? __builtin_amdgcn_readfirstlane(e.z) : 0, 0};
   };
   auto stage_entry = [&](int i) { return uniform_entry(elds[i]); };
 
@@ -371,8 +373,7 @@ __global__ __launch_bounds__(64 * KVC_ATTN32_WAVES, 1) void attn32_kernel(AttnPa
   // the pool's row layout; V is vin - kin bytes past K there.
   const uint8_t* kin = nullptr;
   uint64_t vin_delta = 0;
-  const bool fused = p.fused != 0;
-  if (fused) {
+  if constexpr (FUSED) {
     const void* kb = p.kin[0];
     const void* vb = p.vin[0];
 #pragma unroll
@@ -420,7 +421,7 @@ __global__ __launch_bounds__(64 * KVC_ATTN32_WAVES, 1) void attn32_kernel(AttnPa
   // (the unit's first row of the K or V half), so rows are measured from the
   // unit's first row, never below it.
   auto issue_e = [&](int sidx, int4 e) {
-    const bool in = fused && e.z != 0;
+    const bool in = FUSED && e.z != 0;
     const uint8_t* kbase = in ? kin + (uint64_t)(uint32_t)(e.z - 1) * slot_bytes
                               : pool + (uint64_t)(uint32_t)e.x * slot_bytes;
     const uint8_t* ubase = kbase + head_off + (wave_v ? (in ? vin_delta : v_half) : 0);
@@ -807,19 +808,24 @@ __global__ __launch_bounds__(64 * KVC_ATTN32_WAVES, 1) void attn32_kernel(AttnPa
   }
 }
 
-template <int E, bool TAIL>
-int launch32_et(const AttnParams& p, int32_t grid, hipStream_t hs) {
+template <int E, bool TAIL, bool FUSED>
+int launch32_etf(const AttnParams& p, int32_t grid, hipStream_t hs) {
   switch (p.head_dim) {
     case 32:
-      hipLaunchKernelGGL((attn32_kernel<32, E, TAIL>), dim3(grid), dim3(64 * KVC_ATTN32_WAVES), 0, hs, p);
+      hipLaunchKernelGGL((attn32_kernel<32, E, TAIL, FUSED>), dim3(grid), dim3(64 * KVC_ATTN32_WAVES), 0, hs, p);
       break;
     case 64:
-      hipLaunchKernelGGL((attn32_kernel<64, E, TAIL>), dim3(grid), dim3(64 * KVC_ATTN32_WAVES), 0, hs, p);
+      hipLaunchKernelGGL((attn32_kernel<64, E, TAIL, FUSED>), dim3(grid), dim3(64 * KVC_ATTN32_WAVES), 0, hs, p);
       break;
     default:
       return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();
+}
+
+template <int E, bool TAIL>
+int launch32_et(const AttnParams& p, int32_t grid, hipStream_t hs) {
+  return p.fused ? launch32_etf<E, TAIL, true>(p, grid, hs) : launch32_etf<E, TAIL, false>(p, grid, hs);
 }
 
 }  // namespace
