@@ -722,7 +722,9 @@ __global__ __launch_bounds__(64 * KVC_ATTN32_WAVES, 1) void attn32_kernel(AttnPa
     if (st.n_split > 1) {
       // normalised partial output (a convex combination of V rows, rounded
       // to the element type) in the accumulator's lane order, and its
-      // log-sum-exp; rows past the stream's queries are stored too (never merged)
+      // log-sum-exp; rows past the stream's queries are stored too (never
+      // merged).  Non-temporal stores: the merge launch reads them once,
+      // and they leave the L2 before the launch ends.
       const size_t pt = ((size_t)split * H + hd) * p.tiles_cap + st.q_tile0 + tile;
       uint16_t* po = static_cast<uint16_t*>(p.part_o) + pt * (size_t)(DB * 4 * 256) + lane * 4;
 #pragma unroll
@@ -730,9 +732,9 @@ __global__ __launch_bounds__(64 * KVC_ATTN32_WAVES, 1) void attn32_kernel(AttnPa
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const f32x4 v = f32x4{o[db][4 * i], o[db][4 * i + 1], o[db][4 * i + 2], o[db][4 * i + 3]} * inv;
-          *reinterpret_cast<u32x2*>(po + (db * 4 + i) * 256) = El<E>::cvt4(v);
+          __builtin_nontemporal_store(El<E>::cvt4(v), reinterpret_cast<u32x2*>(po + (db * 4 + i) * 256));
         }
-      if (h == 0) p.part_lse[pt * 32 + n] = ref + __log2f(l);
+      if (h == 0) __builtin_nontemporal_store(ref + __log2f(l), p.part_lse + pt * 32 + n);
     } else if (row < st.n_q) {
       uint16_t* orow = static_cast<uint16_t*>(p.o) + ((size_t)(st.q_row0 + row) * H + hd) * D;
 #pragma unroll
@@ -791,9 +793,10 @@ __global__ __launch_bounds__(64 * KVC_ATTN32_WAVES, 1) void attn32_kernel(AttnPa
           for (int db = 0; db < TDB; ++db) {
             const int d = 16 * db + 4 * g4;
             const int b32 = d >> 5, i = (d & 31) >> 3, hh = (d >> 2) & 1;
-            *reinterpret_cast<u32x2*>(po + (b32 * 4 + i) * 256 + (32 * hh + r16) * 4) = El<E>::cvt4(ot[db] * inv);
+            __builtin_nontemporal_store(El<E>::cvt4(ot[db] * inv),
+                                        reinterpret_cast<u32x2*>(po + (b32 * 4 + i) * 256 + (32 * hh + r16) * 4));
           }
-          if (g4 == 0) p.part_lse[pt * 32 + r16] = M + __log2f(lsum);
+          if (g4 == 0) __builtin_nontemporal_store(M + __log2f(lsum), p.part_lse + pt * 32 + r16);
         } else {
           const int row = 32 * st.n_t32 + r16;
           if (row < st.n_q) {

@@ -86,7 +86,7 @@ typedef struct kvc_dev_stream {
   int32_t last_len;   // valid tokens on the last page
   int32_t kv_len;     // valid visible tokens L
   int32_t unit0;      // offset in ints of this stream's unit table from the plan start
-  int32_t n_units;    // work units: n_patch * upp + full special pages * ups + units of the last page
+  int32_t n_units;    // work units (64-slot chunks of the visible pages; fused plans cut the own frames' further)
   int32_t n_split;    // KV splits
   int32_t n_group;    // query groups (work-groups per head and split)
   int32_t item0;      // first attention work item of this stream
