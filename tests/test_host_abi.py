@@ -596,3 +596,31 @@ def test_build_refuses_kernels_that_spill():
     b.check_no_scratch(spill.format("_ZN3kvc13attn32_kernelILi64E"))
     with pytest.raises(RuntimeError, match="SGPRs spilled"):
         b.check_no_scratch(spill.format("_ZN3kvc11attn_kernelILi128E"))
+
+
+def test_fused_append_option_and_plan():
+    """KVC_OPT_FUSED_APPEND: 0 or 1 only; a plan built with it keeps the
+    page tables, split counts and query grouping of the plain plan (only the
+    unit table gains the cuts of the own rows, and the copy table follows
+    the merge order); a metadata-only context has nothing to run."""
+    wl = syn.WORKLOADS["base"]
+    plain = kvc.PagedKVCache(cfg_of(wl), metadata_only=True)
+    fused = kvc.PagedKVCache(cfg_of(wl), metadata_only=True)
+    with pytest.raises(kvc.KvcError):
+        fused.set_option(kvc.KVC_OPT_FUSED_APPEND, 2)
+    fused.set_option(kvc.KVC_OPT_FUSED_APPEND, 1)
+    assert fused.get_option(kvc.KVC_OPT_FUSED_APPEND) == 1
+    for _ in range(200):
+        for c in (plain, fused):
+            c.append_frame(0)
+            c.evict_frames()
+            c.plan()
+    a, b = plain.get_plan(), fused.get_plan()
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+    assert plain.get_plan_shape() == fused.get_plan_shape()
+    ia, ib = plain.get_plan_image(), fused.get_plan_image()
+    T = wl.tokens_per_frame
+    assert len(ib) >= len(ia) + T    # one pool row per input row after the merge order
+    with pytest.raises(kvc.KvcError):
+        fused.raw_run_append(0, [0], [0], 0, 0, 0)
