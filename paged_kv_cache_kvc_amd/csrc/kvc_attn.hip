@@ -643,8 +643,11 @@ __global__ __launch_bounds__(64 * KVC_ATTN32_WAVES, 1) void attn32_kernel(AttnPa
     constexpr bool is_lead = decltype(lead_tag)::value;
     wait_ahead<LPW, NST - 2>(min(nstage - 1 - s, NST - 2));
     ring_barrier();
-    if constexpr (do_issue)
-      issue_e(s + NST - 1, uniform_entry(e_next));
+    // the refill of the slot that stage s - 1 held (every wave has passed
+    // the barrier, so none reads it any more) is issued after this
+    // iteration's QK MFMAs: right after the barrier all 8 waves would queue
+    // their loads at once
+    const int4 e_iss = uniform_entry(e_next);
     const int valid = __builtin_amdgcn_readfirstlane(e_cur.y);
     e_cur = elds[min(s + 1, KVC_MAX_SPLIT_STAGES - 1)];
     e_next = elds[min(s + NST, KVC_MAX_SPLIT_STAGES - 1)];
@@ -653,6 +656,7 @@ __global__ __launch_bounds__(64 * KVC_ATTN32_WAVES, 1) void attn32_kernel(AttnPa
       read_v(s);
       if constexpr (TAIL) read_tail(s);
       qk();
+      if constexpr (do_issue) issue_e(s + NST - 1, e_iss);
       if constexpr (TAIL) {
         sT = El<E>::mfma(tk[0], qT[0], f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
@@ -689,6 +693,7 @@ __global__ __launch_bounds__(64 * KVC_ATTN32_WAVES, 1) void attn32_kernel(AttnPa
       read_k(s);
       read_v(s);
       qk();
+      if constexpr (do_issue) issue_e(s + NST - 1, e_iss);
       if (__builtin_expect(valid < KVC_KV_TILE, 0)) mask32(sc, valid, h);
     }
   };
