@@ -701,6 +701,9 @@ __global__ __launch_bounds__(64 * KVC_ATTN32_WAVES, 1) void attn32_kernel(AttnPa
   // registers (a shared loop with a role branch inside made the compiler
   // copy the output accumulators between the branches every stage)
   if (lead) {
+    // the lead waves issue ahead of their lag partners when both are ready
+    // (measured: 0.17 us shorter launches; the other way round, 1.8 us longer)
+    __builtin_amdgcn_s_setprio(2);
     int s = 0;
     for (; s + NST - 1 < nstage; ++s) stage_body(s, Flag<true>{}, Flag<true>{});
     for (; s < nstage; ++s) stage_body(s, Flag<false>{}, Flag<true>{});
