@@ -143,3 +143,27 @@ def test_fused_call_order_errors():
     c2.set_option(kvc.KVC_OPT_FUSED_APPEND, 1)
     with pytest.raises(kvc.KvcError):
         c2.append_run(0, {0: k}, {0: k}, q)
+
+
+def test_fused_base_full_size():
+    """The benchmark's step at its full shape: H=16, D=64, 262 tokens per
+    frame, 200 frames, two block pools, every step through kvc_run_append
+    where it runs; checked at ragged and steady-state steps against the
+    oracle (the launch configuration bench.py times: 256 work-groups of
+    the 32x32 kernel with tails, 16 splits), pools bit-exact at the end."""
+    _need_gpu()
+    wl = syn.WORKLOADS["base"]
+    checks = {0, 1, 72, 150, 199}
+    h = Harness(wl, num_blocks=2, oracle_blocks=(0, 1), fused=True)
+    for t in range(max(wl.frames)):
+        res = h.step(run=t in checks, check=t in checks)
+        if t in checks:
+            for k in ("kv_indptr", "kv_indices", "last_page_len", "n_patch_pages", "qo_indptr"):
+                assert np.array_equal(res["gpu_plan"][k], res["ora_plan"][k]), k
+            for b in (0, 1):
+                st = check_close(res["out_bits"][b], res["ref"][b])
+            log(f"fused base step {t}: splits {res['gpu_plan']['n_splits']} shape {h.gpu.get_plan_shape()} {st}")
+    assert h.gpu.get_plan_shape() == {"work_items": 256, "group_rows": 272}
+    assert list(res["gpu_plan"]["n_splits"]) == [16]
+    for b in (0, 1):
+        assert np.array_equal(h.pool_bits(b), h.ora.pools[b].data)
