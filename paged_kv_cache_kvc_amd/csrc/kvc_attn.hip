@@ -235,6 +235,84 @@ __device__ __forceinline__ float renorm32(const f32x16 (&s)[2], float sl, int& f
   return sum;
 }
 
+// Exact path of a bfloat16 32x32 tile without the scores: the column's
+// largest packed probability 2^e m (e its exponent field) fixes the integer
+// shift k = e - 126 that brings it into [0.5, 1); the running sum and output
+// are scaled by 2^-k, ref moves up by k and every packed probability is
+// divided by 2^k exactly, by lowering its exponent field (a value that would
+// fall below the normal range becomes 0: under 2^-126 of the new maximum).
+// The result is what exp2 against the moved ref gives, truncated the same
+// way, so the scores need not stay live past the softmax.  It cannot stand in
+// for them when a probability overflowed (exponent field 255) or, on a tile
+// with no state yet and valid slots in the stage, when the largest
+// probability is under 2^-60 (smaller terms may have underflowed): then the
+// wave sets `need` and the caller redoes the split with renorm32.
+template <int DB>
+__device__ __forceinline__ float renorm32pk(int& fresh, float& ref, float& nref, float& l, f32x16 (&o)[DB],
+                                            u32x4 (&pk)[4], int valid, int& need) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  u16x2 m = __builtin_bit_cast(u16x2, pk[0][0]);
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, pk[t][k]));
+  uint32_t mb = m.x > m.y ? m.x : m.y;
+  {
+    uint32_t a = mb, b = mb;
+    swap32(a, b);
+    mb = a > b ? a : b;
+  }
+  const int ex = (int)((mb >> 7) & 0xFF);
+  const bool first = fresh != 0;
+  if (__builtin_amdgcn_ballot_w64(ex == 0xFF || (first && valid > 0 && mb < 0x2180u)) != 0) {
+    need = 1;   // the split is redone with the scores
+    return 0.f;
+  }
+  // a column with no valid slot yet keeps the tile fresh (all slots masked)
+  fresh = __builtin_amdgcn_readfirstlane((int)(first && __builtin_amdgcn_ballot_w64(mb == 0u) != 0));
+  int shift = mb == 0u ? 0 : ex - 126;
+  if (!first && shift < 0) shift = 0;
+  if (!first) {
+    const float alpha = __builtin_amdgcn_ldexpf(1.0f, -shift);
+    l *= alpha;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[db][4 * q4 + j] *= alpha;
+      }
+  }
+  ref += (float)shift;
+  nref = -ref;
+  float a = 0.f, b = 0.f;
+  const int sh7 = shift << 7;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t w = pk[t][k];
+      const int lo0 = (int)(w & 0xFFFFu), hi0 = (int)(w >> 16);
+      const int lo = lo0 - sh7, hi = hi0 - sh7;
+      pk[t][k] = (uint32_t)((lo0 == 0 || lo < 0x80) ? 0 : lo) | ((uint32_t)((hi0 == 0 || hi < 0x80) ? 0 : hi) << 16);
+    }
+    a = El<0>::dot_ones(pk[t][0], a);
+    b = El<0>::dot_ones(pk[t][1], b);
+    a = El<0>::dot_ones(pk[t][2], a);
+    b = El<0>::dot_ones(pk[t][3], b);
+  }
+  float sum = a + b;
+  {
+    uint32_t x = __builtin_bit_cast(uint32_t, sum), y = x;
+    swap32(x, y);
+    sum = __builtin_bit_cast(float, x) + __builtin_bit_cast(float, y);
+  }
+  asm volatile("s_nop 3" ::: "memory");
+  return sum;
+}
+
 // The same for the tail's 16x16 block (4 slots per lane; a column's 16
 // slots sit in lanes l, l ^ 16, l ^ 32, l ^ 48).  Returns the lane's sum.
 template <int TDB, int E>
@@ -302,6 +380,8 @@ __global__ __launch_bounds__(64 * KVC_ATTN32_WAVES, 1) void attn32_kernel(AttnPa
   constexpr int P0 = NST - 3;   // stages loaded before the query operands are read
   __shared__ __attribute__((aligned(1024))) uint8_t ring[NST * S::STAGE];
   __shared__ __attribute__((aligned(1024))) int4 elds[KVC_MAX_SPLIT_STAGES];
+  // set when a wave needs the split redone with the exact path on the scores
+  __shared__ int xflag[1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -582,10 +662,19 @@ __global__ __launch_bounds__(64 * KVC_ATTN32_WAVES, 1) void attn32_kernel(AttnPa
   };
   // lazy check of the tile (column sums of the probabilities with the current
   // ref; the exact path when a sum is too large or the tile is fresh)
-  auto check = [&](const f32x4& rs) {
+  // (bfloat16, first pass: the exact path from the packed probabilities, so
+  // that the scores die with the softmax; the pass with `exact` set, and
+  // float16, rebase from the scores)
+  int need_exact = 0;
+  auto check = [&](const f32x4& rs, int vld, auto exact_tag) {
+    constexpr bool exact = decltype(exact_tag)::value;
     float cs = rs[0];
-    if (__builtin_expect(fresh || __builtin_amdgcn_ballot_w64(cs > LAZY_COL_LIMIT), 0))
-      cs = renorm32<DB, E>(sc, sl, fresh, ref, nref, l, o, pk);
+    if (__builtin_expect(fresh || __builtin_amdgcn_ballot_w64(sum_exceeds(cs, LAZY_COL_LIMIT)), 0)) {
+      if constexpr (E == 0 && !exact)
+        cs = renorm32pk<DB>(fresh, ref, nref, l, o, pk, vld, need_exact);
+      else
+        cs = renorm32<DB, E>(sc, sl, fresh, ref, nref, l, o, pk);
+    }
     l += cs;
   };
   bf16x8 qv[KS], qT[TKS];
@@ -604,6 +693,7 @@ __global__ __launch_bounds__(64 * KVC_ATTN32_WAVES, 1) void attn32_kernel(AttnPa
       for (int db = 0; db < DB; ++db) o[db] = MM::mfma32(vop[t][db], __builtin_bit_cast(bf16x8, pk[t]), o[db]);
   };
   // ---- prologue: query operands and stage 0 ----
+  if (tid == 0) xflag[0] = 0;         // published by the barrier below
   wait_ahead<LPW, P0 - 1>(pre - 1);   // queries, entries and stage 0 landed (own loads)
   block_barrier();                    // ... and everyone's
   {
@@ -638,7 +728,8 @@ __global__ __launch_bounds__(64 * KVC_ATTN32_WAVES, 1) void attn32_kernel(AttnPa
   // s + NST - 1 (two loops, with and without those loads) ----
   int4 e_next = elds[min(NST - 1, KVC_MAX_SPLIT_STAGES - 1)];
   int4 e_cur = elds[0];
-  auto stage_body = [&](int s, auto issue_tag, auto lead_tag) {
+  int valid_prev = 0;   // lag waves: valid slots of stage s - 1 (stage -1: none)
+  auto stage_body = [&](int s, auto issue_tag, auto lead_tag, auto exact_tag) {
     constexpr bool do_issue = decltype(issue_tag)::value;
     constexpr bool is_lead = decltype(lead_tag)::value;
     wait_ahead<LPW, NST - 2>(min(nstage - 1 - s, NST - 2));
@@ -674,11 +765,11 @@ __global__ __launch_bounds__(64 * KVC_ATTN32_WAVES, 1) void attn32_kernel(AttnPa
         pT[1] = El<E>::pack_p(__builtin_amdgcn_exp2f(__builtin_fmaf(sT[2], sl, nrefT)),
                               __builtin_amdgcn_exp2f(__builtin_fmaf(sT[3], sl, nrefT)));
         float lt = El<E>::dot_ones(pT[1], El<E>::dot_ones(pT[0], 0.f));
-        if (__builtin_expect(freshT || __builtin_amdgcn_ballot_w64(lt > LAZY_SUM_LIMIT), 0))
+        if (__builtin_expect(freshT || __builtin_amdgcn_ballot_w64(sum_exceeds(lt, LAZY_SUM_LIMIT)), 0))
           lt = renorm16<TDB, E>(sT, sl, freshT, refT, nrefT, lT, oT, pT);
         lT += lt;
       }
-      check(rs);
+      check(rs, valid, exact_tag);
       pv();
       if constexpr (TAIL) {
 #pragma unroll
@@ -687,7 +778,8 @@ __global__ __launch_bounds__(64 * KVC_ATTN32_WAVES, 1) void attn32_kernel(AttnPa
     } else {
       // stage s - 1: scores in sc, V in vop
       softmax();
-      check(rowsum());
+      check(rowsum(), valid_prev, exact_tag);
+      valid_prev = valid;
       pv();
       // stage s: V into vop for the next iteration, scores into sc
       read_k(s);
@@ -700,23 +792,57 @@ __global__ __launch_bounds__(64 * KVC_ATTN32_WAVES, 1) void attn32_kernel(AttnPa
   // one loop per role: each keeps its loop-carried accumulators in its own
   // registers (a shared loop with a role branch inside made the compiler
   // copy the output accumulators between the branches every stage)
-  if (lead) {
-    // the lead waves issue ahead of their lag partners when both are ready
-    // (measured: 0.17 us shorter launches; the other way round, 1.8 us longer)
-    __builtin_amdgcn_s_setprio(2);
-    int s = 0;
-    for (; s + NST - 1 < nstage; ++s) stage_body(s, Flag<true>{}, Flag<true>{});
-    for (; s < nstage; ++s) stage_body(s, Flag<false>{}, Flag<true>{});
-  } else {
-    int s = 0;
-    for (; s + NST - 1 < nstage; ++s) stage_body(s, Flag<true>{}, Flag<false>{});
-    for (; s < nstage; ++s) stage_body(s, Flag<false>{}, Flag<false>{});
-  }
-  // ---- drain: the lag waves' last stage ----
-  if (!lead) {
-    softmax();
-    check(rowsum());
-    pv();
+  // the lead waves issue ahead of their lag partners when both are ready
+  // (measured: 0.17 us shorter launches; the other way round, 1.8 us longer)
+  if (lead) __builtin_amdgcn_s_setprio(2);
+  auto pass = [&](auto exact_tag) {
+    if (lead) {
+      int s = 0;
+      for (; s + NST - 1 < nstage; ++s) stage_body(s, Flag<true>{}, Flag<true>{}, exact_tag);
+      for (; s < nstage; ++s) stage_body(s, Flag<false>{}, Flag<true>{}, exact_tag);
+    } else {
+      int s = 0;
+      for (; s + NST - 1 < nstage; ++s) stage_body(s, Flag<true>{}, Flag<false>{}, exact_tag);
+      for (; s < nstage; ++s) stage_body(s, Flag<false>{}, Flag<false>{}, exact_tag);
+    }
+    // ---- drain: the lag waves' last stage ----
+    if (!lead) {
+      softmax();
+      check(rowsum(), valid_prev, exact_tag);
+      pv();
+    }
+  };
+  pass(Flag<false>{});
+  if constexpr (E == 0) {
+    // A wave whose packed probabilities could not stand in for the scores
+    // (an overflow, or a first stage far below the reference) asks for the
+    // split again with the exact path on the scores; the work-group decides
+    // together (every wave is done with the ring at the barrier).
+    if (need_exact && lane == 0) xflag[0] = 1;
+    ring_barrier();
+    if (__builtin_amdgcn_readfirstlane(xflag[0])) {
+      ref = nref = l = refT = nrefT = lT = 0.f;
+      fresh = freshT = 1;
+      valid_prev = 0;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
+#pragma unroll
+      for (int db = 0; db < TDB; ++db) oT[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sc[sb][e] = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) vop[t][db] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+      e_next = elds[min(NST - 1, KVC_MAX_SPLIT_STAGES - 1)];
+      e_cur = elds[0];
+      for (int i = 0; i < min(nstage, NST - 1); ++i) issue_e(i, stage_entry(i));
+      pass(Flag<true>{});
+    }
   }
   // the epilogue reads the accumulators the last MFMAs wrote
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");

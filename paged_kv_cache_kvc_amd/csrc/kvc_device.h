@@ -214,6 +214,15 @@ __device__ __forceinline__ kvc_dev_stream stream_of_item(const AttnParams& p, in
 constexpr float LAZY_SUM_LIMIT = 256.0f;
 constexpr float LAZY_COL_LIMIT = 4.0f * LAZY_SUM_LIMIT;
 
+// The lazy checks compare a sum's bit pattern with the limit's: a sum of
+// non-negative terms orders like its bits, and so an infinite sum and a NaN
+// one (an overflowed probability times a 0 entry of a mask operand) exceed
+// the limit too, which a float compare in a build that assumes no NaN can
+// miss.
+__device__ __forceinline__ bool sum_exceeds(float x, float limit) {
+  return __builtin_bit_cast(uint32_t, x) > __builtin_bit_cast(uint32_t, limit);
+}
+
 }  // namespace dev
 }  // namespace kvc
 

@@ -670,7 +670,7 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
     if constexpr (SH) O::qk1(ksh, q2, sc2);
     // own tile 0: check its stage sum before its P.V
     float lt = cs0[0];
-    if (fresh0 || __builtin_amdgcn_ballot_w64(lt > LAZY_COL_LIMIT))
+    if (fresh0 || __builtin_amdgcn_ballot_w64(sum_exceeds(lt, LAZY_COL_LIMIT)))
       lt = lane_swap_sum(renorm<4, DB, E>(sc0, sl, fresh0, ref0, nref0, l0, o0, pk0));
     l0 += lt;
     {
@@ -706,11 +706,11 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_kernel(AttnParams
     }
     // own tile 1: check its stage sum (its P.V follows in the next step 0)
     lt = cs1[0];
-    if (fresh1 || __builtin_amdgcn_ballot_w64(lt > LAZY_COL_LIMIT))
+    if (fresh1 || __builtin_amdgcn_ballot_w64(sum_exceeds(lt, LAZY_COL_LIMIT)))
       lt = lane_swap_sum(renorm<4, DB, E>(sc1, sl, fresh1, ref1, nref1, l1, o1, pk1));
     l1 += lt;
     if constexpr (SH) {
-      if (fresh2 || __builtin_amdgcn_ballot_w64(lt2 > LAZY_SUM_LIMIT))
+      if (fresh2 || __builtin_amdgcn_ballot_w64(sum_exceeds(lt2, LAZY_SUM_LIMIT)))
         lt2 = renorm<1, DB, E>(sc2, sl, fresh2, ref2, nref2, l2, o2, pk2);
       l2 += lt2;
       // P^T of the shared block: its 4 slots sit at positions 4*half..4*half+3
