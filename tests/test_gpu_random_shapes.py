@@ -1,7 +1,7 @@
 """Seeded random shapes against the oracle.
 
 Each case draws the cache's geometry and the planner's options: head count,
-head_dim (32, 64, 128), element type (bf16, f16), patch tokens per frame and
+head_dim (32, 64, 128), element type (bf16, f16, f32), patch tokens per frame and
 the page size above them, special tokens per frame and the rows they take in
 the frame, scale frames, window, one to three streams (later ones joining
 late), shuffled free lists, a multi-frame first step, the split cap, the
@@ -11,9 +11,9 @@ FlashInfer's Paged KV Cache Attention Outperforms SDPA Fallback in Streaming
 Inference" §Dual-Stream Attention; [p1] "How FlashInfer KV Cache Attention
 Accelerates Streaming 3D Reconstruction Over SDPA" §Two-Stream Design for
 Token Types): at the checked steps the plan equals the oracle's and the
-output is within the 16-bit bounds of tests/stream_harness.py; at the end
-the pools equal the oracle's bit for bit.  The draws are bounded so that a
-case runs in a few seconds."""
+output is within the element type's bounds of tests/stream_harness.py; at
+the end the pools equal the oracle's bit for bit.  The draws are bounded so
+that a case runs in a few seconds."""
 import dataclasses
 
 import numpy as np
@@ -39,7 +39,7 @@ def draw_case(i: int):
     rng = np.random.default_rng(7100 + i)
     D = int(rng.choice([32, 64, 128]))
     H = int(rng.choice([1, 2, 3, 4] if D == 128 else [1, 2, 3, 4, 6, 8]))
-    dtype = str(rng.choice(["bf16", "f16"]))
+    dtype = str(rng.choice(["bf16", "f16", "f32"], p=[0.4, 0.4, 0.2]))
     P = int(rng.integers(1, 261))
     n_s = int(rng.choice([0, 1, 5, int(rng.integers(1, 17))]))
     # (at least 4 slots: one frame's specials then span at most 8 pages)
@@ -79,7 +79,8 @@ def test_draws_cover_the_options():
         seen |= {("D", wl.head_dim), ("dtype", wl.dtype), ("streams>1", wl.num_streams > 1), ("multi", multi),
                  ("fused", fused), ("mid", wl.row_offset < wl.patch_tokens and wl.num_special_tokens > 0),
                  ("tile", opts.get(kvc.KVC_OPT_QUERY_TILE, 0))}
-    for want in (("D", 32), ("D", 64), ("D", 128), ("dtype", "bf16"), ("dtype", "f16"), ("streams>1", True),
+    for want in (("D", 32), ("D", 64), ("D", 128), ("dtype", "bf16"), ("dtype", "f16"), ("dtype", "f32"),
+                 ("streams>1", True),
                  ("multi", True), ("fused", True), ("fused", False), ("mid", True)):
         assert want in seen, want
 
