@@ -29,6 +29,9 @@ HIP_FLAGS = [
     "-mllvm", "-amdgpu-mfma-vgpr-form",
     # scores are never NaN (masked slots are -inf): max needs no NaN quieting
     "-fno-honor-nans",
+    # leading scalar kernel arguments preloaded into scalar registers at
+    # dispatch (the merge kernel's plan offsets)
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
 ]
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 HIP_FLAGS.append(f"-I{INCLUDE}")

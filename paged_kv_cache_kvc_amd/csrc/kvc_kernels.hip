@@ -1014,19 +1014,24 @@ __device__ __forceinline__ void copy_own_rows(const MergeParams& p, int wg, int 
 }
 
 template <int D, int E, int CH>
-__global__ __launch_bounds__(64 * (D / 32) * 4) void merge_kernel(MergeParams p) {
+// plan, merge_table and merge_slots repeat fields of p as leading scalar
+// arguments, which the dispatch preloads into scalar registers: the merge
+// order's entry is then read without waiting for the argument segment.
+__global__ __launch_bounds__(64 * (D / 32) * 4) void merge_kernel(const int32_t* __restrict__ plan,
+                                                                   int32_t merge_table, int32_t merge_slots,
+                                                                   MergeParams p) {
   constexpr int SLICES = D / 32 * 4;
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int H = p.num_heads;
-  if ((int)blockIdx.x >= KVC_NUM_XCD * p.merge_slots) {   // uniform over the work-group
-    copy_own_rows(p, (int)blockIdx.x - KVC_NUM_XCD * p.merge_slots, 64 * (D / 32) * 4);
+  if ((int)blockIdx.x >= KVC_NUM_XCD * merge_slots) {   // uniform over the work-group
+    copy_own_rows(p, (int)blockIdx.x - KVC_NUM_XCD * merge_slots, 64 * (D / 32) * 4);
     return;
   }
   const int slot = blockIdx.x >> 3;
   // {tile * H + head, splits, first output row, valid rows}
   const i32x4 te = *reinterpret_cast<const i32x4*>(
-      p.plan + p.merge_table + KVC_MERGE_INTS * ((blockIdx.x & (KVC_NUM_XCD - 1)) * p.merge_slots + slot));
+      plan + merge_table + KVC_MERGE_INTS * ((blockIdx.x & (KVC_NUM_XCD - 1)) * merge_slots + slot));
   const int pair = te.x;
   if (pair < 0) return;
   const int gt = pair / H;                // global 32-row tile
@@ -1190,13 +1195,16 @@ template <int E, int CH>
 static int launch_merge_ec(const MergeParams& p, int grid, hipStream_t hs) {
   switch (p.head_dim) {
     case 32:
-      hipLaunchKernelGGL((merge_kernel<32, E, CH>), dim3(grid), dim3(64 * 4), 0, hs, p);
+      hipLaunchKernelGGL((merge_kernel<32, E, CH>), dim3(grid), dim3(64 * 4), 0, hs, p.plan, p.merge_table,
+                         p.merge_slots, p);
       break;
     case 64:
-      hipLaunchKernelGGL((merge_kernel<64, E, CH>), dim3(grid), dim3(64 * 8), 0, hs, p);
+      hipLaunchKernelGGL((merge_kernel<64, E, CH>), dim3(grid), dim3(64 * 8), 0, hs, p.plan, p.merge_table,
+                         p.merge_slots, p);
       break;
     case 128:
-      hipLaunchKernelGGL((merge_kernel<128, E, CH>), dim3(grid), dim3(64 * 16), 0, hs, p);
+      hipLaunchKernelGGL((merge_kernel<128, E, CH>), dim3(grid), dim3(64 * 16), 0, hs, p.plan, p.merge_table,
+                         p.merge_slots, p);
       break;
     default:
       return (int)hipErrorInvalidValue;
